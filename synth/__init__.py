@@ -1,0 +1,179 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the smoke check.
+
+This module draws random numbers and casts them to storage types; it holds none of the
+attention method's arithmetic.  Every tensor comes from a torch.Generator seeded from
+(seed, tensor id, extra ids), so any chunk can be drawn again on its own.  Both the HIP
+path and the CPU oracle receive exactly the same bytes: a test draws a tensor once, hands
+it to the library, and gives a host copy to the oracle.
+
+Workload shapes follow the five layer configurations the attention path is measured on:
+  c1   tiny prefill, fp32: n=256, d=256, m=4, c=64 (RoPE 16), 4 heads, indexer 2x16, k=8,
+       n_win=16
+  c2   Flash-shaped decode: 16 sequences x 131072 tokens (32768 entries), d=4096, 64 heads
+       of 512, indexer 64x128, k=512, n_win=128, E4M3+bf16 KV
+  c3   Pro-shaped decode: 4 x 1048576 tokens (262144 entries), d=7168, 128 heads, k=1024
+  c4a  Flash chunked prefill: a 32768-token chunk after a 1048576-token prefix
+  c4b  the same after a 262144-token prefix
+  c5   HCA decode: 8 x 1048576 tokens, m'=128 (8192 entries), dense, 64 heads
+Value distributions: hidden states N(0,1); projection weights N(0, 1/fan_in); positional
+biases and sink logits N(0, 0.1) (second argument read as the variance); queries, indexer
+queries and indexer head weights N(0,1).  Synthetic cache rows (used where a decode stage is
+tested on its own) are N(0,1) per dimension, the scale of an RMS-normalised row; synthetic
+indexer keys are N(0, 0.25).
+"""
+from __future__ import annotations
+
+import hashlib
+import math
+
+import torch
+
+__all__ = ["CONFIGS", "config", "generator", "randn", "weights", "hidden", "queries",
+           "synthetic_cache", "row_bytes", "SEED"]
+
+SEED = 0
+
+_BASE = dict(rope_base=10000.0, eps=1e-6)
+
+CONFIGS = {
+    "c1": dict(name="c1", B=1, prefix=0, T=256, d=256, c=64, rope_dim=16, n_h=4, c_I=16, n_hI=2,
+               m=4, dual=True, top_k=8, n_win=16, kv_fmt="f32", idx_fmt="f32", act="f32",
+               sink=True, **_BASE),
+    "c2": dict(name="c2", B=16, prefix=131072, T=1, d=4096, c=512, rope_dim=64, n_h=64, c_I=128,
+               n_hI=64, m=4, dual=True, top_k=512, n_win=128, kv_fmt="q", idx_fmt="e4m3",
+               act="bf16", sink=True, **_BASE),
+    "c3": dict(name="c3", B=4, prefix=1048576, T=1, d=7168, c=512, rope_dim=64, n_h=128, c_I=128,
+               n_hI=64, m=4, dual=True, top_k=1024, n_win=128, kv_fmt="q", idx_fmt="e4m3",
+               act="bf16", sink=True, **_BASE),
+    "c4a": dict(name="c4a", B=1, prefix=1048576, T=32768, d=4096, c=512, rope_dim=64, n_h=64,
+                c_I=128, n_hI=64, m=4, dual=True, top_k=512, n_win=128, kv_fmt="q",
+                idx_fmt="e4m3", act="bf16", sink=True, **_BASE),
+    "c4b": dict(name="c4b", B=1, prefix=262144, T=32768, d=4096, c=512, rope_dim=64, n_h=64,
+                c_I=128, n_hI=64, m=4, dual=True, top_k=512, n_win=128, kv_fmt="q",
+                idx_fmt="e4m3", act="bf16", sink=True, **_BASE),
+    "c5": dict(name="c5", B=8, prefix=1048576, T=1, d=4096, c=512, rope_dim=64, n_h=64, c_I=0,
+               n_hI=0, m=128, dual=False, top_k=0, n_win=128, kv_fmt="q", idx_fmt="e4m3",
+               act="bf16", sink=True, **_BASE),
+}
+
+
+def config(name: str, **over) -> dict:
+    """A copy of a named configuration with fields overridden."""
+    cfg = dict(CONFIGS[name])
+    cfg.update(over)
+    return cfg
+
+
+def row_bytes(cfg: dict) -> int:
+    """Bytes of one stored KV row: 4c for fp32, (c - r) E4M3 + r bf16 otherwise."""
+    if cfg["kv_fmt"] == "f32":
+        return 4 * cfg["c"]
+    return cfg["c"] - cfg["rope_dim"] + 2 * cfg["rope_dim"]
+
+
+def _seed_of(*ids) -> int:
+    h = hashlib.sha256(repr(tuple(ids)).encode()).digest()
+    return int.from_bytes(h[:8], "little") & ((1 << 63) - 1)
+
+
+def generator(device, *ids) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed_of(*ids))
+    return g
+
+
+def randn(shape, std, device, *ids) -> torch.Tensor:
+    """float32 N(0, std^2) drawn from a generator seeded by ``ids``."""
+    g = generator(device, *ids)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
+
+
+def _store(x: torch.Tensor, kind: str) -> torch.Tensor:
+    if kind == "f32":
+        return x.to(torch.float32)
+    if kind == "bf16":
+        return x.to(torch.bfloat16)
+    if kind == "e4m3":
+        return x.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    raise ValueError(kind)
+
+
+def weights(cfg: dict, seed: int = SEED, device="cpu") -> dict:
+    """Projection weights (rows = output features, [width][d]), biases, gamma and sink.
+
+    CSA: kv_a kv_b z_a z_b [c][d]; ki_a ki_b zi_a zi_b [c_I][d]; B_a B_b [m][c];
+         BI_a BI_b [m][c_I].  HCA: kv z [c][d]; B [m][c].
+    Weights are stored in the activation type (fp32 or bf16); biases, gamma (ones) and the
+    sink are fp32.
+    """
+    d, c, cI, m = cfg["d"], cfg["c"], cfg["c_I"], cfg["m"]
+    act = cfg["act"]
+    std_w = 1.0 / math.sqrt(d)
+    std_b = math.sqrt(0.1)
+    W = {}
+    names = ("kv_a", "kv_b", "z_a", "z_b") if cfg["dual"] else ("kv", "z")
+    for i, nm in enumerate(names):
+        W[nm] = _store(randn((c, d), std_w, device, seed, "w", nm), act)
+    if cfg["dual"]:
+        for nm in ("ki_a", "ki_b", "zi_a", "zi_b"):
+            W[nm] = _store(randn((cI, d), std_w, device, seed, "w", nm), act)
+        W["B_a"] = randn((m, c), std_b, device, seed, "b", "a")
+        W["B_b"] = randn((m, c), std_b, device, seed, "b", "b")
+        W["BI_a"] = randn((m, cI), std_b, device, seed, "b", "ia")
+        W["BI_b"] = randn((m, cI), std_b, device, seed, "b", "ib")
+    else:
+        W["B"] = randn((m, c), std_b, device, seed, "b", "hca")
+    W["gamma_kv"] = torch.ones(c, device=device, dtype=torch.float32)
+    W["gamma_q"] = torch.ones(c, device=device, dtype=torch.float32)
+    W["sink"] = (randn((cfg["n_h"],), std_b, device, seed, "sink") if cfg.get("sink", True)
+                 else None)
+    return W
+
+
+def hidden(cfg: dict, seq: int, t0: int, t1: int, seed: int = SEED, device="cpu",
+           chunk: int = 4096) -> torch.Tensor:
+    """Hidden states of tokens t0..t1-1 of sequence ``seq``, [t1-t0][d] in the activation type.
+    Drawn in aligned chunks of ``chunk`` tokens so that any range can be drawn again."""
+    d = cfg["d"]
+    parts = []
+    c0 = (t0 // chunk) * chunk
+    while c0 < t1:
+        blk = randn((chunk, d), 1.0, device, seed, "h", seq, c0)
+        lo, hi = max(t0, c0) - c0, min(t1, c0 + chunk) - c0
+        parts.append(_store(blk[lo:hi], cfg["act"]))
+        c0 += chunk
+    return torch.cat(parts, 0)
+
+
+def queries(cfg: dict, Q: int, seed: int = SEED, device="cpu", tag="q") -> dict:
+    """Per-query inputs: q [Q][n_h][c] (activation type), qI [Q][n_hI][c_I] (index format),
+    w [Q][n_hI] (activation type).  All N(0,1)."""
+    out = {"q": _store(randn((Q, cfg["n_h"], cfg["c"]), 1.0, device, seed, tag, "q"), cfg["act"])}
+    if cfg["dual"]:
+        out["qI"] = _store(randn((Q, cfg["n_hI"], cfg["c_I"]), 1.0, device, seed, tag, "qI"),
+                           cfg["idx_fmt"])
+        out["w"] = _store(randn((Q, cfg["n_hI"]), 1.0, device, seed, tag, "w"), cfg["act"])
+    return out
+
+
+def synthetic_cache(cfg: dict, B: int, N: int, R: int, seed: int = SEED, device="cpu") -> dict:
+    """A synthetic compressed cache for testing the decode stages on their own.
+
+    kv  [B][N][row] uint8 rows (N(0,1) per dimension, stored in the KV format)
+    ki  [B][N][c_I] indexer keys (N(0, 0.25), stored in the index format)
+    win [B][R][row] window ring rows, N(0,1) like kv.
+    """
+    c, r = cfg["c"], cfg["rope_dim"]
+
+    def rows(n, *ids):
+        x = randn((B, n, c), 1.0, device, seed, *ids)
+        if cfg["kv_fmt"] == "f32":
+            return x.contiguous().view(torch.uint8).reshape(B, n, 4 * c)
+        nope = _store(x[..., : c - r], "e4m3")
+        rope = x[..., c - r:].to(torch.bfloat16).contiguous().view(torch.uint8)
+        return torch.cat([nope, rope], dim=-1).contiguous()
+
+    out = {"kv": rows(N, "ckv"), "win": rows(R, "cwin")}
+    if cfg["dual"]:
+        out["ki"] = _store(randn((B, N, cfg["c_I"]), 0.5, device, seed, "cki"), cfg["idx_fmt"])
+    return out
