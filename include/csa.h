@@ -1,0 +1,278 @@
+/*
+ * csa.h — C ABI of the compressed sparse attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes one attention layer of the kind the DeepSeek-V4 pages describe:
+ *   1. overlapping dual-window KV compression: every m tokens fold into one entry, the
+ *      softmax taken per column over 2m weighted projections with a learned positional bias
+ *      (reading notes "DeepSeekV4技术报告阅读笔记", zouxinn.github.io, §2.3.1 eqs. 9-12;
+ *      PaperTrace "02 · DeepSeek-V4: 压缩注意力撑起 1M 上下文" §2.1), or the single-path,
+ *      non-overlapping variant with m' tokens per entry (reading notes §2.4.1 eqs. 20-23);
+ *   2. lightning-indexer scores I_{t,s} = sum_h w_{t,h} ReLU(q^I_{t,h} . K^I_s)
+ *      (reading notes §2.3.2 eq. 16);
+ *   3. per-query top-k over the visible entries (reading notes eq. 17);
+ *   4. shared-KV multi-query attention over the selected entries plus a window of the
+ *      n_win most recent uncompressed tokens, with a per-head sink logit in the softmax
+ *      denominator, RMSNorm on query and KV heads, RoPE on the last rope_dim dims and the
+ *      output de-rotated by the query position (reading notes eq. 19, §2.5.1-2.5.4 eq. 27;
+ *      PaperTrace §2.4).
+ *
+ * Conventions that hold for every entry point:
+ *   - Every pointer argument that names a tensor is a DEVICE pointer owned by the caller.
+ *     The library allocates no device memory and keeps no state between calls; scratch space
+ *     is the caller's `ws` buffer, sized with csa_workspace_size().
+ *   - Work is enqueued on `stream` and the call returns without waiting for it.  A fault
+ *     inside a kernel surfaces at the caller's next synchronisation.
+ *   - Positions are 0-based token indices and live in device memory, so they cannot be
+ *     checked on the host: they are clamped, not validated (visible entries of a query at
+ *     position tau are min(tau / m, n_entries[seq])).
+ *   - All argument checks run on the host before anything is enqueued.  On error nothing
+ *     is enqueued, the return value is a csa_status and csa_last_error() holds a message.
+ *   - Tensors are dense, row-major, with the shapes given in brackets.
+ *   - Calls that share a cache, workspace or output buffer and overlap in time (different
+ *     streams without ordering) race.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum csa_status {
+  CSA_OK = 0,
+  CSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive or inconsistent sizes */
+  CSA_ERR_UNSUPPORTED = 2,      /* a size/format combination this build has no kernel for */
+  CSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  CSA_ERR_HIP = 4               /* a HIP launch failed; csa_last_error() has the HIP text */
+} csa_status;
+
+typedef enum csa_format {
+  CSA_FMT_F32 = 0,        /* float32 */
+  CSA_FMT_BF16 = 1,       /* bfloat16 */
+  CSA_FMT_E4M3 = 2,       /* OCP FP8 E4M3 (e4m3fn), unit scale */
+  CSA_FMT_E4M3_BF16 = 3   /* KV rows: c - rope_dim E4M3 bytes, then rope_dim bfloat16 */
+} csa_format;
+
+/* Operation selector for csa_workspace_size(). */
+typedef enum csa_op {
+  CSA_OP_COMPRESS = 0,
+  CSA_OP_INDEX_TOPK = 1,
+  CSA_OP_ATTEND = 2,
+  CSA_OP_FORWARD = 3
+} csa_op;
+
+/*
+ * Layer shape and formats.
+ *   d         hidden size of h_t.
+ *   c         width of a KV entry and of each query head (reading notes eq. 19: o in R^c).
+ *   rope_dim  trailing dims under RoPE (the pages use 64); even, <= c.
+ *   n_h       query heads; n_hI, c_I indexer heads and width (reading notes §2.3.2).
+ *   m         tokens per entry: m for CSA (pages: 4), m' for HCA (pages: 128).
+ *   dual      1 = CSA (a|b overlapping fold, indexer, top-k); 0 = HCA (single path, dense).
+ *   top_k     entries kept per query (pages: 512 Flash, 1024 Pro); 0 with dual = 0.
+ *   n_win     sliding-window length (pages: 128); the window of a query at tau covers
+ *             positions max(0, tau - n_win + 1) .. tau, the query's own token included.
+ *   scale     softmax scale on q.k; <= 0 selects 1/sqrt(c).
+ *   rope_base RoPE base (10000); pair j of the RoPE dims turns by pos * base^(-2j/rope_dim).
+ *   rms_eps   RMSNorm epsilon (1e-6).
+ *   act_fmt   F32 or BF16: hidden states, projection weights, queries q, indexer weights w,
+ *             and the attention output.
+ *   kv_fmt    F32 (c floats per row) or E4M3_BF16 (c - rope_dim + 2 * rope_dim bytes per row:
+ *             RoPE dims kept in BF16, the rest in FP8, as the explainer's key-numbers table and
+ *             PaperTrace §2.5 state).
+ *   idx_fmt   F32 or E4M3: indexer keys K^I and indexer queries q^I.
+ */
+typedef struct csa_dims {
+  int32_t d, c, rope_dim, n_h, c_I, n_hI, m;
+  int32_t dual;
+  int32_t top_k;
+  int32_t n_win;
+  float scale;
+  float rope_base;
+  float rms_eps;
+  int32_t act_fmt;
+  int32_t kv_fmt;
+  int32_t idx_fmt;
+} csa_dims;
+
+/*
+ * Compression weights, stored transposed (row u of a [width][d] matrix is column u of the
+ * pages' W in R^{d x width}), in act_fmt.
+ *   CSA: w_kv  [4][c][d]   = W^{aKV}, W^{bKV}, W^{aZ}, W^{bZ}       (reading notes eqs. 9-10)
+ *        w_idx [4][c_I][d] = the same four for the indexer keys   (K^IComp: "the same
+ *                            compression, smaller output width", deep dive §3.2)
+ *        bias     [2][m][c]   = B^a, B^b (float32)                 (eq. 11)
+ *        bias_idx [2][m][c_I] = the indexer's B^a, B^b (float32)
+ *   HCA: w_kv  [2][c][d]   = W^{KV}, W^{Z}                          (eqs. 20-21)
+ *        w_idx = NULL, bias [m][c] = B (float32) (eq. 22), bias_idx = NULL
+ *   gamma_kv [c] float32 RMSNorm weight of the KV head, or NULL for ones.
+ */
+typedef struct csa_weights {
+  const void* w_kv;
+  const void* w_idx;
+  const float* bias;
+  const float* bias_idx;
+  const float* gamma_kv;
+} csa_weights;
+
+/*
+ * Per-sequence cache, all caller-owned device memory.
+ *   B        number of sequences.
+ *   cap      entry capacity per sequence; entries past it are not stored.
+ *   win_cap  window ring rows per sequence, >= n_win.  Token j's raw row sits in slot
+ *            j % win_cap.  A compress call of T tokens needs win_cap >= T + n_win - 1 for
+ *            the chunk's own queries to find their window rows.
+ *   kv       [B][cap][row_bytes]   finalized entries (RMSNorm, RoPE at position m*i).
+ *   ki       [B][cap][c_I]         indexer keys in idx_fmt (CSA only; NULL for HCA).
+ *   n_entries[B] int32             complete entries; written by csa_compress.
+ *   win      [B][win_cap][row_bytes] raw window rows: the a-path row C^a_j (HCA: C_j),
+ *                                  finalized at position j.
+ *   win_pos  [B][win_cap] int32    position held by each ring slot, -1 when empty; the
+ *                                  caller fills it with -1 before a sequence's first call.
+ *   state    [B][S][P] float32     projections of the last S tokens (S = 2m for CSA, m for
+ *                                  HCA; P = 4c + 4c_I for CSA, 2c for HCA), slot j % S, so
+ *                                  that a block split across calls still folds.
+ * Successive csa_compress calls on a sequence must cover consecutive positions.
+ */
+typedef struct csa_cache {
+  int32_t B;
+  int32_t cap;
+  int32_t win_cap;
+  void* kv;
+  void* ki;
+  int32_t* n_entries;
+  void* win;
+  int32_t* win_pos;
+  float* state;
+} csa_cache;
+
+/* Version of this header the library was built from (CSA_ABI_VERSION). */
+int csa_abi_version(void);
+
+/* Static text for a csa_status value. */
+const char* csa_status_string(int status);
+
+/* Message of the last failed call on this host thread ("" if none).  Thread-local. */
+const char* csa_last_error(void);
+
+/* Bytes of one stored KV row for these dims (4c, or c - rope_dim + 2 rope_dim); 0 if the
+ * dims are invalid. */
+size_t csa_row_bytes(const csa_dims* dims);
+
+/* Floats per token held in csa_cache.state (P above) and state rows per sequence (S). */
+int32_t csa_state_width(const csa_dims* dims);
+int32_t csa_state_rows(const csa_dims* dims);
+
+/*
+ * Workspace bytes for one call of `op`:
+ *   COMPRESS   B sequences x T tokens.
+ *   INDEX_TOPK Q queries against entry capacity cap.
+ *   ATTEND     Q queries (cap unused).
+ *   FORWARD    B x T new tokens, queries = those tokens, entry capacity cap.  With
+ *              q_chunk > 0 the indexer works on q_chunk queries at a time and the score
+ *              buffer shrinks accordingly; 0 means all B*T at once.
+ * Returns CSA_OK and writes *bytes, or an error for invalid dims.
+ */
+int csa_workspace_size(const csa_dims* dims, int32_t op, int32_t B, int32_t T, int32_t Q,
+                       int32_t cap, int32_t q_chunk, size_t* bytes);
+
+/*
+ * Compress T new tokens of each of cache->B sequences (reading notes eqs. 9-12 / 20-23).
+ *   H     [B][T][d] hidden states in act_fmt; token t of sequence b sits at position
+ *         pos0[b] + t.
+ *   pos0  [B] int32 device array: position of each sequence's first new token.
+ * Writes: the raw window row of every new token (ring slot, win_pos); every entry whose
+ * block completes inside the chunk (kv, ki; entry i of a CSA layer folds the a-rows of
+ * tokens m i .. m i + m - 1 and the b-rows of tokens m(i-1) .. m i - 1, entry 0 a-rows only);
+ * n_entries[b] = min(cap, (pos0[b] + T) / m); and the projection state.
+ * Entries are RMS-normalised with gamma_kv and rotated to position m*i; indexer keys are
+ * stored as folded (no norm, no rotation).
+ * Errors: INVALID_ARGUMENT (null pointer, T < 1, win_cap < n_win), UNSUPPORTED,
+ * WORKSPACE_TOO_SMALL, HIP_ERROR.
+ */
+int csa_compress(const csa_dims* dims, const csa_weights* w, const csa_cache* cache,
+                 const void* H, int32_t T, const int32_t* pos0, void* ws, size_t ws_bytes,
+                 hipStream_t stream);
+
+/*
+ * Indexer scores and top-k selection for Q queries (reading notes eqs. 16-17), CSA only.
+ *   qI      [Q][n_hI][c_I] indexer queries in idx_fmt.
+ *   w       [Q][n_hI] indexer head weights in act_fmt.
+ *   q_seq   [Q] int32 sequence of each query; q_pos [Q] int32 its position tau.
+ *   idx_out [Q][top_k] int32: the selected entry indices in increasing order, -1 padded.
+ *           A query sees V = min(tau / m, n_entries[seq]) entries (its own block is
+ *           excluded); if V <= top_k all V are taken; equal scores go to the lower index.
+ *   scores_out  NULL, or [Q][cap] float32 receiving the scores of the visible entries
+ *           (entries s >= V are left untouched).
+ * Errors: INVALID_ARGUMENT (null pointer, Q < 1, dual = 0 or top_k < 1), UNSUPPORTED
+ * (V could exceed what the selection kernels handle for this top_k), WORKSPACE_TOO_SMALL,
+ * HIP_ERROR.
+ */
+int csa_index_topk(const csa_dims* dims, const csa_cache* cache, const void* qI,
+                   const void* w, const int32_t* q_seq, const int32_t* q_pos, int32_t Q,
+                   int32_t* idx_out, float* scores_out, void* ws, size_t ws_bytes,
+                   hipStream_t stream);
+
+/*
+ * The indexer on its own (reading notes eq. 16): scores[q][s] for s < V of each query, in
+ * float32, row stride ld (>= the largest V; cache->cap always works).  Entries s >= V are
+ * left untouched.  csa_index_topk = csa_index_scores + csa_topk.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, HIP_ERROR.
+ */
+int csa_index_scores(const csa_dims* dims, const csa_cache* cache, const void* qI,
+                     const void* w, const int32_t* q_seq, const int32_t* q_pos, int32_t Q,
+                     float* scores, int64_t ld, hipStream_t stream);
+
+/*
+ * The top-k selection on its own (reading notes eq. 17) over scores [Q][ld] as written by
+ * csa_index_scores: idx_out[Q][top_k] as in csa_index_topk.  ws as csa_workspace_size(
+ * INDEX_TOPK) minus the score buffer: csa_topk_workspace_size().
+ */
+int csa_topk(const csa_dims* dims, const csa_cache* cache, const int32_t* q_seq,
+             const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld,
+             int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes of csa_topk for Q queries against entry capacity cap. */
+size_t csa_topk_workspace_size(const csa_dims* dims, int32_t Q, int32_t cap);
+
+/*
+ * Shared-KV MQA for Q queries (reading notes eqs. 19/26, 27; §2.5.1-2.5.2).
+ *   q       [Q][n_h][c] query heads in act_fmt (before RMSNorm and RoPE).
+ *   gamma_q [c] float32 RMSNorm weight shared by the query heads, or NULL for ones.
+ *   sink    [n_h] float32 sink logits z'_h, or NULL for no sink.
+ *   idx     [Q][top_k] int32 entry indices (-1 = unused slot), or NULL to attend densely to
+ *           every visible entry (HCA).
+ *   out     [Q][n_h][c] in act_fmt: for each head, sum_j s_j key_j over the selected entries
+ *           and the window rows in one softmax with the sink in the denominator, the last
+ *           rope_dim dims rotated by -tau.  Keys are shared by all heads (K = V).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR.
+ */
+int csa_attend(const csa_dims* dims, const csa_cache* cache, const void* q,
+               const float* gamma_q, const float* sink, const int32_t* q_seq,
+               const int32_t* q_pos, int32_t Q, const int32_t* idx, void* out, void* ws,
+               size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The whole path for a chunk of T new tokens per sequence: csa_compress, then (CSA)
+ * csa_index_topk and csa_attend with the new tokens as queries (query b*T + t sits at
+ * position pos0[b] + t), or (HCA) dense csa_attend.
+ *   q, qI, w  per-query inputs as in csa_index_topk / csa_attend, Q = B*T.
+ *   idx_out   [Q][top_k] int32 receiving the selection, or NULL (CSA: then it lives in ws).
+ * The indexer works on q_chunk queries at a time, the largest that fits ws_bytes.
+ */
+int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cache,
+                const void* H, int32_t T, const int32_t* pos0, const void* q, const void* qI,
+                const void* wI, const float* gamma_q, const float* sink, void* out,
+                int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H_ */

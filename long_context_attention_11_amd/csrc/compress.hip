@@ -1,0 +1,413 @@
+// KV compression for gfx950: projection GEMM, dual-window (or single-path) softmax fold,
+// RMSNorm + RoPE finalize and storage rounding, and the projection state carried between
+// calls.
+//
+// Sources: reading notes "DeepSeekV4技术报告阅读笔记" (zouxinn.github.io) §2.3.1 eqs. 9-12
+// (CSA fold), §2.4.1 eqs. 20-23 (HCA fold), §2.5.1-2.5.2 (RMSNorm, partial RoPE);
+// PaperTrace "02 · DeepSeek-V4: 压缩注意力撑起 1M 上下文" §2.1 (m = 4 worked case), §2.5
+// (RoPE dims in BF16, the rest FP8); deep dive "DeepSeek-V4 架构设计深度解析" §3.2 (indexer keys
+// use the same compression with a smaller width).
+#include "csa_internal.h"
+
+namespace csa {
+
+// ============================================================================ projection
+//
+// P[ks][M][NP] = H[M][K-range ks] . Wall[NP][K-range ks]^T, Wall = [w_kv rows; w_idx rows].
+// Column order of P (CSA): C^a | C^b | Z^a | Z^b (c each) | the same four of width c_I.
+// HCA: C | Z.  Split-K partials are summed by the consumers in a fixed order.
+
+namespace {
+
+constexpr int PJ_BM = 64, PJ_BN = 64, PJ_BK = 64, PJ_LD = PJ_BK + 8;  // LDS row pitch (bf16)
+
+__device__ __forceinline__ const uint16_t* wall_row(const uint16_t* wkv, const uint16_t* widx,
+                                                    int nkv, int n, int K) {
+  return n < nkv ? wkv + (size_t)n * K : widx + (size_t)(n - nkv) * K;
+}
+
+// bf16 MFMA GEMM: 64x64 tile per workgroup, 4 waves each 32x32 (2x2 MFMA 16x16x32 tiles).
+__global__ __launch_bounds__(256) void k_project_bf16(const uint16_t* __restrict__ H,
+                                                      const uint16_t* __restrict__ wkv,
+                                                      const uint16_t* __restrict__ widx, int nkv,
+                                                      int M, int NP, int K, int kchunk,
+                                                      float* __restrict__ P) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][PJ_BM * PJ_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][PJ_BN * PJ_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.y * PJ_BM, n0 = blockIdx.x * PJ_BN, ks = blockIdx.z;
+  const int k_begin = ks * kchunk, k_end = min(K, k_begin + kchunk);
+  // loader mapping: 64 rows x 64 k per stage = 512 chunks of 8 bf16 (16 B); 2 per thread
+  const int lr = tid >> 3, lc = (tid & 7) * 8;  // row 0..31 (+32), col chunk
+  const uint16_t* arow[2];
+  const uint16_t* brow[2];
+  bool aval[2], bval[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int r = lr + 32 * h;
+    aval[h] = (m0 + r) < M;
+    arow[h] = H + (size_t)min(m0 + r, M - 1) * K;
+    bval[h] = (n0 + r) < NP;
+    brow[h] = wall_row(wkv, widx, nkv, min(n0 + r, NP - 1), K);
+  }
+  uint4 ra[2], rb[2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ra[h] = aval[h] ? *reinterpret_cast<const uint4*>(arow[h] + k0 + lc) : make_uint4(0, 0, 0, 0);
+      rb[h] = bval[h] ? *reinterpret_cast<const uint4*>(brow[h] + k0 + lc) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<uint4*>(&As[buf][(lr + 32 * h) * PJ_LD + lc]) = ra[h];
+      *reinterpret_cast<uint4*>(&Bs[buf][(lr + 32 * h) * PJ_LD + lc]) = rb[h];
+    }
+  };
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const int fr = lane & 15, fg = lane >> 4;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+  int buf = 0;
+  if (k_begin < k_end) gload(k_begin);
+  for (int k0 = k_begin; k0 < k_end; k0 += PJ_BK) {
+    sstore(buf);
+    __syncthreads();
+    if (k0 + PJ_BK < k_end) gload(k0 + PJ_BK);
+#pragma unroll
+    for (int kk = 0; kk < PJ_BK; kk += 32) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm + 16 * i + fr) * PJ_LD + kk + fg * 8]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(wn + 16 * j + fr) * PJ_LD + kk + fg * 8]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    buf ^= 1;
+  }
+  // D layout of a 16x16 MFMA tile: lane holds column (lane & 15), rows 4*(lane >> 4) + e.
+  float* Pk = P + (size_t)ks * M * NP;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      int col = n0 + wn + 16 * j + fr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        int row = m0 + wm + 16 * i + 4 * fg + e;
+        if (row < M && col < NP) Pk[(size_t)row * NP + col] = acc[i][j][e];
+      }
+    }
+}
+
+// float32 GEMM on the vector ALUs (fp32 activations): 16x16 outputs per workgroup.
+__global__ __launch_bounds__(256) void k_project_f32(const float* __restrict__ H,
+                                                     const float* __restrict__ wkv,
+                                                     const float* __restrict__ widx, int nkv,
+                                                     int M, int NP, int K, float* __restrict__ P) {
+  __shared__ float As[16][17], Bs[16][17];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int row = blockIdx.y * 16 + ty, col = blockIdx.x * 16 + tx;
+  const int brow_n = blockIdx.x * 16 + ty;
+  const float* bsrc = brow_n < NP ? (brow_n < nkv ? wkv + (size_t)brow_n * K
+                                                  : widx + (size_t)(brow_n - nkv) * K)
+                                  : nullptr;
+  float acc = 0.f;
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    As[ty][tx] = (row < M && k0 + tx < K) ? H[(size_t)row * K + k0 + tx] : 0.f;
+    Bs[ty][tx] = (bsrc && k0 + tx < K) ? bsrc[k0 + tx] : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) acc = fmaf(As[ty][kk], Bs[tx][kk], acc);
+    __syncthreads();
+  }
+  if (row < M && col < NP) P[(size_t)row * NP + col] = acc;
+}
+
+// ============================================================================ fold / finalize
+
+struct FoldArgs {
+  const float* P;        // [ksplit][B*T][NP]
+  int ksplit;
+  const float* state;    // [B][S][NP]
+  int S, NP;
+  int T, m, dual, c, r, cI;
+  const int32_t* pos0;
+  const float* bias;     // CSA [2][m][c], HCA [m][c]
+  const float* bias_idx; // CSA [2][m][cI]
+  const float* gamma;    // [c] or null
+  float eps;
+  double rope_base;
+  int kv_fmt, idx_fmt;
+  int cap, win_cap, rowB;
+  uint8_t* kv;
+  uint8_t* ki;
+  uint8_t* win;
+  int32_t* win_pos;
+  int32_t* n_entries;
+};
+
+// Projection value of token j (global position) in column col of sequence b.
+__device__ __forceinline__ float proj(const FoldArgs& a, int b, int p0, int j, int col) {
+  if (j >= p0) {
+    size_t row = (size_t)b * a.T + (j - p0);
+    float v = 0.f;
+    for (int k = 0; k < a.ksplit; ++k) v += a.P[((size_t)k * gridDim.y * a.T + row) * a.NP + col];
+    return v;
+  }
+  return a.state[((size_t)b * a.S + (j % a.S)) * a.NP + col];
+}
+
+// Softmax fold of one column (reading notes eqs. 11-12 / 22-23).
+//   CSA: logits Z^a_{mi+r} + B^a_r and Z^b_{m(i-1)+r} + B^b_r (b half absent for i = 0),
+//        values C^a and C^b.  HCA: logits Z_{mi+r} + B_r over the m rows of block i.
+// colC/colZ name the projection columns of the a path; b-path columns are +boff.
+__device__ float fold_column(const FoldArgs& a, int b, int p0, int i, int colCa, int colZa,
+                             int boff, const float* Ba, const float* Bb, int bstride_col,
+                             int u) {
+  const int m = a.m;
+  const int ja = m * i, jb = m * (i - 1);
+  const bool has_b = a.dual && i > 0;
+  float mx = -INFINITY;
+  for (int r = 0; r < m; ++r) mx = fmaxf(mx, proj(a, b, p0, ja + r, colZa) + Ba[r * bstride_col + u]);
+  if (has_b)
+    for (int r = 0; r < m; ++r)
+      mx = fmaxf(mx, proj(a, b, p0, jb + r, colZa + boff) + Bb[r * bstride_col + u]);
+  float den = 0.f, num = 0.f;
+  for (int r = 0; r < m; ++r) {
+    float e = expf(proj(a, b, p0, ja + r, colZa) + Ba[r * bstride_col + u] - mx);
+    den += e;
+    num = fmaf(e, proj(a, b, p0, ja + r, colCa), num);
+  }
+  if (has_b)
+    for (int r = 0; r < m; ++r) {
+      float e = expf(proj(a, b, p0, jb + r, colZa + boff) + Bb[r * bstride_col + u] - mx);
+      den += e;
+      num = fmaf(e, proj(a, b, p0, jb + r, colCa + boff), num);
+    }
+  return num / den;
+}
+
+__device__ float block_sum_256(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// RMSNorm over c columns (each thread holds columns 2t, 2t+1), RoPE at pos on the last r
+// columns, then store the row in its format.  Threads with 2t >= c hold zeros.
+__device__ void finalize_store(const FoldArgs& a, float x0, float x1, int64_t pos, uint8_t* dst,
+                               float* red) {
+  const int t = threadIdx.x, u = 2 * t;
+  const bool act = u < a.c;
+  float ss = block_sum_256(act ? x0 * x0 + x1 * x1 : 0.f, red);
+  float inv = 1.0f / sqrtf(ss / (float)a.c + a.eps);
+  if (!act) return;
+  float g0 = a.gamma ? a.gamma[u] : 1.f, g1 = a.gamma ? a.gamma[u + 1] : 1.f;
+  float y0 = g0 * (x0 * inv), y1 = g1 * (x1 * inv);
+  const int rs = a.c - a.r;
+  if (u >= rs) {
+    float cs, sn;
+    rope_cos_sin(pos, (u - rs) >> 1, a.r, a.rope_base, cs, sn);
+    float z0 = y0 * cs - y1 * sn, z1 = y0 * sn + y1 * cs;
+    y0 = z0;
+    y1 = z1;
+  }
+  if (a.kv_fmt == CSA_FMT_F32) {
+    float2 v = make_float2(y0, y1);
+    *reinterpret_cast<float2*>(dst + 4 * u) = v;
+  } else if (u < rs) {
+    uint32_t code = f32_to_e4m3(y0) | (f32_to_e4m3(y1) << 8);
+    *reinterpret_cast<uint16_t*>(dst + u) = (uint16_t)code;
+  } else {
+    uint32_t bits = f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16);
+    *reinterpret_cast<uint32_t*>(dst + rs + 2 * (u - rs)) = bits;
+  }
+}
+
+// grid: x = T raw rows + (T/m + 1) entry slots, y = sequence.  256 threads, 2 columns each.
+__global__ __launch_bounds__(256) void k_fold(FoldArgs a) {
+  __shared__ float red[4];
+  const int b = blockIdx.y, slot = blockIdx.x, t = threadIdx.x;
+  const int p0 = a.pos0[b];
+  const int u = 2 * t;
+  if (slot < a.T) {
+    // raw window row of token j = p0 + slot: a-path row (HCA: C), finalized at position j.
+    const int j = p0 + slot;
+    if (slot == 0 && t == 0) a.n_entries[b] = min(a.cap, (p0 + a.T) / a.m);
+    if (slot < a.T - a.win_cap) return;  // an older token of this chunk the ring cannot keep
+    const int ws = j % a.win_cap;
+    float x0 = 0.f, x1 = 0.f;
+    if (u < a.c) {
+      x0 = proj(a, b, p0, j, u);
+      x1 = proj(a, b, p0, j, u + 1);
+    }
+    uint8_t* dst = a.win + ((size_t)b * a.win_cap + ws) * a.rowB;
+    finalize_store(a, x0, x1, j, dst, red);
+    if (t == 0) a.win_pos[(size_t)b * a.win_cap + ws] = j;
+    return;
+  }
+  const int i = p0 / a.m + (slot - a.T);
+  if (a.m * (i + 1) > p0 + a.T || i >= a.cap) return;  // block not complete in this chunk
+  // main KV entry: columns C^a at 0, C^b at c, Z^a at 2c, Z^b at 3c (HCA: C at 0, Z at c)
+  float x0 = 0.f, x1 = 0.f;
+  if (u < a.c) {
+    if (a.dual) {
+      x0 = fold_column(a, b, p0, i, u, 2 * a.c + u, a.c, a.bias, a.bias + a.m * a.c, a.c, u);
+      x1 = fold_column(a, b, p0, i, u + 1, 2 * a.c + u + 1, a.c, a.bias, a.bias + a.m * a.c, a.c, u + 1);
+    } else {
+      x0 = fold_column(a, b, p0, i, u, a.c + u, 0, a.bias, a.bias, a.c, u);
+      x1 = fold_column(a, b, p0, i, u + 1, a.c + u + 1, 0, a.bias, a.bias, a.c, u + 1);
+    }
+  }
+  uint8_t* dst = a.kv + ((size_t)b * a.cap + i) * a.rowB;
+  finalize_store(a, x0, x1, (int64_t)a.m * i, dst, red);
+  // indexer key: same fold with its own columns and biases; stored as folded
+  if (a.dual && u < a.cI) {
+    const int base = 4 * a.c;
+    const float* BIa = a.bias_idx;
+    const float* BIb = a.bias_idx + a.m * a.cI;
+    float k0 = fold_column(a, b, p0, i, base + u, base + 2 * a.cI + u, a.cI, BIa, BIb, a.cI, u);
+    float k1 = fold_column(a, b, p0, i, base + u + 1, base + 2 * a.cI + u + 1, a.cI, BIa, BIb, a.cI, u + 1);
+    if (a.idx_fmt == CSA_FMT_F32) {
+      float* kd = reinterpret_cast<float*>(a.ki) + ((size_t)b * a.cap + i) * a.cI;
+      kd[u] = k0;
+      kd[u + 1] = k1;
+    } else {
+      uint8_t* kd = a.ki + ((size_t)b * a.cap + i) * a.cI;
+      *reinterpret_cast<uint16_t*>(kd + u) = (uint16_t)(f32_to_e4m3(k0) | (f32_to_e4m3(k1) << 8));
+    }
+  }
+}
+
+// Keep the projections of the last S tokens of each sequence: slot j % S.
+__global__ __launch_bounds__(256) void k_state_update(const float* __restrict__ P, int ksplit,
+                                                      int T, int NP, int S,
+                                                      const int32_t* __restrict__ pos0,
+                                                      float* __restrict__ state) {
+  const int b = blockIdx.y;
+  const int first = max(0, T - S);
+  const int t = first + blockIdx.x;
+  if (t >= T) return;
+  const int j = pos0[b] + t;
+  const size_t row = (size_t)b * T + t;
+  const size_t MT = (size_t)gridDim.y * T;
+  float* dst = state + ((size_t)b * S + (j % S)) * NP;
+  for (int col = threadIdx.x; col < NP; col += blockDim.x) {
+    float v = 0.f;
+    for (int k = 0; k < ksplit; ++k) v += P[((size_t)k * MT + row) * NP + col];
+    dst[col] = v;
+  }
+}
+
+// Query metadata of a forward chunk: query b*T + t is sequence b at position pos0[b] + t.
+__global__ void k_query_meta(int B, int T, const int32_t* __restrict__ pos0,
+                             int32_t* __restrict__ q_seq, int32_t* __restrict__ q_pos) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * T) return;
+  const int b = i / T;
+  q_seq[i] = b;
+  q_pos[i] = pos0[b] + (i - b * T);
+}
+
+}  // namespace
+
+hipError_t launch_query_meta(int32_t B, int32_t T, const int32_t* pos0, int32_t* q_seq,
+                             int32_t* q_pos, hipStream_t s) {
+  const int n = B * T;
+  hipLaunchKernelGGL(k_query_meta, dim3((n + 255) / 256), dim3(256), 0, s, B, T, pos0, q_seq, q_pos);
+  return hipGetLastError();
+}
+
+int32_t state_width(const csa_dims& d) { return d.dual ? 4 * d.c + 4 * d.c_I : 2 * d.c; }
+int32_t state_rows(const csa_dims& d) { return d.dual ? 2 * d.m : d.m; }
+size_t row_bytes(const csa_dims& d) {
+  return d.kv_fmt == CSA_FMT_F32 ? (size_t)4 * d.c : (size_t)(d.c - d.rope_dim) + 2 * (size_t)d.rope_dim;
+}
+
+int32_t project_ksplit(const csa_dims& d, int32_t M) {
+  if (d.act_fmt != CSA_FMT_BF16) return 1;
+  // Small M (decode): split K so that enough workgroups stream the weights.
+  const int NP = state_width(d);
+  const int tiles = ((M + PJ_BM - 1) / PJ_BM) * ((NP + PJ_BN - 1) / PJ_BN);
+  int ks = 1;
+  while (tiles * ks < 512 && (d.d / (ks * 2)) >= 256 && (d.d % (ks * 2 * PJ_BK)) == 0) ks *= 2;
+  return ks;
+}
+
+hipError_t launch_project(const csa_dims& d, const csa_weights& w, const void* H, int32_t M,
+                          int32_t ksplit, float* P, hipStream_t s) {
+  const int NP = state_width(d);
+  const int nkv = d.dual ? 4 * d.c : 2 * d.c;
+  if (d.act_fmt == CSA_FMT_BF16) {
+    dim3 grid((NP + PJ_BN - 1) / PJ_BN, (M + PJ_BM - 1) / PJ_BM, ksplit);
+    hipLaunchKernelGGL(k_project_bf16, grid, dim3(256), 0, s, (const uint16_t*)H,
+                       (const uint16_t*)w.w_kv, (const uint16_t*)w.w_idx, nkv, M, NP, d.d,
+                       d.d / ksplit, P);
+  } else {
+    dim3 grid((NP + 15) / 16, (M + 15) / 16);
+    hipLaunchKernelGGL(k_project_f32, grid, dim3(256), 0, s, (const float*)H,
+                       (const float*)w.w_kv, (const float*)w.w_idx, nkv, M, NP, d.d, P);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fold(const csa_dims& d, const csa_weights& w, const csa_cache& c, int32_t T,
+                       const int32_t* pos0, const float* P, int32_t ksplit, hipStream_t s) {
+  FoldArgs a;
+  a.P = P;
+  a.ksplit = ksplit;
+  a.state = c.state;
+  a.S = state_rows(d);
+  a.NP = state_width(d);
+  a.T = T;
+  a.m = d.m;
+  a.dual = d.dual;
+  a.c = d.c;
+  a.r = d.rope_dim;
+  a.cI = d.dual ? d.c_I : 0;
+  a.pos0 = pos0;
+  a.bias = w.bias;
+  a.bias_idx = w.bias_idx;
+  a.gamma = w.gamma_kv;
+  a.eps = d.rms_eps;
+  a.rope_base = d.rope_base;
+  a.kv_fmt = d.kv_fmt;
+  a.idx_fmt = d.idx_fmt;
+  a.cap = c.cap;
+  a.win_cap = c.win_cap;
+  a.rowB = (int)row_bytes(d);
+  a.kv = (uint8_t*)c.kv;
+  a.ki = (uint8_t*)c.ki;
+  a.win = (uint8_t*)c.win;
+  a.win_pos = c.win_pos;
+  a.n_entries = c.n_entries;
+  dim3 grid(T + T / d.m + 1, c.B);
+  hipLaunchKernelGGL(k_fold, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_update(const csa_dims& d, const csa_cache& c, int32_t T,
+                               const int32_t* pos0, const float* P, int32_t ksplit,
+                               hipStream_t s) {
+  const int S = state_rows(d);
+  dim3 grid(min(T, S), c.B);
+  hipLaunchKernelGGL(k_state_update, grid, dim3(256), 0, s, P, ksplit, T, state_width(d), S,
+                     pos0, c.state);
+  return hipGetLastError();
+}
+
+}  // namespace csa

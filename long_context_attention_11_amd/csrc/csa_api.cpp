@@ -1,0 +1,374 @@
+// C ABI of the CSA library: argument checks, workspace planning and kernel dispatch.
+// Every check runs on the host before anything is enqueued; nothing here allocates device
+// memory or synchronises the stream.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "csa_internal.h"
+
+namespace csa {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+namespace {
+
+int fail(int code, const std::string& msg) {
+  set_error(msg);
+  return code;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Checks the dims on their own.  Returns CSA_OK or an error (message set).
+int check_dims(const csa_dims* d) {
+  if (!d) return fail(CSA_ERR_INVALID_ARGUMENT, "dims is NULL");
+  if (d->d < 1 || d->c < 2 || d->n_h < 1 || d->m < 1 || d->n_win < 1)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "d, c, n_h, m and n_win must be positive (c >= 2)");
+  if (d->rope_dim < 0 || d->rope_dim > d->c || (d->rope_dim & 1) || (d->c & 1))
+    return fail(CSA_ERR_INVALID_ARGUMENT, "rope_dim must be even and <= c, c even");
+  if (d->n_win < d->m && d->dual)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "n_win must be >= m so the window covers the open block");
+  if (d->dual != 0 && d->dual != 1) return fail(CSA_ERR_INVALID_ARGUMENT, "dual must be 0 or 1");
+  if (d->dual) {
+    if (d->c_I < 2 || (d->c_I & 1) || d->n_hI < 1)
+      return fail(CSA_ERR_INVALID_ARGUMENT, "CSA needs c_I >= 2 (even) and n_hI >= 1");
+    if (d->top_k < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "CSA needs top_k >= 1");
+  } else if (d->top_k != 0) {
+    return fail(CSA_ERR_INVALID_ARGUMENT, "HCA (dual = 0) is dense: top_k must be 0");
+  }
+  if (!(d->rope_base > 0.f) || !(d->rms_eps >= 0.f))
+    return fail(CSA_ERR_INVALID_ARGUMENT, "rope_base must be > 0 and rms_eps >= 0");
+  if (d->c > 512) return fail(CSA_ERR_UNSUPPORTED, "c > 512 is not built");
+  const bool f32 = d->act_fmt == CSA_FMT_F32 && d->kv_fmt == CSA_FMT_F32 &&
+                   (!d->dual || d->idx_fmt == CSA_FMT_F32);
+  const bool q = d->act_fmt == CSA_FMT_BF16 && d->kv_fmt == CSA_FMT_E4M3_BF16 &&
+                 (!d->dual || d->idx_fmt == CSA_FMT_E4M3);
+  if (!f32 && !q)
+    return fail(CSA_ERR_UNSUPPORTED,
+                "supported formats: all F32, or act BF16 + kv E4M3_BF16 + idx E4M3");
+  if (q) {
+    if (d->c != 512 || d->rope_dim != 64)
+      return fail(CSA_ERR_UNSUPPORTED, "E4M3_BF16 rows are built for c = 512, rope_dim = 64");
+    if (d->n_h % 16) return fail(CSA_ERR_UNSUPPORTED, "n_h must be a multiple of 16");
+    if (d->dual && (d->c_I != 128 || (d->n_hI != 16 && d->n_hI != 32 && d->n_hI != 64)))
+      return fail(CSA_ERR_UNSUPPORTED, "E4M3 indexer is built for c_I = 128, n_hI in {16, 32, 64}");
+    if (d->d % 64) return fail(CSA_ERR_UNSUPPORTED, "bf16 projection needs d % 64 == 0");
+  }
+  return CSA_OK;
+}
+
+int check_cache(const csa_dims* d, const csa_cache* c, bool need_state) {
+  if (!c) return fail(CSA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (c->B < 1 || c->cap < 1 || c->win_cap < 1)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "cache B, cap and win_cap must be positive");
+  if (c->win_cap < d->n_win) return fail(CSA_ERR_INVALID_ARGUMENT, "win_cap must be >= n_win");
+  if (!c->kv || !c->n_entries || !c->win || !c->win_pos)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "cache kv, n_entries, win and win_pos must be set");
+  if (d->dual && !c->ki) return fail(CSA_ERR_INVALID_ARGUMENT, "CSA cache needs ki");
+  if (need_state && !c->state) return fail(CSA_ERR_INVALID_ARGUMENT, "cache state is NULL");
+  const size_t rb = row_bytes(*d);
+  if ((size_t)c->cap * rb > (size_t)1 << 40)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "cache capacity overflows");
+  return CSA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(CSA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+struct Layout {
+  size_t off[8] = {0};
+  size_t total = 0;
+  size_t add(int i, size_t bytes) {
+    off[i] = total;
+    total = align_up(total + bytes, 256);
+    return off[i];
+  }
+};
+
+size_t compress_ws(const csa_dims& d, int32_t B, int32_t T) {
+  const int32_t M = B * T;
+  return (size_t)project_ksplit(d, M) * M * state_width(d) * sizeof(float);
+}
+
+// scores [q][cap] + top-k candidates for `Qc` queries
+size_t index_ws(const csa_dims& d, int32_t Qc, int32_t cap) {
+  return align_up((size_t)Qc * cap * sizeof(float), 256) + topk_workspace_bytes(d, Qc, cap);
+}
+
+}  // namespace
+}  // namespace csa
+
+using namespace csa;
+
+extern "C" {
+
+int csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+const char* csa_status_string(int status) {
+  switch (status) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case CSA_ERR_UNSUPPORTED: return "unsupported";
+    case CSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case CSA_ERR_HIP: return "hip error";
+    default: return "unknown status";
+  }
+}
+
+const char* csa_last_error(void) { return g_last_error.c_str(); }
+
+size_t csa_row_bytes(const csa_dims* dims) {
+  if (check_dims(dims) != CSA_OK) return 0;
+  return row_bytes(*dims);
+}
+
+int32_t csa_state_width(const csa_dims* dims) {
+  if (check_dims(dims) != CSA_OK) return 0;
+  return state_width(*dims);
+}
+
+int32_t csa_state_rows(const csa_dims* dims) {
+  if (check_dims(dims) != CSA_OK) return 0;
+  return state_rows(*dims);
+}
+
+int csa_workspace_size(const csa_dims* dims, int32_t op, int32_t B, int32_t T, int32_t Q,
+                       int32_t cap, int32_t q_chunk, size_t* bytes) {
+  g_last_error.clear();
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!bytes) return fail(CSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  const csa_dims& d = *dims;
+  switch (op) {
+    case CSA_OP_COMPRESS:
+      if (B < 1 || T < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "B and T must be positive");
+      *bytes = compress_ws(d, B, T);
+      return CSA_OK;
+    case CSA_OP_INDEX_TOPK:
+      if (!d.dual) return fail(CSA_ERR_INVALID_ARGUMENT, "HCA has no indexer");
+      if (Q < 1 || cap < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "Q and cap must be positive");
+      *bytes = index_ws(d, Q, cap);
+      return CSA_OK;
+    case CSA_OP_ATTEND:
+      if (Q < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "Q must be positive");
+      *bytes = attend_workspace_bytes(d, Q, std::max(cap, 1));
+      return CSA_OK;
+    case CSA_OP_FORWARD: {
+      if (B < 1 || T < 1 || cap < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "B, T, cap must be positive");
+      const int32_t Qn = B * T;
+      const int32_t Qc = (q_chunk > 0 && q_chunk < Qn) ? q_chunk : Qn;
+      Layout L;
+      L.add(0, 2 * sizeof(int32_t) * (size_t)Qn);                 // q_seq, q_pos
+      L.add(1, d.dual ? sizeof(int32_t) * (size_t)Qn * d.top_k : 0);  // idx
+      size_t phase = compress_ws(d, B, T);
+      if (d.dual) phase = std::max(phase, index_ws(d, Qc, cap));
+      phase = std::max(phase, attend_workspace_bytes(d, Qn, cap));
+      L.add(2, phase);
+      *bytes = L.total;
+      return CSA_OK;
+    }
+    default:
+      return fail(CSA_ERR_INVALID_ARGUMENT, "unknown op");
+  }
+}
+
+int csa_compress(const csa_dims* dims, const csa_weights* w, const csa_cache* cache,
+                 const void* H, int32_t T, const int32_t* pos0, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_dims(dims);
+  if (st) return st;
+  const csa_dims& d = *dims;
+  if ((st = check_cache(dims, cache, true))) return st;
+  if (!w || !w->w_kv || !w->bias || (d.dual && (!w->w_idx || !w->bias_idx)))
+    return fail(CSA_ERR_INVALID_ARGUMENT, "weights: w_kv and bias (and w_idx, bias_idx for CSA) are required");
+  if (!H || !pos0) return fail(CSA_ERR_INVALID_ARGUMENT, "H and pos0 must be set");
+  if (T < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "T must be >= 1");
+  const int32_t M = cache->B * T;
+  const size_t need = compress_ws(d, cache->B, T);
+  if (need && (!ws || ws_bytes < need))
+    return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "compress needs " + std::to_string(need) + " bytes of workspace");
+  const int32_t ks = project_ksplit(d, M);
+  float* P = (float*)ws;
+  hipError_t e = launch_project(d, *w, H, M, ks, P, stream);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  e = launch_fold(d, *w, *cache, T, pos0, P, ks, stream);
+  if (e != hipSuccess) return hip_fail(e, "fold launch");
+  e = launch_state_update(d, *cache, T, pos0, P, ks, stream);
+  if (e != hipSuccess) return hip_fail(e, "state launch");
+  return CSA_OK;
+}
+
+static int index_topk_impl(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
+                           const int32_t* q_seq, const int32_t* q_pos, int32_t Q, int32_t* idx_out,
+                           float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const size_t sc_bytes = scores_out ? 0 : align_up((size_t)Q * c.cap * sizeof(float), 256);
+  const size_t need = sc_bytes + topk_workspace_bytes(d, Q, c.cap);
+  if (need && (!ws || ws_bytes < need))
+    return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "index_topk needs " + std::to_string(need) + " bytes of workspace");
+  float* scores = scores_out ? scores_out : (float*)ws;
+  void* tws = (char*)ws + sc_bytes;
+  hipError_t e = launch_indexer(d, c, qI, w, q_seq, q_pos, Q, scores, c.cap, stream);
+  if (e != hipSuccess) return hip_fail(e, "indexer launch");
+  e = launch_topk(d, c, q_seq, q_pos, Q, scores, c.cap, idx_out, tws, stream);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  return CSA_OK;
+}
+
+int csa_index_topk(const csa_dims* dims, const csa_cache* cache, const void* qI, const void* w,
+                   const int32_t* q_seq, const int32_t* q_pos, int32_t Q, int32_t* idx_out,
+                   float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_dims(dims);
+  if (st) return st;
+  const csa_dims& d = *dims;
+  if (!d.dual) return fail(CSA_ERR_INVALID_ARGUMENT, "HCA (dual = 0) has no indexer");
+  if ((st = check_cache(dims, cache, false))) return st;
+  if (!qI || !w || !q_seq || !q_pos || !idx_out)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "qI, w, q_seq, q_pos and idx_out must be set");
+  if (Q < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "Q must be >= 1");
+  if (cache->cap > topk_max_visible(d))
+    return fail(CSA_ERR_UNSUPPORTED, "cap exceeds the entries the top-k kernels handle for this top_k (" +
+                                         std::to_string(topk_max_visible(d)) + ")");
+  return index_topk_impl(d, *cache, qI, w, q_seq, q_pos, Q, idx_out, scores_out, ws, ws_bytes,
+                         stream);
+}
+
+int csa_index_scores(const csa_dims* dims, const csa_cache* cache, const void* qI, const void* w,
+                     const int32_t* q_seq, const int32_t* q_pos, int32_t Q, float* scores,
+                     int64_t ld, hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!dims->dual) return fail(CSA_ERR_INVALID_ARGUMENT, "HCA (dual = 0) has no indexer");
+  if ((st = check_cache(dims, cache, false))) return st;
+  if (!qI || !w || !q_seq || !q_pos || !scores)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "qI, w, q_seq, q_pos and scores must be set");
+  if (Q < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "Q must be >= 1");
+  if (ld < cache->cap) return fail(CSA_ERR_INVALID_ARGUMENT, "ld must be >= cap");
+  hipError_t e = launch_indexer(*dims, *cache, qI, w, q_seq, q_pos, Q, scores, ld, stream);
+  if (e != hipSuccess) return hip_fail(e, "indexer launch");
+  return CSA_OK;
+}
+
+size_t csa_topk_workspace_size(const csa_dims* dims, int32_t Q, int32_t cap) {
+  if (check_dims(dims) != CSA_OK || Q < 1 || cap < 1) return 0;
+  return topk_workspace_bytes(*dims, Q, cap);
+}
+
+int csa_topk(const csa_dims* dims, const csa_cache* cache, const int32_t* q_seq,
+             const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld, int32_t* idx_out,
+             void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!dims->dual) return fail(CSA_ERR_INVALID_ARGUMENT, "HCA (dual = 0) has no top-k");
+  if ((st = check_cache(dims, cache, false))) return st;
+  if (!q_seq || !q_pos || !scores || !idx_out)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "q_seq, q_pos, scores and idx_out must be set");
+  if (Q < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "Q must be >= 1");
+  if (ld < cache->cap || (ld & 3)) return fail(CSA_ERR_INVALID_ARGUMENT, "ld must be >= cap and a multiple of 4");
+  if (cache->cap > topk_max_visible(*dims))
+    return fail(CSA_ERR_UNSUPPORTED, "cap exceeds the entries the top-k kernels handle for this top_k");
+  const size_t need = topk_workspace_bytes(*dims, Q, cache->cap);
+  if (need && (!ws || ws_bytes < need))
+    return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "top-k needs " + std::to_string(need) + " bytes of workspace");
+  hipError_t e = launch_topk(*dims, *cache, q_seq, q_pos, Q, scores, ld, idx_out, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  return CSA_OK;
+}
+
+static int attend_checks(const csa_dims& d, const csa_cache& c, bool sparse) {
+  if (d.kv_fmt == CSA_FMT_F32) {
+    const long rows = (long)(sparse ? d.top_k : c.cap) + d.n_win;
+    if (rows > 4096) return fail(CSA_ERR_UNSUPPORTED, "fp32 attention handles at most 4096 keys per query");
+    if (d.c > 1024) return fail(CSA_ERR_UNSUPPORTED, "fp32 attention handles c <= 1024");
+  }
+  return CSA_OK;
+}
+
+int csa_attend(const csa_dims* dims, const csa_cache* cache, const void* q, const float* gamma_q,
+               const float* sink, const int32_t* q_seq, const int32_t* q_pos, int32_t Q,
+               const int32_t* idx, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_dims(dims);
+  if (st) return st;
+  const csa_dims& d = *dims;
+  if ((st = check_cache(dims, cache, false))) return st;
+  if (!q || !q_seq || !q_pos || !out) return fail(CSA_ERR_INVALID_ARGUMENT, "q, q_seq, q_pos and out must be set");
+  if (Q < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "Q must be >= 1");
+  if ((st = attend_checks(d, *cache, idx != nullptr))) return st;
+  const size_t need = attend_workspace_bytes(d, Q, cache->cap);
+  if (need && (!ws || ws_bytes < need))
+    return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "attend needs " + std::to_string(need) + " bytes of workspace");
+  hipError_t e = launch_attend(d, *cache, q, gamma_q, sink, q_seq, q_pos, Q, idx, out, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "attend launch");
+  return CSA_OK;
+}
+
+int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cache, const void* H,
+                int32_t T, const int32_t* pos0, const void* q, const void* qI, const void* wI,
+                const float* gamma_q, const float* sink, void* out, int32_t* idx_out, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_dims(dims);
+  if (st) return st;
+  const csa_dims& d = *dims;
+  if ((st = check_cache(dims, cache, true))) return st;
+  if (!w || !w->w_kv || !w->bias || (d.dual && (!w->w_idx || !w->bias_idx)))
+    return fail(CSA_ERR_INVALID_ARGUMENT, "weights: w_kv and bias (and w_idx, bias_idx for CSA) are required");
+  if (!H || !pos0 || !q || !out) return fail(CSA_ERR_INVALID_ARGUMENT, "H, pos0, q and out must be set");
+  if (d.dual && (!qI || !wI)) return fail(CSA_ERR_INVALID_ARGUMENT, "CSA forward needs qI and wI");
+  if (T < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "T must be >= 1");
+  if (cache->win_cap < T + d.n_win - 1)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "win_cap must be >= T + n_win - 1 for the chunk's queries");
+  if (d.dual && cache->cap > topk_max_visible(d))
+    return fail(CSA_ERR_UNSUPPORTED, "cap exceeds the entries the top-k kernels handle for this top_k");
+  if ((st = attend_checks(d, *cache, d.dual != 0))) return st;
+  const int32_t Qn = cache->B * T;
+  // fixed part of the workspace, then the largest query chunk the rest allows
+  Layout L;
+  L.add(0, 2 * sizeof(int32_t) * (size_t)Qn);
+  L.add(1, (d.dual && !idx_out) ? sizeof(int32_t) * (size_t)Qn * d.top_k : 0);
+  const size_t fixed = L.total;
+  size_t min_phase = std::max(compress_ws(d, cache->B, T), attend_workspace_bytes(d, Qn, cache->cap));
+  if (d.dual) min_phase = std::max(min_phase, index_ws(d, 1, cache->cap));
+  if (!ws || ws_bytes < fixed + min_phase)
+    return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "forward needs at least " + std::to_string(fixed + min_phase) + " bytes of workspace");
+  int32_t* q_seq = (int32_t*)((char*)ws + L.off[0]);
+  int32_t* q_pos = q_seq + Qn;
+  int32_t* idx = idx_out ? idx_out : (int32_t*)((char*)ws + L.off[1]);
+  void* phase_ws = (char*)ws + fixed;
+  const size_t phase_bytes = ws_bytes - fixed;
+
+  st = csa_compress(dims, w, cache, H, T, pos0, phase_ws, phase_bytes, stream);
+  if (st) return st;
+  hipError_t e = launch_query_meta(cache->B, T, pos0, q_seq, q_pos, stream);
+  if (e != hipSuccess) return hip_fail(e, "query metadata launch");
+  if (d.dual) {
+    // largest chunk whose scores and candidates fit
+    int32_t Qc = Qn;
+    while (Qc > 1 && index_ws(d, Qc, cache->cap) > phase_bytes) Qc = (Qc + 1) / 2;
+    const size_t qI_row = (size_t)d.n_hI * d.c_I * (d.idx_fmt == CSA_FMT_F32 ? 4 : 1);
+    const size_t w_row = (size_t)d.n_hI * (d.act_fmt == CSA_FMT_F32 ? 4 : 2);
+    for (int32_t q0 = 0; q0 < Qn; q0 += Qc) {
+      const int32_t n = std::min(Qc, Qn - q0);
+      st = index_topk_impl(d, *cache, (const char*)qI + q0 * qI_row, (const char*)wI + q0 * w_row,
+                           q_seq + q0, q_pos + q0, n, idx + (size_t)q0 * d.top_k, nullptr, phase_ws,
+                           phase_bytes, stream);
+      if (st) return st;
+    }
+  }
+  e = launch_attend(d, *cache, q, gamma_q, sink, q_seq, q_pos, Qn, d.dual ? idx : nullptr, out,
+                    phase_ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "attend launch");
+  return CSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// Internal declarations of the CSA library: device helpers shared by the kernels and the
+// host-side launch functions the C ABI calls.  Built for gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string>
+
+#include "../../include/csa.h"
+
+namespace csa {
+
+// ----------------------------------------------------------------------------- formats
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (read once; not kept in the caches).
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// float32 -> bfloat16 bits, round to nearest even; NaN -> quiet NaN with the input's sign.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// float32 -> OCP E4M3 (e4m3fn) code: nearest, ties to even, saturating at +-448; NaN -> 0x7f.
+// Written from the format's definition: 4 exponent bits (bias 7), 3 mantissa bits,
+// subnormals in units of 2^-9, no infinities.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = fabsf(f);
+  if (!(a == a)) return 0x7fu;
+  if (a >= 448.0f) return sign | 0x7eu;
+  if (a < 0.015625f) {                         // below 2^-6: subnormal grid of 2^-9
+    float q = __builtin_rintf(a * 512.0f);     // exact scaling, round half to even
+    return sign | (uint32_t)q;                 // q == 8 is the smallest normal, code 0x08
+  }
+  uint32_t ua = __float_as_uint(a);
+  int ef = (int)(ua >> 23) - 127 + 7;          // biased E4M3 exponent, 1..15
+  uint32_t mant = ua & 0x7fffffu;
+  uint32_t keep = mant >> 20, rest = mant & 0xfffffu;
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ++keep;
+  if (keep == 8u) { keep = 0u; ++ef; }
+  uint32_t code = ((uint32_t)ef << 3) | keep;
+  if (code > 0x7eu) code = 0x7eu;
+  return sign | code;
+}
+
+// Four E4M3 codes (one dword) -> four bfloat16 (two dwords).  Exact: every E4M3 value is a
+// bfloat16 value.  Uses the gfx950 scaled conversion with scale 1.
+__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t src, uint32_t& lo, uint32_t& hi) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)src, 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)src, 1.0f, true);
+  lo = __builtin_bit_cast(uint32_t, a);
+  hi = __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  uint32_t lo, hi;
+  e4m3x4_to_bf16x4(code & 0xffu, lo, hi);
+  return bf16_bits_to_f32(lo & 0xffffu);
+}
+
+// Order-preserving map of a float score to uint32 (larger score -> larger key); -0 -> +0.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ----------------------------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Map a hardware workgroup id to a logical one so that logical ids [k*n/8, (k+1)*n/8) run on
+// XCD k (workgroups are dealt to the 8 XCDs round-robin).  Neighbouring logical tiles then
+// share an L2.  Identity when n is not a multiple of 8.
+__device__ __forceinline__ uint32_t xcd_logical_id(uint32_t hw, uint32_t n) {
+  if (n % 8u) return hw;
+  return (hw % 8u) * (n / 8u) + hw / 8u;
+}
+
+// RoPE angle in float64: a float32 product pos * theta is ~0.06 rad off at pos ~ 1e6.
+__device__ __forceinline__ void rope_cos_sin(int64_t pos, int pair, int rope_dim, double base,
+                                             float& c, float& s) {
+  double theta = pow(base, -2.0 * (double)pair / (double)rope_dim);
+  double ang = (double)pos * theta;
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+// ----------------------------------------------------------------------------- host side
+
+struct Status {
+  int code = CSA_OK;
+  std::string msg;
+};
+
+void set_error(const std::string& msg);
+
+// Kernel launchers (defined in the .hip files).  Each returns a hipError_t of its launch.
+hipError_t launch_project(const csa_dims& d, const csa_weights& w, const void* H, int32_t M,
+                          int32_t ksplit, float* P, hipStream_t s);
+hipError_t launch_fold(const csa_dims& d, const csa_weights& w, const csa_cache& c,
+                       int32_t T, const int32_t* pos0, const float* P, int32_t ksplit,
+                       hipStream_t s);
+hipError_t launch_state_update(const csa_dims& d, const csa_cache& c, int32_t T,
+                               const int32_t* pos0, const float* P, int32_t ksplit,
+                               hipStream_t s);
+hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
+                          const int32_t* q_seq, const int32_t* q_pos, int32_t Q, float* scores,
+                          int64_t ld_scores, hipStream_t s);
+hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
+                       const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld_scores,
+                       int32_t* idx, void* ws, hipStream_t s);
+hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
+                         const float* gamma_q, const float* sink, const int32_t* q_seq,
+                         const int32_t* q_pos, int32_t Q, const int32_t* idx, void* out,
+                         void* ws, hipStream_t s);
+hipError_t launch_query_meta(int32_t B, int32_t T, const int32_t* pos0, int32_t* q_seq,
+                             int32_t* q_pos, hipStream_t s);
+
+// Planning helpers shared by the API and the launchers (pure host arithmetic).
+int32_t project_ksplit(const csa_dims& d, int32_t M);
+size_t topk_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap);
+int32_t topk_max_visible(const csa_dims& d);
+size_t attend_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap);
+int32_t state_width(const csa_dims& d);
+int32_t state_rows(const csa_dims& d);
+size_t row_bytes(const csa_dims& d);
+
+}  // namespace csa

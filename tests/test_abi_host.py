@@ -1,0 +1,118 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports every symbol
+include/csa.h declares, and rejects bad arguments on the host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_attention_11_amd as L
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "csa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    if not os.path.exists(L.lib_path()):
+        pytest.skip("libcsa.so not built")
+    lib = L.load()
+    declared = _declared_symbols()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(lib, name), f"libcsa.so does not export {name}"
+    assert set(L.EXPORTED_SYMBOLS) == set(declared)
+    assert L.csa_abi_version() == 1
+
+
+def _lib():
+    if not os.path.exists(L.lib_path()):
+        pytest.skip("libcsa.so not built")
+    return L.load()
+
+
+def test_sizes_follow_the_storage_layout():
+    _lib()
+    d2 = L.Dims.from_config(synth.config("c2"))
+    assert L.csa_row_bytes(d2) == 576  # 448 E4M3 + 64 bf16
+    assert L.csa_state_rows(d2) == 8 and L.csa_state_width(d2) == 4 * 512 + 4 * 128
+    d1 = L.Dims.from_config(synth.config("c1"))
+    assert L.csa_row_bytes(d1) == 4 * 64
+    d5 = L.Dims.from_config(synth.config("c5"))
+    assert L.csa_state_rows(d5) == 128 and L.csa_state_width(d5) == 2 * 512
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_invalid_dims_are_rejected_on_the_host():
+    lib = _lib()
+    bad = [
+        dict(c=63),                      # odd c
+        dict(rope_dim=70),               # rope_dim > c
+        dict(top_k=0),                   # CSA needs top_k
+        dict(n_win=2),                   # n_win < m
+        dict(dual=False),                # HCA with top_k > 0
+    ]
+    for over in bad:
+        d = L.Dims.from_config(synth.config("c1"), **over)
+        out = ctypes.c_size_t(0)
+        st = lib.csa_workspace_size(ctypes.byref(d.struct()), L.OP_COMPRESS, 1, 1, 1, 1, 0,
+                                    ctypes.byref(out))
+        assert st == 1, over
+        assert lib.csa_last_error().decode()
+    # an unbuilt combination: quantized rows need c = 512
+    d = L.Dims.from_config(synth.config("c2"), c=256)
+    out = ctypes.c_size_t(0)
+    assert lib.csa_workspace_size(ctypes.byref(d.struct()), L.OP_COMPRESS, 1, 1, 1, 1, 0,
+                                  ctypes.byref(out)) == 2
+
+
+def test_null_and_workspace_errors_without_a_device():
+    """Argument errors return before any HIP call, so they can be forced on a CPU host."""
+    lib = _lib()
+    d = L.Dims.from_config(synth.config("c2"))
+    ds = d.struct()
+    # NULL cache
+    st = lib.csa_compress(ctypes.byref(ds), None, None, None, 1, None, None, 0, None)
+    assert st == 1
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: checks fail before any launch
+    cache = L._Cache(2, 64, 128, fake, fake, fake, fake, fake, fake)
+    w = L._Weights(fake, fake, fake, fake, None)
+    # T = 0
+    assert lib.csa_compress(ctypes.byref(ds), ctypes.byref(w), ctypes.byref(cache), fake, 0, fake,
+                            fake, 1 << 30, None) == 1
+    # workspace too small
+    assert lib.csa_compress(ctypes.byref(ds), ctypes.byref(w), ctypes.byref(cache), fake, 4, fake,
+                            fake, 16, None) == 3
+    # win_cap < n_win
+    small = L._Cache(2, 64, 64, fake, fake, fake, fake, fake, fake)
+    assert lib.csa_attend(ctypes.byref(ds), ctypes.byref(small), fake, None, None, fake, fake, 1,
+                          fake, fake, fake, 1 << 30, None) == 1
+    # HCA has no indexer
+    d5 = L.Dims.from_config(synth.config("c5")).struct()
+    assert lib.csa_index_topk(ctypes.byref(d5), ctypes.byref(cache), fake, fake, fake, fake, 1, fake,
+                              None, fake, 1 << 30, None) == 1
+    # cap beyond what the selection kernels handle for this top_k
+    huge = L._Cache(1, 1 << 24, 128, fake, fake, fake, fake, fake, fake)
+    assert lib.csa_index_topk(ctypes.byref(ds), ctypes.byref(huge), fake, fake, fake, fake, 1, fake,
+                              None, fake, 1 << 40, None) == 2
+    # forward needs a ring that holds the chunk's window
+    assert lib.csa_forward(ctypes.byref(ds), ctypes.byref(w), ctypes.byref(cache), fake, 64, fake,
+                           fake, fake, fake, None, None, fake, None, fake, 1 << 30, None) == 1
+    assert lib.csa_status_string(3) == b"workspace too small"
+
+
+def test_workspace_sizes_are_consistent():
+    _lib()
+    d = L.Dims.from_config(synth.config("c2"))
+    full = L.csa_workspace_size(d, L.OP_FORWARD, B=1, T=32768, cap=270336)
+    chunked = L.csa_workspace_size(d, L.OP_FORWARD, B=1, T=32768, cap=270336, q_chunk=2048)
+    assert chunked < full
+    assert L.csa_workspace_size(d, L.OP_INDEX_TOPK, Q=16, cap=32768) >= 16 * 32768 * 4
