@@ -41,7 +41,7 @@ struct AttendArgs {
   int cap, win_cap, m, n_win;
   float scale_log2;           // softmax scale * log2(e)
   float eps;
-  double rope_base;
+  double log2_base;
   int splits, tiles_per_split;
   uint16_t* out;              // [Q][n_h][512] bf16 (splits == 1)
   float* part_o;              // [Q][n_h][splits][512] (splits > 1)
@@ -68,6 +68,68 @@ __device__ __forceinline__ int64_t row_offset(const AttendArgs& a, int q, int se
 __device__ __forceinline__ int vt_index(int d, int r) {
   const int chunk = (r >> 3) ^ ((d >> 3) & 7);
   return d * AV_LD + chunk * 8 + (r & 7);
+}
+
+// Sum of squares of 8 bf16 values packed in a uint4.
+__device__ __forceinline__ float sumsq_bf16x8(const uint4& v) {
+  float s = 0.f;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float lo = bf16_bits_to_f32(w[e] & 0xffffu), hi = bf16_bits_to_f32(w[e] >> 16);
+    s = fmaf(lo, lo, s);
+    s = fmaf(hi, hi, s);
+  }
+  return s;
+}
+
+// Normalise 8 query dims (dim0 .. dim0+7), rotate them to tau when they are RoPE dims, and
+// pack them as a bf16 MFMA operand.
+__device__ __forceinline__ bf16x8 prep_q8(const uint4& v, float inv, const float* gamma,
+                                          int dim0, bool rope, int64_t tau, double log2_base) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int dim = dim0 + 2 * e;
+    float y0 = bf16_bits_to_f32(w[e] & 0xffffu) * inv;
+    float y1 = bf16_bits_to_f32(w[e] >> 16) * inv;
+    if (gamma) {
+      y0 *= gamma[dim];
+      y1 *= gamma[dim + 1];
+    }
+    if (rope) {
+      float cs, sn;
+      rope_cos_sin(tau, (dim - ANOPE) >> 1, AR, log2_base, cs, sn);
+      const float z0 = y0 * cs - y1 * sn, z1 = y0 * sn + y1 * cs;
+      y0 = z0;
+      y1 = z1;
+    }
+    o[e] = f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16);
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// Scale 4 output dims (d0 .. d0+3) of one head by 1/L, rotate RoPE dims back by -tau, and
+// store them as bf16.
+__device__ __forceinline__ void store_out4(const f32x4& o, float invL, uint16_t* orow, int d0,
+                                           bool rope, int64_t tau, double log2_base) {
+  float y[4] = {o[0] * invL, o[1] * invL, o[2] * invL, o[3] * invL};
+  if (rope) {
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      float cs, sn;
+      rope_cos_sin(tau, (d0 + e - ANOPE) >> 1, AR, log2_base, cs, sn);
+      const float z0 = y[e] * cs + y[e + 1] * sn;  // rotate by -tau
+      const float z1 = -y[e] * sn + y[e + 1] * cs;
+      y[e] = z0;
+      y[e + 1] = z1;
+    }
+  }
+  uint2 pk;
+  pk.x = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
+  pk.y = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
+  *reinterpret_cast<uint2*>(orow + d0) = pk;
 }
 
 __global__ __launch_bounds__(256) void k_attend_mfma(AttendArgs a) {
@@ -100,49 +162,21 @@ __global__ __launch_bounds__(256) void k_attend_mfma(AttendArgs a) {
   bf16x8 Qop[16];
   {
     const uint16_t* qrow = a.q + ((size_t)q * a.n_h + hh) * AC;
-    float x[16][8];
+    uint4 raw[16];
     float ss = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
-      uint4 v = *reinterpret_cast<const uint4*>(qrow + ks * 32 + g * 8);
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[ks][2 * e] = bf16_bits_to_f32(wv[e] & 0xffffu);
-        x[ks][2 * e + 1] = bf16_bits_to_f32(wv[e] >> 16);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf(x[ks][e], x[ks][e], ss);
+      raw[ks] = *reinterpret_cast<const uint4*>(qrow + ks * 32 + g * 8);
+      ss += sumsq_bf16x8(raw[ks]);
     }
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
     const float inv = 1.0f / sqrtf(ss / (float)AC + a.eps);
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dim = ks * 32 + g * 8 + e;
-        x[ks][e] = (a.gamma_q ? a.gamma_q[dim] : 1.f) * (x[ks][e] * inv);
-      }
-      if (ks >= ANOPE / 32) {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int dim = ks * 32 + g * 8 + e;
-          float cs, sn;
-          rope_cos_sin(tau, (dim - ANOPE) >> 1, AR, a.rope_base, cs, sn);
-          const float y0 = x[ks][e] * cs - x[ks][e + 1] * sn;
-          const float y1 = x[ks][e] * sn + x[ks][e + 1] * cs;
-          x[ks][e] = y0;
-          x[ks][e + 1] = y1;
-        }
-      }
-      uint4 pk;
-      pk.x = f32_to_bf16_bits(x[ks][0]) | (f32_to_bf16_bits(x[ks][1]) << 16);
-      pk.y = f32_to_bf16_bits(x[ks][2]) | (f32_to_bf16_bits(x[ks][3]) << 16);
-      pk.z = f32_to_bf16_bits(x[ks][4]) | (f32_to_bf16_bits(x[ks][5]) << 16);
-      pk.w = f32_to_bf16_bits(x[ks][6]) | (f32_to_bf16_bits(x[ks][7]) << 16);
-      Qop[ks] = __builtin_bit_cast(bf16x8, pk);
-    }
+    for (int ks = 0; ks < ANOPE / 32; ++ks)
+      Qop[ks] = prep_q8(raw[ks], inv, a.gamma_q, ks * 32 + g * 8, false, tau, a.log2_base);
+    Qop[14] = prep_q8(raw[14], inv, a.gamma_q, 14 * 32 + g * 8, true, tau, a.log2_base);
+    Qop[15] = prep_q8(raw[15], inv, a.gamma_q, 15 * 32 + g * 8, true, tau, a.log2_base);
   }
 
   const float sink2 = (a.sink && head_ok) ? a.sink[hh] * LOG2E : NEG_BIG;
@@ -161,12 +195,14 @@ __global__ __launch_bounds__(256) void k_attend_mfma(AttendArgs a) {
       rowoff[tid] = r < r_hi ? row_offset(a, q, seq, V, nsel, w0, r) : (int64_t)-1;
     }
     __syncthreads();
-    // ---- gather 64 rows x 512 dims into Ks (row-major) and Vt (dim-major), as bf16
-    {
-      uint32_t colv[16][4];  // 16 rows x 8 bf16 of this dim-group
+    // ---- gather 64 rows x 512 dims into Ks (row-major) and Vt (dim-major), as bf16.
+    // Thread: dim-group dg (8 dims) of rows rsub*16 .. +15, in batches of 4 rows.
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int row = rsub * 16 + rr;
+    for (int rb = 0; rb < 4; ++rb) {
+      uint32_t colv[4][4];  // 4 rows x 8 bf16
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = rsub * 16 + rb * 4 + rr;
         const int64_t off = rowoff[row];
         uint4 v = make_uint4(0, 0, 0, 0);
         if (off >= 0) {
@@ -186,20 +222,14 @@ __global__ __launch_bounds__(256) void k_attend_mfma(AttendArgs a) {
         colv[rr][2] = v.z;
         colv[rr][3] = v.w;
       }
-      // transpose: for each of the 8 dims, 16 consecutive rows -> two 16-byte chunks
+      // transpose: each of the 8 dims gets 4 consecutive rows (8 bytes)
+      const int r0 = rsub * 16 + rb * 4;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int d = dg * 8 + e;
-        uint32_t pk[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          const uint32_t lo = (colv[2 * p][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-          const uint32_t hi = (colv[2 * p + 1][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-          pk[p] = lo | (hi << 16);
-        }
-        const int r0 = rsub * 16;
-        *reinterpret_cast<uint4*>(&Vt[vt_index(d, r0)]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        *reinterpret_cast<uint4*>(&Vt[vt_index(d, r0 + 8)]) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        const int sh = (e & 1) * 16;
+        const uint32_t r01 = ((colv[0][e >> 1] >> sh) & 0xffffu) | (((colv[1][e >> 1] >> sh) & 0xffffu) << 16);
+        const uint32_t r23 = ((colv[2][e >> 1] >> sh) & 0xffffu) | (((colv[3][e >> 1] >> sh) & 0xffffu) << 16);
+        *reinterpret_cast<uint2*>(&Vt[vt_index(dg * 8 + e, r0)]) = make_uint2(r01, r23);
       }
     }
     __syncthreads();
@@ -275,25 +305,9 @@ __global__ __launch_bounds__(256) void k_attend_mfma(AttendArgs a) {
     const float invL = Lsum > 0.f ? 1.0f / Lsum : 0.f;
     uint16_t* orow = a.out + ((size_t)q * a.n_h + h) * AC;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      float y[4] = {O[dt][0] * invL, O[dt][1] * invL, O[dt][2] * invL, O[dt][3] * invL};
-      const int d0 = dt * 16 + 4 * g;
-      if (d0 >= ANOPE) {
+    for (int dt = 0; dt < ANOPE / 16; ++dt) store_out4(O[dt], invL, orow, dt * 16 + 4 * g, false, tau, a.log2_base);
 #pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          float cs, sn;
-          rope_cos_sin(tau, (d0 + e - ANOPE) >> 1, AR, a.rope_base, cs, sn);
-          const float z0 = y[e] * cs + y[e + 1] * sn;   // rotate by -tau
-          const float z1 = -y[e] * sn + y[e + 1] * cs;
-          y[e] = z0;
-          y[e + 1] = z1;
-        }
-      }
-      uint2 pk;
-      pk.x = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
-      pk.y = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
-      *reinterpret_cast<uint2*>(orow + d0) = pk;
-    }
+    for (int dt = ANOPE / 16; dt < 32; ++dt) store_out4(O[dt], invL, orow, dt * 16 + 4 * g, true, tau, a.log2_base);
   } else {
     const size_t pidx = ((size_t)q * a.n_h + h) * a.splits + split;
     float* po = a.part_o + pidx * AC;
@@ -331,7 +345,7 @@ __global__ __launch_bounds__(256) void k_attend_combine(AttendArgs a) {
   y1 *= invL;
   if (d >= ANOPE) {
     float cs, sn;
-    rope_cos_sin(tau, (d - ANOPE) >> 1, AR, a.rope_base, cs, sn);
+    rope_cos_sin(tau, (d - ANOPE) >> 1, AR, a.log2_base, cs, sn);
     const float z0 = y0 * cs + y1 * sn, z1 = -y0 * sn + y1 * cs;
     y0 = z0;
     y1 = z1;
@@ -355,7 +369,7 @@ __global__ __launch_bounds__(64) void k_attend_f32(const float* __restrict__ qv,
                                                    const int32_t* __restrict__ win_pos,
                                                    const int32_t* __restrict__ n_entries,
                                                    int cap, int win_cap, int m, int n_win, int c,
-                                                   int r, float scale, float eps, double rope_base,
+                                                   int r, float scale, float eps, double log2_base,
                                                    float* __restrict__ out) {
   __shared__ float qs[1024];
   __shared__ float z[AF_MAXK];
@@ -379,7 +393,7 @@ __global__ __launch_bounds__(64) void k_attend_f32(const float* __restrict__ qv,
     float y1 = (gamma_q ? gamma_q[u + 1] : 1.f) * (qs[u + 1] * inv);
     if (u >= c - r) {
       float cs, sn;
-      rope_cos_sin(tau, (u - (c - r)) >> 1, r, rope_base, cs, sn);
+      rope_cos_sin(tau, (u - (c - r)) >> 1, r, log2_base, cs, sn);
       const float z0 = y0 * cs - y1 * sn, z1 = y0 * sn + y1 * cs;
       y0 = z0;
       y1 = z1;
@@ -430,7 +444,7 @@ __global__ __launch_bounds__(64) void k_attend_f32(const float* __restrict__ qv,
     }
     if (u >= c - r) {
       float cs, sn;
-      rope_cos_sin(tau, (u - (c - r)) >> 1, r, rope_base, cs, sn);
+      rope_cos_sin(tau, (u - (c - r)) >> 1, r, log2_base, cs, sn);
       const float z0 = y0 * cs + y1 * sn, z1 = -y0 * sn + y1 * cs;
       y0 = z0;
       y1 = z1;
@@ -475,7 +489,7 @@ hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
     hipLaunchKernelGGL(k_attend_f32, dim3(Q * d.n_h), dim3(64), 0, s, (const float*)q, gamma_q,
                        sink, q_seq, q_pos, d.n_h, idx, d.top_k, (const float*)c.kv,
                        (const float*)c.win, c.win_pos, c.n_entries, c.cap, c.win_cap, d.m,
-                       d.n_win, d.c, d.rope_dim, scale, d.rms_eps, (double)d.rope_base,
+                       d.n_win, d.c, d.rope_dim, scale, d.rms_eps, std::log2((double)d.rope_base),
                        (float*)out);
     return hipGetLastError();
   }
@@ -499,7 +513,7 @@ hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
   a.n_win = d.n_win;
   a.scale_log2 = scale * LOG2E;
   a.eps = d.rms_eps;
-  a.rope_base = d.rope_base;
+  a.log2_base = std::log2((double)d.rope_base);
   SplitPlan p = plan_splits(d, Q, c.cap, idx == nullptr);
   a.splits = p.splits;
   a.tiles_per_split = p.tiles_per_split;

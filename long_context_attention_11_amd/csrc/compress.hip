@@ -137,8 +137,7 @@ __global__ __launch_bounds__(256) void k_project_f32(const float* __restrict__ H
 // ============================================================================ fold / finalize
 
 struct FoldArgs {
-  const float* P;        // [ksplit][B*T][NP]
-  int ksplit;
+  const float* P;        // [B*T][NP] summed projections
   const float* state;    // [B][S][NP]
   int S, NP;
   int T, m, dual, c, r, cI;
@@ -147,7 +146,7 @@ struct FoldArgs {
   const float* bias_idx; // CSA [2][m][cI]
   const float* gamma;    // [c] or null
   float eps;
-  double rope_base;
+  double log2_base;
   int kv_fmt, idx_fmt;
   int cap, win_cap, rowB;
   uint8_t* kv;
@@ -159,12 +158,7 @@ struct FoldArgs {
 
 // Projection value of token j (global position) in column col of sequence b.
 __device__ __forceinline__ float proj(const FoldArgs& a, int b, int p0, int j, int col) {
-  if (j >= p0) {
-    size_t row = (size_t)b * a.T + (j - p0);
-    float v = 0.f;
-    for (int k = 0; k < a.ksplit; ++k) v += a.P[((size_t)k * gridDim.y * a.T + row) * a.NP + col];
-    return v;
-  }
+  if (j >= p0) return a.P[((size_t)b * a.T + (j - p0)) * a.NP + col];
   return a.state[((size_t)b * a.S + (j % a.S)) * a.NP + col];
 }
 
@@ -221,7 +215,7 @@ __device__ void finalize_store(const FoldArgs& a, float x0, float x1, int64_t po
   const int rs = a.c - a.r;
   if (u >= rs) {
     float cs, sn;
-    rope_cos_sin(pos, (u - rs) >> 1, a.r, a.rope_base, cs, sn);
+    rope_cos_sin(pos, (u - rs) >> 1, a.r, a.log2_base, cs, sn);
     float z0 = y0 * cs - y1 * sn, z1 = y0 * sn + y1 * cs;
     y0 = z0;
     y1 = z1;
@@ -294,23 +288,32 @@ __global__ __launch_bounds__(256) void k_fold(FoldArgs a) {
 }
 
 // Keep the projections of the last S tokens of each sequence: slot j % S.
-__global__ __launch_bounds__(256) void k_state_update(const float* __restrict__ P, int ksplit,
-                                                      int T, int NP, int S,
-                                                      const int32_t* __restrict__ pos0,
+// grid: x = column blocks of 256, y = the last min(T, S) tokens, z = sequence.
+__global__ __launch_bounds__(256) void k_state_update(const float* __restrict__ P, int T, int NP,
+                                                      int S, const int32_t* __restrict__ pos0,
                                                       float* __restrict__ state) {
-  const int b = blockIdx.y;
-  const int first = max(0, T - S);
-  const int t = first + blockIdx.x;
-  if (t >= T) return;
+  const int b = blockIdx.z;
+  const int t = max(0, T - S) + blockIdx.y;
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T || col >= NP) return;
   const int j = pos0[b] + t;
-  const size_t row = (size_t)b * T + t;
-  const size_t MT = (size_t)gridDim.y * T;
-  float* dst = state + ((size_t)b * S + (j % S)) * NP;
-  for (int col = threadIdx.x; col < NP; col += blockDim.x) {
-    float v = 0.f;
-    for (int k = 0; k < ksplit; ++k) v += P[((size_t)k * MT + row) * NP + col];
-    dst[col] = v;
+  state[((size_t)b * S + (j % S)) * NP + col] = P[((size_t)b * T + t) * NP + col];
+}
+
+// Sum split-K partials: out[i] = sum_k P[k][i], in a fixed order (deterministic).
+__global__ __launch_bounds__(256) void k_reduce_partials(const float* __restrict__ P, int ksplit,
+                                                         int64_t n, float* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  float4 acc = *reinterpret_cast<const float4*>(P + i);
+  for (int k = 1; k < ksplit; ++k) {
+    const float4 v = *reinterpret_cast<const float4*>(P + (size_t)k * n + i);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
   }
+  *reinterpret_cast<float4*>(out + i) = acc;
 }
 
 // Query metadata of a forward chunk: query b*T + t is sequence b at position pos0[b] + t.
@@ -367,9 +370,9 @@ hipError_t launch_project(const csa_dims& d, const csa_weights& w, const void* H
 
 hipError_t launch_fold(const csa_dims& d, const csa_weights& w, const csa_cache& c, int32_t T,
                        const int32_t* pos0, const float* P, int32_t ksplit, hipStream_t s) {
+  if (ksplit != 1) return hipErrorInvalidValue;  // partials are summed first
   FoldArgs a;
   a.P = P;
-  a.ksplit = ksplit;
   a.state = c.state;
   a.S = state_rows(d);
   a.NP = state_width(d);
@@ -384,7 +387,7 @@ hipError_t launch_fold(const csa_dims& d, const csa_weights& w, const csa_cache&
   a.bias_idx = w.bias_idx;
   a.gamma = w.gamma_kv;
   a.eps = d.rms_eps;
-  a.rope_base = d.rope_base;
+  a.log2_base = std::log2((double)d.rope_base);
   a.kv_fmt = d.kv_fmt;
   a.idx_fmt = d.idx_fmt;
   a.cap = c.cap;
@@ -403,10 +406,19 @@ hipError_t launch_fold(const csa_dims& d, const csa_weights& w, const csa_cache&
 hipError_t launch_state_update(const csa_dims& d, const csa_cache& c, int32_t T,
                                const int32_t* pos0, const float* P, int32_t ksplit,
                                hipStream_t s) {
-  const int S = state_rows(d);
-  dim3 grid(min(T, S), c.B);
-  hipLaunchKernelGGL(k_state_update, grid, dim3(256), 0, s, P, ksplit, T, state_width(d), S,
-                     pos0, c.state);
+  if (ksplit != 1) return hipErrorInvalidValue;  // partials are summed first
+  const int S = state_rows(d), NP = state_width(d);
+  dim3 grid((NP + 255) / 256, min(T, S), c.B);
+  hipLaunchKernelGGL(k_state_update, grid, dim3(256), 0, s, P, T, NP, S, pos0, c.state);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_partials(const float* P, int32_t ksplit, int64_t n, float* out,
+                                  hipStream_t s) {
+  // n is a multiple of 4 (NP is a multiple of 4 for every supported layout)
+  const int64_t threads = (n + 3) / 4;
+  hipLaunchKernelGGL(k_reduce_partials, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     P, ksplit, n, out);
   return hipGetLastError();
 }
 

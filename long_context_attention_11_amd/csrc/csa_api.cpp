@@ -91,9 +91,11 @@ struct Layout {
   }
 };
 
+// split-K partials [ks][M][P] and, when ks > 1, their sum [M][P]
 size_t compress_ws(const csa_dims& d, int32_t B, int32_t T) {
   const int32_t M = B * T;
-  return (size_t)project_ksplit(d, M) * M * state_width(d) * sizeof(float);
+  const int32_t ks = project_ksplit(d, M);
+  return (size_t)(ks + (ks > 1 ? 1 : 0)) * M * state_width(d) * sizeof(float);
 }
 
 // scores [q][cap] + top-k candidates for `Qc` queries
@@ -198,9 +200,16 @@ int csa_compress(const csa_dims* dims, const csa_weights* w, const csa_cache* ca
   float* P = (float*)ws;
   hipError_t e = launch_project(d, *w, H, M, ks, P, stream);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
-  e = launch_fold(d, *w, *cache, T, pos0, P, ks, stream);
+  if (ks > 1) {
+    const int64_t n = (int64_t)M * state_width(d);
+    float* Psum = P + (size_t)ks * n;
+    e = launch_reduce_partials(P, ks, n, Psum, stream);
+    if (e != hipSuccess) return hip_fail(e, "split-K reduce launch");
+    P = Psum;
+  }
+  e = launch_fold(d, *w, *cache, T, pos0, P, 1, stream);
   if (e != hipSuccess) return hip_fail(e, "fold launch");
-  e = launch_state_update(d, *cache, T, pos0, P, ks, stream);
+  e = launch_state_update(d, *cache, T, pos0, P, 1, stream);
   if (e != hipSuccess) return hip_fail(e, "state launch");
   return CSA_OK;
 }

@@ -99,15 +99,18 @@ __device__ __forceinline__ uint32_t xcd_logical_id(uint32_t hw, uint32_t n) {
   return (hw % 8u) * (n / 8u) + hw / 8u;
 }
 
-// RoPE angle in float64: a float32 product pos * theta is ~0.06 rad off at pos ~ 1e6.
-__device__ __forceinline__ void rope_cos_sin(int64_t pos, int pair, int rope_dim, double base,
-                                             float& c, float& s) {
-  double theta = pow(base, -2.0 * (double)pair / (double)rope_dim);
-  double ang = (double)pos * theta;
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
+// RoPE cos/sin of the angle pos * theta_j, theta_j = base^(-2j/rope_dim).  The product is
+// formed in float64 (a float32 product is ~0.06 rad off at pos ~ 1e6), reduced to [-pi, pi]
+// with a two-constant Cody-Waite step in float64, and only the reduced angle goes through
+// float32 sincos.  log2_base = log2(base), computed on the host.
+__device__ __forceinline__ void rope_cos_sin(int64_t pos, int pair, int rope_dim,
+                                             double log2_base, float& c, float& s) {
+  const double theta = exp2(-2.0 * (double)pair / (double)rope_dim * log2_base);
+  const double ang = (double)pos * theta;
+  const double k = rint(ang * 0.15915494309189535);            // 1 / (2 pi)
+  double red = fma(-k, 6.283185307179586, ang);                 // 2 pi, high part
+  red = fma(-k, 2.4492935982947064e-16, red);                   // 2 pi - high part
+  sincosf((float)red, &s, &c);
 }
 
 // ----------------------------------------------------------------------------- host side
@@ -138,6 +141,8 @@ hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
                          const float* gamma_q, const float* sink, const int32_t* q_seq,
                          const int32_t* q_pos, int32_t Q, const int32_t* idx, void* out,
                          void* ws, hipStream_t s);
+hipError_t launch_reduce_partials(const float* P, int32_t ksplit, int64_t n, float* out,
+                                  hipStream_t s);
 hipError_t launch_query_meta(int32_t B, int32_t T, const int32_t* pos0, int32_t* q_seq,
                              int32_t* q_pos, hipStream_t s);
 

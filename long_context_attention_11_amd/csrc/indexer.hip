@@ -79,36 +79,44 @@ __global__ __launch_bounds__(256) void k_indexer_bf16(
     }
   }
   const uint8_t* kbase = ki + (size_t)seq * cap * IX_CI + g * 32;
-  // software pipeline: raw bytes of the next tile are in flight while this one computes
-  uint4 nlo, nhi;
-  auto load_tile = [&](int s0) {
+  // Register ring of DEPTH tiles: the raw bytes of the next DEPTH tiles are in flight while
+  // one computes (each tile: 16 entries x 128 B per wave, 32 B per lane).
+  constexpr int DEPTH = 4;
+  uint4 rlo[DEPTH], rhi[DEPTH];
+  auto load_tile = [&](int s0, uint4& lo, uint4& hi) {
     const int s = min(s0 + col, w_hi - 1);
     const uint8_t* src = kbase + (size_t)s * IX_CI;
-    nlo = load_stream16(src);
-    nhi = load_stream16(src + 16);
+    lo = load_stream16(src);
+    hi = load_stream16(src + 16);
   };
-  load_tile(w_lo);
-  for (int s0 = w_lo; s0 < w_hi; s0 += 16) {
-    const uint4 clo = nlo, chi = nhi;
-    if (s0 + 16 < w_hi) load_tile(s0 + 16);
-    bf16x8 B[4];
-    e4m3x32_to_ops(clo, chi, B);
 #pragma unroll
-    for (int qq = 0; qq < QPW; ++qq) {
-      float part = 0.f;
+  for (int i = 0; i < DEPTH; ++i) load_tile(w_lo + 16 * i, rlo[i], rhi[i]);
+  for (int base = w_lo; base < w_hi; base += 16 * DEPTH) {
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        f32x4 acc = {0, 0, 0, 0};
+    for (int i = 0; i < DEPTH; ++i) {
+      const int s0 = base + 16 * i;
+      if (s0 >= w_hi) break;
+      const uint4 clo = rlo[i], chi = rhi[i];
+      if (s0 + 16 * DEPTH < w_hi) load_tile(s0 + 16 * DEPTH, rlo[i], rhi[i]);
+      bf16x8 B[4];
+      e4m3x32_to_ops(clo, chi, B);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[qq][ht][ks], B[ks], acc, 0, 0, 0);
+      for (int qq = 0; qq < QPW; ++qq) {
+        float part = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) part = fmaf(W[qq][ht][e], fmaxf(acc[e], 0.f), part);
+        for (int ht = 0; ht < HT; ++ht) {
+          f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[qq][ht][ks], B[ks], acc, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part = fmaf(W[qq][ht][e], fmaxf(acc[e], 0.f), part);
+        }
+        part += __shfl_xor(part, 16, 64);
+        part += __shfl_xor(part, 32, 64);
+        const int s = s0 + col;
+        if (g == 0 && s < V[qq] && s < w_hi) scores[(size_t)(q0 + qq) * ld + s] = part;
       }
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 32, 64);
-      const int s = s0 + col;
-      if (g == 0 && s < V[qq] && s < w_hi) scores[(size_t)(q0 + qq) * ld + s] = part;
     }
   }
 }
@@ -149,7 +157,7 @@ hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI,
     return hipGetLastError();
   }
   // E4M3 keys: bf16 MFMA.  One query per group; entry chunks sized to fill the GPU.
-  const int chunk = 1024;
+  const int chunk = 512;
   dim3 grid(Q, (c.cap + chunk - 1) / chunk);
   switch (d.n_hI) {
     case 64:

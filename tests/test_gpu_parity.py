@@ -356,3 +356,125 @@ def test_deterministic_repeat():
         outs.append((idx.cpu().clone(), out.view(torch.int16).cpu().clone()))
     assert torch.equal(outs[0][0], outs[1][0])
     assert torch.equal(outs[0][1], outs[1][1])
+
+
+# ----------------------------------------------------------------------------- full sizes
+
+
+def _decode_full(name, B=None, check_scores_for=2):
+    """A decode step of a full-size configuration on a synthetic cache: every query's
+    selection (under the tie rule) and output are checked against the oracle."""
+    cfg = synth.config(name)
+    B = B or cfg["B"]
+    N = cfg["prefix"] // cfg["m"]
+    tau = cfg["prefix"]
+    taus = [(b, tau) for b in range(B)]
+    dims, cache, qs, W, q_seq, q_pos = _synthetic_decode_setup(cfg, B, N, cfg["n_win"], taus, seed=31)
+    stats = _run_index_attend_and_check(cfg, dims, cache, qs, W, q_seq, q_pos, taus,
+                                        check_scores=True)
+    return stats
+
+
+def test_c2_decode_full_size():
+    """Flash decode, 16 sequences x 32768 entries, k=512: the bench's kernels and grid."""
+    _decode_full("c2")
+
+
+def test_c3_decode_full_size():
+    """Pro decode, 4 sequences x 262144 entries (1M tokens), 128 heads, k=1024 (segmented
+    top-k with a merge stage)."""
+    _decode_full("c3")
+
+
+def test_c5_hca_decode_full_size():
+    """HCA decode, 8 sequences x 8192 entries (1M tokens, m'=128), dense attention."""
+    _decode_full("c5")
+
+
+def test_c4_prefill_full_size_sampled():
+    """Flash chunked prefill at full size: a 32768-token chunk after a 1048576-token prefix
+    (262144 entries).  The prefix cache, its window ring and the projection state of the
+    block before the chunk (zeros) are inputs given to both sides; csa_forward compresses the
+    chunk (8192 new entries), scores every query against up to 270335 entries, selects 512 and
+    attends.  Sampled queries across the chunk are checked against the oracle, which folds
+    the chunk's entries from the same hidden states."""
+    cfg = synth.config("c4a")
+    dims = L.Dims.from_config(cfg)
+    od = oracle_dims(cfg)
+    m, k, T, p0 = cfg["m"], cfg["top_k"], cfg["T"], cfg["prefix"]
+    N0 = p0 // m
+    cap = (p0 + T) // m
+    R_win = T + cfg["n_win"]
+    taus0 = [(0, p0 - 1)]
+    dims, cache, _, _, _, _ = _synthetic_decode_setup(cfg, 1, cap, R_win, taus0, seed=41,
+                                                      n_entries=[N0])
+    cache.state.zero_()
+    W = synth.weights(cfg, seed=41, device=DEV)
+    H = synth.hidden(cfg, 0, p0, p0 + T, seed=41, device=DEV)
+    qs = synth.queries(cfg, T, seed=41, device=DEV, tag="prefill")
+    out = torch.zeros((T, cfg["n_h"], cfg["c"]), dtype=torch.bfloat16, device=DEV)
+    idx = torch.zeros((T, k), dtype=torch.int32, device=DEV)
+    # inputs both sides see: prefix entries, keys and ring rows (before the chunk overwrites)
+    prefix_entries = decode_rows(cache.kv[0, :N0].cpu().numpy(), cfg)
+    prefix_ki = decode_keys(cache.ki[0, :N0], cfg)
+    ring = decode_rows(cache.win[0].cpu().numpy(), cfg)
+    ring_pos = cache.win_pos[0].cpu().numpy()
+    ws = _ws(L.csa_workspace_size(dims, L.OP_FORWARD, B=1, T=T, cap=cap, q_chunk=4096))
+    L.csa_forward(dims, lib_weights(W, True), cache, H.unsqueeze(0).contiguous(), T,
+                  _i32([p0]), qs["q"], qs["qI"], qs["w"], W["gamma_q"], W["sink"], out, idx, ws)
+    torch.cuda.synchronize()
+    assert int(cache.n_entries[0]) == cap
+
+    # oracle: the chunk's projections, entries (first block's b rows = the given zero state)
+    OW = oracle_weights(W)
+    Hn = host64(H)
+    P = {p: R.project(Hn, OW[p]) for p in ("kv_a", "kv_b", "z_a", "z_b", "ki_a", "ki_b", "zi_a", "zi_b")}
+    zc = np.zeros((m, cfg["c"]))
+    zi = np.zeros((m, cfg["c_I"]))
+    pre = R.csa_fold(P["kv_a"], P["kv_b"], P["z_a"], P["z_b"], OW["B_a"], OW["B_b"], m, prev_b=(zc, zc))
+    kpre = R.csa_fold(P["ki_a"], P["ki_b"], P["zi_a"], P["zi_b"], OW["BI_a"], OW["BI_b"], m, prev_b=(zi, zi))
+    fin = R.finalize_kv(pre, m * (N0 + np.arange(T // m)), OW["gamma_kv"], od)
+    ent_new, _ = R.store_kv(fin, od)
+    ki_new, _ = R.store_index_keys(kpre, od)
+    raw_fin = R.finalize_kv(P["kv_a"], p0 + np.arange(T), OW["gamma_kv"], od)
+    raw_new, _ = R.store_kv(raw_fin, od)
+    # the GPU's new entries/keys/rows against the oracle's (storage rounding rule)
+    g_new = decode_rows(cache.kv[0, N0:cap].cpu().numpy(), cfg)
+    c, r = cfg["c"], cfg["rope_dim"]
+    check_stored_codes(g_new[:, :c - r], fin[:, :c - r], "e4m3", "c4 new entries/nope")
+    check_stored_codes(g_new[:, c - r:], fin[:, c - r:], "bf16", "c4 new entries/rope")
+    g_ki_new = decode_keys(cache.ki[0, N0:cap], cfg)
+    check_stored_codes(g_ki_new, kpre, "e4m3", "c4 new keys")
+    entries = np.concatenate([prefix_entries, ent_new])
+    ki = np.concatenate([prefix_ki, ki_new])
+    g_entries = np.concatenate([prefix_entries, g_new])
+    g_ki = np.concatenate([prefix_ki, g_ki_new])
+
+    def raw_of(pos):
+        pos = np.asarray(pos)
+        old = pos < p0
+        rows = np.empty((len(pos), cfg["c"]))
+        slots = pos[old] % R_win
+        assert np.all(ring_pos[slots] == pos[old])
+        rows[old] = ring[slots]
+        rows[~old] = raw_new[pos[~old] - p0]
+        return rows
+
+    q, qI, w = host64(qs["q"]), qI_host(qs["qI"], cfg), host64(qs["w"])
+    sink = host64(W["sink"])
+    gi, go = idx.cpu().numpy(), host64(out)
+    sample = [0, 1, 2, 3, 4, 5, 127, 128, 1000, 4097, 16383, 20000, 32766, 32767]
+    for t in sample:
+        tau = p0 + t
+        o_ref, sel, sc = R.query_step(tau, q[t], qI[t], w[t], None, sink, entries, ki, raw_of, cap, od)
+        try:
+            same = check_topk(gi[t], sc, k, f"c4 t={t}")
+        except AssertionError:
+            V = R.visible_entries(tau, m, cap)
+            check_topk(gi[t], R.index_scores(qI[t], w[t], g_ki[:V]), k, f"c4 t={t} (GPU keys)")
+            same = False
+        if not same:
+            sel_g = gi[t][gi[t] >= 0]
+            keys = np.concatenate([g_entries[sel_g], raw_of(R.window_positions(tau, cfg["n_win"]))])
+            o_ref = R.attend(q[t], tau, keys, None, sink, od)
+        assert_close_q(go[t], o_ref, f"c4 out t={t}")
