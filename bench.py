@@ -1,21 +1,26 @@
-"""Benchmark of the compressed sparse attention decode step on one MI355X.
+"""Benchmark of the compressed sparse attention path on one MI355X.
 
-Workload (Flash-shaped CSA decode): 16 sequences, each with a 131072-token context already
-compressed into 32768 entries (m = 4); d = 4096, 64 query heads of 512 (RoPE on the last 64),
-indexer 64 heads x 128, top-k = 512, window 128, sink per head; KV rows E4M3 + bf16 RoPE dims,
-indexer keys E4M3.  The cache is built untimed by compressing synthetic hidden states N(0,1)
-with weights N(0, 1/4096).
+Default workload (the reported line): Flash-shaped CSA decode, config c2 -- 16 sequences,
+each with a 131072-token context already compressed into 32768 entries (m = 4); d = 4096,
+64 query heads of 512 (RoPE on the last 64), indexer 64 heads x 128, top-k 512, window 128,
+sink per head; KV rows E4M3 + bf16 RoPE dims, indexer keys E4M3.  The cache is built untimed
+by compressing synthetic hidden states N(0,1) with weights N(0, 1/4096).
 
-One step = the whole path for one new token per sequence (position 131072): compress the
-token (projection GEMM, window row, projection state), indexer scores over the 32768 visible
-entries, top-k, and attention over the 512 selected entries + 128 window rows.  The step is
-captured as three HIP graphs (compress | indexer | top-k + attend) and replayed; HIP events
-between them time the indexer kernel inside the timed region.  Three copies of the cache
-rotate between steps so every step reads its cache from HBM (one copy exceeds what the 256 MB
-Infinity Cache could keep warm across three steps).
+One decode step = the whole path for one new token per sequence: compress the token
+(projection GEMM, window row, projection state; an entry when a block completes), indexer
+scores over the visible entries, top-k, attention over the selected entries + window rows.
+Each step is one captured HIP graph; several copies of the cache rotate between steps so every
+step reads its cache from HBM rather than from the 256 MB Infinity Cache.
 
-Prints one JSON line: queries/s (16 per step), the indexer's achieved HBM bandwidth against
-8 TB/s, and the CPU oracle timed on a bounded sample of the same step.
+Other workloads (--config): c3 (Pro decode, 4 x 1M tokens), c5 (HCA decode, 8 x 1M tokens),
+c4a / c4b (32768-token prefill chunk after a 1M- / 262144-token prefix; one step = one
+csa_forward of the chunk), c1 (tiny fp32 prefill).
+
+Per-kernel durations: each kernel of the step is also launched 20 times back to back inside
+one graph (same inputs, same grid), timed with HIP events around the replay; the dominant
+kernel's average gives the roofline line.
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -28,36 +33,49 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK = 8.0e12  # bytes/s, MI355X HBM3E
+HBM_PEAK = 8.0e12        # bytes/s, MI355X HBM3E
+BF16_PEAK = 2.5e15       # dense bf16 MFMA FLOP/s
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4a", "c4b", "c5"])
+    ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--eager", action="store_true", help="launch eagerly instead of graphs")
     return ap.parse_args()
 
 
-def build_cache(L, synth, cfg, dims, W, lw, dev, chunk=8192):
+def lib_weights(L, W, dual):
     import torch
-    B, Lc = cfg["B"], cfg["prefix"]
-    cache = L.Cache(dims, B=B, cap=Lc // cfg["m"], win_cap=cfg["n_win"], device=dev)
-    ws = torch.empty(L.csa_workspace_size(dims, L.OP_COMPRESS, B=B, T=chunk), dtype=torch.uint8, device=dev)
-    for t0 in range(0, Lc, chunk):
-        H = torch.stack([synth.hidden(cfg, b, t0, t0 + chunk, device=dev) for b in range(B)])
-        pos0 = torch.full((B,), t0, dtype=torch.int32, device=dev)
-        L.csa_compress(dims, lw, cache, H, chunk, pos0, ws)
+    if dual:
+        return L.Weights(torch.stack([W["kv_a"], W["kv_b"], W["z_a"], W["z_b"]]).contiguous(),
+                         torch.stack([W["B_a"], W["B_b"]]).contiguous(),
+                         torch.stack([W["ki_a"], W["ki_b"], W["zi_a"], W["zi_b"]]).contiguous(),
+                         torch.stack([W["BI_a"], W["BI_b"]]).contiguous(), W["gamma_kv"])
+    return L.Weights(torch.stack([W["kv"], W["z"]]).contiguous(), W["B"].contiguous(), None, None,
+                     W["gamma_kv"])
+
+
+def build_cache(L, synth, cfg, dims, lw, dev, B, n_tokens, cap, win_cap, chunk=8192):
+    """Compress n_tokens synthetic tokens of each sequence into a fresh cache (untimed)."""
+    import torch
+    cache = L.Cache(dims, B=B, cap=cap, win_cap=win_cap, device=dev)
+    chunk = min(chunk, n_tokens)
+    ws = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_COMPRESS, B=B, T=chunk)), dtype=torch.uint8, device=dev)
+    for t0 in range(0, n_tokens, chunk):
+        T = min(chunk, n_tokens - t0)
+        H = torch.stack([synth.hidden(cfg, b, t0, t0 + T, device=dev) for b in range(B)])
+        L.csa_compress(dims, lw, cache, H, T, torch.full((B,), t0, dtype=torch.int32, device=dev), ws)
         del H
     torch.cuda.synchronize()
     return cache
 
 
-def clone_cache(L, c):
+def clone_cache(c):
     import copy
     d = copy.copy(c)
     for k in ("kv", "ki", "n_entries", "win", "win_pos", "state"):
@@ -66,12 +84,47 @@ def clone_cache(L, c):
     return d
 
 
-def cpu_baseline(cfg, seconds):
-    """The oracle on a bounded sample of the same step: for sampled queries, the compress of
-    the new token (all projections + its window row), indexer scores over 32768 entries,
-    top-k and attention.  Inputs are synthetic with the workload's shapes."""
-    import numpy as np
+def capture(fn):
+    """Capture fn() (HIP launches on the current stream) into a graph; return its replay."""
     import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def kernel_time_us(fns, reps=20, rounds=5):
+    """Average duration of one launch: `reps` launches (cycling through fns) captured back to
+    back in one graph, HIP events around each replay; the median round is kept."""
+    import torch
+    g = capture(lambda: [fns[i % len(fns)]() for i in range(reps)])
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / reps)
+    times.sort()
+    return times[len(times) // 2]
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+
+def cpu_baseline(cfg, seconds):
+    """The oracle, untuned, on a bounded sample of the same decode step: single queries
+    (compress of the new token: every projection and its window row; indexer over all visible
+    entries; top-k; attention), synthetic inputs of the workload's shapes."""
+    import numpy as np
 
     import synth
     from oracle import codecs
@@ -83,8 +136,8 @@ def cpu_baseline(cfg, seconds):
     except Exception:
         threads = os.cpu_count() or 1
     od = R.Dims(d=cfg["d"], c=cfg["c"], rope_dim=cfg["rope_dim"], n_h=cfg["n_h"], c_I=cfg["c_I"],
-                n_hI=cfg["n_hI"], m=cfg["m"], dual=True, top_k=cfg["top_k"], n_win=cfg["n_win"],
-                kv_fmt="q", idx_fmt="e4m3")
+                n_hI=cfg["n_hI"], m=cfg["m"], dual=cfg["dual"], top_k=cfg["top_k"],
+                n_win=cfg["n_win"], kv_fmt="q", idx_fmt="e4m3")
     N = cfg["prefix"] // cfg["m"]
     tau = cfg["prefix"]
     W = synth.weights(cfg, device="cpu")
@@ -93,19 +146,20 @@ def cpu_baseline(cfg, seconds):
     sink = W["sink"].numpy().astype(np.float64)
     sc = synth.synthetic_cache(cfg, 1, N, cfg["n_win"], device="cpu")
     c, r = cfg["c"], cfg["rope_dim"]
-    kvb = sc["kv"][0].numpy()
-    entries = np.concatenate([codecs.e4m3_decode(kvb[:, :c - r]),
-                              codecs.bf16_decode(kvb[:, c - r:].copy().view("<u2"))], axis=1)
-    ki = codecs.e4m3_decode(sc["ki"][0].numpy())
-    winb = sc["win"][0].numpy()
-    win = np.concatenate([codecs.e4m3_decode(winb[:, :c - r]),
-                          codecs.bf16_decode(winb[:, c - r:].copy().view("<u2"))], axis=1)
+
+    def dec(b):
+        return np.concatenate([codecs.e4m3_decode(b[:, :c - r]),
+                               codecs.bf16_decode(b[:, c - r:].copy().view("<u2"))], axis=1)
+    entries = dec(sc["kv"][0].numpy())
+    win = dec(sc["win"][0].numpy())
+    ki = codecs.e4m3_decode(sc["ki"][0].numpy()) if cfg["dual"] else None
     qs = synth.queries(cfg, 8, device="cpu")
     q = qs["q"].float().numpy().astype(np.float64)
-    qI = codecs.e4m3_decode(qs["qI"].numpy())
-    w = qs["w"].float().numpy().astype(np.float64)
+    qI = codecs.e4m3_decode(qs["qI"].numpy()) if cfg["dual"] else [None] * 8
+    w = qs["w"].float().numpy().astype(np.float64) if cfg["dual"] else [None] * 8
     h = synth.hidden(cfg, 0, tau, tau + 1, device="cpu").float().numpy().astype(np.float64)
-    paths = ("kv_a", "kv_b", "z_a", "z_b", "ki_a", "ki_b", "zi_a", "zi_b")
+    paths = (("kv_a", "kv_b", "z_a", "z_b", "ki_a", "ki_b", "zi_a", "zi_b") if cfg["dual"]
+             else ("kv", "z"))
     n = 0
     t0 = time.perf_counter()
     while True:
@@ -122,10 +176,253 @@ def cpu_baseline(cfg, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": n / el, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+    what = (f"indexer over {N} entries, top-{cfg['top_k']}, attention over {cfg['top_k']}+{cfg['n_win']} rows"
+            if cfg["dual"] else f"dense attention over {N}+{cfg['n_win']} rows")
+    return {"value": round(n / el, 2), "unit": "queries/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} single-query decode steps of the same workload (compress of the new "
-                      f"token, indexer over {N} entries, top-{cfg['top_k']}, attention over "
-                      f"{cfg['top_k']}+{cfg['n_win']} rows), synthetic cache, {el:.1f} s"}
+                      f"token, {what}), synthetic inputs of the same shapes, {el:.1f} s"}
+
+
+def cpu_baseline_prefill(cfg, seconds):
+    """The oracle on a bounded sample of the prefill chunk: the chunk's compression for the
+    first 64 tokens plus single-query steps, scaled to tokens/s of the whole chunk's work."""
+    import numpy as np
+
+    import synth
+    from oracle import codecs
+    from oracle import csa_ref as R
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    od = R.Dims(d=cfg["d"], c=cfg["c"], rope_dim=cfg["rope_dim"], n_h=cfg["n_h"], c_I=cfg["c_I"],
+                n_hI=cfg["n_hI"], m=cfg["m"], dual=True, top_k=cfg["top_k"], n_win=cfg["n_win"],
+                kv_fmt=cfg["kv_fmt"], idx_fmt=cfg["idx_fmt"])
+    p0 = cfg["prefix"]
+    N = p0 // cfg["m"]
+    W = synth.weights(cfg, device="cpu")
+    OW = {k: (None if v is None else v.float().numpy().astype(np.float64)) for k, v in W.items()
+          if k not in ("gamma_q", "sink")}
+    sink = W["sink"].numpy().astype(np.float64)
+    sc = synth.synthetic_cache(cfg, 1, N, cfg["n_win"], device="cpu")
+    c, r = cfg["c"], cfg["rope_dim"]
+    if cfg["kv_fmt"] == "f32":
+        entries = sc["kv"][0].numpy().view(np.float32).astype(np.float64)
+        win = sc["win"][0].numpy().view(np.float32).astype(np.float64)
+        ki = sc["ki"][0].numpy().astype(np.float64)
+    else:
+        entries = np.concatenate([codecs.e4m3_decode(sc["kv"][0].numpy()[:, :c - r]),
+                                  codecs.bf16_decode(sc["kv"][0].numpy()[:, c - r:].copy().view("<u2"))], 1)
+        win = np.concatenate([codecs.e4m3_decode(sc["win"][0].numpy()[:, :c - r]),
+                              codecs.bf16_decode(sc["win"][0].numpy()[:, c - r:].copy().view("<u2"))], 1)
+        ki = codecs.e4m3_decode(sc["ki"][0].numpy())
+    qs = synth.queries(cfg, 8, device="cpu")
+    q = qs["q"].float().numpy().astype(np.float64)
+    qI = qs["qI"].float().numpy().astype(np.float64) if cfg["idx_fmt"] == "f32" else codecs.e4m3_decode(qs["qI"].numpy())
+    w = qs["w"].float().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    H = synth.hidden(cfg, 0, p0, p0 + 64, device="cpu").float().numpy().astype(np.float64)
+    R.compress_sequence(H, OW, od)
+    t_comp = (time.perf_counter() - t0) / 64
+    n = 0
+    t1 = time.perf_counter()
+    while True:
+        i = n % 8
+        R.query_step(p0 + i, q[i], qI[i], w[i], None, sink, entries, ki,
+                     lambda pos: win[np.asarray(pos) % cfg["n_win"]], N, od)
+        n += 1
+        if time.perf_counter() - t1 >= seconds:
+            break
+    t_q = (time.perf_counter() - t1) / n
+    return {"value": round(1.0 / (t_comp + t_q), 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"compression of 64 chunk tokens plus {n} single-query steps against the "
+                      f"{N}-entry prefix (synthetic inputs of the workload's shapes); per-token cost "
+                      f"= compress share + one query"}
+
+
+# ----------------------------------------------------------------------------- GPU runs
+
+
+def run_decode(args, cfg):
+    import torch
+
+    import long_context_attention_11_amd as L
+    import synth
+
+    dev = "cuda:0"
+    B, tau, k = cfg["B"], cfg["prefix"], cfg["top_k"]
+    dual = cfg["dual"]
+    dims = L.Dims.from_config(cfg)
+    W = synth.weights(cfg, device=dev)
+    lw = lib_weights(L, W, dual)
+    N = tau // cfg["m"]
+    t_build = time.perf_counter()
+    base = build_cache(L, synth, cfg, dims, lw, dev, B, tau, N, cfg["n_win"])
+    t_build = time.perf_counter() - t_build
+    copies = args.copies or 3
+    caches = [base] + [clone_cache(base) for _ in range(copies - 1)]
+
+    H1 = torch.stack([synth.hidden(cfg, b, tau, tau + 1, device=dev) for b in range(B)])
+    qs = synth.queries(cfg, B, device=dev, tag="decode")
+    pos0 = torch.full((B,), tau, dtype=torch.int32, device=dev)
+    q_seq = torch.arange(B, dtype=torch.int32, device=dev)
+    q_pos = torch.full((B,), tau, dtype=torch.int32, device=dev)
+    ws_c = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_COMPRESS, B=B, T=1)), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_ATTEND, Q=B, cap=N)), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, cfg["n_h"], cfg["c"]), dtype=torch.bfloat16, device=dev)
+    if dual:
+        ws_t = torch.empty(max(1, L.csa_topk_workspace_size(dims, B, N)), dtype=torch.uint8, device=dev)
+        scores = torch.empty((B, N), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+
+    def k_compress(c):
+        L.csa_compress(dims, lw, c, H1, 1, pos0, ws_c)
+
+    def k_index(c):
+        L.csa_index_scores(dims, c, qs["qI"], qs["w"], q_seq, q_pos, B, scores, N)
+
+    def k_topk(c):
+        L.csa_topk(dims, c, q_seq, q_pos, B, scores, N, idx, ws_t)
+
+    def k_attend(c):
+        L.csa_attend(dims, c, qs["q"], W["gamma_q"], W["sink"], q_seq, q_pos, B, idx if dual else None, out, ws_a)
+
+    phases = [k_compress, k_index, k_topk, k_attend] if dual else [k_compress, k_attend]
+
+    def step(c):
+        for f in phases:
+            f(c)
+
+    step(caches[0])
+    torch.cuda.synchronize()
+    ref = (out.clone(), idx.clone() if dual else None)
+    graphs = [capture(lambda c=c: step(c)) for c in caches]
+    torch.cuda.synchronize()
+    steps = args.steps or 200
+    warm = args.warmup if args.warmup is not None else 10
+    for s in range(warm):
+        graphs[s % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        graphs[s % len(graphs)].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ok = torch.equal(out, ref[0]) and (not dual or torch.equal(idx, ref[1]))
+
+    # per-kernel launch durations (same inputs and grids, rotating cache copies)
+    kt = {name: kernel_time_us([lambda c=c, f=f: f(c) for c in caches])
+          for name, f in zip(["compress", "index_scores", "topk", "attend"] if dual else ["compress", "attend"], phases)}
+    res = {
+        "metric": ("CSA decode queries/s (Flash-shaped, 128K context, batch 16)" if cfg["name"] == "c2"
+                   else f"CSA decode queries/s ({cfg['name']})"),
+        "value": round(B * steps / wall, 1), "unit": "queries/s", "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": round(wall / steps * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 MFMA on E4M3/bf16 storage, fp32 accumulate",
+        "data": "synthetic (seeded N(0,1) hidden states and queries, N(0,1/fan_in) weights)",
+    }
+    if dual:
+        bytes_per_query = N * cfg["c_I"] + cfg["n_hI"] * cfg["c_I"] + 2 * cfg["n_hI"]
+        alg = B * bytes_per_query
+        dur = kt["index_scores"] * 1e-6
+        res["roofline"] = {"bound": "hbm", "kernel": "indexer (k_indexer_bf16)",
+                           "achieved": round(alg / dur / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                           "frac": round(alg / dur / HBM_PEAK, 4), "traffic": None,
+                           "alg_bytes_per_launch": alg, "avg_launch_us": round(kt["index_scores"], 2)}
+    else:
+        rows = N + cfg["n_win"]
+        alg = B * (rows * 576 + 2 * 2 * cfg["n_h"] * cfg["c"])
+        dur = kt["attend"] * 1e-6
+        res["roofline"] = {"bound": "hbm", "kernel": "attention (k_attend_mfma + combine)",
+                           "achieved": round(alg / dur / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                           "frac": round(alg / dur / HBM_PEAK, 4), "traffic": None,
+                           "alg_bytes_per_launch": alg, "avg_launch_us": round(kt["attend"], 2)}
+    res["kernels_us"] = {k_: round(v, 2) for k_, v in kt.items()}
+    res["graph_replay_matches_eager"] = bool(ok)
+    res["cache_build_s"] = round(t_build, 2)
+    desc = {"c2": "Flash-shaped CSA decode, 16 seqs x 131072-token context (32768 entries), d=4096, "
+                  "64 heads x 512, indexer 64x128, top-k 512, n_win 128, one new token per sequence per step",
+            "c3": "Pro-shaped CSA decode, 4 seqs x 1048576-token context (262144 entries), d=7168, "
+                  "128 heads x 512, indexer 64x128, top-k 1024, n_win 128",
+            "c5": "HCA decode, 8 seqs x 1048576-token context (8192 entries, m'=128), d=4096, "
+                  "64 heads x 512, dense, n_win 128"}[cfg["name"]]
+    res["config"] = {"workload": f"{cfg['name']}: {desc}", "global_batch": B, "seq_len": tau,
+                     "parallelism": "single GPU", "launch": "one HIP graph per step",
+                     "cache_copies": len(caches)}
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    return res, ok
+
+
+def run_prefill(args, cfg):
+    import torch
+
+    import long_context_attention_11_amd as L
+    import synth
+
+    dev = "cuda:0"
+    T, p0, k = cfg["T"], cfg["prefix"], cfg["top_k"]
+    dims = L.Dims.from_config(cfg)
+    W = synth.weights(cfg, device=dev)
+    lw = lib_weights(L, W, True)
+    cap = (p0 + T) // cfg["m"]
+    win_cap = T + cfg["n_win"]
+    t_build = time.perf_counter()
+    cache = build_cache(L, synth, cfg, dims, lw, dev, 1, p0, cap, win_cap) if p0 else \
+        L.Cache(dims, B=1, cap=cap, win_cap=win_cap, device=dev)
+    t_build = time.perf_counter() - t_build
+    H = synth.hidden(cfg, 0, p0, p0 + T, device=dev).unsqueeze(0).contiguous()
+    qs = synth.queries(cfg, T, device=dev, tag="prefill")
+    pos0 = torch.full((1,), p0, dtype=torch.int32, device=dev)
+    dt = torch.float32 if cfg["act"] == "f32" else torch.bfloat16
+    out = torch.empty((T, cfg["n_h"], cfg["c"]), dtype=dt, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    q_chunk = min(T, 4096)
+    ws = torch.empty(L.csa_workspace_size(dims, L.OP_FORWARD, B=1, T=T, cap=cap, q_chunk=q_chunk),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        L.csa_forward(dims, lw, cache, H, T, pos0, qs["q"], qs["qI"], qs["w"], W["gamma_q"], W["sink"],
+                      out, idx, ws)
+
+    step()
+    torch.cuda.synchronize()
+    steps = args.steps or (5 if p0 else 50)
+    warm = args.warmup if args.warmup is not None else 1
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for _ in range(steps):
+        step()
+    ev[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev[0].elapsed_time(ev[1]) / steps
+    res = {"metric": f"CSA prefill tokens/s ({cfg['name']})", "value": round(T * steps / wall, 1),
+           "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+           "ms_per_step": round(wall / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None,
+           "dtype": "fp32" if cfg["act"] == "f32" else "bf16 MFMA on E4M3/bf16 storage, fp32 accumulate",
+           "data": "synthetic (seeded N(0,1) hidden states and queries, N(0,1/fan_in) weights)",
+           "gpu_ms_per_step": round(gpu_ms, 4), "cache_build_s": round(t_build, 2),
+           "config": {"workload": f"{cfg['name']}: chunked prefill, {T}-token chunk after a {p0}-token prefix, "
+                                  f"d={cfg['d']}, {cfg['n_h']} heads x {cfg['c']}, top-k {k}",
+                      "global_batch": 1, "seq_len": p0 + T, "parallelism": "single GPU",
+                      "launch": "eager csa_forward"}}
+    if cfg["kv_fmt"] != "f32":
+        # the indexer's contraction: per query 64 heads x 128 dims x V entries, 2 FLOP each
+        Vs = [min((p0 + t) // cfg["m"], cap) for t in range(T)]
+        flops = 2.0 * cfg["n_hI"] * cfg["c_I"] * sum(Vs)
+        res["indexer_tflop_per_step"] = round(flops / 1e12, 2)
+    if not args.no_cpu and cfg["name"] != "c1":
+        res["cpu_baseline"] = cpu_baseline_prefill(cfg, args.cpu_seconds)
+    return res, True
 
 
 def main():
@@ -136,134 +433,13 @@ def main():
         sys.exit(2)
     import torch
 
-    import long_context_attention_11_amd as L
     import synth
-
-    dev = "cuda:0"
     torch.cuda.set_device(0)
-    cfg = synth.config("c2")
-    B, tau, k = cfg["B"], cfg["prefix"], cfg["top_k"]
-    dims = L.Dims.from_config(cfg)
-    W = synth.weights(cfg, device=dev)
-    lw = L.Weights(torch.stack([W["kv_a"], W["kv_b"], W["z_a"], W["z_b"]]).contiguous(),
-                   torch.stack([W["B_a"], W["B_b"]]).contiguous(),
-                   torch.stack([W["ki_a"], W["ki_b"], W["zi_a"], W["zi_b"]]).contiguous(),
-                   torch.stack([W["BI_a"], W["BI_b"]]).contiguous(), W["gamma_kv"])
-    t_build = time.perf_counter()
-    base = build_cache(L, synth, cfg, dims, W, lw, dev)
-    t_build = time.perf_counter() - t_build
-    caches = [base] + [clone_cache(L, base) for _ in range(args.copies - 1)]
-    N = base.cap
-
-    # per-step inputs: the new token of each sequence and its queries
-    H1 = torch.stack([synth.hidden(cfg, b, tau, tau + 1, device=dev) for b in range(B)])
-    qs = synth.queries(cfg, B, device=dev, tag="decode")
-    pos0 = torch.full((B,), tau, dtype=torch.int32, device=dev)
-    q_seq = torch.arange(B, dtype=torch.int32, device=dev)
-    q_pos = torch.full((B,), tau, dtype=torch.int32, device=dev)
-    ws_c = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_COMPRESS, B=B, T=1)), dtype=torch.uint8, device=dev)
-    ws_t = torch.empty(max(1, L.csa_topk_workspace_size(dims, B, N)), dtype=torch.uint8, device=dev)
-    ws_a = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_ATTEND, Q=B, cap=N)), dtype=torch.uint8, device=dev)
-    scores = torch.empty((B, N), dtype=torch.float32, device=dev)
-    idx = torch.empty((B, k), dtype=torch.int32, device=dev)
-    out = torch.empty((B, cfg["n_h"], cfg["c"]), dtype=torch.bfloat16, device=dev)
-
-    def phase_compress(c):
-        L.csa_compress(dims, lw, c, H1, 1, pos0, ws_c)
-
-    def phase_index(c):
-        L.csa_index_scores(dims, c, qs["qI"], qs["w"], q_seq, q_pos, B, scores, N)
-
-    def phase_rest(c):
-        L.csa_topk(dims, c, q_seq, q_pos, B, scores, N, idx, ws_t)
-        L.csa_attend(dims, c, qs["q"], W["gamma_q"], W["sink"], q_seq, q_pos, B, idx, out, ws_a)
-
-    phases = (phase_compress, phase_index, phase_rest)
-    # eager reference output (checked against every graph replay below)
-    for f in phases:
-        f(caches[0])
-    torch.cuda.synchronize()
-    ref_out, ref_idx = out.clone(), idx.clone()
-
-    runners = []
-    if args.eager:
-        for c in caches:
-            runners.append([lambda f=f, c=c: f(c) for f in phases])
+    cfg = synth.config(args.config)
+    if args.config in ("c2", "c3", "c5"):
+        res, ok = run_decode(args, cfg)
     else:
-        side = torch.cuda.Stream()
-        for c in caches:
-            gs = []
-            for f in phases:
-                side.wait_stream(torch.cuda.current_stream())
-                with torch.cuda.stream(side):
-                    f(c)
-                torch.cuda.current_stream().wait_stream(side)
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    f(c)
-                gs.append(g.replay)
-            runners.append(gs)
-        torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for s in range(args.warmup):
-        for r in runners[s % len(runners)]:
-            r()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        e = ev[s]
-        run = runners[s % len(runners)]
-        e[0].record()
-        run[0]()
-        e[1].record()
-        run[1]()
-        e[2].record()
-        run[2]()
-        e[3].record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
-    idx_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    step_ms = [e[0].elapsed_time(e[3]) for e in ev]
-    ok = torch.equal(out, ref_out) and torch.equal(idx, ref_idx)
-
-    K = args.steps
-    qps = B * K / wall
-    idx_avg_s = sum(idx_ms) / len(idx_ms) / 1e3
-    bytes_per_query = N * cfg["c_I"] + cfg["n_hI"] * cfg["c_I"] + 2 * cfg["n_hI"]
-    alg_bytes = B * bytes_per_query
-    achieved = alg_bytes / idx_avg_s
-    res = {
-        "metric": "CSA decode queries/s (Flash-shaped, 128K context, batch 16)",
-        "value": round(qps, 1),
-        "unit": "queries/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall / K * 1e3, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16 MFMA on E4M3/bf16 storage, fp32 accumulate",
-        "data": "synthetic (seeded N(0,1) hidden states and queries, N(0,1/fan_in) weights)",
-        "config": {"workload": "c2: Flash-shaped CSA decode, 16 seqs x 131072-token context "
-                               "(32768 entries), d=4096, 64 heads x 512, indexer 64x128, top-k 512, "
-                               "n_win 128, one new token per sequence per step",
-                   "global_batch": B, "seq_len": tau, "parallelism": "single GPU",
-                   "launch": "eager" if args.eager else "hip graphs",
-                   "cache_copies": len(caches)},
-        "roofline": {"bound": "hbm", "kernel": "indexer (k_indexer_bf16)",
-                     "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
-                     "alg_bytes_per_launch": alg_bytes,
-                     "avg_launch_us": round(idx_avg_s * 1e6, 2)},
-        "step_gpu_us_avg": round(sum(step_ms) / len(step_ms) * 1e3, 2),
-        "graph_replay_matches_eager": bool(ok),
-        "cache_build_s": round(t_build, 2),
-    }
-    if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        res, ok = run_prefill(args, cfg)
     print(json.dumps(res), flush=True)
     if not ok:
         sys.exit(1)

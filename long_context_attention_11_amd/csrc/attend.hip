@@ -8,20 +8,17 @@
 // "02 · DeepSeek-V4: 压缩注意力撑起 1M 上下文" §2.4 (window rows join the compressed entries in
 // one attention).
 //
-// E4M3/bf16 rows: 64-row tiles are gathered into LDS as bf16 (the E4M3 -> bf16 widening is
+// E4M3/bf16 rows: 32-row tiles are gathered into LDS as bf16 (the E4M3 -> bf16 widening is
 // exact) in two layouts, row-major for Q.K and dim-major for P.V, and contracted on bf16
-// MFMA with float32 accumulation.  A workgroup (4 waves, 16 heads each) covers 64 heads of
-// one query, so every staged row serves 64 heads.  Decode splits a query's rows over several
-// workgroups and merges their (max, sum, output) triples in a second kernel.
+// MFMA with float32 accumulation.  A workgroup (8 waves) covers 64 heads of one query, so
+// every staged row serves 64 heads.  Decode splits a query's rows over several workgroups
+// and merges their (max, sum, output) triples in a second kernel.
 #include "csa_internal.h"
 
 namespace csa {
 namespace {
 
 constexpr int AC = 512, AR = 64, ANOPE = AC - AR, AROWB = ANOPE + 2 * AR;  // 576 B rows
-constexpr int ATILE = 64;
-constexpr int AK_LD = AC + 8;        // bf16 pitch of the row-major tile (1040 B)
-constexpr int AV_LD = ATILE + 8;     // bf16 pitch of the dim-major tile (144 B)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float NEG_BIG = -1.0e30f;
 
@@ -63,13 +60,6 @@ __device__ __forceinline__ int64_t row_offset(const AttendArgs& a, int q, int se
   return ((int64_t)seq * a.win_cap + slot) * AROWB | ((int64_t)1 << 62);  // tag: window ring
 }
 
-// Swizzled position of (dim d, row r) in the dim-major tile: 16-byte chunks of a dim's row
-// are XOR-permuted by (d >> 3) & 7 so that writers stepping over dims spread across banks.
-__device__ __forceinline__ int vt_index(int d, int r) {
-  const int chunk = (r >> 3) ^ ((d >> 3) & 7);
-  return d * AV_LD + chunk * 8 + (r & 7);
-}
-
 // Sum of squares of 8 bf16 values packed in a uint4.
 __device__ __forceinline__ float sumsq_bf16x8(const uint4& v) {
   float s = 0.f;
@@ -83,62 +73,81 @@ __device__ __forceinline__ float sumsq_bf16x8(const uint4& v) {
   return s;
 }
 
-// Normalise 8 query dims (dim0 .. dim0+7), rotate them to tau when they are RoPE dims, and
-// pack them as a bf16 MFMA operand.
-__device__ __forceinline__ bf16x8 prep_q8(const uint4& v, float inv, const float* gamma,
-                                          int dim0, bool rope, int64_t tau, double log2_base) {
+// Normalise 8 query dims (dim0 .. dim0+7), rotate them to tau when they are RoPE dims (cos/sin
+// of pair j at cs[2j], cs[2j+1]), and return them as packed bf16.
+__device__ __forceinline__ uint4 prep_q8(const uint4& v, float inv, const float* gamma, int dim0,
+                                         const float* cs) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float gm[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+  if (gamma) {
+    const float4 g0 = *reinterpret_cast<const float4*>(gamma + dim0);
+    const float4 g1 = *reinterpret_cast<const float4*>(gamma + dim0 + 4);
+    gm[0] = g0.x; gm[1] = g0.y; gm[2] = g0.z; gm[3] = g0.w;
+    gm[4] = g1.x; gm[5] = g1.y; gm[6] = g1.z; gm[7] = g1.w;
+  }
+  const bool rope = dim0 >= ANOPE;
   uint32_t o[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int dim = dim0 + 2 * e;
-    float y0 = bf16_bits_to_f32(w[e] & 0xffffu) * inv;
-    float y1 = bf16_bits_to_f32(w[e] >> 16) * inv;
-    if (gamma) {
-      y0 *= gamma[dim];
-      y1 *= gamma[dim + 1];
-    }
+    float y0 = bf16_bits_to_f32(w[e] & 0xffffu) * inv * gm[2 * e];
+    float y1 = bf16_bits_to_f32(w[e] >> 16) * inv * gm[2 * e + 1];
     if (rope) {
-      float cs, sn;
-      rope_cos_sin(tau, (dim - ANOPE) >> 1, AR, log2_base, cs, sn);
-      const float z0 = y0 * cs - y1 * sn, z1 = y0 * sn + y1 * cs;
+      const int j = (dim0 + 2 * e - ANOPE) >> 1;
+      const float c = cs[2 * j], sn = cs[2 * j + 1];
+      const float z0 = y0 * c - y1 * sn, z1 = y0 * sn + y1 * c;
       y0 = z0;
       y1 = z1;
     }
-    o[e] = f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16);
+    o[e] = pack_bf16x2(y0, y1);
   }
-  return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+  return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Scale 4 output dims (d0 .. d0+3) of one head by 1/L, rotate RoPE dims back by -tau, and
-// store them as bf16.
+// Scale 4 output dims (d0 .. d0+3) of one head by 1/L, rotate RoPE dims back by -tau (table
+// cs as above), and store them as bf16.
 __device__ __forceinline__ void store_out4(const f32x4& o, float invL, uint16_t* orow, int d0,
-                                           bool rope, int64_t tau, double log2_base) {
+                                           const float* cs) {
   float y[4] = {o[0] * invL, o[1] * invL, o[2] * invL, o[3] * invL};
-  if (rope) {
+  if (d0 >= ANOPE) {
 #pragma unroll
     for (int e = 0; e < 4; e += 2) {
-      float cs, sn;
-      rope_cos_sin(tau, (d0 + e - ANOPE) >> 1, AR, log2_base, cs, sn);
-      const float z0 = y[e] * cs + y[e + 1] * sn;  // rotate by -tau
-      const float z1 = -y[e] * sn + y[e + 1] * cs;
+      const int j = (d0 + e - ANOPE) >> 1;
+      const float c = cs[2 * j], sn = cs[2 * j + 1];
+      const float z0 = y[e] * c + y[e + 1] * sn;  // rotate by -tau
+      const float z1 = -y[e] * sn + y[e + 1] * c;
       y[e] = z0;
       y[e + 1] = z1;
     }
   }
-  uint2 pk;
-  pk.x = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
-  pk.y = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
-  *reinterpret_cast<uint2*>(orow + d0) = pk;
+  *reinterpret_cast<uint2*>(orow + d0) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
 }
 
-__global__ __launch_bounds__(256) void k_attend_mfma(AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[ATILE * AK_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[AC * AV_LD];
-  __shared__ int64_t rowoff[ATILE];
+// One workgroup = 8 waves = 64 heads of one query over a range of 32-row tiles.
+// Wave w: heads 16*(w & 3) .. +15 (hq), dims 256*(w >> 2) .. +255 (half).  Q.K is split over
+// the pair's halves of the contraction and summed through LDS in a fixed order, so both
+// waves of a pair hold identical scores, maxima and sums; each then accumulates P.V for its
+// own 256 output dims.  The next tile's rows are loaded into registers while the current one
+// computes.
+constexpr int T2 = 32;               // rows per tile
+constexpr int K2_LD = AC + 8;        // bf16 pitch of the row-major tile (1040 B)
+constexpr int V2_LD = T2 + 8;        // bf16 pitch of the dim-major tile (80 B)
+
+// (dim d, row r) in the dim-major tile: the four 16-byte chunks of a dim's row are XOR-permuted
+// by (d >> 3) & 3, so writers stepping over dim groups spread over the banks.
+__device__ __forceinline__ int vt2_index(int d, int r) {
+  return d * V2_LD + (((r >> 3) ^ ((d >> 3) & 3)) << 3) + (r & 7);
+}
+
+__global__ __launch_bounds__(512) void k_attend_mfma(AttendArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[T2 * K2_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[AC * V2_LD];
+  __shared__ __attribute__((aligned(16))) f32x4 Sx[8][2][64];   // partial S per wave
+  __shared__ int64_t rowoff[2][T2];
+  __shared__ float rope_cs[AR];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
+  const int hq = wave & 3, half = wave >> 2;
   const int nhg = (a.n_h + 63) / 64;
   const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
   const int split = L % a.splits;
@@ -151,170 +160,185 @@ __global__ __launch_bounds__(256) void k_attend_mfma(AttendArgs a) {
   const int nsel = a.idx ? a.k : V;
   const int w0 = max(0, tau - a.n_win + 1);
   const int nrows = nsel + (tau - w0 + 1);
-  const int r_lo = split * a.tiles_per_split * ATILE;
-  const int r_hi = min(nrows, r_lo + a.tiles_per_split * ATILE);
-  const int h = hg * 64 + wave * 16 + col;   // this lane's head
-  const bool head_ok = (hg * 64 + wave * 16) < a.n_h;
+  const int r_lo = split * a.tiles_per_split * T2;
+  const int r_hi = min(nrows, r_lo + a.tiles_per_split * T2);
+  const int h = hg * 64 + hq * 16 + col;   // this lane's head
+  const bool head_ok = (hg * 64 + hq * 16) < a.n_h;
   const int hh = min(h, a.n_h - 1);
+  const int dbase = half * 256;            // this wave's output dims
 
-  // ---- query prep: RMSNorm over 512 dims, RoPE at tau on dims 448..511, round to bf16.
-  // B operand of step ks (dims ks*32 .. +31): lane holds dims ks*32 + g*8 .. +7 of head h.
-  bf16x8 Qop[16];
+  if (tid < AR / 2) rope_cos_sin(tau, tid, AR, a.log2_base, rope_cs[2 * tid], rope_cs[2 * tid + 1]);
+  if (tid < T2) {
+    const int r = r_lo + tid;
+    rowoff[0][tid] = r < r_hi ? row_offset(a, q, seq, V, nsel, w0, r) : (int64_t)-1;
+  }
+  __syncthreads();
+
+  // ---- query prep: RMSNorm over 512 dims, RoPE at tau on dims 448..511, bf16.  B operand of
+  // step ks (dims dbase + ks*32 .. +31): lane holds dims dbase + ks*32 + g*8 .. +7 of head h.
+  bf16x8 Qop[8];
   {
     const uint16_t* qrow = a.q + ((size_t)q * a.n_h + hh) * AC;
+    // all 16 loads in flight at once; this wave's 8 are kept for the operands
     uint4 raw[16];
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) raw[ks] = *reinterpret_cast<const uint4*>(qrow + ks * 32 + g * 8);
     float ss = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      raw[ks] = *reinterpret_cast<const uint4*>(qrow + ks * 32 + g * 8);
-      ss += sumsq_bf16x8(raw[ks]);
-    }
+    for (int ks = 0; ks < 16; ++ks) ss += sumsq_bf16x8(raw[ks]);
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
     const float inv = 1.0f / sqrtf(ss / (float)AC + a.eps);
 #pragma unroll
-    for (int ks = 0; ks < ANOPE / 32; ++ks)
-      Qop[ks] = prep_q8(raw[ks], inv, a.gamma_q, ks * 32 + g * 8, false, tau, a.log2_base);
-    Qop[14] = prep_q8(raw[14], inv, a.gamma_q, 14 * 32 + g * 8, true, tau, a.log2_base);
-    Qop[15] = prep_q8(raw[15], inv, a.gamma_q, 15 * 32 + g * 8, true, tau, a.log2_base);
+    for (int ks = 0; ks < 8; ++ks) {
+      const int dim0 = dbase + ks * 32 + g * 8;
+      const uint4 pk = prep_q8(half ? raw[8 + ks] : raw[ks], inv, a.gamma_q, dim0, rope_cs);
+      Qop[ks] = __builtin_bit_cast(bf16x8, pk);
+    }
   }
 
   const float sink2 = (a.sink && head_ok) ? a.sink[hh] * LOG2E : NEG_BIG;
   float m_run = a.sink ? sink2 : NEG_BIG;
   float l_run = 0.f;
-  f32x4 O[32];
+  f32x4 O[16];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) O[i] = f32x4{0, 0, 0, 0};
+  for (int i = 0; i < 16; ++i) O[i] = f32x4{0, 0, 0, 0};
 
-  // staging map: thread covers dim-group dg (8 dims) of rows rsub*16 .. rsub*16+15
-  const int dg = tid >> 2, rsub = tid & 3;
-
-  for (int t0 = r_lo; t0 < r_hi; t0 += ATILE) {
-    if (tid < ATILE) {
-      const int r = t0 + tid;
-      rowoff[tid] = r < r_hi ? row_offset(a, q, seq, V, nsel, w0, r) : (int64_t)-1;
+  // staging map: thread covers dim-group dg (8 dims) of rows 4*rq .. 4*rq+3
+  const int dg = tid & 63, rq = tid >> 6;
+  const bool nope_group = dg < ANOPE / 8;
+  // byte offset of this group's 16-byte load: 8 E4M3 dims (the next 8 bytes are unused), or
+  // 8 bf16 RoPE dims
+  const int col_off = nope_group ? dg * 8 : ANOPE + (dg - ANOPE / 8) * 16;
+  uint4 pre[4];
+  auto gather = [&](int buf) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int64_t off = rowoff[buf][rq * 4 + rr];
+      const uint8_t* base = ((off >> 62) & 1) ? a.win : a.kv;
+      const uint8_t* src = off >= 0 ? base + (off & (((int64_t)1 << 62) - 1)) : a.kv;
+      pre[rr] = *reinterpret_cast<const uint4*>(src + col_off);
+    }
+  };
+  gather(0);
+  int buf = 0;
+  for (int t0 = r_lo; t0 < r_hi; t0 += T2) {
+    // ---- convert the prefetched rows; write Ks (row-major) and Vt (dim-major)
+    uint4 v[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const bool ok = rowoff[buf][rq * 4 + rr] >= 0;
+      uint32_t x0, x1, x2, x3;
+      e4m3x4_to_bf16x4(pre[rr].x, x0, x1);
+      e4m3x4_to_bf16x4(pre[rr].y, x2, x3);
+      uint4 o = nope_group ? make_uint4(x0, x1, x2, x3) : pre[rr];
+      if (!ok) o = make_uint4(0u, 0u, 0u, 0u);
+      v[rr] = o;
+      *reinterpret_cast<uint4*>(&Ks[(rq * 4 + rr) * K2_LD + dg * 8]) = o;
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a0 = reinterpret_cast<const uint32_t*>(&v[0])[w];
+      const uint32_t a1 = reinterpret_cast<const uint32_t*>(&v[1])[w];
+      const uint32_t a2 = reinterpret_cast<const uint32_t*>(&v[2])[w];
+      const uint32_t a3 = reinterpret_cast<const uint32_t*>(&v[3])[w];
+      const uint2 lo = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u));
+      const uint2 hi = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u));
+      *reinterpret_cast<uint2*>(&Vt[vt2_index(dg * 8 + 2 * w, rq * 4)]) = lo;
+      *reinterpret_cast<uint2*>(&Vt[vt2_index(dg * 8 + 2 * w + 1, rq * 4)]) = hi;
+    }
+    // row sources of the next tile
+    const int t1 = t0 + T2;
+    if (tid < T2) {
+      const int r = t1 + tid;
+      rowoff[buf ^ 1][tid] = r < r_hi ? row_offset(a, q, seq, V, nsel, w0, r) : (int64_t)-1;
     }
     __syncthreads();
-    // ---- gather 64 rows x 512 dims into Ks (row-major) and Vt (dim-major), as bf16.
-    // Thread: dim-group dg (8 dims) of rows rsub*16 .. +15, in batches of 4 rows.
+    if (t1 < r_hi) gather(buf ^ 1);   // in flight while this tile computes
+
+    // ---- partial S^T = K . Q^T over this wave's 256 dims, 2 row tiles
+    f32x4 S[2];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      uint32_t colv[4][4];  // 4 rows x 8 bf16
+    for (int rt = 0; rt < 2; ++rt) {
+      S[rt] = f32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int row = rsub * 16 + rb * 4 + rr;
-        const int64_t off = rowoff[row];
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (off >= 0) {
-          const uint8_t* base = ((off >> 62) & 1) ? a.win : a.kv;
-          const uint8_t* src = base + (off & (((int64_t)1 << 62) - 1));
-          if (dg < ANOPE / 8) {
-            uint2 raw = *reinterpret_cast<const uint2*>(src + dg * 8);
-            e4m3x4_to_bf16x4(raw.x, v.x, v.y);
-            e4m3x4_to_bf16x4(raw.y, v.z, v.w);
-          } else {
-            v = *reinterpret_cast<const uint4*>(src + ANOPE + (dg - ANOPE / 8) * 16);
-          }
-        }
-        *reinterpret_cast<uint4*>(&Ks[row * AK_LD + dg * 8]) = v;
-        colv[rr][0] = v.x;
-        colv[rr][1] = v.y;
-        colv[rr][2] = v.z;
-        colv[rr][3] = v.w;
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(&Ks[(rt * 16 + col) * K2_LD + dbase + ks * 32 + g * 8]);
+        S[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Qop[ks], S[rt], 0, 0, 0);
       }
-      // transpose: each of the 8 dims gets 4 consecutive rows (8 bytes)
-      const int r0 = rsub * 16 + rb * 4;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        const uint32_t r01 = ((colv[0][e >> 1] >> sh) & 0xffffu) | (((colv[1][e >> 1] >> sh) & 0xffffu) << 16);
-        const uint32_t r23 = ((colv[2][e >> 1] >> sh) & 0xffffu) | (((colv[3][e >> 1] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<uint2*>(&Vt[vt_index(dg * 8 + e, r0)]) = make_uint2(r01, r23);
-      }
+      Sx[wave][rt][lane] = S[rt];
     }
     __syncthreads();
+    // full scores: half 0 + half 1, the same order in both waves of the pair
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) S[rt] = Sx[hq][rt][lane] + Sx[hq + 4][rt][lane];
 
-    if (head_ok) {
-      // ---- S^T = K . Q^T for 4 row tiles: lane holds head col, rows 16*rt + 4g + e
-      f32x4 S[4];
+    // ---- online softmax (log2 domain), sink already in m_run; lane holds head col, rows
+    // 16*rt + 4g + e
+    float mx = NEG_BIG;
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        S[rt] = f32x4{0, 0, 0, 0};
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-          bf16x8 A = *reinterpret_cast<const bf16x8*>(&Ks[(rt * 16 + col) * AK_LD + ks * 32 + g * 8]);
-          S[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Qop[ks], S[rt], 0, 0, 0);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = rowoff[buf][rt * 16 + 4 * g + e] >= 0;
+        S[rt][e] = ok ? S[rt][e] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, S[rt][e]);
       }
-      // ---- online softmax (log2 domain), sink already in m_run
-      float mx = NEG_BIG;
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    float ls = 0.f;
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = rt * 16 + 4 * g + e;
-          const bool ok = rowoff[row] >= 0;
-          S[rt][e] = ok ? S[rt][e] * a.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, S[rt][e]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
-      float ls = 0.f;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          S[rt][e] = exp2f(S[rt][e] - m_new);
-          ls += S[rt][e];
-        }
-      ls += __shfl_xor(ls, 16, 64);
-      ls += __shfl_xor(ls, 32, 64);
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) O[i] *= alpha;
-      // ---- O^T += V^T . P^T over 64 rows (2 K steps of 32).  K step kk pairs lane group g's
-      // rows {32kk + 4g + e} and {32kk + 16 + 4g + e} (e < 4) on both operands.
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        uint4 pb;
-        pb.x = f32_to_bf16_bits(S[2 * kk][0]) | (f32_to_bf16_bits(S[2 * kk][1]) << 16);
-        pb.y = f32_to_bf16_bits(S[2 * kk][2]) | (f32_to_bf16_bits(S[2 * kk][3]) << 16);
-        pb.z = f32_to_bf16_bits(S[2 * kk + 1][0]) | (f32_to_bf16_bits(S[2 * kk + 1][1]) << 16);
-        pb.w = f32_to_bf16_bits(S[2 * kk + 1][2]) | (f32_to_bf16_bits(S[2 * kk + 1][3]) << 16);
-        const bf16x8 Bp = __builtin_bit_cast(bf16x8, pb);
-#pragma unroll
-        for (int dt = 0; dt < 32; ++dt) {
-          const int d = dt * 16 + col;
-          const uint2 lo = *reinterpret_cast<const uint2*>(&Vt[vt_index(d, kk * 32 + 4 * g)]);
-          const uint2 hi = *reinterpret_cast<const uint2*>(&Vt[vt_index(d, kk * 32 + 16 + 4 * g)]);
-          const bf16x8 Av = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Bp, O[dt], 0, 0, 0);
-        }
+      for (int e = 0; e < 4; ++e) {
+        S[rt][e] = exp2f(S[rt][e] - m_new);
+        ls += S[rt][e];
       }
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+    if (t0 != r_lo && __any(alpha != 1.0f)) {  // O is zero on the first tile; skip when no max moved
+#pragma unroll
+      for (int i = 0; i < 16; ++i) O[i] *= alpha;
     }
+    // ---- O^T += V^T . P^T over the 32 rows (one K step): lane group g pairs rows
+    // {4g + e} and {16 + 4g + e} (e < 4) on both operands
+    uint4 pb;
+    pb.x = pack_bf16x2(S[0][0], S[0][1]);
+    pb.y = pack_bf16x2(S[0][2], S[0][3]);
+    pb.z = pack_bf16x2(S[1][0], S[1][1]);
+    pb.w = pack_bf16x2(S[1][2], S[1][3]);
+    const bf16x8 Bp = __builtin_bit_cast(bf16x8, pb);
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) {
+      const int d = dbase + dt * 16 + col;
+      const uint2 lo = *reinterpret_cast<const uint2*>(&Vt[vt2_index(d, 4 * g)]);
+      const uint2 hi = *reinterpret_cast<const uint2*>(&Vt[vt2_index(d, 16 + 4 * g)]);
+      const bf16x8 Av = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Bp, O[dt], 0, 0, 0);
+    }
+    buf ^= 1;
     __syncthreads();
   }
 
   if (!head_ok) return;
-  // O[dt][e] holds head col, dim dt*16 + 4g + e.
+  // O[dt][e] holds head col, dim dbase + dt*16 + 4g + e.
   if (a.splits == 1) {
-    float Lsum = l_run + (a.sink ? exp2f(sink2 - m_run) : 0.f);
+    const float Lsum = l_run + (a.sink ? exp2f(sink2 - m_run) : 0.f);
     const float invL = Lsum > 0.f ? 1.0f / Lsum : 0.f;
     uint16_t* orow = a.out + ((size_t)q * a.n_h + h) * AC;
 #pragma unroll
-    for (int dt = 0; dt < ANOPE / 16; ++dt) store_out4(O[dt], invL, orow, dt * 16 + 4 * g, false, tau, a.log2_base);
-#pragma unroll
-    for (int dt = ANOPE / 16; dt < 32; ++dt) store_out4(O[dt], invL, orow, dt * 16 + 4 * g, true, tau, a.log2_base);
+    for (int dt = 0; dt < 16; ++dt) store_out4(O[dt], invL, orow, dbase + dt * 16 + 4 * g, rope_cs);
   } else {
     const size_t pidx = ((size_t)q * a.n_h + h) * a.splits + split;
     float* po = a.part_o + pidx * AC;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt)
-      *reinterpret_cast<float4*>(po + dt * 16 + 4 * g) = make_float4(O[dt][0], O[dt][1], O[dt][2], O[dt][3]);
-    if (g == 0) {
+    for (int dt = 0; dt < 16; ++dt)
+      *reinterpret_cast<float4*>(po + dbase + dt * 16 + 4 * g) = make_float4(O[dt][0], O[dt][1], O[dt][2], O[dt][3]);
+    if (g == 0 && half == 0) {
       a.part_ml[pidx * 2] = m_run;
       a.part_ml[pidx * 2 + 1] = l_run;
     }
@@ -322,25 +346,47 @@ __global__ __launch_bounds__(256) void k_attend_mfma(AttendArgs a) {
 }
 
 // Merge split partials: one workgroup of 256 threads per (query, head), 2 dims per thread.
+// Splits are taken 8 at a time (all loads of a chunk in flight), merged with a running max.
+constexpr int COMB_MAX = 64;   // most splits a plan uses
+
 __global__ __launch_bounds__(256) void k_attend_combine(AttendArgs a) {
   const int qh = blockIdx.x;
   const int q = qh / a.n_h, h = qh % a.n_h;
   const int tau = a.q_pos[q];
+  const int d = 2 * threadIdx.x;
   const float* ml = a.part_ml + (size_t)qh * a.splits * 2;
+  const float* po = a.part_o + (size_t)qh * a.splits * AC + d;
   const float sink2 = a.sink ? a.sink[h] * LOG2E : NEG_BIG;
   float M = a.sink ? sink2 : NEG_BIG;
-  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, ml[2 * s]);
-  float Lsum = a.sink ? exp2f(sink2 - M) : 0.f;
-  for (int s = 0; s < a.splits; ++s) Lsum += ml[2 * s + 1] * exp2f(ml[2 * s] - M);
-  const float invL = Lsum > 0.f ? 1.0f / Lsum : 0.f;
-  const int d = 2 * threadIdx.x;
+  float Lsum = a.sink ? 1.0f : 0.f;   // the sink's term exp2(sink2 - M) with M = sink2
   float y0 = 0.f, y1 = 0.f;
-  const float* po = a.part_o + (size_t)qh * a.splits * AC;
-  for (int s = 0; s < a.splits; ++s) {
-    const float f = exp2f(ml[2 * s] - M);
-    y0 = fmaf(po[(size_t)s * AC + d], f, y0);
-    y1 = fmaf(po[(size_t)s * AC + d + 1], f, y1);
+  for (int s0 = 0; s0 < a.splits; s0 += 8) {
+    float2 mls[8], ov[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int s = min(s0 + i, a.splits - 1);
+      mls[i] = *reinterpret_cast<const float2*>(ml + 2 * s);
+      ov[i] = *reinterpret_cast<const float2*>(po + (size_t)s * AC);
+    }
+    float Mc = M;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (s0 + i < a.splits) Mc = fmaxf(Mc, mls[i].x);
+    const float r = exp2f(M - Mc);
+    Lsum *= r;
+    y0 *= r;
+    y1 *= r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (s0 + i >= a.splits) break;
+      const float f = exp2f(mls[i].x - Mc);
+      Lsum = fmaf(mls[i].y, f, Lsum);
+      y0 = fmaf(ov[i].x, f, y0);
+      y1 = fmaf(ov[i].y, f, y1);
+    }
+    M = Mc;
   }
+  const float invL = Lsum > 0.f ? 1.0f / Lsum : 0.f;
   y0 *= invL;
   y1 *= invL;
   if (d >= ANOPE) {
@@ -350,8 +396,7 @@ __global__ __launch_bounds__(256) void k_attend_combine(AttendArgs a) {
     y0 = z0;
     y1 = z1;
   }
-  *reinterpret_cast<uint32_t*>(a.out + (size_t)qh * AC + d) =
-      f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16);
+  *reinterpret_cast<uint32_t*>(a.out + (size_t)qh * AC + d) = pack_bf16x2(y0, y1);
 }
 
 // float32 rows (fp32 formats): one workgroup of 64 threads per (query, head); exact
@@ -460,10 +505,11 @@ struct SplitPlan {
 
 SplitPlan plan_splits(const csa_dims& d, int32_t Q, int32_t cap, bool dense) {
   const int max_rows = (dense ? cap : d.top_k) + d.n_win;
-  const int ntiles = (max_rows + ATILE - 1) / ATILE;
+  const int ntiles = (max_rows + T2 - 1) / T2;
   const int blocks = Q * ((d.n_h + 63) / 64);
-  int target = (512 + blocks - 1) / blocks;
-  target = std::max(1, std::min(target, ntiles));
+  // about one workgroup per CU (each holds 91 KB of LDS)
+  int target = (256 + blocks - 1) / blocks;
+  target = std::max(1, std::min(std::min(target, ntiles), COMB_MAX));
   const int tps = (ntiles + target - 1) / target;
   return {(ntiles + tps - 1) / tps, tps};
 }
@@ -521,7 +567,7 @@ hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
   a.part_o = (float*)ws;
   a.part_ml = p.splits > 1 ? (float*)ws + (size_t)Q * d.n_h * p.splits * AC : nullptr;
   const int nhg = (d.n_h + 63) / 64;
-  hipLaunchKernelGGL(k_attend_mfma, dim3(Q * nhg * p.splits), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_attend_mfma, dim3(Q * nhg * p.splits), dim3(512), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   hipLaunchKernelGGL(k_attend_combine, dim3(Q * d.n_h), dim3(256), 0, s, a);

@@ -282,7 +282,7 @@ int csa_topk(const csa_dims* dims, const csa_cache* cache, const int32_t* q_seq,
   if (!q_seq || !q_pos || !scores || !idx_out)
     return fail(CSA_ERR_INVALID_ARGUMENT, "q_seq, q_pos, scores and idx_out must be set");
   if (Q < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "Q must be >= 1");
-  if (ld < cache->cap || (ld & 3)) return fail(CSA_ERR_INVALID_ARGUMENT, "ld must be >= cap and a multiple of 4");
+  if (ld < cache->cap) return fail(CSA_ERR_INVALID_ARGUMENT, "ld must be >= cap");
   if (cache->cap > topk_max_visible(*dims))
     return fail(CSA_ERR_UNSUPPORTED, "cap exceeds the entries the top-k kernels handle for this top_k");
   const size_t need = topk_workspace_bytes(*dims, Q, cache->cap);

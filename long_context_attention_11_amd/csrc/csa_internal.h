@@ -27,9 +27,18 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as
 
 // float32 -> bfloat16 bits, round to nearest even; NaN -> quiet NaN with the input's sign.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t qnan = ((u >> 16) & 0x8000u) | 0x7fc0u;
+  return ((u & 0x7fffffffu) > 0x7f800000u) ? qnan : rounded;  // select, no branch
+}
+
+// Two float32 -> packed bfloat16 pair (low half = a), round to nearest even, by the gfx950
+// packed conversion instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // float32 -> OCP E4M3 (e4m3fn) code: nearest, ties to even, saturating at +-448; NaN -> 0x7f.

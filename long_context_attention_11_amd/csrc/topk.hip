@@ -8,17 +8,19 @@
 //
 // One workgroup of 1024 threads holds up to 1024*E items in registers, thread t holding a
 // contiguous run, so thread order is index order and in-order compaction is one block scan.
-// Rows longer than one workgroup's share are cut into segments of 16384; each segment keeps
-// its own top-k (a superset of its share of the global top-k under the same total order),
-// and one merge workgroup per query selects from the concatenated candidates.
+// Rows longer than 4096 are cut into segments of 4096; each segment keeps its own top-k (a
+// superset of its share of the global top-k under the same total order).  Merge levels then
+// take groups of candidate lists (up to 16384 candidates per workgroup) down to one list.
+// Every list stays in index order, so the final one is the answer, already sorted.
 #include "csa_internal.h"
 
 namespace csa {
 namespace {
 
 constexpr int TK_THREADS = 1024;
-constexpr int TK_SEG = 16384;      // items per segment workgroup (E = 16)
-constexpr int TK_MERGE_MAX = 32768;  // candidates one merge workgroup can take (E = 32)
+constexpr int TK_DIRECT_MAX = 4096;  // rows up to this length: one workgroup, one launch
+constexpr int TK_SEG0 = 4096;        // scores per level-0 segment (E = 4)
+constexpr int TK_MERGE = 16384;      // candidates one merge workgroup takes (E <= 16)
 
 struct TopkShared {
   int hist[2048];
@@ -149,8 +151,8 @@ __device__ __forceinline__ int visible(const int32_t* q_seq, const int32_t* q_po
   return max(0, min(q_pos[q] / m, n_entries[q_seq[q]]));
 }
 
-// Stage 1 (or the only stage): blockIdx.x = query, blockIdx.y = segment of E*1024 scores.
-// direct != 0: this segment is the whole row; write the final selection to idx_out.
+// Level 0: blockIdx.x = query, blockIdx.y = segment of E*1024 scores.
+// direct != 0: the segment is the whole row; write the final selection to idx_out [Q][k].
 // Otherwise write the segment's candidates to cand_idx/cand_key [Q][nseg][k] (-1 padded).
 template <int E>
 __global__ __launch_bounds__(TK_THREADS) void k_topk_segment(
@@ -175,18 +177,23 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_segment(
   bool valid[E];
   const int first = base + threadIdx.x * E;
   const float* row = scores + (size_t)q * ld;
-  if (first + E <= V && ((ld & 3) == 0)) {
+  bool loaded = false;
+  if constexpr (E % 4 == 0) {
+    if (first + E <= V && ((ld & 3) == 0)) {
 #pragma unroll
-    for (int i = 0; i < E; i += 4) {
-      float4 v = *reinterpret_cast<const float4*>(row + first + i);
-      key[i] = score_key(v.x);
-      key[i + 1] = score_key(v.y);
-      key[i + 2] = score_key(v.z);
-      key[i + 3] = score_key(v.w);
+      for (int i = 0; i < E; i += 4) {
+        float4 v = *reinterpret_cast<const float4*>(row + first + i);
+        key[i] = score_key(v.x);
+        key[i + 1] = score_key(v.y);
+        key[i + 2] = score_key(v.z);
+        key[i + 3] = score_key(v.w);
+      }
+#pragma unroll
+      for (int i = 0; i < E; ++i) { idx[i] = first + i; valid[i] = true; }
+      loaded = true;
     }
-#pragma unroll
-    for (int i = 0; i < E; ++i) { idx[i] = first + i; valid[i] = true; }
-  } else {
+  }
+  if (!loaded) {
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       idx[i] = first + i;
@@ -201,17 +208,20 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_segment(
   }
 }
 
-// Stage 2: one workgroup per query selects from nseg*k candidates (in index order).
+// Merge level: blockIdx.x = query, blockIdx.y = group of G consecutive candidate lists
+// (of nlist per query, k each, in index order).  direct != 0: one group covers every list;
+// write the final selection.  Otherwise write one list of k per group.
 template <int E>
-__global__ __launch_bounds__(TK_THREADS) void k_topk_merge(const int32_t* __restrict__ cand_idx,
-                                                           const uint32_t* __restrict__ cand_key,
-                                                           int nseg, int k,
-                                                           int32_t* __restrict__ idx_out) {
+__global__ __launch_bounds__(TK_THREADS) void k_topk_merge(
+    const int32_t* __restrict__ in_idx, const uint32_t* __restrict__ in_key, int nlist, int G,
+    int k, int direct, int32_t* __restrict__ idx_out, int32_t* __restrict__ out_idx,
+    uint32_t* __restrict__ out_key) {
   __shared__ TopkShared sh;
-  const int q = blockIdx.x;
-  const int n = nseg * k;
-  const int32_t* ci = cand_idx + (size_t)q * n;
-  const uint32_t* ck = cand_key + (size_t)q * n;
+  const int q = blockIdx.x, grp = blockIdx.y, ngrp = gridDim.y;
+  const int l0 = grp * G, l1 = min(nlist, l0 + G);
+  const int n = (l1 - l0) * k;
+  const int32_t* ci = in_idx + ((size_t)q * nlist + l0) * k;
+  const uint32_t* ck = in_key + ((size_t)q * nlist + l0) * k;
   uint32_t key[E];
   int idx[E];
   bool valid[E];
@@ -222,66 +232,119 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_merge(const int32_t* __rest
     valid[i] = idx[i] >= 0;
     key[i] = valid[i] ? ck[p] : 0u;
   }
-  int32_t* oidx = idx_out + (size_t)q * k;
-  const int cnt = block_select<E>(key, idx, valid, k, sh, oidx, nullptr);
-  for (int i = cnt + threadIdx.x; i < k; i += TK_THREADS) oidx[i] = -1;
+  int32_t* oidx;
+  uint32_t* okey = nullptr;
+  if (direct) {
+    oidx = idx_out + (size_t)q * k;
+  } else {
+    oidx = out_idx + ((size_t)q * ngrp + grp) * k;
+    okey = out_key + ((size_t)q * ngrp + grp) * k;
+  }
+  const int cnt = block_select<E>(key, idx, valid, k, sh, oidx, okey);
+  for (int i = cnt + threadIdx.x; i < k; i += TK_THREADS) {
+    oidx[i] = -1;
+    if (okey) okey[i] = 0u;
+  }
 }
 
-int merge_E(int n) {
+int items_E(int n) {
   int E = 1;
   while (E * TK_THREADS < n) E *= 2;
   return E;
 }
 
+// One selection tree: segments of TK_SEG0 scores, then merges of up to TK_MERGE candidates.
+struct TopkPlan {
+  int nseg;        // level-0 segments (0: one direct segment)
+  int seg_E;
+  int levels;      // merge levels after level 0
+};
+
+TopkPlan plan_topk(int k, int cap) {
+  TopkPlan p{0, items_E(cap), 0};
+  if (cap <= TK_DIRECT_MAX) return p;
+  p.nseg = (cap + TK_SEG0 - 1) / TK_SEG0;
+  p.seg_E = TK_SEG0 / TK_THREADS;
+  int lists = p.nseg;
+  const int G = std::max(2, TK_MERGE / k);
+  while (true) {
+    ++p.levels;
+    if ((long)lists * k <= TK_MERGE) break;
+    lists = (lists + G - 1) / G;
+  }
+  return p;
+}
+
+
+#define TK_SEG_LAUNCH(EE, grid, direct, out_idx, cidx, ckey)                                     \
+  hipLaunchKernelGGL((k_topk_segment<EE>), grid, dim3(TK_THREADS), 0, s, scores, ld, q_seq, q_pos, \
+                     c.n_entries, d.m, k, direct, out_idx, cidx, ckey)
+#define TK_MERGE_LAUNCH(EE, grid, group)                                                          \
+  hipLaunchKernelGGL((k_topk_merge<EE>), grid, dim3(TK_THREADS), 0, s, in_i, in_k, lists, group, k, \
+                     direct, idx, out_i, out_k)
+
 }  // namespace
 
 int32_t topk_max_visible(const csa_dims& d) {
-  if (d.top_k <= 0) return 0;
-  const long nseg_max = TK_MERGE_MAX / d.top_k;
-  return (int32_t)std::min<long>(nseg_max * TK_SEG, (long)INT32_MAX);
+  if (d.top_k <= 0 || d.top_k > TK_MERGE) return 0;
+  return INT32_MAX / 2;
 }
 
 size_t topk_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap) {
-  if (cap <= 2 * TK_SEG) return 0;  // one direct stage
-  const size_t nseg = (size_t)(cap + TK_SEG - 1) / TK_SEG;
-  return (size_t)Q * nseg * d.top_k * (sizeof(int32_t) + sizeof(uint32_t));
+  const TopkPlan p = plan_topk(d.top_k, cap);
+  if (p.nseg == 0) return 0;
+  // two ping-pong candidate buffers, the first sized for level 0
+  const int G = std::max(2, TK_MERGE / d.top_k);
+  const size_t lists1 = (size_t)(p.nseg + G - 1) / G;
+  const size_t per = (size_t)Q * d.top_k * (sizeof(int32_t) + sizeof(uint32_t));
+  return per * ((size_t)p.nseg + lists1);
 }
 
 hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
                        const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld,
                        int32_t* idx, void* ws, hipStream_t s) {
   const int k = d.top_k;
-  const int cap = c.cap;
-  if (cap <= TK_SEG / 16) {
-    hipLaunchKernelGGL((k_topk_segment<1>), dim3(Q, 1), dim3(TK_THREADS), 0, s, scores, ld, q_seq,
-                       q_pos, c.n_entries, d.m, k, 1, idx, nullptr, nullptr);
+  const TopkPlan p = plan_topk(k, c.cap);
+  if (p.nseg == 0) {
+    switch (p.seg_E) {
+      case 1: TK_SEG_LAUNCH(1, dim3(Q, 1), 1, idx, nullptr, nullptr); break;
+      case 2: TK_SEG_LAUNCH(2, dim3(Q, 1), 1, idx, nullptr, nullptr); break;
+      default: TK_SEG_LAUNCH(4, dim3(Q, 1), 1, idx, nullptr, nullptr); break;
+    }
     return hipGetLastError();
   }
-  if (cap <= TK_SEG) {
-    hipLaunchKernelGGL((k_topk_segment<16>), dim3(Q, 1), dim3(TK_THREADS), 0, s, scores, ld, q_seq,
-                       q_pos, c.n_entries, d.m, k, 1, idx, nullptr, nullptr);
-    return hipGetLastError();
-  }
-  if (cap <= 2 * TK_SEG) {
-    hipLaunchKernelGGL((k_topk_segment<32>), dim3(Q, 1), dim3(TK_THREADS), 0, s, scores, ld, q_seq,
-                       q_pos, c.n_entries, d.m, k, 1, idx, nullptr, nullptr);
-    return hipGetLastError();
-  }
-  const int nseg = (cap + TK_SEG - 1) / TK_SEG;
-  int32_t* cidx = (int32_t*)ws;
-  uint32_t* ckey = (uint32_t*)((char*)ws + (size_t)Q * nseg * k * sizeof(int32_t));
-  hipLaunchKernelGGL((k_topk_segment<16>), dim3(Q, nseg), dim3(TK_THREADS), 0, s, scores, ld,
-                     q_seq, q_pos, c.n_entries, d.m, k, 0, idx, cidx, ckey);
+  const int G = std::max(2, TK_MERGE / k);
+  const size_t lists1 = (size_t)(p.nseg + G - 1) / G;
+  int32_t* bufA_i = (int32_t*)ws;
+  uint32_t* bufA_k = (uint32_t*)(bufA_i + (size_t)Q * p.nseg * k);
+  int32_t* bufB_i = (int32_t*)(bufA_k + (size_t)Q * p.nseg * k);
+  uint32_t* bufB_k = (uint32_t*)(bufB_i + (size_t)Q * lists1 * k);
+  TK_SEG_LAUNCH(4, dim3(Q, p.nseg), 0, idx, bufA_i, bufA_k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  switch (merge_E(nseg * k)) {
-    case 1: hipLaunchKernelGGL((k_topk_merge<1>), dim3(Q), dim3(TK_THREADS), 0, s, cidx, ckey, nseg, k, idx); break;
-    case 2: hipLaunchKernelGGL((k_topk_merge<2>), dim3(Q), dim3(TK_THREADS), 0, s, cidx, ckey, nseg, k, idx); break;
-    case 4: hipLaunchKernelGGL((k_topk_merge<4>), dim3(Q), dim3(TK_THREADS), 0, s, cidx, ckey, nseg, k, idx); break;
-    case 8: hipLaunchKernelGGL((k_topk_merge<8>), dim3(Q), dim3(TK_THREADS), 0, s, cidx, ckey, nseg, k, idx); break;
-    case 16: hipLaunchKernelGGL((k_topk_merge<16>), dim3(Q), dim3(TK_THREADS), 0, s, cidx, ckey, nseg, k, idx); break;
-    case 32: hipLaunchKernelGGL((k_topk_merge<32>), dim3(Q), dim3(TK_THREADS), 0, s, cidx, ckey, nseg, k, idx); break;
-    default: return hipErrorInvalidValue;
+  int lists = p.nseg;
+  const int32_t* in_i = bufA_i;
+  const uint32_t* in_k = bufA_k;
+  bool in_A = true;
+  for (int lev = 0; lev < p.levels; ++lev) {
+    const int direct = (long)lists * k <= TK_MERGE ? 1 : 0;
+    const int groups = direct ? 1 : (lists + G - 1) / G;
+    const int per_group = direct ? lists : G;
+    int32_t* out_i = in_A ? bufB_i : bufA_i;
+    uint32_t* out_k = in_A ? bufB_k : bufA_k;
+    switch (items_E(per_group * k)) {
+      case 1: TK_MERGE_LAUNCH(1, dim3(Q, groups), per_group); break;
+      case 2: TK_MERGE_LAUNCH(2, dim3(Q, groups), per_group); break;
+      case 4: TK_MERGE_LAUNCH(4, dim3(Q, groups), per_group); break;
+      case 8: TK_MERGE_LAUNCH(8, dim3(Q, groups), per_group); break;
+      default: TK_MERGE_LAUNCH(16, dim3(Q, groups), per_group); break;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess || direct) return e;
+    lists = groups;
+    in_i = out_i;
+    in_k = out_k;
+    in_A = !in_A;
   }
   return hipGetLastError();
 }

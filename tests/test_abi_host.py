@@ -99,9 +99,9 @@ def test_null_and_workspace_errors_without_a_device():
     d5 = L.Dims.from_config(synth.config("c5")).struct()
     assert lib.csa_index_topk(ctypes.byref(d5), ctypes.byref(cache), fake, fake, fake, fake, 1, fake,
                               None, fake, 1 << 30, None) == 1
-    # cap beyond what the selection kernels handle for this top_k
-    huge = L._Cache(1, 1 << 24, 128, fake, fake, fake, fake, fake, fake)
-    assert lib.csa_index_topk(ctypes.byref(ds), ctypes.byref(huge), fake, fake, fake, fake, 1, fake,
+    # a top_k larger than one selection workgroup's share is not built
+    dk = L.Dims.from_config(synth.config("c2"), top_k=20000).struct()
+    assert lib.csa_index_topk(ctypes.byref(dk), ctypes.byref(cache), fake, fake, fake, fake, 1, fake,
                               None, fake, 1 << 40, None) == 2
     # forward needs a ring that holds the chunk's window
     assert lib.csa_forward(ctypes.byref(ds), ctypes.byref(w), ctypes.byref(cache), fake, 64, fake,

@@ -478,3 +478,43 @@ def test_c4_prefill_full_size_sampled():
             keys = np.concatenate([g_entries[sel_g], raw_of(R.window_positions(tau, cfg["n_win"]))])
             o_ref = R.attend(q[t], tau, keys, None, sink, od)
         assert_close_q(go[t], o_ref, f"c4 out t={t}")
+
+
+def test_topk_exact_on_crafted_scores():
+    """csa_topk on given scores must equal the oracle's selection exactly (same input bits):
+    heavy ties (integer scores), -0/+0, rows shorter than k, exactly k, k + 1, ragged segment
+    tails, and a row long enough for two merge levels (90001 entries, k = 1024)."""
+    for k, cap in ((1024, 90001), (512, 4096), (8, 37), (512, 33000)):
+        cfg = _qcfg(top_k=k)
+        dims = L.Dims.from_config(cfg)
+        m = cfg["m"]
+        Vs = sorted({0, 1, min(k, cap), min(k + 1, cap), cap // 3, cap - 5, cap})
+        Q = len(Vs) * 3
+        cache = L.Cache(dims, B=1, cap=cap, win_cap=128)
+        cache.n_entries.fill_(cap)
+        rng = np.random.default_rng(k + cap)
+        sc = np.zeros((Q, cap), dtype=np.float32)
+        pos = []
+        for i in range(Q):
+            V = Vs[i // 3]
+            kind = i % 3
+            if kind == 0:
+                sc[i] = rng.standard_normal(cap).astype(np.float32)
+            elif kind == 1:
+                sc[i] = rng.integers(-3, 4, cap).astype(np.float32)
+            else:
+                sc[i] = np.where(rng.random(cap) < 0.5, -0.0, 0.0).astype(np.float32)
+                sc[i, rng.integers(0, cap, 5)] = 1.0
+            pos.append(m * V + (i % m))
+        scores = torch.from_numpy(sc).to(DEV)
+        idx = torch.full((Q, k), -7, dtype=torch.int32, device=DEV)
+        ws = _ws(L.csa_topk_workspace_size(dims, Q, cap))
+        L.csa_topk(dims, cache, _i32([0] * Q), _i32(pos), Q, scores, cap, idx, ws)
+        torch.cuda.synchronize()
+        gi = idx.cpu().numpy()
+        for i in range(Q):
+            V = Vs[i // 3]
+            ref = R.topk(sc[i, :V].astype(np.float64), k)
+            got = gi[i][gi[i] >= 0]
+            assert np.array_equal(got, ref), f"k={k} cap={cap} V={V} kind={i % 3}"
+            assert np.all(gi[i][len(got):] == -1)
