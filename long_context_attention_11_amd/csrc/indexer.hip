@@ -41,6 +41,7 @@ __global__ __launch_bounds__(256) void k_indexer_bf16(
     const uint8_t* __restrict__ ki, int cap, const int32_t* __restrict__ n_entries, int m,
     float* __restrict__ scores, int64_t ld, int chunk) {
   constexpr int HT = NH / 16;
+  constexpr int DEPTH = 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int q0 = blockIdx.x * QPW;
@@ -54,52 +55,72 @@ __global__ __launch_bounds__(256) void k_indexer_bf16(
     V[qq] = q < Q ? max(0, min(q_pos[q] / m, nent)) : 0;
     Vmax = max(Vmax, V[qq]);
   }
+  // this wave's entries: tiles of 16 dealt round-robin over the 4 waves of the chunk
   const int c_lo = blockIdx.y * chunk;
   const int c_hi = min(c_lo + chunk, Vmax);
   if (c_lo >= c_hi) return;
-  const int per_wave = (chunk / 4 + 15) & ~15;
-  const int w_lo = c_lo + wave * per_wave;
-  const int w_hi = min(c_hi, w_lo + per_wave);
-  if (w_lo >= w_hi) return;
+  const int w_lo = c_lo + 16 * wave;
+  if (w_lo >= c_hi) return;
+  const int stride = 64;  // 4 waves x 16 entries
 
-  // A operands (q^I) and head weights, per query, kept in registers.
-  bf16x8 A[QPW][HT][4];
-  float W[QPW][HT][4];
+  const uint8_t* kbase = ki + (size_t)seq * cap * IX_CI + g * 32;
+  // Prologue: the query operands (q^I rows, head weights) and the first DEPTH tiles of keys
+  // are all requested before anything waits, so their latencies overlap.  The ring holds
+  // DEPTH tiles (16 entries x 128 B per wave, 32 B per lane); waits count outstanding loads
+  // in issue order, so tile 0 is issued first among the keys.
+  uint4 araw[QPW][HT][2];
+  uint2 wraw[QPW][HT];
 #pragma unroll
   for (int qq = 0; qq < QPW; ++qq) {
     const int q = min(q0 + qq, Q - 1);
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const uint8_t* src = qI + ((size_t)q * NH + ht * 16 + col) * IX_CI + g * 32;
-      uint4 lo = *reinterpret_cast<const uint4*>(src);
-      uint4 hi = *reinterpret_cast<const uint4*>(src + 16);
-      e4m3x32_to_ops(lo, hi, A[qq][ht]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) W[qq][ht][e] = bf16_bits_to_f32(wI[(size_t)q * NH + ht * 16 + 4 * g + e]);
+      araw[qq][ht][0] = *reinterpret_cast<const uint4*>(src);
+      araw[qq][ht][1] = *reinterpret_cast<const uint4*>(src + 16);
+      wraw[qq][ht] = *reinterpret_cast<const uint2*>(wI + (size_t)q * NH + ht * 16 + 4 * g);
     }
   }
-  const uint8_t* kbase = ki + (size_t)seq * cap * IX_CI + g * 32;
-  // Register ring of DEPTH tiles: the raw bytes of the next DEPTH tiles are in flight while
-  // one computes (each tile: 16 entries x 128 B per wave, 32 B per lane).
-  constexpr int DEPTH = 4;
   uint4 rlo[DEPTH], rhi[DEPTH];
   auto load_tile = [&](int s0, uint4& lo, uint4& hi) {
-    const int s = min(s0 + col, w_hi - 1);
+    const int s = min(s0 + col, c_hi - 1);
     const uint8_t* src = kbase + (size_t)s * IX_CI;
-    lo = load_stream16(src);
-    hi = load_stream16(src + 16);
+    lo = *reinterpret_cast<const uint4*>(src);
+    hi = *reinterpret_cast<const uint4*>(src + 16);
   };
 #pragma unroll
-  for (int i = 0; i < DEPTH; ++i) load_tile(w_lo + 16 * i, rlo[i], rhi[i]);
-  for (int base = w_lo; base < w_hi; base += 16 * DEPTH) {
+  for (int i = 0; i < DEPTH; ++i) load_tile(w_lo + stride * i, rlo[i], rhi[i]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  bf16x8 A[QPW][HT][4];
+  float W[QPW][HT][4];
+#pragma unroll
+  for (int qq = 0; qq < QPW; ++qq) {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      e4m3x32_to_ops(araw[qq][ht][0], araw[qq][ht][1], A[qq][ht]);
+      const uint2 w4 = wraw[qq][ht];
+      W[qq][ht][0] = bf16_bits_to_f32(w4.x & 0xffffu);
+      W[qq][ht][1] = bf16_bits_to_f32(w4.x >> 16);
+      W[qq][ht][2] = bf16_bits_to_f32(w4.y & 0xffffu);
+      W[qq][ht][3] = bf16_bits_to_f32(w4.y >> 16);
+    }
+  }
+  // Straight-line ring: every wave runs whole rounds of DEPTH tiles.  Loads past the end are
+  // clamped to the last entry (same cache line for every lane) and their results discarded,
+  // so no load is conditional and the loads of the next round stay in flight while this
+  // round's tiles are multiplied.
+  const int rounds = (c_hi - w_lo + stride * DEPTH - 1) / (stride * DEPTH);
+  int it = 0;
+  do {  // rounds >= 1 since w_lo < c_hi
+    const int base = w_lo + it * stride * DEPTH;
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) {
-      const int s0 = base + 16 * i;
-      if (s0 >= w_hi) break;
-      const uint4 clo = rlo[i], chi = rhi[i];
-      if (s0 + 16 * DEPTH < w_hi) load_tile(s0 + 16 * DEPTH, rlo[i], rhi[i]);
-      bf16x8 B[4];
-      e4m3x32_to_ops(clo, chi, B);
+      const int s0 = base + stride * i;
+      // widen the tile first, then reuse its registers for the load of the next round
+      bf16x8 Bop[4];
+      e4m3x32_to_ops(rlo[i], rhi[i], Bop);
+      load_tile(s0 + stride * DEPTH, rlo[i], rhi[i]);
 #pragma unroll
       for (int qq = 0; qq < QPW; ++qq) {
         float part = 0.f;
@@ -108,17 +129,17 @@ __global__ __launch_bounds__(256) void k_indexer_bf16(
           f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[qq][ht][ks], B[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[qq][ht][ks], Bop[ks], acc, 0, 0, 0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) part = fmaf(W[qq][ht][e], fmaxf(acc[e], 0.f), part);
         }
         part += __shfl_xor(part, 16, 64);
         part += __shfl_xor(part, 32, 64);
         const int s = s0 + col;
-        if (g == 0 && s < V[qq] && s < w_hi) scores[(size_t)(q0 + qq) * ld + s] = part;
+        if (g == 0 && s < min(V[qq], c_hi)) scores[(size_t)(q0 + qq) * ld + s] = part;
       }
     }
-  }
+  } while (++it < rounds);
 }
 
 // float32 indexer (fp32 formats): one thread per (query, entry).
@@ -156,8 +177,12 @@ hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI,
                        d.c_I, scores, ld);
     return hipGetLastError();
   }
-  // E4M3 keys: bf16 MFMA.  One query per group; entry chunks sized to fill the GPU.
-  const int chunk = 512;
+  // E4M3 keys: bf16 MFMA.  One query per group; entry chunks sized so that the grid is about
+  // two workgroups (8 waves) per CU, each wave streaming a long run of tiles.
+  const int target_wgs = 512;
+  const int per_q = std::max(1, target_wgs / std::max(Q, 1));
+  int chunk = (c.cap + per_q - 1) / per_q;
+  chunk = std::max(256, (chunk + 255) / 256 * 256);
   dim3 grid(Q, (c.cap + chunk - 1) / chunk);
   switch (d.n_hI) {
     case 64:
