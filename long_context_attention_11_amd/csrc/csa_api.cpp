@@ -216,14 +216,15 @@ int csa_compress(const csa_dims* dims, const csa_weights* w, const csa_cache* ca
 
 static int index_topk_impl(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
                            const int32_t* q_seq, const int32_t* q_pos, int32_t Q, int32_t* idx_out,
-                           float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+                           float* scores_out, void* ws, size_t ws_bytes, bool tiled,
+                           hipStream_t stream) {
   const size_t sc_bytes = scores_out ? 0 : align_up((size_t)Q * c.cap * sizeof(float), 256);
   const size_t need = sc_bytes + topk_workspace_bytes(d, Q, c.cap);
   if (need && (!ws || ws_bytes < need))
     return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "index_topk needs " + std::to_string(need) + " bytes of workspace");
   float* scores = scores_out ? scores_out : (float*)ws;
   void* tws = (char*)ws + sc_bytes;
-  hipError_t e = launch_indexer(d, c, qI, w, q_seq, q_pos, Q, scores, c.cap, stream);
+  hipError_t e = launch_indexer(d, c, qI, w, q_seq, q_pos, Q, scores, c.cap, tiled, stream);
   if (e != hipSuccess) return hip_fail(e, "indexer launch");
   e = launch_topk(d, c, q_seq, q_pos, Q, scores, c.cap, idx_out, tws, stream);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
@@ -246,7 +247,7 @@ int csa_index_topk(const csa_dims* dims, const csa_cache* cache, const void* qI,
     return fail(CSA_ERR_UNSUPPORTED, "cap exceeds the entries the top-k kernels handle for this top_k (" +
                                          std::to_string(topk_max_visible(d)) + ")");
   return index_topk_impl(d, *cache, qI, w, q_seq, q_pos, Q, idx_out, scores_out, ws, ws_bytes,
-                         stream);
+                         false, stream);
 }
 
 int csa_index_scores(const csa_dims* dims, const csa_cache* cache, const void* qI, const void* w,
@@ -261,7 +262,7 @@ int csa_index_scores(const csa_dims* dims, const csa_cache* cache, const void* q
     return fail(CSA_ERR_INVALID_ARGUMENT, "qI, w, q_seq, q_pos and scores must be set");
   if (Q < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "Q must be >= 1");
   if (ld < cache->cap) return fail(CSA_ERR_INVALID_ARGUMENT, "ld must be >= cap");
-  hipError_t e = launch_indexer(*dims, *cache, qI, w, q_seq, q_pos, Q, scores, ld, stream);
+  hipError_t e = launch_indexer(*dims, *cache, qI, w, q_seq, q_pos, Q, scores, ld, false, stream);
   if (e != hipSuccess) return hip_fail(e, "indexer launch");
   return CSA_OK;
 }
@@ -364,13 +365,17 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
     // largest chunk whose scores and candidates fit
     int32_t Qc = Qn;
     while (Qc > 1 && index_ws(d, Qc, cache->cap) > phase_bytes) Qc = (Qc + 1) / 2;
+    // Query q is token q % T of sequence q / T.  With T and the chunk a multiple of 16, every
+    // aligned group of 16 queries of a chunk is one sequence and the indexer can tile them.
+    if (Qc >= 16) Qc -= Qc % 16;
+    const bool tiled = T % 16 == 0 && Qc % 16 == 0;
     const size_t qI_row = (size_t)d.n_hI * d.c_I * (d.idx_fmt == CSA_FMT_F32 ? 4 : 1);
     const size_t w_row = (size_t)d.n_hI * (d.act_fmt == CSA_FMT_F32 ? 4 : 2);
     for (int32_t q0 = 0; q0 < Qn; q0 += Qc) {
       const int32_t n = std::min(Qc, Qn - q0);
       st = index_topk_impl(d, *cache, (const char*)qI + q0 * qI_row, (const char*)wI + q0 * w_row,
                            q_seq + q0, q_pos + q0, n, idx + (size_t)q0 * d.top_k, nullptr, phase_ws,
-                           phase_bytes, stream);
+                           phase_bytes, tiled, stream);
       if (st) return st;
     }
   }

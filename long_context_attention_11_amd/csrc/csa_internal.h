@@ -140,9 +140,11 @@ hipError_t launch_fold(const csa_dims& d, const csa_weights& w, const csa_cache&
 hipError_t launch_state_update(const csa_dims& d, const csa_cache& c, int32_t T,
                                const int32_t* pos0, const float* P, int32_t ksplit,
                                hipStream_t s);
+// `tiled`: every aligned group of 16 queries (0-15, 16-31, ...) belongs to one sequence, so
+// the prefill-shaped kernel may share key tiles between them.
 hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
                           const int32_t* q_seq, const int32_t* q_pos, int32_t Q, float* scores,
-                          int64_t ld_scores, hipStream_t s);
+                          int64_t ld_scores, bool tiled, hipStream_t s);
 hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
                        const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld_scores,
                        int32_t* idx, void* ws, hipStream_t s);

@@ -133,13 +133,170 @@ __global__ __launch_bounds__(256) void k_indexer_bf16(
 #pragma unroll
           for (int e = 0; e < 4; ++e) part = fmaf(W[qq][ht][e], fmaxf(acc[e], 0.f), part);
         }
-        part += __shfl_xor(part, 16, 64);
+        // lane groups summed as (g + g^2) + (g^1 + g^3), the order the tiled kernel uses
         part += __shfl_xor(part, 32, 64);
+        part += __shfl_xor(part, 16, 64);
         const int s = s0 + col;
         if (g == 0 && s < min(V[qq], c_hi)) scores[(size_t)(q0 + qq) * ld + s] = part;
       }
     }
   } while (++it < rounds);
+}
+
+// Prefill-shaped indexer: a workgroup of 8 waves scores IT_Q = 16 queries of ONE sequence
+// (2 per wave) against that sequence's entries [e_lo, e_hi).  Keys are shared by every query
+// of the tile, so they are staged once through LDS (64-entry stages, double buffered, one
+// 16-byte load per thread per stage, widened to bf16 once while staging) instead of being
+// fetched and widened per query.  Each wave keeps its two queries' q^I (64 heads, widened to
+// bf16) in registers; per 16-entry tile it reads the keys from LDS and runs 2 x 4 head tiles
+// x 4 K-steps of bf16 MFMA, with the same operand mapping and epilogue order as
+// k_indexer_bf16 (so the scores are identical).
+constexpr int IT_Q = 16;        // queries per workgroup
+constexpr int IT_STAGE = 64;    // entries per LDS stage
+constexpr int IT_LD = 272;      // LDS bytes per entry row: 128 dims in bf16 + 16 pad (spreads the banks)
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_indexer_tile(
+    const uint8_t* __restrict__ qI, const uint16_t* __restrict__ wI,
+    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int Q,
+    const uint8_t* __restrict__ ki, int cap, const int32_t* __restrict__ n_entries, int m,
+    float* __restrict__ scores, int64_t ld, int chunk) {
+  constexpr int NH = 64, HT = NH / 16;
+  __shared__ __align__(16) uint8_t kbuf[2][IT_STAGE * IT_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int qt0 = blockIdx.x * IT_Q;
+  const int seq = q_seq[qt0];
+  const int nent = n_entries[seq];
+  // visible entries of the tile's queries (clamped duplicates past Q store nothing)
+  int Vmax = 0;
+  for (int i = 0; i < IT_Q; ++i) {
+    const int q = min(qt0 + i, Q - 1);
+    Vmax = max(Vmax, max(0, min(q_pos[q] / m, nent)));
+  }
+  const int e_lo = blockIdx.y * chunk;
+  const int e_hi = min(e_lo + chunk, Vmax);
+  if (e_lo >= e_hi) return;  // uniform over the workgroup
+
+  int V[2];
+  bf16x8 A[2][HT][4];
+  float W[2][HT][4];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int qr = qt0 + 2 * wave + qq;
+    const int q = min(qr, Q - 1);
+    V[qq] = qr < Q ? max(0, min(q_pos[q] / m, nent)) : 0;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const uint8_t* src = qI + ((size_t)q * NH + ht * 16 + col) * IX_CI + g * 32;
+      e4m3x32_to_ops(*reinterpret_cast<const uint4*>(src), *reinterpret_cast<const uint4*>(src + 16),
+                     A[qq][ht]);
+      const uint2 w4 = *reinterpret_cast<const uint2*>(wI + (size_t)q * NH + ht * 16 + 4 * g);
+      W[qq][ht][0] = bf16_bits_to_f32(w4.x & 0xffffu);
+      W[qq][ht][1] = bf16_bits_to_f32(w4.x >> 16);
+      W[qq][ht][2] = bf16_bits_to_f32(w4.y & 0xffffu);
+      W[qq][ht][3] = bf16_bits_to_f32(w4.y >> 16);
+    }
+  }
+
+  // stage loader: thread t moves dims 8p .. 8p+7 and 64+8p .. 64+8p+7 (p = t % 8) of entry
+  // t / 8 of the stage, widened to bf16; the 8 threads of an entry write two contiguous
+  // 128-byte runs, which keeps the LDS writes free of bank conflicts
+  const uint8_t* kseq = ki + (size_t)seq * cap * IX_CI;
+  const int le = tid >> 3, lp = (tid & 7) * 8;
+  constexpr int RPT = IT_STAGE / 64;  // entries per thread per stage
+  auto gload = [&](int st, uint4 (&v)[RPT]) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int e = min(e_lo + st * IT_STAGE + 64 * r + le, e_hi - 1);
+      const uint8_t* src = kseq + (size_t)e * IX_CI + lp;
+      const uint2 a = *reinterpret_cast<const uint2*>(src);
+      const uint2 b = *reinterpret_cast<const uint2*>(src + 64);
+      v[r] = make_uint4(a.x, a.y, b.x, b.y);
+    }
+  };
+  auto lstore = [&](int buf, const uint4 (&v)[RPT]) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      uint32_t b[8];
+      e4m3x4_to_bf16x4(v[r].x, b[0], b[1]);
+      e4m3x4_to_bf16x4(v[r].y, b[2], b[3]);
+      e4m3x4_to_bf16x4(v[r].z, b[4], b[5]);
+      e4m3x4_to_bf16x4(v[r].w, b[6], b[7]);
+      uint8_t* dst = &kbuf[buf][(64 * r + le) * IT_LD + 2 * lp];
+      *reinterpret_cast<uint4*>(dst) = make_uint4(b[0], b[1], b[2], b[3]);
+      *reinterpret_cast<uint4*>(dst + 128) = make_uint4(b[4], b[5], b[6], b[7]);
+    }
+  };
+  const int nst = (e_hi - e_lo + IT_STAGE - 1) / IT_STAGE;
+  uint4 nxt[RPT];
+  gload(0, nxt);
+  lstore(0, nxt);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    if (st + 1 < nst) gload(st + 1, nxt);
+#pragma unroll
+    for (int sub = 0; sub < RPT; ++sub) {
+      const uint8_t* kb = kbuf[st & 1] + sub * 64 * IT_LD;
+      // per lane partial head sums: part[t][qq] for tile t of the stage, query qq (the lane's
+      // 4 heads of each head tile); reduced over the 4 lane groups once per 64 entries
+      float part[4][2];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        // dims g*32 + ks*8 .. +7 (the mapping e4m3x32_to_ops gives the q^I operands)
+        const uint8_t* row = kb + (t * 16 + col) * IT_LD + g * 64;
+        bf16x8 Bop[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) Bop[ks] = *reinterpret_cast<const bf16x8*>(row + 16 * ks);
+        // K-step outermost: the 8 accumulators are independent, so consecutive MFMAs never
+        // wait on each other's results
+        f32x4 acc[2][HT];
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) acc[qq][ht] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht)
+              acc[qq][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[qq][ht][ks], Bop[ks], acc[qq][ht], 0, 0, 0);
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          float p = 0.f;
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p = fmaf(W[qq][ht][e], fmaxf(acc[qq][ht][e], 0.f), p);
+          part[t][qq] = p;
+        }
+      }
+      // Reduce-scatter over the lane groups g = lane >> 4: after the exchange with lane ^ 32
+      // a lane keeps tiles {0,1} (g < 2) or {2,3}; after lane ^ 16 it keeps tile g.  Lane
+      // (col, g) then holds entry t*16 + col of tile t = g, summed over all 64 heads, and the
+      // 64 lanes store one contiguous run of 64 scores per query.
+      const bool hi2 = g >= 2, odd = g & 1;
+      float r1[2][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          const float keep = hi2 ? part[2 + j][qq] : part[j][qq];
+          const float send = hi2 ? part[j][qq] : part[2 + j][qq];
+          r1[j][qq] = keep + __shfl_xor(send, 32, 64);
+        }
+      const int s = e_lo + st * IT_STAGE + sub * 64 + g * 16 + col;
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const float keep = odd ? r1[1][qq] : r1[0][qq];
+        const float send = odd ? r1[0][qq] : r1[1][qq];
+        const float total = keep + __shfl_xor(send, 16, 64);
+        if (s < min(V[qq], e_hi)) scores[(size_t)(qt0 + 2 * wave + qq) * ld + s] = total;
+      }
+    }
+    if (st + 1 < nst) lstore((st + 1) & 1, nxt);
+    __syncthreads();
+  }
 }
 
 // float32 indexer (fp32 formats): one thread per (query, entry).
@@ -169,7 +326,19 @@ __global__ __launch_bounds__(256) void k_indexer_f32(
 
 hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
                           const int32_t* q_seq, const int32_t* q_pos, int32_t Q, float* scores,
-                          int64_t ld, hipStream_t s) {
+                          int64_t ld, bool tiled, hipStream_t s) {
+  if (tiled && d.idx_fmt == CSA_FMT_E4M3 && d.n_hI == 64 && Q >= IT_Q) {
+    // every aligned group of IT_Q queries belongs to one sequence (the caller guarantees it)
+    const int ntile = (Q + IT_Q - 1) / IT_Q;
+    const int nsplit = std::max(1, (256 + ntile - 1) / ntile);
+    int chunk = (c.cap + nsplit - 1) / nsplit;
+    chunk = (chunk + IT_STAGE - 1) / IT_STAGE * IT_STAGE;
+    dim3 grid(ntile, (c.cap + chunk - 1) / chunk);
+    hipLaunchKernelGGL(k_indexer_tile, grid, dim3(512), 0, s, (const uint8_t*)qI,
+                       (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki, c.cap,
+                       c.n_entries, d.m, scores, ld, chunk);
+    return hipGetLastError();
+  }
   if (d.idx_fmt == CSA_FMT_F32) {
     dim3 grid((c.cap + 255) / 256, Q);
     hipLaunchKernelGGL(k_indexer_f32, grid, dim3(256), 0, s, (const float*)qI, (const float*)w,
