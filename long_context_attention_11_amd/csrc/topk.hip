@@ -1,149 +1,301 @@
 // Per-query top-k selection for gfx950 (reading notes "DeepSeekV4技术报告阅读笔记" §2.3.2
 // eq. 17: keep the entries whose index score is among the k largest).
 //
-// Keys are the scores mapped to order-preserving uint32 (-0 counts as +0).  The selection is
-// exact: the k-th largest key T is found by a radix select (digits of 11, 11 and 10 bits,
-// LDS histograms), every key > T is taken, and of the keys == T the lowest indices fill the
-// remaining slots.  Output indices are in increasing order, padded with -1.
+// Keys are the scores mapped to order-preserving uint32 (-0 counts as +0); scores are
+// finite.  The selection is exact: equal scores go to the lower index, and the output holds
+// the chosen indices in increasing order, padded with -1.
 //
-// One workgroup of 1024 threads holds up to 1024*E items in registers, thread t holding a
-// contiguous run, so thread order is index order and in-order compaction is one block scan.
-// Rows longer than 4096 are cut into segments of 4096; each segment keeps its own top-k (a
-// superset of its share of the global top-k under the same total order).  Merge levels then
-// take groups of candidate lists (up to 16384 candidates per workgroup) down to one list.
-// Every list stays in index order, so the final one is the answer, already sorted.
+// One workgroup of 1024 threads selects from up to 1024*E items held in registers, thread t
+// holding the contiguous run [t*E, t*E + E), so thread order is index order:
+//   1. a block min/max of the scores, then a 2048-bin histogram linear in the score over
+//      [min, max]; the bin holding the k-th largest is found by one wave, and every item in
+//      a higher bin is taken.  Linear bins spread the scores over many bins, so the bin
+//      that is left (the "window") is small and the LDS atomics rarely collide;
+//   2. inside the window, radix passes over the keys (offset by the window's smallest key,
+//      11 bits at a time) narrow it until it is a single key value or is taken whole;
+//   3. one packed block scan gives every taken item its output slot: all items above the
+//      window, and the `need` lowest-index items of the window.
+// Rows of up to 8192 scores take one workgroup and one launch.  Longer rows are cut into
+// 8192-score segments; each keeps its own top k (a superset of its share of the answer
+// under the same total order), and a merge level selects from the candidate lists, which
+// stay in index order.
 #include "csa_internal.h"
 
 namespace csa {
 namespace {
 
 constexpr int TK_THREADS = 1024;
-constexpr int TK_DIRECT_MAX = 4096;  // rows up to this length: one workgroup, one launch
-constexpr int TK_SEG0 = 4096;        // scores per level-0 segment (E = 4)
-constexpr int TK_MERGE = 16384;      // candidates one merge workgroup takes (E <= 16)
+constexpr int TK_WAVES = TK_THREADS / 64;
+constexpr int TK_BINS = 2048;
+constexpr int TK_SEG = 8192;     // scores per segment (E = 8)
+constexpr int TK_MERGE = 8192;   // candidates one merge workgroup takes (E <= 8)
 
 struct TopkShared {
-  int hist[2048];
-  int scan[32];
-  int sel_digit;
-  int sel_gt;
+  int hist[2][TK_BINS];
+  int red_n[TK_WAVES];
+  float red_lo[TK_WAVES], red_hi[TK_WAVES];
+  uint32_t red_klo[TK_WAVES], red_khi[TK_WAVES];
+  int scan[TK_WAVES];
+  int sel_bin, sel_above;
 };
 
-// Exclusive scan of one int per thread across the 1024-thread block; returns the exclusive
-// prefix and writes the total to *total.
-__device__ int block_excl_scan(int v, int* scan, int* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  __syncthreads();
-  if (lane == 63) scan[w] = x;
-  __syncthreads();
-  if (w == 0) {
-    int s = lane < 16 ? scan[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      int y = __shfl_up(s, o, 64);
-      if (lane >= o) s += y;
-    }
-    if (lane < 16) scan[16 + lane] = s;
-  }
-  __syncthreads();
-  const int before = w > 0 ? scan[16 + w - 1] : 0;
-  *total = scan[16 + 15];
-  return before + x - v;
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Select the top k of the valid items held by the block; write them in index order to
-// out_idx[0..) (and out_key if non-null); return the count written (min(k, valid)).
-template <int E>
-__device__ int block_select(const uint32_t (&key)[E], const int (&idx)[E], const bool (&valid)[E],
-                            int k, TopkShared& sh, int* out_idx, uint32_t* out_key) {
-  int nv_local = 0;
+__device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
-  for (int i = 0; i < E; ++i) nv_local += valid[i] ? 1 : 0;
-  int nvalid;
-  (void)block_excl_scan(nv_local, sh.scan, &nvalid);
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_min_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
 
-  uint32_t T = 0u;
-  int need = 0;
-  const bool take_all = nvalid <= k;
-  if (!take_all) {
-    uint32_t prefix = 0u, pmask = 0u;
-    int remaining = k;
-    const int shifts[3] = {21, 10, 0};
-    const int widths[3] = {11, 11, 10};
+// Cross-wave reductions of per-wave slots: lane j reads slot j & 15, then 16 lanes combine.
+__device__ __forceinline__ int slots_sum(const int* v) {
+  int x = v[threadIdx.x & 15];
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const int sh_ = shifts[p], nb = 1 << widths[p];
-      const uint32_t dmask = (uint32_t)nb - 1u;
-      for (int b = threadIdx.x; b < 2048; b += TK_THREADS) sh.hist[b] = 0;
-      __syncthreads();
+  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ float slots_min(const float* v) {
+  float x = v[threadIdx.x & 15];
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x = fminf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float slots_max(const float* v) {
+  float x = v[threadIdx.x & 15];
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ uint32_t slots_min_u(const uint32_t* v) {
+  uint32_t x = v[threadIdx.x & 15];
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o, 64));
+  return x;
+}
+__device__ __forceinline__ uint32_t slots_max_u(const uint32_t* v) {
+  uint32_t x = v[threadIdx.x & 15];
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o, 64));
+  return x;
+}
+
+// Wave 0: find the bin d with S(d) >= rem > S(d + 1), S(d) = number of items in bins >= d,
+// and publish d and S(d + 1).  Requires 1 <= rem <= S(0).  Lane l first sums bins
+// 32l .. 32l + 31 (read in a staggered order so the lanes spread over the LDS banks); a
+// suffix scan over the lanes finds the lane whose range holds d, and 32 lanes then scan
+// that range in parallel.
+__device__ void find_bin(const int* H, int rem, TopkShared& sh) {
+  const int lane = threadIdx.x & 63;
+  int own = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) own += H[32 * lane + ((j + lane) & 31)];
+  int suf = own;  // inclusive suffix sum over lanes >= lane
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_down(suf, o, 64);
+    if (lane + o < 64) suf += y;
+  }
+  const int after = suf - own;  // items in bins of higher lanes
+  const unsigned long long hit = __ballot(suf >= rem && after < rem);
+  const int L = __ffsll(hit) - 1;  // exactly one lane
+  const int base = __shfl(after, L, 64);
+  const int j = lane & 31;
+  const int h = H[32 * L + j];
+  int s = h;  // items in bins 32L + j .. 32L + 31
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) {
+    const int y = __shfl_down(s, o, 64);
+    if (j + o < 32) s += y;
+  }
+  if (lane < 32 && base + s >= rem && base + s - h < rem) {
+    sh.sel_bin = 32 * L + j;
+    sh.sel_above = base + s - h;
+  }
+}
+
+// The items a thread holds: E keys with their indices.  A row segment's indices are the
+// contiguous run first .. first + E - 1 (valid below V); a merge's come from the lists
+// (valid when >= 0).
+template <int E>
+struct RunItems {
+  uint32_t key[E];
+  int first, V;
+  __device__ int idx(int i) const { return first + i; }
+  __device__ bool valid(int i) const { return first + i < V; }
+};
+template <int E>
+struct ListItems {
+  uint32_t key[E];
+  int id[E];
+  __device__ int idx(int i) const { return id[i]; }
+  __device__ bool valid(int i) const { return id[i] >= 0; }
+};
+
+// Select the k largest valid items of the block (equal keys: lower index first) and write
+// their indices in index order to out_idx (keys to out_key when non-null).  Returns the
+// number written, min(k, number of valid items).
+template <int E, class Items>
+__device__ int select_topk(const Items& it, int k, TopkShared& sh, int* out_idx, uint32_t* out_key) {
+  const uint32_t (&key)[E] = it.key;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+  // (a) valid count and score range; both histograms cleared
+  int nv = 0;
+  float fmn = INFINITY, fmx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < E; ++i)
+    if (it.valid(i)) {
+      ++nv;
+      const float f = key_score(key[i]);
+      fmn = fminf(fmn, f);
+      fmx = fmaxf(fmx, f);
+    }
+  nv = wave_sum_i(nv);
+  fmn = wave_min_f(fmn);
+  fmx = wave_max_f(fmx);
+  if (lane == 0) { sh.red_n[w] = nv; sh.red_lo[w] = fmn; sh.red_hi[w] = fmx; }
+  for (int b = tid; b < TK_BINS; b += TK_THREADS) { sh.hist[0][b] = 0; sh.hist[1][b] = 0; }
+  __syncthreads();
+  const int nvalid = slots_sum(sh.red_n);
+  fmn = slots_min(sh.red_lo);
+  fmx = slots_max(sh.red_hi);
+  const bool take_all = nvalid <= k;
+
+  // (b) one pass over bins linear in the score; (c) radix passes inside the window.  Each
+  // item's bin is computed once and kept packed, two 16-bit bins per register.
+  const float range = fmx - fmn;
+  const float scale = (range > 0.f && range < INFINITY) ? (float)TK_BINS / range : 0.f;
+  constexpr int NB = (E + 1) / 2;
+  uint32_t bins[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) bins[j] = 0u;
+  auto bin_of = [&](int i) { return (int)((bins[i >> 1] >> (16 * (i & 1))) & 0xffffu); };
+  int wbin = TK_BINS;             // window bin (TK_BINS: no window, every valid item taken)
+  uint32_t lo = 0u, hi = ~0u;     // key range of the window inside its bin
+  int need = 0;                   // items taken from the window, lowest index first
+  if (!take_all) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int b = min(TK_BINS - 1, (int)((key_score(key[i]) - fmn) * scale));
+      bins[i >> 1] |= (uint32_t)b << (16 * (i & 1));
+      if (it.valid(i)) atomicAdd(&sh.hist[0][b], 1);
+    }
+    __syncthreads();
+    if (w == 0) find_bin(sh.hist[0], k, sh);
+    __syncthreads();
+    wbin = sh.sel_bin;
+    int rem = k - sh.sel_above;
+    int nwin = sh.hist[0][wbin];
+    uint32_t kmn = ~0u, kmx = 0u;
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      if (it.valid(i) && bin_of(i) == wbin) { kmn = min(kmn, key[i]); kmx = max(kmx, key[i]); }
+    kmn = wave_min_u(kmn);
+    kmx = wave_max_u(kmx);
+    if (lane == 0) { sh.red_klo[w] = kmn; sh.red_khi[w] = kmx; }
+    __syncthreads();
+    lo = slots_min_u(sh.red_klo);
+    hi = slots_max_u(sh.red_khi);
+    // Histogram p uses hist[p & 1]; the other one is cleared while wave 0 searches, after
+    // every thread has read what it needed from it.  At most 3 passes: each one takes 11
+    // bits off the span of the window.
+    int p = 1;
+    while (lo != hi && rem != nwin) {  // uniform: every operand comes from LDS
+      const int shift = max(0, 32 - __clz(hi - lo) - 11);
+      int* H = sh.hist[p & 1];
 #pragma unroll
       for (int i = 0; i < E; ++i)
-        if (valid[i] && (key[i] & pmask) == prefix) atomicAdd(&sh.hist[(key[i] >> sh_) & dmask], 1);
+        if (it.valid(i) && bin_of(i) == wbin && key[i] >= lo && key[i] <= hi)
+          atomicAdd(&H[(key[i] - lo) >> shift], 1);
       __syncthreads();
-      // suffix counts: S(d) = #items with digit >= d.  Thread t owns digits 2t, 2t+1.
-      const int d0 = 2 * threadIdx.x;
-      int h0 = d0 < nb ? sh.hist[d0] : 0, h1 = d0 + 1 < nb ? sh.hist[d0 + 1] : 0;
-      int tot;
-      int ex = block_excl_scan(h0 + h1, sh.scan, &tot);
-      const int S0 = tot - ex;  // digits >= d0
-      const int S1 = S0 - h0;   // digits >= d0 + 1
-      const int S2 = S1 - h1;   // digits >= d0 + 2
-      if (d0 < nb) {
-        if (S0 >= remaining && S1 < remaining) { sh.sel_digit = d0; sh.sel_gt = S1; }
-        if (d0 + 1 < nb && S1 >= remaining && S2 < remaining) { sh.sel_digit = d0 + 1; sh.sel_gt = S2; }
+      if (w == 0) {
+        find_bin(H, rem, sh);
+      } else {
+        int* other = sh.hist[(p + 1) & 1];
+        for (int b = tid - 64; b < TK_BINS; b += TK_THREADS - 64) other[b] = 0;
       }
       __syncthreads();
-      const int dsel = sh.sel_digit;
-      remaining -= sh.sel_gt;
-      prefix |= (uint32_t)dsel << sh_;
-      pmask |= dmask << sh_;
-      __syncthreads();
+      const int d = sh.sel_bin;
+      rem -= sh.sel_above;
+      nwin = H[d];
+      const uint32_t nlo = lo + ((uint32_t)d << shift);
+      hi = min(hi, nlo + ((1u << shift) - 1u));
+      lo = nlo;
+      ++p;
     }
-    T = prefix;
-    need = remaining;  // how many items equal to T are taken (lowest indices first)
+    need = rem;
   }
-  int eq_local = 0;
-  if (!take_all) {
-#pragma unroll
-    for (int i = 0; i < E; ++i) eq_local += (valid[i] && key[i] == T) ? 1 : 0;
-  }
-  int eq_total;
-  int eq_before = block_excl_scan(eq_local, sh.scan, &eq_total);
-  bool sel[E];
-  int nsel = 0;
+
+  // (d) output slots: above-window items, then the window's lowest-index `need` items
+  auto klass = [&](int i) {  // 2: above the window, 1: in the window, 0: not taken
+    if (!it.valid(i)) return 0;
+    if (take_all) return 2;
+    const int b = bin_of(i);
+    if (b > wbin || (b == wbin && key[i] > hi)) return 2;
+    return (b == wbin && key[i] >= lo) ? 1 : 0;
+  };
+  int gt = 0, eq = 0;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    bool s;
-    if (take_all) {
-      s = valid[i];
-    } else if (valid[i] && key[i] > T) {
-      s = true;
-    } else if (valid[i] && key[i] == T) {
-      s = eq_before < need;
-      ++eq_before;
-    } else {
-      s = false;
-    }
-    sel[i] = s;
-    nsel += s ? 1 : 0;
+    const int c = klass(i);
+    gt += c == 2 ? 1 : 0;
+    eq += c == 1 ? 1 : 0;
   }
-  int total;
-  int pos = block_excl_scan(nsel, sh.scan, &total);
+  // one exclusive block scan of (gt << 16 | eq); block totals stay below 65536
+  int x = (gt << 16) | eq;
+  const int own = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh.scan[w] = x;
+  __syncthreads();
+  int before = (threadIdx.x & 15) < w ? sh.scan[threadIdx.x & 15] : 0;  // waves ahead of this one
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) before += __shfl_xor(before, o, 64);
+  const int ex = x - own + before;
+  int gt_before = ex >> 16, eq_before = ex & 0xffff;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    if (sel[i]) {
-      out_idx[pos] = idx[i];
+    const int c = klass(i);
+    if (c == 2) {
+      const int pos = gt_before + min(eq_before, need);
+      out_idx[pos] = it.idx(i);
       if (out_key) out_key[pos] = key[i];
-      ++pos;
+      ++gt_before;
+    } else if (c == 1) {
+      if (eq_before < need) {
+        const int pos = gt_before + eq_before;
+        out_idx[pos] = it.idx(i);
+        if (out_key) out_key[pos] = key[i];
+      }
+      ++eq_before;
     }
   }
-  return total;
+  return take_all ? nvalid : k;
 }
 
 __device__ __forceinline__ int visible(const int32_t* q_seq, const int32_t* q_pos,
@@ -151,7 +303,7 @@ __device__ __forceinline__ int visible(const int32_t* q_seq, const int32_t* q_po
   return max(0, min(q_pos[q] / m, n_entries[q_seq[q]]));
 }
 
-// Level 0: blockIdx.x = query, blockIdx.y = segment of E*1024 scores.
+// Level 0: blockIdx.x = query, blockIdx.y = segment of 1024*E scores.
 // direct != 0: the segment is the whole row; write the final selection to idx_out [Q][k].
 // Otherwise write the segment's candidates to cand_idx/cand_key [Q][nseg][k] (-1 padded).
 template <int E>
@@ -172,36 +324,30 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_segment(
     oidx = cand_idx + ((size_t)q * nseg + seg) * k;
     okey = cand_key + ((size_t)q * nseg + seg) * k;
   }
-  uint32_t key[E];
-  int idx[E];
-  bool valid[E];
-  const int first = base + threadIdx.x * E;
+  RunItems<E> it;
+  it.first = base + threadIdx.x * E;
+  it.V = V;
+  const int first = it.first;
   const float* row = scores + (size_t)q * ld;
   bool loaded = false;
   if constexpr (E % 4 == 0) {
     if (first + E <= V && ((ld & 3) == 0)) {
 #pragma unroll
       for (int i = 0; i < E; i += 4) {
-        float4 v = *reinterpret_cast<const float4*>(row + first + i);
-        key[i] = score_key(v.x);
-        key[i + 1] = score_key(v.y);
-        key[i + 2] = score_key(v.z);
-        key[i + 3] = score_key(v.w);
+        const float4 v = *reinterpret_cast<const float4*>(row + first + i);
+        it.key[i] = score_key(v.x);
+        it.key[i + 1] = score_key(v.y);
+        it.key[i + 2] = score_key(v.z);
+        it.key[i + 3] = score_key(v.w);
       }
-#pragma unroll
-      for (int i = 0; i < E; ++i) { idx[i] = first + i; valid[i] = true; }
       loaded = true;
     }
   }
   if (!loaded) {
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      idx[i] = first + i;
-      valid[i] = idx[i] < V;
-      key[i] = valid[i] ? score_key(row[idx[i]]) : 0u;
-    }
+    for (int i = 0; i < E; ++i) it.key[i] = first + i < V ? score_key(row[first + i]) : 0u;
   }
-  const int n = block_select<E>(key, idx, valid, k, sh, oidx, okey);
+  const int n = select_topk<E>(it, k, sh, oidx, okey);
   for (int i = n + threadIdx.x; i < k; i += TK_THREADS) {
     oidx[i] = -1;
     if (okey) okey[i] = 0u;
@@ -222,15 +368,12 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_merge(
   const int n = (l1 - l0) * k;
   const int32_t* ci = in_idx + ((size_t)q * nlist + l0) * k;
   const uint32_t* ck = in_key + ((size_t)q * nlist + l0) * k;
-  uint32_t key[E];
-  int idx[E];
-  bool valid[E];
+  ListItems<E> it;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     const int p = threadIdx.x * E + i;
-    idx[i] = p < n ? ci[p] : -1;
-    valid[i] = idx[i] >= 0;
-    key[i] = valid[i] ? ck[p] : 0u;
+    it.id[i] = p < n ? ci[p] : -1;
+    it.key[i] = it.id[i] >= 0 ? ck[p] : 0u;
   }
   int32_t* oidx;
   uint32_t* okey = nullptr;
@@ -240,7 +383,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_merge(
     oidx = out_idx + ((size_t)q * ngrp + grp) * k;
     okey = out_key + ((size_t)q * ngrp + grp) * k;
   }
-  const int cnt = block_select<E>(key, idx, valid, k, sh, oidx, okey);
+  const int cnt = select_topk<E>(it, k, sh, oidx, okey);
   for (int i = cnt + threadIdx.x; i < k; i += TK_THREADS) {
     oidx[i] = -1;
     if (okey) okey[i] = 0u;
@@ -253,18 +396,18 @@ int items_E(int n) {
   return E;
 }
 
-// One selection tree: segments of TK_SEG0 scores, then merges of up to TK_MERGE candidates.
+// One selection tree: segments of TK_SEG scores, then merges of up to TK_MERGE candidates.
 struct TopkPlan {
-  int nseg;        // level-0 segments (0: one direct segment)
+  int nseg;        // level-0 segments (0: the whole row in one direct workgroup)
   int seg_E;
   int levels;      // merge levels after level 0
 };
 
 TopkPlan plan_topk(int k, int cap) {
   TopkPlan p{0, items_E(cap), 0};
-  if (cap <= TK_DIRECT_MAX) return p;
-  p.nseg = (cap + TK_SEG0 - 1) / TK_SEG0;
-  p.seg_E = TK_SEG0 / TK_THREADS;
+  if (cap <= TK_SEG) return p;
+  p.nseg = (cap + TK_SEG - 1) / TK_SEG;
+  p.seg_E = TK_SEG / TK_THREADS;
   int lists = p.nseg;
   const int G = std::max(2, TK_MERGE / k);
   while (true) {
@@ -274,7 +417,6 @@ TopkPlan plan_topk(int k, int cap) {
   }
   return p;
 }
-
 
 #define TK_SEG_LAUNCH(EE, grid, direct, out_idx, cidx, ckey)                                     \
   hipLaunchKernelGGL((k_topk_segment<EE>), grid, dim3(TK_THREADS), 0, s, scores, ld, q_seq, q_pos, \
@@ -286,7 +428,7 @@ TopkPlan plan_topk(int k, int cap) {
 }  // namespace
 
 int32_t topk_max_visible(const csa_dims& d) {
-  if (d.top_k <= 0 || d.top_k > TK_MERGE) return 0;
+  if (d.top_k <= 0 || 2 * d.top_k > TK_MERGE) return 0;
   return INT32_MAX / 2;
 }
 
@@ -309,7 +451,8 @@ hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_s
     switch (p.seg_E) {
       case 1: TK_SEG_LAUNCH(1, dim3(Q, 1), 1, idx, nullptr, nullptr); break;
       case 2: TK_SEG_LAUNCH(2, dim3(Q, 1), 1, idx, nullptr, nullptr); break;
-      default: TK_SEG_LAUNCH(4, dim3(Q, 1), 1, idx, nullptr, nullptr); break;
+      case 4: TK_SEG_LAUNCH(4, dim3(Q, 1), 1, idx, nullptr, nullptr); break;
+      default: TK_SEG_LAUNCH(8, dim3(Q, 1), 1, idx, nullptr, nullptr); break;
     }
     return hipGetLastError();
   }
@@ -319,7 +462,7 @@ hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_s
   uint32_t* bufA_k = (uint32_t*)(bufA_i + (size_t)Q * p.nseg * k);
   int32_t* bufB_i = (int32_t*)(bufA_k + (size_t)Q * p.nseg * k);
   uint32_t* bufB_k = (uint32_t*)(bufB_i + (size_t)Q * lists1 * k);
-  TK_SEG_LAUNCH(4, dim3(Q, p.nseg), 0, idx, bufA_i, bufA_k);
+  TK_SEG_LAUNCH(8, dim3(Q, p.nseg), 0, idx, bufA_i, bufA_k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int lists = p.nseg;
@@ -336,8 +479,7 @@ hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_s
       case 1: TK_MERGE_LAUNCH(1, dim3(Q, groups), per_group); break;
       case 2: TK_MERGE_LAUNCH(2, dim3(Q, groups), per_group); break;
       case 4: TK_MERGE_LAUNCH(4, dim3(Q, groups), per_group); break;
-      case 8: TK_MERGE_LAUNCH(8, dim3(Q, groups), per_group); break;
-      default: TK_MERGE_LAUNCH(16, dim3(Q, groups), per_group); break;
+      default: TK_MERGE_LAUNCH(8, dim3(Q, groups), per_group); break;
     }
     e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
