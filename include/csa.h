@@ -173,7 +173,8 @@ int32_t csa_state_rows(const csa_dims* dims);
  * Workspace bytes for one call of `op`:
  *   COMPRESS   B sequences x T tokens.
  *   INDEX_TOPK Q queries against entry capacity cap.
- *   ATTEND     Q queries (cap unused).
+ *   ATTEND     Q queries against entry capacity cap; enough for a sparse (idx given) or a
+ *              dense (idx = NULL) call.
  *   FORWARD    B x T new tokens, queries = those tokens, entry capacity cap.  With
  *              q_chunk > 0 the indexer works on q_chunk queries at a time and the score
  *              buffer shrinks accordingly; 0 means all B*T at once.

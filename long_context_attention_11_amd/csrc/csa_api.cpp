@@ -159,7 +159,7 @@ int csa_workspace_size(const csa_dims* dims, int32_t op, int32_t B, int32_t T, i
       return CSA_OK;
     case CSA_OP_ATTEND:
       if (Q < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "Q must be positive");
-      *bytes = attend_workspace_bytes(d, Q, std::max(cap, 1));
+      *bytes = attend_workspace_bytes(d, Q, std::max(cap, 1), 2);
       return CSA_OK;
     case CSA_OP_FORWARD: {
       if (B < 1 || T < 1 || cap < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "B, T, cap must be positive");
@@ -170,7 +170,7 @@ int csa_workspace_size(const csa_dims* dims, int32_t op, int32_t B, int32_t T, i
       L.add(1, d.dual ? sizeof(int32_t) * (size_t)Qn * d.top_k : 0);  // idx
       size_t phase = compress_ws(d, B, T);
       if (d.dual) phase = std::max(phase, index_ws(d, Qc, cap));
-      phase = std::max(phase, attend_workspace_bytes(d, Qn, cap));
+      phase = std::max(phase, attend_workspace_bytes(d, Qn, cap, d.dual ? 0 : 1));  // forward attends a CSA layer sparsely
       L.add(2, phase);
       *bytes = L.total;
       return CSA_OK;
@@ -299,6 +299,10 @@ static int attend_checks(const csa_dims& d, const csa_cache& c, bool sparse) {
     const long rows = (long)(sparse ? d.top_k : c.cap) + d.n_win;
     if (rows > 4096) return fail(CSA_ERR_UNSUPPORTED, "fp32 attention handles at most 4096 keys per query");
     if (d.c > 1024) return fail(CSA_ERR_UNSUPPORTED, "fp32 attention handles c <= 1024");
+  } else {
+    const int64_t rows = (int64_t)(sparse ? d.top_k : c.cap) + d.n_win;
+    if (rows > attend_max_rows())
+      return fail(CSA_ERR_UNSUPPORTED, "attention handles at most " + std::to_string(attend_max_rows()) + " keys per query");
   }
   return CSA_OK;
 }
@@ -314,7 +318,7 @@ int csa_attend(const csa_dims* dims, const csa_cache* cache, const void* q, cons
   if (!q || !q_seq || !q_pos || !out) return fail(CSA_ERR_INVALID_ARGUMENT, "q, q_seq, q_pos and out must be set");
   if (Q < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "Q must be >= 1");
   if ((st = attend_checks(d, *cache, idx != nullptr))) return st;
-  const size_t need = attend_workspace_bytes(d, Q, cache->cap);
+  const size_t need = attend_workspace_bytes(d, Q, cache->cap, idx ? 0 : 1);
   if (need && (!ws || ws_bytes < need))
     return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "attend needs " + std::to_string(need) + " bytes of workspace");
   hipError_t e = launch_attend(d, *cache, q, gamma_q, sink, q_seq, q_pos, Q, idx, out, ws, stream);
@@ -347,7 +351,7 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
   L.add(0, 2 * sizeof(int32_t) * (size_t)Qn);
   L.add(1, (d.dual && !idx_out) ? sizeof(int32_t) * (size_t)Qn * d.top_k : 0);
   const size_t fixed = L.total;
-  size_t min_phase = std::max(compress_ws(d, cache->B, T), attend_workspace_bytes(d, Qn, cache->cap));
+  size_t min_phase = std::max(compress_ws(d, cache->B, T), attend_workspace_bytes(d, Qn, cache->cap, d.dual ? 0 : 1));
   if (d.dual) min_phase = std::max(min_phase, index_ws(d, 1, cache->cap));
   if (!ws || ws_bytes < fixed + min_phase)
     return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "forward needs at least " + std::to_string(fixed + min_phase) + " bytes of workspace");

@@ -100,6 +100,15 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS operations complete, then all
+// waves meet.  Unlike __syncthreads() it does not wait for the wave's outstanding global
+// loads, so loads prefetched into registers stay in flight across it (the compiler still
+// waits for each one before its registers are used).  Use only where the barrier orders LDS
+// accesses and no global memory written by one wave is read by another.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Map a hardware workgroup id to a logical one so that logical ids [k*n/8, (k+1)*n/8) run on
 // XCD k (workgroups are dealt to the 8 XCDs round-robin).  Neighbouring logical tiles then
 // share an L2.  Identity when n is not a multiple of 8.
@@ -161,7 +170,9 @@ hipError_t launch_query_meta(int32_t B, int32_t T, const int32_t* pos0, int32_t*
 int32_t project_ksplit(const csa_dims& d, int32_t M);
 size_t topk_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap);
 int32_t topk_max_visible(const csa_dims& d);
-size_t attend_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap);
+// which: 0 = sparse attention (idx given), 1 = dense (idx = NULL), 2 = the larger of both.
+size_t attend_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap, int which);
+int64_t attend_max_rows();  // keys per query the quantized attention path handles
 int32_t state_width(const csa_dims& d);
 int32_t state_rows(const csa_dims& d);
 size_t row_bytes(const csa_dims& d);
