@@ -193,6 +193,14 @@ int csa_compress(const csa_dims* dims, const csa_weights* w, const csa_cache* ca
   if (!H || !pos0) return fail(CSA_ERR_INVALID_ARGUMENT, "H and pos0 must be set");
   if (T < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "T must be >= 1");
   const int32_t M = cache->B * T;
+  if (project_step_ok(d, T)) {
+    // one new token per sequence: project into the state ring, fold from there
+    hipError_t e = launch_project_step(d, *w, *cache, H, pos0, stream);
+    if (e != hipSuccess) return hip_fail(e, "projection launch");
+    e = launch_fold(d, *w, *cache, T, pos0, nullptr, 1, stream);
+    if (e != hipSuccess) return hip_fail(e, "fold launch");
+    return CSA_OK;
+  }
   const size_t need = compress_ws(d, cache->B, T);
   if (need && (!ws || ws_bytes < need))
     return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "compress needs " + std::to_string(need) + " bytes of workspace");

@@ -143,6 +143,11 @@ void set_error(const std::string& msg);
 // Kernel launchers (defined in the .hip files).  Each returns a hipError_t of its launch.
 hipError_t launch_project(const csa_dims& d, const csa_weights& w, const void* H, int32_t M,
                           int32_t ksplit, float* P, hipStream_t s);
+// One-token steps (T = 1, bf16, d % 512 == 0): project straight into the state ring; the
+// fold then runs with P = null.
+bool project_step_ok(const csa_dims& d, int32_t T);
+hipError_t launch_project_step(const csa_dims& d, const csa_weights& w, const csa_cache& c,
+                               const void* H, const int32_t* pos0, hipStream_t s);
 hipError_t launch_fold(const csa_dims& d, const csa_weights& w, const csa_cache& c,
                        int32_t T, const int32_t* pos0, const float* P, int32_t ksplit,
                        hipStream_t s);

@@ -155,6 +155,27 @@ def test_q_compress_chunked_matches_oracle():
     assert flips < 50
 
 
+def test_q_compress_single_token_steps():
+    """Decode-style compression: 17 sequences (two 16-row projection tiles, the second
+    ragged) get a 3-token prefix and then 20 one-token steps, which take the step path
+    (projection straight into the state ring, fold from the ring).  Every stored entry,
+    indexer key and window row matches the oracle up to midpoint flips."""
+    cfg = _qcfg()
+    dims = L.Dims.from_config(cfg)
+    od = oracle_dims(cfg)
+    B, n = 17, 23
+    W = synth.weights(cfg, seed=8, device=DEV)
+    Hs = torch.stack([synth.hidden(cfg, b, 0, n, seed=8, device=DEV) for b in range(B)])
+    cache = L.Cache(dims, B=B, cap=16, win_cap=128)
+    _compress_chunks(dims, W, cache, Hs, [3] + [1] * (n - 3))
+    OW = oracle_weights(W)
+    flips = 0
+    for b in range(B):
+        comp = R.compress_sequence(host64(Hs[b]), OW, od)
+        flips += _check_cache_vs_oracle(cfg, cache, b, comp, n, f"q single-token seq {b}")
+    assert flips < 50
+
+
 def test_hca_compress_matches_oracle():
     """HCA (m'=128, single path, no indexer): 2 sequences x 300 tokens in chunks."""
     cfg = synth.config("c5")
