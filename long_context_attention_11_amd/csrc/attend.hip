@@ -8,11 +8,12 @@
 // "02 · DeepSeek-V4: 压缩注意力撑起 1M 上下文" §2.4 (window rows join the compressed entries in
 // one attention).
 //
-// E4M3/bf16 rows: 32-row tiles are gathered into LDS as bf16 (the E4M3 -> bf16 widening is
-// exact) in two layouts, row-major for Q.K and dim-major for P.V, and contracted on bf16
-// MFMA with float32 accumulation.  A workgroup (8 waves) covers 64 heads of one query, so
-// every staged row serves 64 heads.  Decode splits a query's rows over several workgroups
-// and merges their (max, sum, output) triples in a second kernel.
+// E4M3/bf16 rows: 64-row tiles are loaded straight into MFMA operand registers, widened
+// exactly from E4M3 to bf16, contracted with the queries on bf16 MFMA (float32 accumulation)
+// and written once to LDS, from where P.V reads them transposed.  A workgroup (4 waves) covers
+// 16 heads of one query.  When there are too few such workgroups to fill the CUs, a query's
+// rows are split over several workgroups, whose (max, sum, output) triples a second kernel
+// merges.
 #include <type_traits>
 
 #include "csa_internal.h"
@@ -47,15 +48,16 @@ struct AttendArgs {
   float* part_ml;             // [Q][n_h][splits][2]
 };
 
-// Sum of squares of 8 bf16 values packed in a uint4.
+// Sum of squares of 8 bf16 values packed in a uint4 (packed bf16 dot products with float32
+// accumulation; the values stay packed, so the widened copies are not kept alive).
 __device__ __forceinline__ float sumsq_bf16x8(const uint4& v) {
-  float s = 0.f;
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float s = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float lo = bf16_bits_to_f32(w[e] & 0xffffu), hi = bf16_bits_to_f32(w[e] >> 16);
-    s = fmaf(lo, lo, s);
-    s = fmaf(hi, hi, s);
+    const bf2 x = __builtin_bit_cast(bf2, w[e]);
+    s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);
   }
   return s;
 }
@@ -106,291 +108,335 @@ __device__ __forceinline__ void store_out4(const f32x4& o, float invL, uint16_t*
   *reinterpret_cast<uint2*>(orow + d0) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
 }
 
-// One workgroup = 8 waves = 64 heads of one query over a range of 32-row tiles.
-// Wave w: heads 16*(w & 3) .. +15 (hq), dims 256*(w >> 2) .. +255 (half).  Q.K is split over
-// the pair's halves of the contraction and summed through LDS in a fixed order, so both
-// waves of a pair hold identical scores, maxima and sums; each then accumulates P.V for its
-// own 256 output dims.  The next tile's rows are loaded into registers while the current one
-// computes.
-constexpr int T2 = 32;               // rows per tile
-constexpr int AT_MAX_ROWS = 4096;    // rows one workgroup covers (their indices sit in LDS)
-constexpr int K2_LD = AC + 8;        // bf16 pitch of the row-major tile (1040 B)
-constexpr int V2_LD = T2 + 8;        // bf16 pitch of the dim-major tile (80 B)
+// One workgroup = 4 waves = 16 heads of one query over a range of
+// 64-row tiles (all of the query's rows unless the plan splits them).
+//   Q.K  wave w loads rows 16w .. 16w+15 of a tile straight into MFMA A-operand registers
+//        (lane (row, g) holds a quarter of the row's dims), widens E4M3 to bf16 there and
+//        contracts against the 16 heads' queries, also in registers: no LDS on this side;
+//   P.V  the widened rows are also written to LDS as a bf16 row-major tile, and wave w
+//        produces output dims 128w .. 128w+127 over all 64 rows: A = V^T through the
+//        transposing LDS read, B = P^T from a head-major LDS copy of the probabilities.
+// LDS rows are 1040 bytes apart (a 16-byte bank shift per row).  Tile row p sits in LDS row
+// sigma(p) = 16(p / 16) + 8((p % 16) / 8) + 2(p % 4) + (p / 4) % 2, so the rows that one
+// transposing read gathers (8g + 2x, x < 4; +1 for the second read) are 32 bytes apart in
+// bank space, and MFMA K slot j of lane group g in P.V meets tile row 8g + j again: P^T is
+// stored by tile row.  Both the row writes (16 consecutive tile rows, same chunk) and the
+// transposing reads are then free of bank conflicts, and every LDS address is a per-lane
+// base plus an immediate offset.
+// A row is loaded as nine 64-byte pieces, the four lane groups g taking 16 bytes each, so
+// every load instruction covers whole 64-byte segments.  The contraction over dims then
+// pairs MFMA step ks, lane group g, slot j with
+//   dim 64(ks / 2) + 16g + 8(ks % 2) + j   (ks < 14: E4M3 dims, 16 per 16-byte piece)
+//   dim 448 + 32(ks - 14) + 8g + j         (ks = 14, 15: bf16 RoPE dims, 8 per piece)
+// on both the key and the query side.  The softmax statistics of a tile are combined over
+// the four waves through LDS, so every wave holds the same running max and sum.
+constexpr int HS_ROWS = 64;                        // rows per tile
+constexpr int HS_MAX_ROWS = 2048;                  // rows one workgroup covers
+constexpr int HS_IPT = HS_MAX_ROWS / 256;          // index loads per lane
+constexpr int HS_PLD = 72;                         // bf16 pitch of a head's probabilities
+constexpr int HS_PITCH = AC * 2 + 16;              // LDS row pitch in bytes
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// (dim d, row r) in the dim-major tile: the four 16-byte chunks of a dim's row are XOR-permuted
-// by (d >> 3) & 3, so writers stepping over dim groups spread over the banks.
-__device__ __forceinline__ int vt2_index(int d, int r) {
-  return d * V2_LD + (((r >> 3) ^ ((d >> 3) & 3)) << 3) + (r & 7);
+__device__ __forceinline__ int hs_sigma(int p) {
+  return (p & ~15) + 8 * ((p >> 3) & 1) + 2 * (p & 3) + ((p >> 2) & 1);
 }
 
-__global__ __launch_bounds__(512) void k_attend_mfma(AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[T2 * K2_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[AC * V2_LD];
-  __shared__ __attribute__((aligned(16))) f32x4 Sx[8][2][64];   // partial S per wave
+// First dim of MFMA step ks for lane group g (the dim pairing above).
+__device__ __forceinline__ int hs_dim(int ks, int g) {
+  return ks < 14 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : ANOPE + 32 * (ks - 14) + 8 * g;
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+
+template <bool SPARSE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_attend_hs(AttendArgs a) {
+  // tiles alternate between two buffers (rows and probabilities), so that a wave may widen
+  // and contract the next tile while others still read the current one
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[2 * HS_ROWS * HS_PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t PsT[2 * 16 * HS_PLD];
   __shared__ __attribute__((aligned(16))) float gam[AC];
-  __shared__ int rowok[2][T2];
-  __shared__ int ridx[AT_MAX_ROWS];   // entry index of each of this workgroup's entry rows
+  __shared__ float redm[4][16], reds[4][16];
+  __shared__ int ridx[SPARSE ? HS_MAX_ROWS : 1];
   __shared__ float rope_cs[AR];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
-  const int hq = wave & 3, half = wave >> 2;
-  const int nhg = (a.n_h + 63) / 64;
+  const int nhs = a.n_h / 16;
+  // the head groups of one (query, split) are adjacent, so they share an XCD's L2
   const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int split = L % a.splits;
-  const int rest = L / a.splits;
-  const int hg = rest % nhg;
-  const int q = rest / nhg;
+  const int hgrp = L % nhs;
+  const int rest = L / nhs;
+  const int split = rest % a.splits;
+  const int q = rest / a.splits;
+  const int h = hgrp * 16 + col;       // this lane's head
+  const int myrow = wave * 16 + col;   // this lane's row within a tile (Q.K side)
+  const int r_lo = split * a.tiles_per_split * HS_ROWS;
+  const int32_t* qidx = SPARSE ? a.idx + (size_t)q * a.k : nullptr;
   const int seq = a.q_seq[q];
   const int tau = a.q_pos[q];
-  const int V = max(0, min(tau / a.m, a.n_entries[seq]));
-  const int nsel = a.idx ? a.k : V;
-  const int w0 = max(0, tau - a.n_win + 1);
-  const int nrows = nsel + (tau - w0 + 1);
-  const int r_lo = split * a.tiles_per_split * T2;
-  const int r_hi = min(nrows, r_lo + a.tiles_per_split * T2);
-  const int h = hg * 64 + hq * 16 + col;   // this lane's head
-  const bool head_ok = (hg * 64 + hq * 16) < a.n_h;
-  const int hh = min(h, a.n_h - 1);
-  const int dbase = half * 256;            // this wave's output dims
 
-  // ---- loads are issued in the order they are needed (the wait counter retires them in
-  // order): this workgroup's entry indices (to LDS, so that no gather waits on an index
-  // load), the query norm weights, then the query rows.
-  const int e_hi = min(r_hi, nsel);
-  // A wave loads the indices of exactly the rows it gathers (rows 4*wave .. 4*wave+3 of each
-  // tile): lane l of batch i takes tile (64i + l) / 4, row (64i + l) % 4.  The wave reads
-  // them back itself, so no barrier is needed before the first gathers.
-  constexpr int IPT = AT_MAX_ROWS / 512;   // index loads per thread
-  int rid[IPT];
-  auto rid_row = [&](int i) { const int f = 64 * i + lane; return r_lo + (f >> 2) * T2 + wave * 4 + (f & 3); };
+  // ---- first the loads that depend on no other load: the entry indices of this lane's rows
+  // in the first two tiles, the rest of this wave's indices (lane l of batch i: tile
+  // (64i + l) / 16, row (64i + l) % 16 of the wave's 16), the norm weights, the sink logit
+  // and the 16 heads' query rows (16 KB, 64 contiguous bytes per thread).  Optional inputs
+  // are read through a valid stand-in address and replaced afterwards, so that no load sits
+  // in a branch.
+  int s01[2] = {0, 0};
+  int rid[HS_IPT];
+  auto rid_row = [&](int i) { const int f = 64 * i + lane; return r_lo + (f >> 4) * HS_ROWS + wave * 16 + (f & 15); };
+  if constexpr (SPARSE) {
 #pragma unroll
-  for (int i = 0; i < IPT; ++i) {
-    const int r = rid_row(i);
-    rid[i] = a.idx ? a.idx[(size_t)q * a.k + min(r, a.k - 1)] : r;
+    for (int t = 0; t < 2; ++t) s01[t] = qidx[min(r_lo + t * HS_ROWS + myrow, a.k - 1)];
+#pragma unroll
+    for (int i = 0; i < HS_IPT; ++i) rid[i] = qidx[min(rid_row(i), a.k - 1)];
   }
-  float4 gq = make_float4(1.f, 1.f, 1.f, 1.f);
   const int gu = (tid & 127) * 4;
-  if (a.gamma_q) gq = *reinterpret_cast<const float4*>(a.gamma_q + gu);
-  // every lane holds all 512 dims of its head in 16 chunks (needed for the norm); this wave
-  // keeps its 8 for the operands
-  const uint16_t* qrow = a.q + ((size_t)q * a.n_h + hh) * AC;
-  uint4 raw[16];
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks) raw[ks] = *reinterpret_cast<const uint4*>(qrow + ks * 32 + g * 8);
+  const float4 graw = *reinterpret_cast<const float4*>(a.gamma_q ? a.gamma_q + gu : reinterpret_cast<const float*>(a.q));
+  const float sraw = *(a.sink ? a.sink + h : reinterpret_cast<const float*>(a.q));
+  const uint8_t* qblk = reinterpret_cast<const uint8_t*>(a.q + ((size_t)q * a.n_h + hgrp * 16) * AC);
+  // (four named registers: an array here would be moved to LDS by the compiler)
+  const uint4 qr0 = *reinterpret_cast<const uint4*>(qblk + 64 * tid);
+  const uint4 qr1 = *reinterpret_cast<const uint4*>(qblk + 64 * tid + 16);
+  const uint4 qr2 = *reinterpret_cast<const uint4*>(qblk + 64 * tid + 32);
+  const uint4 qr3 = *reinterpret_cast<const uint4*>(qblk + 64 * tid + 48);
+  // keep the issue order above and below (neither the optimiser nor the scheduler may move
+  // memory operations across these fences, which wait for nothing)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 
-#pragma unroll
-  for (int i = 0; i < IPT; ++i) {
-    const int r = rid_row(i);
-    if (r < e_hi) ridx[r - r_lo] = rid[i];
-  }
-
-  // ---- staging map: thread covers dim-group dg (8 dims) of rows 4*rq .. 4*rq+3 of a tile
-  // (rq = wave, so a wave's row references are uniform across its lanes)
-  const int dg = tid & 63, rq = tid >> 6;
-  const bool nope_group = dg < ANOPE / 8;
-  // byte offset of this group's 16-byte load: 8 E4M3 dims (the next 8 bytes are unused), or
-  // 8 bf16 RoPE dims
-  const int col_off = nope_group ? dg * 8 : ANOPE + (dg - ANOPE / 8) * 16;
-  // Row r of the key list: entries first (idx order, or 0..V-1 when dense), then window
-  // positions w0 .. tau.  Two tiles of rows are in flight ahead of the one being computed.
-  // Every row issues its loads unconditionally (masked rows read entry row 0 of the cache)
-  // so that the compiler's wait counts stay exact; a window row is valid only if its ring
-  // slot still holds its position, read alongside it.
-  uint4 pre[2][4];
-  int wpos[2][4], want[2][4];
-  bool rok[2][4], rwin[2][4];
+  const int w0 = max(0, tau - a.n_win + 1);
+  // entries visible at tau; with an index list it is needed only when the rows are widened
+  int V = 0;
+  if constexpr (!SPARSE) V = max(0, min(tau / a.m, a.n_entries[seq]));
+  const int nsel = SPARSE ? a.k : V;
+  const int nrows = nsel + (tau - w0 + 1);
+  const int r_hi = min(nrows, r_lo + a.tiles_per_split * HS_ROWS);
   const uint8_t* kvseq = a.kv + (size_t)seq * a.cap * AROWB;
   const uint8_t* winseq = a.win + (size_t)seq * a.win_cap * AROWB;
   const int32_t* wpseq = a.win_pos + (size_t)seq * a.win_cap;
-  auto gather = [&](int t0, auto bconst) {
-    constexpr int b = decltype(bconst)::value;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int r = t0 + rq * 4 + rr;
-      const bool in = r < r_hi, ent = r < nsel;
-      const int s = ridx[min(max(r - r_lo, 0), AT_MAX_ROWS - 1)];
-      const bool ok_e = in && ent && s >= 0 && s < V;
-      const int j = w0 + (r - nsel);
-      const int slot = (ent ? 0 : j) % a.win_cap;
-      const uint8_t* src = ent ? kvseq + (size_t)(ok_e ? s : 0) * AROWB
-                               : (in ? winseq + (size_t)slot * AROWB : kvseq);
-      pre[b][rr] = *reinterpret_cast<const uint4*>(src + col_off);
-      wpos[b][rr] = wpseq[slot];
-      want[b][rr] = j;
-      rwin[b][rr] = !ent;
-      rok[b][rr] = ent ? ok_e : in;
-    }
-  };
-  gather(r_lo, std::integral_constant<int, 0>{});
-  gather(r_lo + T2, std::integral_constant<int, 1>{});
 
+  // ---- row gather: lane (row, g) loads bytes 64i + 16g .. +15 of the row (i < 9; pieces
+  // 0..6 hold E4M3 dims, 7 and 8 bf16 RoPE dims) and the position its window slot holds.
+  // Loads are unconditional: masked rows read row 0 of the sequence and are zeroed at
+  // widening.
+  uint4 pre[2][9];
+  int chk[2], wpv[2], sv[2];   // chk: 1 entry row, 0 masked, else window position + 2
+  // source row of this lane for the tile at t0 (plus its window-slot position load and the
+  // facts its validity is decided from)
+  auto gather_src = [&](int t0, int s_in, auto bconst) {
+    constexpr int b = decltype(bconst)::value;
+    const int r = t0 + myrow;
+    const bool in = r < r_hi, ent = r < nsel;
+    const int s = SPARSE ? s_in : r;
+    const bool ok_a = in && ent && s >= 0 && s < a.cap;
+    const int slot = (ent ? 0 : w0 + (r - nsel)) % a.win_cap;
+    const uint8_t* src = ent ? kvseq + (size_t)(ok_a ? s : 0) * AROWB
+                             : (in ? winseq + (size_t)slot * AROWB : kvseq);
+    wpv[b] = wpseq[slot];
+    chk[b] = ent ? (ok_a ? 1 : 0) : (in ? w0 + (r - nsel) + 2 : 0);
+    sv[b] = s;
+    return src;
+  };
+  auto gather_piece = [&](const uint8_t* src, int i, auto bconst) {
+    pre[decltype(bconst)::value][i] = *reinterpret_cast<const uint4*>(src + 64 * i + 16 * g);
+  };
+  auto gather = [&](int t0, int s_in, auto bconst) {
+    const uint8_t* src = gather_src(t0, s_in, bconst);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) gather_piece(src, i, bconst);
+  };
+  gather(r_lo, s01[0], std::integral_constant<int, 0>{});
+  gather(r_lo + HS_ROWS, s01[1], std::integral_constant<int, 1>{});
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (SPARSE) V = max(0, min(tau / a.m, a.n_entries[seq]));
+
+  // ---- LDS: the query rows (in the second tile buffer, pitch HS_PITCH; the first tile to
+  // reuse it comes after a barrier that every wave reaches after its query prep), this
+  // wave's entry indices,
+  // the RoPE table at tau and the norm weights
+  {
+    uint8_t* qd = Ks + HS_ROWS * HS_PITCH + (tid >> 4) * HS_PITCH + 64 * (tid & 15);
+    *reinterpret_cast<uint4*>(qd) = qr0;
+    *reinterpret_cast<uint4*>(qd + 16) = qr1;
+    *reinterpret_cast<uint4*>(qd + 32) = qr2;
+    *reinterpret_cast<uint4*>(qd + 48) = qr3;
+  }
+  if constexpr (SPARSE) {
+#pragma unroll
+    for (int i = 0; i < HS_IPT; ++i) ridx[min(rid_row(i) - r_lo, HS_MAX_ROWS - 1)] = rid[i];
+  }
   if (tid < AR / 2) rope_cos_sin(tau, tid, AR, a.log2_base, rope_cs[2 * tid], rope_cs[2 * tid + 1]);
-  if (tid < 128) *reinterpret_cast<float4*>(&gam[gu]) = gq;
+  if (tid < 128) *reinterpret_cast<float4*>(&gam[gu]) = a.gamma_q ? graw : make_float4(1.f, 1.f, 1.f, 1.f);
   lds_barrier();
 
-  // ---- query prep: RMSNorm over 512 dims, RoPE at tau on dims 448..511, bf16.  B operand of
-  // step ks (dims dbase + ks*32 .. +31): lane holds dims dbase + ks*32 + g*8 .. +7 of head h.
-  bf16x8 Qop[8];
+  // ---- query prep: RMSNorm over the 512 dims (lane groups g hold a quarter each), RoPE at
+  // tau on dims 448..511, bf16 B operands of Q.K
+  // (two passes over LDS, so that the raw query pieces are not all held in registers)
+  bf16x8 Qop[16];
   {
+    const uint8_t* qs = Ks + HS_ROWS * HS_PITCH + col * HS_PITCH;
     float ss = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) ss += sumsq_bf16x8(raw[ks]);
+    for (int ks = 0; ks < 16; ++ks) ss += sumsq_bf16x8(*reinterpret_cast<const uint4*>(qs + 2 * hs_dim(ks, g)));
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
     const float inv = 1.0f / sqrtf(ss / (float)AC + a.eps);
+    asm volatile("" ::: "memory");   // read the pieces again below
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int dim0 = dbase + ks * 32 + g * 8;
-      const uint4 pk = prep_q8(half ? raw[8 + ks] : raw[ks], inv, gam, dim0, rope_cs);
-      Qop[ks] = __builtin_bit_cast(bf16x8, pk);
-    }
+    for (int ks = 0; ks < 16; ++ks)
+      Qop[ks] = __builtin_bit_cast(
+          bf16x8, prep_q8(*reinterpret_cast<const uint4*>(qs + 2 * hs_dim(ks, g)), inv, gam, hs_dim(ks, g), rope_cs));
   }
 
-  const float sink2 = (a.sink && head_ok) ? a.sink[hh] * LOG2E : NEG_BIG;
-  float m_run = a.sink ? sink2 : NEG_BIG;
+  const float sink2 = a.sink ? sraw * LOG2E : NEG_BIG;
+  float m_run = sink2;
   float l_run = 0.f;
-  f32x4 O[16];
+  f32x4 O[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) O[i] = f32x4{0, 0, 0, 0};
+  for (int i = 0; i < 8; ++i) O[i] = f32x4{0, 0, 0, 0};
 
-  // One tile; b (the register/LDS buffer of its rows) is a compile-time constant so that
-  // the row buffers stay in registers.
   auto tile = [&](int t0, auto bconst) {
     constexpr int b = decltype(bconst)::value;
-      // ---- convert the prefetched rows; write Ks (row-major) and Vt (dim-major)
-      uint4 v[4];
-  #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const bool ok = rok[b][rr] && (!rwin[b][rr] || wpos[b][rr] == want[b][rr]);
-        uint32_t x0, x1, x2, x3;
-        e4m3x4_to_bf16x4(pre[b][rr].x, x0, x1);
-        e4m3x4_to_bf16x4(pre[b][rr].y, x2, x3);
-        uint4 o = nope_group ? make_uint4(x0, x1, x2, x3) : pre[b][rr];
-        if (!ok) o = make_uint4(0u, 0u, 0u, 0u);
-        v[rr] = o;
-        *reinterpret_cast<uint4*>(&Ks[(rq * 4 + rr) * K2_LD + dg * 8]) = o;
-        if (dg == 0) rowok[b][rq * 4 + rr] = ok ? 1 : 0;
+    // the entry index of this lane's row in the tile after next, read before this tile's
+    // LDS writes so that waiting for it does not wait for them
+    const int tn = t0 + 2 * HS_ROWS;
+    const int s_next = SPARSE ? ridx[min(max(tn + myrow - r_lo, 0), SPARSE ? HS_MAX_ROWS - 1 : 0)] : 0;
+    const bool ok = (chk[b] == 1 && sv[b] < V) || (chk[b] >= 2 && wpv[b] == chk[b] - 2);
+    const uint64_t okm = __ballot(ok);   // bit r of the low 16: row 16w + r is valid
+    // ---- widen, write the V tile, and contract Q.K for this wave's 16 rows (four
+    // independent accumulation chains, added at the end)
+    f32x4 Sp[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+    uint8_t* const Kb = Ks + b * HS_ROWS * HS_PITCH;
+    uint16_t* const Pb = PsT + b * 16 * HS_PLD;
+    uint8_t* wrow = Kb + hs_sigma(myrow) * HS_PITCH;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      uint4 v = pre[b][i];
+      if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
+      if (i < 7) {
+        uint32_t x[8];
+        e4m3x4_to_bf16x4(v.x, x[0], x[1]);
+        e4m3x4_to_bf16x4(v.y, x[2], x[3]);
+        e4m3x4_to_bf16x4(v.z, x[4], x[5]);
+        e4m3x4_to_bf16x4(v.w, x[6], x[7]);
+        const uint4 c0 = make_uint4(x[0], x[1], x[2], x[3]);
+        const uint4 c1 = make_uint4(x[4], x[5], x[6], x[7]);
+        *reinterpret_cast<uint4*>(wrow + 16 * (8 * i + 2 * g)) = c0;
+        *reinterpret_cast<uint4*>(wrow + 16 * (8 * i + 2 * g + 1)) = c1;
+        Sp[(2 * i) & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c0), Qop[2 * i], Sp[(2 * i) & 3], 0, 0, 0);
+        Sp[(2 * i + 1) & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c1), Qop[2 * i + 1], Sp[(2 * i + 1) & 3], 0, 0, 0);
+      } else {
+        *reinterpret_cast<uint4*>(wrow + 16 * (56 + 4 * (i - 7) + g)) = v;
+        Sp[(7 + i) & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), Qop[7 + i], Sp[(7 + i) & 3], 0, 0, 0);
       }
-  #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a0 = reinterpret_cast<const uint32_t*>(&v[0])[w];
-        const uint32_t a1 = reinterpret_cast<const uint32_t*>(&v[1])[w];
-        const uint32_t a2 = reinterpret_cast<const uint32_t*>(&v[2])[w];
-        const uint32_t a3 = reinterpret_cast<const uint32_t*>(&v[3])[w];
-        const uint2 lo = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u));
-        const uint2 hi = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u));
-        *reinterpret_cast<uint2*>(&Vt[vt2_index(dg * 8 + 2 * w, rq * 4)]) = lo;
-        *reinterpret_cast<uint2*>(&Vt[vt2_index(dg * 8 + 2 * w + 1, rq * 4)]) = hi;
-      }
-      lds_barrier();
-      // the tile after next, into the row buffers just consumed
-      gather(t0 + 2 * T2, bconst);
+    }
+    f32x4 S = (Sp[0] + Sp[1]) + (Sp[2] + Sp[3]);
+    // the tile after next goes into the registers just consumed; its nine loads are spread
+    // over the P.V steps below, so that the vector memory unit works while LDS and MFMA do
+    const uint8_t* nsrc = gather_src(tn, s_next, bconst);
 
-      // ---- partial S^T = K . Q^T over this wave's 256 dims, 2 row tiles
-      f32x4 S[2];
-  #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        S[rt] = f32x4{0, 0, 0, 0};
-  #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8 A = *reinterpret_cast<const bf16x8*>(&Ks[(rt * 16 + col) * K2_LD + dbase + ks * 32 + g * 8]);
-          S[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Qop[ks], S[rt], 0, 0, 0);
-        }
-        Sx[wave][rt][lane] = S[rt];
-      }
-      lds_barrier();
-      // full scores: half 0 + half 1, the same order in both waves of the pair
-  #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) S[rt] = Sx[hq][rt][lane] + Sx[hq + 4][rt][lane];
-
-      // ---- online softmax (log2 domain), sink already in m_run; lane holds head col, rows
-      // 16*rt + 4g + e
-      float mx = NEG_BIG;
-  #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = rowok[b][rt * 16 + 4 * g + e] != 0;
-          S[rt][e] = ok ? S[rt][e] * a.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, S[rt][e]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
-      float ls = 0.f;
-  #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          S[rt][e] = exp2f(S[rt][e] - m_new);
-          ls += S[rt][e];
-        }
-      ls += __shfl_xor(ls, 16, 64);
-      ls += __shfl_xor(ls, 32, 64);
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
-      if (t0 != r_lo && __any(alpha != 1.0f)) {  // O is zero on the first tile; skip when no max moved
-  #pragma unroll
-        for (int i = 0; i < 16; ++i) O[i] *= alpha;
-      }
-      // ---- O^T += V^T . P^T over the 32 rows (one K step): lane group g pairs rows
-      // {4g + e} and {16 + 4g + e} (e < 4) on both operands
-      uint4 pb;
-      pb.x = pack_bf16x2(S[0][0], S[0][1]);
-      pb.y = pack_bf16x2(S[0][2], S[0][3]);
-      pb.z = pack_bf16x2(S[1][0], S[1][1]);
-      pb.w = pack_bf16x2(S[1][2], S[1][3]);
-      const bf16x8 Bp = __builtin_bit_cast(bf16x8, pb);
-  #pragma unroll
-      for (int dt = 0; dt < 16; ++dt) {
-        const int d = dbase + dt * 16 + col;
-        const uint2 lo = *reinterpret_cast<const uint2*>(&Vt[vt2_index(d, 4 * g)]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&Vt[vt2_index(d, 16 + 4 * g)]);
-        const bf16x8 Av = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Bp, O[dt], 0, 0, 0);
-      }
+    // ---- online softmax: lane holds head col, rows 16w + 4g + e
+    float mx = NEG_BIG;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool rv = (okm >> (4 * g + e)) & 1u;
+      S[e] = rv ? S[e] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, S[e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (g == 0) redm[wave][col] = mx;
     lds_barrier();
+    const float m_tile = fmaxf(fmaxf(redm[0][col], redm[1][col]), fmaxf(redm[2][col], redm[3][col]));
+    const float m_new = fmaxf(m_run, m_tile);
+    const float alpha = exp2f(m_run - m_new);
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      S[e] = exp2f(S[e] - m_new);
+      ls += S[e];
+    }
+    // every wave holds the same running max, so each keeps the sum over its own rows and
+    // the four are added once at the end
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+    *reinterpret_cast<uint2*>(&Pb[col * HS_PLD + wave * 16 + 4 * g]) =
+        make_uint2(pack_bf16x2(S[0], S[1]), pack_bf16x2(S[2], S[3]));
+    lds_barrier();
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) O[i] *= alpha;
+    }
+
+    // ---- O^T += V^T . P^T over the 64 rows (two K chunks of 32) for this wave's 128 dims.
+    // Transposing read: source lane j of a 16-lane group reads LDS row 32kc + 8g + 2(j >> 2)
+    // (+1 for the second read), dims c0 + 4(j & 3) .. +3; lane i then holds dim c0 + i of
+    // tile rows 32kc + 8g .. +3 (+4 .. +7).
+    const uint8_t* vbase = Kb + (8 * g + 2 * (col >> 2)) * HS_PITCH + 2 * (wave * 128 + 4 * (col & 3));
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const bf16x8 Bp = *reinterpret_cast<const bf16x8*>(&Pb[col * HS_PLD + 32 * kc + 8 * g]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint8_t* va = vbase + 32 * kc * HS_PITCH + 32 * dt;
+        const s16x4 lo = lds_read_tr16(va);
+        const s16x4 hi = lds_read_tr16(va + HS_PITCH);
+        const bf16x8 Av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Bp, O[dt], 0, 0, 0);
+        if (kc * 8 + dt < 9) gather_piece(nsrc, kc * 8 + dt, bconst);
+      }
+    }
+    // no barrier: the next tile writes the other buffers, and the one after that passes
+    // the next tile's barriers first, which every wave reaches only after this P.V
   };
   // tiles go in pairs (a pair's second tile may be past the end: fully masked, it changes
   // nothing)
-  for (int t0 = r_lo; t0 < r_hi; t0 += 2 * T2) {
+  for (int t0 = r_lo; t0 < r_hi; t0 += 2 * HS_ROWS) {
     tile(t0, std::integral_constant<int, 0>{});
-    tile(t0 + T2, std::integral_constant<int, 1>{});
+    tile(t0 + HS_ROWS, std::integral_constant<int, 1>{});
   }
 
-  if (!head_ok) return;
-  // O[dt][e] holds head col, dim dbase + dt*16 + 4g + e.
+  // the sum over all rows: lanes hold a wave's 16 rows of one tile position (4g + e), summed
+  // over lane groups here and over waves through LDS
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (g == 0) reds[wave][col] = l_run;
+  lds_barrier();
+  l_run = ((reds[0][col] + reds[1][col]) + reds[2][col]) + reds[3][col];
+
+  // O[dt][e]: head h, dim 128w + 16dt + 4g + e
   if (a.splits == 1) {
     const float Lsum = l_run + (a.sink ? exp2f(sink2 - m_run) : 0.f);
     const float invL = Lsum > 0.f ? 1.0f / Lsum : 0.f;
     uint16_t* orow = a.out + ((size_t)q * a.n_h + h) * AC;
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt) store_out4(O[dt], invL, orow, dbase + dt * 16 + 4 * g, rope_cs);
+    for (int dt = 0; dt < 8; ++dt) store_out4(O[dt], invL, orow, wave * 128 + 16 * dt + 4 * g, rope_cs);
   } else {
+    // unnormalised partial output, already rotated back (the rotation is linear, so it
+    // commutes with the merge)
     const size_t pidx = ((size_t)q * a.n_h + h) * a.splits + split;
-    // unnormalised partial output, rounded to bf16 (the final output is bf16 as well)
     uint16_t* po = a.part_o + pidx * AC;
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt)
-      *reinterpret_cast<uint2*>(po + dbase + dt * 16 + 4 * g) =
-          make_uint2(pack_bf16x2(O[dt][0], O[dt][1]), pack_bf16x2(O[dt][2], O[dt][3]));
-    if (g == 0 && half == 0) {
+    for (int dt = 0; dt < 8; ++dt) store_out4(O[dt], 1.0f, po, wave * 128 + 16 * dt + 4 * g, rope_cs);
+    if (wave == 0 && g == 0) {
       a.part_ml[pidx * 2] = m_run;
       a.part_ml[pidx * 2 + 1] = l_run;
     }
   }
 }
 
-// Merge split partials: one workgroup of 256 threads per (query, head), 2 dims per thread.
+// Merge split partials (already rotated back): one workgroup of 256 threads per (query, head),
+// 2 dims per thread.
 // Splits are taken 8 at a time (all loads of a chunk in flight), merged with a running max.
-constexpr int COMB_MAX = 128;  // most splits a plan uses
+constexpr int COMB_MAX = 256;  // most splits a plan uses
 
 __global__ __launch_bounds__(256) void k_attend_combine(AttendArgs a) {
   const int qh = blockIdx.x;
-  const int q = qh / a.n_h, h = qh % a.n_h;
-  const int tau = a.q_pos[q];
+  const int h = qh % a.n_h;
   const int d = 2 * threadIdx.x;
   const float* ml = a.part_ml + (size_t)qh * a.splits * 2;
   const uint16_t* po = a.part_o + (size_t)qh * a.splits * AC + d;
@@ -426,16 +472,7 @@ __global__ __launch_bounds__(256) void k_attend_combine(AttendArgs a) {
     M = Mc;
   }
   const float invL = Lsum > 0.f ? 1.0f / Lsum : 0.f;
-  y0 *= invL;
-  y1 *= invL;
-  if (d >= ANOPE) {
-    float cs, sn;
-    rope_cos_sin(tau, (d - ANOPE) >> 1, AR, a.log2_base, cs, sn);
-    const float z0 = y0 * cs + y1 * sn, z1 = -y0 * sn + y1 * cs;
-    y0 = z0;
-    y1 = z1;
-  }
-  *reinterpret_cast<uint32_t*>(a.out + (size_t)qh * AC + d) = pack_bf16x2(y0, y1);
+  *reinterpret_cast<uint32_t*>(a.out + (size_t)qh * AC + d) = pack_bf16x2(y0 * invL, y1 * invL);
 }
 
 // float32 rows (fp32 formats): one workgroup of 64 threads per (query, head); exact
@@ -542,25 +579,27 @@ struct SplitPlan {
   int splits, tiles_per_split;
 };
 
-// Rows of a query are split over workgroups: about one workgroup per CU (each holds ~94 KB
-// of LDS), but at least AT_MIN_TILES tiles each, so that the two-tile gather prefetch runs
-// ahead of the compute and fewer partial outputs go through memory.
-constexpr int AT_MIN_TILES = 2;
+// Rows of a query are split over workgroups only when there are too few (query, 16-head)
+// workgroups to spread over the CUs, and then into parts of at least HS_MIN_TILES tiles, so
+// that the two-tile gather prefetch runs ahead of the compute and few partial outputs go
+// through memory.  A part holds at most HS_MAX_ROWS rows (their indices sit in LDS).
+constexpr int HS_MIN_TILES = 4;
 
 SplitPlan plan_splits(const csa_dims& d, int32_t Q, int32_t cap, bool dense) {
   const int64_t max_rows = (int64_t)(dense ? cap : d.top_k) + d.n_win;
-  const int ntiles = (int)((max_rows + T2 - 1) / T2);
-  const int blocks = Q * ((d.n_h + 63) / 64);
+  const int ntiles = (int)((max_rows + HS_ROWS - 1) / HS_ROWS);
+  const int blocks = Q * (d.n_h / 16);
   int target = (256 + blocks - 1) / blocks;
-  target = std::max(1, std::min(std::min(target, ntiles), COMB_MAX));
-  int tps = std::max((ntiles + target - 1) / target, std::min(AT_MIN_TILES, ntiles));
-  tps = std::min(tps, AT_MAX_ROWS / T2);
-  return {(ntiles + tps - 1) / tps, tps};
+  target = std::max(1, std::min(target, (ntiles + HS_MIN_TILES - 1) / HS_MIN_TILES));
+  int tps = (ntiles + target - 1) / target;
+  tps = std::max(1, std::min(tps, HS_MAX_ROWS / HS_ROWS));
+  const int splits = (ntiles + tps - 1) / tps;
+  return {std::min(splits, COMB_MAX), tps};
 }
 
 }  // namespace
 
-int64_t attend_max_rows() { return (int64_t)COMB_MAX * AT_MAX_ROWS; }
+int64_t attend_max_rows() { return (int64_t)COMB_MAX * HS_MAX_ROWS; }
 
 // which: 0 = sparse (idx given; CSA only), 1 = dense (idx = NULL), 2 = the larger of the two
 // (a CSA layer may be attended either way when the caller does not say).
@@ -615,8 +654,11 @@ hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
   a.part_o = (uint16_t*)ws;
   const size_t po = ((size_t)Q * d.n_h * p.splits * AC * sizeof(uint16_t) + 255) / 256 * 256;
   a.part_ml = p.splits > 1 ? (float*)((char*)ws + po) : nullptr;
-  const int nhg = (d.n_h + 63) / 64;
-  hipLaunchKernelGGL(k_attend_mfma, dim3(Q * nhg * p.splits), dim3(512), 0, s, a);
+  const dim3 grid(Q * (d.n_h / 16) * p.splits);
+  if (idx)
+    hipLaunchKernelGGL(k_attend_hs<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_attend_hs<false>, grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   hipLaunchKernelGGL(k_attend_combine, dim3(Q * d.n_h), dim3(256), 0, s, a);
