@@ -62,29 +62,29 @@ __device__ __forceinline__ float sumsq_bf16x8(const uint4& v) {
   return s;
 }
 
-// Normalise 8 query dims (dim0 .. dim0+7) with weights gamma (a table of 512), rotate them to
-// tau when they are RoPE dims (cos/sin of pair j at cs[2j], cs[2j+1]), and return them as
-// packed bf16.
-__device__ __forceinline__ uint4 prep_q8(const uint4& v, float inv, const float* gamma, int dim0,
-                                         const float* cs) {
+// Scale 8 bf16 query dims by inv * gamma (gamma dims in g0, g1) and repack them as bf16.
+__device__ __forceinline__ uint4 norm_q8(const uint4& v, float inv, const float4& g0, const float4& g1) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  const float4 g0 = *reinterpret_cast<const float4*>(gamma + dim0);
-  const float4 g1 = *reinterpret_cast<const float4*>(gamma + dim0 + 4);
   const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-  const bool rope = dim0 >= ANOPE;
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    o[e] = pack_bf16x2(bf16_bits_to_f32(w[e] & 0xffffu) * inv * gm[2 * e],
+                       bf16_bits_to_f32(w[e] >> 16) * inv * gm[2 * e + 1]);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Rotate 8 bf16 RoPE dims (dim0 .. dim0+7, dim0 >= 448) to tau: pair j = (dim - 448) / 2
+// turns by the angle whose cos/sin sit at cs[2j], cs[2j+1].
+__device__ __forceinline__ uint4 rope_q8(const uint4& v, int dim0, const float* cs) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t o[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    float y0 = bf16_bits_to_f32(w[e] & 0xffffu) * inv * gm[2 * e];
-    float y1 = bf16_bits_to_f32(w[e] >> 16) * inv * gm[2 * e + 1];
-    if (rope) {
-      const int j = (dim0 + 2 * e - ANOPE) >> 1;
-      const float c = cs[2 * j], sn = cs[2 * j + 1];
-      const float z0 = y0 * c - y1 * sn, z1 = y0 * sn + y1 * c;
-      y0 = z0;
-      y1 = z1;
-    }
-    o[e] = pack_bf16x2(y0, y1);
+    const float y0 = bf16_bits_to_f32(w[e] & 0xffffu), y1 = bf16_bits_to_f32(w[e] >> 16);
+    const int j = (dim0 + 2 * e - ANOPE) >> 1;
+    const float c = cs[2 * j], sn = cs[2 * j + 1];
+    o[e] = pack_bf16x2(y0 * c - y1 * sn, y0 * sn + y1 * c);
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
@@ -135,6 +135,7 @@ constexpr int HS_MAX_ROWS = 2048;                  // rows one workgroup covers
 constexpr int HS_IPT = HS_MAX_ROWS / 256;          // index loads per lane
 constexpr int HS_PLD = 72;                         // bf16 pitch of a head's probabilities
 constexpr int HS_PITCH = AC * 2 + 16;              // LDS row pitch in bytes
+constexpr int HS_DEPTH = 1;                        // tiles loaded ahead of the one in use
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int hs_sigma(int p) {
@@ -151,13 +152,10 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 }
 
 template <bool SPARSE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_attend_hs(AttendArgs a) {
-  // tiles alternate between two buffers (rows and probabilities), so that a wave may widen
-  // and contract the next tile while others still read the current one
-  __shared__ __attribute__((aligned(16))) uint8_t Ks[2 * HS_ROWS * HS_PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t PsT[2 * 16 * HS_PLD];
-  __shared__ __attribute__((aligned(16))) float gam[AC];
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[HS_ROWS * HS_PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t PsT[16 * HS_PLD];
   __shared__ float redm[4][16], reds[4][16];
   __shared__ int ridx[SPARSE ? HS_MAX_ROWS : 1];
   __shared__ float rope_cs[AR];
@@ -184,17 +182,19 @@ void k_attend_hs(AttendArgs a) {
   // and the 16 heads' query rows (16 KB, 64 contiguous bytes per thread).  Optional inputs
   // are read through a valid stand-in address and replaced afterwards, so that no load sits
   // in a branch.
-  int s01[2] = {0, 0};
+  int s01[HS_DEPTH] = {};
   int rid[HS_IPT];
   auto rid_row = [&](int i) { const int f = 64 * i + lane; return r_lo + (f >> 4) * HS_ROWS + wave * 16 + (f & 15); };
   if constexpr (SPARSE) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) s01[t] = qidx[min(r_lo + t * HS_ROWS + myrow, a.k - 1)];
+    for (int t = 0; t < HS_DEPTH; ++t) s01[t] = qidx[min(r_lo + t * HS_ROWS + myrow, a.k - 1)];
 #pragma unroll
     for (int i = 0; i < HS_IPT; ++i) rid[i] = qidx[min(rid_row(i), a.k - 1)];
   }
-  const int gu = (tid & 127) * 4;
-  const float4 graw = *reinterpret_cast<const float4*>(a.gamma_q ? a.gamma_q + gu : reinterpret_cast<const float*>(a.q));
+  const float* gsrc = (a.gamma_q ? a.gamma_q : reinterpret_cast<const float*>(a.q)) + 32 * (tid & 15);
+  float4 gq[8];   // the norm weights of this thread's 32 query dims
+#pragma unroll
+  for (int k = 0; k < 8; ++k) gq[k] = *reinterpret_cast<const float4*>(gsrc + 4 * k);
   const float sraw = *(a.sink ? a.sink + h : reinterpret_cast<const float*>(a.q));
   const uint8_t* qblk = reinterpret_cast<const uint8_t*>(a.q + ((size_t)q * a.n_h + hgrp * 16) * AC);
   // (four named registers: an array here would be moved to LDS by the compiler)
@@ -222,8 +222,8 @@ void k_attend_hs(AttendArgs a) {
   // 0..6 hold E4M3 dims, 7 and 8 bf16 RoPE dims) and the position its window slot holds.
   // Loads are unconditional: masked rows read row 0 of the sequence and are zeroed at
   // widening.
-  uint4 pre[2][9];
-  int chk[2], wpv[2], sv[2];   // chk: 1 entry row, 0 masked, else window position + 2
+  uint4 pre[HS_DEPTH][9];
+  int chk[HS_DEPTH], wpv[HS_DEPTH], sv[HS_DEPTH];   // chk: 1 entry row, 0 masked, else window position + 2
   // source row of this lane for the tile at t0 (plus its window-slot position load and the
   // facts its validity is decided from)
   auto gather_src = [&](int t0, int s_in, auto bconst) {
@@ -249,48 +249,49 @@ void k_attend_hs(AttendArgs a) {
     for (int i = 0; i < 9; ++i) gather_piece(src, i, bconst);
   };
   gather(r_lo, s01[0], std::integral_constant<int, 0>{});
-  gather(r_lo + HS_ROWS, s01[1], std::integral_constant<int, 1>{});
+  if constexpr (HS_DEPTH > 1) gather(r_lo + HS_ROWS, s01[HS_DEPTH - 1], std::integral_constant<int, HS_DEPTH - 1>{});
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (SPARSE) V = max(0, min(tau / a.m, a.n_entries[seq]));
 
-  // ---- LDS: the query rows (in the second tile buffer, pitch HS_PITCH; the first tile to
-  // reuse it comes after a barrier that every wave reaches after its query prep), this
-  // wave's entry indices,
-  // the RoPE table at tau and the norm weights
+  // ---- LDS: the normalised query rows (RMSNorm over a head's 512 dims, whose 16 threads
+  // hold 32 dims each, times the norm weights; in the tile buffer, pitch HS_PITCH), this
+  // wave's entry indices and the RoPE table at tau
   {
-    uint8_t* qd = Ks + HS_ROWS * HS_PITCH + (tid >> 4) * HS_PITCH + 64 * (tid & 15);
-    *reinterpret_cast<uint4*>(qd) = qr0;
-    *reinterpret_cast<uint4*>(qd + 16) = qr1;
-    *reinterpret_cast<uint4*>(qd + 32) = qr2;
-    *reinterpret_cast<uint4*>(qd + 48) = qr3;
+    float ss = (sumsq_bf16x8(qr0) + sumsq_bf16x8(qr1)) + (sumsq_bf16x8(qr2) + sumsq_bf16x8(qr3));
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    ss += __shfl_xor(ss, 4, 64);
+    ss += __shfl_xor(ss, 8, 64);
+    const float inv = 1.0f / sqrtf(ss / (float)AC + a.eps);
+    if (!a.gamma_q) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) gq[k] = make_float4(1.f, 1.f, 1.f, 1.f);
+    }
+    uint8_t* qd = Ks + (tid >> 4) * HS_PITCH + 64 * (tid & 15);
+    *reinterpret_cast<uint4*>(qd) = norm_q8(qr0, inv, gq[0], gq[1]);
+    *reinterpret_cast<uint4*>(qd + 16) = norm_q8(qr1, inv, gq[2], gq[3]);
+    *reinterpret_cast<uint4*>(qd + 32) = norm_q8(qr2, inv, gq[4], gq[5]);
+    *reinterpret_cast<uint4*>(qd + 48) = norm_q8(qr3, inv, gq[6], gq[7]);
   }
   if constexpr (SPARSE) {
 #pragma unroll
     for (int i = 0; i < HS_IPT; ++i) ridx[min(rid_row(i) - r_lo, HS_MAX_ROWS - 1)] = rid[i];
   }
   if (tid < AR / 2) rope_cos_sin(tau, tid, AR, a.log2_base, rope_cs[2 * tid], rope_cs[2 * tid + 1]);
-  if (tid < 128) *reinterpret_cast<float4*>(&gam[gu]) = a.gamma_q ? graw : make_float4(1.f, 1.f, 1.f, 1.f);
   lds_barrier();
 
-  // ---- query prep: RMSNorm over the 512 dims (lane groups g hold a quarter each), RoPE at
-  // tau on dims 448..511, bf16 B operands of Q.K
-  // (two passes over LDS, so that the raw query pieces are not all held in registers)
+  // ---- bf16 B operands of Q.K, with RoPE at tau on dims 448..511 (steps 14 and 15)
   bf16x8 Qop[16];
   {
-    const uint8_t* qs = Ks + HS_ROWS * HS_PITCH + col * HS_PITCH;
-    float ss = 0.f;
+    const uint8_t* qs = Ks + col * HS_PITCH;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) ss += sumsq_bf16x8(*reinterpret_cast<const uint4*>(qs + 2 * hs_dim(ks, g)));
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
-    const float inv = 1.0f / sqrtf(ss / (float)AC + a.eps);
-    asm volatile("" ::: "memory");   // read the pieces again below
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks)
-      Qop[ks] = __builtin_bit_cast(
-          bf16x8, prep_q8(*reinterpret_cast<const uint4*>(qs + 2 * hs_dim(ks, g)), inv, gam, hs_dim(ks, g), rope_cs));
+    for (int ks = 0; ks < 16; ++ks) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qs + 2 * hs_dim(ks, g));
+      Qop[ks] = __builtin_bit_cast(bf16x8, ks < 14 ? v : rope_q8(v, hs_dim(ks, g), rope_cs));
+    }
   }
+  lds_barrier();   // the tile buffer is rewritten next
 
   const float sink2 = a.sink ? sraw * LOG2E : NEG_BIG;
   float m_run = sink2;
@@ -303,15 +304,15 @@ void k_attend_hs(AttendArgs a) {
     constexpr int b = decltype(bconst)::value;
     // the entry index of this lane's row in the tile after next, read before this tile's
     // LDS writes so that waiting for it does not wait for them
-    const int tn = t0 + 2 * HS_ROWS;
+    const int tn = t0 + HS_DEPTH * HS_ROWS;
     const int s_next = SPARSE ? ridx[min(max(tn + myrow - r_lo, 0), SPARSE ? HS_MAX_ROWS - 1 : 0)] : 0;
     const bool ok = (chk[b] == 1 && sv[b] < V) || (chk[b] >= 2 && wpv[b] == chk[b] - 2);
     const uint64_t okm = __ballot(ok);   // bit r of the low 16: row 16w + r is valid
     // ---- widen, write the V tile, and contract Q.K for this wave's 16 rows (four
     // independent accumulation chains, added at the end)
     f32x4 Sp[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-    uint8_t* const Kb = Ks + b * HS_ROWS * HS_PITCH;
-    uint16_t* const Pb = PsT + b * 16 * HS_PLD;
+    uint8_t* const Kb = Ks;
+    uint16_t* const Pb = PsT;
     uint8_t* wrow = Kb + hs_sigma(myrow) * HS_PITCH;
 #pragma unroll
     for (int i = 0; i < 9; ++i) {
@@ -390,14 +391,13 @@ void k_attend_hs(AttendArgs a) {
         if (kc * 8 + dt < 9) gather_piece(nsrc, kc * 8 + dt, bconst);
       }
     }
-    // no barrier: the next tile writes the other buffers, and the one after that passes
-    // the next tile's barriers first, which every wave reaches only after this P.V
+    lds_barrier();   // the next tile rewrites the row and probability buffers
   };
-  // tiles go in pairs (a pair's second tile may be past the end: fully masked, it changes
-  // nothing)
-  for (int t0 = r_lo; t0 < r_hi; t0 += 2 * HS_ROWS) {
+  // with HS_DEPTH > 1 tiles go in groups whose last ones may lie past the end: fully masked,
+  // they change nothing
+  for (int t0 = r_lo; t0 < r_hi; t0 += HS_DEPTH * HS_ROWS) {
     tile(t0, std::integral_constant<int, 0>{});
-    tile(t0 + HS_ROWS, std::integral_constant<int, 1>{});
+    if constexpr (HS_DEPTH > 1) tile(t0 + HS_ROWS, std::integral_constant<int, HS_DEPTH - 1>{});
   }
 
   // the sum over all rows: lanes hold a wave's 16 rows of one tile position (4g + e), summed
@@ -579,22 +579,36 @@ struct SplitPlan {
   int splits, tiles_per_split;
 };
 
-// Rows of a query are split over workgroups only when there are too few (query, 16-head)
-// workgroups to spread over the CUs, and then into parts of at least HS_MIN_TILES tiles, so
-// that the two-tile gather prefetch runs ahead of the compute and few partial outputs go
-// through memory.  A part holds at most HS_MAX_ROWS rows (their indices sit in LDS).
-constexpr int HS_MIN_TILES = 4;
+// Rows of a query are split over workgroups when there are too few (query, 16-head)
+// workgroups to keep the CUs busy.  The plan minimises a cost in tile times: a CU runs up to
+// two workgroups at once, which then finish about 1.2x faster than one after the other; each
+// round of workgroups on a CU pays a prologue of about 1.5 tiles (index, query and first row
+// loads); a split plan pays about 2.5 tiles for the merge pass.  A part holds at most
+// HS_MAX_ROWS rows (their indices sit in LDS).
+constexpr int HS_CUS = 256;
 
 SplitPlan plan_splits(const csa_dims& d, int32_t Q, int32_t cap, bool dense) {
   const int64_t max_rows = (int64_t)(dense ? cap : d.top_k) + d.n_win;
   const int ntiles = (int)((max_rows + HS_ROWS - 1) / HS_ROWS);
-  const int blocks = Q * (d.n_h / 16);
-  int target = (256 + blocks - 1) / blocks;
-  target = std::max(1, std::min(target, (ntiles + HS_MIN_TILES - 1) / HS_MIN_TILES));
-  int tps = (ntiles + target - 1) / target;
-  tps = std::max(1, std::min(tps, HS_MAX_ROWS / HS_ROWS));
-  const int splits = (ntiles + tps - 1) / tps;
-  return {std::min(splits, COMB_MAX), tps};
+  const int64_t blocks = (int64_t)Q * (d.n_h / 16);
+  SplitPlan best{0, 0};
+  double best_cost = 0.0;
+  for (int s = 1; s <= std::min(ntiles, COMB_MAX); ++s) {
+    const int tps = (ntiles + s - 1) / s;
+    if (tps > HS_MAX_ROWS / HS_ROWS || (ntiles + tps - 1) / tps != s) continue;
+    const int64_t per_cu = (blocks * s + HS_CUS - 1) / HS_CUS;
+    const double rounds = (double)((per_cu + 1) / 2);
+    const double cost = rounds * (tps * (per_cu > 1 ? 1.65 : 1.0) + 1.5) + (s > 1 ? 2.5 + 0.02 * s : 0.0);
+    if (best.splits == 0 || cost < best_cost) {
+      best = {s, tps};
+      best_cost = cost;
+    }
+  }
+  if (best.splits == 0) {   // more rows than COMB_MAX parts hold: callers reject such calls
+    const int tps = HS_MAX_ROWS / HS_ROWS;
+    best = {std::min(COMB_MAX, (ntiles + tps - 1) / tps), tps};
+  }
+  return best;
 }
 
 }  // namespace
