@@ -15,10 +15,21 @@
 //      11 bits at a time) narrow it until it is a single key value or is taken whole;
 //   3. one packed block scan gives every taken item its output slot: all items above the
 //      window, and the `need` lowest-index items of the window.
-// Rows of up to 8192 scores take one workgroup and one launch.  Longer rows are cut into
-// 8192-score segments; each keeps its own top k (a superset of its share of the answer
-// under the same total order), and a merge level selects from the candidate lists, which
-// stay in index order.
+// Rows of up to 8192 scores take one workgroup and one launch.  Longer rows go through a
+// threshold pass and a final pass:
+//   filter  one workgroup per (query, 8192-score segment).  All segments of a query draw the
+//           same sample (64 evenly spaced runs of 64 scores) and bin it linearly over its range; the
+//           bin b holding the sample's r-th largest, r chosen so that about 3k scores of the
+//           row are expected at or above it, is the threshold.  Binning is monotone in the
+//           score, so the scores in bins >= b form an upper set of the row: when it holds at
+//           least k scores it holds the top k (ties included).  Each segment writes its
+//           passing scores in index order with their count;
+//   final   one workgroup per query gathers the candidate lists (in index order) and selects
+//           k exactly, holding 2, 4 or 8 candidates per thread as their number requires.
+//           When the candidates are too few, too many, or a segment overflowed its list, it
+//           selects exactly from the whole row instead, 8192 - k scores at a time against the
+//           running top k held in LDS.
+// Wave reductions and scans use DPP lane moves and readlane rather than LDS-routed permutes.
 #include "csa_internal.h"
 
 namespace csa {
@@ -28,7 +39,10 @@ constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
 constexpr int TK_BINS = 2048;
 constexpr int TK_SEG = 8192;     // scores per segment (E = 8)
-constexpr int TK_MERGE = 8192;   // candidates one merge workgroup takes (E <= 8)
+constexpr int TK_NS = 4096;      // threshold sample (4 per thread)
+constexpr int TK_FINAL = 8192;   // candidates the final pass holds (E = 8)
+constexpr int TK_MAXSEG = 1024;  // segments per row
+constexpr int TK_MAXK = 4096;
 
 struct TopkShared {
   int hist[2][TK_BINS];
@@ -43,62 +57,68 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// ---- wave primitives on DPP (row-local lane moves, a few cycles each) and readlane, so
+// that reductions and scans avoid chains of LDS-routed lane permutes.  Every lane of the
+// wave must be active.
+template <int CTRL>
+__device__ __forceinline__ int dpp_(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ float wave_min_f(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-  return v;
+constexpr int DPP_QUAD_1032 = 0xB1, DPP_QUAD_2301 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+constexpr int DPP_SHR1 = 0x111, DPP_SHR2 = 0x112, DPP_SHR4 = 0x114, DPP_SHR8 = 0x118;
+
+// Combine over the 16 lanes of each row; every lane of the row gets the result.
+template <class F>
+__device__ __forceinline__ int row_allreduce(int x, F op) {
+  x = op(x, dpp_<DPP_QUAD_1032>(x));
+  x = op(x, dpp_<DPP_QUAD_2301>(x));
+  x = op(x, dpp_<DPP_HALF_MIRROR>(x));
+  return op(x, dpp_<DPP_MIRROR>(x));
 }
-__device__ __forceinline__ float wave_max_f(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+template <class F>
+__device__ __forceinline__ int wave_allreduce(int x, F op) {
+  x = row_allreduce(x, op);
+  return op(op(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+            op(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
-__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  return v;
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_<DPP_SHR1>(x);
+  x += dpp_<DPP_SHR2>(x);
+  x += dpp_<DPP_SHR4>(x);
+  x += dpp_<DPP_SHR8>(x);
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
 }
 
-// Cross-wave reductions of per-wave slots: lane j reads slot j & 15, then 16 lanes combine.
-__device__ __forceinline__ int slots_sum(const int* v) {
-  int x = v[threadIdx.x & 15];
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
+struct OpAdd { __device__ int operator()(int a, int b) const { return a + b; } };
+struct OpMinU { __device__ int operator()(int a, int b) const { return (int)min((uint32_t)a, (uint32_t)b); } };
+struct OpMaxU { __device__ int operator()(int a, int b) const { return (int)max((uint32_t)a, (uint32_t)b); } };
+struct OpMinF { __device__ int operator()(int a, int b) const { return __float_as_int(fminf(__int_as_float(a), __int_as_float(b))); } };
+struct OpMaxF { __device__ int operator()(int a, int b) const { return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b))); } };
+
+__device__ __forceinline__ int wave_sum_i(int v) { return wave_allreduce(v, OpAdd()); }
+__device__ __forceinline__ float wave_min_f(float v) { return __int_as_float(wave_allreduce(__float_as_int(v), OpMinF())); }
+__device__ __forceinline__ float wave_max_f(float v) { return __int_as_float(wave_allreduce(__float_as_int(v), OpMaxF())); }
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) { return (uint32_t)wave_allreduce((int)v, OpMinU()); }
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) { return (uint32_t)wave_allreduce((int)v, OpMaxU()); }
+
+// Cross-wave reductions of per-wave slots: lane j reads slot j & 15, then each row of 16
+// lanes combines them.
+__device__ __forceinline__ int slots_sum(const int* v) { return row_allreduce(v[threadIdx.x & 15], OpAdd()); }
 __device__ __forceinline__ float slots_min(const float* v) {
-  float x = v[threadIdx.x & 15];
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) x = fminf(x, __shfl_xor(x, o, 64));
-  return x;
+  return __int_as_float(row_allreduce(__float_as_int(v[threadIdx.x & 15]), OpMinF()));
 }
 __device__ __forceinline__ float slots_max(const float* v) {
-  float x = v[threadIdx.x & 15];
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+  return __int_as_float(row_allreduce(__float_as_int(v[threadIdx.x & 15]), OpMaxF()));
 }
 __device__ __forceinline__ uint32_t slots_min_u(const uint32_t* v) {
-  uint32_t x = v[threadIdx.x & 15];
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o, 64));
-  return x;
+  return (uint32_t)row_allreduce((int)v[threadIdx.x & 15], OpMinU());
 }
 __device__ __forceinline__ uint32_t slots_max_u(const uint32_t* v) {
-  uint32_t x = v[threadIdx.x & 15];
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o, 64));
-  return x;
+  return (uint32_t)row_allreduce((int)v[threadIdx.x & 15], OpMaxU());
 }
 
 // Wave 0: find the bin d with S(d) >= rem > S(d + 1), S(d) = number of items in bins >= d,
@@ -111,24 +131,17 @@ __device__ void find_bin(const int* H, int rem, TopkShared& sh) {
   int own = 0;
 #pragma unroll
   for (int j = 0; j < 32; ++j) own += H[32 * lane + ((j + lane) & 31)];
-  int suf = own;  // inclusive suffix sum over lanes >= lane
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_down(suf, o, 64);
-    if (lane + o < 64) suf += y;
-  }
-  const int after = suf - own;  // items in bins of higher lanes
+  const int incl = wave_incl_scan(own);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  const int suf = total - incl + own;  // items in bins of lanes >= lane
+  const int after = suf - own;         // items in bins of higher lanes
   const unsigned long long hit = __ballot(suf >= rem && after < rem);
   const int L = __ffsll(hit) - 1;  // exactly one lane
-  const int base = __shfl(after, L, 64);
+  const int base = __builtin_amdgcn_readlane(after, L);
   const int j = lane & 31;
-  const int h = H[32 * L + j];
-  int s = h;  // items in bins 32L + j .. 32L + 31
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) {
-    const int y = __shfl_down(s, o, 64);
-    if (j + o < 32) s += y;
-  }
+  const int h = lane < 32 ? H[32 * L + j] : 0;
+  const int pin = wave_incl_scan(h);   // lanes 0..31: bins 32L .. 32L + j
+  const int s = __builtin_amdgcn_readlane(pin, 31) - pin + h;  // bins 32L + j .. 32L + 31
   if (lane < 32 && base + s >= rem && base + s - h < rem) {
     sh.sel_bin = 32 * L + j;
     sh.sel_above = base + s - h;
@@ -264,18 +277,12 @@ __device__ int select_topk(const Items& it, int k, TopkShared& sh, int* out_idx,
     eq += c == 1 ? 1 : 0;
   }
   // one exclusive block scan of (gt << 16 | eq); block totals stay below 65536
-  int x = (gt << 16) | eq;
-  const int own = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const int own = (gt << 16) | eq;
+  const int x = wave_incl_scan(own);
   if (lane == 63) sh.scan[w] = x;
   __syncthreads();
-  int before = (threadIdx.x & 15) < w ? sh.scan[threadIdx.x & 15] : 0;  // waves ahead of this one
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) before += __shfl_xor(before, o, 64);
+  // waves ahead of this one
+  const int before = row_allreduce((threadIdx.x & 15) < w ? sh.scan[threadIdx.x & 15] : 0, OpAdd());
   const int ex = x - own + before;
   int gt_before = ex >> 16, eq_before = ex & 0xffff;
 #pragma unroll
@@ -354,40 +361,188 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_segment(
   }
 }
 
-// Merge level: blockIdx.x = query, blockIdx.y = group of G consecutive candidate lists
-// (of nlist per query, k each, in index order).  direct != 0: one group covers every list;
-// write the final selection.  Otherwise write one list of k per group.
-template <int E>
-__global__ __launch_bounds__(TK_THREADS) void k_topk_merge(
-    const int32_t* __restrict__ in_idx, const uint32_t* __restrict__ in_key, int nlist, int G,
-    int k, int direct, int32_t* __restrict__ idx_out, int32_t* __restrict__ out_idx,
-    uint32_t* __restrict__ out_key) {
+// Threshold pass: blockIdx.x = query, blockIdx.y = segment.  Writes the segment's scores in
+// bins at or above the threshold bin (all valid scores when the row has at most TK_FINAL)
+// to cand_idx/cand_key [Q][nseg][cs] in index order, and their count (which may exceed cs)
+// to cand_cnt [Q][nseg].
+__global__ __launch_bounds__(TK_THREADS) void k_topk_filter(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries, int m, int k,
+    int cs, int32_t* __restrict__ cand_idx, uint32_t* __restrict__ cand_key,
+    int32_t* __restrict__ cand_cnt) {
   __shared__ TopkShared sh;
-  const int q = blockIdx.x, grp = blockIdx.y, ngrp = gridDim.y;
-  const int l0 = grp * G, l1 = min(nlist, l0 + G);
-  const int n = (l1 - l0) * k;
-  const int32_t* ci = in_idx + ((size_t)q * nlist + l0) * k;
-  const uint32_t* ck = in_key + ((size_t)q * nlist + l0) * k;
+  const int q = blockIdx.x, seg = blockIdx.y, nseg = gridDim.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int V = visible(q_seq, q_pos, n_entries, m, q);
+  const float* row = scores + (size_t)q * ld;
+  const bool vec = (ld & 3) == 0;
+  const bool take_all = V <= TK_FINAL;
+  // this thread's run of the segment, then its 4 samples: the sample is 64 evenly spaced runs
+  // of 64 scores (V > TK_FINAL, so the runs fit), the same for every segment of the row
+  const int first = seg * TK_SEG + tid * 8;
+  float sv[8], smp[4];
+  if (first + 8 <= V && vec) {
+    const float4 a = *reinterpret_cast<const float4*>(row + first);
+    const float4 b = *reinterpret_cast<const float4*>(row + first + 4);
+    sv[0] = a.x; sv[1] = a.y; sv[2] = a.z; sv[3] = a.w;
+    sv[4] = b.x; sv[5] = b.y; sv[6] = b.z; sv[7] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sv[i] = first + i < V ? row[first + i] : 0.f;
+  }
+  if (!take_all) {   // uniform
+    const int bs = ((int)((int64_t)(tid >> 4) * (V - 64) / 63) & ~3) + 4 * (tid & 15);
+    if (vec) {
+      const float4 v = *reinterpret_cast<const float4*>(row + bs);
+      smp[0] = v.x; smp[1] = v.y; smp[2] = v.z; smp[3] = v.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) smp[i] = row[bs + i];
+    }
+  }
+  int tbin = 0;
+  float fmn = 0.f, scale = 0.f;
+  if (!take_all) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) smp[i] = key_score(score_key(smp[i]));
+    float lo = fminf(fminf(smp[0], smp[1]), fminf(smp[2], smp[3]));
+    float hi = fmaxf(fmaxf(smp[0], smp[1]), fmaxf(smp[2], smp[3]));
+    lo = wave_min_f(lo);
+    hi = wave_max_f(hi);
+    if (lane == 0) { sh.red_lo[w] = lo; sh.red_hi[w] = hi; }
+    for (int b = tid; b < TK_BINS; b += TK_THREADS) sh.hist[0][b] = 0;
+    __syncthreads();
+    fmn = slots_min(sh.red_lo);
+    const float range = slots_max(sh.red_hi) - fmn;
+    scale = (range > 0.f && range < INFINITY) ? (float)TK_BINS / range : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) atomicAdd(&sh.hist[0][min(TK_BINS - 1, (int)((smp[i] - fmn) * scale))], 1);
+    __syncthreads();
+    // samples at or above the threshold: about 3k (at most 3/4 of the final capacity) of
+    // the row's V scores are then expected to pass
+    const int target = min(3 * k, TK_FINAL * 3 / 4);
+    const int r = (int)min((int64_t)TK_NS, ((int64_t)target * TK_NS + V - 1) / V);
+    if (w == 0) find_bin(sh.hist[0], r, sh);
+    __syncthreads();
+    tbin = sh.sel_bin;
+  }
+  // bins are monotone in the score (scores below the sample's minimum fall in bin -1)
+  auto passes = [&](int i) {
+    if (first + i >= V) return false;
+    if (take_all) return true;
+    const float f = key_score(score_key(sv[i]));
+    return (int)fminf(fmaxf((f - fmn) * scale, -1.f), (float)(TK_BINS - 1)) >= tbin;
+  };
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) cnt += passes(i) ? 1 : 0;
+  const int x = wave_incl_scan(cnt);   // over the wave, then over the waves
+  if (lane == 63) sh.scan[w] = x;
+  __syncthreads();
+  const int sw = sh.scan[tid & 15];
+  const int before = row_allreduce((tid & 15) < w ? sw : 0, OpAdd());
+  const int total = row_allreduce(sw, OpAdd());
+  int pos = before + x - cnt;
+  int32_t* ci = cand_idx + ((size_t)q * nseg + seg) * cs;
+  uint32_t* ck = cand_key + ((size_t)q * nseg + seg) * cs;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (passes(i)) {
+      if (pos < cs) {
+        ci[pos] = first + i;
+        ck[pos] = score_key(sv[i]);
+      }
+      ++pos;
+    }
+  if (tid == 0) cand_cnt[(size_t)q * nseg + seg] = total;
+}
+
+struct FinalShared {
+  TopkShared sh;
+  int segoff[TK_MAXSEG + 1];
+  int r_idx[TK_MAXK];
+  uint32_t r_key[TK_MAXK];
+};
+
+// The candidates (N <= TK_THREADS * E, in index order) into E items per thread; select k.
+template <int E>
+__device__ int final_fast(int q, int nseg, int cs, int N, int k, const int32_t* __restrict__ cand_idx,
+                          const uint32_t* __restrict__ cand_key, FinalShared& fs, int32_t* out) {
+  const int tid = threadIdx.x;
   ListItems<E> it;
+  const int p0 = tid * E;
+  int sg = 0;   // segment of p0: the last with segoff <= p0
+  for (int step = TK_MAXSEG; step >= 1; step >>= 1)
+    if (sg + step <= nseg && fs.segoff[sg + step] <= p0) sg += step;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    const int p = threadIdx.x * E + i;
-    it.id[i] = p < n ? ci[p] : -1;
-    it.key[i] = it.id[i] >= 0 ? ck[p] : 0u;
+    const int p = p0 + i;
+    while (sg < nseg && fs.segoff[sg + 1] <= p) ++sg;
+    const int sc = min(sg, nseg - 1);
+    const size_t at = ((size_t)q * nseg + sc) * cs + (p - fs.segoff[sc]);
+    const bool ok = p < N;
+    it.id[i] = ok ? cand_idx[at] : -1;
+    it.key[i] = ok ? cand_key[at] : 0u;
   }
-  int32_t* oidx;
-  uint32_t* okey = nullptr;
-  if (direct) {
-    oidx = idx_out + (size_t)q * k;
+  return select_topk<E>(it, k, fs.sh, out, nullptr);
+}
+
+// Final pass: blockIdx.x = query.  Selects k from the candidate lists, or from the whole row
+// when they cannot be trusted (see the file comment), and writes idx_out [Q][k].
+__global__ __launch_bounds__(TK_THREADS) void k_topk_final(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries, int m, int k,
+    int nseg, int cs, const int32_t* __restrict__ cand_idx, const uint32_t* __restrict__ cand_key,
+    const int32_t* __restrict__ cand_cnt, int32_t* __restrict__ idx_out) {
+  __shared__ FinalShared fs;
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int V = visible(q_seq, q_pos, n_entries, m, q);
+  int32_t* out = idx_out + (size_t)q * k;
+  // segment offsets (one segment per thread, nseg <= TK_MAXSEG = TK_THREADS)
+  const int c = tid < nseg ? cand_cnt[(size_t)q * nseg + tid] : 0;
+  const int x = wave_incl_scan(c);
+  if (lane == 63) fs.sh.scan[w] = x;
+  const bool over = __syncthreads_or(c > cs) != 0;
+  const int sw = fs.sh.scan[tid & 15];
+  const int before = row_allreduce((tid & 15) < w ? sw : 0, OpAdd());
+  const int N = row_allreduce(sw, OpAdd());
+  if (tid < nseg) fs.segoff[tid] = before + x - c;
+  if (tid == 0) fs.segoff[nseg] = N;
+  __syncthreads();
+  int n;
+  if (!over && N >= min(k, V) && N <= TK_FINAL) {   // uniform
+    if (N <= 2 * TK_THREADS) n = final_fast<2>(q, nseg, cs, N, k, cand_idx, cand_key, fs, out);
+    else if (N <= 4 * TK_THREADS) n = final_fast<4>(q, nseg, cs, N, k, cand_idx, cand_key, fs, out);
+    else n = final_fast<8>(q, nseg, cs, N, k, cand_idx, cand_key, fs, out);
   } else {
-    oidx = out_idx + ((size_t)q * ngrp + grp) * k;
-    okey = out_key + ((size_t)q * ngrp + grp) * k;
+    // exact selection over the whole row: the running top k (in index order, in LDS) plus
+    // the next TK_FINAL - k scores, once per chunk
+    const float* row = scores + (size_t)q * ld;
+    const int ch = TK_FINAL - k;
+    int nr = 0;
+    for (int c0 = 0; c0 < V; c0 += ch) {
+      ListItems<8> it;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int p = tid * 8 + i;
+        if (p < nr) {
+          it.id[i] = fs.r_idx[p];
+          it.key[i] = fs.r_key[p];
+        } else {
+          const int e = c0 + (p - nr);
+          const bool ok = p - nr < ch && e < V;
+          it.id[i] = ok ? e : -1;
+          it.key[i] = ok ? score_key(row[e]) : 0u;
+        }
+      }
+      __syncthreads();   // the running list is read before it is rewritten
+      nr = select_topk<8>(it, k, fs.sh, fs.r_idx, fs.r_key);
+      __syncthreads();
+    }
+    for (int i = tid; i < nr; i += TK_THREADS) out[i] = fs.r_idx[i];
+    n = nr;
   }
-  const int cnt = select_topk<E>(it, k, sh, oidx, okey);
-  for (int i = cnt + threadIdx.x; i < k; i += TK_THREADS) {
-    oidx[i] = -1;
-    if (okey) okey[i] = 0u;
-  }
+  for (int i = n + tid; i < k; i += TK_THREADS) out[i] = -1;
 }
 
 int items_E(int n) {
@@ -396,98 +551,50 @@ int items_E(int n) {
   return E;
 }
 
-// One selection tree: segments of TK_SEG scores, then merges of up to TK_MERGE candidates.
-struct TopkPlan {
-  int nseg;        // level-0 segments (0: the whole row in one direct workgroup)
-  int seg_E;
-  int levels;      // merge levels after level 0
-};
-
-TopkPlan plan_topk(int k, int cap) {
-  TopkPlan p{0, items_E(cap), 0};
-  if (cap <= TK_SEG) return p;
-  p.nseg = (cap + TK_SEG - 1) / TK_SEG;
-  p.seg_E = TK_SEG / TK_THREADS;
-  int lists = p.nseg;
-  const int G = std::max(2, TK_MERGE / k);
-  while (true) {
-    ++p.levels;
-    if ((long)lists * k <= TK_MERGE) break;
-    lists = (lists + G - 1) / G;
-  }
-  return p;
-}
-
-#define TK_SEG_LAUNCH(EE, grid, direct, out_idx, cidx, ckey)                                     \
-  hipLaunchKernelGGL((k_topk_segment<EE>), grid, dim3(TK_THREADS), 0, s, scores, ld, q_seq, q_pos, \
-                     c.n_entries, d.m, k, direct, out_idx, cidx, ckey)
-#define TK_MERGE_LAUNCH(EE, grid, group)                                                          \
-  hipLaunchKernelGGL((k_topk_merge<EE>), grid, dim3(TK_THREADS), 0, s, in_i, in_k, lists, group, k, \
-                     direct, idx, out_i, out_k)
+int filter_cap(int k) { return std::min(TK_SEG, std::max(1024, 4 * k)); }
 
 }  // namespace
 
 int32_t topk_max_visible(const csa_dims& d) {
-  if (d.top_k <= 0 || 2 * d.top_k > TK_MERGE) return 0;
-  return INT32_MAX / 2;
+  if (d.top_k <= 0 || d.top_k > TK_MAXK) return 0;
+  return TK_SEG * TK_MAXSEG;
 }
 
 size_t topk_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap) {
-  const TopkPlan p = plan_topk(d.top_k, cap);
-  if (p.nseg == 0) return 0;
-  // two ping-pong candidate buffers, the first sized for level 0
-  const int G = std::max(2, TK_MERGE / d.top_k);
-  const size_t lists1 = (size_t)(p.nseg + G - 1) / G;
-  const size_t per = (size_t)Q * d.top_k * (sizeof(int32_t) + sizeof(uint32_t));
-  return per * ((size_t)p.nseg + lists1);
+  if (cap <= TK_SEG) return 0;
+  const size_t nseg = (size_t)(cap + TK_SEG - 1) / TK_SEG;
+  const size_t cs = (size_t)filter_cap(d.top_k);
+  return (size_t)Q * nseg * (cs * (sizeof(int32_t) + sizeof(uint32_t)) + sizeof(int32_t));
 }
 
 hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
                        const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld,
                        int32_t* idx, void* ws, hipStream_t s) {
   const int k = d.top_k;
-  const TopkPlan p = plan_topk(k, c.cap);
-  if (p.nseg == 0) {
-    switch (p.seg_E) {
-      case 1: TK_SEG_LAUNCH(1, dim3(Q, 1), 1, idx, nullptr, nullptr); break;
-      case 2: TK_SEG_LAUNCH(2, dim3(Q, 1), 1, idx, nullptr, nullptr); break;
-      case 4: TK_SEG_LAUNCH(4, dim3(Q, 1), 1, idx, nullptr, nullptr); break;
-      default: TK_SEG_LAUNCH(8, dim3(Q, 1), 1, idx, nullptr, nullptr); break;
+  if (c.cap <= TK_SEG) {
+#define TK_DIRECT(EE)                                                                          \
+  hipLaunchKernelGGL((k_topk_segment<EE>), dim3(Q, 1), dim3(TK_THREADS), 0, s, scores, ld, q_seq, \
+                     q_pos, c.n_entries, d.m, k, 1, idx, nullptr, nullptr)
+    switch (items_E(c.cap)) {
+      case 1: TK_DIRECT(1); break;
+      case 2: TK_DIRECT(2); break;
+      case 4: TK_DIRECT(4); break;
+      default: TK_DIRECT(8); break;
     }
+#undef TK_DIRECT
     return hipGetLastError();
   }
-  const int G = std::max(2, TK_MERGE / k);
-  const size_t lists1 = (size_t)(p.nseg + G - 1) / G;
-  int32_t* bufA_i = (int32_t*)ws;
-  uint32_t* bufA_k = (uint32_t*)(bufA_i + (size_t)Q * p.nseg * k);
-  int32_t* bufB_i = (int32_t*)(bufA_k + (size_t)Q * p.nseg * k);
-  uint32_t* bufB_k = (uint32_t*)(bufB_i + (size_t)Q * lists1 * k);
-  TK_SEG_LAUNCH(8, dim3(Q, p.nseg), 0, idx, bufA_i, bufA_k);
+  const int nseg = (c.cap + TK_SEG - 1) / TK_SEG;
+  const int cs = filter_cap(k);
+  int32_t* ci = (int32_t*)ws;
+  uint32_t* ck = (uint32_t*)(ci + (size_t)Q * nseg * cs);
+  int32_t* cc = (int32_t*)(ck + (size_t)Q * nseg * cs);
+  hipLaunchKernelGGL(k_topk_filter, dim3(Q, nseg), dim3(TK_THREADS), 0, s, scores, ld, q_seq, q_pos,
+                     c.n_entries, d.m, k, cs, ci, ck, cc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int lists = p.nseg;
-  const int32_t* in_i = bufA_i;
-  const uint32_t* in_k = bufA_k;
-  bool in_A = true;
-  for (int lev = 0; lev < p.levels; ++lev) {
-    const int direct = (long)lists * k <= TK_MERGE ? 1 : 0;
-    const int groups = direct ? 1 : (lists + G - 1) / G;
-    const int per_group = direct ? lists : G;
-    int32_t* out_i = in_A ? bufB_i : bufA_i;
-    uint32_t* out_k = in_A ? bufB_k : bufA_k;
-    switch (items_E(per_group * k)) {
-      case 1: TK_MERGE_LAUNCH(1, dim3(Q, groups), per_group); break;
-      case 2: TK_MERGE_LAUNCH(2, dim3(Q, groups), per_group); break;
-      case 4: TK_MERGE_LAUNCH(4, dim3(Q, groups), per_group); break;
-      default: TK_MERGE_LAUNCH(8, dim3(Q, groups), per_group); break;
-    }
-    e = hipGetLastError();
-    if (e != hipSuccess || direct) return e;
-    lists = groups;
-    in_i = out_i;
-    in_k = out_k;
-    in_A = !in_A;
-  }
+  hipLaunchKernelGGL(k_topk_final, dim3(Q), dim3(TK_THREADS), 0, s, scores, ld, q_seq, q_pos,
+                     c.n_entries, d.m, k, nseg, cs, ci, ck, cc, idx);
   return hipGetLastError();
 }
 

@@ -503,29 +503,35 @@ def test_c4_prefill_full_size_sampled():
 
 def test_topk_exact_on_crafted_scores():
     """csa_topk on given scores must equal the oracle's selection exactly (same input bits):
-    heavy ties (integer scores), -0/+0, rows shorter than k, exactly k, k + 1, ragged segment
-    tails, and a row long enough for two merge levels (90001 entries, k = 1024)."""
+    heavy ties (integer scores), -0/+0, scores rising or falling with the index (every
+    candidate in one segment), rows shorter than k, exactly k, k + 1, ragged segment tails,
+    and long rows (90001 entries, k = 1024).  Ties and -0/+0 rows defeat the sampled
+    threshold, so they also exercise the exact whole-row fallback."""
     for k, cap in ((1024, 90001), (512, 4096), (8, 37), (512, 33000)):
         cfg = _qcfg(top_k=k)
         dims = L.Dims.from_config(cfg)
         m = cfg["m"]
         Vs = sorted({0, 1, min(k, cap), min(k + 1, cap), cap // 3, cap - 5, cap})
-        Q = len(Vs) * 3
+        Q = len(Vs) * 5
         cache = L.Cache(dims, B=1, cap=cap, win_cap=128)
         cache.n_entries.fill_(cap)
         rng = np.random.default_rng(k + cap)
         sc = np.zeros((Q, cap), dtype=np.float32)
         pos = []
         for i in range(Q):
-            V = Vs[i // 3]
-            kind = i % 3
+            V = Vs[i // 5]
+            kind = i % 5
             if kind == 0:
                 sc[i] = rng.standard_normal(cap).astype(np.float32)
             elif kind == 1:
                 sc[i] = rng.integers(-3, 4, cap).astype(np.float32)
-            else:
+            elif kind == 2:
                 sc[i] = np.where(rng.random(cap) < 0.5, -0.0, 0.0).astype(np.float32)
                 sc[i, rng.integers(0, cap, 5)] = 1.0
+            elif kind == 3:
+                sc[i] = (np.arange(cap) * 1e-3 + rng.random(cap) * 1e-4).astype(np.float32)
+            else:
+                sc[i] = (-np.arange(cap) * 1e-3).astype(np.float32)
             pos.append(m * V + (i % m))
         scores = torch.from_numpy(sc).to(DEV)
         idx = torch.full((Q, k), -7, dtype=torch.int32, device=DEV)
@@ -534,8 +540,8 @@ def test_topk_exact_on_crafted_scores():
         torch.cuda.synchronize()
         gi = idx.cpu().numpy()
         for i in range(Q):
-            V = Vs[i // 3]
+            V = Vs[i // 5]
             ref = R.topk(sc[i, :V].astype(np.float64), k)
             got = gi[i][gi[i] >= 0]
-            assert np.array_equal(got, ref), f"k={k} cap={cap} V={V} kind={i % 3}"
+            assert np.array_equal(got, ref), f"k={k} cap={cap} V={V} kind={i % 5}"
             assert np.all(gi[i][len(got):] == -1)
