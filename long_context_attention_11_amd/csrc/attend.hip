@@ -259,10 +259,7 @@ void k_attend_hs(AttendArgs a) {
   // wave's entry indices and the RoPE table at tau
   {
     float ss = (sumsq_bf16x8(qr0) + sumsq_bf16x8(qr1)) + (sumsq_bf16x8(qr2) + sumsq_bf16x8(qr3));
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
-    ss += __shfl_xor(ss, 4, 64);
-    ss += __shfl_xor(ss, 8, 64);
+    ss = __int_as_float(row_allreduce(__float_as_int(ss), OpAddF()));
     const float inv = 1.0f / sqrtf(ss / (float)AC + a.eps);
     if (!a.gamma_q) {
 #pragma unroll
@@ -348,8 +345,8 @@ void k_attend_hs(AttendArgs a) {
       S[e] = rv ? S[e] * a.scale_log2 : -INFINITY;
       mx = fmaxf(mx, S[e]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = fmaxf(mx, lane_xor16(mx));
+    mx = fmaxf(mx, lane_xor32(mx));
     if (g == 0) redm[wave][col] = mx;
     lds_barrier();
     const float m_tile = fmaxf(fmaxf(redm[0][col], redm[1][col]), fmaxf(redm[2][col], redm[3][col]));
@@ -402,8 +399,8 @@ void k_attend_hs(AttendArgs a) {
 
   // the sum over all rows: lanes hold a wave's 16 rows of one tile position (4g + e), summed
   // over lane groups here and over waves through LDS
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run += lane_xor16(l_run);
+  l_run += lane_xor32(l_run);
   if (g == 0) reds[wave][col] = l_run;
   lds_barrier();
   l_run = ((reds[0][col] + reds[1][col]) + reds[2][col]) + reds[3][col];

@@ -134,8 +134,8 @@ __global__ __launch_bounds__(256) void k_indexer_bf16(
           for (int e = 0; e < 4; ++e) part = fmaf(W[qq][ht][e], fmaxf(acc[e], 0.f), part);
         }
         // lane groups summed as (g + g^2) + (g^1 + g^3), the order the tiled kernel uses
-        part += __shfl_xor(part, 32, 64);
-        part += __shfl_xor(part, 16, 64);
+        part += lane_xor32(part);
+        part += lane_xor16(part);
         const int s = s0 + col;
         if (g == 0 && s < min(V[qq], c_hi)) scores[(size_t)(q0 + qq) * ld + s] = part;
       }
@@ -283,14 +283,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int qq = 0; qq < 2; ++qq) {
           const float keep = hi2 ? part[2 + j][qq] : part[j][qq];
           const float send = hi2 ? part[j][qq] : part[2 + j][qq];
-          r1[j][qq] = keep + __shfl_xor(send, 32, 64);
+          r1[j][qq] = keep + lane_xor32(send);
         }
       const int s = e_lo + st * IT_STAGE + sub * 64 + g * 16 + col;
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
         const float keep = odd ? r1[1][qq] : r1[0][qq];
         const float send = odd ? r1[0][qq] : r1[1][qq];
-        const float total = keep + __shfl_xor(send, 16, 64);
+        const float total = keep + lane_xor16(send);
         if (s < min(V[qq], e_hi)) scores[(size_t)(qt0 + 2 * wave + qq) * ld + s] = total;
       }
     }

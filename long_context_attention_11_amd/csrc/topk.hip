@@ -57,42 +57,6 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// ---- wave primitives on DPP (row-local lane moves, a few cycles each) and readlane, so
-// that reductions and scans avoid chains of LDS-routed lane permutes.  Every lane of the
-// wave must be active.
-template <int CTRL>
-__device__ __forceinline__ int dpp_(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
-}
-constexpr int DPP_QUAD_1032 = 0xB1, DPP_QUAD_2301 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
-constexpr int DPP_SHR1 = 0x111, DPP_SHR2 = 0x112, DPP_SHR4 = 0x114, DPP_SHR8 = 0x118;
-
-// Combine over the 16 lanes of each row; every lane of the row gets the result.
-template <class F>
-__device__ __forceinline__ int row_allreduce(int x, F op) {
-  x = op(x, dpp_<DPP_QUAD_1032>(x));
-  x = op(x, dpp_<DPP_QUAD_2301>(x));
-  x = op(x, dpp_<DPP_HALF_MIRROR>(x));
-  return op(x, dpp_<DPP_MIRROR>(x));
-}
-template <class F>
-__device__ __forceinline__ int wave_allreduce(int x, F op) {
-  x = row_allreduce(x, op);
-  return op(op(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
-            op(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
-}
-// Inclusive prefix sum over the 64 lanes.
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  x += dpp_<DPP_SHR1>(x);
-  x += dpp_<DPP_SHR2>(x);
-  x += dpp_<DPP_SHR4>(x);
-  x += dpp_<DPP_SHR8>(x);
-  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
-            r2 = __builtin_amdgcn_readlane(x, 47);
-  const int row = (threadIdx.x & 63) >> 4;
-  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
-}
-
 struct OpAdd { __device__ int operator()(int a, int b) const { return a + b; } };
 struct OpMinU { __device__ int operator()(int a, int b) const { return (int)min((uint32_t)a, (uint32_t)b); } };
 struct OpMaxU { __device__ int operator()(int a, int b) const { return (int)max((uint32_t)a, (uint32_t)b); } };
