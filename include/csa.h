@@ -266,6 +266,11 @@ int csa_attend(const csa_dims* dims, const csa_cache* cache, const void* q,
  *   q, qI, w  per-query inputs as in csa_index_topk / csa_attend, Q = B*T.
  *   idx_out   [Q][top_k] int32 receiving the selection, or NULL (CSA: then it lives in ws).
  * The indexer works on q_chunk queries at a time, the largest that fits ws_bytes.
+ * With T = 1 a query at tau sees floor(tau / m) entries, none of which the call's own
+ * compression writes, so for CSA the library may score and select before compressing (the
+ * one-token projection then shares a launch with the top-k threshold pass).  For a cache whose
+ * n_entries keeps pace with the positions the result is the same either way; when it trails
+ * them, T = 1 calls score the entries present before the call.
  */
 int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cache,
                 const void* H, int32_t T, const int32_t* pos0, const void* q, const void* qI,

@@ -173,7 +173,7 @@ void k_attend_hs(AttendArgs a) {
   const int myrow = wave * 16 + col;   // this lane's row within a tile (Q.K side)
   const int r_lo = split * a.tiles_per_split * HS_ROWS;
   const int32_t* qidx = SPARSE ? a.idx + (size_t)q * a.k : nullptr;
-  const int seq = a.q_seq[q];
+  const int seq = a.q_seq ? a.q_seq[q] : q;
   const int tau = a.q_pos[q];
 
   // ---- first the loads that depend on no other load: the entry indices of this lane's rows
@@ -494,7 +494,7 @@ __global__ __launch_bounds__(64) void k_attend_f32(const float* __restrict__ qv,
   __shared__ const float* rows[AF_MAXK];
   const int qh = blockIdx.x;
   const int q = qh / n_h, h = qh % n_h, t = threadIdx.x;
-  const int seq = q_seq[q], tau = q_pos[q];
+  const int seq = q_seq ? q_seq[q] : q, tau = q_pos[q];
   const int V = max(0, min(tau / m, n_entries[seq]));
   const int nsel = idx ? k : V;
   const int w0 = max(0, tau - n_win + 1);

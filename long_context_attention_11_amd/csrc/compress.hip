@@ -8,6 +8,7 @@
 // (RoPE dims in BF16, the rest FP8); deep dive "DeepSeek-V4 架构设计深度解析" §3.2 (indexer keys
 // use the same compression with a smaller width).
 #include "csa_internal.h"
+#include "step_project.h"
 
 namespace csa {
 
@@ -136,64 +137,9 @@ __global__ __launch_bounds__(256) void k_project_f32(const float* __restrict__ H
 
 // ============================================================================ fold / finalize
 
-// One-token step (T = 1), bf16: a 16-row x 16-column output tile per workgroup of 16 waves.
-// The waves split K in sixteen; each loads its weight rows straight into MFMA operands
-// (DEPTH steps per round: at d = 4096 one round, so every load is in flight at once), and
-// the sixteen partial tiles are summed through LDS in a fixed order.  The result goes directly into the
-// sequence's projection-state slot for the token (pos0[b] % S), where the fold reads it,
-// so there is no separate split-K reduction or state copy.
-constexpr int SK_DEPTH = 8;
-
-constexpr int SK_WAVES = 16;
-
-__global__ __launch_bounds__(1024) void k_project_step(const uint16_t* __restrict__ H,
-                                                      const uint16_t* __restrict__ wkv,
-                                                      const uint16_t* __restrict__ widx, int nkv,
-                                                      int M, int NP, int K,
-                                                      const int32_t* __restrict__ pos0, int S,
-                                                      float* __restrict__ state) {
-  __shared__ float red[SK_WAVES][16 * 16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int fr = lane & 15, fg = lane >> 4;
-  const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
-  const int kq = K / SK_WAVES;                // this wave's share of K (a multiple of 32)
-  const int kb = wave * kq + fg * 8;
-  const uint16_t* arow = H + (size_t)min(m0 + fr, M - 1) * K + kb;
-  const uint16_t* brow = wall_row(wkv, widx, nkv, min(n0 + fr, NP - 1), K) + kb;
-  const int nsteps = kq / 32;
-  uint4 ra[SK_DEPTH], rb[SK_DEPTH];
-#pragma unroll
-  for (int i = 0; i < SK_DEPTH; ++i) {
-    const int k = min(i, nsteps - 1) * 32;
-    ra[i] = *reinterpret_cast<const uint4*>(arow + k);
-    rb[i] = *reinterpret_cast<const uint4*>(brow + k);
-  }
-  f32x4 acc = {0, 0, 0, 0};
-  for (int s0 = 0; s0 < nsteps; s0 += SK_DEPTH) {
-#pragma unroll
-    for (int i = 0; i < SK_DEPTH; ++i) {
-      // a step past the end reloads the last one and is not accumulated
-      const bool live = s0 + i < nsteps;
-      const bf16x8 A = __builtin_bit_cast(bf16x8, ra[i]);
-      const bf16x8 Bv = __builtin_bit_cast(bf16x8, rb[i]);
-      const f32x4 nxt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bv, acc, 0, 0, 0);
-      acc = live ? nxt : acc;
-      const int k = min(s0 + i + SK_DEPTH, nsteps - 1) * 32;
-      ra[i] = *reinterpret_cast<const uint4*>(arow + k);
-      rb[i] = *reinterpret_cast<const uint4*>(brow + k);
-    }
-  }
-  // D layout: lane holds column fr, rows 4*fg + e
-#pragma unroll
-  for (int e = 0; e < 4; ++e) red[wave][(4 * fg + e) * 16 + fr] = acc[e];
-  __syncthreads();
-  if (tid >= 256) return;
-  const int row = tid >> 4, col = tid & 15;
-  float v = red[0][tid];
-#pragma unroll
-  for (int w = 1; w < SK_WAVES; ++w) v += red[w][tid];
-  const int b = m0 + row, n = n0 + col;
-  if (b < M && n < NP) state[((size_t)b * S + (pos0[b] % S)) * NP + n] = v;
+__global__ __launch_bounds__(1024) void k_project_step(ProjectStepArgs a) {
+  __shared__ float red[PS_WAVES][256];
+  project_step_tile(a, blockIdx.x, blockIdx.y, red);
 }
 
 struct FoldArgs {
@@ -430,17 +376,30 @@ hipError_t launch_project(const csa_dims& d, const csa_weights& w, const void* H
 }
 
 bool project_step_ok(const csa_dims& d, int32_t T) {
-  return T == 1 && d.act_fmt == CSA_FMT_BF16 && d.d % (32 * SK_WAVES) == 0;
+  return T == 1 && d.act_fmt == CSA_FMT_BF16 && d.d % (32 * PS_WAVES) == 0;
+}
+
+ProjectStepArgs project_step_args(const csa_dims& d, const csa_weights& w, const csa_cache& c,
+                                  const void* H, const int32_t* pos0) {
+  ProjectStepArgs a;
+  a.H = (const uint16_t*)H;
+  a.wkv = (const uint16_t*)w.w_kv;
+  a.widx = (const uint16_t*)w.w_idx;
+  a.nkv = d.dual ? 4 * d.c : 2 * d.c;
+  a.M = c.B;
+  a.NP = state_width(d);
+  a.K = d.d;
+  a.pos0 = pos0;
+  a.S = state_rows(d);
+  a.state = c.state;
+  return a;
 }
 
 hipError_t launch_project_step(const csa_dims& d, const csa_weights& w, const csa_cache& c,
                                const void* H, const int32_t* pos0, hipStream_t s) {
-  const int NP = state_width(d);
-  const int nkv = d.dual ? 4 * d.c : 2 * d.c;
-  dim3 grid((NP + 15) / 16, (c.B + 15) / 16);
-  hipLaunchKernelGGL(k_project_step, grid, dim3(64 * SK_WAVES), 0, s, (const uint16_t*)H,
-                     (const uint16_t*)w.w_kv, (const uint16_t*)w.w_idx, nkv, c.B, NP, d.d, pos0,
-                     state_rows(d), c.state);
+  const ProjectStepArgs a = project_step_args(d, w, c, H, pos0);
+  dim3 grid(project_step_grid_x(a.NP), project_step_grid_y(a.M));
+  hipLaunchKernelGGL(k_project_step, grid, dim3(64 * PS_WAVES), 0, s, a);
   return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@
 #include <string>
 
 #include "csa_internal.h"
+#include "step_project.h"
 
 namespace csa {
 
@@ -225,7 +226,7 @@ int csa_compress(const csa_dims* dims, const csa_weights* w, const csa_cache* ca
 static int index_topk_impl(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
                            const int32_t* q_seq, const int32_t* q_pos, int32_t Q, int32_t* idx_out,
                            float* scores_out, void* ws, size_t ws_bytes, bool tiled,
-                           hipStream_t stream) {
+                           hipStream_t stream, const ProjectStepArgs* step = nullptr) {
   const size_t sc_bytes = scores_out ? 0 : align_up((size_t)Q * c.cap * sizeof(float), 256);
   const size_t need = sc_bytes + topk_workspace_bytes(d, Q, c.cap);
   if (need && (!ws || ws_bytes < need))
@@ -234,7 +235,7 @@ static int index_topk_impl(const csa_dims& d, const csa_cache& c, const void* qI
   void* tws = (char*)ws + sc_bytes;
   hipError_t e = launch_indexer(d, c, qI, w, q_seq, q_pos, Q, scores, c.cap, tiled, stream);
   if (e != hipSuccess) return hip_fail(e, "indexer launch");
-  e = launch_topk(d, c, q_seq, q_pos, Q, scores, c.cap, idx_out, tws, stream);
+  e = launch_topk(d, c, q_seq, q_pos, Q, scores, c.cap, idx_out, tws, stream, step);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return CSA_OK;
 }
@@ -369,29 +370,60 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
   void* phase_ws = (char*)ws + fixed;
   const size_t phase_bytes = ws_bytes - fixed;
 
+  // One new token per sequence (decode) with rows longer than a top-k segment: the query at
+  // tau sees floor(tau / m) entries, all completed by earlier tokens, so the entry this call
+  // may complete is not among them and the compression can move after scoring.  Its
+  // projection step then rides in the top-k threshold launch (independent work on the CUs
+  // that pass leaves idle) and its fold runs after the selection.  With a cache whose entry
+  // count trails the positions, this order scores the entries present before the call.
+  // With T = 1, query i is token pos0[i] of sequence i, so the kernels take the sequence as
+  // the query index (null q_seq) and pos0 as q_pos.
+  const ProjectStepArgs pa = project_step_args(d, *w, *cache, H, pos0);
+  if (d.dual && project_step_ok(d, T) &&
+      topk_can_carry_step(*cache, Qn, project_step_grid_x(pa.NP) * project_step_grid_y(pa.M)) &&
+      index_ws(d, Qn, cache->cap) <= phase_bytes) {
+    st = index_topk_impl(d, *cache, qI, wI, nullptr, pos0, Qn, idx, nullptr, phase_ws, phase_bytes,
+                         false, stream, &pa);
+    if (st) return st;
+    hipError_t e = launch_fold(d, *w, *cache, T, pos0, nullptr, 1, stream);
+    if (e != hipSuccess) return hip_fail(e, "fold launch");
+    e = launch_attend(d, *cache, q, gamma_q, sink, nullptr, pos0, Qn, idx, out, phase_ws, stream);
+    if (e != hipSuccess) return hip_fail(e, "attend launch");
+    return CSA_OK;
+  }
+
   st = csa_compress(dims, w, cache, H, T, pos0, phase_ws, phase_bytes, stream);
   if (st) return st;
-  hipError_t e = launch_query_meta(cache->B, T, pos0, q_seq, q_pos, stream);
-  if (e != hipSuccess) return hip_fail(e, "query metadata launch");
+  // largest query chunk whose scores and candidates fit
+  int32_t Qc = Qn;
   if (d.dual) {
-    // largest chunk whose scores and candidates fit
-    int32_t Qc = Qn;
     while (Qc > 1 && index_ws(d, Qc, cache->cap) > phase_bytes) Qc = (Qc + 1) / 2;
     // Query q is token q % T of sequence q / T.  With T and the chunk a multiple of 16, every
     // aligned group of 16 queries of a chunk is one sequence and the indexer can tile them.
     if (Qc >= 16) Qc -= Qc % 16;
+  }
+  // T = 1 in one chunk: the query index is the sequence and pos0 the positions (null q_seq)
+  const bool ident = T == 1 && Qc == Qn;
+  const int32_t* qs_ = ident ? nullptr : q_seq;
+  const int32_t* qp_ = ident ? pos0 : q_pos;
+  hipError_t e;
+  if (!ident) {
+    e = launch_query_meta(cache->B, T, pos0, q_seq, q_pos, stream);
+    if (e != hipSuccess) return hip_fail(e, "query metadata launch");
+  }
+  if (d.dual) {
     const bool tiled = T % 16 == 0 && Qc % 16 == 0;
     const size_t qI_row = (size_t)d.n_hI * d.c_I * (d.idx_fmt == CSA_FMT_F32 ? 4 : 1);
     const size_t w_row = (size_t)d.n_hI * (d.act_fmt == CSA_FMT_F32 ? 4 : 2);
     for (int32_t q0 = 0; q0 < Qn; q0 += Qc) {
       const int32_t n = std::min(Qc, Qn - q0);
       st = index_topk_impl(d, *cache, (const char*)qI + q0 * qI_row, (const char*)wI + q0 * w_row,
-                           q_seq + q0, q_pos + q0, n, idx + (size_t)q0 * d.top_k, nullptr, phase_ws,
-                           phase_bytes, tiled, stream);
+                           qs_ ? qs_ + q0 : nullptr, qp_ + q0, n, idx + (size_t)q0 * d.top_k, nullptr,
+                           phase_ws, phase_bytes, tiled, stream);
       if (st) return st;
     }
   }
-  e = launch_attend(d, *cache, q, gamma_q, sink, q_seq, q_pos, Qn, d.dual ? idx : nullptr, out,
+  e = launch_attend(d, *cache, q, gamma_q, sink, qs_, qp_, Qn, d.dual ? idx : nullptr, out,
                     phase_ws, stream);
   if (e != hipSuccess) return hip_fail(e, "attend launch");
   return CSA_OK;

@@ -10,6 +10,8 @@
 
 namespace csa {
 
+struct ProjectStepArgs;
+
 // ----------------------------------------------------------------------------- formats
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -210,9 +212,13 @@ hipError_t launch_state_update(const csa_dims& d, const csa_cache& c, int32_t T,
 hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
                           const int32_t* q_seq, const int32_t* q_pos, int32_t Q, float* scores,
                           int64_t ld_scores, bool tiled, hipStream_t s);
+// With step non-null (only where topk_can_carry_step allows it), the threshold pass also
+// runs that one-token projection step in its launch.
+bool topk_can_carry_step(const csa_cache& c, int32_t Q, int32_t step_blocks);
 hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
                        const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld_scores,
-                       int32_t* idx, void* ws, hipStream_t s);
+                       int32_t* idx, void* ws, hipStream_t s,
+                       const struct ProjectStepArgs* step = nullptr);
 hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
                          const float* gamma_q, const float* sink, const int32_t* q_seq,
                          const int32_t* q_pos, int32_t Q, const int32_t* idx, void* out,

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void k_indexer_bf16(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int q0 = blockIdx.x * QPW;
-  const int seq = q_seq[q0];
+  const int seq = q_seq ? q_seq[q0] : q0;
   const int nent = n_entries[seq];
   int V[QPW];
   int Vmax = 0;
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int qt0 = blockIdx.x * IT_Q;
-  const int seq = q_seq[qt0];
+  const int seq = q_seq ? q_seq[qt0] : qt0;
   const int nent = n_entries[seq];
   // visible entries of the tile's queries (clamped duplicates past Q store nothing)
   int Vmax = 0;
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(256) void k_indexer_f32(
   const int q = blockIdx.y;
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= Q) return;
-  const int seq = q_seq[q];
+  const int seq = q_seq ? q_seq[q] : q;
   const int V = max(0, min(q_pos[q] / m, n_entries[seq]));
   if (s >= V) return;
   const float* k = ki + ((size_t)seq * cap + s) * cI;

@@ -31,6 +31,7 @@
 //           running top k held in LDS.
 // Wave reductions and scans use DPP lane moves and readlane rather than LDS-routed permutes.
 #include "csa_internal.h"
+#include "step_project.h"
 
 namespace csa {
 namespace {
@@ -271,7 +272,7 @@ __device__ int select_topk(const Items& it, int k, TopkShared& sh, int* out_idx,
 
 __device__ __forceinline__ int visible(const int32_t* q_seq, const int32_t* q_pos,
                                        const int32_t* n_entries, int m, int q) {
-  return max(0, min(q_pos[q] / m, n_entries[q_seq[q]]));
+  return max(0, min(q_pos[q] / m, n_entries[q_seq ? q_seq[q] : q]));
 }
 
 // Level 0: blockIdx.x = query, blockIdx.y = segment of 1024*E scores.
@@ -329,13 +330,28 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_segment(
 // bins at or above the threshold bin (all valid scores when the row has at most TK_FINAL)
 // to cand_idx/cand_key [Q][nseg][cs] in index order, and their count (which may exceed cs)
 // to cand_cnt [Q][nseg].
-__global__ __launch_bounds__(TK_THREADS) void k_topk_filter(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_seq,
-    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries, int m, int k,
-    int cs, int32_t* __restrict__ cand_idx, uint32_t* __restrict__ cand_key,
-    int32_t* __restrict__ cand_cnt) {
-  __shared__ TopkShared sh;
-  const int q = blockIdx.x, seg = blockIdx.y, nseg = gridDim.y;
+struct FilterArgs {
+  const float* scores;
+  int64_t ld;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  const int32_t* n_entries;
+  int m, k, cs, nseg;
+  int32_t* cand_idx;
+  uint32_t* cand_key;
+  int32_t* cand_cnt;
+};
+
+__device__ __forceinline__ void topk_filter_body(const FilterArgs& fa, int q, int seg, TopkShared& sh) {
+  const float* __restrict__ scores = fa.scores;
+  const int64_t ld = fa.ld;
+  const int m = fa.m, k = fa.k, cs = fa.cs, nseg = fa.nseg;
+  const int32_t* __restrict__ q_seq = fa.q_seq;
+  const int32_t* __restrict__ q_pos = fa.q_pos;
+  const int32_t* __restrict__ n_entries = fa.n_entries;
+  int32_t* __restrict__ cand_idx = fa.cand_idx;
+  uint32_t* __restrict__ cand_key = fa.cand_key;
+  int32_t* __restrict__ cand_cnt = fa.cand_cnt;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int V = visible(q_seq, q_pos, n_entries, m, q);
   const float* row = scores + (size_t)q * ld;
@@ -419,6 +435,24 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_filter(
       ++pos;
     }
   if (tid == 0) cand_cnt[(size_t)q * nseg + seg] = total;
+}
+
+__global__ __launch_bounds__(TK_THREADS) void k_topk_filter(FilterArgs fa) {
+  __shared__ TopkShared sh;
+  topk_filter_body(fa, blockIdx.x, blockIdx.y, sh);
+}
+
+// The threshold pass and a one-token projection step in one launch (they are independent;
+// blocks [0, Q * nseg) filter, the rest project), so the projection's weight stream runs on
+// the CUs the filter leaves idle.
+__global__ __launch_bounds__(TK_THREADS) void k_topk_filter_project(FilterArgs fa, int Q, ProjectStepArgs pa,
+                                                                     int px) {
+  __shared__ TopkShared sh;
+  __shared__ float red[PS_WAVES][256];
+  const int nf = Q * fa.nseg;
+  const int b = blockIdx.x;
+  if (b < nf) topk_filter_body(fa, b % Q, b / Q, sh);
+  else project_step_tile(pa, (b - nf) % px, (b - nf) / px, red);
 }
 
 struct FinalShared {
@@ -531,11 +565,20 @@ size_t topk_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap) {
   return (size_t)Q * nseg * (cs * (sizeof(int32_t) + sizeof(uint32_t)) + sizeof(int32_t));
 }
 
+// Only while the threshold blocks and the projection blocks fit on the 256 CUs at once (one
+// 1024-thread workgroup each): beyond that the carried step only lengthens the pass.
+bool topk_can_carry_step(const csa_cache& c, int32_t Q, int32_t step_blocks) {
+  if (c.cap <= TK_SEG) return false;
+  const int64_t nseg = (c.cap + TK_SEG - 1) / TK_SEG;
+  return (int64_t)Q * nseg + step_blocks <= 256;
+}
+
 hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
                        const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld,
-                       int32_t* idx, void* ws, hipStream_t s) {
+                       int32_t* idx, void* ws, hipStream_t s, const ProjectStepArgs* step) {
   const int k = d.top_k;
   if (c.cap <= TK_SEG) {
+    if (step) return hipErrorInvalidValue;   // the carrying pass exists only for long rows
 #define TK_DIRECT(EE)                                                                          \
   hipLaunchKernelGGL((k_topk_segment<EE>), dim3(Q, 1), dim3(TK_THREADS), 0, s, scores, ld, q_seq, \
                      q_pos, c.n_entries, d.m, k, 1, idx, nullptr, nullptr)
@@ -553,8 +596,14 @@ hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_s
   int32_t* ci = (int32_t*)ws;
   uint32_t* ck = (uint32_t*)(ci + (size_t)Q * nseg * cs);
   int32_t* cc = (int32_t*)(ck + (size_t)Q * nseg * cs);
-  hipLaunchKernelGGL(k_topk_filter, dim3(Q, nseg), dim3(TK_THREADS), 0, s, scores, ld, q_seq, q_pos,
-                     c.n_entries, d.m, k, cs, ci, ck, cc);
+  const FilterArgs fa{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, cs, nseg, ci, ck, cc};
+  if (step) {
+    const int px = project_step_grid_x(step->NP), py = project_step_grid_y(step->M);
+    hipLaunchKernelGGL(k_topk_filter_project, dim3(Q * nseg + px * py), dim3(TK_THREADS), 0, s, fa, Q,
+                       *step, px);
+  } else {
+    hipLaunchKernelGGL(k_topk_filter, dim3(Q, nseg), dim3(TK_THREADS), 0, s, fa);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_topk_final, dim3(Q), dim3(TK_THREADS), 0, s, scores, ld, q_seq, q_pos,

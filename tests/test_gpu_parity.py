@@ -360,6 +360,64 @@ def test_q_forward_end_to_end():
             assert_close_q(go[i], o_ref, f"e2e out seq {b} tau={tau}")
 
 
+def test_q_forward_decode_steps():
+    """Nine one-token forward steps (tau = 600 .. 608, two of them completing an entry) on a
+    cache whose capacity spans two top-k segments: the path that scores before compressing
+    and runs the projection step inside the top-k threshold launch.  Outputs, selections and
+    the cache afterwards are checked against the oracle as in the chunked test."""
+    cfg = _qcfg()
+    dims = L.Dims.from_config(cfg)
+    od = oracle_dims(cfg)
+    B, n0, steps = 2, 600, 9
+    k = cfg["top_k"]
+    W = synth.weights(cfg, seed=23, device=DEV)
+    lw = lib_weights(W, True)
+    Hs = torch.stack([synth.hidden(cfg, b, 0, n0 + steps, seed=23, device=DEV) for b in range(B)])
+    cache = L.Cache(dims, B=B, cap=16384, win_cap=128)
+    _compress_chunks(dims, W, cache, Hs[:, :n0].contiguous(), [256, 344])
+    qs = synth.queries(cfg, B * steps, seed=23, device=DEV)
+    ws = _ws(L.csa_workspace_size(dims, L.OP_FORWARD, B=B, T=1, cap=cache.cap))
+    outs, idxs = [], []
+    for t in range(steps):
+        rows = [b * steps + t for b in range(B)]
+        out = torch.zeros((B, cfg["n_h"], cfg["c"]), dtype=torch.bfloat16, device=DEV)
+        idx = torch.zeros((B, k), dtype=torch.int32, device=DEV)
+        L.csa_forward(dims, lw, cache, Hs[:, n0 + t:n0 + t + 1].contiguous(), 1, _i32([n0 + t] * B),
+                      qs["q"][rows].contiguous(), qs["qI"][rows].contiguous(), qs["w"][rows].contiguous(),
+                      W["gamma_q"], W["sink"], out, idx, ws)
+        outs.append(out)
+        idxs.append(idx)
+    torch.cuda.synchronize()
+    OW = oracle_weights(W)
+    q, qI, w = host64(qs["q"]), qI_host(qs["qI"], cfg), host64(qs["w"])
+    sink = host64(W["sink"])
+    for b in range(B):
+        comp = R.compress_sequence(host64(Hs[b]), OW, od)
+        _check_cache_vs_oracle(cfg, cache, b, comp, n0 + steps, f"decode steps seq {b}")
+        g_entries = decode_rows(cache.kv[b].cpu().numpy(), cfg)
+        g_ki = decode_keys(cache.ki[b], cfg)
+        nb = (n0 + steps) // cfg["m"]
+        for t in range(steps):
+            i = b * steps + t
+            tau = n0 + t
+            gi = idxs[t][b].cpu().numpy()
+            go = host64(outs[t][b:b + 1])[0]
+            o_ref, sel, sc = R.query_step(tau, q[i], qI[i], w[i], None, sink, comp["entry"], comp["ki"],
+                                          lambda p: comp["raw"][p], nb, od)
+            try:
+                same = check_topk(gi, sc, k, f"decode seq {b} tau={tau}")
+            except AssertionError:
+                V = R.visible_entries(tau, cfg["m"], nb)
+                sc_g = R.index_scores(qI[i], w[i], g_ki[:V])
+                same = check_topk(gi, sc_g, k, f"decode seq {b} tau={tau} (GPU keys)")
+                same = False
+            if not same:
+                sel_g = gi[gi >= 0]
+                keys = np.concatenate([g_entries[sel_g], comp["raw"][R.window_positions(tau, cfg["n_win"])]])
+                o_ref = R.attend(q[i], tau, keys, None, sink, od)
+            assert_close_q(go, o_ref, f"decode out seq {b} tau={tau}")
+
+
 def test_deterministic_repeat():
     """Two runs of index + top-k + attend on the same inputs give identical bits."""
     cfg = _qcfg()
