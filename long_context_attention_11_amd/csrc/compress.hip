@@ -9,6 +9,7 @@
 // use the same compression with a smaller width).
 #include "csa_internal.h"
 #include "step_project.h"
+#include "fold.h"
 
 namespace csa {
 
@@ -142,156 +143,10 @@ __global__ __launch_bounds__(1024) void k_project_step(ProjectStepArgs a) {
   project_step_tile(a, blockIdx.x, blockIdx.y, red);
 }
 
-struct FoldArgs {
-  const float* P;        // [B*T][NP] summed projections, or null: all in the state ring
-  const float* state;    // [B][S][NP]
-  int S, NP;
-  int T, m, dual, c, r, cI;
-  const int32_t* pos0;
-  const float* bias;     // CSA [2][m][c], HCA [m][c]
-  const float* bias_idx; // CSA [2][m][cI]
-  const float* gamma;    // [c] or null
-  float eps;
-  double log2_base;
-  int kv_fmt, idx_fmt;
-  int cap, win_cap, rowB;
-  uint8_t* kv;
-  uint8_t* ki;
-  uint8_t* win;
-  int32_t* win_pos;
-  int32_t* n_entries;
-};
-
-// Projection value of token j (global position) in column col of sequence b.
-// With P null every token's projections are read from the state ring (one-token steps).
-__device__ __forceinline__ float proj(const FoldArgs& a, int b, int p0, int j, int col) {
-  if (a.P && j >= p0) return a.P[((size_t)b * a.T + (j - p0)) * a.NP + col];
-  return a.state[((size_t)b * a.S + (j % a.S)) * a.NP + col];
-}
-
-// Softmax fold of one column (reading notes eqs. 11-12 / 22-23).
-//   CSA: logits Z^a_{mi+r} + B^a_r and Z^b_{m(i-1)+r} + B^b_r (b half absent for i = 0),
-//        values C^a and C^b.  HCA: logits Z_{mi+r} + B_r over the m rows of block i.
-// colC/colZ name the projection columns of the a path; b-path columns are +boff.
-__device__ float fold_column(const FoldArgs& a, int b, int p0, int i, int colCa, int colZa,
-                             int boff, const float* Ba, const float* Bb, int bstride_col,
-                             int u) {
-  const int m = a.m;
-  const int ja = m * i, jb = m * (i - 1);
-  const bool has_b = a.dual && i > 0;
-  float mx = -INFINITY;
-  for (int r = 0; r < m; ++r) mx = fmaxf(mx, proj(a, b, p0, ja + r, colZa) + Ba[r * bstride_col + u]);
-  if (has_b)
-    for (int r = 0; r < m; ++r)
-      mx = fmaxf(mx, proj(a, b, p0, jb + r, colZa + boff) + Bb[r * bstride_col + u]);
-  float den = 0.f, num = 0.f;
-  for (int r = 0; r < m; ++r) {
-    float e = expf(proj(a, b, p0, ja + r, colZa) + Ba[r * bstride_col + u] - mx);
-    den += e;
-    num = fmaf(e, proj(a, b, p0, ja + r, colCa), num);
-  }
-  if (has_b)
-    for (int r = 0; r < m; ++r) {
-      float e = expf(proj(a, b, p0, jb + r, colZa + boff) + Bb[r * bstride_col + u] - mx);
-      den += e;
-      num = fmaf(e, proj(a, b, p0, jb + r, colCa + boff), num);
-    }
-  return num / den;
-}
-
-__device__ float block_sum_256(float v, float* red) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  return red[0] + red[1] + red[2] + red[3];
-}
-
-// RMSNorm over c columns (each thread holds columns 2t, 2t+1), RoPE at pos on the last r
-// columns, then store the row in its format.  Threads with 2t >= c hold zeros.
-__device__ void finalize_store(const FoldArgs& a, float x0, float x1, int64_t pos, uint8_t* dst,
-                               float* red) {
-  const int t = threadIdx.x, u = 2 * t;
-  const bool act = u < a.c;
-  float ss = block_sum_256(act ? x0 * x0 + x1 * x1 : 0.f, red);
-  float inv = 1.0f / sqrtf(ss / (float)a.c + a.eps);
-  if (!act) return;
-  float g0 = a.gamma ? a.gamma[u] : 1.f, g1 = a.gamma ? a.gamma[u + 1] : 1.f;
-  float y0 = g0 * (x0 * inv), y1 = g1 * (x1 * inv);
-  const int rs = a.c - a.r;
-  if (u >= rs) {
-    float cs, sn;
-    rope_cos_sin(pos, (u - rs) >> 1, a.r, a.log2_base, cs, sn);
-    float z0 = y0 * cs - y1 * sn, z1 = y0 * sn + y1 * cs;
-    y0 = z0;
-    y1 = z1;
-  }
-  if (a.kv_fmt == CSA_FMT_F32) {
-    float2 v = make_float2(y0, y1);
-    *reinterpret_cast<float2*>(dst + 4 * u) = v;
-  } else if (u < rs) {
-    uint32_t code = f32_to_e4m3(y0) | (f32_to_e4m3(y1) << 8);
-    *reinterpret_cast<uint16_t*>(dst + u) = (uint16_t)code;
-  } else {
-    uint32_t bits = f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16);
-    *reinterpret_cast<uint32_t*>(dst + rs + 2 * (u - rs)) = bits;
-  }
-}
-
 // grid: x = T raw rows + (T/m + 1) entry slots, y = sequence.  256 threads, 2 columns each.
 __global__ __launch_bounds__(256) void k_fold(FoldArgs a) {
   __shared__ float red[4];
-  const int b = blockIdx.y, slot = blockIdx.x, t = threadIdx.x;
-  const int p0 = a.pos0[b];
-  const int u = 2 * t;
-  if (slot < a.T) {
-    // raw window row of token j = p0 + slot: a-path row (HCA: C), finalized at position j.
-    const int j = p0 + slot;
-    if (slot == 0 && t == 0) a.n_entries[b] = min(a.cap, (p0 + a.T) / a.m);
-    if (slot < a.T - a.win_cap) return;  // an older token of this chunk the ring cannot keep
-    const int ws = j % a.win_cap;
-    float x0 = 0.f, x1 = 0.f;
-    if (u < a.c) {
-      x0 = proj(a, b, p0, j, u);
-      x1 = proj(a, b, p0, j, u + 1);
-    }
-    uint8_t* dst = a.win + ((size_t)b * a.win_cap + ws) * a.rowB;
-    finalize_store(a, x0, x1, j, dst, red);
-    if (t == 0) a.win_pos[(size_t)b * a.win_cap + ws] = j;
-    return;
-  }
-  const int i = p0 / a.m + (slot - a.T);
-  if (a.m * (i + 1) > p0 + a.T || i >= a.cap) return;  // block not complete in this chunk
-  // main KV entry: columns C^a at 0, C^b at c, Z^a at 2c, Z^b at 3c (HCA: C at 0, Z at c)
-  float x0 = 0.f, x1 = 0.f;
-  if (u < a.c) {
-    if (a.dual) {
-      x0 = fold_column(a, b, p0, i, u, 2 * a.c + u, a.c, a.bias, a.bias + a.m * a.c, a.c, u);
-      x1 = fold_column(a, b, p0, i, u + 1, 2 * a.c + u + 1, a.c, a.bias, a.bias + a.m * a.c, a.c, u + 1);
-    } else {
-      x0 = fold_column(a, b, p0, i, u, a.c + u, 0, a.bias, a.bias, a.c, u);
-      x1 = fold_column(a, b, p0, i, u + 1, a.c + u + 1, 0, a.bias, a.bias, a.c, u + 1);
-    }
-  }
-  uint8_t* dst = a.kv + ((size_t)b * a.cap + i) * a.rowB;
-  finalize_store(a, x0, x1, (int64_t)a.m * i, dst, red);
-  // indexer key: same fold with its own columns and biases; stored as folded
-  if (a.dual && u < a.cI) {
-    const int base = 4 * a.c;
-    const float* BIa = a.bias_idx;
-    const float* BIb = a.bias_idx + a.m * a.cI;
-    float k0 = fold_column(a, b, p0, i, base + u, base + 2 * a.cI + u, a.cI, BIa, BIb, a.cI, u);
-    float k1 = fold_column(a, b, p0, i, base + u + 1, base + 2 * a.cI + u + 1, a.cI, BIa, BIb, a.cI, u + 1);
-    if (a.idx_fmt == CSA_FMT_F32) {
-      float* kd = reinterpret_cast<float*>(a.ki) + ((size_t)b * a.cap + i) * a.cI;
-      kd[u] = k0;
-      kd[u + 1] = k1;
-    } else {
-      uint8_t* kd = a.ki + ((size_t)b * a.cap + i) * a.cI;
-      *reinterpret_cast<uint16_t*>(kd + u) = (uint16_t)(f32_to_e4m3(k0) | (f32_to_e4m3(k1) << 8));
-    }
-  }
+  fold_block<4>(a, blockIdx.x, blockIdx.y, red);
 }
 
 // Keep the projections of the last S tokens of each sequence: slot j % S.
@@ -403,9 +258,8 @@ hipError_t launch_project_step(const csa_dims& d, const csa_weights& w, const cs
   return hipGetLastError();
 }
 
-hipError_t launch_fold(const csa_dims& d, const csa_weights& w, const csa_cache& c, int32_t T,
-                       const int32_t* pos0, const float* P, int32_t ksplit, hipStream_t s) {
-  if (ksplit != 1) return hipErrorInvalidValue;  // partials are summed first
+FoldArgs fold_args(const csa_dims& d, const csa_weights& w, const csa_cache& c, int32_t T,
+                   const int32_t* pos0, const float* P) {
   FoldArgs a;
   a.P = P;
   a.state = c.state;
@@ -433,7 +287,14 @@ hipError_t launch_fold(const csa_dims& d, const csa_weights& w, const csa_cache&
   a.win = (uint8_t*)c.win;
   a.win_pos = c.win_pos;
   a.n_entries = c.n_entries;
-  dim3 grid(T + T / d.m + 1, c.B);
+  return a;
+}
+
+hipError_t launch_fold(const csa_dims& d, const csa_weights& w, const csa_cache& c, int32_t T,
+                       const int32_t* pos0, const float* P, int32_t ksplit, hipStream_t s) {
+  if (ksplit != 1) return hipErrorInvalidValue;  // partials are summed first
+  const FoldArgs a = fold_args(d, w, c, T, pos0, P);
+  dim3 grid(fold_grid_x(d, T), c.B);
   hipLaunchKernelGGL(k_fold, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -9,6 +9,7 @@
 
 #include "csa_internal.h"
 #include "step_project.h"
+#include "fold.h"
 
 namespace csa {
 
@@ -226,7 +227,8 @@ int csa_compress(const csa_dims* dims, const csa_weights* w, const csa_cache* ca
 static int index_topk_impl(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
                            const int32_t* q_seq, const int32_t* q_pos, int32_t Q, int32_t* idx_out,
                            float* scores_out, void* ws, size_t ws_bytes, bool tiled,
-                           hipStream_t stream, const ProjectStepArgs* step = nullptr) {
+                           hipStream_t stream, const ProjectStepArgs* step = nullptr,
+                           const FoldArgs* fold = nullptr) {
   const size_t sc_bytes = scores_out ? 0 : align_up((size_t)Q * c.cap * sizeof(float), 256);
   const size_t need = sc_bytes + topk_workspace_bytes(d, Q, c.cap);
   if (need && (!ws || ws_bytes < need))
@@ -235,7 +237,7 @@ static int index_topk_impl(const csa_dims& d, const csa_cache& c, const void* qI
   void* tws = (char*)ws + sc_bytes;
   hipError_t e = launch_indexer(d, c, qI, w, q_seq, q_pos, Q, scores, c.cap, tiled, stream);
   if (e != hipSuccess) return hip_fail(e, "indexer launch");
-  e = launch_topk(d, c, q_seq, q_pos, Q, scores, c.cap, idx_out, tws, stream, step);
+  e = launch_topk(d, c, q_seq, q_pos, Q, scores, c.cap, idx_out, tws, stream, step, fold);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return CSA_OK;
 }
@@ -374,20 +376,24 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
   // tau sees floor(tau / m) entries, all completed by earlier tokens, so the entry this call
   // may complete is not among them and the compression can move after scoring.  Its
   // projection step then rides in the top-k threshold launch (independent work on the CUs
-  // that pass leaves idle) and its fold runs after the selection.  With a cache whose entry
-  // count trails the positions, this order scores the entries present before the call.
+  // that pass leaves idle) when both fit on the CUs at once, else runs first, and its fold
+  // rides in the final selection's launch.  With a cache whose entry count trails the
+  // positions, this order scores the entries present before the call.
   // With T = 1, query i is token pos0[i] of sequence i, so the kernels take the sequence as
   // the query index (null q_seq) and pos0 as q_pos.
   const ProjectStepArgs pa = project_step_args(d, *w, *cache, H, pos0);
-  if (d.dual && project_step_ok(d, T) &&
-      topk_can_carry_step(*cache, Qn, project_step_grid_x(pa.NP) * project_step_grid_y(pa.M)) &&
+  if (d.dual && project_step_ok(d, T) && topk_two_pass(*cache) &&
       index_ws(d, Qn, cache->cap) <= phase_bytes) {
+    const bool carry = topk_can_carry_step(*cache, Qn, project_step_grid_x(pa.NP) * project_step_grid_y(pa.M));
+    if (!carry) {   // too many blocks to share the threshold launch: project first
+      hipError_t e = launch_project_step(d, *w, *cache, H, pos0, stream);
+      if (e != hipSuccess) return hip_fail(e, "projection launch");
+    }
+    const FoldArgs fo = fold_args(d, *w, *cache, T, pos0, nullptr);
     st = index_topk_impl(d, *cache, qI, wI, nullptr, pos0, Qn, idx, nullptr, phase_ws, phase_bytes,
-                         false, stream, &pa);
+                         false, stream, carry ? &pa : nullptr, &fo);
     if (st) return st;
-    hipError_t e = launch_fold(d, *w, *cache, T, pos0, nullptr, 1, stream);
-    if (e != hipSuccess) return hip_fail(e, "fold launch");
-    e = launch_attend(d, *cache, q, gamma_q, sink, nullptr, pos0, Qn, idx, out, phase_ws, stream);
+    hipError_t e = launch_attend(d, *cache, q, gamma_q, sink, nullptr, pos0, Qn, idx, out, phase_ws, stream);
     if (e != hipSuccess) return hip_fail(e, "attend launch");
     return CSA_OK;
   }

@@ -11,6 +11,7 @@
 namespace csa {
 
 struct ProjectStepArgs;
+struct FoldArgs;
 
 // ----------------------------------------------------------------------------- formats
 
@@ -213,12 +214,15 @@ hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI,
                           const int32_t* q_seq, const int32_t* q_pos, int32_t Q, float* scores,
                           int64_t ld_scores, bool tiled, hipStream_t s);
 // With step non-null (only where topk_can_carry_step allows it), the threshold pass also
-// runs that one-token projection step in its launch.
+// runs that one-token projection step in its launch; with fold non-null the final pass runs
+// that fold (of the same cache) in its launch.
+bool topk_two_pass(const csa_cache& c);   // threshold + final passes (fold may ride along)
 bool topk_can_carry_step(const csa_cache& c, int32_t Q, int32_t step_blocks);
 hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
                        const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld_scores,
                        int32_t* idx, void* ws, hipStream_t s,
-                       const struct ProjectStepArgs* step = nullptr);
+                       const struct ProjectStepArgs* step = nullptr,
+                       const struct FoldArgs* fold = nullptr);
 hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
                          const float* gamma_q, const float* sink, const int32_t* q_seq,
                          const int32_t* q_pos, int32_t Q, const int32_t* idx, void* out,

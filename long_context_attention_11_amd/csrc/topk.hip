@@ -32,6 +32,7 @@
 // Wave reductions and scans use DPP lane moves and readlane rather than LDS-routed permutes.
 #include "csa_internal.h"
 #include "step_project.h"
+#include "fold.h"
 
 namespace csa {
 namespace {
@@ -340,6 +341,7 @@ struct FilterArgs {
   int32_t* cand_idx;
   uint32_t* cand_key;
   int32_t* cand_cnt;
+  int32_t* vis;           // [Q] the visible count each query was filtered with
 };
 
 __device__ __forceinline__ void topk_filter_body(const FilterArgs& fa, int q, int seg, TopkShared& sh) {
@@ -435,6 +437,7 @@ __device__ __forceinline__ void topk_filter_body(const FilterArgs& fa, int q, in
       ++pos;
     }
   if (tid == 0) cand_cnt[(size_t)q * nseg + seg] = total;
+  if (tid == 0 && seg == 0) fa.vis[q] = V;
 }
 
 __global__ __launch_bounds__(TK_THREADS) void k_topk_filter(FilterArgs fa) {
@@ -487,14 +490,38 @@ __device__ int final_fast(int q, int nseg, int cs, int N, int k, const int32_t* 
 
 // Final pass: blockIdx.x = query.  Selects k from the candidate lists, or from the whole row
 // when they cannot be trusted (see the file comment), and writes idx_out [Q][k].
-__global__ __launch_bounds__(TK_THREADS) void k_topk_final(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_seq,
-    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries, int m, int k,
-    int nseg, int cs, const int32_t* __restrict__ cand_idx, const uint32_t* __restrict__ cand_key,
-    const int32_t* __restrict__ cand_cnt, int32_t* __restrict__ idx_out) {
-  __shared__ FinalShared fs;
-  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int V = visible(q_seq, q_pos, n_entries, m, q);
+struct FinalArgs {
+  const float* scores;
+  int64_t ld;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  const int32_t* n_entries;
+  int m, k, nseg, cs;
+  const int32_t* cand_idx;
+  const uint32_t* cand_key;
+  const int32_t* cand_cnt;
+  const int32_t* vis;     // [Q] visible counts from the threshold pass (entry counts may have
+                          // moved since, when a fold shares the launch)
+  int32_t* idx_out;
+};
+
+__device__ __forceinline__ void topk_final_body(const FinalArgs& fa, int q, FinalShared& fs) {
+  const float* __restrict__ scores = fa.scores;
+  const int64_t ld = fa.ld;
+  const int32_t* __restrict__ q_seq = fa.q_seq;
+  const int32_t* __restrict__ q_pos = fa.q_pos;
+  const int32_t* __restrict__ n_entries = fa.n_entries;
+  const int m = fa.m, k = fa.k, nseg = fa.nseg, cs = fa.cs;
+  const int32_t* __restrict__ cand_idx = fa.cand_idx;
+  const uint32_t* __restrict__ cand_key = fa.cand_key;
+  const int32_t* __restrict__ cand_cnt = fa.cand_cnt;
+  int32_t* __restrict__ idx_out = fa.idx_out;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int V = fa.vis[q];
+  (void)q_seq;
+  (void)q_pos;
+  (void)n_entries;
+  (void)m;
   int32_t* out = idx_out + (size_t)q * k;
   // segment offsets (one segment per thread, nseg <= TK_MAXSEG = TK_THREADS)
   const int c = tid < nseg ? cand_cnt[(size_t)q * nseg + tid] : 0;
@@ -543,6 +570,21 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_final(
   for (int i = n + tid; i < k; i += TK_THREADS) out[i] = -1;
 }
 
+__global__ __launch_bounds__(TK_THREADS) void k_topk_final(FinalArgs fa) {
+  __shared__ FinalShared fs;
+  topk_final_body(fa, blockIdx.x, fs);
+}
+
+// The final pass and a one-token fold in one launch (independent: blocks [0, Q) select, the
+// rest fold with 1024-thread blocks, whose columns past c hold zeros).
+__global__ __launch_bounds__(TK_THREADS) void k_topk_final_fold(FinalArgs fa, int Q, FoldArgs fo, int fx) {
+  __shared__ FinalShared fs;
+  __shared__ float red[TK_WAVES];
+  const int b = blockIdx.x;
+  if (b < Q) topk_final_body(fa, b, fs);
+  else fold_block<TK_WAVES>(fo, (b - Q) % fx, (b - Q) / fx, red);
+}
+
 int items_E(int n) {
   int E = 1;
   while (E * TK_THREADS < n) E *= 2;
@@ -562,11 +604,14 @@ size_t topk_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap) {
   if (cap <= TK_SEG) return 0;
   const size_t nseg = (size_t)(cap + TK_SEG - 1) / TK_SEG;
   const size_t cs = (size_t)filter_cap(d.top_k);
-  return (size_t)Q * nseg * (cs * (sizeof(int32_t) + sizeof(uint32_t)) + sizeof(int32_t));
+  return (size_t)Q * nseg * (cs * (sizeof(int32_t) + sizeof(uint32_t)) + sizeof(int32_t)) +
+         (size_t)Q * sizeof(int32_t);
 }
 
 // Only while the threshold blocks and the projection blocks fit on the 256 CUs at once (one
 // 1024-thread workgroup each): beyond that the carried step only lengthens the pass.
+bool topk_two_pass(const csa_cache& c) { return c.cap > TK_SEG; }
+
 bool topk_can_carry_step(const csa_cache& c, int32_t Q, int32_t step_blocks) {
   if (c.cap <= TK_SEG) return false;
   const int64_t nseg = (c.cap + TK_SEG - 1) / TK_SEG;
@@ -575,10 +620,11 @@ bool topk_can_carry_step(const csa_cache& c, int32_t Q, int32_t step_blocks) {
 
 hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
                        const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld,
-                       int32_t* idx, void* ws, hipStream_t s, const ProjectStepArgs* step) {
+                       int32_t* idx, void* ws, hipStream_t s, const ProjectStepArgs* step,
+                       const FoldArgs* fold) {
   const int k = d.top_k;
   if (c.cap <= TK_SEG) {
-    if (step) return hipErrorInvalidValue;   // the carrying pass exists only for long rows
+    if (step || fold) return hipErrorInvalidValue;   // the carrying passes exist only for long rows
 #define TK_DIRECT(EE)                                                                          \
   hipLaunchKernelGGL((k_topk_segment<EE>), dim3(Q, 1), dim3(TK_THREADS), 0, s, scores, ld, q_seq, \
                      q_pos, c.n_entries, d.m, k, 1, idx, nullptr, nullptr)
@@ -596,7 +642,8 @@ hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_s
   int32_t* ci = (int32_t*)ws;
   uint32_t* ck = (uint32_t*)(ci + (size_t)Q * nseg * cs);
   int32_t* cc = (int32_t*)(ck + (size_t)Q * nseg * cs);
-  const FilterArgs fa{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, cs, nseg, ci, ck, cc};
+  int32_t* vis = cc + (size_t)Q * nseg;
+  const FilterArgs fa{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, cs, nseg, ci, ck, cc, vis};
   if (step) {
     const int px = project_step_grid_x(step->NP), py = project_step_grid_y(step->M);
     hipLaunchKernelGGL(k_topk_filter_project, dim3(Q * nseg + px * py), dim3(TK_THREADS), 0, s, fa, Q,
@@ -606,8 +653,13 @@ hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_s
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_topk_final, dim3(Q), dim3(TK_THREADS), 0, s, scores, ld, q_seq, q_pos,
-                     c.n_entries, d.m, k, nseg, cs, ci, ck, cc, idx);
+  const FinalArgs fin{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, nseg, cs, ci, ck, cc, vis, idx};
+  if (fold) {
+    const int fx = fold->T + fold->T / fold->m + 1;
+    hipLaunchKernelGGL(k_topk_final_fold, dim3(Q + fx * c.B), dim3(TK_THREADS), 0, s, fin, Q, *fold, fx);
+  } else {
+    hipLaunchKernelGGL(k_topk_final, dim3(Q), dim3(TK_THREADS), 0, s, fin);
+  }
   return hipGetLastError();
 }
 
