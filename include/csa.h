@@ -233,7 +233,8 @@ int csa_index_scores(const csa_dims* dims, const csa_cache* cache, const void* q
 /*
  * The top-k selection on its own (reading notes eq. 17) over scores [Q][ld] as written by
  * csa_index_scores: idx_out[Q][top_k] as in csa_index_topk.  ws as csa_workspace_size(
- * INDEX_TOPK) minus the score buffer: csa_topk_workspace_size().
+ * INDEX_TOPK) minus the score buffer: csa_topk_workspace_size(), which is 0 for caches of
+ * up to 65536 entries (one workgroup selects each query's row) and ws may then be NULL.
  */
 int csa_topk(const csa_dims* dims, const csa_cache* cache, const int32_t* q_seq,
              const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld,

@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void k_project_f32(const float* __restrict__ H
 
 __global__ __launch_bounds__(1024) void k_project_step(ProjectStepArgs a) {
   __shared__ float red[PS_WAVES][256];
-  project_step_tile(a, blockIdx.x, blockIdx.y, red);
+  project_step_tile<PS_WAVES>(a, blockIdx.x, blockIdx.y, red);
 }
 
 // grid: x = T raw rows + (T/m + 1) entry slots, y = sequence.  256 threads, 2 columns each.

@@ -105,6 +105,11 @@ size_t index_ws(const csa_dims& d, int32_t Qc, int32_t cap) {
   return align_up((size_t)Qc * cap * sizeof(float), 256) + topk_workspace_bytes(d, Qc, cap);
 }
 
+// The same through the threshold + final passes, whose launches carry a one-token step.
+size_t index_ws_carry(const csa_dims& d, int32_t Qc, int32_t cap) {
+  return align_up((size_t)Qc * cap * sizeof(float), 256) + topk_filter_workspace_bytes(d, Qc, cap);
+}
+
 }  // namespace
 }  // namespace csa
 
@@ -172,6 +177,7 @@ int csa_workspace_size(const csa_dims* dims, int32_t op, int32_t B, int32_t T, i
       L.add(1, d.dual ? sizeof(int32_t) * (size_t)Qn * d.top_k : 0);  // idx
       size_t phase = compress_ws(d, B, T);
       if (d.dual) phase = std::max(phase, index_ws(d, Qc, cap));
+      if (d.dual && T == 1) phase = std::max(phase, index_ws_carry(d, Qn, cap));
       phase = std::max(phase, attend_workspace_bytes(d, Qn, cap, d.dual ? 0 : 1));  // forward attends a CSA layer sparsely
       L.add(2, phase);
       *bytes = L.total;
@@ -230,7 +236,8 @@ static int index_topk_impl(const csa_dims& d, const csa_cache& c, const void* qI
                            hipStream_t stream, const ProjectStepArgs* step = nullptr,
                            const FoldArgs* fold = nullptr) {
   const size_t sc_bytes = scores_out ? 0 : align_up((size_t)Q * c.cap * sizeof(float), 256);
-  const size_t need = sc_bytes + topk_workspace_bytes(d, Q, c.cap);
+  const size_t need = sc_bytes + ((step || fold) ? topk_filter_workspace_bytes(d, Q, c.cap)
+                                                   : topk_workspace_bytes(d, Q, c.cap));
   if (need && (!ws || ws_bytes < need))
     return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "index_topk needs " + std::to_string(need) + " bytes of workspace");
   float* scores = scores_out ? scores_out : (float*)ws;
@@ -381,9 +388,9 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
   // positions, this order scores the entries present before the call.
   // With T = 1, query i is token pos0[i] of sequence i, so the kernels take the sequence as
   // the query index (null q_seq) and pos0 as q_pos.
-  const ProjectStepArgs pa = project_step_args(d, *w, *cache, H, pos0);
-  if (d.dual && project_step_ok(d, T) && topk_two_pass(*cache) &&
-      index_ws(d, Qn, cache->cap) <= phase_bytes) {
+  if (d.dual && project_step_ok(d, T) && topk_can_carry(*cache) &&
+      index_ws_carry(d, Qn, cache->cap) <= phase_bytes) {
+    const ProjectStepArgs pa = project_step_args(d, *w, *cache, H, pos0);
     const bool carry = topk_can_carry_step(*cache, Qn, project_step_grid_x(pa.NP) * project_step_grid_y(pa.M));
     if (!carry) {   // too many blocks to share the threshold launch: project first
       hipError_t e = launch_project_step(d, *w, *cache, H, pos0, stream);

@@ -213,10 +213,13 @@ hipError_t launch_state_update(const csa_dims& d, const csa_cache& c, int32_t T,
 hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
                           const int32_t* q_seq, const int32_t* q_pos, int32_t Q, float* scores,
                           int64_t ld_scores, bool tiled, hipStream_t s);
-// With step non-null (only where topk_can_carry_step allows it), the threshold pass also
-// runs that one-token projection step in its launch; with fold non-null the final pass runs
-// that fold (of the same cache) in its launch.
-bool topk_two_pass(const csa_cache& c);   // threshold + final passes (fold may ride along)
+// Rows longer than one top-k segment (topk_can_carry) can take the threshold + final passes,
+// whose launches carry other work: with step non-null (only where topk_can_carry_step allows
+// it) the threshold pass also runs that one-token projection step, and with fold non-null the
+// final pass runs that fold (of the same cache).  Those passes need
+// topk_filter_workspace_bytes of workspace; without step and fold, rows of up to 65536
+// entries are selected in one launch with none (topk_workspace_bytes).
+bool topk_can_carry(const csa_cache& c);
 bool topk_can_carry_step(const csa_cache& c, int32_t Q, int32_t step_blocks);
 hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
                        const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld_scores,
@@ -235,6 +238,7 @@ hipError_t launch_query_meta(int32_t B, int32_t T, const int32_t* pos0, int32_t*
 // Planning helpers shared by the API and the launchers (pure host arithmetic).
 int32_t project_ksplit(const csa_dims& d, int32_t M);
 size_t topk_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap);
+size_t topk_filter_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap);
 int32_t topk_max_visible(const csa_dims& d);
 // which: 0 = sparse attention (idx given), 1 = dense (idx = NULL), 2 = the larger of both.
 size_t attend_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap, int which);

@@ -34,19 +34,40 @@ __device__ __forceinline__ void e4m3x32_to_ops(const uint4& lo, const uint4& hi,
 // over c_I.  Lane l holds head/entry (l & 15) and, within each 32-wide K step ks, dims
 // g*32 + ks*8 .. +7 with g = l >> 4 -- the same mapping on both operands, so each product
 // pairs equal dims.  Output tile: lane l holds entry (l & 15), heads 4g .. 4g+3.
+struct IndexerArgs {
+  const uint8_t* qI;
+  const uint16_t* wI;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  int Q;
+  const uint8_t* ki;
+  int cap;
+  const int32_t* n_entries;
+  int m;
+  float* scores;
+  int64_t ld;
+  int chunk;
+};
+
+// Workgroup (bx, by): queries bx * QPW .. +QPW-1 against entry chunk by.
 template <int NH, int QPW>
-__global__ __launch_bounds__(256) void k_indexer_bf16(
-    const uint8_t* __restrict__ qI, const uint16_t* __restrict__ wI,
-    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int Q,
-    const uint8_t* __restrict__ ki, int cap, const int32_t* __restrict__ n_entries, int m,
-    float* __restrict__ scores, int64_t ld, int chunk) {
+__device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx, int by) {
+  const uint8_t* __restrict__ qI = ia.qI;
+  const uint16_t* __restrict__ wI = ia.wI;
+  const int32_t* __restrict__ q_seq = ia.q_seq;
+  const int32_t* __restrict__ q_pos = ia.q_pos;
+  const int Q = ia.Q;
+  const uint8_t* __restrict__ ki = ia.ki;
+  const int cap = ia.cap, m = ia.m, chunk = ia.chunk;
+  float* __restrict__ scores = ia.scores;
+  const int64_t ld = ia.ld;
   constexpr int HT = NH / 16;
   constexpr int DEPTH = 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
-  const int q0 = blockIdx.x * QPW;
+  const int q0 = bx * QPW;
   const int seq = q_seq ? q_seq[q0] : q0;
-  const int nent = n_entries[seq];
+  const int nent = ia.n_entries[seq];
   int V[QPW];
   int Vmax = 0;
 #pragma unroll
@@ -56,7 +77,7 @@ __global__ __launch_bounds__(256) void k_indexer_bf16(
     Vmax = max(Vmax, V[qq]);
   }
   // this wave's entries: tiles of 16 dealt round-robin over the 4 waves of the chunk
-  const int c_lo = blockIdx.y * chunk;
+  const int c_lo = by * chunk;
   const int c_hi = min(c_lo + chunk, Vmax);
   if (c_lo >= c_hi) return;
   const int w_lo = c_lo + 16 * wave;
@@ -141,6 +162,11 @@ __global__ __launch_bounds__(256) void k_indexer_bf16(
       }
     }
   } while (++it < rounds);
+}
+
+template <int NH, int QPW>
+__global__ __launch_bounds__(256) void k_indexer_bf16(IndexerArgs ia) {
+  indexer_bf16_body<NH, QPW>(ia, blockIdx.x, blockIdx.y);
 }
 
 // Prefill-shaped indexer: a workgroup of 8 waves scores IT_Q = 16 queries of ONE sequence
@@ -352,25 +378,15 @@ hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI,
   const int per_q = std::max(1, target_wgs / std::max(Q, 1));
   int chunk = (c.cap + per_q - 1) / per_q;
   chunk = std::max(256, (chunk + 255) / 256 * 256);
-  dim3 grid(Q, (c.cap + chunk - 1) / chunk);
+  const int nchunk = (c.cap + chunk - 1) / chunk;
+  const IndexerArgs ia{(const uint8_t*)qI, (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki,
+                       c.cap, c.n_entries, d.m, scores, ld, chunk};
+  dim3 grid(Q, nchunk);
   switch (d.n_hI) {
-    case 64:
-      hipLaunchKernelGGL((k_indexer_bf16<64, 1>), grid, dim3(256), 0, s, (const uint8_t*)qI,
-                         (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki, c.cap,
-                         c.n_entries, d.m, scores, ld, chunk);
-      break;
-    case 32:
-      hipLaunchKernelGGL((k_indexer_bf16<32, 1>), grid, dim3(256), 0, s, (const uint8_t*)qI,
-                         (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki, c.cap,
-                         c.n_entries, d.m, scores, ld, chunk);
-      break;
-    case 16:
-      hipLaunchKernelGGL((k_indexer_bf16<16, 1>), grid, dim3(256), 0, s, (const uint8_t*)qI,
-                         (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki, c.cap,
-                         c.n_entries, d.m, scores, ld, chunk);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 64: hipLaunchKernelGGL((k_indexer_bf16<64, 1>), grid, dim3(256), 0, s, ia); break;
+    case 32: hipLaunchKernelGGL((k_indexer_bf16<32, 1>), grid, dim3(256), 0, s, ia); break;
+    case 16: hipLaunchKernelGGL((k_indexer_bf16<16, 1>), grid, dim3(256), 0, s, ia); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -44,6 +44,7 @@ constexpr int TK_SEG = 8192;     // scores per segment (E = 8)
 constexpr int TK_NS = 4096;      // threshold sample (4 per thread)
 constexpr int TK_FINAL = 8192;   // candidates the final pass holds (E = 8)
 constexpr int TK_MAXSEG = 1024;  // segments per row
+constexpr int TK_ROW_MAX = 65536; // rows up to this long: one workgroup per query, one launch
 constexpr int TK_MAXK = 4096;
 
 struct TopkShared {
@@ -327,8 +328,23 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_segment(
   }
 }
 
-// Threshold pass: blockIdx.x = query, blockIdx.y = segment.  Writes the segment's scores in
-// bins at or above the threshold bin (all valid scores when the row has at most TK_FINAL)
+// The smallest key in the threshold bin tbin or above: bins split [fmn, fmn + TK_BINS / scale)
+// evenly; scale 0 puts every score in bin 0.  Any key works as a threshold (the selection
+// checks the count it lets through), so rounding at the bin edge does not matter.
+__device__ __forceinline__ uint32_t threshold_key(float fmn, float scale, int tbin) {
+  return scale > 0.f ? score_key(fmn + (float)tbin / scale) : 0u;
+}
+
+// Bit i: element first + i of the row is visible (below V) and its key is at least tkey.
+__device__ __forceinline__ uint32_t pass_mask(const uint32_t (&key)[8], int first, int V, uint32_t tkey) {
+  uint32_t mask = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mask |= (first + i < V && key[i] >= tkey) ? 1u << i : 0u;
+  return mask;
+}
+
+// Threshold pass: blockIdx.x = query, blockIdx.y = segment.  Writes the segment's scores with
+// keys at or above the threshold key (all valid scores when the row has at most TK_FINAL)
 // to cand_idx/cand_key [Q][nseg][cs] in index order, and their count (which may exceed cs)
 // to cand_cnt [Q][nseg].
 struct FilterArgs {
@@ -382,8 +398,7 @@ __device__ __forceinline__ void topk_filter_body(const FilterArgs& fa, int q, in
       for (int i = 0; i < 4; ++i) smp[i] = row[bs + i];
     }
   }
-  int tbin = 0;
-  float fmn = 0.f, scale = 0.f;
+  uint32_t tkey = 0u;   // 0: every valid score passes
   if (!take_all) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) smp[i] = key_score(score_key(smp[i]));
@@ -394,9 +409,9 @@ __device__ __forceinline__ void topk_filter_body(const FilterArgs& fa, int q, in
     if (lane == 0) { sh.red_lo[w] = lo; sh.red_hi[w] = hi; }
     for (int b = tid; b < TK_BINS; b += TK_THREADS) sh.hist[0][b] = 0;
     __syncthreads();
-    fmn = slots_min(sh.red_lo);
+    const float fmn = slots_min(sh.red_lo);
     const float range = slots_max(sh.red_hi) - fmn;
-    scale = (range > 0.f && range < INFINITY) ? (float)TK_BINS / range : 0.f;
+    const float scale = (range > 0.f && range < INFINITY) ? (float)TK_BINS / range : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) atomicAdd(&sh.hist[0][min(TK_BINS - 1, (int)((smp[i] - fmn) * scale))], 1);
     __syncthreads();
@@ -406,18 +421,13 @@ __device__ __forceinline__ void topk_filter_body(const FilterArgs& fa, int q, in
     const int r = (int)min((int64_t)TK_NS, ((int64_t)target * TK_NS + V - 1) / V);
     if (w == 0) find_bin(sh.hist[0], r, sh);
     __syncthreads();
-    tbin = sh.sel_bin;
+    tkey = threshold_key(fmn, scale, sh.sel_bin);
   }
-  // bins are monotone in the score (scores below the sample's minimum fall in bin -1)
-  auto passes = [&](int i) {
-    if (first + i >= V) return false;
-    if (take_all) return true;
-    const float f = key_score(score_key(sv[i]));
-    return (int)fminf(fmaxf((f - fmn) * scale, -1.f), (float)(TK_BINS - 1)) >= tbin;
-  };
-  int cnt = 0;
+  uint32_t key[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) cnt += passes(i) ? 1 : 0;
+  for (int i = 0; i < 8; ++i) key[i] = score_key(sv[i]);
+  const uint32_t mask = pass_mask(key, first, V, tkey);
+  const int cnt = __popc(mask);
   const int x = wave_incl_scan(cnt);   // over the wave, then over the waves
   if (lane == 63) sh.scan[w] = x;
   __syncthreads();
@@ -429,10 +439,10 @@ __device__ __forceinline__ void topk_filter_body(const FilterArgs& fa, int q, in
   uint32_t* ck = cand_key + ((size_t)q * nseg + seg) * cs;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    if (passes(i)) {
+    if (mask >> i & 1u) {
       if (pos < cs) {
         ci[pos] = first + i;
-        ck[pos] = score_key(sv[i]);
+        ck[pos] = key[i];
       }
       ++pos;
     }
@@ -455,7 +465,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_filter_project(FilterArgs f
   const int nf = Q * fa.nseg;
   const int b = blockIdx.x;
   if (b < nf) topk_filter_body(fa, b % Q, b / Q, sh);
-  else project_step_tile(pa, (b - nf) % px, (b - nf) / px, red);
+  else project_step_tile<PS_WAVES>(pa, (b - nf) % px, (b - nf) / px, red);
 }
 
 struct FinalShared {
@@ -585,6 +595,204 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_final_fold(FinalArgs fa, in
   else fold_block<TK_WAVES>(fo, (b - Q) % fx, (b - Q) / fx, red);
 }
 
+// ----------------------------------------------------------------------- one-launch rows
+// Rows of up to TK_ROW_MAX scores: one workgroup per query draws a sample of the row, takes a
+// threshold from it (as the filter pass does), streams the row in TK_SEG-score chunks keeping
+// the scores at or above the threshold in LDS (in index order), and selects k from them; the
+// same whole-row fallback covers the cases the threshold cannot.
+//
+// Chunk layout: wave w holds the run of 512 scores at 512 w, lane l element i at 64 i + l, so
+// each load instruction is one contiguous 256-byte read and a wave's (i, l) order is index
+// order.  A wave's passing scores are compacted with ballots: one compare per score, the
+// write position from the ballot's lane count below the lane.
+struct RowShared {
+  TopkShared sh;
+  int c_idx[TK_FINAL + 1];        // +1: the spare slot writes past TK_FINAL land in
+  uint32_t c_key[TK_FINAL + 1];   // raw score bits in the filter phase, keys in the fallback
+};
+
+struct RowArgs {
+  const float* scores;
+  int64_t ld;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  const int32_t* n_entries;
+  int m, k;
+  int32_t* idx_out;
+};
+
+template <int E>
+__device__ __forceinline__ int select_lds(RowShared& rs, int N, int k, int32_t* out) {
+  ListItems<E> it;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int p = threadIdx.x * E + i;
+    it.id[i] = p < N ? rs.c_idx[p] : -1;
+    it.key[i] = p < N ? score_key(__uint_as_float(rs.c_key[p])) : 0u;
+  }
+  return select_topk<E>(it, k, rs.sh, out, nullptr);
+}
+
+// Raw float bits u pass iff u - lo <= span (unsigned): exactly the scores whose key is at
+// least score_key(t) (-0 equal to +0, NaNs beyond the infinities on their sign's side).
+__device__ __forceinline__ void pass_interval(float t, uint32_t& lo, uint32_t& span) {
+  uint32_t b = __float_as_uint(t);
+  if (b == 0x80000000u) b = 0u;
+  if (b != 0u && (b & 0x80000000u) == 0u) {   // t > 0: the positive floats from t up, +NaN
+    lo = b;
+    span = 0x7fffffffu - b;
+  } else {                                     // t <= 0: everything from +NaN down to t
+    lo = 0u;
+    span = b == 0u ? 0x80000000u : b;
+  }
+}
+
+// One chunk of the row (scores v, wave w's run starting at a0 = s + 512 w) into the LDS
+// candidate list at N.  Element e = a0 + 64 i + lane counts when c0 <= e < V (FULL: all do).
+template <bool FULL>
+__device__ __forceinline__ void row_chunk(const float (&v)[8], int a0, int c0, int V, uint32_t lo,
+                                          uint32_t span, int& N, RowShared& rs, int w, int lane) {
+  bool p[8];
+  uint64_t bal[8];
+  int cnt = 0;
+  const int vlo = max(0, c0 - a0), vspan = max(0, min(512, V - a0) - vlo);   // uniform
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = __float_as_uint(v[i]) - lo <= span;
+    if constexpr (!FULL) p[i] = p[i] && (uint32_t)(64 * i + lane - vlo) < (uint32_t)vspan;
+    bal[i] = __ballot(p[i]);
+    cnt += __popcll(bal[i]);
+  }
+  if (lane == 0) rs.sh.scan[w] = cnt;
+  __syncthreads();
+  const int sw = rs.sh.scan[lane & 15];
+  const int before = __builtin_amdgcn_readfirstlane(row_allreduce((lane & 15) < w ? sw : 0, OpAdd()));
+  const int total = __builtin_amdgcn_readfirstlane(row_allreduce(sw, OpAdd()));
+  uint32_t base = (uint32_t)(N + before);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (p[i]) {
+      const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[i] >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal[i], base));
+      const int slot = min(pos, TK_FINAL);   // past TK_FINAL: the count overflows, the fallback runs
+      rs.c_idx[slot] = a0 + 64 * i + lane;
+      rs.c_key[slot] = __float_as_uint(v[i]);
+    }
+    base += (uint32_t)__popcll(bal[i]);
+  }
+  N += total;
+  __syncthreads();   // sh.scan is rewritten by the next chunk
+}
+
+__device__ __forceinline__ void topk_row_body(const RowArgs& ra, int q, RowShared& rs) {
+  TopkShared& sh = rs.sh;
+  const int k = ra.k;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int V = visible(ra.q_seq, ra.q_pos, ra.n_entries, ra.m, q);
+  const float* row = ra.scores + (size_t)q * ra.ld;
+  int32_t* out = ra.idx_out + (size_t)q * k;
+  const bool take_all = V <= TK_FINAL;
+  // Reads of chunk c0 start at min(c0, L - TK_SEG), L = max(V, TK_SEG) <= the row stride (the
+  // rows here are longer than TK_SEG), so every read stays in the row; the last chunk's run is
+  // moved back to end at V and its elements below c0 are masked.
+  const int L = max(V, TK_SEG);
+  // the sample first (64 evenly spaced runs of 64; rows of at most TK_FINAL take every score
+  // and ignore it), then RG chunks at once, so the latencies overlap
+  const int bs = ((int)((int64_t)(tid >> 4) * (L - 64) / 63) & ~3) + 4 * (tid & 15);
+  float smp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) smp[i] = row[bs + i];
+  constexpr int RG = 4;
+  float sv[RG][8];
+  auto load_group = [&](int g0) {
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+      const float* p = row + min(g0 + j * TK_SEG, L - TK_SEG) + 512 * w + lane;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sv[j][i] = p[64 * i];
+    }
+  };
+  load_group(0);
+  // the threshold: scores at or above t pass (lo = 0, span = ~0: every score)
+  uint32_t lo = 0u, span = 0xffffffffu;
+  if (!take_all) {   // uniform
+#pragma unroll
+    for (int i = 0; i < 4; ++i) smp[i] = key_score(score_key(smp[i]));
+    float mn = fminf(fminf(smp[0], smp[1]), fminf(smp[2], smp[3]));
+    float mx = fmaxf(fmaxf(smp[0], smp[1]), fmaxf(smp[2], smp[3]));
+    mn = wave_min_f(mn);
+    mx = wave_max_f(mx);
+    if (lane == 0) { sh.red_lo[w] = mn; sh.red_hi[w] = mx; }
+    for (int b = tid; b < TK_BINS; b += TK_THREADS) sh.hist[0][b] = 0;
+    __syncthreads();
+    const float fmn = slots_min(sh.red_lo);
+    const float range = slots_max(sh.red_hi) - fmn;
+    const float scale = (range > 0.f && range < INFINITY) ? (float)TK_BINS / range : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) atomicAdd(&sh.hist[0][min(TK_BINS - 1, (int)((smp[i] - fmn) * scale))], 1);
+    __syncthreads();
+    // samples at or above the threshold: about 3k (at most 3/4 of TK_FINAL) of the row's V
+    // scores are then expected to pass
+    const int target = min(3 * k, TK_FINAL * 3 / 4);
+    const int r = (int)min((int64_t)TK_NS, ((int64_t)target * TK_NS + V - 1) / V);
+    if (w == 0) find_bin(sh.hist[0], r, sh);
+    __syncthreads();
+    if (scale > 0.f) pass_interval(fmn + (float)sh.sel_bin / scale, lo, span);
+  }
+  // the row, chunk by chunk: passing scores go to LDS in index order
+  int N = 0;   // uniform
+  for (int g0 = 0; g0 < V; g0 += RG * TK_SEG) {
+    if (g0 > 0) load_group(g0);
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+      const int c0 = g0 + j * TK_SEG;
+      if (c0 >= V) break;   // uniform
+      const int s = min(c0, L - TK_SEG);
+      if (s == c0 && c0 + TK_SEG <= V) row_chunk<true>(sv[j], s + 512 * w, c0, V, lo, span, N, rs, w, lane);
+      else row_chunk<false>(sv[j], s + 512 * w, c0, V, lo, span, N, rs, w, lane);
+    }
+  }
+  int n;
+  if (N >= min(k, V) && N <= TK_FINAL) {   // uniform
+    if (N <= 2 * TK_THREADS) n = select_lds<2>(rs, N, k, out);
+    else if (N <= 4 * TK_THREADS) n = select_lds<4>(rs, N, k, out);
+    else n = select_lds<8>(rs, N, k, out);
+  } else {
+    // exact selection over the whole row: the running top k (in index order, in LDS) plus
+    // the next TK_FINAL - k scores, once per chunk
+    const int ch = TK_FINAL - k;
+    int nr = 0;
+    for (int c0 = 0; c0 < V; c0 += ch) {
+      ListItems<8> it;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int p = tid * 8 + i;
+        if (p < nr) {
+          it.id[i] = rs.c_idx[p];
+          it.key[i] = rs.c_key[p];
+        } else {
+          const int e = c0 + (p - nr);
+          const bool ok = p - nr < ch && e < V;
+          it.id[i] = ok ? e : -1;
+          it.key[i] = ok ? score_key(row[e]) : 0u;
+        }
+      }
+      __syncthreads();   // the running list is read before it is rewritten
+      nr = select_topk<8>(it, k, sh, rs.c_idx, rs.c_key);
+      __syncthreads();
+    }
+    for (int i = tid; i < nr; i += TK_THREADS) out[i] = rs.c_idx[i];
+    n = nr;
+  }
+  for (int i = n + tid; i < k; i += TK_THREADS) out[i] = -1;
+}
+
+__global__ __launch_bounds__(TK_THREADS) void k_topk_row(RowArgs ra) {
+  __shared__ RowShared rs;
+  topk_row_body(ra, blockIdx.x, rs);
+}
+
 int items_E(int n) {
   int E = 1;
   while (E * TK_THREADS < n) E *= 2;
@@ -601,6 +809,10 @@ int32_t topk_max_visible(const csa_dims& d) {
 }
 
 size_t topk_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap) {
+  return cap <= TK_ROW_MAX ? 0 : topk_filter_workspace_bytes(d, Q, cap);
+}
+
+size_t topk_filter_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap) {
   if (cap <= TK_SEG) return 0;
   const size_t nseg = (size_t)(cap + TK_SEG - 1) / TK_SEG;
   const size_t cs = (size_t)filter_cap(d.top_k);
@@ -608,14 +820,13 @@ size_t topk_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap) {
          (size_t)Q * sizeof(int32_t);
 }
 
+bool topk_can_carry(const csa_cache& c) { return c.cap > TK_SEG; }
+
 // Only while the threshold blocks and the projection blocks fit on the 256 CUs at once (one
 // 1024-thread workgroup each): beyond that the carried step only lengthens the pass.
-bool topk_two_pass(const csa_cache& c) { return c.cap > TK_SEG; }
-
 bool topk_can_carry_step(const csa_cache& c, int32_t Q, int32_t step_blocks) {
-  if (c.cap <= TK_SEG) return false;
-  const int64_t nseg = (c.cap + TK_SEG - 1) / TK_SEG;
-  return (int64_t)Q * nseg + step_blocks <= 256;
+  if (!topk_can_carry(c)) return false;
+  return (int64_t)Q * ((c.cap + TK_SEG - 1) / TK_SEG) + step_blocks <= 256;
 }
 
 hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
@@ -637,13 +848,18 @@ hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_s
 #undef TK_DIRECT
     return hipGetLastError();
   }
+  if (c.cap <= TK_ROW_MAX && !step && !fold) {
+    const RowArgs ra{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, idx};
+    hipLaunchKernelGGL(k_topk_row, dim3(Q), dim3(TK_THREADS), 0, s, ra);
+    return hipGetLastError();
+  }
   const int nseg = (c.cap + TK_SEG - 1) / TK_SEG;
   const int cs = filter_cap(k);
   int32_t* ci = (int32_t*)ws;
   uint32_t* ck = (uint32_t*)(ci + (size_t)Q * nseg * cs);
   int32_t* cc = (int32_t*)(ck + (size_t)Q * nseg * cs);
-  int32_t* vis = cc + (size_t)Q * nseg;
-  const FilterArgs fa{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, cs, nseg, ci, ck, cc, vis};
+  int32_t* fvis = cc + (size_t)Q * nseg;   // the counts the threshold pass filtered with
+  const FilterArgs fa{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, cs, nseg, ci, ck, cc, fvis};
   if (step) {
     const int px = project_step_grid_x(step->NP), py = project_step_grid_y(step->M);
     hipLaunchKernelGGL(k_topk_filter_project, dim3(Q * nseg + px * py), dim3(TK_THREADS), 0, s, fa, Q,
@@ -653,7 +869,7 @@ hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_s
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const FinalArgs fin{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, nseg, cs, ci, ck, cc, vis, idx};
+  const FinalArgs fin{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, nseg, cs, ci, ck, cc, fvis, idx};
   if (fold) {
     const int fx = fold->T + fold->T / fold->m + 1;
     hipLaunchKernelGGL(k_topk_final_fold, dim3(Q + fx * c.B), dim3(TK_THREADS), 0, s, fin, Q, *fold, fx);

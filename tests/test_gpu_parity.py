@@ -563,9 +563,10 @@ def test_topk_exact_on_crafted_scores():
     """csa_topk on given scores must equal the oracle's selection exactly (same input bits):
     heavy ties (integer scores), -0/+0, scores rising or falling with the index (every
     candidate in one segment), rows shorter than k, exactly k, k + 1, ragged segment tails,
-    and long rows (90001 entries, k = 1024).  Ties and -0/+0 rows defeat the sampled
+    rows one workgroup selects from (33000 and 65536 entries) and longer ones (90001 entries,
+    k = 1024).  Ties and -0/+0 rows defeat the sampled
     threshold, so they also exercise the exact whole-row fallback."""
-    for k, cap in ((1024, 90001), (512, 4096), (8, 37), (512, 33000)):
+    for k, cap in ((1024, 90001), (512, 4096), (8, 37), (512, 33000), (2048, 65536)):
         cfg = _qcfg(top_k=k)
         dims = L.Dims.from_config(cfg)
         m = cfg["m"]
