@@ -138,12 +138,13 @@ __global__ __launch_bounds__(256) void k_project_f32(const float* __restrict__ H
 
 // ============================================================================ fold / finalize
 
-__global__ __launch_bounds__(1024) void k_project_step(ProjectStepArgs a) {
-  __shared__ float red[PS_WAVES][256];
-  project_step_tile<PS_WAVES>(a, blockIdx.x, blockIdx.y, red);
+// One-token projection: one unit per 64-thread workgroup.
+__global__ __launch_bounds__(64) void k_project_step(ProjectStepArgs a, int units) {
+  if ((int)blockIdx.x < units) project_unit<2>(a, blockIdx.x);
 }
 
-// grid: x = T raw rows + (T/m + 1) entry slots, y = sequence.  256 threads, 2 columns each.
+// grid: x = T raw rows + (T/m + 1) entry slots (+ state writers), y = sequence.  256
+// threads, 2 columns each.
 __global__ __launch_bounds__(256) void k_fold(FoldArgs a) {
   __shared__ float red[4];
   fold_block<4>(a, blockIdx.x, blockIdx.y, red);
@@ -231,11 +232,17 @@ hipError_t launch_project(const csa_dims& d, const csa_weights& w, const void* H
 }
 
 bool project_step_ok(const csa_dims& d, int32_t T) {
-  return T == 1 && d.act_fmt == CSA_FMT_BF16 && d.d % (32 * PS_WAVES) == 0;
+  return T == 1 && d.act_fmt == CSA_FMT_BF16 && d.d % (64 * PU_SLICES) == 0;
 }
 
+size_t project_part_bytes(const csa_dims& d, int32_t B) {
+  return (size_t)PU_SLICES * B * state_width(d) * sizeof(float);
+}
+
+int32_t project_step_units(const csa_dims& d, int32_t B) { return project_units(state_width(d), B, 2); }
+
 ProjectStepArgs project_step_args(const csa_dims& d, const csa_weights& w, const csa_cache& c,
-                                  const void* H, const int32_t* pos0) {
+                                  const void* H, float* part) {
   ProjectStepArgs a;
   a.H = (const uint16_t*)H;
   a.wkv = (const uint16_t*)w.w_kv;
@@ -244,24 +251,24 @@ ProjectStepArgs project_step_args(const csa_dims& d, const csa_weights& w, const
   a.M = c.B;
   a.NP = state_width(d);
   a.K = d.d;
-  a.pos0 = pos0;
-  a.S = state_rows(d);
-  a.state = c.state;
+  a.part = part;
   return a;
 }
 
 hipError_t launch_project_step(const csa_dims& d, const csa_weights& w, const csa_cache& c,
-                               const void* H, const int32_t* pos0, hipStream_t s) {
-  const ProjectStepArgs a = project_step_args(d, w, c, H, pos0);
-  dim3 grid(project_step_grid_x(a.NP), project_step_grid_y(a.M));
-  hipLaunchKernelGGL(k_project_step, grid, dim3(64 * PS_WAVES), 0, s, a);
+                               const void* H, float* part, hipStream_t s) {
+  const ProjectStepArgs a = project_step_args(d, w, c, H, part);
+  const int units = project_units(a.NP, a.M, 2);
+  hipLaunchKernelGGL(k_project_step, dim3(units), dim3(64), 0, s, a, units);
   return hipGetLastError();
 }
 
 FoldArgs fold_args(const csa_dims& d, const csa_weights& w, const csa_cache& c, int32_t T,
-                   const int32_t* pos0, const float* P) {
+                   const int32_t* pos0, const float* P, const float* part) {
   FoldArgs a;
   a.P = P;
+  a.part = (T == 1 && !P) ? part : nullptr;
+  a.B = c.B;
   a.state = c.state;
   a.S = state_rows(d);
   a.NP = state_width(d);
@@ -291,10 +298,11 @@ FoldArgs fold_args(const csa_dims& d, const csa_weights& w, const csa_cache& c, 
 }
 
 hipError_t launch_fold(const csa_dims& d, const csa_weights& w, const csa_cache& c, int32_t T,
-                       const int32_t* pos0, const float* P, int32_t ksplit, hipStream_t s) {
+                       const int32_t* pos0, const float* P, int32_t ksplit, hipStream_t s,
+                       const float* part) {
   if (ksplit != 1) return hipErrorInvalidValue;  // partials are summed first
-  const FoldArgs a = fold_args(d, w, c, T, pos0, P);
-  dim3 grid(fold_grid_x(d, T), c.B);
+  const FoldArgs a = fold_args(d, w, c, T, pos0, P, part);
+  dim3 grid(fold_grid_x(a), c.B);
   hipLaunchKernelGGL(k_fold, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

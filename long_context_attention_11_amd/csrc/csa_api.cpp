@@ -95,6 +95,7 @@ struct Layout {
 
 // split-K partials [ks][M][P] and, when ks > 1, their sum [M][P]
 size_t compress_ws(const csa_dims& d, int32_t B, int32_t T) {
+  if (project_step_ok(d, T)) return project_part_bytes(d, B);
   const int32_t M = B * T;
   const int32_t ks = project_ksplit(d, M);
   return (size_t)(ks + (ks > 1 ? 1 : 0)) * M * state_width(d) * sizeof(float);
@@ -177,7 +178,8 @@ int csa_workspace_size(const csa_dims* dims, int32_t op, int32_t B, int32_t T, i
       L.add(1, d.dual ? sizeof(int32_t) * (size_t)Qn * d.top_k : 0);  // idx
       size_t phase = compress_ws(d, B, T);
       if (d.dual) phase = std::max(phase, index_ws(d, Qc, cap));
-      if (d.dual && T == 1) phase = std::max(phase, index_ws_carry(d, Qn, cap));
+      if (d.dual && T == 1)
+        phase = std::max(phase, align_up(index_ws_carry(d, Qn, cap), 256) + project_part_bytes(d, B));
       phase = std::max(phase, attend_workspace_bytes(d, Qn, cap, d.dual ? 0 : 1));  // forward attends a CSA layer sparsely
       L.add(2, phase);
       *bytes = L.total;
@@ -201,17 +203,19 @@ int csa_compress(const csa_dims* dims, const csa_weights* w, const csa_cache* ca
   if (!H || !pos0) return fail(CSA_ERR_INVALID_ARGUMENT, "H and pos0 must be set");
   if (T < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "T must be >= 1");
   const int32_t M = cache->B * T;
-  if (project_step_ok(d, T)) {
-    // one new token per sequence: project into the state ring, fold from there
-    hipError_t e = launch_project_step(d, *w, *cache, H, pos0, stream);
-    if (e != hipSuccess) return hip_fail(e, "projection launch");
-    e = launch_fold(d, *w, *cache, T, pos0, nullptr, 1, stream);
-    if (e != hipSuccess) return hip_fail(e, "fold launch");
-    return CSA_OK;
-  }
   const size_t need = compress_ws(d, cache->B, T);
   if (need && (!ws || ws_bytes < need))
     return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "compress needs " + std::to_string(need) + " bytes of workspace");
+  if (project_step_ok(d, T)) {
+    // one new token per sequence: partial projections, then the fold adds them up (and
+    // stores the token's row in the state ring)
+    float* part = (float*)ws;
+    hipError_t e = launch_project_step(d, *w, *cache, H, part, stream);
+    if (e != hipSuccess) return hip_fail(e, "projection launch");
+    e = launch_fold(d, *w, *cache, T, pos0, nullptr, 1, stream, part);
+    if (e != hipSuccess) return hip_fail(e, "fold launch");
+    return CSA_OK;
+  }
   const int32_t ks = project_ksplit(d, M);
   float* P = (float*)ws;
   hipError_t e = launch_project(d, *w, H, M, ks, P, stream);
@@ -388,15 +392,17 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
   // positions, this order scores the entries present before the call.
   // With T = 1, query i is token pos0[i] of sequence i, so the kernels take the sequence as
   // the query index (null q_seq) and pos0 as q_pos.
+  const size_t ix_bytes = align_up(index_ws_carry(d, Qn, cache->cap), 256);
   if (d.dual && project_step_ok(d, T) && topk_can_carry(*cache) &&
-      index_ws_carry(d, Qn, cache->cap) <= phase_bytes) {
-    const ProjectStepArgs pa = project_step_args(d, *w, *cache, H, pos0);
-    const bool carry = topk_can_carry_step(*cache, Qn, project_step_grid_x(pa.NP) * project_step_grid_y(pa.M));
-    if (!carry) {   // too many blocks to share the threshold launch: project first
-      hipError_t e = launch_project_step(d, *w, *cache, H, pos0, stream);
+      ix_bytes + project_part_bytes(d, cache->B) <= phase_bytes) {
+    float* part = (float*)((char*)phase_ws + ix_bytes);
+    const ProjectStepArgs pa = project_step_args(d, *w, *cache, H, part);
+    const bool carry = topk_can_carry_step(*cache, Qn, project_step_units(d, cache->B));
+    if (!carry) {   // too many workgroups to share the threshold launch: project first
+      hipError_t e = launch_project_step(d, *w, *cache, H, part, stream);
       if (e != hipSuccess) return hip_fail(e, "projection launch");
     }
-    const FoldArgs fo = fold_args(d, *w, *cache, T, pos0, nullptr);
+    const FoldArgs fo = fold_args(d, *w, *cache, T, pos0, nullptr, part);
     st = index_topk_impl(d, *cache, qI, wI, nullptr, pos0, Qn, idx, nullptr, phase_ws, phase_bytes,
                          false, stream, carry ? &pa : nullptr, &fo);
     if (st) return st;

@@ -197,14 +197,17 @@ void set_error(const std::string& msg);
 // Kernel launchers (defined in the .hip files).  Each returns a hipError_t of its launch.
 hipError_t launch_project(const csa_dims& d, const csa_weights& w, const void* H, int32_t M,
                           int32_t ksplit, float* P, hipStream_t s);
-// One-token steps (T = 1, bf16, d % 512 == 0): project straight into the state ring; the
-// fold then runs with P = null.
+// One-token steps (T = 1, bf16, d % 1024 == 0): the projection writes partial sums over
+// slices of K to part (project_part_bytes); the fold (P = null, the same part) adds them and
+// also stores the new token's row into the state ring.
 bool project_step_ok(const csa_dims& d, int32_t T);
+size_t project_part_bytes(const csa_dims& d, int32_t B);
+int32_t project_step_units(const csa_dims& d, int32_t B);   // wave-sized units
 hipError_t launch_project_step(const csa_dims& d, const csa_weights& w, const csa_cache& c,
-                               const void* H, const int32_t* pos0, hipStream_t s);
+                               const void* H, float* part, hipStream_t s);
 hipError_t launch_fold(const csa_dims& d, const csa_weights& w, const csa_cache& c,
                        int32_t T, const int32_t* pos0, const float* P, int32_t ksplit,
-                       hipStream_t s);
+                       hipStream_t s, const float* part = nullptr);
 hipError_t launch_state_update(const csa_dims& d, const csa_cache& c, int32_t T,
                                const int32_t* pos0, const float* P, int32_t ksplit,
                                hipStream_t s);
@@ -220,7 +223,7 @@ hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI,
 // topk_filter_workspace_bytes of workspace; without step and fold, rows of up to 65536
 // entries are selected in one launch with none (topk_workspace_bytes).
 bool topk_can_carry(const csa_cache& c);
-bool topk_can_carry_step(const csa_cache& c, int32_t Q, int32_t step_blocks);
+bool topk_can_carry_step(const csa_cache& c, int32_t Q, int32_t step_units);
 hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
                        const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld_scores,
                        int32_t* idx, void* ws, hipStream_t s,

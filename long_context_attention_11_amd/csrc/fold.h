@@ -7,12 +7,16 @@
 #pragma once
 
 #include "csa_internal.h"
+#include "step_project.h"
 
 namespace csa {
 
 struct FoldArgs {
   const float* P;        // [B*T][NP] summed projections, or null: all in the state ring
-  const float* state;    // [B][S][NP]
+  const float* part;     // T = 1: [PU_SLICES][B][NP] partial projections of the new token
+                         // (then also written, summed, into the state ring), or null
+  int B;
+  float* state;          // [B][S][NP]
   int S, NP;
   int T, m, dual, c, r, cI;
   const int32_t* pos0;
@@ -31,9 +35,16 @@ struct FoldArgs {
 };
 
 // Projection value of token j (global position) in column col of sequence b.
-// With P null every token's projections are read from the state ring (one-token steps).
+// With P null, earlier tokens come from the state ring and the new token (T = 1) from its
+// partial sums, added in slice order.
 __device__ __forceinline__ float proj(const FoldArgs& a, int b, int p0, int j, int col) {
   if (a.P && j >= p0) return a.P[((size_t)b * a.T + (j - p0)) * a.NP + col];
+  if (a.part && j == p0) {
+    float v = 0.f;
+#pragma unroll
+    for (int s = 0; s < PU_SLICES; ++s) v += a.part[((size_t)s * a.B + b) * a.NP + col];
+    return v;
+  }
   return a.state[((size_t)b * a.S + (j % a.S)) * a.NP + col];
 }
 
@@ -124,6 +135,14 @@ __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, f
   const int t = threadIdx.x;
   const int p0 = a.pos0[b];
   const int u = 2 * t;
+  const int nfold = a.T + a.T / a.m + 1;
+  if (slot >= nfold) {
+    // the new token's summed projections (512 columns per block) into its state slot
+    const int c0 = 512 * (slot - nfold);
+    float* dst = a.state + ((size_t)b * a.S + (p0 % a.S)) * a.NP;
+    for (int col = c0 + t; col < min(c0 + 512, a.NP); col += 64 * NW) dst[col] = proj(a, b, p0, p0, col);
+    return;
+  }
   if (slot < a.T) {
     // raw window row of token j = p0 + slot: a-path row (HCA: C), finalized at position j.
     const int j = p0 + slot;
@@ -175,9 +194,11 @@ __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, f
 
 
 // Host: the arguments of a fold of T tokens per sequence of cache c (P: summed projections of
-// the chunk, or null when every token's projections sit in the state ring).
+// the chunk, or null when the projections sit in the state ring; part: with T = 1 and P null,
+// the new token's partial projections, or null when it too is in the state ring).
 FoldArgs fold_args(const csa_dims& d, const csa_weights& w, const csa_cache& c, int32_t T,
-                   const int32_t* pos0, const float* P);
-inline int fold_grid_x(const csa_dims& d, int32_t T) { return T + T / d.m + 1; }
+                   const int32_t* pos0, const float* P, const float* part = nullptr);
+// Blocks per sequence: T raw rows, T/m + 1 entry slots, and with part the state writers.
+inline int fold_grid_x(const FoldArgs& a) { return a.T + a.T / a.m + 1 + (a.part ? (a.NP + 511) / 512 : 0); }
 
 }  // namespace csa

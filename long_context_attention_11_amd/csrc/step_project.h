@@ -9,90 +9,90 @@
 
 namespace csa {
 
-// One 16-row x 16-column output tile per workgroup of NW waves (NW = 16: 1024 threads; NW = 4:
-// the 256-thread launches).  K is split in PS_WAVES = 16 slices, PS_WAVES / NW per wave, each
-// accumulated on its own (its weight rows loaded straight into MFMA operands, PS_DEPTH steps
-// per round: at d = 4096 one round per slice, every load of the round in flight at once); the
-// sixteen partial tiles are summed through LDS in a fixed order, so the result does not depend
-// on NW.  It goes directly into the sequence's projection-state slot for the token
-// (pos0[b] % S), where the fold reads it, so there is no separate split-K reduction or state
-// copy.
-constexpr int PS_DEPTH = 8;
-constexpr int PS_WAVES = 16;
+// The work is cut into wave-sized units so that it spreads over every CU (one CU streams
+// only some 25 GB/s from HBM, so a launch needs all of them): a unit is TILES 16-column
+// output tiles x one of PU_SLICES slices of K, for one 16-row tile of tokens, and its partial
+// sums go to part[slice][row][col].  The fold adds the PU_SLICES partials in slice order (so
+// the result is deterministic) and also writes the summed row into the projection state.
+// Each lane reads 32 contiguous bytes per pair of K steps: lane group g takes elements
+// 16g .. 16g+15 of each 64-element pair, the first eight for the pair's first MFMA step and
+// the rest for its second, on both operands alike, so the four lane groups together read
+// whole 128-byte lines of the 16 rows.  The tiles of a unit share the token operand.
+constexpr int PU_SLICES = 16;   // slices of K (partial sums per output)
+constexpr int PU_PAIRS = 4;     // 64-element pairs per load round
 
 struct ProjectStepArgs {
   const uint16_t* H;      // [M][K] bf16
   const uint16_t* wkv;    // [nkv][K] bf16
   const uint16_t* widx;   // [NP - nkv][K] bf16
-  int nkv, M, NP, K;
-  const int32_t* pos0;    // [M]
-  int S;                  // state rows
-  float* state;           // [M][S][NP]
+  int nkv, M, NP, K;      // K a multiple of 64 * PU_SLICES
+  float* part;            // [PU_SLICES][M][NP]
 };
 
-// Tile (bx, by) = output columns 16 bx .. +15, rows 16 by .. +15.  red: LDS [PS_WAVES][256].
-template <int NW>
-__device__ __forceinline__ void project_step_tile(const ProjectStepArgs& a, int bx, int by,
-                                                  float (*red)[256]) {
-  static_assert(PS_WAVES % NW == 0, "slices per wave");
-  constexpr int SL = PS_WAVES / NW;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int fr = lane & 15, fg = lane >> 4;
-  const int n0 = bx * 16, m0 = by * 16;
-  const int K = a.K;
-  const int kq = K / PS_WAVES;                // one slice of K (a multiple of 32)
-  const int nsteps = kq / 32;
-  const int n = min(n0 + fr, a.NP - 1);
-  const uint16_t* arow0 = a.H + (size_t)min(m0 + fr, a.M - 1) * K + fg * 8;
-  const uint16_t* brow0 = (n < a.nkv ? a.wkv + (size_t)n * K : a.widx + (size_t)(n - a.nkv) * K) + fg * 8;
+__host__ __device__ inline int project_col_groups(int NP, int tiles) { return ((NP + 15) / 16 + tiles - 1) / tiles; }
+inline int project_units(int NP, int M, int tiles) { return project_col_groups(NP, tiles) * PU_SLICES * ((M + 15) / 16); }
+
+// Unit u (one wave): column group u % G, slice (u / G) % PU_SLICES, row tile u / (G PU_SLICES).
+template <int TILES>
+__device__ __forceinline__ void project_unit(const ProjectStepArgs& a, int u) {
+  const int lane = threadIdx.x & 63, fr = lane & 15, fg = lane >> 4;
+  const int ncg = project_col_groups(a.NP, TILES), px = (a.NP + 15) / 16;
+  const int cg = u % ncg, sl = (u / ncg) % PU_SLICES, rt = u / (ncg * PU_SLICES);
+  const int K = a.K, kq = K / PU_SLICES, npair = kq / 64;
+  const uint16_t* arow = a.H + (size_t)min(16 * rt + fr, a.M - 1) * K + sl * kq + 16 * fg;
+  const uint16_t* brow[TILES];
 #pragma unroll
-  for (int sl = 0; sl < SL; ++sl) {
-    const int slice = wave * SL + sl;
-    const uint16_t* arow = arow0 + slice * kq;
-    const uint16_t* brow = brow0 + slice * kq;
-    uint4 ra[PS_DEPTH], rb[PS_DEPTH];
+  for (int c = 0; c < TILES; ++c) {
+    const int n = min(16 * min(cg * TILES + c, px - 1) + fr, a.NP - 1);
+    brow[c] = (n < a.nkv ? a.wkv + (size_t)n * K : a.widx + (size_t)(n - a.nkv) * K) + sl * kq + 16 * fg;
+  }
+  f32x4 acc[TILES];
 #pragma unroll
-    for (int i = 0; i < PS_DEPTH; ++i) {
-      const int k = min(i, nsteps - 1) * 32;
-      ra[i] = *reinterpret_cast<const uint4*>(arow + k);
-      rb[i] = *reinterpret_cast<const uint4*>(brow + k);
-    }
-    f32x4 acc = {0, 0, 0, 0};
-    for (int s0 = 0; s0 < nsteps; s0 += PS_DEPTH) {
+  for (int c = 0; c < TILES; ++c) acc[c] = f32x4{0, 0, 0, 0};
+  for (int p0 = 0; p0 < npair; p0 += PU_PAIRS) {
+    // a pair past the end reloads the last one and is not accumulated
+    uint4 ra[2 * PU_PAIRS], rb[TILES][2 * PU_PAIRS];
 #pragma unroll
-      for (int i = 0; i < PS_DEPTH; ++i) {
-        // a step past the end reloads the last one and is not accumulated
-        const bool live = s0 + i < nsteps;
-        const bf16x8 A = __builtin_bit_cast(bf16x8, ra[i]);
-        const bf16x8 Bv = __builtin_bit_cast(bf16x8, rb[i]);
-        const f32x4 nxt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bv, acc, 0, 0, 0);
-        acc = live ? nxt : acc;
-        if (s0 + PS_DEPTH < nsteps) {   // uniform
-          const int k = min(s0 + i + PS_DEPTH, nsteps - 1) * 32;
-          ra[i] = *reinterpret_cast<const uint4*>(arow + k);
-          rb[i] = *reinterpret_cast<const uint4*>(brow + k);
-        }
+    for (int p = 0; p < PU_PAIRS; ++p) {
+      const int k = 64 * min(p0 + p, npair - 1);
+      ra[2 * p] = *reinterpret_cast<const uint4*>(arow + k);
+      ra[2 * p + 1] = *reinterpret_cast<const uint4*>(arow + k + 8);
+#pragma unroll
+      for (int c = 0; c < TILES; ++c) {
+        rb[c][2 * p] = *reinterpret_cast<const uint4*>(brow[c] + k);
+        rb[c][2 * p + 1] = *reinterpret_cast<const uint4*>(brow[c] + k + 8);
       }
     }
-    // D layout: lane holds column fr, rows 4*fg + e
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[slice][(4 * fg + e) * 16 + fr] = acc[e];
+    for (int p = 0; p < PU_PAIRS; ++p) {
+      const bool live = p0 + p < npair;
+#pragma unroll
+      for (int c = 0; c < TILES; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f32x4 nxt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, ra[2 * p + h]), __builtin_bit_cast(bf16x8, rb[c][2 * p + h]), acc[c], 0, 0, 0);
+          acc[c] = live ? nxt : acc[c];
+        }
+    }
   }
-  __syncthreads();
-  if (tid >= 256) return;
-  const int row = tid >> 4, col = tid & 15;
-  float v = red[0][tid];
+  // D layout: lane holds column fr, rows 4*fg + e
 #pragma unroll
-  for (int w = 1; w < PS_WAVES; ++w) v += red[w][tid];
-  const int b = m0 + row, nn = n0 + col;
-  if (b < a.M && nn < a.NP) a.state[((size_t)b * a.S + (a.pos0[b] % a.S)) * a.NP + nn] = v;
+  for (int c = 0; c < TILES; ++c) {
+    const int tile = cg * TILES + c, col = 16 * tile + fr;
+    if (tile < px && col < a.NP) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * rt + 4 * fg + e;
+        if (row < a.M) a.part[((size_t)sl * a.M + row) * a.NP + col] = acc[c][e];
+      }
+    }
+  }
 }
 
-// Host: the arguments for a one-token step of cache c (defined with the compressor).
+// Host: the arguments for a one-token step of cache c (defined with the compressor); part
+// holds project_part_bytes.
 ProjectStepArgs project_step_args(const csa_dims& d, const csa_weights& w, const csa_cache& c,
-                                  const void* H, const int32_t* pos0);
-
-inline int project_step_grid_x(int NP) { return (NP + 15) / 16; }
-inline int project_step_grid_y(int M) { return (M + 15) / 16; }
+                                  const void* H, float* part);
 
 }  // namespace csa

@@ -93,7 +93,8 @@ __device__ __forceinline__ uint32_t slots_max_u(const uint32_t* v) {
 // 32l .. 32l + 31 (read in a staggered order so the lanes spread over the LDS banks); a
 // suffix scan over the lanes finds the lane whose range holds d, and 32 lanes then scan
 // that range in parallel.
-__device__ void find_bin(const int* H, int rem, TopkShared& sh) {
+template <class SH>
+__device__ void find_bin(const int* H, int rem, SH& sh) {
   const int lane = threadIdx.x & 63;
   int own = 0;
 #pragma unroll
@@ -328,25 +329,24 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_segment(
   }
 }
 
-// The smallest key in the threshold bin tbin or above: bins split [fmn, fmn + TK_BINS / scale)
-// evenly; scale 0 puts every score in bin 0.  Any key works as a threshold (the selection
-// checks the count it lets through), so rounding at the bin edge does not matter.
-__device__ __forceinline__ uint32_t threshold_key(float fmn, float scale, int tbin) {
-  return scale > 0.f ? score_key(fmn + (float)tbin / scale) : 0u;
+// Raw float bits u pass iff u - lo <= span (unsigned): exactly the scores whose key is at
+// least score_key(t) (-0 equal to +0, NaNs beyond the infinities on their sign's side).
+__device__ __forceinline__ void pass_interval(float t, uint32_t& lo, uint32_t& span) {
+  uint32_t b = __float_as_uint(t);
+  if (b == 0x80000000u) b = 0u;
+  if (b != 0u && (b & 0x80000000u) == 0u) {   // t > 0: the positive floats from t up, +NaN
+    lo = b;
+    span = 0x7fffffffu - b;
+  } else {                                     // t <= 0: everything from +NaN down to t
+    lo = 0u;
+    span = b == 0u ? 0x80000000u : b;
+  }
 }
 
-// Bit i: element first + i of the row is visible (below V) and its key is at least tkey.
-__device__ __forceinline__ uint32_t pass_mask(const uint32_t (&key)[8], int first, int V, uint32_t tkey) {
-  uint32_t mask = 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) mask |= (first + i < V && key[i] >= tkey) ? 1u << i : 0u;
-  return mask;
-}
-
-// Threshold pass: blockIdx.x = query, blockIdx.y = segment.  Writes the segment's scores with
-// keys at or above the threshold key (all valid scores when the row has at most TK_FINAL)
-// to cand_idx/cand_key [Q][nseg][cs] in index order, and their count (which may exceed cs)
-// to cand_cnt [Q][nseg].
+// Threshold pass: one workgroup per (query, segment of TK_SEG scores).  Writes the segment's
+// scores with keys at or above the threshold key (all valid scores when the row has at most
+// TK_FINAL) to cand_idx/cand_key [Q][nseg][cs] in index order, and their count (which may
+// exceed cs) to cand_cnt [Q][nseg].
 struct FilterArgs {
   const float* scores;
   int64_t ld;
@@ -360,53 +360,42 @@ struct FilterArgs {
   int32_t* vis;           // [Q] the visible count each query was filtered with
 };
 
+// Every workgroup of a row draws the same sample, 64 evenly spaced runs of 64 scores, and
+// takes as threshold the lower edge of the histogram bin (2048 bins between the sample's
+// extremes) above which about 3k of the row's V scores are expected (at most 3/4 of the final
+// pass's TK_FINAL).  Segment layout: wave w reads the run at 512 w, lane l element i at
+// 64 i + l (each load one contiguous 256-byte read, a wave's (i, l) order is index order);
+// the passing scores are compacted with wave ballots and lane counts below the lane.  Reads
+// of a segment start at min(c0, L - TK_SEG), L = max(V, TK_SEG) <= the row stride (these
+// rows are longer than TK_SEG), so every read stays in the row; elements outside [c0, V) are
+// masked.
 __device__ __forceinline__ void topk_filter_body(const FilterArgs& fa, int q, int seg, TopkShared& sh) {
-  const float* __restrict__ scores = fa.scores;
-  const int64_t ld = fa.ld;
-  const int m = fa.m, k = fa.k, cs = fa.cs, nseg = fa.nseg;
-  const int32_t* __restrict__ q_seq = fa.q_seq;
-  const int32_t* __restrict__ q_pos = fa.q_pos;
-  const int32_t* __restrict__ n_entries = fa.n_entries;
-  int32_t* __restrict__ cand_idx = fa.cand_idx;
-  uint32_t* __restrict__ cand_key = fa.cand_key;
-  int32_t* __restrict__ cand_cnt = fa.cand_cnt;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int V = visible(q_seq, q_pos, n_entries, m, q);
-  const float* row = scores + (size_t)q * ld;
-  const bool vec = (ld & 3) == 0;
+  const int k = fa.k, cs = fa.cs, nseg = fa.nseg;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int V = visible(fa.q_seq, fa.q_pos, fa.n_entries, fa.m, q);
+  const float* row = fa.scores + (size_t)q * fa.ld;
   const bool take_all = V <= TK_FINAL;
-  // this thread's run of the segment, then its 4 samples: the sample is 64 evenly spaced runs
-  // of 64 scores (V > TK_FINAL, so the runs fit), the same for every segment of the row
-  const int first = seg * TK_SEG + tid * 8;
-  float sv[8], smp[4];
-  if (first + 8 <= V && vec) {
-    const float4 a = *reinterpret_cast<const float4*>(row + first);
-    const float4 b = *reinterpret_cast<const float4*>(row + first + 4);
-    sv[0] = a.x; sv[1] = a.y; sv[2] = a.z; sv[3] = a.w;
-    sv[4] = b.x; sv[5] = b.y; sv[6] = b.z; sv[7] = b.w;
-  } else {
+  const int L = max(V, TK_SEG);
+  // the sample first, then the segment, so their latencies overlap
+  const int bs = ((int)((int64_t)(tid >> 4) * (L - 64) / 63) & ~3) + 4 * (tid & 15);
+  float smp[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sv[i] = first + i < V ? row[first + i] : 0.f;
-  }
+  for (int i = 0; i < 4; ++i) smp[i] = row[bs + i];
+  const int c0 = seg * TK_SEG;
+  const int a0 = min(c0, L - TK_SEG) + 512 * w;
+  float sv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sv[i] = row[a0 + 64 * i + lane];
+  uint32_t lo = 0u, span = 0xffffffffu;   // every score passes
   if (!take_all) {   // uniform
-    const int bs = ((int)((int64_t)(tid >> 4) * (V - 64) / 63) & ~3) + 4 * (tid & 15);
-    if (vec) {
-      const float4 v = *reinterpret_cast<const float4*>(row + bs);
-      smp[0] = v.x; smp[1] = v.y; smp[2] = v.z; smp[3] = v.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) smp[i] = row[bs + i];
-    }
-  }
-  uint32_t tkey = 0u;   // 0: every valid score passes
-  if (!take_all) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) smp[i] = key_score(score_key(smp[i]));
-    float lo = fminf(fminf(smp[0], smp[1]), fminf(smp[2], smp[3]));
-    float hi = fmaxf(fmaxf(smp[0], smp[1]), fmaxf(smp[2], smp[3]));
-    lo = wave_min_f(lo);
-    hi = wave_max_f(hi);
-    if (lane == 0) { sh.red_lo[w] = lo; sh.red_hi[w] = hi; }
+    float mn = fminf(fminf(smp[0], smp[1]), fminf(smp[2], smp[3]));
+    float mx = fmaxf(fmaxf(smp[0], smp[1]), fmaxf(smp[2], smp[3]));
+    mn = wave_min_f(mn);
+    mx = wave_max_f(mx);
+    if (lane == 0) { sh.red_lo[w] = mn; sh.red_hi[w] = mx; }
     for (int b = tid; b < TK_BINS; b += TK_THREADS) sh.hist[0][b] = 0;
     __syncthreads();
     const float fmn = slots_min(sh.red_lo);
@@ -415,38 +404,43 @@ __device__ __forceinline__ void topk_filter_body(const FilterArgs& fa, int q, in
 #pragma unroll
     for (int i = 0; i < 4; ++i) atomicAdd(&sh.hist[0][min(TK_BINS - 1, (int)((smp[i] - fmn) * scale))], 1);
     __syncthreads();
-    // samples at or above the threshold: about 3k (at most 3/4 of the final capacity) of
-    // the row's V scores are then expected to pass
     const int target = min(3 * k, TK_FINAL * 3 / 4);
     const int r = (int)min((int64_t)TK_NS, ((int64_t)target * TK_NS + V - 1) / V);
     if (w == 0) find_bin(sh.hist[0], r, sh);
     __syncthreads();
-    tkey = threshold_key(fmn, scale, sh.sel_bin);
+    if (scale > 0.f) pass_interval(fmn + (float)sh.sel_bin / scale, lo, span);
   }
-  uint32_t key[8];
+  const int vlo = max(0, c0 - a0), vspan = max(0, min(512, V - a0) - vlo);   // uniform
+  bool p[8];
+  uint64_t bal[8];
+  int cnt = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) key[i] = score_key(sv[i]);
-  const uint32_t mask = pass_mask(key, first, V, tkey);
-  const int cnt = __popc(mask);
-  const int x = wave_incl_scan(cnt);   // over the wave, then over the waves
-  if (lane == 63) sh.scan[w] = x;
+  for (int i = 0; i < 8; ++i) {
+    p[i] = __float_as_uint(sv[i]) - lo <= span && (uint32_t)(64 * i + lane - vlo) < (uint32_t)vspan;
+    bal[i] = __ballot(p[i]);
+    cnt += __popcll(bal[i]);
+  }
+  if (lane == 0) sh.scan[w] = cnt;
   __syncthreads();
-  const int sw = sh.scan[tid & 15];
-  const int before = row_allreduce((tid & 15) < w ? sw : 0, OpAdd());
-  const int total = row_allreduce(sw, OpAdd());
-  int pos = before + x - cnt;
-  int32_t* ci = cand_idx + ((size_t)q * nseg + seg) * cs;
-  uint32_t* ck = cand_key + ((size_t)q * nseg + seg) * cs;
+  const int sw = sh.scan[lane & 15];
+  const int before = __builtin_amdgcn_readfirstlane(row_allreduce((lane & 15) < w ? sw : 0, OpAdd()));
+  const int total = row_allreduce(sw, OpAdd());   // every lane of the row takes part
+  int32_t* ci = fa.cand_idx + ((size_t)q * nseg + seg) * cs;
+  uint32_t* ck = fa.cand_key + ((size_t)q * nseg + seg) * cs;
+  uint32_t base = (uint32_t)before;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (mask >> i & 1u) {
+  for (int i = 0; i < 8; ++i) {
+    if (p[i]) {
+      const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[i] >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal[i], base));
       if (pos < cs) {
-        ci[pos] = first + i;
-        ck[pos] = key[i];
+        ci[pos] = a0 + 64 * i + lane;
+        ck[pos] = score_key(sv[i]);
       }
-      ++pos;
     }
-  if (tid == 0) cand_cnt[(size_t)q * nseg + seg] = total;
+    base += (uint32_t)__popcll(bal[i]);
+  }
+  if (tid == 0) fa.cand_cnt[(size_t)q * nseg + seg] = total;
   if (tid == 0 && seg == 0) fa.vis[q] = V;
 }
 
@@ -455,17 +449,29 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_filter(FilterArgs fa) {
   topk_filter_body(fa, blockIdx.x, blockIdx.y, sh);
 }
 
-// The threshold pass and a one-token projection step in one launch (they are independent;
-// blocks [0, Q * nseg) filter, the rest project), so the projection's weight stream runs on
-// the CUs the filter leaves idle.
+// The threshold pass and a one-token projection in one launch (they are independent), so the
+// projection's weight stream runs beside the filter.  Blocks [0, Q * nseg) filter; in the
+// rest, waves 0 .. upb - 1 run one projection unit each and the others have nothing to do,
+// upb chosen so that the workgroups of the launch fill the 256 CUs once: each CU then streams
+// its fair share of the weights.
 __global__ __launch_bounds__(TK_THREADS) void k_topk_filter_project(FilterArgs fa, int Q, ProjectStepArgs pa,
-                                                                     int px) {
+                                                                     int units, int upb) {
   __shared__ TopkShared sh;
-  __shared__ float red[PS_WAVES][256];
   const int nf = Q * fa.nseg;
-  const int b = blockIdx.x;
-  if (b < nf) topk_filter_body(fa, b % Q, b / Q, sh);
-  else project_step_tile<PS_WAVES>(pa, (b - nf) % px, (b - nf) / px, red);
+  const int b = blockIdx.x, wave = threadIdx.x >> 6;
+  if (b < nf) {
+    topk_filter_body(fa, b % Q, b / Q, sh);
+  } else if (wave < upb) {
+    const int u = upb * (b - nf) + wave;
+    if (u < units) project_unit<2>(pa, u);
+  }
+}
+
+// Projection units per workgroup of the combined launch (0: the launch cannot carry them).
+int carry_units_per_block(int nf, int units) {
+  if (nf >= 256) return 0;
+  const int upb = (units + (256 - nf) - 1) / (256 - nf);
+  return upb <= TK_WAVES ? upb : 0;
 }
 
 struct FinalShared {
@@ -631,20 +637,6 @@ __device__ __forceinline__ int select_lds(RowShared& rs, int N, int k, int32_t* 
     it.key[i] = p < N ? score_key(__uint_as_float(rs.c_key[p])) : 0u;
   }
   return select_topk<E>(it, k, rs.sh, out, nullptr);
-}
-
-// Raw float bits u pass iff u - lo <= span (unsigned): exactly the scores whose key is at
-// least score_key(t) (-0 equal to +0, NaNs beyond the infinities on their sign's side).
-__device__ __forceinline__ void pass_interval(float t, uint32_t& lo, uint32_t& span) {
-  uint32_t b = __float_as_uint(t);
-  if (b == 0x80000000u) b = 0u;
-  if (b != 0u && (b & 0x80000000u) == 0u) {   // t > 0: the positive floats from t up, +NaN
-    lo = b;
-    span = 0x7fffffffu - b;
-  } else {                                     // t <= 0: everything from +NaN down to t
-    lo = 0u;
-    span = b == 0u ? 0x80000000u : b;
-  }
 }
 
 // One chunk of the row (scores v, wave w's run starting at a0 = s + 512 w) into the LDS
@@ -822,11 +814,12 @@ size_t topk_filter_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap) {
 
 bool topk_can_carry(const csa_cache& c) { return c.cap > TK_SEG; }
 
-// Only while the threshold blocks and the projection blocks fit on the 256 CUs at once (one
-// 1024-thread workgroup each): beyond that the carried step only lengthens the pass.
-bool topk_can_carry_step(const csa_cache& c, int32_t Q, int32_t step_blocks) {
+// Only while the threshold and projection workgroups (1024 threads, one per CU) all fit on
+// the 256 CUs at once: beyond that the carried step only lengthens the pass.
+bool topk_can_carry_step(const csa_cache& c, int32_t Q, int32_t step_units) {
   if (!topk_can_carry(c)) return false;
-  return (int64_t)Q * ((c.cap + TK_SEG - 1) / TK_SEG) + step_blocks <= 256;
+  const int64_t nf = (int64_t)Q * ((c.cap + TK_SEG - 1) / TK_SEG);
+  return nf < 256 && carry_units_per_block((int)nf, step_units) > 0;
 }
 
 hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
@@ -861,9 +854,11 @@ hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_s
   int32_t* fvis = cc + (size_t)Q * nseg;   // the counts the threshold pass filtered with
   const FilterArgs fa{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, cs, nseg, ci, ck, cc, fvis};
   if (step) {
-    const int px = project_step_grid_x(step->NP), py = project_step_grid_y(step->M);
-    hipLaunchKernelGGL(k_topk_filter_project, dim3(Q * nseg + px * py), dim3(TK_THREADS), 0, s, fa, Q,
-                       *step, px);
+    const int units = project_units(step->NP, step->M, 2);
+    const int upb = carry_units_per_block(Q * nseg, units);
+    if (upb == 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_topk_filter_project, dim3(Q * nseg + (units + upb - 1) / upb), dim3(TK_THREADS), 0, s,
+                       fa, Q, *step, units, upb);
   } else {
     hipLaunchKernelGGL(k_topk_filter, dim3(Q, nseg), dim3(TK_THREADS), 0, s, fa);
   }
@@ -871,7 +866,7 @@ hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_s
   if (e != hipSuccess) return e;
   const FinalArgs fin{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, nseg, cs, ci, ck, cc, fvis, idx};
   if (fold) {
-    const int fx = fold->T + fold->T / fold->m + 1;
+    const int fx = fold_grid_x(*fold);
     hipLaunchKernelGGL(k_topk_final_fold, dim3(Q + fx * c.B), dim3(TK_THREADS), 0, s, fin, Q, *fold, fx);
   } else {
     hipLaunchKernelGGL(k_topk_final, dim3(Q), dim3(TK_THREADS), 0, s, fin);
