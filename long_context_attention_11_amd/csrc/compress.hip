@@ -145,9 +145,10 @@ __global__ __launch_bounds__(64) void k_project_step(ProjectStepArgs a, int unit
 
 // grid: x = T raw rows + (T/m + 1) entry slots (+ state writers), y = sequence.  256
 // threads, 2 columns each.
+template <bool PART>
 __global__ __launch_bounds__(256) void k_fold(FoldArgs a) {
   __shared__ float red[4];
-  fold_block<4>(a, blockIdx.x, blockIdx.y, red);
+  fold_block<4, PART>(a, blockIdx.x, blockIdx.y, red);
 }
 
 // Keep the projections of the last S tokens of each sequence: slot j % S.
@@ -303,7 +304,8 @@ hipError_t launch_fold(const csa_dims& d, const csa_weights& w, const csa_cache&
   if (ksplit != 1) return hipErrorInvalidValue;  // partials are summed first
   const FoldArgs a = fold_args(d, w, c, T, pos0, P, part);
   dim3 grid(fold_grid_x(a), c.B);
-  hipLaunchKernelGGL(k_fold, grid, dim3(256), 0, s, a);
+  if (a.part) hipLaunchKernelGGL(k_fold<true>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_fold<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

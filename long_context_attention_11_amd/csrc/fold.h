@@ -35,15 +35,20 @@ struct FoldArgs {
 };
 
 // Projection value of token j (global position) in column col of sequence b.
-// With P null, earlier tokens come from the state ring and the new token (T = 1) from its
-// partial sums, added in slice order.
+// PART (one-token steps, a.part set): earlier tokens come from the state ring and the new
+// token from its partial sums, added in slice order.  Otherwise tokens of the chunk come from
+// P (or, with P null, everything from the state ring).
+template <bool PART>
 __device__ __forceinline__ float proj(const FoldArgs& a, int b, int p0, int j, int col) {
-  if (a.P && j >= p0) return a.P[((size_t)b * a.T + (j - p0)) * a.NP + col];
-  if (a.part && j == p0) {
-    float v = 0.f;
+  if constexpr (PART) {
+    if (j == p0) {
+      float v = 0.f;
 #pragma unroll
-    for (int s = 0; s < PU_SLICES; ++s) v += a.part[((size_t)s * a.B + b) * a.NP + col];
-    return v;
+      for (int s = 0; s < PU_SLICES; ++s) v += a.part[((size_t)s * a.B + b) * a.NP + col];
+      return v;
+    }
+  } else {
+    if (a.P && j >= p0) return a.P[((size_t)b * a.T + (j - p0)) * a.NP + col];
   }
   return a.state[((size_t)b * a.S + (j % a.S)) * a.NP + col];
 }
@@ -52,6 +57,7 @@ __device__ __forceinline__ float proj(const FoldArgs& a, int b, int p0, int j, i
 //   CSA: logits Z^a_{mi+r} + B^a_r and Z^b_{m(i-1)+r} + B^b_r (b half absent for i = 0),
 //        values C^a and C^b.  HCA: logits Z_{mi+r} + B_r over the m rows of block i.
 // colC/colZ name the projection columns of the a path; b-path columns are +boff.
+template <bool PART>
 __device__ __forceinline__ float fold_column(const FoldArgs& a, int b, int p0, int i, int colCa, int colZa,
                              int boff, const float* Ba, const float* Bb, int bstride_col,
                              int u) {
@@ -59,21 +65,21 @@ __device__ __forceinline__ float fold_column(const FoldArgs& a, int b, int p0, i
   const int ja = m * i, jb = m * (i - 1);
   const bool has_b = a.dual && i > 0;
   float mx = -INFINITY;
-  for (int r = 0; r < m; ++r) mx = fmaxf(mx, proj(a, b, p0, ja + r, colZa) + Ba[r * bstride_col + u]);
+  for (int r = 0; r < m; ++r) mx = fmaxf(mx, proj<PART>(a, b, p0, ja + r, colZa) + Ba[r * bstride_col + u]);
   if (has_b)
     for (int r = 0; r < m; ++r)
-      mx = fmaxf(mx, proj(a, b, p0, jb + r, colZa + boff) + Bb[r * bstride_col + u]);
+      mx = fmaxf(mx, proj<PART>(a, b, p0, jb + r, colZa + boff) + Bb[r * bstride_col + u]);
   float den = 0.f, num = 0.f;
   for (int r = 0; r < m; ++r) {
-    float e = expf(proj(a, b, p0, ja + r, colZa) + Ba[r * bstride_col + u] - mx);
+    float e = expf(proj<PART>(a, b, p0, ja + r, colZa) + Ba[r * bstride_col + u] - mx);
     den += e;
-    num = fmaf(e, proj(a, b, p0, ja + r, colCa), num);
+    num = fmaf(e, proj<PART>(a, b, p0, ja + r, colCa), num);
   }
   if (has_b)
     for (int r = 0; r < m; ++r) {
-      float e = expf(proj(a, b, p0, jb + r, colZa + boff) + Bb[r * bstride_col + u] - mx);
+      float e = expf(proj<PART>(a, b, p0, jb + r, colZa + boff) + Bb[r * bstride_col + u] - mx);
       den += e;
-      num = fmaf(e, proj(a, b, p0, jb + r, colCa + boff), num);
+      num = fmaf(e, proj<PART>(a, b, p0, jb + r, colCa + boff), num);
     }
   return num / den;
 }
@@ -130,17 +136,17 @@ __device__ __forceinline__ void finalize_store(const FoldArgs& a, float x0, floa
 // the entry slot - T past pos0[b] / m (when its block completes in this chunk).  Threads hold
 // columns 2t, 2t + 1; a block of NW waves (NW >= 4; those past the c columns hold zeros).
 // red: LDS [NW].
-template <int NW>
+template <int NW, bool PART>
 __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, float* red) {
   const int t = threadIdx.x;
   const int p0 = a.pos0[b];
   const int u = 2 * t;
   const int nfold = a.T + a.T / a.m + 1;
-  if (slot >= nfold) {
+  if (PART && slot >= nfold) {
     // the new token's summed projections (512 columns per block) into its state slot
     const int c0 = 512 * (slot - nfold);
     float* dst = a.state + ((size_t)b * a.S + (p0 % a.S)) * a.NP;
-    for (int col = c0 + t; col < min(c0 + 512, a.NP); col += 64 * NW) dst[col] = proj(a, b, p0, p0, col);
+    for (int col = c0 + t; col < min(c0 + 512, a.NP); col += 64 * NW) dst[col] = proj<PART>(a, b, p0, p0, col);
     return;
   }
   if (slot < a.T) {
@@ -151,8 +157,8 @@ __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, f
     const int ws = j % a.win_cap;
     float x0 = 0.f, x1 = 0.f;
     if (u < a.c) {
-      x0 = proj(a, b, p0, j, u);
-      x1 = proj(a, b, p0, j, u + 1);
+      x0 = proj<PART>(a, b, p0, j, u);
+      x1 = proj<PART>(a, b, p0, j, u + 1);
     }
     uint8_t* dst = a.win + ((size_t)b * a.win_cap + ws) * a.rowB;
     finalize_store<NW>(a, x0, x1, j, dst, red);
@@ -165,11 +171,11 @@ __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, f
   float x0 = 0.f, x1 = 0.f;
   if (u < a.c) {
     if (a.dual) {
-      x0 = fold_column(a, b, p0, i, u, 2 * a.c + u, a.c, a.bias, a.bias + a.m * a.c, a.c, u);
-      x1 = fold_column(a, b, p0, i, u + 1, 2 * a.c + u + 1, a.c, a.bias, a.bias + a.m * a.c, a.c, u + 1);
+      x0 = fold_column<PART>(a, b, p0, i, u, 2 * a.c + u, a.c, a.bias, a.bias + a.m * a.c, a.c, u);
+      x1 = fold_column<PART>(a, b, p0, i, u + 1, 2 * a.c + u + 1, a.c, a.bias, a.bias + a.m * a.c, a.c, u + 1);
     } else {
-      x0 = fold_column(a, b, p0, i, u, a.c + u, 0, a.bias, a.bias, a.c, u);
-      x1 = fold_column(a, b, p0, i, u + 1, a.c + u + 1, 0, a.bias, a.bias, a.c, u + 1);
+      x0 = fold_column<PART>(a, b, p0, i, u, a.c + u, 0, a.bias, a.bias, a.c, u);
+      x1 = fold_column<PART>(a, b, p0, i, u + 1, a.c + u + 1, 0, a.bias, a.bias, a.c, u + 1);
     }
   }
   uint8_t* dst = a.kv + ((size_t)b * a.cap + i) * a.rowB;
@@ -179,8 +185,8 @@ __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, f
     const int base = 4 * a.c;
     const float* BIa = a.bias_idx;
     const float* BIb = a.bias_idx + a.m * a.cI;
-    float k0 = fold_column(a, b, p0, i, base + u, base + 2 * a.cI + u, a.cI, BIa, BIb, a.cI, u);
-    float k1 = fold_column(a, b, p0, i, base + u + 1, base + 2 * a.cI + u + 1, a.cI, BIa, BIb, a.cI, u + 1);
+    float k0 = fold_column<PART>(a, b, p0, i, base + u, base + 2 * a.cI + u, a.cI, BIa, BIb, a.cI, u);
+    float k1 = fold_column<PART>(a, b, p0, i, base + u + 1, base + 2 * a.cI + u + 1, a.cI, BIa, BIb, a.cI, u + 1);
     if (a.idx_fmt == CSA_FMT_F32) {
       float* kd = reinterpret_cast<float*>(a.ki) + ((size_t)b * a.cap + i) * a.cI;
       kd[u] = k0;

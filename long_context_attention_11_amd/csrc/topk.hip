@@ -598,7 +598,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_final_fold(FinalArgs fa, in
   __shared__ float red[TK_WAVES];
   const int b = blockIdx.x;
   if (b < Q) topk_final_body(fa, b, fs);
-  else fold_block<TK_WAVES>(fo, (b - Q) % fx, (b - Q) / fx, red);
+  else fold_block<TK_WAVES, true>(fo, (b - Q) % fx, (b - Q) / fx, red);
 }
 
 // ----------------------------------------------------------------------- one-launch rows
@@ -866,6 +866,7 @@ hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_s
   if (e != hipSuccess) return e;
   const FinalArgs fin{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, nseg, cs, ci, ck, cc, fvis, idx};
   if (fold) {
+    if (!fold->part) return hipErrorInvalidValue;   // the carried fold is a one-token step's
     const int fx = fold_grid_x(*fold);
     hipLaunchKernelGGL(k_topk_final_fold, dim3(Q + fx * c.B), dim3(TK_THREADS), 0, s, fin, Q, *fold, fx);
   } else {
