@@ -79,7 +79,7 @@ class Dims:
     top_k    entries kept per query; 0 means every visible entry (HCA, [RN] eq. 26)
     n_win    sliding-window length over uncompressed tokens ([RN] §2.5.3; [PT] §2.4)
     kv_fmt   "f32" or "q" (E4M3 for the non-RoPE dims, bfloat16 for the RoPE dims)
-    idx_fmt  "f32" or "e4m3" (indexer keys)
+    idx_fmt  "f32", "e4m3" or "mxfp4" (indexer keys and queries)
     """
 
     d: int
@@ -230,13 +230,17 @@ def store_kv(y, dims: Dims):
 
 
 def store_index_keys(k, dims: Dims):
-    """Round indexer keys to storage: float32, or E4M3 with unit scale (reading: the pages'
-    FP4 indexer path is a later refinement; E4M3 is the storage taken here).  Returns
-    (values, bytes)."""
+    """Round indexer keys to storage: float32, E4M3 with unit scale, or MXFP4 (the pages'
+    later FP4 indexer path, reading notes §3.3-3.4).  Returns (values, bytes); for MXFP4 the
+    bytes are the packed element codes followed by the block scale codes, per key."""
     k = np.asarray(k, np.float64)
     if dims.idx_fmt == "f32":
         v = codecs.to_f32(k)
         return v, v.astype(np.float32).view(np.uint8).reshape(k.shape[:-1] + (4 * k.shape[-1],))
+    if dims.idx_fmt == "mxfp4":
+        codes, scales = codecs.mxfp4_encode(k)
+        packed = codecs.mxfp4_pack(codes)
+        return codecs.mxfp4_decode(packed, scales), np.concatenate([packed, scales], axis=-1)
     code = codecs.e4m3_encode(k)
     return codecs.e4m3_decode(code), code
 

@@ -119,6 +119,67 @@ def test_bf16_matches_torch():
 # ----------------------------------------------------------------------------- fold
 
 
+def test_e2m1_e8m0_tables_match_format_definition():
+    """OCP MX v1.0: E2M1 positive values 0, 0.5, 1, 1.5, 2, 3, 4, 6 (code 8 is -0); E8M0
+    code c is 2^(c - 127), 255 is NaN.  Values written out by hand, not by the oracle's
+    formula."""
+    pos = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    t = codecs.e2m1_values()
+    assert list(t[:8]) == pos
+    assert list(-t[8:]) == pos and np.signbit(t[8])
+    assert codecs.e8m0_decode(127) == 1.0 and codecs.e8m0_decode(128) == 2.0
+    assert codecs.e8m0_decode(0) == 2.0 ** -127 and codecs.e8m0_decode(254) == 2.0 ** 127
+    assert np.isnan(codecs.e8m0_decode(255))
+
+
+def test_mxfp4_rounding_ties_and_saturation():
+    """Scaled values at every midpoint round to the even code; past 6 they saturate."""
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    want = [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
+    assert list(codecs.e2m1_decode(codecs.e2m1_encode_scaled(ties, 0))) == want
+    assert list(codecs.e2m1_decode(codecs.e2m1_encode_scaled(-ties, 0))) == [-v for v in want]
+    near = np.array([0.26, 0.74, 1.26, 1.74, 2.51, 3.49, 5.01, 6.5, 7.99, 100.0])
+    assert list(codecs.e2m1_decode(codecs.e2m1_encode_scaled(near, 0))) == \
+        [0.5, 0.5, 1.5, 1.5, 3.0, 3.0, 6.0, 6.0, 6.0, 6.0]
+    # the same decisions at another scale: X = 2^-3
+    assert list(codecs.e2m1_decode(codecs.e2m1_encode_scaled(ties / 8, -3))) == want
+    # brute force: the chosen magnitude is the nearest, ties to the even code
+    rng = np.random.default_rng(7)
+    a = rng.uniform(0, 6, 20000)
+    got = codecs.e2m1_encode_scaled(a, 0) & 7
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    for x, g in zip(a.astype(np.float32).astype(np.float64), got):
+        d = np.abs(mags - x)
+        best = np.flatnonzero(d == d.min())
+        assert g == (best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0])
+
+
+def test_mxfp4_scale_rule_and_round_trip():
+    """X = 2^(floor(log2 max|v|) - 2) per block of 32; representable blocks come back
+    unchanged; blocks are independent; an all-zero block takes X = 1."""
+    blk = np.zeros((1, 32)); blk[0, 3] = 1.0                     # max 1 -> X = 2^-2, 1/X = 4
+    c, s = codecs.mxfp4_encode(blk)
+    assert s[0, 0] == 127 - 2 and codecs.e2m1_decode(c[0, 3]) == 4.0
+    for amax, e in ((4.0, 0), (7.99, 0), (8.0, 1), (0.3, -4), (6.0 * 2.0 ** -10, -10)):
+        b = np.zeros((1, 32)); b[0, 0] = amax
+        assert codecs.mxfp4_scale_exponent(b)[0, 0] == e, (amax, e)
+    z = np.zeros((2, 64))
+    c, s = codecs.mxfp4_encode(z)
+    assert np.all(s == 127) and np.all(c == 0)
+    rng = np.random.default_rng(3)
+    vals = codecs.e2m1_values()[rng.integers(0, 16, (50, 64))]
+    vals[:, 0], vals[:, 32] = 6.0, -4.0                          # each block's max is 4 or 6
+    scale = np.ldexp(1.0, rng.integers(-6, 4, (50, 2)))
+    x = vals * np.repeat(scale, 32, axis=1)
+    c, s = codecs.mxfp4_encode(x)
+    assert np.array_equal(codecs.mxfp4_decode(codecs.mxfp4_pack(c), s), x)
+    c1, s1 = codecs.mxfp4_encode(x[:, :32])
+    c2, s2 = codecs.mxfp4_encode(x[:, 32:])
+    assert np.array_equal(c, np.concatenate([c1, c2], 1)) and np.array_equal(s, np.concatenate([s1, s2], 1))
+    assert codecs.mxfp4_pack(np.array([1, 2], np.uint8))[0] == 0x21
+    assert np.array_equal(codecs.mxfp4_unpack(np.array([0x9F], np.uint8)), [0xF, 0x9])
+
+
 def test_fold_softmax_columns_sum_to_one():
     rng = np.random.default_rng(3)
     n, c, m = 24, 7, 4
@@ -320,6 +381,15 @@ def test_index_scores_closed_form_and_exactness():
     for j in range(50):
         exact = sum((Fraction(float(a)) * Fraction(float(b)) for a, b in zip(q[0], K[j])), Fraction(0))
         assert s[j] == float(max(exact, Fraction(0)))  # bit-exact: dots of E4M3 values fit float64
+    # MXFP4 operands (per-block scales differ): the dots are exact in float64 as well
+    cq, sq = codecs.mxfp4_encode(rng.standard_normal((1, 128)) * 3)
+    ck, sk = codecs.mxfp4_encode(rng.standard_normal((20, 128)) * np.array([0.05, 0.5, 2.0, 0.01]).repeat(32))
+    q4 = codecs.mxfp4_decode(codecs.mxfp4_pack(cq), sq)
+    K4 = codecs.mxfp4_decode(codecs.mxfp4_pack(ck), sk)
+    s4 = R.index_scores(q4, np.ones(1), K4)
+    for j in range(20):
+        exact = sum((Fraction(float(a)) * Fraction(float(b)) for a, b in zip(q4[0], K4[j])), Fraction(0))
+        assert s4[j] == float(max(exact, Fraction(0)))
     # several heads: sum_h w_h ReLU(q_h . K_s)
     qh = rng.standard_normal((3, 64))
     w = np.array([0.5, -2.0, 1.25])
