@@ -56,7 +56,8 @@ typedef enum csa_format {
   CSA_FMT_F32 = 0,        /* float32 */
   CSA_FMT_BF16 = 1,       /* bfloat16 */
   CSA_FMT_E4M3 = 2,       /* OCP FP8 E4M3 (e4m3fn), unit scale */
-  CSA_FMT_E4M3_BF16 = 3   /* KV rows: c - rope_dim E4M3 bytes, then rope_dim bfloat16 */
+  CSA_FMT_E4M3_BF16 = 3,  /* KV rows: c - rope_dim E4M3 bytes, then rope_dim bfloat16 */
+  CSA_FMT_MXFP4 = 4       /* OCP MX FP4: blocks of 32 E2M1 elements sharing one E8M0 scale */
 } csa_format;
 
 /* Operation selector for csa_workspace_size(). */
@@ -86,7 +87,15 @@ typedef enum csa_op {
  *   kv_fmt    F32 (c floats per row) or E4M3_BF16 (c - rope_dim + 2 * rope_dim bytes per row:
  *             RoPE dims kept in BF16, the rest in FP8, as the explainer's key-numbers table and
  *             PaperTrace §2.5 state).
- *   idx_fmt   F32 or E4M3: indexer keys K^I and indexer queries q^I.
+ *   idx_fmt   F32, E4M3 or MXFP4: indexer keys K^I and indexer queries q^I.  MXFP4 is the
+ *             pages' later FP4 indexer path (reading notes §3.3-3.4: 1x32 sub-blocks with
+ *             their own scales) in the OCP MX v1.0 format: per block of 32 dims one E8M0
+ *             scale code (2^(code - 127)) and 32 E2M1 codes, two per byte (dim 2i in the low
+ *             nibble).  Per sequence, ki holds cap rows of c_I / 2 element bytes, then cap
+ *             rows of c_I / 32 scale codes; per query, q^I holds n_hI rows of c_I / 2 element
+ *             bytes, then n_hI rows of c_I / 32 scale codes.  Keys are encoded by the MX rule:
+ *             scale 2^(floor(log2 max|v|) - 2) (1 for an all-zero block), elements rounded to
+ *             nearest, ties to even, saturating at +-6.
  */
 typedef struct csa_dims {
   int32_t d, c, rope_dim, n_h, c_I, n_hI, m;

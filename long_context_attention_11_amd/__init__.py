@@ -19,11 +19,11 @@ __all__ = [
     "csa_abi_version", "csa_row_bytes", "csa_state_width", "csa_state_rows",
     "csa_workspace_size", "csa_compress", "csa_index_topk", "csa_attend", "csa_forward",
     "csa_index_scores", "csa_topk", "csa_topk_workspace_size", "OP_COMPRESS", "OP_INDEX_TOPK", "OP_ATTEND", "OP_FORWARD",
-    "FMT_F32", "FMT_BF16", "FMT_E4M3", "FMT_E4M3_BF16", "EXPORTED_SYMBOLS",
+    "FMT_F32", "FMT_BF16", "FMT_E4M3", "FMT_E4M3_BF16", "FMT_MXFP4", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-FMT_F32, FMT_BF16, FMT_E4M3, FMT_E4M3_BF16 = 0, 1, 2, 3
+FMT_F32, FMT_BF16, FMT_E4M3, FMT_E4M3_BF16, FMT_MXFP4 = 0, 1, 2, 3, 4
 OP_COMPRESS, OP_INDEX_TOPK, OP_ATTEND, OP_FORWARD = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = (
@@ -114,13 +114,13 @@ def _check(status: int):
 
 # ----------------------------------------------------------------------------- structures
 
-_FMT = {"f32": FMT_F32, "bf16": FMT_BF16, "e4m3": FMT_E4M3, "q": FMT_E4M3_BF16}
+_FMT = {"f32": FMT_F32, "bf16": FMT_BF16, "e4m3": FMT_E4M3, "q": FMT_E4M3_BF16, "mxfp4": FMT_MXFP4}
 
 
 @dataclass
 class Dims:
     """Layer shape and formats (mirrors csa_dims).  ``kv_fmt``: "f32" or "q" (E4M3 + bf16
-    RoPE dims); ``idx_fmt``: "f32" or "e4m3"; ``act``: "f32" or "bf16"."""
+    RoPE dims); ``idx_fmt``: "f32", "e4m3" or "mxfp4"; ``act``: "f32" or "bf16"."""
     d: int
     c: int
     rope_dim: int
@@ -204,7 +204,10 @@ class Cache:
         self.row_bytes = rb
         u8 = dict(dtype=torch.uint8, device=device)
         self.kv = torch.zeros((B, cap, rb), **u8)
-        if dims.dual:
+        if dims.dual and dims.idx_fmt == "mxfp4":
+            # per sequence: cap rows of c_I / 2 element bytes, then cap rows of c_I / 32 scales
+            self.ki = torch.zeros((B, cap * (dims.c_I // 2 + dims.c_I // 32)), **u8)
+        elif dims.dual:
             kib = dims.c_I * (4 if dims.idx_fmt == "f32" else 1)
             self.ki = torch.zeros((B, cap, kib), **u8)
         else:
@@ -214,6 +217,18 @@ class Cache:
         self.win_pos = torch.full((B, win_cap), -1, dtype=torch.int32, device=device)
         self.state = torch.zeros((B, csa_state_rows(dims), csa_state_width(dims)),
                                  dtype=torch.float32, device=device)
+
+    @property
+    def ki_codes(self):
+        """MXFP4 keys: the element bytes, a [B][cap][c_I / 2] view of ki."""
+        n = self.cap * (self.dims.c_I // 2)
+        return self.ki[:, :n].view(self.B, self.cap, self.dims.c_I // 2)
+
+    @property
+    def ki_scales(self):
+        """MXFP4 keys: the block scale codes, a [B][cap][c_I / 32] view of ki."""
+        n = self.cap * (self.dims.c_I // 2)
+        return self.ki[:, n:].view(self.B, self.cap, self.dims.c_I // 32)
 
     def reset(self):
         self.n_entries.zero_()

@@ -49,16 +49,16 @@ int check_dims(const csa_dims* d) {
   const bool f32 = d->act_fmt == CSA_FMT_F32 && d->kv_fmt == CSA_FMT_F32 &&
                    (!d->dual || d->idx_fmt == CSA_FMT_F32);
   const bool q = d->act_fmt == CSA_FMT_BF16 && d->kv_fmt == CSA_FMT_E4M3_BF16 &&
-                 (!d->dual || d->idx_fmt == CSA_FMT_E4M3);
+                 (!d->dual || d->idx_fmt == CSA_FMT_E4M3 || d->idx_fmt == CSA_FMT_MXFP4);
   if (!f32 && !q)
     return fail(CSA_ERR_UNSUPPORTED,
-                "supported formats: all F32, or act BF16 + kv E4M3_BF16 + idx E4M3");
+                "supported formats: all F32, or act BF16 + kv E4M3_BF16 + idx E4M3 or MXFP4");
   if (q) {
     if (d->c != 512 || d->rope_dim != 64)
       return fail(CSA_ERR_UNSUPPORTED, "E4M3_BF16 rows are built for c = 512, rope_dim = 64");
     if (d->n_h % 16) return fail(CSA_ERR_UNSUPPORTED, "n_h must be a multiple of 16");
     if (d->dual && (d->c_I != 128 || (d->n_hI != 16 && d->n_hI != 32 && d->n_hI != 64)))
-      return fail(CSA_ERR_UNSUPPORTED, "E4M3 indexer is built for c_I = 128, n_hI in {16, 32, 64}");
+      return fail(CSA_ERR_UNSUPPORTED, "the quantized indexer is built for c_I = 128, n_hI in {16, 32, 64}");
     if (d->d % 64) return fail(CSA_ERR_UNSUPPORTED, "bf16 projection needs d % 64 == 0");
   }
   return CSA_OK;
@@ -432,7 +432,8 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
   }
   if (d.dual) {
     const bool tiled = T % 16 == 0 && Qc % 16 == 0;
-    const size_t qI_row = (size_t)d.n_hI * d.c_I * (d.idx_fmt == CSA_FMT_F32 ? 4 : 1);
+    const size_t qI_row = d.idx_fmt == CSA_FMT_MXFP4 ? (size_t)d.n_hI * (d.c_I / 2 + d.c_I / 32)
+                                                      : (size_t)d.n_hI * d.c_I * (d.idx_fmt == CSA_FMT_F32 ? 4 : 1);
     const size_t w_row = (size_t)d.n_hI * (d.act_fmt == CSA_FMT_F32 ? 4 : 2);
     for (int32_t q0 = 0; q0 < Qn; q0 += Qc) {
       const int32_t n = std::min(Qc, Qn - q0);

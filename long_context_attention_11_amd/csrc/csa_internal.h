@@ -83,6 +83,15 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
   return bf16_bits_to_f32(lo & 0xffffu);
 }
 
+// FP4 E2M1 code of x (already divided by its block scale): nearest of 0, 0.5, 1, 1.5, 2, 3, 4,
+// 6 with ties to the even code, saturating at 6; the sign is kept (code 8 is -0).
+__device__ __forceinline__ uint32_t e2m1_code(float x) {
+  const float a = fabsf(x);
+  const uint32_t mag = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                       (a >= 3.5f) + (a > 5.0f);
+  return (signbit(x) ? 8u : 0u) | mag;
+}
+
 // Order-preserving map of a float score to uint32 (larger score -> larger key); -0 -> +0.
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);

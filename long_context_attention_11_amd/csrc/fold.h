@@ -34,6 +34,9 @@ struct FoldArgs {
   int32_t* n_entries;
 };
 
+// Maximum of the bit patterns of non-negative floats (ordered as the floats are).
+struct MaxBits { __device__ int operator()(int a, int b) const { return max(a, b); } };
+
 // Projection value of token j (global position) in column col of sequence b.
 // PART (one-token steps, a.part set): earlier tokens come from the state ring and the new
 // token from its partial sums, added in slice order.  Otherwise tokens of the chunk come from
@@ -191,6 +194,20 @@ __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, f
       float* kd = reinterpret_cast<float*>(a.ki) + ((size_t)b * a.cap + i) * a.cI;
       kd[u] = k0;
       kd[u + 1] = k1;
+    } else if (a.idx_fmt == CSA_FMT_MXFP4) {
+      // a block of 32 dims is the 16 threads of one DPP row: its largest magnitude sets the
+      // scale, then each thread encodes its two elements into one byte
+      const float amax = __int_as_float(row_allreduce(__float_as_int(fmaxf(fabsf(k0), fabsf(k1))), MaxBits()));
+      int e = 0;
+      if (amax > 0.f) {
+        int ex;
+        frexpf(amax, &ex);   // amax = f 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
+        e = min(127, max(-127, ex - 1 - 2));
+      }
+      const size_t krow = (size_t)a.cI / 2 + a.cI / 32;
+      uint8_t* kseq = a.ki + (size_t)b * a.cap * krow;
+      kseq[(size_t)i * (a.cI / 2) + t] = (uint8_t)(e2m1_code(ldexpf(k0, -e)) | (e2m1_code(ldexpf(k1, -e)) << 4));
+      if ((t & 15) == 0) kseq[(size_t)a.cap * (a.cI / 2) + (size_t)i * (a.cI / 32) + (t >> 4)] = (uint8_t)(e + 127);
     } else {
       uint8_t* kd = a.ki + ((size_t)b * a.cap + i) * a.cI;
       *reinterpret_cast<uint16_t*>(kd + u) = (uint16_t)(f32_to_e4m3(k0) | (f32_to_e4m3(k1) << 8));

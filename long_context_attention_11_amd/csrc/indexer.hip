@@ -28,6 +28,33 @@ __device__ __forceinline__ void e4m3x32_to_ops(const uint4& lo, const uint4& hi,
   }
 }
 
+// 32 MXFP4 elements (16 bytes, element 2i in the low nibble of byte i) with their E8M0 scale
+// code into four bf16x8 MFMA operands, exactly: the conversion multiplies each E2M1 value by
+// the power of two 2^(scale - 127).
+__device__ __forceinline__ void mxfp4x32_to_ops(const uint4& codes, uint32_t scale, bf16x8 op[4]) {
+  const float sc = scale ? __uint_as_float(scale << 23) : __uint_as_float(0x00400000u);  // 2^-127
+  const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint4 v = make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[ks], sc, 0)),
+                               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[ks], sc, 1)),
+                               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[ks], sc, 2)),
+                               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[ks], sc, 3)));
+    op[ks] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+// A lane's 32 dims of one key or query row, as loaded: E4M3 codes (32 bytes), or MXFP4
+// element bytes (16) and the block's scale code.
+template <bool FP4>
+struct RawOp {
+  uint4 a, b;
+  __device__ void to_ops(bf16x8 op[4]) const {
+    if constexpr (FP4) mxfp4x32_to_ops(a, b.x, op);
+    else e4m3x32_to_ops(a, b, op);
+  }
+};
+
 // One workgroup = 4 waves; blockIdx.x = group of QPW queries (same sequence), blockIdx.y =
 // entry chunk; wave w scans its quarter of the chunk in tiles of 16 entries.
 // MFMA mapping (16x16x32 bf16): A = q^I rows (heads), B = K^I rows (entries), contraction
@@ -50,7 +77,10 @@ struct IndexerArgs {
 };
 
 // Workgroup (bx, by): queries bx * QPW .. +QPW-1 against entry chunk by.
-template <int NH, int QPW>
+// FP4: keys and queries in MXFP4.  A sequence's keys are cap rows of 64 element bytes, then
+// cap rows of 4 scale codes; a query's q^I is NH rows of 64 element bytes, then NH rows of 4
+// scale codes.  Lane group g reads block g of a row: 16 element bytes and one scale code.
+template <int NH, int QPW, bool FP4>
 __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx, int by) {
   const uint8_t* __restrict__ qI = ia.qI;
   const uint16_t* __restrict__ wI = ia.wI;
@@ -84,33 +114,46 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
   if (w_lo >= c_hi) return;
   const int stride = 64;  // 4 waves x 16 entries
 
-  const uint8_t* kbase = ki + (size_t)seq * cap * IX_CI + g * 32;
+  constexpr int KROW = FP4 ? IX_CI / 2 + IX_CI / 32 : IX_CI;   // bytes per key or q^I row
+  const uint8_t* kseq = ki + (size_t)seq * cap * KROW;
   // Prologue: the query operands (q^I rows, head weights) and the first DEPTH tiles of keys
   // are all requested before anything waits, so their latencies overlap.  The ring holds
   // DEPTH tiles (16 entries x 128 B per wave, 32 B per lane); waits count outstanding loads
   // in issue order, so tile 0 is issued first among the keys.
-  uint4 araw[QPW][HT][2];
+  RawOp<FP4> araw[QPW][HT];
   uint2 wraw[QPW][HT];
 #pragma unroll
   for (int qq = 0; qq < QPW; ++qq) {
     const int q = min(q0 + qq, Q - 1);
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      const uint8_t* src = qI + ((size_t)q * NH + ht * 16 + col) * IX_CI + g * 32;
-      araw[qq][ht][0] = *reinterpret_cast<const uint4*>(src);
-      araw[qq][ht][1] = *reinterpret_cast<const uint4*>(src + 16);
+      const int h = ht * 16 + col;
+      if constexpr (FP4) {
+        const uint8_t* qrow = qI + (size_t)q * NH * KROW;
+        araw[qq][ht].a = *reinterpret_cast<const uint4*>(qrow + h * (IX_CI / 2) + g * 16);
+        araw[qq][ht].b.x = qrow[NH * (IX_CI / 2) + h * (IX_CI / 32) + g];
+      } else {
+        const uint8_t* src = qI + ((size_t)q * NH + h) * IX_CI + g * 32;
+        araw[qq][ht].a = *reinterpret_cast<const uint4*>(src);
+        araw[qq][ht].b = *reinterpret_cast<const uint4*>(src + 16);
+      }
       wraw[qq][ht] = *reinterpret_cast<const uint2*>(wI + (size_t)q * NH + ht * 16 + 4 * g);
     }
   }
-  uint4 rlo[DEPTH], rhi[DEPTH];
-  auto load_tile = [&](int s0, uint4& lo, uint4& hi) {
+  RawOp<FP4> rk[DEPTH];
+  auto load_tile = [&](int s0, RawOp<FP4>& r) {
     const int s = min(s0 + col, c_hi - 1);
-    const uint8_t* src = kbase + (size_t)s * IX_CI;
-    lo = *reinterpret_cast<const uint4*>(src);
-    hi = *reinterpret_cast<const uint4*>(src + 16);
+    if constexpr (FP4) {
+      r.a = *reinterpret_cast<const uint4*>(kseq + (size_t)s * (IX_CI / 2) + g * 16);
+      r.b.x = kseq[(size_t)cap * (IX_CI / 2) + (size_t)s * (IX_CI / 32) + g];
+    } else {
+      const uint8_t* src = kseq + (size_t)s * IX_CI + g * 32;
+      r.a = *reinterpret_cast<const uint4*>(src);
+      r.b = *reinterpret_cast<const uint4*>(src + 16);
+    }
   };
 #pragma unroll
-  for (int i = 0; i < DEPTH; ++i) load_tile(w_lo + stride * i, rlo[i], rhi[i]);
+  for (int i = 0; i < DEPTH; ++i) load_tile(w_lo + stride * i, rk[i]);
   __builtin_amdgcn_sched_barrier(0);
 
   bf16x8 A[QPW][HT][4];
@@ -119,7 +162,7 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
   for (int qq = 0; qq < QPW; ++qq) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      e4m3x32_to_ops(araw[qq][ht][0], araw[qq][ht][1], A[qq][ht]);
+      araw[qq][ht].to_ops(A[qq][ht]);
       const uint2 w4 = wraw[qq][ht];
       W[qq][ht][0] = bf16_bits_to_f32(w4.x & 0xffffu);
       W[qq][ht][1] = bf16_bits_to_f32(w4.x >> 16);
@@ -140,8 +183,8 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
       const int s0 = base + stride * i;
       // widen the tile first, then reuse its registers for the load of the next round
       bf16x8 Bop[4];
-      e4m3x32_to_ops(rlo[i], rhi[i], Bop);
-      load_tile(s0 + stride * DEPTH, rlo[i], rhi[i]);
+      rk[i].to_ops(Bop);
+      load_tile(s0 + stride * DEPTH, rk[i]);
 #pragma unroll
       for (int qq = 0; qq < QPW; ++qq) {
         float part = 0.f;
@@ -164,9 +207,9 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
   } while (++it < rounds);
 }
 
-template <int NH, int QPW>
+template <int NH, int QPW, bool FP4>
 __global__ __launch_bounds__(256) void k_indexer_bf16(IndexerArgs ia) {
-  indexer_bf16_body<NH, QPW>(ia, blockIdx.x, blockIdx.y);
+  indexer_bf16_body<NH, QPW, FP4>(ia, blockIdx.x, blockIdx.y);
 }
 
 // Prefill-shaped indexer: a workgroup of 8 waves scores IT_Q = 16 queries of ONE sequence
@@ -382,12 +425,17 @@ hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI,
   const IndexerArgs ia{(const uint8_t*)qI, (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki,
                        c.cap, c.n_entries, d.m, scores, ld, chunk};
   dim3 grid(Q, nchunk);
+  const bool fp4 = d.idx_fmt == CSA_FMT_MXFP4;
+#define IX_LAUNCH(NHV)                                                                          \
+  if (fp4) hipLaunchKernelGGL((k_indexer_bf16<NHV, 1, true>), grid, dim3(256), 0, s, ia);         \
+  else hipLaunchKernelGGL((k_indexer_bf16<NHV, 1, false>), grid, dim3(256), 0, s, ia)
   switch (d.n_hI) {
-    case 64: hipLaunchKernelGGL((k_indexer_bf16<64, 1>), grid, dim3(256), 0, s, ia); break;
-    case 32: hipLaunchKernelGGL((k_indexer_bf16<32, 1>), grid, dim3(256), 0, s, ia); break;
-    case 16: hipLaunchKernelGGL((k_indexer_bf16<16, 1>), grid, dim3(256), 0, s, ia); break;
+    case 64: IX_LAUNCH(64); break;
+    case 32: IX_LAUNCH(32); break;
+    case 16: IX_LAUNCH(16); break;
     default: return hipErrorInvalidValue;
   }
+#undef IX_LAUNCH
   return hipGetLastError();
 }
 

@@ -250,7 +250,7 @@ __device__ int select_topk(const Items& it, int k, TopkShared& sh, int* out_idx,
   if (lane == 63) sh.scan[w] = x;
   __syncthreads();
   // waves ahead of this one
-  const int before = row_allreduce((threadIdx.x & 15) < w ? sh.scan[threadIdx.x & 15] : 0, OpAdd());
+  const int before = row_allreduce((tid & 15) < w ? sh.scan[tid & 15] : 0, OpAdd());
   const int ex = x - own + before;
   int gt_before = ex >> 16, eq_before = ex & 0xffff;
 #pragma unroll

@@ -28,7 +28,7 @@ import math
 
 import torch
 
-__all__ = ["CONFIGS", "config", "generator", "randn", "weights", "hidden", "queries",
+__all__ = ["CONFIGS", "config", "generator", "randn", "mxfp4_random", "weights", "hidden", "queries",
            "synthetic_cache", "row_bytes", "SEED"]
 
 SEED = 0
@@ -86,6 +86,16 @@ def randn(shape, std, device, *ids) -> torch.Tensor:
     """float32 N(0, std^2) drawn from a generator seeded by ``ids``."""
     g = generator(device, *ids)
     return torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
+
+
+def mxfp4_random(rows: int, n: int, device, *ids):
+    """Random MXFP4 rows (n elements each): uniformly drawn element bytes [rows][n / 2] (two
+    E2M1 codes each) and block scale codes [rows][n / 32] in 124 .. 127 (2^-3 .. 1).  Drawn
+    directly as codes, so both sides decode the same bytes and no encoding is involved."""
+    g = generator(device, *ids)
+    codes = torch.randint(0, 256, (rows, n // 2), generator=g, device=device, dtype=torch.int32)
+    scales = torch.randint(124, 128, (rows, n // 32), generator=g, device=device, dtype=torch.int32)
+    return codes.to(torch.uint8), scales.to(torch.uint8)
 
 
 def _store(x: torch.Tensor, kind: str) -> torch.Tensor:
@@ -147,11 +157,17 @@ def hidden(cfg: dict, seq: int, t0: int, t1: int, seed: int = SEED, device="cpu"
 
 def queries(cfg: dict, Q: int, seed: int = SEED, device="cpu", tag="q") -> dict:
     """Per-query inputs: q [Q][n_h][c] (activation type), qI [Q][n_hI][c_I] (index format),
-    w [Q][n_hI] (activation type).  All N(0,1)."""
+    w [Q][n_hI] (activation type).  All N(0,1), except MXFP4 q^I: random codes
+    (mxfp4_random), laid out per query as element bytes then scale codes."""
     out = {"q": _store(randn((Q, cfg["n_h"], cfg["c"]), 1.0, device, seed, tag, "q"), cfg["act"])}
-    if cfg["dual"]:
+    if cfg["dual"] and cfg["idx_fmt"] == "mxfp4":
+        # per query: n_hI rows of element bytes, then n_hI rows of scale codes
+        codes, scales = mxfp4_random(Q * cfg["n_hI"], cfg["c_I"], device, seed, tag, "qI4")
+        out["qI"] = torch.cat([codes.view(Q, -1), scales.view(Q, -1)], dim=1).contiguous()
+    elif cfg["dual"]:
         out["qI"] = _store(randn((Q, cfg["n_hI"], cfg["c_I"]), 1.0, device, seed, tag, "qI"),
                            cfg["idx_fmt"])
+    if cfg["dual"]:
         out["w"] = _store(randn((Q, cfg["n_hI"]), 1.0, device, seed, tag, "w"), cfg["act"])
     return out
 
@@ -174,6 +190,10 @@ def synthetic_cache(cfg: dict, B: int, N: int, R: int, seed: int = SEED, device=
         return torch.cat([nope, rope], dim=-1).contiguous()
 
     out = {"kv": rows(N, "ckv"), "win": rows(R, "cwin")}
-    if cfg["dual"]:
+    if cfg["dual"] and cfg["idx_fmt"] == "mxfp4":
+        # per sequence: N rows of element bytes, then N rows of scale codes
+        codes, scales = mxfp4_random(B * N, cfg["c_I"], device, seed, "cki4")
+        out["ki"] = torch.cat([codes.view(B, -1), scales.view(B, -1)], dim=1).contiguous()
+    elif cfg["dual"]:
         out["ki"] = _store(randn((B, N, cfg["c_I"]), 0.5, device, seed, "cki"), cfg["idx_fmt"])
     return out

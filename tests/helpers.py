@@ -79,9 +79,22 @@ def decode_keys(k: torch.Tensor, cfg: dict) -> np.ndarray:
     return codecs.e4m3_decode(a)
 
 
+def keys_of(cache, b: int, lo: int, hi: int, cfg: dict) -> np.ndarray:
+    """Stored indexer keys lo .. hi - 1 of sequence b, decoded by the oracle's codecs."""
+    if cfg["idx_fmt"] == "mxfp4":
+        return codecs.mxfp4_decode(cache.ki_codes[b, lo:hi].cpu().numpy(), cache.ki_scales[b, lo:hi].cpu().numpy())
+    return decode_keys(cache.ki[b, lo:hi], cfg)
+
+
 def qI_host(qI: torch.Tensor, cfg: dict) -> np.ndarray:
     if cfg["idx_fmt"] == "f32":
         return host64(qI)
+    if cfg["idx_fmt"] == "mxfp4":
+        a = qI.cpu().numpy()
+        Q, nh, cI = a.shape[0], cfg["n_hI"], cfg["c_I"]
+        codes = a[:, : nh * cI // 2].reshape(Q, nh, cI // 2)
+        scales = a[:, nh * cI // 2:].reshape(Q, nh, cI // 32)
+        return codecs.mxfp4_decode(codes, scales)
     return codecs.e4m3_decode(qI.cpu().numpy())
 
 
@@ -119,6 +132,34 @@ def assert_close_f32(got: np.ndarray, ref: np.ndarray, what: str = ""):
     mx = np.abs(got - ref).max()
     assert mx <= F32_MAX_ABS, f"{what}: max abs {mx:.3g}"
     return mx
+
+
+def check_stored_mxfp4(codes: np.ndarray, scales: np.ndarray, ref_pre: np.ndarray, what: str = "",
+                       rel: float = 2.0 ** -16):
+    """Stored MXFP4 keys (element bytes [rows][n/2], scale codes [rows][n/32]) vs the oracle's
+    pre-storage float64 keys [rows][n], with the tolerance of check_stored_codes: each block's
+    scale must be the one the MX rule gives for a block maximum within eps of the oracle's,
+    and each element, under the stored scale, the rounding of a value within eps of the
+    oracle's.  Returns how many elements differ from the oracle's own encoding."""
+    x = np.asarray(ref_pre, np.float64)
+    rms = np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) * np.ones_like(x)
+    eps = rel * np.maximum(np.abs(x), rms)
+    e_got = scales.astype(np.int64) - 127
+    blk = lambda a: a.reshape(a.shape[:-1] + (a.shape[-1] // 32, 32))
+    amax, emax = np.abs(blk(x)).max(-1), blk(eps).max(-1)
+    e_lo = codecs.mxfp4_scale_exponent(np.repeat(np.maximum(amax - emax, 0.0), 32, -1))
+    e_hi = codecs.mxfp4_scale_exponent(np.repeat(amax + emax, 32, -1))
+    ok_s = (e_got >= e_lo) & (e_got <= e_hi)
+    assert ok_s.all(), f"{what}: {int((~ok_s).sum())} block scales off the MX rule; got {e_got[~ok_s][:4]}, want {e_lo[~ok_s][:4]}"
+    e_el = np.repeat(e_got, 32, -1)
+    got = codecs.mxfp4_decode(codes, scales)
+    rnd = lambda v: codecs.e2m1_decode(codecs.e2m1_encode_scaled(v, e_el)) * np.ldexp(1.0, e_el)
+    lo, hi = rnd(x - eps), rnd(x + eps)
+    ok = (got >= lo) & (got <= hi)
+    assert ok.all(), (f"{what}: {int((~ok).sum())} stored elements outside the rounding of the oracle's "
+                      f"value +- eps; first: got {got[~ok][:3]}, pre {x[~ok][:3]}")
+    c_ref, s_ref = codecs.mxfp4_encode(x)
+    return int((codecs.mxfp4_decode(codecs.mxfp4_pack(c_ref), s_ref) != got).sum())
 
 
 def check_stored_codes(got_vals: np.ndarray, ref_pre: np.ndarray, fmt: str, what: str = "",

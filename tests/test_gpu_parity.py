@@ -13,7 +13,7 @@ import long_context_attention_11_amd as L
 import synth
 from helpers import (assert_close_f32, assert_close_q, check_stored_codes, check_topk,
                      decode_keys, decode_rows, host64, lib_weights, oracle_dims, oracle_weights,
-                     qI_host)
+                     keys_of, qI_host, check_stored_mxfp4)
 from oracle import codecs
 from oracle import csa_ref as R
 
@@ -54,11 +54,13 @@ def _check_cache_vs_oracle(cfg, cache, b, comp, n_tokens, what):
         flips += check_stored_codes(got[:, : c - r], comp["entry_fin"][:, : c - r], "e4m3", what + " entries/nope")
         flips += check_stored_codes(got[:, c - r:], comp["entry_fin"][:, c - r:], "bf16", what + " entries/rope")
     if cfg["dual"]:
-        gk = decode_keys(cache.ki[b, :nb], cfg)
-        if cfg["idx_fmt"] == "f32":
-            assert_close_f32(gk, comp["ki_pre"], what + " index keys")
+        if cfg["idx_fmt"] == "mxfp4":
+            flips += check_stored_mxfp4(cache.ki_codes[b, :nb].cpu().numpy(), cache.ki_scales[b, :nb].cpu().numpy(),
+                                        comp["ki_pre"], what + " index keys")
+        elif cfg["idx_fmt"] == "f32":
+            assert_close_f32(keys_of(cache, b, 0, nb, cfg), comp["ki_pre"], what + " index keys")
         else:
-            flips += check_stored_codes(gk, comp["ki_pre"], "e4m3", what + " index keys")
+            flips += check_stored_codes(keys_of(cache, b, 0, nb, cfg), comp["ki_pre"], "e4m3", what + " index keys")
     # window ring: the last min(win_cap, n) tokens
     wp = cache.win_pos[b].cpu().numpy()
     for j in range(max(0, n_tokens - cache.win_cap), n_tokens):
@@ -136,10 +138,12 @@ def _qcfg(**over):
     return synth.config("c2", **over)
 
 
-def test_q_compress_chunked_matches_oracle():
-    """E4M3/bf16 storage, Flash dims (d=4096, c=512, c_I=128): 2 sequences x 301 tokens in
-    ragged chunks; stored codes match the oracle up to midpoint flips."""
-    cfg = _qcfg()
+@pytest.mark.parametrize("idx_fmt", ["e4m3", "mxfp4"])
+def test_q_compress_chunked_matches_oracle(idx_fmt):
+    """E4M3/bf16 storage, Flash dims (d=4096, c=512, c_I=128), indexer keys in E4M3 or MXFP4:
+    2 sequences x 301 tokens in ragged chunks; stored codes match the oracle up to midpoint
+    flips."""
+    cfg = _qcfg(idx_fmt=idx_fmt)
     dims = L.Dims.from_config(cfg)
     od = oracle_dims(cfg)
     B, n = 2, 301
@@ -155,12 +159,13 @@ def test_q_compress_chunked_matches_oracle():
     assert flips < 50
 
 
-def test_q_compress_single_token_steps():
+@pytest.mark.parametrize("idx_fmt", ["e4m3", "mxfp4"])
+def test_q_compress_single_token_steps(idx_fmt):
     """Decode-style compression: 17 sequences (two 16-row projection tiles, the second
     ragged) get a 3-token prefix and then 20 one-token steps, which take the step path
     (projection straight into the state ring, fold from the ring).  Every stored entry,
     indexer key and window row matches the oracle up to midpoint flips."""
-    cfg = _qcfg()
+    cfg = _qcfg(idx_fmt=idx_fmt)
     dims = L.Dims.from_config(cfg)
     od = oracle_dims(cfg)
     B, n = 17, 23
@@ -221,7 +226,7 @@ def _synthetic_decode_setup(cfg, B, N, R_win, taus, seed=11, sink=True, n_entrie
 
 def _oracle_cache(cfg, cache, b):
     entries = decode_rows(cache.kv[b].cpu().numpy(), cfg)
-    ki = decode_keys(cache.ki[b], cfg) if cfg["dual"] else None
+    ki = keys_of(cache, b, 0, cache.cap, cfg) if cfg["dual"] else None
     win = decode_rows(cache.win[b].cpu().numpy(), cfg)
     wp = cache.win_pos[b].cpu().numpy()
 
@@ -277,10 +282,12 @@ def _run_index_attend_and_check(cfg, dims, cache, qs, W, q_seq, q_pos, taus, che
     return stats
 
 
-def test_q_index_topk_attend_small():
+@pytest.mark.parametrize("idx_fmt", ["e4m3", "mxfp4"])
+def test_q_index_topk_attend_small(idx_fmt):
     """Flash dims on a synthetic cache of 5003 entries (ragged tile tail): queries whose
-    visible range is empty, below k, not a multiple of 16, and full; windows clipped at 0."""
-    cfg = _qcfg()
+    visible range is empty, below k, not a multiple of 16, and full; windows clipped at 0.
+    Indexer keys and queries in E4M3 or MXFP4."""
+    cfg = _qcfg(idx_fmt=idx_fmt)
     N = 5003
     tt = [3, 4, 130, 2051, 4 * 700 + 3, 4 * 5003, 4 * 5003 + 77, 4 * 3333 + 1, 9000 * 4]
     taus = list(enumerate(tt))
@@ -337,7 +344,7 @@ def test_q_forward_end_to_end():
         comp = R.compress_sequence(host64(Hs[b]), OW, od)
         _check_cache_vs_oracle(cfg, cache, b, comp, n0 + T, f"e2e seq {b}")
         g_entries = decode_rows(cache.kv[b].cpu().numpy(), cfg)
-        g_ki = decode_keys(cache.ki[b], cfg)
+        g_ki = keys_of(cache, b, 0, cache.cap, cfg)
         nb = (n0 + T) // cfg["m"]
         for t in range(T):
             i = b * T + t
@@ -360,12 +367,13 @@ def test_q_forward_end_to_end():
             assert_close_q(go[i], o_ref, f"e2e out seq {b} tau={tau}")
 
 
-def test_q_forward_decode_steps():
+@pytest.mark.parametrize("idx_fmt", ["e4m3", "mxfp4"])
+def test_q_forward_decode_steps(idx_fmt):
     """Nine one-token forward steps (tau = 600 .. 608, two of them completing an entry) on a
     cache whose capacity spans two top-k segments: the path that scores before compressing
     and runs the projection step inside the top-k threshold launch.  Outputs, selections and
     the cache afterwards are checked against the oracle as in the chunked test."""
-    cfg = _qcfg()
+    cfg = _qcfg(idx_fmt=idx_fmt)
     dims = L.Dims.from_config(cfg)
     od = oracle_dims(cfg)
     B, n0, steps = 2, 600, 9
@@ -395,7 +403,7 @@ def test_q_forward_decode_steps():
         comp = R.compress_sequence(host64(Hs[b]), OW, od)
         _check_cache_vs_oracle(cfg, cache, b, comp, n0 + steps, f"decode steps seq {b}")
         g_entries = decode_rows(cache.kv[b].cpu().numpy(), cfg)
-        g_ki = decode_keys(cache.ki[b], cfg)
+        g_ki = keys_of(cache, b, 0, cache.cap, cfg)
         nb = (n0 + steps) // cfg["m"]
         for t in range(steps):
             i = b * steps + t
@@ -440,10 +448,10 @@ def test_deterministic_repeat():
 # ----------------------------------------------------------------------------- full sizes
 
 
-def _decode_full(name, B=None, check_scores_for=2):
+def _decode_full(name, B=None, check_scores_for=2, **over):
     """A decode step of a full-size configuration on a synthetic cache: every query's
     selection (under the tie rule) and output are checked against the oracle."""
-    cfg = synth.config(name)
+    cfg = synth.config(name, **over)
     B = B or cfg["B"]
     N = cfg["prefix"] // cfg["m"]
     tau = cfg["prefix"]
@@ -457,6 +465,11 @@ def _decode_full(name, B=None, check_scores_for=2):
 def test_c2_decode_full_size():
     """Flash decode, 16 sequences x 32768 entries, k=512: the bench's kernels and grid."""
     _decode_full("c2")
+
+
+def test_c2_decode_full_size_mxfp4():
+    """The same with the indexer's keys and queries in MXFP4."""
+    _decode_full("c2", idx_fmt="mxfp4")
 
 
 def test_c3_decode_full_size():
@@ -495,7 +508,7 @@ def test_c4_prefill_full_size_sampled():
     idx = torch.zeros((T, k), dtype=torch.int32, device=DEV)
     # inputs both sides see: prefix entries, keys and ring rows (before the chunk overwrites)
     prefix_entries = decode_rows(cache.kv[0, :N0].cpu().numpy(), cfg)
-    prefix_ki = decode_keys(cache.ki[0, :N0], cfg)
+    prefix_ki = keys_of(cache, 0, 0, N0, cfg)
     ring = decode_rows(cache.win[0].cpu().numpy(), cfg)
     ring_pos = cache.win_pos[0].cpu().numpy()
     ws = _ws(L.csa_workspace_size(dims, L.OP_FORWARD, B=1, T=T, cap=cap, q_chunk=4096))
@@ -522,7 +535,7 @@ def test_c4_prefill_full_size_sampled():
     c, r = cfg["c"], cfg["rope_dim"]
     check_stored_codes(g_new[:, :c - r], fin[:, :c - r], "e4m3", "c4 new entries/nope")
     check_stored_codes(g_new[:, c - r:], fin[:, c - r:], "bf16", "c4 new entries/rope")
-    g_ki_new = decode_keys(cache.ki[0, N0:cap], cfg)
+    g_ki_new = keys_of(cache, 0, N0, cap, cfg)
     check_stored_codes(g_ki_new, kpre, "e4m3", "c4 new keys")
     entries = np.concatenate([prefix_entries, ent_new])
     ki = np.concatenate([prefix_ki, ki_new])
