@@ -75,7 +75,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4a", "c4b", "c5"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2fp4", "c3", "c4a", "c4b", "c5"])
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -374,7 +374,8 @@ def run_decode(args, cfg):
         "data": "synthetic (seeded N(0,1) hidden states and queries, N(0,1/fan_in) weights)",
     }
     if dual:
-        bytes_per_query = N * cfg["c_I"] + cfg["n_hI"] * cfg["c_I"] + 2 * cfg["n_hI"]
+        key_bytes = cfg["c_I"] // 2 + cfg["c_I"] // 32 if cfg["idx_fmt"] == "mxfp4" else cfg["c_I"]
+        bytes_per_query = N * key_bytes + cfg["n_hI"] * key_bytes + 2 * cfg["n_hI"]
         alg = B * bytes_per_query
         dur = kt["index_scores"] * 1e-6
         res["roofline"] = {"bound": "hbm", "kernel": "indexer (k_indexer_bf16)",
@@ -395,6 +396,8 @@ def run_decode(args, cfg):
     res["cache_build_s"] = round(t_build, 2)
     desc = {"c2": "Flash-shaped CSA decode, 16 seqs x 131072-token context (32768 entries), d=4096, "
                   "64 heads x 512, indexer 64x128, top-k 512, n_win 128, one new token per sequence per step",
+            "c2fp4": "Flash-shaped CSA decode as c2, with the indexer's keys and queries in MXFP4 "
+                     "(the pages' FP4 indexer path)",
             "c3": "Pro-shaped CSA decode, 4 seqs x 1048576-token context (262144 entries), d=7168, "
                   "128 heads x 512, indexer 64x128, top-k 1024, n_win 128",
             "c5": "HCA decode, 8 seqs x 1048576-token context (8192 entries, m'=128), d=4096, "
@@ -486,7 +489,7 @@ def main():
     import synth
     torch.cuda.set_device(0)
     cfg = synth.config(args.config)
-    if args.config in ("c2", "c3", "c5"):
+    if args.config in ("c2", "c2fp4", "c3", "c5"):
         res, ok = run_decode(args, cfg)
     else:
         res, ok = run_prefill(args, cfg)

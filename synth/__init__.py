@@ -42,6 +42,10 @@ CONFIGS = {
     "c2": dict(name="c2", B=16, prefix=131072, T=1, d=4096, c=512, rope_dim=64, n_h=64, c_I=128,
                n_hI=64, m=4, dual=True, top_k=512, n_win=128, kv_fmt="q", idx_fmt="e4m3",
                act="bf16", sink=True, **_BASE),
+    # c2 with the indexer's QK path in MXFP4 (the pages' later FP4 indexer revision)
+    "c2fp4": dict(name="c2fp4", B=16, prefix=131072, T=1, d=4096, c=512, rope_dim=64, n_h=64,
+                  c_I=128, n_hI=64, m=4, dual=True, top_k=512, n_win=128, kv_fmt="q",
+                  idx_fmt="mxfp4", act="bf16", sink=True, **_BASE),
     "c3": dict(name="c3", B=4, prefix=1048576, T=1, d=7168, c=512, rope_dim=64, n_h=128, c_I=128,
                n_hI=64, m=4, dual=True, top_k=1024, n_win=128, kv_fmt="q", idx_fmt="e4m3",
                act="bf16", sink=True, **_BASE),
