@@ -36,6 +36,7 @@ __all__ = [
     "e4m3_encode",
     "bf16_encode",
     "bf16_decode",
+    "bf16_round_nearest",
     "to_f32",
     "E2M1_MAX",
     "e2m1_values",
@@ -125,6 +126,16 @@ def bf16_encode(x) -> np.ndarray:
     nan = np.isnan(f)
     qnan = (((u >> 16) & 0x8000) | 0x7FC0).astype(np.uint16)
     return np.where(nan, qnan, r).astype(np.uint16)
+
+
+def bf16_round_nearest(x) -> np.ndarray:
+    """float64 values -> the nearest bfloat16 values (ties to even), rounded once from the
+    float64 value itself (no float32 step, so no double rounding): with x = f 2^e, f in
+    [0.5, 1), the 8 significant bits are rint(f 2^8) 2^(e - 8).  Used for the MXFP4
+    indexer's BF16 scores, whose kernel rounds from an exact float64 sum."""
+    x = np.asarray(x, np.float64)
+    f, e = np.frexp(x)
+    return np.ldexp(np.rint(np.ldexp(f, 8)), e - 8)
 
 
 def bf16_decode(bits) -> np.ndarray:

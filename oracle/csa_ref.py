@@ -377,6 +377,15 @@ def index_scores(qI, w, KI):
     return np.maximum(dots, 0.0) @ np.asarray(w, np.float64)
 
 
+def stored_scores(scores, dims: Dims):
+    """The scores top-k selects from: as computed, or with an MXFP4 QK path the pages' BF16
+    index scores (reading notes §3.4: scores drop from FP32 to BF16 with the FP4 indexer),
+    rounded to nearest even from the exact value."""
+    if dims.idx_fmt == "mxfp4":
+        return codecs.bf16_round_nearest(scores)
+    return np.asarray(scores, np.float64)
+
+
 def topk(scores, k: int) -> np.ndarray:
     """Indices of the k largest scores, as a set emitted in increasing index order
     ([RN] eq. 17).  Reading: when V <= k every entry is taken; equal scores go to the lower
@@ -440,7 +449,7 @@ def query_step(tau: int, q, qI, w, gamma_q, sink, entries, ki, raw_of, n_entries
         if dims.top_k == 0:
             sel = np.arange(V)
         else:
-            scores = index_scores(qI, w, ki[:V])
+            scores = stored_scores(index_scores(qI, w, ki[:V]), dims)
             sel = topk(scores, dims.top_k)
     sel = np.asarray(sel, dtype=np.int64)
     keys = np.concatenate([np.asarray(entries)[sel], raw_of(window_positions(tau, dims.n_win))], axis=0)

@@ -180,6 +180,34 @@ def test_mxfp4_scale_rule_and_round_trip():
     assert np.array_equal(codecs.mxfp4_unpack(np.array([0x9F], np.uint8)), [0xF, 0x9])
 
 
+def test_bf16_round_nearest_exact():
+    """Rounding straight from float64: ties to even, and a value just above a tie rounds up
+    where a float32 step would first land on the tie (the double-rounding case); random
+    values agree with an exact nearest search over the neighbouring bfloat16 values."""
+    ulp = 2.0 ** -7
+    cases = [(1.0 + ulp / 2, 1.0), (1.0 + 3 * ulp / 2, 1.0 + 2 * ulp), (-(1.0 + ulp / 2), -1.0),
+             (1.0 + ulp / 2 + 2.0 ** -30, 1.0 + ulp), (3.0, 3.0), (0.0, 0.0)]
+    for x, want in cases:
+        assert codecs.bf16_round_nearest(x) == want, (x, want)
+    rng = np.random.default_rng(21)
+    xs = rng.standard_normal(3000) * np.exp2(rng.integers(-20, 20, 3000))
+    got = codecs.bf16_round_nearest(xs)
+    for x, g in zip(xs, got):
+        f, e = math.frexp(x)
+        lo = math.floor(f * 256) / 256 * 2.0 ** e
+        hi = lo + 2.0 ** (e - 8)
+        dl, dh = Fraction(x) - Fraction(lo), Fraction(hi) - Fraction(x)
+        if dl < dh:
+            want = lo
+        elif dh < dl:
+            want = hi
+        else:
+            want = lo if int(abs(lo) / 2.0 ** (e - 8)) % 2 == 0 else hi
+        assert g == want, (x, g, want)
+        # the result is a bfloat16 value
+        assert codecs.bf16_decode(codecs.bf16_encode(g)) == g
+
+
 def test_fold_softmax_columns_sum_to_one():
     rng = np.random.default_rng(3)
     n, c, m = 24, 7, 4
