@@ -312,7 +312,8 @@ def run_decode(args, cfg):
     out = torch.empty((B, cfg["n_h"], cfg["c"]), dtype=torch.bfloat16, device=dev)
     if dual:
         ws_t = torch.empty(max(1, L.csa_topk_workspace_size(dims, B, N)), dtype=torch.uint8, device=dev)
-        scores = torch.empty((B, N), dtype=torch.float32, device=dev)
+        scores = torch.empty((B, N), dtype=torch.bfloat16 if dims.idx_fmt == "mxfp4" else torch.float32,
+                             device=dev)
         idx = torch.empty((B, k), dtype=torch.int32, device=dev)
 
     def k_compress(c):
@@ -370,7 +371,8 @@ def run_decode(args, cfg):
         "value": round(B * steps / wall, 1), "unit": "queries/s", "n_gpus": 1, "steps": steps,
         "warmup": warm, "ms_per_step": round(wall / steps * 1e3, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 MFMA on E4M3/bf16 storage, fp32 accumulate",
+        "dtype": ("bf16 MFMA on MXFP4 indexer / E4M3+bf16 KV storage, fp32 accumulate, bf16 index scores"
+                  if cfg["idx_fmt"] == "mxfp4" else "bf16 MFMA on E4M3/bf16 storage, fp32 accumulate"),
         "data": "synthetic (seeded N(0,1) hidden states and queries, N(0,1/fan_in) weights)",
     }
     if dual:

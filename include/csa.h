@@ -218,35 +218,37 @@ int csa_compress(const csa_dims* dims, const csa_weights* w, const csa_cache* ca
  *   idx_out [Q][top_k] int32: the selected entry indices in increasing order, -1 padded.
  *           A query sees V = min(tau / m, n_entries[seq]) entries (its own block is
  *           excluded); if V <= top_k all V are taken; equal scores go to the lower index.
- *   scores_out  NULL, or [Q][cap] float32 receiving the scores of the visible entries
- *           (entries s >= V are left untouched).
+ *   scores_out  NULL, or [Q][cap] receiving the scores of the visible entries (entries
+ *           s >= V are left untouched): float32, or with idx_fmt MXFP4 bfloat16, the pages'
+ *           BF16 index scores of the FP4 path (reading notes §3.4), each the exact score
+ *           rounded to nearest even.
  * Errors: INVALID_ARGUMENT (null pointer, Q < 1, dual = 0 or top_k < 1), UNSUPPORTED
  * (V could exceed what the selection kernels handle for this top_k), WORKSPACE_TOO_SMALL,
  * HIP_ERROR.
  */
 int csa_index_topk(const csa_dims* dims, const csa_cache* cache, const void* qI,
                    const void* w, const int32_t* q_seq, const int32_t* q_pos, int32_t Q,
-                   int32_t* idx_out, float* scores_out, void* ws, size_t ws_bytes,
+                   int32_t* idx_out, void* scores_out, void* ws, size_t ws_bytes,
                    hipStream_t stream);
 
 /*
  * The indexer on its own (reading notes eq. 16): scores[q][s] for s < V of each query, in
- * float32, row stride ld (>= the largest V; cache->cap always works).  Entries s >= V are
+ * float32 (bfloat16 with idx_fmt MXFP4, as in csa_index_topk), row stride ld (>= the largest V; cache->cap always works).  Entries s >= V are
  * left untouched.  csa_index_topk = csa_index_scores + csa_topk.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED, HIP_ERROR.
  */
 int csa_index_scores(const csa_dims* dims, const csa_cache* cache, const void* qI,
                      const void* w, const int32_t* q_seq, const int32_t* q_pos, int32_t Q,
-                     float* scores, int64_t ld, hipStream_t stream);
+                     void* scores, int64_t ld, hipStream_t stream);
 
 /*
  * The top-k selection on its own (reading notes eq. 17) over scores [Q][ld] as written by
- * csa_index_scores: idx_out[Q][top_k] as in csa_index_topk.  ws as csa_workspace_size(
+ * csa_index_scores (float32, or bfloat16 with idx_fmt MXFP4): idx_out[Q][top_k] as in csa_index_topk.  ws as csa_workspace_size(
  * INDEX_TOPK) minus the score buffer: csa_topk_workspace_size(), which is 0 for caches of
  * up to 65536 entries (one workgroup selects each query's row) and ws may then be NULL.
  */
 int csa_topk(const csa_dims* dims, const csa_cache* cache, const int32_t* q_seq,
-             const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld,
+             const int32_t* q_pos, int32_t Q, const void* scores, int64_t ld,
              int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes of csa_topk for Q queries against entry capacity cap. */

@@ -264,8 +264,19 @@ def csa_compress(dims: Dims, w: Weights, cache: Cache, H, T: int, pos0, ws=None,
                                _stream(stream)))
 
 
+def _check_scores(dims: Dims, t):
+    """Scores are float32, or bfloat16 with the MXFP4 indexer path."""
+    if t is None:
+        return
+    import torch
+    want = torch.bfloat16 if dims.idx_fmt == "mxfp4" else torch.float32
+    if t.dtype != want:
+        raise ValueError(f"scores must be {want} for idx_fmt {dims.idx_fmt!r}, got {t.dtype}")
+
+
 def csa_index_topk(dims: Dims, cache: Cache, qI, w, q_seq, q_pos, Q: int, idx_out,
                    scores_out=None, ws=None, stream=None):
+    _check_scores(dims, scores_out)
     wp, wn = _ws(ws)
     _check(load().csa_index_topk(ctypes.byref(dims.struct()), ctypes.byref(cache.struct()),
                                  _ptr(qI), _ptr(w), _ptr(q_seq), _ptr(q_pos), Q, _ptr(idx_out),
@@ -274,6 +285,7 @@ def csa_index_topk(dims: Dims, cache: Cache, qI, w, q_seq, q_pos, Q: int, idx_ou
 
 def csa_index_scores(dims: Dims, cache: Cache, qI, w, q_seq, q_pos, Q: int, scores, ld: int,
                      stream=None):
+    _check_scores(dims, scores)
     _check(load().csa_index_scores(ctypes.byref(dims.struct()), ctypes.byref(cache.struct()),
                                    _ptr(qI), _ptr(w), _ptr(q_seq), _ptr(q_pos), Q, _ptr(scores),
                                    ld, _stream(stream)))
@@ -285,6 +297,7 @@ def csa_topk_workspace_size(dims: Dims, Q: int, cap: int) -> int:
 
 def csa_topk(dims: Dims, cache: Cache, q_seq, q_pos, Q: int, scores, ld: int, idx_out, ws=None,
              stream=None):
+    _check_scores(dims, scores)
     wp, wn = _ws(ws)
     _check(load().csa_topk(ctypes.byref(dims.struct()), ctypes.byref(cache.struct()), _ptr(q_seq),
                            _ptr(q_pos), Q, _ptr(scores), ld, _ptr(idx_out), wp, wn, _stream(stream)))

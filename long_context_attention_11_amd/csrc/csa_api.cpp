@@ -236,7 +236,7 @@ int csa_compress(const csa_dims* dims, const csa_weights* w, const csa_cache* ca
 
 static int index_topk_impl(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
                            const int32_t* q_seq, const int32_t* q_pos, int32_t Q, int32_t* idx_out,
-                           float* scores_out, void* ws, size_t ws_bytes, bool tiled,
+                           void* scores_out, void* ws, size_t ws_bytes, bool tiled,
                            hipStream_t stream, const ProjectStepArgs* step = nullptr,
                            const FoldArgs* fold = nullptr) {
   const size_t sc_bytes = scores_out ? 0 : align_up((size_t)Q * c.cap * sizeof(float), 256);
@@ -244,7 +244,7 @@ static int index_topk_impl(const csa_dims& d, const csa_cache& c, const void* qI
                                                    : topk_workspace_bytes(d, Q, c.cap));
   if (need && (!ws || ws_bytes < need))
     return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "index_topk needs " + std::to_string(need) + " bytes of workspace");
-  float* scores = scores_out ? scores_out : (float*)ws;
+  void* scores = scores_out ? scores_out : ws;
   void* tws = (char*)ws + sc_bytes;
   hipError_t e = launch_indexer(d, c, qI, w, q_seq, q_pos, Q, scores, c.cap, tiled, stream);
   if (e != hipSuccess) return hip_fail(e, "indexer launch");
@@ -255,7 +255,7 @@ static int index_topk_impl(const csa_dims& d, const csa_cache& c, const void* qI
 
 int csa_index_topk(const csa_dims* dims, const csa_cache* cache, const void* qI, const void* w,
                    const int32_t* q_seq, const int32_t* q_pos, int32_t Q, int32_t* idx_out,
-                   float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+                   void* scores_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_last_error.clear();
   int st = check_dims(dims);
   if (st) return st;
@@ -273,7 +273,7 @@ int csa_index_topk(const csa_dims* dims, const csa_cache* cache, const void* qI,
 }
 
 int csa_index_scores(const csa_dims* dims, const csa_cache* cache, const void* qI, const void* w,
-                     const int32_t* q_seq, const int32_t* q_pos, int32_t Q, float* scores,
+                     const int32_t* q_seq, const int32_t* q_pos, int32_t Q, void* scores,
                      int64_t ld, hipStream_t stream) {
   g_last_error.clear();
   int st = check_dims(dims);
@@ -295,7 +295,7 @@ size_t csa_topk_workspace_size(const csa_dims* dims, int32_t Q, int32_t cap) {
 }
 
 int csa_topk(const csa_dims* dims, const csa_cache* cache, const int32_t* q_seq,
-             const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld, int32_t* idx_out,
+             const int32_t* q_pos, int32_t Q, const void* scores, int64_t ld, int32_t* idx_out,
              void* ws, size_t ws_bytes, hipStream_t stream) {
   g_last_error.clear();
   int st = check_dims(dims);

@@ -222,8 +222,9 @@ hipError_t launch_state_update(const csa_dims& d, const csa_cache& c, int32_t T,
                                hipStream_t s);
 // `tiled`: every aligned group of 16 queries (0-15, 16-31, ...) belongs to one sequence, so
 // the prefill-shaped kernel may share key tiles between them.
+// Scores are float32, or bfloat16 with the MXFP4 indexer path.
 hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
-                          const int32_t* q_seq, const int32_t* q_pos, int32_t Q, float* scores,
+                          const int32_t* q_seq, const int32_t* q_pos, int32_t Q, void* scores,
                           int64_t ld_scores, bool tiled, hipStream_t s);
 // Rows longer than one top-k segment (topk_can_carry) can take the threshold + final passes,
 // whose launches carry other work: with step non-null (only where topk_can_carry_step allows
@@ -234,7 +235,7 @@ hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI,
 bool topk_can_carry(const csa_cache& c);
 bool topk_can_carry_step(const csa_cache& c, int32_t Q, int32_t step_units);
 hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
-                       const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld_scores,
+                       const int32_t* q_pos, int32_t Q, const void* scores, int64_t ld_scores,
                        int32_t* idx, void* ws, hipStream_t s,
                        const struct ProjectStepArgs* step = nullptr,
                        const struct FoldArgs* fold = nullptr);

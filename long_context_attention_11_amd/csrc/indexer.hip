@@ -44,6 +44,27 @@ __device__ __forceinline__ void mxfp4x32_to_ops(const uint4& codes, uint32_t sca
   }
 }
 
+// The value of the lane 32 (16) apart, for a float64.
+__device__ __forceinline__ double lane_xor32_d(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const float lo = lane_xor32(__uint_as_float((uint32_t)u)), hi = lane_xor32(__uint_as_float((uint32_t)(u >> 32)));
+  return __builtin_bit_cast(double, (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32));
+}
+__device__ __forceinline__ double lane_xor16_d(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const float lo = lane_xor16(__uint_as_float((uint32_t)u)), hi = lane_xor16(__uint_as_float((uint32_t)(u >> 32)));
+  return __builtin_bit_cast(double, (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32));
+}
+
+// The nearest bfloat16 to a float64 (ties to even), rounded once: with x = f 2^e, f in
+// [0.5, 1), the value keeps rint(f 2^8) 2^(e - 8), which float32 holds exactly.
+__device__ __forceinline__ uint16_t bf16_nearest_from_f64(double x) {
+  int e;
+  const double f = frexp(x, &e);
+  const float v = (float)ldexp(rint(ldexp(f, 8)), e - 8);
+  return (uint16_t)(__float_as_uint(v) >> 16);
+}
+
 // A lane's 32 dims of one key or query row, as loaded: E4M3 codes (32 bytes), or MXFP4
 // element bytes (16) and the block's scale code.
 template <bool FP4>
@@ -71,7 +92,7 @@ struct IndexerArgs {
   int cap;
   const int32_t* n_entries;
   int m;
-  float* scores;
+  void* scores;           // float32, or bfloat16 with FP4
   int64_t ld;
   int chunk;
 };
@@ -89,7 +110,7 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
   const int Q = ia.Q;
   const uint8_t* __restrict__ ki = ia.ki;
   const int cap = ia.cap, m = ia.m, chunk = ia.chunk;
-  float* __restrict__ scores = ia.scores;
+  float* __restrict__ scores = static_cast<float*>(ia.scores);
   const int64_t ld = ia.ld;
   constexpr int HT = NH / 16;
   constexpr int DEPTH = 4;
@@ -187,21 +208,41 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
       load_tile(s0 + stride * DEPTH, rk[i]);
 #pragma unroll
       for (int qq = 0; qq < QPW; ++qq) {
-        float part = 0.f;
+        if constexpr (FP4) {
+          // BF16 scores: the head sum in float64 (exact for these operands: products of a
+          // bf16 weight and an exact fp32 dot), rounded once to the nearest bfloat16
+          double part = 0.0;
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          f32x4 acc = {0, 0, 0, 0};
+          for (int ht = 0; ht < HT; ++ht) {
+            f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[qq][ht][ks], Bop[ks], acc, 0, 0, 0);
+            for (int ks = 0; ks < 4; ++ks)
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[qq][ht][ks], Bop[ks], acc, 0, 0, 0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) part = fmaf(W[qq][ht][e], fmaxf(acc[e], 0.f), part);
+            for (int e = 0; e < 4; ++e) part = fma((double)W[qq][ht][e], (double)fmaxf(acc[e], 0.f), part);
+          }
+          part += lane_xor32_d(part);
+          part += lane_xor16_d(part);
+          const int s = s0 + col;
+          if (g == 0 && s < min(V[qq], c_hi))
+            static_cast<uint16_t*>(ia.scores)[(size_t)(q0 + qq) * ld + s] = bf16_nearest_from_f64(part);
+        } else {
+          float part = 0.f;
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) {
+            f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[qq][ht][ks], Bop[ks], acc, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part = fmaf(W[qq][ht][e], fmaxf(acc[e], 0.f), part);
+          }
+          // lane groups summed as (g + g^2) + (g^1 + g^3), the order the tiled kernel uses
+          part += lane_xor32(part);
+          part += lane_xor16(part);
+          const int s = s0 + col;
+          if (g == 0 && s < min(V[qq], c_hi)) scores[(size_t)(q0 + qq) * ld + s] = part;
         }
-        // lane groups summed as (g + g^2) + (g^1 + g^3), the order the tiled kernel uses
-        part += lane_xor32(part);
-        part += lane_xor16(part);
-        const int s = s0 + col;
-        if (g == 0 && s < min(V[qq], c_hi)) scores[(size_t)(q0 + qq) * ld + s] = part;
       }
     }
   } while (++it < rounds);
@@ -394,7 +435,7 @@ __global__ __launch_bounds__(256) void k_indexer_f32(
 }  // namespace
 
 hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
-                          const int32_t* q_seq, const int32_t* q_pos, int32_t Q, float* scores,
+                          const int32_t* q_seq, const int32_t* q_pos, int32_t Q, void* scores,
                           int64_t ld, bool tiled, hipStream_t s) {
   if (tiled && d.idx_fmt == CSA_FMT_E4M3 && d.n_hI == 64 && Q >= IT_Q) {
     // every aligned group of IT_Q queries belongs to one sequence (the caller guarantees it)
@@ -405,17 +446,17 @@ hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI,
     dim3 grid(ntile, (c.cap + chunk - 1) / chunk);
     hipLaunchKernelGGL(k_indexer_tile, grid, dim3(512), 0, s, (const uint8_t*)qI,
                        (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki, c.cap,
-                       c.n_entries, d.m, scores, ld, chunk);
+                       c.n_entries, d.m, static_cast<float*>(scores), ld, chunk);
     return hipGetLastError();
   }
   if (d.idx_fmt == CSA_FMT_F32) {
     dim3 grid((c.cap + 255) / 256, Q);
     hipLaunchKernelGGL(k_indexer_f32, grid, dim3(256), 0, s, (const float*)qI, (const float*)w,
                        q_seq, q_pos, Q, (const float*)c.ki, c.cap, c.n_entries, d.m, d.n_hI,
-                       d.c_I, scores, ld);
+                       d.c_I, static_cast<float*>(scores), ld);
     return hipGetLastError();
   }
-  // E4M3 keys: bf16 MFMA.  One query per group; entry chunks sized so that the grid is about
+  // E4M3 or MXFP4 keys: bf16 MFMA.  One query per group; entry chunks sized so that the grid is about
   // two workgroups (8 waves) per CU, each wave streaming a long run of tiles.
   const int target_wgs = 512;
   const int per_q = std::max(1, target_wgs / std::max(Q, 1));

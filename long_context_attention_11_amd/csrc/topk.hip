@@ -278,12 +278,27 @@ __device__ __forceinline__ int visible(const int32_t* q_seq, const int32_t* q_po
   return max(0, min(q_pos[q] / m, n_entries[q_seq ? q_seq[q] : q]));
 }
 
+// A query's row of scores: float32, or (BF) bfloat16 widened exactly to float32.
+template <bool BF>
+struct ScoreRow {
+  const void* p;
+  __device__ __forceinline__ float operator[](int e) const {
+    if constexpr (BF) return __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[e] << 16);
+    else return static_cast<const float*>(p)[e];
+  }
+};
+template <bool BF>
+__device__ __forceinline__ ScoreRow<BF> score_row(const void* scores, int64_t ld, int q) {
+  if constexpr (BF) return {static_cast<const uint16_t*>(scores) + (size_t)q * ld};
+  else return {static_cast<const float*>(scores) + (size_t)q * ld};
+}
+
 // Level 0: blockIdx.x = query, blockIdx.y = segment of 1024*E scores.
 // direct != 0: the segment is the whole row; write the final selection to idx_out [Q][k].
 // Otherwise write the segment's candidates to cand_idx/cand_key [Q][nseg][k] (-1 padded).
-template <int E>
+template <int E, bool BF>
 __global__ __launch_bounds__(TK_THREADS) void k_topk_segment(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_seq,
+    const void* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries, int m, int k,
     int direct, int32_t* __restrict__ idx_out, int32_t* __restrict__ cand_idx,
     uint32_t* __restrict__ cand_key) {
@@ -303,13 +318,13 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_segment(
   it.first = base + threadIdx.x * E;
   it.V = V;
   const int first = it.first;
-  const float* row = scores + (size_t)q * ld;
+  const ScoreRow<BF> row = score_row<BF>(scores, ld, q);
   bool loaded = false;
-  if constexpr (E % 4 == 0) {
+  if constexpr (E % 4 == 0 && !BF) {
     if (first + E <= V && ((ld & 3) == 0)) {
 #pragma unroll
       for (int i = 0; i < E; i += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(row + first + i);
+        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(row.p) + first + i);
         it.key[i] = score_key(v.x);
         it.key[i + 1] = score_key(v.y);
         it.key[i + 2] = score_key(v.z);
@@ -348,7 +363,7 @@ __device__ __forceinline__ void pass_interval(float t, uint32_t& lo, uint32_t& s
 // TK_FINAL) to cand_idx/cand_key [Q][nseg][cs] in index order, and their count (which may
 // exceed cs) to cand_cnt [Q][nseg].
 struct FilterArgs {
-  const float* scores;
+  const void* scores;     // float32, or bfloat16 (BF)
   int64_t ld;
   const int32_t* q_seq;
   const int32_t* q_pos;
@@ -369,12 +384,13 @@ struct FilterArgs {
 // of a segment start at min(c0, L - TK_SEG), L = max(V, TK_SEG) <= the row stride (these
 // rows are longer than TK_SEG), so every read stays in the row; elements outside [c0, V) are
 // masked.
+template <bool BF>
 __device__ __forceinline__ void topk_filter_body(const FilterArgs& fa, int q, int seg, TopkShared& sh) {
   const int k = fa.k, cs = fa.cs, nseg = fa.nseg;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int V = visible(fa.q_seq, fa.q_pos, fa.n_entries, fa.m, q);
-  const float* row = fa.scores + (size_t)q * fa.ld;
+  const ScoreRow<BF> row = score_row<BF>(fa.scores, fa.ld, q);
   const bool take_all = V <= TK_FINAL;
   const int L = max(V, TK_SEG);
   // the sample first, then the segment, so their latencies overlap
@@ -444,9 +460,10 @@ __device__ __forceinline__ void topk_filter_body(const FilterArgs& fa, int q, in
   if (tid == 0 && seg == 0) fa.vis[q] = V;
 }
 
+template <bool BF>
 __global__ __launch_bounds__(TK_THREADS) void k_topk_filter(FilterArgs fa) {
   __shared__ TopkShared sh;
-  topk_filter_body(fa, blockIdx.x, blockIdx.y, sh);
+  topk_filter_body<BF>(fa, blockIdx.x, blockIdx.y, sh);
 }
 
 // The threshold pass and a one-token projection in one launch (they are independent), so the
@@ -454,13 +471,14 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_filter(FilterArgs fa) {
 // rest, waves 0 .. upb - 1 run one projection unit each and the others have nothing to do,
 // upb chosen so that the workgroups of the launch fill the 256 CUs once: each CU then streams
 // its fair share of the weights.
+template <bool BF>
 __global__ __launch_bounds__(TK_THREADS) void k_topk_filter_project(FilterArgs fa, int Q, ProjectStepArgs pa,
                                                                      int units, int upb) {
   __shared__ TopkShared sh;
   const int nf = Q * fa.nseg;
   const int b = blockIdx.x, wave = threadIdx.x >> 6;
   if (b < nf) {
-    topk_filter_body(fa, b % Q, b / Q, sh);
+    topk_filter_body<BF>(fa, b % Q, b / Q, sh);
   } else if (wave < upb) {
     const int u = upb * (b - nf) + wave;
     if (u < units) project_unit<2>(pa, u);
@@ -507,7 +525,7 @@ __device__ int final_fast(int q, int nseg, int cs, int N, int k, const int32_t* 
 // Final pass: blockIdx.x = query.  Selects k from the candidate lists, or from the whole row
 // when they cannot be trusted (see the file comment), and writes idx_out [Q][k].
 struct FinalArgs {
-  const float* scores;
+  const void* scores;     // float32, or bfloat16 (BF)
   int64_t ld;
   const int32_t* q_seq;
   const int32_t* q_pos;
@@ -521,8 +539,8 @@ struct FinalArgs {
   int32_t* idx_out;
 };
 
+template <bool BF>
 __device__ __forceinline__ void topk_final_body(const FinalArgs& fa, int q, FinalShared& fs) {
-  const float* __restrict__ scores = fa.scores;
   const int64_t ld = fa.ld;
   const int32_t* __restrict__ q_seq = fa.q_seq;
   const int32_t* __restrict__ q_pos = fa.q_pos;
@@ -558,7 +576,7 @@ __device__ __forceinline__ void topk_final_body(const FinalArgs& fa, int q, Fina
   } else {
     // exact selection over the whole row: the running top k (in index order, in LDS) plus
     // the next TK_FINAL - k scores, once per chunk
-    const float* row = scores + (size_t)q * ld;
+    const ScoreRow<BF> row = score_row<BF>(fa.scores, ld, q);
     const int ch = TK_FINAL - k;
     int nr = 0;
     for (int c0 = 0; c0 < V; c0 += ch) {
@@ -586,18 +604,20 @@ __device__ __forceinline__ void topk_final_body(const FinalArgs& fa, int q, Fina
   for (int i = n + tid; i < k; i += TK_THREADS) out[i] = -1;
 }
 
+template <bool BF>
 __global__ __launch_bounds__(TK_THREADS) void k_topk_final(FinalArgs fa) {
   __shared__ FinalShared fs;
-  topk_final_body(fa, blockIdx.x, fs);
+  topk_final_body<BF>(fa, blockIdx.x, fs);
 }
 
 // The final pass and a one-token fold in one launch (independent: blocks [0, Q) select, the
 // rest fold with 1024-thread blocks, whose columns past c hold zeros).
+template <bool BF>
 __global__ __launch_bounds__(TK_THREADS) void k_topk_final_fold(FinalArgs fa, int Q, FoldArgs fo, int fx) {
   __shared__ FinalShared fs;
   __shared__ float red[TK_WAVES];
   const int b = blockIdx.x;
-  if (b < Q) topk_final_body(fa, b, fs);
+  if (b < Q) topk_final_body<BF>(fa, b, fs);
   else fold_block<TK_WAVES, true>(fo, (b - Q) % fx, (b - Q) / fx, red);
 }
 
@@ -618,7 +638,7 @@ struct RowShared {
 };
 
 struct RowArgs {
-  const float* scores;
+  const void* scores;     // float32, or bfloat16 (BF)
   int64_t ld;
   const int32_t* q_seq;
   const int32_t* q_pos;
@@ -676,13 +696,14 @@ __device__ __forceinline__ void row_chunk(const float (&v)[8], int a0, int c0, i
   __syncthreads();   // sh.scan is rewritten by the next chunk
 }
 
+template <bool BF>
 __device__ __forceinline__ void topk_row_body(const RowArgs& ra, int q, RowShared& rs) {
   TopkShared& sh = rs.sh;
   const int k = ra.k;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int V = visible(ra.q_seq, ra.q_pos, ra.n_entries, ra.m, q);
-  const float* row = ra.scores + (size_t)q * ra.ld;
+  const ScoreRow<BF> row = score_row<BF>(ra.scores, ra.ld, q);
   int32_t* out = ra.idx_out + (size_t)q * k;
   const bool take_all = V <= TK_FINAL;
   // Reads of chunk c0 start at min(c0, L - TK_SEG), L = max(V, TK_SEG) <= the row stride (the
@@ -700,9 +721,9 @@ __device__ __forceinline__ void topk_row_body(const RowArgs& ra, int q, RowShare
   auto load_group = [&](int g0) {
 #pragma unroll
     for (int j = 0; j < RG; ++j) {
-      const float* p = row + min(g0 + j * TK_SEG, L - TK_SEG) + 512 * w + lane;
+      const int e0 = min(g0 + j * TK_SEG, L - TK_SEG) + 512 * w + lane;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sv[j][i] = p[64 * i];
+      for (int i = 0; i < 8; ++i) sv[j][i] = row[e0 + 64 * i];
     }
   };
   load_group(0);
@@ -780,9 +801,10 @@ __device__ __forceinline__ void topk_row_body(const RowArgs& ra, int q, RowShare
   for (int i = n + tid; i < k; i += TK_THREADS) out[i] = -1;
 }
 
+template <bool BF>
 __global__ __launch_bounds__(TK_THREADS) void k_topk_row(RowArgs ra) {
   __shared__ RowShared rs;
-  topk_row_body(ra, blockIdx.x, rs);
+  topk_row_body<BF>(ra, blockIdx.x, rs);
 }
 
 int items_E(int n) {
@@ -822,15 +844,16 @@ bool topk_can_carry_step(const csa_cache& c, int32_t Q, int32_t step_units) {
   return nf < 256 && carry_units_per_block((int)nf, step_units) > 0;
 }
 
-hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
-                       const int32_t* q_pos, int32_t Q, const float* scores, int64_t ld,
-                       int32_t* idx, void* ws, hipStream_t s, const ProjectStepArgs* step,
-                       const FoldArgs* fold) {
+template <bool BF>
+hipError_t launch_topk_t(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
+                         const int32_t* q_pos, int32_t Q, const void* scores, int64_t ld,
+                         int32_t* idx, void* ws, hipStream_t s, const ProjectStepArgs* step,
+                         const FoldArgs* fold) {
   const int k = d.top_k;
   if (c.cap <= TK_SEG) {
     if (step || fold) return hipErrorInvalidValue;   // the carrying passes exist only for long rows
 #define TK_DIRECT(EE)                                                                          \
-  hipLaunchKernelGGL((k_topk_segment<EE>), dim3(Q, 1), dim3(TK_THREADS), 0, s, scores, ld, q_seq, \
+  hipLaunchKernelGGL((k_topk_segment<EE, BF>), dim3(Q, 1), dim3(TK_THREADS), 0, s, scores, ld, q_seq, \
                      q_pos, c.n_entries, d.m, k, 1, idx, nullptr, nullptr)
     switch (items_E(c.cap)) {
       case 1: TK_DIRECT(1); break;
@@ -843,7 +866,7 @@ hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_s
   }
   if (c.cap <= TK_ROW_MAX && !step && !fold) {
     const RowArgs ra{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, idx};
-    hipLaunchKernelGGL(k_topk_row, dim3(Q), dim3(TK_THREADS), 0, s, ra);
+    hipLaunchKernelGGL(k_topk_row<BF>, dim3(Q), dim3(TK_THREADS), 0, s, ra);
     return hipGetLastError();
   }
   const int nseg = (c.cap + TK_SEG - 1) / TK_SEG;
@@ -857,10 +880,10 @@ hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_s
     const int units = project_units(step->NP, step->M, 2);
     const int upb = carry_units_per_block(Q * nseg, units);
     if (upb == 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_topk_filter_project, dim3(Q * nseg + (units + upb - 1) / upb), dim3(TK_THREADS), 0, s,
+    hipLaunchKernelGGL(k_topk_filter_project<BF>, dim3(Q * nseg + (units + upb - 1) / upb), dim3(TK_THREADS), 0, s,
                        fa, Q, *step, units, upb);
   } else {
-    hipLaunchKernelGGL(k_topk_filter, dim3(Q, nseg), dim3(TK_THREADS), 0, s, fa);
+    hipLaunchKernelGGL(k_topk_filter<BF>, dim3(Q, nseg), dim3(TK_THREADS), 0, s, fa);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -868,11 +891,20 @@ hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_s
   if (fold) {
     if (!fold->part) return hipErrorInvalidValue;   // the carried fold is a one-token step's
     const int fx = fold_grid_x(*fold);
-    hipLaunchKernelGGL(k_topk_final_fold, dim3(Q + fx * c.B), dim3(TK_THREADS), 0, s, fin, Q, *fold, fx);
+    hipLaunchKernelGGL(k_topk_final_fold<BF>, dim3(Q + fx * c.B), dim3(TK_THREADS), 0, s, fin, Q, *fold, fx);
   } else {
-    hipLaunchKernelGGL(k_topk_final, dim3(Q), dim3(TK_THREADS), 0, s, fin);
+    hipLaunchKernelGGL(k_topk_final<BF>, dim3(Q), dim3(TK_THREADS), 0, s, fin);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_seq,
+                       const int32_t* q_pos, int32_t Q, const void* scores, int64_t ld,
+                       int32_t* idx, void* ws, hipStream_t s, const ProjectStepArgs* step,
+                       const FoldArgs* fold) {
+  // the MXFP4 indexer path scores in bfloat16
+  if (d.idx_fmt == CSA_FMT_MXFP4) return launch_topk_t<true>(d, c, q_seq, q_pos, Q, scores, ld, idx, ws, s, step, fold);
+  return launch_topk_t<false>(d, c, q_seq, q_pos, Q, scores, ld, idx, ws, s, step, fold);
 }
 
 }  // namespace csa

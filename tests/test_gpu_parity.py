@@ -242,7 +242,8 @@ def _run_index_attend_and_check(cfg, dims, cache, qs, W, q_seq, q_pos, taus, che
     Q, k = len(taus), cfg["top_k"]
     od = oracle_dims(cfg)
     idx = torch.full((Q, max(k, 1)), -7, dtype=torch.int32, device=DEV)
-    scores = torch.zeros((Q, cache.cap), dtype=torch.float32, device=DEV) if check_scores else None
+    sdt = torch.bfloat16 if cfg["idx_fmt"] == "mxfp4" else torch.float32
+    scores = torch.zeros((Q, cache.cap), dtype=sdt, device=DEV) if check_scores else None
     out = torch.zeros((Q, cfg["n_h"], cfg["c"]), dtype=torch.bfloat16, device=DEV)
     if cfg["dual"]:
         ws = _ws(L.csa_workspace_size(dims, L.OP_INDEX_TOPK, Q=Q, cap=cache.cap))
@@ -257,7 +258,7 @@ def _run_index_attend_and_check(cfg, dims, cache, qs, W, q_seq, q_pos, taus, che
     sink = host64(W["sink"]) if W["sink"] is not None else None
     gi = idx.cpu().numpy()
     go = host64(out)
-    gs = scores.cpu().numpy().astype(np.float64) if scores is not None else None
+    gs = scores.float().cpu().numpy().astype(np.float64) if scores is not None else None
     per_seq = {}
     stats = []
     for i, (b, tau) in enumerate(taus):
@@ -269,7 +270,12 @@ def _run_index_attend_and_check(cfg, dims, cache, qs, W, q_seq, q_pos, taus, che
                                       None, sink, entries, ki, raw_of, ne, od)
         if cfg["dual"]:
             V = R.visible_entries(tau, cfg["m"], ne)
-            if gs is not None and V:
+            if gs is not None and V and cfg["idx_fmt"] == "mxfp4":
+                # BF16 scores: the exact score rounded once to nearest even, on both sides
+                bad = np.flatnonzero(gs[i, :V] != sc)
+                assert len(bad) == 0, (f"bf16 scores tau={tau}: {len(bad)} differ, first {bad[:3]}: "
+                                       f"{gs[i, bad[:3]]} vs {sc[bad[:3]]}")
+            elif gs is not None and V:
                 # scores: float32 accumulation of exact products
                 dots = np.abs(ki[:V]) @ np.abs(qI[i]).T
                 scale = dots @ np.abs(w[i])
@@ -357,7 +363,7 @@ def test_q_forward_end_to_end():
                 # allowed only if the GPU's selection is the exact top-k of the scores its own
                 # (validated, flip-only) stored keys give
                 V = R.visible_entries(tau, cfg["m"], nb)
-                sc_g = R.index_scores(qI[i], w[i], g_ki[:V])
+                sc_g = R.stored_scores(R.index_scores(qI[i], w[i], g_ki[:V]), od)
                 same = check_topk(gi[i], sc_g, k, f"e2e seq {b} tau={tau} (GPU keys)")
                 same = False
             if not same:
@@ -416,7 +422,7 @@ def test_q_forward_decode_steps(idx_fmt):
                 same = check_topk(gi, sc, k, f"decode seq {b} tau={tau}")
             except AssertionError:
                 V = R.visible_entries(tau, cfg["m"], nb)
-                sc_g = R.index_scores(qI[i], w[i], g_ki[:V])
+                sc_g = R.stored_scores(R.index_scores(qI[i], w[i], g_ki[:V]), od)
                 same = check_topk(gi, sc_g, k, f"decode seq {b} tau={tau} (GPU keys)")
                 same = False
             if not same:
@@ -563,7 +569,8 @@ def test_c4_prefill_full_size_sampled():
             same = check_topk(gi[t], sc, k, f"c4 t={t}")
         except AssertionError:
             V = R.visible_entries(tau, m, cap)
-            check_topk(gi[t], R.index_scores(qI[t], w[t], g_ki[:V]), k, f"c4 t={t} (GPU keys)")
+            check_topk(gi[t], R.stored_scores(R.index_scores(qI[t], w[t], g_ki[:V]), od), k,
+                       f"c4 t={t} (GPU keys)")
             same = False
         if not same:
             sel_g = gi[t][gi[t] >= 0]
