@@ -16,7 +16,8 @@ layers would be), so a graph launch is paid once per cycle rather than once per 
 
 Other workloads (--config): c3 (Pro decode, 4 x 1M tokens), c5 (HCA decode, 8 x 1M tokens),
 c4a / c4b (32768-token prefill chunk after a 1M- / 262144-token prefix; one step = one
-csa_forward of the chunk), c1 (tiny fp32 prefill).
+csa_forward of the chunk), c1 (tiny fp32 prefill); c2fp4 and c4bfp4 are c2 and c4b with the
+indexer's keys and queries in MXFP4.
 
 Per-kernel durations: each kernel of the step is also launched 20 times back to back inside
 one graph (same inputs, same grid), timed with HIP events around the replay; the dominant
@@ -75,7 +76,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2fp4", "c3", "c4a", "c4b", "c5"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2fp4", "c3", "c4a", "c4b", "c4bfp4", "c5"])
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -371,7 +372,7 @@ def run_decode(args, cfg):
         "value": round(B * steps / wall, 1), "unit": "queries/s", "n_gpus": 1, "steps": steps,
         "warmup": warm, "ms_per_step": round(wall / steps * 1e3, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": ("bf16 MFMA on MXFP4 indexer / E4M3+bf16 KV storage, fp32 accumulate, bf16 index scores"
+        "dtype": ("MXFP4 MFMA indexer, bf16 index scores; bf16 MFMA on E4M3/bf16 KV storage, fp32 accumulate"
                   if cfg["idx_fmt"] == "mxfp4" else "bf16 MFMA on E4M3/bf16 storage, fp32 accumulate"),
         "data": "synthetic (seeded N(0,1) hidden states and queries, N(0,1/fan_in) weights)",
     }
@@ -380,7 +381,8 @@ def run_decode(args, cfg):
         bytes_per_query = N * key_bytes + cfg["n_hI"] * key_bytes + 2 * cfg["n_hI"]
         alg = B * bytes_per_query
         dur = kt["index_scores"] * 1e-6
-        res["roofline"] = {"bound": "hbm", "kernel": "indexer (k_indexer_bf16)",
+        kname = "k_indexer_fp4" if cfg["idx_fmt"] == "mxfp4" else "k_indexer_bf16"
+        res["roofline"] = {"bound": "hbm", "kernel": f"indexer ({kname})",
                            "achieved": round(alg / dur / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                            "frac": round(alg / dur / HBM_PEAK, 4),
                            "traffic": measured_traffic() if cfg["name"] == "c2" else None,
@@ -463,7 +465,9 @@ def run_prefill(args, cfg):
            "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm,
            "ms_per_step": round(wall / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None,
-           "dtype": "fp32" if cfg["act"] == "f32" else "bf16 MFMA on E4M3/bf16 storage, fp32 accumulate",
+           "dtype": ("fp32" if cfg["act"] == "f32" else
+                     "MXFP4 MFMA indexer, bf16 index scores; bf16 MFMA on E4M3/bf16 KV storage, fp32 accumulate"
+                     if cfg["idx_fmt"] == "mxfp4" else "bf16 MFMA on E4M3/bf16 storage, fp32 accumulate"),
            "data": "synthetic (seeded N(0,1) hidden states and queries, N(0,1/fan_in) weights)",
            "gpu_ms_per_step": round(gpu_ms, 4), "cache_build_s": round(t_build, 2),
            "config": {"workload": f"{cfg['name']}: chunked prefill, {T}-token chunk after a {p0}-token prefix, "

@@ -3,10 +3,14 @@
 // (reading notes "DeepSeekV4技术报告阅读笔记" §2.3.2 eq. 16 and the causal rule after eq. 17;
 // deep dive "DeepSeek-V4 架构设计深度解析" §3.2; PaperTrace "02 · DeepSeek-V4" §2.2).
 //
-// The contraction over c_I runs on bf16 MFMA: E4M3 values widen to bf16 exactly, products
-// are exact and accumulate in float32.  (The fp8 MFMA forms accumulate with fewer bits:
-// measured errors of ~2^-16 of sum|a_k b_k|, which top-k selection cannot tolerate.)
-// The ReLU, the head weight and the sum over heads are fused into the MFMA epilogue.
+// With E4M3 keys and queries the contraction over c_I runs on bf16 MFMA: E4M3 values widen to
+// bf16 exactly, products are exact and accumulate in float32.  (The fp8 MFMA forms accumulate
+// with fewer bits: measured errors of ~2^-16 of sum|a_k b_k|, which top-k selection cannot
+// tolerate.)  With MXFP4 keys and queries (the FP4 indexer path, reading notes §3.3-3.4) the
+// codes and scales go to the block-scaled FP4 MFMA as stored; measured on gfx950 it returns
+// the float32 rounding of the exact dot, exactly the dot for these operands.  The ReLU, the
+// head weight and the sum over heads are fused into the MFMA epilogue; the FP4 path sums in
+// float64 and stores the BF16 score rounded once.
 #include "csa_internal.h"
 
 namespace csa {
@@ -28,20 +32,17 @@ __device__ __forceinline__ void e4m3x32_to_ops(const uint4& lo, const uint4& hi,
   }
 }
 
-// 32 MXFP4 elements (16 bytes, element 2i in the low nibble of byte i) with their E8M0 scale
-// code into four bf16x8 MFMA operands, exactly: the conversion multiplies each E2M1 value by
-// the power of two 2^(scale - 127).
-__device__ __forceinline__ void mxfp4x32_to_ops(const uint4& codes, uint32_t scale, bf16x8 op[4]) {
-  const float sc = scale ? __uint_as_float(scale << 23) : __uint_as_float(0x00400000u);  // 2^-127
-  const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const uint4 v = make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[ks], sc, 0)),
-                               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[ks], sc, 1)),
-                               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[ks], sc, 2)),
-                               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[ks], sc, 3)));
-    op[ks] = __builtin_bit_cast(bf16x8, v);
-  }
+// One block-scaled 16x16x128 MFMA over E2M1 operands (OCP MX FP4): lane l supplies row
+// (l & 15), elements 32g .. 32g+31 with g = l >> 4 (16 bytes, element 2i in the low nibble of
+// byte i) and that block's E8M0 scale code; the result lane l holds column (l & 15), rows
+// 4g .. 4g+3.  Products of E2M1 values are exact, and so is the sum whenever it fits a
+// float32 significand (it does when the scales of a row pair lie within a few octaves).
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma_fp4(const uint4& a, int sa, const uint4& b, int sb) {
+  const i32x8 av = {(int32_t)a.x, (int32_t)a.y, (int32_t)a.z, (int32_t)a.w, 0, 0, 0, 0};
+  const i32x8 bv = {(int32_t)b.x, (int32_t)b.y, (int32_t)b.z, (int32_t)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, sa,
+                                                          0, sb);
 }
 
 // The value of the lane 32 (16) apart, for a float64.
@@ -65,16 +66,21 @@ __device__ __forceinline__ uint16_t bf16_nearest_from_f64(double x) {
   return (uint16_t)(__float_as_uint(v) >> 16);
 }
 
-// A lane's 32 dims of one key or query row, as loaded: E4M3 codes (32 bytes), or MXFP4
-// element bytes (16) and the block's scale code.
-template <bool FP4>
-struct RawOp {
-  uint4 a, b;
-  __device__ void to_ops(bf16x8 op[4]) const {
-    if constexpr (FP4) mxfp4x32_to_ops(a, b.x, op);
-    else e4m3x32_to_ops(a, b, op);
+// Head sum of one query's MFMA tile with its weights, for the BF16 scores of the FP4 path:
+// the products of a bf16 weight and an exact float32 dot are exact in float64, and so is
+// their sum for these magnitudes; the score is rounded once, at the store.
+template <int HT>
+__device__ __forceinline__ double head_sum_f64(const uint4 (&qa)[HT], const int (&qs)[HT],
+                                               const double (&W)[HT][4], const uint4& b, int bs) {
+  double part = 0.0;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const f32x4 acc = mfma_fp4(qa[ht], qs[ht], b, bs);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) part = fma(W[ht][e], (double)fmaxf(acc[e], 0.f), part);
   }
-};
+  return part;
+}
 
 // One workgroup = 4 waves; blockIdx.x = group of QPW queries (same sequence), blockIdx.y =
 // entry chunk; wave w scans its quarter of the chunk in tiles of 16 entries.
@@ -92,24 +98,41 @@ struct IndexerArgs {
   int cap;
   const int32_t* n_entries;
   int m;
-  void* scores;           // float32, or bfloat16 with FP4
+  void* scores;           // float32, or bfloat16 with MXFP4
   int64_t ld;
   int chunk;
 };
 
-// Workgroup (bx, by): queries bx * QPW .. +QPW-1 against entry chunk by.
-// FP4: keys and queries in MXFP4.  A sequence's keys are cap rows of 64 element bytes, then
-// cap rows of 4 scale codes; a query's q^I is NH rows of 64 element bytes, then NH rows of 4
-// scale codes.  Lane group g reads block g of a row: 16 element bytes and one scale code.
-template <int NH, int QPW, bool FP4>
+// The part of a workgroup's work every indexer body shares: its queries' visible ranges and
+// the wave's first tile of the chunk.  Returns false when the wave has nothing to score.
+template <int QPW>
+__device__ __forceinline__ bool indexer_range(const IndexerArgs& ia, int bx, int by, int wave, int& seq,
+                                              int (&V)[QPW], int& c_hi, int& w_lo) {
+  const int q0 = bx * QPW;
+  seq = ia.q_seq ? ia.q_seq[q0] : q0;
+  const int nent = ia.n_entries[seq];
+  int Vmax = 0;
+#pragma unroll
+  for (int qq = 0; qq < QPW; ++qq) {
+    const int q = q0 + qq;
+    V[qq] = q < ia.Q ? max(0, min(ia.q_pos[q] / ia.m, nent)) : 0;
+    Vmax = max(Vmax, V[qq]);
+  }
+  // this wave's entries: tiles of 16 dealt round-robin over the 4 waves of the chunk
+  const int c_lo = by * ia.chunk;
+  c_hi = min(c_lo + ia.chunk, Vmax);
+  w_lo = c_lo + 16 * wave;
+  return c_lo < c_hi && w_lo < c_hi;
+}
+
+// E4M3 keys and queries.  Workgroup (bx, by): queries bx * QPW .. +QPW-1 against entry chunk by.
+template <int NH, int QPW>
 __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx, int by) {
   const uint8_t* __restrict__ qI = ia.qI;
   const uint16_t* __restrict__ wI = ia.wI;
-  const int32_t* __restrict__ q_seq = ia.q_seq;
-  const int32_t* __restrict__ q_pos = ia.q_pos;
   const int Q = ia.Q;
   const uint8_t* __restrict__ ki = ia.ki;
-  const int cap = ia.cap, m = ia.m, chunk = ia.chunk;
+  const int cap = ia.cap;
   float* __restrict__ scores = static_cast<float*>(ia.scores);
   const int64_t ld = ia.ld;
   constexpr int HT = NH / 16;
@@ -117,61 +140,34 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int q0 = bx * QPW;
-  const int seq = q_seq ? q_seq[q0] : q0;
-  const int nent = ia.n_entries[seq];
-  int V[QPW];
-  int Vmax = 0;
-#pragma unroll
-  for (int qq = 0; qq < QPW; ++qq) {
-    const int q = q0 + qq;
-    V[qq] = q < Q ? max(0, min(q_pos[q] / m, nent)) : 0;
-    Vmax = max(Vmax, V[qq]);
-  }
-  // this wave's entries: tiles of 16 dealt round-robin over the 4 waves of the chunk
-  const int c_lo = by * chunk;
-  const int c_hi = min(c_lo + chunk, Vmax);
-  if (c_lo >= c_hi) return;
-  const int w_lo = c_lo + 16 * wave;
-  if (w_lo >= c_hi) return;
+  int seq, V[QPW], c_hi, w_lo;
+  if (!indexer_range<QPW>(ia, bx, by, wave, seq, V, c_hi, w_lo)) return;
   const int stride = 64;  // 4 waves x 16 entries
 
-  constexpr int KROW = FP4 ? IX_CI / 2 + IX_CI / 32 : IX_CI;   // bytes per key or q^I row
-  const uint8_t* kseq = ki + (size_t)seq * cap * KROW;
+  const uint8_t* kseq = ki + (size_t)seq * cap * IX_CI;
   // Prologue: the query operands (q^I rows, head weights) and the first DEPTH tiles of keys
   // are all requested before anything waits, so their latencies overlap.  The ring holds
   // DEPTH tiles (16 entries x 128 B per wave, 32 B per lane); waits count outstanding loads
   // in issue order, so tile 0 is issued first among the keys.
-  RawOp<FP4> araw[QPW][HT];
+  uint4 araw[QPW][HT][2];
   uint2 wraw[QPW][HT];
 #pragma unroll
   for (int qq = 0; qq < QPW; ++qq) {
     const int q = min(q0 + qq, Q - 1);
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      const int h = ht * 16 + col;
-      if constexpr (FP4) {
-        const uint8_t* qrow = qI + (size_t)q * NH * KROW;
-        araw[qq][ht].a = *reinterpret_cast<const uint4*>(qrow + h * (IX_CI / 2) + g * 16);
-        araw[qq][ht].b.x = qrow[NH * (IX_CI / 2) + h * (IX_CI / 32) + g];
-      } else {
-        const uint8_t* src = qI + ((size_t)q * NH + h) * IX_CI + g * 32;
-        araw[qq][ht].a = *reinterpret_cast<const uint4*>(src);
-        araw[qq][ht].b = *reinterpret_cast<const uint4*>(src + 16);
-      }
+      const uint8_t* src = qI + ((size_t)q * NH + ht * 16 + col) * IX_CI + g * 32;
+      araw[qq][ht][0] = *reinterpret_cast<const uint4*>(src);
+      araw[qq][ht][1] = *reinterpret_cast<const uint4*>(src + 16);
       wraw[qq][ht] = *reinterpret_cast<const uint2*>(wI + (size_t)q * NH + ht * 16 + 4 * g);
     }
   }
-  RawOp<FP4> rk[DEPTH];
-  auto load_tile = [&](int s0, RawOp<FP4>& r) {
+  uint4 rk[DEPTH][2];
+  auto load_tile = [&](int s0, uint4 (&r)[2]) {
     const int s = min(s0 + col, c_hi - 1);
-    if constexpr (FP4) {
-      r.a = *reinterpret_cast<const uint4*>(kseq + (size_t)s * (IX_CI / 2) + g * 16);
-      r.b.x = kseq[(size_t)cap * (IX_CI / 2) + (size_t)s * (IX_CI / 32) + g];
-    } else {
-      const uint8_t* src = kseq + (size_t)s * IX_CI + g * 32;
-      r.a = *reinterpret_cast<const uint4*>(src);
-      r.b = *reinterpret_cast<const uint4*>(src + 16);
-    }
+    const uint8_t* src = kseq + (size_t)s * IX_CI + g * 32;
+    r[0] = *reinterpret_cast<const uint4*>(src);
+    r[1] = *reinterpret_cast<const uint4*>(src + 16);
   };
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) load_tile(w_lo + stride * i, rk[i]);
@@ -183,7 +179,7 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
   for (int qq = 0; qq < QPW; ++qq) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      araw[qq][ht].to_ops(A[qq][ht]);
+      e4m3x32_to_ops(araw[qq][ht][0], araw[qq][ht][1], A[qq][ht]);
       const uint2 w4 = wraw[qq][ht];
       W[qq][ht][0] = bf16_bits_to_f32(w4.x & 0xffffu);
       W[qq][ht][1] = bf16_bits_to_f32(w4.x >> 16);
@@ -204,53 +200,118 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
       const int s0 = base + stride * i;
       // widen the tile first, then reuse its registers for the load of the next round
       bf16x8 Bop[4];
-      rk[i].to_ops(Bop);
+      e4m3x32_to_ops(rk[i][0], rk[i][1], Bop);
       load_tile(s0 + stride * DEPTH, rk[i]);
 #pragma unroll
       for (int qq = 0; qq < QPW; ++qq) {
-        if constexpr (FP4) {
-          // BF16 scores: the head sum in float64 (exact for these operands: products of a
-          // bf16 weight and an exact fp32 dot), rounded once to the nearest bfloat16
-          double part = 0.0;
+        float part = 0.f;
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht) {
-            f32x4 acc = {0, 0, 0, 0};
+        for (int ht = 0; ht < HT; ++ht) {
+          f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[qq][ht][ks], Bop[ks], acc, 0, 0, 0);
+          for (int ks = 0; ks < 4; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[qq][ht][ks], Bop[ks], acc, 0, 0, 0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) part = fma((double)W[qq][ht][e], (double)fmaxf(acc[e], 0.f), part);
-          }
-          part += lane_xor32_d(part);
-          part += lane_xor16_d(part);
-          const int s = s0 + col;
-          if (g == 0 && s < min(V[qq], c_hi))
-            static_cast<uint16_t*>(ia.scores)[(size_t)(q0 + qq) * ld + s] = bf16_nearest_from_f64(part);
-        } else {
-          float part = 0.f;
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) {
-            f32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[qq][ht][ks], Bop[ks], acc, 0, 0, 0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) part = fmaf(W[qq][ht][e], fmaxf(acc[e], 0.f), part);
-          }
-          // lane groups summed as (g + g^2) + (g^1 + g^3), the order the tiled kernel uses
-          part += lane_xor32(part);
-          part += lane_xor16(part);
-          const int s = s0 + col;
-          if (g == 0 && s < min(V[qq], c_hi)) scores[(size_t)(q0 + qq) * ld + s] = part;
+          for (int e = 0; e < 4; ++e) part = fmaf(W[qq][ht][e], fmaxf(acc[e], 0.f), part);
         }
+        // lane groups summed as (g + g^2) + (g^1 + g^3), the order the tiled kernel uses
+        part += lane_xor32(part);
+        part += lane_xor16(part);
+        const int s = s0 + col;
+        if (g == 0 && s < min(V[qq], c_hi)) scores[(size_t)(q0 + qq) * ld + s] = part;
       }
     }
   } while (++it < rounds);
 }
 
-template <int NH, int QPW, bool FP4>
+// MXFP4 keys and queries, with the same work split and ring as indexer_bf16_body.  A
+// sequence's keys are cap rows of 64 element bytes, then cap rows of 4 scale codes; a query's
+// q^I is NH rows of 64 element bytes, then NH rows of 4 scale codes.  Lane group g reads
+// block g of a row (16 element bytes and one scale code), which is exactly the lane's share
+// of a block-scaled MFMA operand, so the codes go to the matrix cores as loaded: one
+// 16x16x128 MFMA per head tile covers all 128 dims.  Scores are bfloat16.
+template <int NH, int QPW>
+__device__ __forceinline__ void indexer_fp4_body(const IndexerArgs& ia, int bx, int by) {
+  constexpr int KC = IX_CI / 2, KS = IX_CI / 32;  // element bytes, scale codes per row
+  constexpr int HT = NH / 16;
+  constexpr int DEPTH = 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int q0 = bx * QPW;
+  int seq, V[QPW], c_hi, w_lo;
+  if (!indexer_range<QPW>(ia, bx, by, wave, seq, V, c_hi, w_lo)) return;
+  const int stride = 64;  // 4 waves x 16 entries
+  uint16_t* __restrict__ scores = static_cast<uint16_t*>(ia.scores);
+
+  const uint8_t* kcode = ia.ki + (size_t)seq * ia.cap * (KC + KS);
+  const uint8_t* kscale = kcode + (size_t)ia.cap * KC;
+  uint4 qa[QPW][HT];
+  int qs[QPW][HT];
+  uint2 wraw[QPW][HT];
+#pragma unroll
+  for (int qq = 0; qq < QPW; ++qq) {
+    const int q = min(q0 + qq, ia.Q - 1);
+    const uint8_t* qrow = ia.qI + (size_t)q * NH * (KC + KS);
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int h = ht * 16 + col;
+      qa[qq][ht] = *reinterpret_cast<const uint4*>(qrow + h * KC + g * 16);
+      qs[qq][ht] = qrow[NH * KC + h * KS + g];
+      wraw[qq][ht] = *reinterpret_cast<const uint2*>(ia.wI + (size_t)q * NH + ht * 16 + 4 * g);
+    }
+  }
+  uint4 kc[DEPTH];
+  int ks[DEPTH];
+  auto load_tile = [&](int s0, uint4& c, int& sc) {
+    const int s = min(s0 + col, c_hi - 1);
+    c = *reinterpret_cast<const uint4*>(kcode + (size_t)s * KC + g * 16);
+    sc = kscale[(size_t)s * KS + g];
+  };
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i) load_tile(w_lo + stride * i, kc[i], ks[i]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  double W[QPW][HT][4];
+#pragma unroll
+  for (int qq = 0; qq < QPW; ++qq)
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const uint2 w4 = wraw[qq][ht];
+      W[qq][ht][0] = bf16_bits_to_f32(w4.x & 0xffffu);
+      W[qq][ht][1] = bf16_bits_to_f32(w4.x >> 16);
+      W[qq][ht][2] = bf16_bits_to_f32(w4.y & 0xffffu);
+      W[qq][ht][3] = bf16_bits_to_f32(w4.y >> 16);
+    }
+  const int rounds = (c_hi - w_lo + stride * DEPTH - 1) / (stride * DEPTH);
+  int it = 0;
+  do {  // rounds >= 1 since w_lo < c_hi
+    const int base = w_lo + it * stride * DEPTH;
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) {
+      const int s0 = base + stride * i;
+      const uint4 b = kc[i];
+      const int bs = ks[i];
+      load_tile(s0 + stride * DEPTH, kc[i], ks[i]);
+#pragma unroll
+      for (int qq = 0; qq < QPW; ++qq) {
+        double part = head_sum_f64<HT>(qa[qq], qs[qq], W[qq], b, bs);
+        part += lane_xor32_d(part);
+        part += lane_xor16_d(part);
+        const int s = s0 + col;
+        if (g == 0 && s < min(V[qq], c_hi)) scores[(size_t)(q0 + qq) * ia.ld + s] = bf16_nearest_from_f64(part);
+      }
+    }
+  } while (++it < rounds);
+}
+
+template <int NH, int QPW>
 __global__ __launch_bounds__(256) void k_indexer_bf16(IndexerArgs ia) {
-  indexer_bf16_body<NH, QPW, FP4>(ia, blockIdx.x, blockIdx.y);
+  indexer_bf16_body<NH, QPW>(ia, blockIdx.x, blockIdx.y);
+}
+
+template <int NH, int QPW>
+__global__ __launch_bounds__(256) void k_indexer_fp4(IndexerArgs ia) {
+  indexer_fp4_body<NH, QPW>(ia, blockIdx.x, blockIdx.y);
 }
 
 // Prefill-shaped indexer: a workgroup of 8 waves scores IT_Q = 16 queries of ONE sequence
@@ -409,6 +470,128 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// Prefill-shaped MXFP4 indexer: the work split of k_indexer_tile (8 waves, IT_Q = 16 queries of
+// one sequence, 2 per wave), with the keys kept in MXFP4 all the way to the matrix cores.  A
+// stage of IF_STAGE entries is copied to LDS as stored (one 16-byte load of element bytes per
+// thread; the first IF_STAGE threads also move an entry's 4 scale codes), double buffered.
+// Per 16-entry tile a lane reads its block of the entry (16 bytes and the scale code) and
+// runs one block-scaled 16x16x128 MFMA per head tile and query; the head sum is the FP4
+// decode kernel's (float64, scores rounded once to bfloat16), reduced over lane groups as
+// in k_indexer_tile so that 64 lanes store 64 contiguous scores.
+constexpr int IF_STAGE = 128;  // entries per LDS stage
+constexpr int IF_RS = 80;      // LDS bytes per entry row: 64 element bytes + 16 pad, so the 16
+                               // rows a read touches start in 16 distinct 16-byte bank groups
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_indexer_tile_fp4(
+    const uint8_t* __restrict__ qI, const uint16_t* __restrict__ wI,
+    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int Q,
+    const uint8_t* __restrict__ ki, int cap, const int32_t* __restrict__ n_entries, int m,
+    uint16_t* __restrict__ scores, int64_t ld, int chunk) {
+  constexpr int NH = 64, HT = NH / 16, KC = IX_CI / 2, KS = IX_CI / 32;
+  __shared__ __align__(16) uint8_t kbuf[2][IF_STAGE * IF_RS];
+  __shared__ __align__(16) uint8_t sbuf[2][IF_STAGE * KS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int qt0 = blockIdx.x * IT_Q;
+  const int seq = q_seq ? q_seq[qt0] : qt0;
+  const int nent = n_entries[seq];
+  int Vmax = 0;
+  for (int i = 0; i < IT_Q; ++i) {
+    const int q = min(qt0 + i, Q - 1);
+    Vmax = max(Vmax, max(0, min(q_pos[q] / m, nent)));
+  }
+  const int e_lo = blockIdx.y * chunk;
+  const int e_hi = min(e_lo + chunk, Vmax);
+  if (e_lo >= e_hi) return;  // uniform over the workgroup
+
+  int V[2];
+  uint4 qa[2][HT];
+  int qs[2][HT];
+  double W[2][HT][4];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int qr = qt0 + 2 * wave + qq;
+    const int q = min(qr, Q - 1);
+    V[qq] = qr < Q ? max(0, min(q_pos[q] / m, nent)) : 0;
+    const uint8_t* qrow = qI + (size_t)q * NH * (KC + KS);
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int h = ht * 16 + col;
+      qa[qq][ht] = *reinterpret_cast<const uint4*>(qrow + h * KC + g * 16);
+      qs[qq][ht] = qrow[NH * KC + h * KS + g];
+      const uint2 w4 = *reinterpret_cast<const uint2*>(wI + (size_t)q * NH + ht * 16 + 4 * g);
+      W[qq][ht][0] = bf16_bits_to_f32(w4.x & 0xffffu);
+      W[qq][ht][1] = bf16_bits_to_f32(w4.x >> 16);
+      W[qq][ht][2] = bf16_bits_to_f32(w4.y & 0xffffu);
+      W[qq][ht][3] = bf16_bits_to_f32(w4.y >> 16);
+    }
+  }
+
+  // stage loader: thread t moves element bytes 16 (t % 4) .. +15 of entry t / 4 of the stage;
+  // threads t < IF_STAGE also move entry t's scale codes (clamped past the end, unused there)
+  const uint8_t* kcode = ki + (size_t)seq * cap * (KC + KS);
+  const uint8_t* kscale = kcode + (size_t)cap * KC;
+  const int le = tid >> 2, lp = (tid & 3) * 16;
+  auto gload = [&](int st, uint4& v, uint32_t& sv) {
+    const int e = min(e_lo + st * IF_STAGE + le, e_hi - 1);
+    v = *reinterpret_cast<const uint4*>(kcode + (size_t)e * KC + lp);
+    if (tid < IF_STAGE) {
+      const int es = min(e_lo + st * IF_STAGE + tid, e_hi - 1);
+      sv = *reinterpret_cast<const uint32_t*>(kscale + (size_t)es * KS);
+    }
+  };
+  auto lstore = [&](int buf, const uint4& v, uint32_t sv) {
+    *reinterpret_cast<uint4*>(&kbuf[buf][le * IF_RS + lp]) = v;
+    if (tid < IF_STAGE) *reinterpret_cast<uint32_t*>(&sbuf[buf][tid * KS]) = sv;
+  };
+  const int nst = (e_hi - e_lo + IF_STAGE - 1) / IF_STAGE;
+  uint4 nv;
+  uint32_t ns = 0;
+  gload(0, nv, ns);
+  lstore(0, nv, ns);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    if (st + 1 < nst) gload(st + 1, nv, ns);
+    const uint8_t* kb = kbuf[st & 1];
+    const uint8_t* sb = sbuf[st & 1];
+#pragma unroll
+    for (int sub = 0; sub < IF_STAGE / 64; ++sub) {
+      // part[t][qq]: tile t of this 64-entry run, query qq, the lane's 16 heads
+      double part[4][2];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = sub * 64 + t * 16 + col;
+        const uint4 b = *reinterpret_cast<const uint4*>(kb + r * IF_RS + g * 16);
+        const int bs = sb[r * KS + g];
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) part[t][qq] = head_sum_f64<HT>(qa[qq], qs[qq], W[qq], b, bs);
+      }
+      // reduce-scatter over the lane groups as in k_indexer_tile: lane (col, g) ends with entry
+      // g * 16 + col of the run, summed over all 64 heads
+      const bool hi2 = g >= 2, odd = g & 1;
+      double r1[2][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          const double keep = hi2 ? part[2 + j][qq] : part[j][qq];
+          const double send = hi2 ? part[j][qq] : part[2 + j][qq];
+          r1[j][qq] = keep + lane_xor32_d(send);
+        }
+      const int s = e_lo + st * IF_STAGE + sub * 64 + g * 16 + col;
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const double keep = odd ? r1[1][qq] : r1[0][qq];
+        const double send = odd ? r1[0][qq] : r1[1][qq];
+        const double total = keep + lane_xor16_d(send);
+        if (s < min(V[qq], e_hi)) scores[(size_t)(qt0 + 2 * wave + qq) * ld + s] = bf16_nearest_from_f64(total);
+      }
+    }
+    if (st + 1 < nst) lstore((st + 1) & 1, nv, ns);
+    __syncthreads();
+  }
+}
+
 // float32 indexer (fp32 formats): one thread per (query, entry).
 __global__ __launch_bounds__(256) void k_indexer_f32(
     const float* __restrict__ qI, const float* __restrict__ wI, const int32_t* __restrict__ q_seq,
@@ -437,16 +620,23 @@ __global__ __launch_bounds__(256) void k_indexer_f32(
 hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
                           const int32_t* q_seq, const int32_t* q_pos, int32_t Q, void* scores,
                           int64_t ld, bool tiled, hipStream_t s) {
-  if (tiled && d.idx_fmt == CSA_FMT_E4M3 && d.n_hI == 64 && Q >= IT_Q) {
+  const bool fp4 = d.idx_fmt == CSA_FMT_MXFP4;
+  if (tiled && (fp4 || d.idx_fmt == CSA_FMT_E4M3) && d.n_hI == 64 && Q >= IT_Q) {
     // every aligned group of IT_Q queries belongs to one sequence (the caller guarantees it)
     const int ntile = (Q + IT_Q - 1) / IT_Q;
     const int nsplit = std::max(1, (256 + ntile - 1) / ntile);
+    const int stage = fp4 ? IF_STAGE : IT_STAGE;
     int chunk = (c.cap + nsplit - 1) / nsplit;
-    chunk = (chunk + IT_STAGE - 1) / IT_STAGE * IT_STAGE;
+    chunk = (chunk + stage - 1) / stage * stage;
     dim3 grid(ntile, (c.cap + chunk - 1) / chunk);
-    hipLaunchKernelGGL(k_indexer_tile, grid, dim3(512), 0, s, (const uint8_t*)qI,
-                       (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki, c.cap,
-                       c.n_entries, d.m, static_cast<float*>(scores), ld, chunk);
+    if (fp4)
+      hipLaunchKernelGGL(k_indexer_tile_fp4, grid, dim3(512), 0, s, (const uint8_t*)qI,
+                         (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki, c.cap,
+                         c.n_entries, d.m, static_cast<uint16_t*>(scores), ld, chunk);
+    else
+      hipLaunchKernelGGL(k_indexer_tile, grid, dim3(512), 0, s, (const uint8_t*)qI,
+                         (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki, c.cap,
+                         c.n_entries, d.m, static_cast<float*>(scores), ld, chunk);
     return hipGetLastError();
   }
   if (d.idx_fmt == CSA_FMT_F32) {
@@ -456,7 +646,7 @@ hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI,
                        d.c_I, static_cast<float*>(scores), ld);
     return hipGetLastError();
   }
-  // E4M3 or MXFP4 keys: bf16 MFMA.  One query per group; entry chunks sized so that the grid is about
+  // E4M3 keys (bf16 MFMA) or MXFP4 keys (block-scaled FP4 MFMA).  One query per group; entry chunks sized so that the grid is about
   // two workgroups (8 waves) per CU, each wave streaming a long run of tiles.
   const int target_wgs = 512;
   const int per_q = std::max(1, target_wgs / std::max(Q, 1));
@@ -466,10 +656,9 @@ hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI,
   const IndexerArgs ia{(const uint8_t*)qI, (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki,
                        c.cap, c.n_entries, d.m, scores, ld, chunk};
   dim3 grid(Q, nchunk);
-  const bool fp4 = d.idx_fmt == CSA_FMT_MXFP4;
 #define IX_LAUNCH(NHV)                                                                          \
-  if (fp4) hipLaunchKernelGGL((k_indexer_bf16<NHV, 1, true>), grid, dim3(256), 0, s, ia);         \
-  else hipLaunchKernelGGL((k_indexer_bf16<NHV, 1, false>), grid, dim3(256), 0, s, ia)
+  if (fp4) hipLaunchKernelGGL((k_indexer_fp4<NHV, 1>), grid, dim3(256), 0, s, ia);                \
+  else hipLaunchKernelGGL((k_indexer_bf16<NHV, 1>), grid, dim3(256), 0, s, ia)
   switch (d.n_hI) {
     case 64: IX_LAUNCH(64); break;
     case 32: IX_LAUNCH(32); break;

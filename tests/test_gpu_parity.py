@@ -321,12 +321,14 @@ def test_hca_dense_attend_small():
     _run_index_attend_and_check(cfg, dims, cache, qs, W, q_seq, q_pos, taus)
 
 
-def test_q_forward_end_to_end():
+@pytest.mark.parametrize("idx_fmt", ["e4m3", "mxfp4"])
+def test_q_forward_end_to_end(idx_fmt):
     """Compress a 600-token prefix in chunks, then a 96-token forward chunk (compress +
     index + top-k + attend) on 2 sequences; the oracle builds its own cache from the same
     hidden states.  Queries whose selection differs only through ties or a stored-code flip
-    are checked for validity on the GPU's selection."""
-    cfg = _qcfg()
+    are checked for validity on the GPU's selection.  The chunk's queries take the tiled
+    (prefill) indexer, with E4M3 or MXFP4 keys."""
+    cfg = _qcfg(idx_fmt=idx_fmt)
     dims = L.Dims.from_config(cfg)
     od = oracle_dims(cfg)
     B, n0, T = 2, 600, 96
@@ -489,14 +491,15 @@ def test_c5_hca_decode_full_size():
     _decode_full("c5")
 
 
-def test_c4_prefill_full_size_sampled():
+@pytest.mark.parametrize("idx_fmt", ["e4m3", "mxfp4"])
+def test_c4_prefill_full_size_sampled(idx_fmt):
     """Flash chunked prefill at full size: a 32768-token chunk after a 1048576-token prefix
     (262144 entries).  The prefix cache, its window ring and the projection state of the
     block before the chunk (zeros) are inputs given to both sides; csa_forward compresses the
     chunk (8192 new entries), scores every query against up to 270335 entries, selects 512 and
     attends.  Sampled queries across the chunk are checked against the oracle, which folds
-    the chunk's entries from the same hidden states."""
-    cfg = synth.config("c4a")
+    the chunk's entries from the same hidden states.  Indexer keys in E4M3 or MXFP4."""
+    cfg = dict(synth.config("c4a"), idx_fmt=idx_fmt)
     dims = L.Dims.from_config(cfg)
     od = oracle_dims(cfg)
     m, k, T, p0 = cfg["m"], cfg["top_k"], cfg["T"], cfg["prefix"]
@@ -542,7 +545,11 @@ def test_c4_prefill_full_size_sampled():
     check_stored_codes(g_new[:, :c - r], fin[:, :c - r], "e4m3", "c4 new entries/nope")
     check_stored_codes(g_new[:, c - r:], fin[:, c - r:], "bf16", "c4 new entries/rope")
     g_ki_new = keys_of(cache, 0, N0, cap, cfg)
-    check_stored_codes(g_ki_new, kpre, "e4m3", "c4 new keys")
+    if idx_fmt == "mxfp4":
+        check_stored_mxfp4(cache.ki_codes[0, N0:cap].cpu().numpy(), cache.ki_scales[0, N0:cap].cpu().numpy(),
+                           kpre, "c4 new keys")
+    else:
+        check_stored_codes(g_ki_new, kpre, "e4m3", "c4 new keys")
     entries = np.concatenate([prefix_entries, ent_new])
     ki = np.concatenate([prefix_ki, ki_new])
     g_entries = np.concatenate([prefix_entries, g_new])
