@@ -45,6 +45,10 @@ __device__ __forceinline__ f32x4 mfma_fp4(const uint4& a, int sa, const uint4& b
                                                           0, sb);
 }
 
+// ReLU of an MFMA result as one integer max on its bits: negative floats (and -0) are
+// negative integers.  (fmaxf would first canonicalize its operand, a second instruction.)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // The value of the lane 32 (16) apart, for a float64.
 __device__ __forceinline__ double lane_xor32_d(double x) {
   const uint64_t u = __builtin_bit_cast(uint64_t, x);
@@ -77,7 +81,7 @@ __device__ __forceinline__ double head_sum_f64(const uint4 (&qa)[HT], const int 
   for (int ht = 0; ht < HT; ++ht) {
     const f32x4 acc = mfma_fp4(qa[ht], qs[ht], b, bs);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) part = fma(W[ht][e], (double)fmaxf(acc[e], 0.f), part);
+    for (int e = 0; e < 4; ++e) part = fma(W[ht][e], (double)relu(acc[e]), part);
   }
   return part;
 }
@@ -212,7 +216,7 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
           for (int ks = 0; ks < 4; ++ks)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[qq][ht][ks], Bop[ks], acc, 0, 0, 0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) part = fmaf(W[qq][ht][e], fmaxf(acc[e], 0.f), part);
+          for (int e = 0; e < 4; ++e) part = fmaf(W[qq][ht][e], relu(acc[e]), part);
         }
         // lane groups summed as (g + g^2) + (g^1 + g^3), the order the tiled kernel uses
         part += lane_xor32(part);
@@ -438,7 +442,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) p = fmaf(W[qq][ht][e], fmaxf(acc[qq][ht][e], 0.f), p);
+            for (int e = 0; e < 4; ++e) p = fmaf(W[qq][ht][e], relu(acc[qq][ht][e]), p);
           part[t][qq] = p;
         }
       }
@@ -550,41 +554,62 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   gload(0, nv, ns);
   lstore(0, nv, ns);
   __syncthreads();
+  // A unit is (tile t of the stage, query qq), u = 2t + qq.  Software pipeline over the
+  // units: the MFMAs of unit u + 1 are issued before the epilogue of unit u, so the matrix
+  // cores run while the vector ALUs sum the heads (the epilogue is the larger part).
+  constexpr int NT = IF_STAGE / 16, NU = 2 * NT;
   for (int st = 0; st < nst; ++st) {
     if (st + 1 < nst) gload(st + 1, nv, ns);
     const uint8_t* kb = kbuf[st & 1];
     const uint8_t* sb = sbuf[st & 1];
+    // the stage's key operands: the lane's block of entry 16t + col, read once per tile
+    uint4 b[NT];
+    int bs[NT];
 #pragma unroll
-    for (int sub = 0; sub < IF_STAGE / 64; ++sub) {
-      // part[t][qq]: tile t of this 64-entry run, query qq, the lane's 16 heads
-      double part[4][2];
+    for (int t = 0; t < NT; ++t) {
+      const int r = t * 16 + col;
+      b[t] = *reinterpret_cast<const uint4*>(kb + r * IF_RS + g * 16);
+      bs[t] = sb[r * KS + g];
+    }
+    f32x4 acc[2][HT];
+    auto mm = [&](int u, f32x4 (&a)[HT]) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = sub * 64 + t * 16 + col;
-        const uint4 b = *reinterpret_cast<const uint4*>(kb + r * IF_RS + g * 16);
-        const int bs = sb[r * KS + g];
+      for (int ht = 0; ht < HT; ++ht) a[ht] = mfma_fp4(qa[u & 1][ht], qs[u & 1][ht], b[u >> 1], bs[u >> 1]);
+    };
+    // part[t][qq]: tile t of the current 64-entry run, query qq, the lane's 16 heads
+    double part[4][2];
+    mm(0, acc[0]);
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq) part[t][qq] = head_sum_f64<HT>(qa[qq], qs[qq], W[qq], b, bs);
-      }
-      // reduce-scatter over the lane groups as in k_indexer_tile: lane (col, g) ends with entry
-      // g * 16 + col of the run, summed over all 64 heads
+    for (int u = 0; u < NU; ++u) {
+      if (u + 1 < NU) mm(u + 1, acc[(u + 1) & 1]);
+      const int qq = u & 1, t = (u >> 1) & 3;
+      // the head sum of head_sum_f64, in the same order
+      double p = 0.0;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p = fma(W[qq][ht][e], (double)relu(acc[u & 1][ht][e]), p);
+      part[t][qq] = p;
+      if ((u & 7) != 7) continue;
+      // a 64-entry run is complete: reduce-scatter over the lane groups as in k_indexer_tile,
+      // so lane (col, g) ends with entry g * 16 + col of the run, summed over all 64 heads
       const bool hi2 = g >= 2, odd = g & 1;
       double r1[2][2];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-          const double keep = hi2 ? part[2 + j][qq] : part[j][qq];
-          const double send = hi2 ? part[j][qq] : part[2 + j][qq];
-          r1[j][qq] = keep + lane_xor32_d(send);
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const double keep = hi2 ? part[2 + j][q2] : part[j][q2];
+          const double send = hi2 ? part[j][q2] : part[2 + j][q2];
+          r1[j][q2] = keep + lane_xor32_d(send);
         }
-      const int s = e_lo + st * IF_STAGE + sub * 64 + g * 16 + col;
+      const int s = e_lo + st * IF_STAGE + (u >> 3) * 64 + g * 16 + col;
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
-        const double keep = odd ? r1[1][qq] : r1[0][qq];
-        const double send = odd ? r1[0][qq] : r1[1][qq];
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const double keep = odd ? r1[1][q2] : r1[0][q2];
+        const double send = odd ? r1[0][q2] : r1[1][q2];
         const double total = keep + lane_xor16_d(send);
-        if (s < min(V[qq], e_hi)) scores[(size_t)(qt0 + 2 * wave + qq) * ld + s] = bf16_nearest_from_f64(total);
+        if (s < min(V[q2], e_hi)) scores[(size_t)(qt0 + 2 * wave + q2) * ld + s] = bf16_nearest_from_f64(total);
       }
     }
     if (st + 1 < nst) lstore((st + 1) & 1, nv, ns);
