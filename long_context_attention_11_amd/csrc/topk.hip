@@ -501,7 +501,7 @@ struct FinalShared {
 
 // The candidates (N <= TK_THREADS * E, in index order) into E items per thread; select k.
 template <int E>
-__device__ int final_fast(int q, int nseg, int cs, int N, int k, const int32_t* __restrict__ cand_idx,
+__device__ __forceinline__ int final_fast(int q, int nseg, int cs, int N, int k, const int32_t* __restrict__ cand_idx,
                           const uint32_t* __restrict__ cand_key, FinalShared& fs, int32_t* out) {
   const int tid = threadIdx.x;
   ListItems<E> it;
