@@ -289,6 +289,70 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
                 const void* wI, const float* gamma_q, const float* sink, void* out,
                 int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * The projections around the attention core: the low-rank query path before it (reading
+ * notes "DeepSeekV4技术报告阅读笔记" §2.3.2 eqs. 13-15 and §2.3.3 eq. 18: one latent
+ * c^Q = h W^DQ of width d_c feeds both the attention queries q = c^Q W^UQ and the indexer
+ * queries q^I = c^Q W^IUQ; the indexer head weights are w = h W^w) and the grouped output
+ * projection after it (§2.3.3, "Grouped Output Projection"; deep dive "DeepSeek-V4 架构设计深度
+ * 解析" stage three: the n_h heads form g consecutive groups, group i's c n_h / g values are
+ * projected to d_g by its own map, and the g d_g concatenated values are projected to d;
+ * g = 16 (Pro) or 8 (Flash), d_g = 1024; explainer "DeepSeek V4 架构解读" §2.2: d_c = 1536).
+ * Every matrix W in R^{a x b} is stored transposed, bf16 [b][a] (one row per output column,
+ * the a inputs contiguous).  The weights are the caller's; the library only reads them.
+ */
+typedef struct csa_proj_weights {
+  const void* w_dq;   /* [d_c][d] bf16: W^DQ */
+  const void* w_uq;   /* [n_h * c][d_c] bf16: W^UQ */
+  const void* w_iuq;  /* [n_hI * c_I][d_c] bf16: W^IUQ (CSA; not read when dual = 0) */
+  const void* w_w;    /* [n_hI][d] bf16: W^w (CSA; not read when dual = 0) */
+  const void* w_og;   /* [g][d_g][n_h * c / g] bf16: group i's map at w_og + i d_g (n_h c / g) */
+  const void* w_o;    /* [d][g * d_g] bf16: the map of the concatenated groups to d */
+  int32_t d_c;        /* latent width, a multiple of 64 */
+  int32_t g;          /* output groups: divides n_h, with c n_h / g a multiple of 64 */
+  int32_t d_g;        /* width of a group's projection, a multiple of 64 */
+} csa_proj_weights;
+
+/*
+ * Bytes of workspace csa_query_project needs for T tokens (0 on invalid arguments).
+ */
+size_t csa_query_project_workspace_size(const csa_dims* dims, const csa_proj_weights* pw,
+                                        int32_t T);
+
+/*
+ * The query side for T tokens, formats act BF16 (with kv E4M3_BF16):
+ *   h   [T][d] bf16 hidden states (device).
+ *   q   [T][n_h][c] bf16 out: the attention queries, as csa_attend reads them.
+ *   qI  [T] rows out in the indexer's format (idx_fmt E4M3: [n_hI][c_I] codes; MXFP4: n_hI
+ *       rows of c_I / 2 element bytes then n_hI rows of c_I / 32 scale codes, the encoding
+ *       of the keys), as csa_index_topk reads them.  CSA only; NULL when dual = 0.
+ *   w   [T][n_hI] bf16 out: the indexer head weights.  CSA only; NULL when dual = 0.
+ * c^Q is held in bf16 between the two products; accumulation is float32.  ws (device,
+ * csa_query_project_workspace_size bytes) holds c^Q and split-K partial sums.
+ * Errors: INVALID_ARGUMENT (null pointer, T < 1), UNSUPPORTED (formats or widths outside the
+ * above), WORKSPACE_TOO_SMALL, HIP_ERROR.
+ */
+int csa_query_project(const csa_dims* dims, const csa_proj_weights* pw, const void* h,
+                      int32_t T, void* q, void* qI, void* w, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/*
+ * Bytes of workspace csa_output_project needs for T tokens (0 on invalid arguments).
+ */
+size_t csa_output_project_workspace_size(const csa_dims* dims, const csa_proj_weights* pw,
+                                         int32_t T);
+
+/*
+ * The grouped output projection for T tokens:
+ *   o    [T][n_h][c] bf16 attention output (device; csa_attend's out).
+ *   out  [T][d] bf16 out.
+ * The g d_g concatenated group outputs are held in bf16 before the last product;
+ * accumulation is float32.  ws as csa_output_project_workspace_size.
+ * Errors: as csa_query_project.
+ */
+int csa_output_project(const csa_dims* dims, const csa_proj_weights* pw, const void* o,
+                       int32_t T, void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,8 @@ __all__ = [
     "lib_path", "load", "Dims", "Cache", "Weights", "CsaError",
     "csa_abi_version", "csa_row_bytes", "csa_state_width", "csa_state_rows",
     "csa_workspace_size", "csa_compress", "csa_index_topk", "csa_attend", "csa_forward",
-    "csa_index_scores", "csa_topk", "csa_topk_workspace_size", "OP_COMPRESS", "OP_INDEX_TOPK", "OP_ATTEND", "OP_FORWARD",
+    "csa_index_scores", "csa_topk", "csa_topk_workspace_size", "ProjWeights", "csa_query_project",
+    "csa_query_project_workspace_size", "csa_output_project", "csa_output_project_workspace_size", "OP_COMPRESS", "OP_INDEX_TOPK", "OP_ATTEND", "OP_FORWARD",
     "FMT_F32", "FMT_BF16", "FMT_E4M3", "FMT_E4M3_BF16", "FMT_MXFP4", "EXPORTED_SYMBOLS",
 ]
 
@@ -30,7 +31,8 @@ EXPORTED_SYMBOLS = (
     "csa_abi_version", "csa_status_string", "csa_last_error", "csa_row_bytes",
     "csa_state_width", "csa_state_rows", "csa_workspace_size", "csa_compress",
     "csa_index_topk", "csa_attend", "csa_forward", "csa_index_scores", "csa_topk",
-    "csa_topk_workspace_size",
+    "csa_topk_workspace_size", "csa_query_project", "csa_query_project_workspace_size",
+    "csa_output_project", "csa_output_project_workspace_size",
 )
 
 
@@ -50,6 +52,11 @@ class _Dims(ctypes.Structure):
 class _Weights(ctypes.Structure):
     _fields_ = [("w_kv", ctypes.c_void_p), ("w_idx", ctypes.c_void_p), ("bias", ctypes.c_void_p),
                 ("bias_idx", ctypes.c_void_p), ("gamma_kv", ctypes.c_void_p)]
+
+
+class _ProjWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_dq", "w_uq", "w_iuq", "w_w", "w_og", "w_o")] + [
+        (n, ctypes.c_int32) for n in ("d_c", "g", "d_g")]
 
 
 class _Cache(ctypes.Structure):
@@ -103,6 +110,15 @@ def load():
     lib.csa_forward.restype = ctypes.c_int
     lib.csa_forward.argtypes = [dims_p, ctypes.POINTER(_Weights), ctypes.POINTER(_Cache), P, I32, P,
                                 P, P, P, P, P, P, P, P, SZ, P]
+    pw_p = ctypes.POINTER(_ProjWeights)
+    lib.csa_query_project_workspace_size.restype = SZ
+    lib.csa_query_project_workspace_size.argtypes = [dims_p, pw_p, I32]
+    lib.csa_query_project.restype = ctypes.c_int
+    lib.csa_query_project.argtypes = [dims_p, pw_p, P, I32, P, P, P, P, SZ, P]
+    lib.csa_output_project_workspace_size.restype = SZ
+    lib.csa_output_project_workspace_size.argtypes = [dims_p, pw_p, I32]
+    lib.csa_output_project.restype = ctypes.c_int
+    lib.csa_output_project.argtypes = [dims_p, pw_p, P, I32, P, P, SZ, P]
     _lib = lib
     return lib
 
@@ -318,3 +334,38 @@ def csa_forward(dims: Dims, w: Weights, cache: Cache, H, T: int, pos0, q, qI, wI
                               ctypes.byref(cache.struct()), _ptr(H), T, _ptr(pos0), _ptr(q),
                               _ptr(qI), _ptr(wI), _ptr(gamma_q), _ptr(sink), _ptr(out),
                               _ptr(idx_out), wp, wn, _stream(stream)))
+
+
+class ProjWeights:
+    """Weights of the projections around the path (csa_proj_weights in csa.h), bf16, each
+    matrix stored transposed: ``w_dq`` [d_c][d], ``w_uq`` [n_h c][d_c], ``w_iuq``
+    [n_hI c_I][d_c], ``w_w`` [n_hI][d], ``w_og`` [g][d_g][c n_h / g], ``w_o`` [d][g d_g]."""
+
+    def __init__(self, w_dq, w_uq, w_iuq, w_w, w_og, w_o):
+        self.w_dq, self.w_uq, self.w_iuq, self.w_w, self.w_og, self.w_o = w_dq, w_uq, w_iuq, w_w, w_og, w_o
+        self.d_c = int(w_dq.shape[0])
+        self.g, self.d_g = int(w_og.shape[0]), int(w_og.shape[1])
+
+    def struct(self) -> _ProjWeights:
+        return _ProjWeights(_ptr(self.w_dq), _ptr(self.w_uq), _ptr(self.w_iuq), _ptr(self.w_w), _ptr(self.w_og),
+                            _ptr(self.w_o), self.d_c, self.g, self.d_g)
+
+
+def csa_query_project_workspace_size(dims: Dims, pw: ProjWeights, T: int) -> int:
+    return load().csa_query_project_workspace_size(ctypes.byref(dims.struct()), ctypes.byref(pw.struct()), T)
+
+
+def csa_query_project(dims: Dims, pw: ProjWeights, h, T: int, q, qI, w, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check(load().csa_query_project(ctypes.byref(dims.struct()), ctypes.byref(pw.struct()), _ptr(h), T, _ptr(q),
+                                    _ptr(qI), _ptr(w), wp, wn, _stream(stream)))
+
+
+def csa_output_project_workspace_size(dims: Dims, pw: ProjWeights, T: int) -> int:
+    return load().csa_output_project_workspace_size(ctypes.byref(dims.struct()), ctypes.byref(pw.struct()), T)
+
+
+def csa_output_project(dims: Dims, pw: ProjWeights, o, T: int, out, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check(load().csa_output_project(ctypes.byref(dims.struct()), ctypes.byref(pw.struct()), _ptr(o), T, _ptr(out),
+                                     wp, wn, _stream(stream)))

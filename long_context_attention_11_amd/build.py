@@ -13,7 +13,7 @@ import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["csa_api.cpp", "compress.hip", "indexer.hip", "topk.hip", "attend.hip"]
+SOURCES = ["csa_api.cpp", "compress.hip", "indexer.hip", "topk.hip", "attend.hip", "proj.hip"]
 LIB = os.path.join(HERE, "libcsa.so")
 ARCH = "gfx950"
 

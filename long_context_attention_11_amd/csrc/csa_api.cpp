@@ -449,4 +449,62 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
   return CSA_OK;
 }
 
+// ------------------------------------------------------------------ projections around the path
+
+static int check_proj(const csa_dims* dims, const csa_proj_weights* pw, int32_t T) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!pw) return fail(CSA_ERR_INVALID_ARGUMENT, "projection weights are NULL");
+  if (T < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "T must be >= 1");
+  if (dims->act_fmt != CSA_FMT_BF16)
+    return fail(CSA_ERR_UNSUPPORTED, "the projections are built for act BF16");
+  if (pw->d_c < 64 || pw->d_c % 64) return fail(CSA_ERR_UNSUPPORTED, "d_c must be a positive multiple of 64");
+  if (pw->g < 1 || dims->n_h % pw->g || (dims->n_h * dims->c / pw->g) % 64)
+    return fail(CSA_ERR_UNSUPPORTED, "g must divide n_h with c n_h / g a multiple of 64");
+  if (pw->d_g < 64 || pw->d_g % 64) return fail(CSA_ERR_UNSUPPORTED, "d_g must be a positive multiple of 64");
+  return CSA_OK;
+}
+
+size_t csa_query_project_workspace_size(const csa_dims* dims, const csa_proj_weights* pw, int32_t T) {
+  if (check_proj(dims, pw, T) != CSA_OK) return 0;
+  return csa::query_project_ws_bytes(*dims, pw->d_c, T);
+}
+
+int csa_query_project(const csa_dims* dims, const csa_proj_weights* pw, const void* h, int32_t T, void* q,
+                      void* qI, void* w, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_proj(dims, pw, T);
+  if (st) return st;
+  if (!h || !q || !pw->w_dq || !pw->w_uq)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "h, q, w_dq and w_uq must be set");
+  if (dims->dual && (!qI || !w || !pw->w_iuq || !pw->w_w))
+    return fail(CSA_ERR_INVALID_ARGUMENT, "CSA needs qI, w, w_iuq and w_w");
+  const size_t need = csa::query_project_ws_bytes(*dims, pw->d_c, T);
+  if (!ws || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "query projection needs " + std::to_string(need) + " bytes of workspace");
+  hipError_t e = csa::launch_query_project(*dims, *pw, h, T, q, qI, w, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "query projection launch");
+  return CSA_OK;
+}
+
+size_t csa_output_project_workspace_size(const csa_dims* dims, const csa_proj_weights* pw, int32_t T) {
+  if (check_proj(dims, pw, T) != CSA_OK) return 0;
+  return csa::output_project_ws_bytes(*dims, pw->g, pw->d_g, T);
+}
+
+int csa_output_project(const csa_dims* dims, const csa_proj_weights* pw, const void* o, int32_t T, void* out,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_proj(dims, pw, T);
+  if (st) return st;
+  if (!o || !out || !pw->w_og || !pw->w_o)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "o, out, w_og and w_o must be set");
+  const size_t need = csa::output_project_ws_bytes(*dims, pw->g, pw->d_g, T);
+  if (!ws || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "output projection needs " + std::to_string(need) + " bytes of workspace");
+  hipError_t e = csa::launch_output_project(*dims, *pw, o, T, out, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "output projection launch");
+  return CSA_OK;
+}
+
 }  // extern "C"

@@ -260,4 +260,12 @@ int32_t state_width(const csa_dims& d);
 int32_t state_rows(const csa_dims& d);
 size_t row_bytes(const csa_dims& d);
 
+// proj.hip: the query-side and grouped output projections
+size_t query_project_ws_bytes(const csa_dims& d, int32_t d_c, int32_t T);
+size_t output_project_ws_bytes(const csa_dims& d, int32_t g, int32_t d_g, int32_t T);
+hipError_t launch_query_project(const csa_dims& d, const csa_proj_weights& w, const void* h, int32_t T,
+                                void* q, void* qI, void* wI, void* ws, hipStream_t s);
+hipError_t launch_output_project(const csa_dims& d, const csa_proj_weights& w, const void* o, int32_t T,
+                                 void* out, void* ws, hipStream_t s);
+
 }  // namespace csa

@@ -1,0 +1,376 @@
+// The projections around the attention core, for gfx950:
+//   query side   c^Q = h W^DQ, q = c^Q W^UQ, q^I = c^Q W^IUQ, w = h W^w
+//   output side  the grouped output projection: heads in g consecutive groups, group i's
+//                c n_h / g values projected to d_g by its own map, the g results
+//                concatenated and projected to d
+// (reading notes "DeepSeekV4技术报告阅读笔记" §2.3.2 eqs. 13-15, §2.3.3 eq. 18 and its grouped
+// output projection paragraph; deep dive "DeepSeek-V4 架构设计深度解析" stage three for g and
+// d_g; explainer "DeepSeek V4 架构解读" §2.2 for Pro's d_c = 1536.)
+//
+// All six maps are plain bf16 GEMMs with float32 accumulation on MFMA.  One kernel serves
+// them: 64x64 output tiles, BK = 64 stages double buffered in LDS, a group index (the g
+// group maps of the output side run in one launch) and split-K for short inputs, whose
+// partials finishing kernels sum in a fixed order.  Weights are stored one row per output
+// column ([N][K], K contiguous), the layout the tiles load with 16-byte reads.
+#include "csa_internal.h"
+
+namespace csa {
+namespace {
+
+constexpr int GM_BM = 64, GM_BN = 64, GM_BK = 64, GM_LD = GM_BK + 8;  // LDS row pitch (bf16)
+constexpr int GM_ROWS = 8192;   // rows per pass of the host loops (bounds the workspace)
+
+struct GemmArgs {
+  const uint16_t* A;   // [M][lda]; group z reads columns z * a_zoff .. + K
+  int64_t lda, a_zoff;
+  const uint16_t* B;   // weight rows n < nb1: B + n * ldb (+ z * b_zstride) ...
+  const uint16_t* B2;  // ... rows n >= nb1: B2 + (n - nb1) * ldb
+  int nb1;
+  int64_t ldb, b_zstride;
+  int M, N, K, kchunk, ksplit;
+  int n_bf;            // columns n < n_bf are stored to D in bfloat16 (ksplit == 1 only)
+  uint16_t* D;
+  int64_t ldd, d_zoff;
+  float* P;            // columns n >= n_bf: P[ks * p_ks + row * ldp + z * p_zoff + n - n_bf]
+  int64_t ldp, p_zoff, p_ks;
+};
+
+// blockIdx = (column tile, row tile, z * ksplit + ks); 4 waves, each a 32x32 quarter of the
+// tile as 2x2 MFMA 16x16x32 tiles.
+__global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][GM_BM * GM_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GM_BN * GM_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.y * GM_BM, n0 = blockIdx.x * GM_BN;
+  const int z = blockIdx.z / g.ksplit, ks = blockIdx.z % g.ksplit;
+  const int k_begin = ks * g.kchunk, k_end = min(g.K, k_begin + g.kchunk);
+  // loader: a stage is 64 rows x 64 k of each operand, 512 pieces of 8 bf16; 2 per thread
+  const int lr = tid >> 3, lc = (tid & 7) * 8;
+  const uint16_t* arow[2];
+  const uint16_t* brow[2];
+  bool aval[2], bval[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = lr + 32 * h;
+    aval[h] = m0 + r < g.M;
+    arow[h] = g.A + (size_t)min(m0 + r, g.M - 1) * g.lda + (size_t)z * g.a_zoff;
+    const int n = min(n0 + r, g.N - 1);
+    bval[h] = n0 + r < g.N;
+    brow[h] = (n < g.nb1 ? g.B + (size_t)n * g.ldb : g.B2 + (size_t)(n - g.nb1) * g.ldb) +
+              (size_t)z * g.b_zstride;
+  }
+  uint4 ra[2], rb[2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ra[h] = aval[h] ? *reinterpret_cast<const uint4*>(arow[h] + k0 + lc) : make_uint4(0, 0, 0, 0);
+      rb[h] = bval[h] ? *reinterpret_cast<const uint4*>(brow[h] + k0 + lc) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<uint4*>(&As[buf][(lr + 32 * h) * GM_LD + lc]) = ra[h];
+      *reinterpret_cast<uint4*>(&Bs[buf][(lr + 32 * h) * GM_LD + lc]) = rb[h];
+    }
+  };
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const int fr = lane & 15, fg = lane >> 4;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+  int buf = 0;
+  if (k_begin < k_end) gload(k_begin);
+  for (int k0 = k_begin; k0 < k_end; k0 += GM_BK) {
+    sstore(buf);
+    __syncthreads();
+    if (k0 + GM_BK < k_end) gload(k0 + GM_BK);
+#pragma unroll
+    for (int kk = 0; kk < GM_BK; kk += 32) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm + 16 * i + fr) * GM_LD + kk + fg * 8]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(wn + 16 * j + fr) * GM_LD + kk + fg * 8]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    buf ^= 1;
+  }
+  // an MFMA 16x16 result: lane holds column (lane & 15), rows 4 (lane >> 4) + e
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn + 16 * j + fr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + wm + 16 * i + 4 * fg + e;
+        if (row >= g.M || col >= g.N) continue;
+        if (col < g.n_bf)
+          g.D[(size_t)row * g.ldd + (size_t)z * g.d_zoff + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][e]);
+        else
+          g.P[(size_t)ks * g.p_ks + (size_t)row * g.ldp + (size_t)z * g.p_zoff + (col - g.n_bf)] = acc[i][j][e];
+      }
+    }
+}
+
+// Split-K partials of an fp32 block [M][ncol] (row pitch ldp, partial pitch p_ks) summed in
+// partial order and stored in bfloat16 to D [M][ldd].
+__global__ __launch_bounds__(256) void k_sum_bf16(const float* __restrict__ P, int ksplit, int64_t p_ks,
+                                                  int M, int ncol, int64_t ldp, uint16_t* __restrict__ D,
+                                                  int64_t ldd) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)M * ncol) return;
+  const int r = (int)(i / ncol), c = (int)(i % ncol);
+  float s = 0.f;
+  for (int k = 0; k < ksplit; ++k) s += P[(size_t)k * p_ks + (size_t)r * ldp + c];
+  D[(size_t)r * ldd + c] = (uint16_t)f32_to_bf16_bits(s);
+}
+
+// q^I: split-K partials summed, then stored in the indexer's format.  One thread per block of
+// 32 dims of one head.  E4M3: [n_hI][c_I] codes per query.  MXFP4: per query n_hI rows of
+// c_I / 2 element bytes (dim 2i in the low nibble), then n_hI rows of c_I / 32 scale codes;
+// the block scale is 2^(floor(log2 max|v|) - 2) (1 for an all-zero block), the elements the
+// nearest E2M1 values of v / scale, ties to even, saturating at 6.
+__global__ __launch_bounds__(256) void k_store_qI(const float* __restrict__ P, int ksplit, int64_t p_ks,
+                                                  int M, int64_t ldp, int n_hI, int c_I, int fmt,
+                                                  uint8_t* __restrict__ qI) {
+  const int nblk = c_I / 32;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)M * n_hI * nblk) return;
+  const int r = (int)(i / (n_hI * nblk)), rem = (int)(i % (n_hI * nblk));
+  const int h = rem / nblk, b = rem % nblk;
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const size_t col = (size_t)h * c_I + b * 32 + j;
+    float s = 0.f;
+    for (int k = 0; k < ksplit; ++k) s += P[(size_t)k * p_ks + (size_t)r * ldp + col];
+    v[j] = s;
+  }
+  if (fmt == CSA_FMT_MXFP4) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    int e = 0;
+    if (amax > 0.f) {
+      int ex;
+      frexpf(amax, &ex);   // amax = f 2^ex with f in [0.5, 1): floor(log2 amax) = ex - 1
+      e = min(127, max(-127, ex - 1 - 2));
+    }
+    const size_t row = (size_t)n_hI * (c_I / 2 + c_I / 32);
+    uint8_t* dst = qI + (size_t)r * row + (size_t)h * (c_I / 2) + b * 16;
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      w[j >> 2] |= (e2m1_code(ldexpf(v[2 * j], -e)) | (e2m1_code(ldexpf(v[2 * j + 1], -e)) << 4)) << (8 * (j & 3));
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    qI[(size_t)r * row + (size_t)n_hI * (c_I / 2) + (size_t)h * (c_I / 32) + b] = (uint8_t)(e + 127);
+  } else {
+    uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) w[j >> 2] |= f32_to_e4m3(v[j]) << (8 * (j & 3));
+    uint8_t* dst = qI + ((size_t)r * n_hI + h) * c_I + b * 32;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+// Split K for short inputs so that about 512 workgroups stream the weights; each K range
+// stays a multiple of the 64-deep stage and at least 256 long.
+int gemm_ksplit(int M, int N, int Z, int K) {
+  const int tiles = ((M + GM_BM - 1) / GM_BM) * ((N + GM_BN - 1) / GM_BN) * Z;
+  int ks = 1;
+  while (tiles * ks < 512 && K % (ks * 2 * GM_BK) == 0 && K / (ks * 2) >= 256) ks *= 2;
+  return ks;
+}
+
+// One GEMM plan: output columns [0, n_direct) go to D in bfloat16 when K is not split; the
+// rest (or all, when split) go to fp32 partials at P.
+struct Plan {
+  int ks;
+  int n_bf;
+  int64_t ldp;      // fp32 columns per row (all groups)
+  size_t p_floats;  // partial buffer size
+};
+
+Plan plan_of(int M, int N, int Z, int K, int n_direct) {
+  Plan p;
+  p.ks = gemm_ksplit(M, N, Z, K);
+  p.n_bf = p.ks == 1 ? n_direct : 0;
+  p.ldp = (int64_t)Z * (N - p.n_bf);
+  p.p_floats = (size_t)p.ks * M * p.ldp;
+  return p;
+}
+
+hipError_t launch_gemm(const GemmArgs& g, int Z, hipStream_t s) {
+  dim3 grid((g.N + GM_BN - 1) / GM_BN, (g.M + GM_BM - 1) / GM_BM, Z * g.ksplit);
+  hipLaunchKernelGGL(k_gemm_bf16, grid, dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_bf16(const float* P, int ks, int64_t p_ks, int M, int ncol, int64_t ldp, uint16_t* D,
+                           int64_t ldd, hipStream_t s) {
+  const int64_t n = (int64_t)M * ncol;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_sum_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, P, ks, p_ks, M, ncol, ldp,
+                     D, ldd);
+  return hipGetLastError();
+}
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Rows of the first and the last pass (the largest partial buffers come from one of them).
+template <typename F>
+size_t max_over_passes(int32_t T, F f) {
+  const int first = std::min<int32_t>(T, GM_ROWS);
+  const int last = T % GM_ROWS ? T % GM_ROWS : first;
+  return std::max(f(first), f(last));
+}
+
+size_t query_ws_rows(const csa_dims& d, int32_t d_c, int M) {
+  const int n1 = d_c + (d.dual ? d.n_hI : 0);
+  const int n2 = d.n_h * d.c + (d.dual ? d.n_hI * d.c_I : 0);
+  const Plan p1 = plan_of(M, n1, 1, d.d, d_c);
+  const Plan p2 = plan_of(M, n2, 1, d_c, d.n_h * d.c);
+  return align256((size_t)M * d_c * 2) + align256(p1.p_floats * 4) + align256(p2.p_floats * 4);
+}
+
+size_t output_ws_rows(const csa_dims& d, int32_t g, int32_t d_g, int M) {
+  const Plan p3 = plan_of(M, d_g, g, d.n_h * d.c / g, d_g);
+  const Plan p4 = plan_of(M, d.d, 1, g * d_g, d.d);
+  return align256((size_t)M * g * d_g * 2) + align256(p3.p_floats * 4) + align256(p4.p_floats * 4);
+}
+
+}  // namespace
+
+size_t query_project_ws_bytes(const csa_dims& d, int32_t d_c, int32_t T) {
+  return max_over_passes(T, [&](int M) { return query_ws_rows(d, d_c, M); });
+}
+
+size_t output_project_ws_bytes(const csa_dims& d, int32_t g, int32_t d_g, int32_t T) {
+  return max_over_passes(T, [&](int M) { return output_ws_rows(d, g, d_g, M); });
+}
+
+hipError_t launch_query_project(const csa_dims& d, const csa_proj_weights& w, const void* h, int32_t T,
+                                void* q, void* qI, void* wI, void* ws, hipStream_t s) {
+  const int d_c = w.d_c;
+  const int nq = d.n_h * d.c, nqI = d.dual ? d.n_hI * d.c_I : 0, nw = d.dual ? d.n_hI : 0;
+  const size_t qI_row = d.idx_fmt == CSA_FMT_MXFP4 ? (size_t)d.n_hI * (d.c_I / 2 + d.c_I / 32)
+                                                   : (size_t)d.n_hI * d.c_I;
+  for (int t0 = 0; t0 < T; t0 += GM_ROWS) {
+    const int M = std::min<int>(GM_ROWS, T - t0);
+    const Plan p1 = plan_of(M, d_c + nw, 1, d.d, d_c);
+    const Plan p2 = plan_of(M, nq + nqI, 1, d_c, nq);
+    char* base = static_cast<char*>(ws);
+    uint16_t* cQ = reinterpret_cast<uint16_t*>(base);
+    float* P1 = reinterpret_cast<float*>(base + align256((size_t)M * d_c * 2));
+    float* P2 = reinterpret_cast<float*>(base + align256((size_t)M * d_c * 2) + align256(p1.p_floats * 4));
+    // eqs. 13 and 15: [c^Q | w] = h [W^DQ | W^w]
+    GemmArgs g1{};
+    g1.A = static_cast<const uint16_t*>(h) + (size_t)t0 * d.d;
+    g1.lda = d.d;
+    g1.B = static_cast<const uint16_t*>(w.w_dq);
+    g1.B2 = static_cast<const uint16_t*>(w.w_w);
+    g1.nb1 = d_c;
+    g1.ldb = d.d;
+    g1.M = M, g1.N = d_c + nw, g1.K = d.d, g1.ksplit = p1.ks, g1.kchunk = d.d / p1.ks;
+    g1.n_bf = p1.n_bf, g1.D = cQ, g1.ldd = d_c;
+    g1.P = P1, g1.ldp = p1.ldp, g1.p_ks = (int64_t)M * p1.ldp;
+    hipError_t e = launch_gemm(g1, 1, s);
+    if (e != hipSuccess) return e;
+    if (p1.ks > 1) {
+      if ((e = launch_sum_bf16(P1, p1.ks, g1.p_ks, M, d_c, p1.ldp, cQ, d_c, s)) != hipSuccess) return e;
+    }
+    if (nw) {
+      const float* Pw = P1 + (d_c - p1.n_bf);   // the w columns of the partials
+      if ((e = launch_sum_bf16(Pw, p1.ks, g1.p_ks, M, nw, p1.ldp, static_cast<uint16_t*>(wI) + (size_t)t0 * nw,
+                               nw, s)) != hipSuccess)
+        return e;
+    }
+    // eqs. 18 and 14: [q | q^I] = c^Q [W^UQ | W^IUQ]
+    GemmArgs g2{};
+    g2.A = cQ;
+    g2.lda = d_c;
+    g2.B = static_cast<const uint16_t*>(w.w_uq);
+    g2.B2 = static_cast<const uint16_t*>(w.w_iuq);
+    g2.nb1 = nq;
+    g2.ldb = d_c;
+    g2.M = M, g2.N = nq + nqI, g2.K = d_c, g2.ksplit = p2.ks, g2.kchunk = d_c / p2.ks;
+    g2.n_bf = p2.n_bf, g2.D = static_cast<uint16_t*>(q) + (size_t)t0 * nq, g2.ldd = nq;
+    g2.P = P2, g2.ldp = p2.ldp, g2.p_ks = (int64_t)M * p2.ldp;
+    if ((e = launch_gemm(g2, 1, s)) != hipSuccess) return e;
+    if (p2.ks > 1) {
+      if ((e = launch_sum_bf16(P2, p2.ks, g2.p_ks, M, nq, p2.ldp, static_cast<uint16_t*>(q) + (size_t)t0 * nq, nq,
+                               s)) != hipSuccess)
+        return e;
+    }
+    if (nqI) {
+      const float* PqI = P2 + (nq - p2.n_bf);
+      const int64_t n = (int64_t)M * d.n_hI * (d.c_I / 32);
+      hipLaunchKernelGGL(k_store_qI, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, PqI, p2.ks, g2.p_ks, M,
+                         p2.ldp, d.n_hI, d.c_I, d.idx_fmt, static_cast<uint8_t*>(qI) + (size_t)t0 * qI_row);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_output_project(const csa_dims& d, const csa_proj_weights& w, const void* o, int32_t T, void* out,
+                                 void* ws, hipStream_t s) {
+  const int g = w.g, d_g = w.d_g, G = d.n_h * d.c / g, width = d.n_h * d.c;
+  for (int t0 = 0; t0 < T; t0 += GM_ROWS) {
+    const int M = std::min<int>(GM_ROWS, T - t0);
+    const Plan p3 = plan_of(M, d_g, g, G, d_g);
+    const Plan p4 = plan_of(M, d.d, 1, g * d_g, d.d);
+    char* base = static_cast<char*>(ws);
+    uint16_t* mid = reinterpret_cast<uint16_t*>(base);
+    float* P3 = reinterpret_cast<float*>(base + align256((size_t)M * g * d_g * 2));
+    float* P4 = reinterpret_cast<float*>(base + align256((size_t)M * g * d_g * 2) + align256(p3.p_floats * 4));
+    // group i: o[:, i G .. (i + 1) G] W^{O,i}, into columns i d_g .. of the concatenation
+    GemmArgs g3{};
+    g3.A = static_cast<const uint16_t*>(o) + (size_t)t0 * width;
+    g3.lda = width;
+    g3.a_zoff = G;
+    g3.B = static_cast<const uint16_t*>(w.w_og);
+    g3.nb1 = d_g;
+    g3.ldb = G;
+    g3.b_zstride = (int64_t)d_g * G;
+    g3.M = M, g3.N = d_g, g3.K = G, g3.ksplit = p3.ks, g3.kchunk = G / p3.ks;
+    g3.n_bf = p3.n_bf, g3.D = mid, g3.ldd = (int64_t)g * d_g, g3.d_zoff = d_g;
+    g3.P = P3, g3.ldp = p3.ldp, g3.p_zoff = d_g - p3.n_bf, g3.p_ks = (int64_t)M * p3.ldp;
+    hipError_t e = launch_gemm(g3, g, s);
+    if (e != hipSuccess) return e;
+    if (p3.ks > 1) {
+      if ((e = launch_sum_bf16(P3, p3.ks, g3.p_ks, M, g * d_g, p3.ldp, mid, (int64_t)g * d_g, s)) != hipSuccess)
+        return e;
+    }
+    // the concatenation to d
+    GemmArgs g4{};
+    g4.A = mid;
+    g4.lda = (int64_t)g * d_g;
+    g4.B = static_cast<const uint16_t*>(w.w_o);
+    g4.nb1 = d.d;
+    g4.ldb = (int64_t)g * d_g;
+    g4.M = M, g4.N = d.d, g4.K = g * d_g, g4.ksplit = p4.ks, g4.kchunk = g * d_g / p4.ks;
+    g4.n_bf = p4.n_bf, g4.D = static_cast<uint16_t*>(out) + (size_t)t0 * d.d, g4.ldd = d.d;
+    g4.P = P4, g4.ldp = p4.ldp, g4.p_ks = (int64_t)M * p4.ldp;
+    if ((e = launch_gemm(g4, 1, s)) != hipSuccess) return e;
+    if (p4.ks > 1) {
+      if ((e = launch_sum_bf16(P4, p4.ks, g4.p_ks, M, d.d, p4.ldp, static_cast<uint16_t*>(out) + (size_t)t0 * d.d,
+                               d.d, s)) != hipSuccess)
+        return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace csa

@@ -30,7 +30,7 @@ import math
 import torch
 
 __all__ = ["CONFIGS", "config", "generator", "randn", "mxfp4_random", "weights", "hidden", "queries",
-           "synthetic_cache", "row_bytes", "SEED"]
+           "synthetic_cache", "row_bytes", "proj_weights", "small_ints", "SEED"]
 
 SEED = 0
 
@@ -205,4 +205,33 @@ def synthetic_cache(cfg: dict, B: int, N: int, R: int, seed: int = SEED, device=
         out["ki"] = torch.cat([codes.view(B, -1), scales.view(B, -1)], dim=1).contiguous()
     elif cfg["dual"]:
         out["ki"] = _store(randn((B, N, cfg["c_I"]), 0.5, device, seed, "cki"), cfg["idx_fmt"])
+    return out
+
+
+def small_ints(shape, lo: int, hi: int, scale: float, device, *ids) -> torch.Tensor:
+    """float32 tensor of integers uniform in lo..hi times ``scale`` (a power of two), drawn
+    from a generator seeded by ``ids``: inputs whose sums of products stay exact in float32."""
+    g = generator(device, *ids)
+    return torch.randint(lo, hi + 1, shape, generator=g, device=device).to(torch.float32) * scale
+
+
+def proj_weights(cfg: dict, d_c: int, g: int, d_g: int, seed: int = SEED, device="cpu",
+                 exact_first: bool = False) -> dict:
+    """Weights of the projections around the path, bf16, each stored transposed ([out][in]):
+    w_dq [d_c][d], w_uq [n_h c][d_c], w_iuq [n_hI c_I][d_c], w_w [n_hI][d],
+    w_og [g][d_g][n_h c / g], w_o [d][g d_g]; N(0, 1/fan_in).  With ``exact_first`` the maps
+    applied first to their input (w_dq, w_w, w_og) take values k/64, k uniform in -2..2, so
+    that with small-integer inputs their float32 sums are exact."""
+    d, nq, nqI, nI = cfg["d"], cfg["n_h"] * cfg["c"], cfg["n_hI"] * cfg["c_I"], cfg["n_hI"]
+    G = nq // g
+    shapes = {"w_dq": (d_c, d), "w_uq": (nq, d_c), "w_iuq": (nqI, d_c), "w_w": (nI, d),
+              "w_og": (g, d_g, G), "w_o": (d, g * d_g)}
+    fan_in = {"w_dq": d, "w_uq": d_c, "w_iuq": d_c, "w_w": d, "w_og": G, "w_o": g * d_g}
+    out = {}
+    for i, (name, shp) in enumerate(shapes.items()):
+        if exact_first and name in ("w_dq", "w_w", "w_og"):
+            t = small_ints(shp, -2, 2, 1.0 / 64, device, seed, 700 + i)
+        else:
+            t = randn(shp, fan_in[name] ** -0.5, device, seed, 700 + i)
+        out[name] = t.to(torch.bfloat16)
     return out

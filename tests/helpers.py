@@ -188,3 +188,27 @@ def check_stored_codes(got_vals: np.ndarray, ref_pre: np.ndarray, fmt: str, what
     assert ok.all(), (f"{what}: {int((~ok).sum())} stored values outside the rounding of the oracle's "
                       f"value +- eps; first: got {got_vals[~ok][:3]}, oracle {mid[~ok][:3]}, pre {x[~ok][:3]}")
     return int((got_vals != mid).sum())
+
+
+def check_rounded(got_vals: np.ndarray, ref_pre: np.ndarray, bound: np.ndarray, rnd, what: str = "",
+                  max_flip_frac: float = 0.02) -> int:
+    """Stored values vs the oracle's pre-storage values: each stored value must be the
+    rounding (``rnd``, monotone) of some value within ``bound`` of the oracle's, i.e.
+    rnd(x - bound) <= got <= rnd(x + bound), and at most ``max_flip_frac`` of them may differ
+    from rnd(x).  Returns how many differ."""
+    x = np.asarray(ref_pre, np.float64)
+    b = np.asarray(bound, np.float64) * np.ones_like(x)
+    lo, hi, mid = rnd(x - b), rnd(x + b), rnd(x)
+    ok = (got_vals >= lo) & (got_vals <= hi)
+    assert ok.all(), (f"{what}: {int((~ok).sum())} of {ok.size} values outside the rounding of the oracle's "
+                      f"value +- bound; first: got {got_vals[~ok][:3]}, oracle {mid[~ok][:3]}")
+    flips = int((got_vals != mid).sum())
+    assert flips <= max_flip_frac * max(1, got_vals.size), f"{what}: {flips} of {got_vals.size} differ from the rounding"
+    return flips
+
+
+def sum_bound(a: np.ndarray, bT: np.ndarray, ksplit_max: int = 64) -> np.ndarray:
+    """Worst-case error of a float32 sum of the K products a[r, k] * bT[n, k] in any order
+    (MFMA accumulation plus split-K additions): (K + ksplit) 2^-24 sum_k |a b|."""
+    K = a.shape[-1]
+    return (K + ksplit_max) * 2.0 ** -24 * (np.abs(a) @ np.abs(bT).T)

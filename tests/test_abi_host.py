@@ -116,3 +116,38 @@ def test_workspace_sizes_are_consistent():
     chunked = L.csa_workspace_size(d, L.OP_FORWARD, B=1, T=32768, cap=270336, q_chunk=2048)
     assert chunked < full
     assert L.csa_workspace_size(d, L.OP_INDEX_TOPK, Q=16, cap=32768) >= 16 * 32768 * 4
+
+
+def test_projection_entry_points_reject_bad_arguments():
+    """csa_query_project / csa_output_project: argument checks fail on the host."""
+    lib = _lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: checks fail before any launch
+    d2 = L.Dims.from_config(synth.config("c2")).struct()
+
+    def pw(d_c=1536, g=8, d_g=1024):
+        return L._ProjWeights(fake, fake, fake, fake, fake, fake, d_c, g, d_g)
+
+    ok = pw()
+    need = lib.csa_query_project_workspace_size(ctypes.byref(d2), ctypes.byref(ok), 16)
+    assert need > 0
+    # widths the GEMM tiles do not take, and a g that does not divide the heads
+    for bad in (pw(d_c=100), pw(g=3), pw(d_g=1000), pw(g=0)):
+        assert lib.csa_query_project(ctypes.byref(d2), ctypes.byref(bad), fake, 16, fake, fake, fake, fake,
+                                     1 << 40, None) == 2
+        assert lib.csa_query_project_workspace_size(ctypes.byref(d2), ctypes.byref(bad), 16) == 0
+    # T = 0, missing outputs, too little workspace
+    assert lib.csa_query_project(ctypes.byref(d2), ctypes.byref(ok), fake, 0, fake, fake, fake, fake,
+                                 1 << 40, None) == 1
+    assert lib.csa_query_project(ctypes.byref(d2), ctypes.byref(ok), fake, 16, fake, None, fake, fake,
+                                 1 << 40, None) == 1
+    assert lib.csa_query_project(ctypes.byref(d2), ctypes.byref(ok), fake, 16, fake, fake, fake, fake,
+                                 need - 1, None) == 3
+    # fp32 activations are not built for the projections
+    d1 = L.Dims.from_config(synth.config("c1")).struct()
+    assert lib.csa_output_project(ctypes.byref(d1), ctypes.byref(pw(d_c=64, g=4, d_g=64)), fake, 4, fake,
+                                  fake, 1 << 40, None) == 2
+    need_o = lib.csa_output_project_workspace_size(ctypes.byref(d2), ctypes.byref(ok), 16)
+    assert need_o > 0
+    assert lib.csa_output_project(ctypes.byref(d2), ctypes.byref(ok), fake, 16, None, fake, 1 << 40, None) == 1
+    assert lib.csa_output_project(ctypes.byref(d2), ctypes.byref(ok), fake, 16, fake, fake, need_o - 1,
+                                  None) == 3
