@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--layer", action="store_true",
+                    help="decode configs: time the whole attention layer, the query-side projections "
+                         "before the path and the grouped output projection after it included")
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2fp4", "c3", "c4a", "c4b", "c4bfp4", "c5"])
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -332,15 +335,39 @@ def run_decode(args, cfg):
     phases = [k_compress, k_index, k_topk, k_attend] if dual else [k_compress, k_attend]
     ws_f = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_FORWARD, B=B, T=1, cap=N)), dtype=torch.uint8, device=dev)
 
+    if args.layer:
+        # the layer h -> output: query-side projections, the path, grouped output projection
+        PW = synth.proj_weights(cfg, cfg["d_c"], cfg["g"], cfg["d_g"], device=dev)
+        pw = L.ProjWeights(**PW)
+        h = H1.reshape(B, cfg["d"])
+        q_l = torch.empty_like(qs["q"])
+        qI_l = torch.empty_like(qs["qI"]) if dual else None
+        w_l = torch.empty_like(qs["w"]) if dual else None
+        y = torch.empty((B, cfg["d"]), dtype=torch.bfloat16, device=dev)
+        ws_q = torch.empty(max(1, L.csa_query_project_workspace_size(dims, pw, B)), dtype=torch.uint8, device=dev)
+        ws_o = torch.empty(max(1, L.csa_output_project_workspace_size(dims, pw, B)), dtype=torch.uint8, device=dev)
+
+        def k_qproj(c):
+            L.csa_query_project(dims, pw, h, B, q_l, qI_l, w_l, ws_q)
+
+        def k_oproj(c):
+            L.csa_output_project(dims, pw, out, B, y, ws_o)
+
     def step(c):
         # one pass of the whole path through the library's forward entry point
+        if args.layer:
+            k_qproj(c)
+            L.csa_forward(dims, lw, c, H1, 1, pos0, q_l, qI_l, w_l, W["gamma_q"], W["sink"], out,
+                          idx if dual else None, ws_f)
+            k_oproj(c)
+            return
         L.csa_forward(dims, lw, c, H1, 1, pos0, qs["q"], qs["qI"] if dual else None,
                       qs["w"] if dual else None, W["gamma_q"], W["sink"], out,
                       idx if dual else None, ws_f)
 
     step(caches[0])
     torch.cuda.synchronize()
-    ref = (out.clone(), idx.clone() if dual else None)
+    ref = (y.clone() if args.layer else out.clone(), idx.clone() if dual else None)
     steps = args.steps or 200
     warm = args.warmup if args.warmup is not None else 10
     G = len(caches)
@@ -361,14 +388,17 @@ def run_decode(args, cfg):
     run_steps(steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ok = torch.equal(out, ref[0]) and (not dual or torch.equal(idx, ref[1]))
+    ok = torch.equal(y if args.layer else out, ref[0]) and (not dual or torch.equal(idx, ref[1]))
 
     # per-kernel launch durations (same inputs and grids, rotating cache copies)
     kt = {name: kernel_time_us([lambda c=c, f=f: f(c) for c in caches])
           for name, f in zip(["compress", "index_scores", "topk", "attend"] if dual else ["compress", "attend"], phases)}
+    if args.layer:
+        kt["q_proj"] = kernel_time_us([lambda c=c: k_qproj(c) for c in caches])
+        kt["o_proj"] = kernel_time_us([lambda c=c: k_oproj(c) for c in caches])
     res = {
-        "metric": ("CSA decode queries/s (Flash-shaped, 128K context, batch 16)" if cfg["name"] == "c2"
-                   else f"CSA decode queries/s ({cfg['name']})"),
+        "metric": ("CSA decode queries/s (Flash-shaped, 128K context, batch 16)" if cfg["name"] == "c2" and not args.layer
+                   else f"CSA {'attention-layer ' if args.layer else ''}decode queries/s ({cfg['name']})"),
         "value": round(B * steps / wall, 1), "unit": "queries/s", "n_gpus": 1, "steps": steps,
         "warmup": warm, "ms_per_step": round(wall / steps * 1e3, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
@@ -406,10 +436,24 @@ def run_decode(args, cfg):
                   "128 heads x 512, indexer 64x128, top-k 1024, n_win 128",
             "c5": "HCA decode, 8 seqs x 1048576-token context (8192 entries, m'=128), d=4096, "
                   "64 heads x 512, dense, n_win 128"}[cfg["name"]]
+    if args.layer:
+        # the projections stream their weights once per step: HBM-bound at decode
+        d, dc, nq = cfg["d"], cfg["d_c"], cfg["n_h"] * cfg["c"]
+        wq = 2 * (dc * d + nq * dc + ((cfg["n_hI"] * cfg["c_I"] * dc + cfg["n_hI"] * d) if dual else 0))
+        wo = 2 * (nq * cfg["d_g"] + d * cfg["g"] * cfg["d_g"])
+        tq, to = kt["q_proj"] * 1e-6, kt["o_proj"] * 1e-6
+        res["roofline_projections"] = {
+            "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK / 1e9,
+            "query_side": {"weight_bytes": wq, "us": round(kt["q_proj"], 2), "achieved": round(wq / tq / 1e9, 1),
+                           "frac": round(wq / tq / HBM_PEAK, 4)},
+            "output_side": {"weight_bytes": wo, "us": round(kt["o_proj"], 2), "achieved": round(wo / to / 1e9, 1),
+                            "frac": round(wo / to / HBM_PEAK, 4)}}
+        desc += (f"; whole attention layer: query-side projections (d_c {cfg['d_c']}) before the path and the "
+                 f"grouped output projection (g {cfg['g']}, d_g {cfg['d_g']}) after it")
     res["config"] = {"workload": f"{cfg['name']}: {desc}", "global_batch": B, "seq_len": tau,
                      "parallelism": "single GPU", "launch": f"HIP graphs of {len(caches)} steps (one per cache copy)",
                      "cache_copies": len(caches)}
-    if not args.no_cpu:
+    if not args.no_cpu and not args.layer:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     return res, ok
 

@@ -35,6 +35,9 @@ __all__ = ["CONFIGS", "config", "generator", "randn", "mxfp4_random", "weights",
 SEED = 0
 
 _BASE = dict(rope_base=10000.0, eps=1e-6)
+# projections around the path: d_c = 1536 (Pro's, and read as Flash's), d_g = 1024 groups
+_FLASH_PROJ = dict(d_c=1536, g=8, d_g=1024)
+_PRO_PROJ = dict(d_c=1536, g=16, d_g=1024)
 
 CONFIGS = {
     "c1": dict(name="c1", B=1, prefix=0, T=256, d=256, c=64, rope_dim=16, n_h=4, c_I=16, n_hI=2,
@@ -42,27 +45,27 @@ CONFIGS = {
                sink=True, **_BASE),
     "c2": dict(name="c2", B=16, prefix=131072, T=1, d=4096, c=512, rope_dim=64, n_h=64, c_I=128,
                n_hI=64, m=4, dual=True, top_k=512, n_win=128, kv_fmt="q", idx_fmt="e4m3",
-               act="bf16", sink=True, **_BASE),
+               act="bf16", sink=True, **_BASE, **_FLASH_PROJ),
     # c2 with the indexer's QK path in MXFP4 (the pages' later FP4 indexer revision)
     "c2fp4": dict(name="c2fp4", B=16, prefix=131072, T=1, d=4096, c=512, rope_dim=64, n_h=64,
                   c_I=128, n_hI=64, m=4, dual=True, top_k=512, n_win=128, kv_fmt="q",
-                  idx_fmt="mxfp4", act="bf16", sink=True, **_BASE),
+                  idx_fmt="mxfp4", act="bf16", sink=True, **_BASE, **_FLASH_PROJ),
     "c3": dict(name="c3", B=4, prefix=1048576, T=1, d=7168, c=512, rope_dim=64, n_h=128, c_I=128,
                n_hI=64, m=4, dual=True, top_k=1024, n_win=128, kv_fmt="q", idx_fmt="e4m3",
-               act="bf16", sink=True, **_BASE),
+               act="bf16", sink=True, **_BASE, **_PRO_PROJ),
     "c4a": dict(name="c4a", B=1, prefix=1048576, T=32768, d=4096, c=512, rope_dim=64, n_h=64,
                 c_I=128, n_hI=64, m=4, dual=True, top_k=512, n_win=128, kv_fmt="q",
-                idx_fmt="e4m3", act="bf16", sink=True, **_BASE),
+                idx_fmt="e4m3", act="bf16", sink=True, **_BASE, **_FLASH_PROJ),
     "c4b": dict(name="c4b", B=1, prefix=262144, T=32768, d=4096, c=512, rope_dim=64, n_h=64,
                 c_I=128, n_hI=64, m=4, dual=True, top_k=512, n_win=128, kv_fmt="q",
-                idx_fmt="e4m3", act="bf16", sink=True, **_BASE),
+                idx_fmt="e4m3", act="bf16", sink=True, **_BASE, **_FLASH_PROJ),
     # c4b with the indexer's QK path in MXFP4
     "c4bfp4": dict(name="c4bfp4", B=1, prefix=262144, T=32768, d=4096, c=512, rope_dim=64, n_h=64,
                    c_I=128, n_hI=64, m=4, dual=True, top_k=512, n_win=128, kv_fmt="q",
-                   idx_fmt="mxfp4", act="bf16", sink=True, **_BASE),
+                   idx_fmt="mxfp4", act="bf16", sink=True, **_BASE, **_FLASH_PROJ),
     "c5": dict(name="c5", B=8, prefix=1048576, T=1, d=4096, c=512, rope_dim=64, n_h=64, c_I=0,
                n_hI=0, m=128, dual=False, top_k=0, n_win=128, kv_fmt="q", idx_fmt="e4m3",
-               act="bf16", sink=True, **_BASE),
+               act="bf16", sink=True, **_BASE, **_FLASH_PROJ),
 }
 
 
