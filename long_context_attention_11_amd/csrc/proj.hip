@@ -122,75 +122,92 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
     }
 }
 
-// Split-K partials of an fp32 block [M][ncol] (row pitch ldp, partial pitch p_ks) summed in
-// partial order and stored in bfloat16 to D [M][ldd].
+// Split-K partials of an fp32 block [M][n1 + n2] (row pitch ldp, partial pitch p_ks) summed in
+// partial order and stored in bfloat16: columns c < n1 to D1 [M][ldd1], the rest to D2 [M][ldd2].
 __global__ __launch_bounds__(256) void k_sum_bf16(const float* __restrict__ P, int ksplit, int64_t p_ks,
-                                                  int M, int ncol, int64_t ldp, uint16_t* __restrict__ D,
-                                                  int64_t ldd) {
+                                                  int M, int64_t ldp, int n1, uint16_t* __restrict__ D1,
+                                                  int64_t ldd1, int n2, uint16_t* __restrict__ D2,
+                                                  int64_t ldd2) {
+  const int ncol = n1 + n2;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)M * ncol) return;
   const int r = (int)(i / ncol), c = (int)(i % ncol);
   float s = 0.f;
   for (int k = 0; k < ksplit; ++k) s += P[(size_t)k * p_ks + (size_t)r * ldp + c];
-  D[(size_t)r * ldd + c] = (uint16_t)f32_to_bf16_bits(s);
+  if (c < n1) D1[(size_t)r * ldd1 + c] = (uint16_t)f32_to_bf16_bits(s);
+  else D2[(size_t)r * ldd2 + (c - n1)] = (uint16_t)f32_to_bf16_bits(s);
 }
 
-// q^I: split-K partials summed, then stored in the indexer's format.  One thread per block of
-// 32 dims of one head.  E4M3: [n_hI][c_I] codes per query.  MXFP4: per query n_hI rows of
-// c_I / 2 element bytes (dim 2i in the low nibble), then n_hI rows of c_I / 32 scale codes;
-// the block scale is 2^(floor(log2 max|v|) - 2) (1 for an all-zero block), the elements the
-// nearest E2M1 values of v / scale, ties to even, saturating at 6.
-__global__ __launch_bounds__(256) void k_store_qI(const float* __restrict__ P, int ksplit, int64_t p_ks,
-                                                  int M, int64_t ldp, int n_hI, int c_I, int fmt,
+// The query side's finish, one launch: blocks [0, nsum) sum the split-K partials of q (when K
+// was split) into bfloat16; the rest store q^I in the indexer's format, one wave per (token,
+// head): lane l takes dims 2l, 2l + 1 (partials summed in order), so a block of 32 dims is
+// the 16 lanes of one DPP row.  E4M3: [n_hI][c_I] codes per token.  MXFP4: per token n_hI
+// rows of c_I / 2 element bytes (dim 2i in the low nibble of byte i), then n_hI rows of
+// c_I / 32 scale codes; the block scale is 2^(floor(log2 max|v|) - 2) (1 for an all-zero
+// block), the elements the nearest E2M1 values of v / scale, ties to even, saturating at 6.
+// Built for c_I = 128 (64 lanes x 2 dims).
+__global__ __launch_bounds__(256) void k_finish_q(const float* __restrict__ P, int ksplit, int64_t p_ks, int M,
+                                                  int64_t ldp, int nq, uint16_t* __restrict__ q, int nsum,
+                                                  const float* __restrict__ PqI, int n_hI, int fmt,
                                                   uint8_t* __restrict__ qI) {
-  const int nblk = c_I / 32;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)M * n_hI * nblk) return;
-  const int r = (int)(i / (n_hI * nblk)), rem = (int)(i % (n_hI * nblk));
-  const int h = rem / nblk, b = rem % nblk;
-  float v[32];
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const size_t col = (size_t)h * c_I + b * 32 + j;
+  constexpr int CI = 128;
+  if ((int)blockIdx.x < nsum) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)M * nq) return;
+    const int r = (int)(i / nq), c = (int)(i % nq);
     float s = 0.f;
-    for (int k = 0; k < ksplit; ++k) s += P[(size_t)k * p_ks + (size_t)r * ldp + col];
-    v[j] = s;
+    for (int k = 0; k < ksplit; ++k) s += P[(size_t)k * p_ks + (size_t)r * ldp + c];
+    q[(size_t)r * nq + c] = (uint16_t)f32_to_bf16_bits(s);
+    return;
+  }
+  const int wid = ((int)blockIdx.x - nsum) * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wid >= M * n_hI) return;   // uniform per wave
+  const int r = wid / n_hI, h = wid % n_hI;
+  float v0 = 0.f, v1 = 0.f;
+  for (int k = 0; k < ksplit; ++k) {
+    const float2 p = *reinterpret_cast<const float2*>(PqI + (size_t)k * p_ks + (size_t)r * ldp + h * CI + 2 * lane);
+    v0 += p.x;
+    v1 += p.y;
   }
   if (fmt == CSA_FMT_MXFP4) {
-    float amax = 0.f;
+    float amax = fmaxf(fabsf(v0), fabsf(v1));
 #pragma unroll
-    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
     int e = 0;
     if (amax > 0.f) {
       int ex;
       frexpf(amax, &ex);   // amax = f 2^ex with f in [0.5, 1): floor(log2 amax) = ex - 1
       e = min(127, max(-127, ex - 1 - 2));
     }
-    const size_t row = (size_t)n_hI * (c_I / 2 + c_I / 32);
-    uint8_t* dst = qI + (size_t)r * row + (size_t)h * (c_I / 2) + b * 16;
-    uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      w[j >> 2] |= (e2m1_code(ldexpf(v[2 * j], -e)) | (e2m1_code(ldexpf(v[2 * j + 1], -e)) << 4)) << (8 * (j & 3));
-    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-    qI[(size_t)r * row + (size_t)n_hI * (c_I / 2) + (size_t)h * (c_I / 32) + b] = (uint8_t)(e + 127);
+    const size_t row = (size_t)n_hI * (CI / 2 + CI / 32);
+    uint8_t* base = qI + (size_t)r * row;
+    base[(size_t)h * (CI / 2) + lane] = (uint8_t)(e2m1_code(ldexpf(v0, -e)) | (e2m1_code(ldexpf(v1, -e)) << 4));
+    if ((lane & 15) == 0) base[(size_t)n_hI * (CI / 2) + (size_t)h * (CI / 32) + (lane >> 4)] = (uint8_t)(e + 127);
   } else {
-    uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < 32; ++j) w[j >> 2] |= f32_to_e4m3(v[j]) << (8 * (j & 3));
-    uint8_t* dst = qI + ((size_t)r * n_hI + h) * c_I + b * 32;
-    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-    *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+    *reinterpret_cast<uint16_t*>(qI + ((size_t)r * n_hI + h) * CI + 2 * lane) =
+        (uint16_t)(f32_to_e4m3(v0) | (f32_to_e4m3(v1) << 8));
   }
 }
 
-// Split K for short inputs so that about 512 workgroups stream the weights; each K range
+// Split K for short inputs, so that the weight stream spreads evenly over the 256 CUs (one CU
+// streams only ~25 GB/s): the split minimizing the largest per-CU share of tiles, ceil(tiles
+// ks / 256) / ks, with ties going to the workgroup count nearest 512 (two per CU: one
+// workgroup per CU streams slower, e.g. Pro's 256 group tiles unsplit took 122 us against
+// 104 us split in two).  Each K range
 // stays a multiple of the 64-deep stage and at least 256 long.
 int gemm_ksplit(int M, int N, int Z, int K) {
   const int tiles = ((M + GM_BM - 1) / GM_BM) * ((N + GM_BN - 1) / GM_BN) * Z;
-  int ks = 1;
-  while (tiles * ks < 512 && K % (ks * 2 * GM_BK) == 0 && K / (ks * 2) >= 256) ks *= 2;
-  return ks;
+  int best = 1;
+  double best_cost = (double)((tiles + 255) / 256);
+  for (int ks = 2; K % (ks * GM_BK) == 0 && K / ks >= 256; ks *= 2) {
+    const double cost = (double)((tiles * ks + 255) / 256) / ks;
+    const bool tie = cost == best_cost;
+    if (cost < best_cost || (tie && std::abs(tiles * ks - 512) < std::abs(tiles * best - 512))) {
+      best = ks;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 // One GEMM plan: output columns [0, n_direct) go to D in bfloat16 when K is not split; the
@@ -217,12 +234,12 @@ hipError_t launch_gemm(const GemmArgs& g, int Z, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_sum_bf16(const float* P, int ks, int64_t p_ks, int M, int ncol, int64_t ldp, uint16_t* D,
-                           int64_t ldd, hipStream_t s) {
-  const int64_t n = (int64_t)M * ncol;
+hipError_t launch_sum_bf16(const float* P, int ks, int64_t p_ks, int M, int64_t ldp, int n1, uint16_t* D1,
+                           int64_t ldd1, int n2, uint16_t* D2, int64_t ldd2, hipStream_t s) {
+  const int64_t n = (int64_t)M * (n1 + n2);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_sum_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, P, ks, p_ks, M, ncol, ldp,
-                     D, ldd);
+  hipLaunchKernelGGL(k_sum_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, P, ks, p_ks, M, ldp, n1, D1,
+                     ldd1, n2, D2, ldd2);
   return hipGetLastError();
 }
 
@@ -287,15 +304,10 @@ hipError_t launch_query_project(const csa_dims& d, const csa_proj_weights& w, co
     g1.P = P1, g1.ldp = p1.ldp, g1.p_ks = (int64_t)M * p1.ldp;
     hipError_t e = launch_gemm(g1, 1, s);
     if (e != hipSuccess) return e;
-    if (p1.ks > 1) {
-      if ((e = launch_sum_bf16(P1, p1.ks, g1.p_ks, M, d_c, p1.ldp, cQ, d_c, s)) != hipSuccess) return e;
-    }
-    if (nw) {
-      const float* Pw = P1 + (d_c - p1.n_bf);   // the w columns of the partials
-      if ((e = launch_sum_bf16(Pw, p1.ks, g1.p_ks, M, nw, p1.ldp, static_cast<uint16_t*>(wI) + (size_t)t0 * nw,
-                               nw, s)) != hipSuccess)
-        return e;
-    }
+    // the partial columns: c^Q (when K was split) then w, one launch
+    uint16_t* wout = nw ? static_cast<uint16_t*>(wI) + (size_t)t0 * nw : nullptr;
+    if ((e = launch_sum_bf16(P1, p1.ks, g1.p_ks, M, p1.ldp, d_c - p1.n_bf, cQ, d_c, nw, wout, nw, s)) != hipSuccess)
+      return e;
     // eqs. 18 and 14: [q | q^I] = c^Q [W^UQ | W^IUQ]
     GemmArgs g2{};
     g2.A = cQ;
@@ -308,16 +320,13 @@ hipError_t launch_query_project(const csa_dims& d, const csa_proj_weights& w, co
     g2.n_bf = p2.n_bf, g2.D = static_cast<uint16_t*>(q) + (size_t)t0 * nq, g2.ldd = nq;
     g2.P = P2, g2.ldp = p2.ldp, g2.p_ks = (int64_t)M * p2.ldp;
     if ((e = launch_gemm(g2, 1, s)) != hipSuccess) return e;
-    if (p2.ks > 1) {
-      if ((e = launch_sum_bf16(P2, p2.ks, g2.p_ks, M, nq, p2.ldp, static_cast<uint16_t*>(q) + (size_t)t0 * nq, nq,
-                               s)) != hipSuccess)
-        return e;
-    }
-    if (nqI) {
-      const float* PqI = P2 + (nq - p2.n_bf);
-      const int64_t n = (int64_t)M * d.n_hI * (d.c_I / 32);
-      hipLaunchKernelGGL(k_store_qI, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, PqI, p2.ks, g2.p_ks, M,
-                         p2.ldp, d.n_hI, d.c_I, d.idx_fmt, static_cast<uint8_t*>(qI) + (size_t)t0 * qI_row);
+    // q from the partials (when K was split) and q^I in the indexer's format, one launch
+    const int nsum = p2.ks > 1 ? (int)(((int64_t)M * nq + 255) / 256) : 0;
+    const int nwav = nqI ? (M * d.n_hI + 3) / 4 : 0;
+    if (nsum + nwav) {
+      hipLaunchKernelGGL(k_finish_q, dim3(nsum + nwav), dim3(256), 0, s, P2, p2.ks, g2.p_ks, M, p2.ldp, nq,
+                         static_cast<uint16_t*>(q) + (size_t)t0 * nq, nsum, P2 + (nq - p2.n_bf), d.n_hI,
+                         d.idx_fmt, nqI ? static_cast<uint8_t*>(qI) + (size_t)t0 * qI_row : nullptr);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
@@ -350,7 +359,8 @@ hipError_t launch_output_project(const csa_dims& d, const csa_proj_weights& w, c
     hipError_t e = launch_gemm(g3, g, s);
     if (e != hipSuccess) return e;
     if (p3.ks > 1) {
-      if ((e = launch_sum_bf16(P3, p3.ks, g3.p_ks, M, g * d_g, p3.ldp, mid, (int64_t)g * d_g, s)) != hipSuccess)
+      if ((e = launch_sum_bf16(P3, p3.ks, g3.p_ks, M, p3.ldp, g * d_g, mid, (int64_t)g * d_g, 0, nullptr, 0, s)) !=
+          hipSuccess)
         return e;
     }
     // the concatenation to d
@@ -365,8 +375,8 @@ hipError_t launch_output_project(const csa_dims& d, const csa_proj_weights& w, c
     g4.P = P4, g4.ldp = p4.ldp, g4.p_ks = (int64_t)M * p4.ldp;
     if ((e = launch_gemm(g4, 1, s)) != hipSuccess) return e;
     if (p4.ks > 1) {
-      if ((e = launch_sum_bf16(P4, p4.ks, g4.p_ks, M, d.d, p4.ldp, static_cast<uint16_t*>(out) + (size_t)t0 * d.d,
-                               d.d, s)) != hipSuccess)
+      if ((e = launch_sum_bf16(P4, p4.ks, g4.p_ks, M, p4.ldp, d.d, static_cast<uint16_t*>(out) + (size_t)t0 * d.d,
+                               d.d, 0, nullptr, 0, s)) != hipSuccess)
         return e;
     }
   }
