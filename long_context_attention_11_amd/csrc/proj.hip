@@ -17,8 +17,8 @@
 namespace csa {
 namespace {
 
-constexpr int GM_BM = 64, GM_BN = 64, GM_BK = 64, GM_LD = GM_BK + 8;  // LDS row pitch (bf16)
 constexpr int GM_ROWS = 8192;   // rows per pass of the host loops (bounds the workspace)
+constexpr int GM_BIG_M = 256;   // inputs of at least this many rows take the 128x128 tiles
 
 struct GemmArgs {
   const uint16_t* A;   // [M][lda]; group z reads columns z * a_zoff .. + K
@@ -35,80 +35,92 @@ struct GemmArgs {
   int64_t ldp, p_zoff, p_ks;
 };
 
-// blockIdx = (column tile, row tile, z * ksplit + ks); 4 waves, each a 32x32 quarter of the
-// tile as 2x2 MFMA 16x16x32 tiles.
+// blockIdx = (column tile, row tile, z * ksplit + ks).  A workgroup of 4 waves computes a
+// BM x BN tile, each wave a (BM/2) x (BN/2) quarter as (BM/32) x (BN/32) MFMA 16x16x32 tiles;
+// stages of BK k are double buffered in LDS with rows padded by 8 bf16 (the 16 rows one read
+// instruction touches then start in distinct 16-byte bank groups).  64x64 / BK 64 serves short
+// inputs; 128x128 / BK 32 reads each operand fragment from LDS once per 4 MFMAs instead of 2.
+template <int BM, int BN, int BK>
 __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][GM_BM * GM_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GM_BN * GM_LD];
+  constexpr int LD = BK + 8;
+  constexpr int PR = BK / 8;                 // 16-byte pieces per row of a stage
+  constexpr int RPP = 256 / PR;              // rows covered by one pass of the 256 threads
+  constexpr int PA = BM / RPP, PB = BN / RPP;
+  constexpr int TI = BM / 32, TJ = BN / 32;  // MFMA tiles per wave
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m0 = blockIdx.y * GM_BM, n0 = blockIdx.x * GM_BN;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int z = blockIdx.z / g.ksplit, ks = blockIdx.z % g.ksplit;
   const int k_begin = ks * g.kchunk, k_end = min(g.K, k_begin + g.kchunk);
-  // loader: a stage is 64 rows x 64 k of each operand, 512 pieces of 8 bf16; 2 per thread
-  const int lr = tid >> 3, lc = (tid & 7) * 8;
-  const uint16_t* arow[2];
-  const uint16_t* brow[2];
-  bool aval[2], bval[2];
+  const int lr = tid / PR, lc = (tid % PR) * 8;
+  const uint16_t* arow[PA];
+  const uint16_t* brow[PB];
+  bool aval[PA], bval[PB];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = lr + 32 * h;
+  for (int h = 0; h < PA; ++h) {
+    const int r = lr + RPP * h;
     aval[h] = m0 + r < g.M;
     arow[h] = g.A + (size_t)min(m0 + r, g.M - 1) * g.lda + (size_t)z * g.a_zoff;
+  }
+#pragma unroll
+  for (int h = 0; h < PB; ++h) {
+    const int r = lr + RPP * h;
     const int n = min(n0 + r, g.N - 1);
     bval[h] = n0 + r < g.N;
     brow[h] = (n < g.nb1 ? g.B + (size_t)n * g.ldb : g.B2 + (size_t)(n - g.nb1) * g.ldb) +
               (size_t)z * g.b_zstride;
   }
-  uint4 ra[2], rb[2];
+  uint4 ra[PA], rb[PB];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < PA; ++h)
       ra[h] = aval[h] ? *reinterpret_cast<const uint4*>(arow[h] + k0 + lc) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < PB; ++h)
       rb[h] = bval[h] ? *reinterpret_cast<const uint4*>(brow[h] + k0 + lc) : make_uint4(0, 0, 0, 0);
-    }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      *reinterpret_cast<uint4*>(&As[buf][(lr + 32 * h) * GM_LD + lc]) = ra[h];
-      *reinterpret_cast<uint4*>(&Bs[buf][(lr + 32 * h) * GM_LD + lc]) = rb[h];
-    }
+    for (int h = 0; h < PA; ++h) *reinterpret_cast<uint4*>(&As[buf][(lr + RPP * h) * LD + lc]) = ra[h];
+#pragma unroll
+    for (int h = 0; h < PB; ++h) *reinterpret_cast<uint4*>(&Bs[buf][(lr + RPP * h) * LD + lc]) = rb[h];
   };
-  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (BN / 2);
   const int fr = lane & 15, fg = lane >> 4;
-  f32x4 acc[2][2];
+  f32x4 acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
   int buf = 0;
   if (k_begin < k_end) gload(k_begin);
-  for (int k0 = k_begin; k0 < k_end; k0 += GM_BK) {
+  for (int k0 = k_begin; k0 < k_end; k0 += BK) {
     sstore(buf);
     __syncthreads();
-    if (k0 + GM_BK < k_end) gload(k0 + GM_BK);
+    if (k0 + BK < k_end) gload(k0 + BK);
 #pragma unroll
-    for (int kk = 0; kk < GM_BK; kk += 32) {
-      bf16x8 a[2], b[2];
+    for (int kk = 0; kk < BK; kk += 32) {
+      bf16x8 a[TI], b[TJ];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm + 16 * i + fr) * GM_LD + kk + fg * 8]);
+      for (int i = 0; i < TI; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm + 16 * i + fr) * LD + kk + fg * 8]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(wn + 16 * j + fr) * GM_LD + kk + fg * 8]);
+      for (int j = 0; j < TJ; ++j)
+        b[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(wn + 16 * j + fr) * LD + kk + fg * 8]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     buf ^= 1;
   }
   // an MFMA 16x16 result: lane holds column (lane & 15), rows 4 (lane >> 4) + e
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TJ; ++j) {
       const int col = n0 + wn + 16 * j + fr;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -195,11 +207,14 @@ __global__ __launch_bounds__(256) void k_finish_q(const float* __restrict__ P, i
 // workgroup per CU streams slower, e.g. Pro's 256 group tiles unsplit took 122 us against
 // 104 us split in two).  Each K range
 // stays a multiple of the 64-deep stage and at least 256 long.
+int gemm_tile(int M) { return M >= GM_BIG_M ? 128 : 64; }
+
 int gemm_ksplit(int M, int N, int Z, int K) {
-  const int tiles = ((M + GM_BM - 1) / GM_BM) * ((N + GM_BN - 1) / GM_BN) * Z;
+  const int t = gemm_tile(M);
+  const int tiles = ((M + t - 1) / t) * ((N + t - 1) / t) * Z;
   int best = 1;
   double best_cost = (double)((tiles + 255) / 256);
-  for (int ks = 2; K % (ks * GM_BK) == 0 && K / ks >= 256; ks *= 2) {
+  for (int ks = 2; K % (ks * 64) == 0 && K / ks >= 256; ks *= 2) {
     const double cost = (double)((tiles * ks + 255) / 256) / ks;
     const bool tie = cost == best_cost;
     if (cost < best_cost || (tie && std::abs(tiles * ks - 512) < std::abs(tiles * best - 512))) {
@@ -229,8 +244,10 @@ Plan plan_of(int M, int N, int Z, int K, int n_direct) {
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int Z, hipStream_t s) {
-  dim3 grid((g.N + GM_BN - 1) / GM_BN, (g.M + GM_BM - 1) / GM_BM, Z * g.ksplit);
-  hipLaunchKernelGGL(k_gemm_bf16, grid, dim3(256), 0, s, g);
+  const int t = gemm_tile(g.M);
+  dim3 grid((g.N + t - 1) / t, (g.M + t - 1) / t, Z * g.ksplit);
+  if (t == 128) hipLaunchKernelGGL((k_gemm_bf16<128, 128, 32>), grid, dim3(256), 0, s, g);
+  else hipLaunchKernelGGL((k_gemm_bf16<64, 64, 64>), grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
