@@ -186,3 +186,24 @@ def test_projections_realistic_values():
     err = np.abs(host64(out) - ro["out"])
     assert err.sum() / np.abs(ro["out"]).sum() <= 1e-2, f"out: mean rel {err.sum() / np.abs(ro['out']).sum():.3g}"
     assert err.max() <= 2e-2 * max(1.0, np.abs(ro["out"]).max()), f"out: max abs {err.max():.3g}"
+
+
+def test_projections_hca_and_single_token():
+    """HCA layers (dual = 0) have no indexer: only q is produced (q^I and w pointers NULL).
+    One token (T = 1) through both sides at Flash shapes."""
+    cfg = _cfg("c5")
+    dims = L.Dims.from_config(cfg)
+    W = synth.proj_weights(cfg, 1536, 8, 1024, seed=56, device=DEV, exact_first=True)
+    pw = L.ProjWeights(W["w_dq"], W["w_uq"], None, None, W["w_og"], W["w_o"])
+    h = synth.small_ints((1, cfg["d"]), -1, 1, 1.0, DEV, 56, 1).to(torch.bfloat16)
+    q = torch.zeros((1, cfg["n_h"], cfg["c"]), dtype=torch.bfloat16, device=DEV)
+    ws = _ws(L.csa_query_project_workspace_size(dims, pw, 1))
+    L.csa_query_project(dims, pw, h, 1, q, None, None, ws)
+    torch.cuda.synchronize()
+    OW = _oracle_w(W)
+    hn = host64(h)
+    cQ = LR.to_bf16(hn @ OW["dq"].T)
+    q_pre = cQ @ OW["uq"].T
+    check_rounded(host64(q).reshape(1, -1), q_pre, sum_bound(cQ, OW["uq"]), bf16, "hca q")
+    o = synth.small_ints((1, cfg["n_h"], cfg["c"]), -1, 1, 1.0, DEV, 56, 2).to(torch.bfloat16)
+    _check_output_exact(cfg, W, o, np.arange(1), "single token")
