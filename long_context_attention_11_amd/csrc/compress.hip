@@ -219,6 +219,11 @@ hipError_t launch_project(const csa_dims& d, const csa_weights& w, const void* H
                           int32_t ksplit, float* P, hipStream_t s) {
   const int NP = state_width(d);
   const int nkv = d.dual ? 4 * d.c : 2 * d.c;
+  if (d.act_fmt == CSA_FMT_BF16 && project_gemm_ok(M)) {
+    // long chunks: the 128x128-tile GEMM (same partial layout)
+    return launch_project_gemm((const uint16_t*)H, (const uint16_t*)w.w_kv, (const uint16_t*)w.w_idx, nkv, M,
+                               NP, d.d, ksplit, P, s);
+  }
   if (d.act_fmt == CSA_FMT_BF16) {
     dim3 grid((NP + PJ_BN - 1) / PJ_BN, (M + PJ_BM - 1) / PJ_BM, ksplit);
     hipLaunchKernelGGL(k_project_bf16, grid, dim3(256), 0, s, (const uint16_t*)H,

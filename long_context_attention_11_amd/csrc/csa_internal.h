@@ -260,7 +260,11 @@ int32_t state_width(const csa_dims& d);
 int32_t state_rows(const csa_dims& d);
 size_t row_bytes(const csa_dims& d);
 
-// proj.hip: the query-side and grouped output projections
+// proj.hip: the query-side and grouped output projections, and the large-input GEMM the
+// compression projection uses
+bool project_gemm_ok(int32_t M);
+hipError_t launch_project_gemm(const uint16_t* H, const uint16_t* wkv, const uint16_t* widx, int nkv, int M,
+                               int NP, int K, int ksplit, float* P, hipStream_t s);
 size_t query_project_ws_bytes(const csa_dims& d, int32_t d_c, int32_t T);
 size_t output_project_ws_bytes(const csa_dims& d, int32_t g, int32_t d_g, int32_t T);
 hipError_t launch_query_project(const csa_dims& d, const csa_proj_weights& w, const void* h, int32_t T,

@@ -286,6 +286,25 @@ size_t output_ws_rows(const csa_dims& d, int32_t g, int32_t d_g, int M) {
 
 }  // namespace
 
+// The compression projection P[ks][M][NP] = H . [w_kv rows; w_idx rows]^T for inputs of at
+// least 256 rows, on the 128x128 tiles (the chunked compress path).
+bool project_gemm_ok(int32_t M) { return M >= GM_BIG_M; }
+
+hipError_t launch_project_gemm(const uint16_t* H, const uint16_t* wkv, const uint16_t* widx, int nkv, int M,
+                               int NP, int K, int ksplit, float* P, hipStream_t s) {
+  GemmArgs g{};
+  g.A = H;
+  g.lda = K;
+  g.B = wkv;
+  g.B2 = widx;
+  g.nb1 = nkv;
+  g.ldb = K;
+  g.M = M, g.N = NP, g.K = K, g.ksplit = ksplit, g.kchunk = K / ksplit;
+  g.n_bf = 0;
+  g.P = P, g.ldp = NP, g.p_ks = (int64_t)M * NP;
+  return launch_gemm(g, 1, s);
+}
+
 size_t query_project_ws_bytes(const csa_dims& d, int32_t d_c, int32_t T) {
   return max_over_passes(T, [&](int M) { return query_ws_rows(d, d_c, M); });
 }
