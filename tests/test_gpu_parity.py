@@ -80,14 +80,22 @@ def _check_cache_vs_oracle(cfg, cache, b, comp, n_tokens, what):
 
 
 def test_c1_forward_matches_oracle():
-    """Tiny fp32 prefill (n=256, d=256, m=4, c=64, 4 heads, k=8, n_win=16): every query."""
+    """Tiny fp32 prefill (n=256, d=256, m=4, c=64, 4 heads, k=8, n_win=16): every query.  The
+    queries come from the hidden states through the low-rank query path (eqs. 13-15 and 18,
+    d_c = 64), computed in float64 and handed to both sides as the same float32 arrays."""
     cfg = synth.config("c1")
     dims = L.Dims.from_config(cfg)
     od = oracle_dims(cfg)
     T, m, k = cfg["T"], cfg["m"], cfg["top_k"]
     W = synth.weights(cfg, device=DEV)
     H = synth.hidden(cfg, 0, 0, T, device=DEV)
-    qs = synth.queries(cfg, T, device=DEV)
+    PW = {n: host64(t) for n, t in synth.proj_weights(cfg, 64, 1, 64, device=DEV).items()}
+    hn = host64(H)
+    cQ = hn @ PW["w_dq"].T                                              # eq. 13
+    f32 = lambda a, shape: torch.as_tensor(a.reshape(shape), dtype=torch.float32, device=DEV).contiguous()
+    qs = {"q": f32(cQ @ PW["w_uq"].T, (T, cfg["n_h"], cfg["c"])),        # eq. 18
+          "qI": f32(cQ @ PW["w_iuq"].T, (T, cfg["n_hI"], cfg["c_I"])),   # eq. 14
+          "w": f32(hn @ PW["w_w"].T, (T, cfg["n_hI"]))}                  # eq. 15
     cache = L.Cache(dims, B=1, cap=T // m, win_cap=T + cfg["n_win"])
     out = torch.zeros((T, cfg["n_h"], cfg["c"]), dtype=torch.float32, device=DEV)
     idx = torch.zeros((T, k), dtype=torch.int32, device=DEV)
