@@ -594,15 +594,18 @@ def test_c4_prefill_full_size_sampled(idx_fmt):
         assert_close_q(go[t], o_ref, f"c4 out t={t}")
 
 
-def test_topk_exact_on_crafted_scores():
+@pytest.mark.parametrize("fmt", ["f32", "bf16"])
+def test_topk_exact_on_crafted_scores(fmt):
     """csa_topk on given scores must equal the oracle's selection exactly (same input bits):
     heavy ties (integer scores), -0/+0, scores rising or falling with the index (every
     candidate in one segment), rows shorter than k, exactly k, k + 1, ragged segment tails,
     rows one workgroup selects from (33000 and 65536 entries) and longer ones (90001 entries,
     k = 1024).  Ties and -0/+0 rows defeat the sampled
-    threshold, so they also exercise the exact whole-row fallback."""
+    threshold, so they also exercise the exact whole-row fallback.  float32 rows, and the
+    bfloat16 rows of the MXFP4 indexer path (whose rounding turns the slow ramps into runs of
+    equal scores)."""
     for k, cap in ((1024, 90001), (512, 4096), (8, 37), (512, 33000), (2048, 65536)):
-        cfg = _qcfg(top_k=k)
+        cfg = _qcfg(top_k=k, idx_fmt="mxfp4" if fmt == "bf16" else "e4m3")
         dims = L.Dims.from_config(cfg)
         m = cfg["m"]
         Vs = sorted({0, 1, min(k, cap), min(k + 1, cap), cap // 3, cap - 5, cap})
@@ -628,6 +631,9 @@ def test_topk_exact_on_crafted_scores():
                 sc[i] = (-np.arange(cap) * 1e-3).astype(np.float32)
             pos.append(m * V + (i % m))
         scores = torch.from_numpy(sc).to(DEV)
+        if fmt == "bf16":
+            scores = scores.to(torch.bfloat16)
+            sc = scores.float().cpu().numpy()
         idx = torch.full((Q, k), -7, dtype=torch.int32, device=DEV)
         ws = _ws(L.csa_topk_workspace_size(dims, Q, cap))
         L.csa_topk(dims, cache, _i32([0] * Q), _i32(pos), Q, scores, cap, idx, ws)
