@@ -16,8 +16,8 @@ layers would be), so a graph launch is paid once per cycle rather than once per 
 
 Other workloads (--config): c3 (Pro decode, 4 x 1M tokens), c5 (HCA decode, 8 x 1M tokens),
 c4a / c4b (32768-token prefill chunk after a 1M- / 262144-token prefix; one step = one
-csa_forward of the chunk), c1 (tiny fp32 prefill); c2fp4 and c4bfp4 are c2 and c4b with the
-indexer's keys and queries in MXFP4.
+csa_forward of the chunk), c1 (tiny fp32 prefill); c2fp4, c4afp4 and c4bfp4 are c2, c4a and
+c4b with the indexer's keys and queries in MXFP4.
 
 Per-kernel durations: each kernel of the step is also launched 20 times back to back inside
 one graph (same inputs, same grid), timed with HIP events around the replay; the dominant
@@ -79,7 +79,7 @@ def parse():
     ap.add_argument("--layer", action="store_true",
                     help="decode configs: time the whole attention layer, the query-side projections "
                          "before the path and the grouped output projection after it included")
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2fp4", "c3", "c4a", "c4b", "c4bfp4", "c5"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2fp4", "c3", "c4a", "c4afp4", "c4b", "c4bfp4", "c5"])
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

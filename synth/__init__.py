@@ -14,7 +14,7 @@ Workload shapes follow the five layer configurations the attention path is measu
   c3   Pro-shaped decode: 4 x 1048576 tokens (262144 entries), d=7168, 128 heads, k=1024
   c4a  Flash chunked prefill: a 32768-token chunk after a 1048576-token prefix
   c4b  the same after a 262144-token prefix
-  c2fp4, c4bfp4  c2 and c4b with the indexer's keys and queries in MXFP4
+  c2fp4, c4afp4, c4bfp4  c2, c4a and c4b with the indexer's keys and queries in MXFP4
   c5   HCA decode: 8 x 1048576 tokens, m'=128 (8192 entries), dense, 64 heads
 Value distributions: hidden states N(0,1); projection weights N(0, 1/fan_in); positional
 biases and sink logits N(0, 0.1) (second argument read as the variance); queries, indexer
@@ -59,7 +59,10 @@ CONFIGS = {
     "c4b": dict(name="c4b", B=1, prefix=262144, T=32768, d=4096, c=512, rope_dim=64, n_h=64,
                 c_I=128, n_hI=64, m=4, dual=True, top_k=512, n_win=128, kv_fmt="q",
                 idx_fmt="e4m3", act="bf16", sink=True, **_BASE, **_FLASH_PROJ),
-    # c4b with the indexer's QK path in MXFP4
+    # c4a and c4b with the indexer's QK path in MXFP4
+    "c4afp4": dict(name="c4afp4", B=1, prefix=1048576, T=32768, d=4096, c=512, rope_dim=64, n_h=64,
+                   c_I=128, n_hI=64, m=4, dual=True, top_k=512, n_win=128, kv_fmt="q",
+                   idx_fmt="mxfp4", act="bf16", sink=True, **_BASE, **_FLASH_PROJ),
     "c4bfp4": dict(name="c4bfp4", B=1, prefix=262144, T=32768, d=4096, c=512, rope_dim=64, n_h=64,
                    c_I=128, n_hI=64, m=4, dual=True, top_k=512, n_win=128, kv_fmt="q",
                    idx_fmt="mxfp4", act="bf16", sink=True, **_BASE, **_FLASH_PROJ),
