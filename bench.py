@@ -77,8 +77,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--layer", action="store_true",
-                    help="decode configs: time the whole attention layer, the query-side projections "
-                         "before the path and the grouped output projection after it included")
+                    help="time the whole attention layer: the query-side projections before the path "
+                         "and the grouped output projection after it included (bf16 configurations)")
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2fp4", "c3", "c4a", "c4afp4", "c4b", "c4bfp4", "c5"])
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -485,7 +485,22 @@ def run_prefill(args, cfg):
     ws = torch.empty(L.csa_workspace_size(dims, L.OP_FORWARD, B=1, T=T, cap=cap, q_chunk=q_chunk),
                      dtype=torch.uint8, device=dev)
 
+    if args.layer:
+        # the layer h -> output for the chunk: query-side projections, the path, grouped output
+        PW = synth.proj_weights(cfg, cfg["d_c"], cfg["g"], cfg["d_g"], device=dev)
+        pw = L.ProjWeights(**PW)
+        h2 = H.reshape(T, cfg["d"])
+        q_l, qI_l, w_l = torch.empty_like(qs["q"]), torch.empty_like(qs["qI"]), torch.empty_like(qs["w"])
+        y = torch.empty((T, cfg["d"]), dtype=torch.bfloat16, device=dev)
+        ws_q = torch.empty(max(1, L.csa_query_project_workspace_size(dims, pw, T)), dtype=torch.uint8, device=dev)
+        ws_o = torch.empty(max(1, L.csa_output_project_workspace_size(dims, pw, T)), dtype=torch.uint8, device=dev)
+
     def step():
+        if args.layer:
+            L.csa_query_project(dims, pw, h2, T, q_l, qI_l, w_l, ws_q)
+            L.csa_forward(dims, lw, cache, H, T, pos0, q_l, qI_l, w_l, W["gamma_q"], W["sink"], out, idx, ws)
+            L.csa_output_project(dims, pw, out, T, y, ws_o)
+            return
         L.csa_forward(dims, lw, cache, H, T, pos0, qs["q"], qs["qI"], qs["w"], W["gamma_q"], W["sink"],
                       out, idx, ws)
 
@@ -505,7 +520,8 @@ def run_prefill(args, cfg):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev[0].elapsed_time(ev[1]) / steps
-    res = {"metric": f"CSA prefill tokens/s ({cfg['name']})", "value": round(T * steps / wall, 1),
+    res = {"metric": f"CSA {'attention-layer ' if args.layer else ''}prefill tokens/s ({cfg['name']})",
+           "value": round(T * steps / wall, 1),
            "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm,
            "ms_per_step": round(wall / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None,
@@ -523,7 +539,13 @@ def run_prefill(args, cfg):
         Vs = [min((p0 + t) // cfg["m"], cap) for t in range(T)]
         flops = 2.0 * cfg["n_hI"] * cfg["c_I"] * sum(Vs)
         res["indexer_tflop_per_step"] = round(flops / 1e12, 2)
-    if not args.no_cpu and cfg["name"] != "c1":
+    if args.layer:
+        d, dc, nq = cfg["d"], cfg["d_c"], cfg["n_h"] * cfg["c"]
+        res["projection_tflop_per_step"] = round(2.0 * T * (d * (dc + cfg["n_hI"]) + dc * (nq + cfg["n_hI"] * cfg["c_I"])
+                                                          + nq * cfg["d_g"] + cfg["g"] * cfg["d_g"] * d) / 1e12, 2)
+        res["config"]["workload"] += (f"; whole attention layer: query-side projections (d_c {cfg['d_c']}) and the "
+                                      f"grouped output projection (g {cfg['g']}, d_g {cfg['d_g']})")
+    if not args.no_cpu and cfg["name"] != "c1" and not args.layer:
         res["cpu_baseline"] = cpu_baseline_prefill(cfg, args.cpu_seconds)
     return res, True
 
