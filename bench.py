@@ -553,7 +553,7 @@ def run_prefill(args, cfg):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     import torch

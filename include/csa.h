@@ -47,7 +47,7 @@ extern "C" {
 typedef enum csa_status {
   CSA_OK = 0,
   CSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive or inconsistent sizes */
-  CSA_ERR_UNSUPPORTED = 2,      /* a size/format combination this build has no kernel for */
+  CSA_ERR_UNSUPPORTED = 2,      /* a size/format combination the library has no kernel for */
   CSA_ERR_WORKSPACE_TOO_SMALL = 3,
   CSA_ERR_HIP = 4               /* a HIP launch failed; csa_last_error() has the HIP text */
 } csa_status;
