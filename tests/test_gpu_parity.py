@@ -494,6 +494,12 @@ def test_c3_decode_full_size():
     _decode_full("c3")
 
 
+def test_c3_decode_full_size_mxfp4():
+    """The same with MXFP4 indexer keys and queries: bfloat16 score rows of 262144 entries
+    through the threshold and final passes with k = 1024."""
+    _decode_full("c3", idx_fmt="mxfp4")
+
+
 def test_c5_hca_decode_full_size():
     """HCA decode, 8 sequences x 8192 entries (1M tokens, m'=128), dense attention."""
     _decode_full("c5")
