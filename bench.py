@@ -44,16 +44,26 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_c2_traffic.txt")
 INDEXER_SRC = os.path.join(ROOT, "long_context_attention_11_amd", "csrc", "indexer.hip")
 
 
+def code_digest(path):
+    """sha256 of a C++/HIP source with its comments and blank lines removed and each line
+    stripped: a change to the code changes it, a change to a comment does not."""
+    import hashlib
+    import re
+    src = open(path, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    code = "\n".join(l.strip() for l in src.splitlines() if l.strip())
+    return hashlib.sha256(code.encode()).hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per indexer launch from the committed counter summary, or None when the
-    indexer source changed since the counters were taken (the summary records its hash)."""
-    import hashlib
+    indexer's code changed since the counters were taken (the summary records its digest)."""
     try:
         kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
     except OSError:
         return None
-    src = hashlib.sha256(open(INDEXER_SRC, "rb").read()).hexdigest()
-    if kv.get("indexer_source_sha256", "").strip() != src:
+    if kv.get("indexer_code_sha256", "").strip() != code_digest(INDEXER_SRC):
         return None
     try:
         return int(float(kv["traffic_bytes_per_launch"]))

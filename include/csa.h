@@ -79,6 +79,8 @@ typedef enum csa_op {
  *   top_k     entries kept per query (pages: 512 Flash, 1024 Pro); 0 with dual = 0.
  *   n_win     sliding-window length (pages: 128); the window of a query at tau covers
  *             positions max(0, tau - n_win + 1) .. tau, the query's own token included.
+ *             n_win >= m is required (INVALID_ARGUMENT otherwise), for CSA and HCA alike: a
+ *             query sees only complete entries, so the window must cover the open block.
  *   scale     softmax scale on q.k; <= 0 selects 1/sqrt(c).
  *   rope_base RoPE base (10000); pair j of the RoPE dims turns by pos * base^(-2j/rope_dim).
  *   rms_eps   RMSNorm epsilon (1e-6).
@@ -88,8 +90,8 @@ typedef enum csa_op {
  *             RoPE dims kept in BF16, the rest in FP8, as the explainer's key-numbers table and
  *             PaperTrace §2.5 state).
  *   idx_fmt   F32, E4M3 or MXFP4: indexer keys K^I and indexer queries q^I.  MXFP4 is the
- *             pages' later FP4 indexer path (reading notes §3.3-3.4: 1x32 sub-blocks with
- *             their own scales) in the OCP MX v1.0 format: per block of 32 dims one E8M0
+ *             pages' later FP4 indexer path (PaperTrace §3.3: 1x32 sub-blocks with their own
+ *             scales) in the OCP MX v1.0 format: per block of 32 dims one E8M0
  *             scale code (2^(code - 127)) and 32 E2M1 codes, two per byte (dim 2i in the low
  *             nibble).  Per sequence, ki holds cap rows of c_I / 2 element bytes, then cap
  *             rows of c_I / 32 scale codes; per query, q^I holds n_hI rows of c_I / 2 element
@@ -220,7 +222,7 @@ int csa_compress(const csa_dims* dims, const csa_weights* w, const csa_cache* ca
  *           excluded); if V <= top_k all V are taken; equal scores go to the lower index.
  *   scores_out  NULL, or [Q][cap] receiving the scores of the visible entries (entries
  *           s >= V are left untouched): float32, or with idx_fmt MXFP4 bfloat16, the pages'
- *           BF16 index scores of the FP4 path (reading notes §3.4), each the exact score
+ *           BF16 index scores of the FP4 path (PaperTrace §3.3), each the exact score
  *           rounded to nearest even.
  * Errors: INVALID_ARGUMENT (null pointer, Q < 1, dual = 0 or top_k < 1), UNSUPPORTED
  * (V could exceed what the selection kernels handle for this top_k), WORKSPACE_TOO_SMALL,
@@ -297,7 +299,8 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
  * projection after it (§2.3.3, "Grouped Output Projection"; deep dive "DeepSeek-V4 架构设计深度
  * 解析" stage three: the n_h heads form g consecutive groups, group i's c n_h / g values are
  * projected to d_g by its own map, and the g d_g concatenated values are projected to d;
- * g = 16 (Pro) or 8 (Flash), d_g = 1024; explainer "DeepSeek V4 架构解读" §2.2: d_c = 1536).
+ * g = 16 (Pro) or 8 (Flash), d_g = 1024; PaperTrace §1: d_c = 1536 from the 1536 x 128 x 512
+ * query up-projection, §2.2: g and d_g).
  * Every matrix W in R^{a x b} is stored transposed, bf16 [b][a] (one row per output column,
  * the a inputs contiguous).  The weights are the caller's; the library only reads them.
  */

@@ -33,7 +33,9 @@ int check_dims(const csa_dims* d) {
     return fail(CSA_ERR_INVALID_ARGUMENT, "d, c, n_h, m and n_win must be positive (c >= 2)");
   if (d->rope_dim < 0 || d->rope_dim > d->c || (d->rope_dim & 1) || (d->c & 1))
     return fail(CSA_ERR_INVALID_ARGUMENT, "rope_dim must be even and <= c, c even");
-  if (d->n_win < d->m && d->dual)
+  // a query at tau sees the entries of complete blocks only, so the window must reach back
+  // over the open block's tokens (m * floor(tau / m) .. tau), for CSA and HCA alike
+  if (d->n_win < d->m)
     return fail(CSA_ERR_INVALID_ARGUMENT, "n_win must be >= m so the window covers the open block");
   if (d->dual != 0 && d->dual != 1) return fail(CSA_ERR_INVALID_ARGUMENT, "dual must be 0 or 1");
   if (d->dual) {

@@ -6,7 +6,7 @@
 // With E4M3 keys and queries the contraction over c_I runs on bf16 MFMA: E4M3 values widen to
 // bf16 exactly, products are exact and accumulate in float32.  (The fp8 MFMA forms accumulate
 // with fewer bits: measured errors of ~2^-16 of sum|a_k b_k|, which top-k selection cannot
-// tolerate.)  With MXFP4 keys and queries (the FP4 indexer path, reading notes §3.3-3.4) the
+// tolerate.)  With MXFP4 keys and queries (the FP4 indexer path, PaperTrace §3.3) the
 // codes and scales go to the block-scaled FP4 MFMA as stored; measured on gfx950 it returns
 // the float32 rounding of the exact dot, exactly the dot for these operands.  The ReLU, the
 // head weight and the sum over heads are fused into the MFMA epilogue; the FP4 path sums in

@@ -5,7 +5,8 @@
 //                concatenated and projected to d
 // (reading notes "DeepSeekV4技术报告阅读笔记" §2.3.2 eqs. 13-15, §2.3.3 eq. 18 and its grouped
 // output projection paragraph; deep dive "DeepSeek-V4 架构设计深度解析" stage three for g and
-// d_g; explainer "DeepSeek V4 架构解读" §2.2 for Pro's d_c = 1536.)
+// d_g; PaperTrace "02 · DeepSeek-V4: 压缩注意力撑起 1M 上下文" §1 for Pro's d_c = 1536, from its
+// 1536 x 128 x 512 query up-projection, and §2.2 for g and d_g.)
 //
 // All six maps are plain bf16 GEMMs with float32 accumulation on MFMA.  One kernel serves
 // them: 64x64 output tiles, BK = 64 stages double buffered in LDS, a group index (the g

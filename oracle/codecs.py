@@ -12,8 +12,8 @@ and §3.3).  The pages do not name the FP8 variant; the reading taken here is OC
 ties to even, saturating to +-448.
 
 The indexer's QK path may instead hold its keys and queries in MXFP4, the pages' later
-revision of it (reading notes "DeepSeekV4技术报告阅读笔记" §3.3-3.4: FP4 (MXFP4) with 1x32
-sub-blocks carrying their own scale factors).  The format is the OCP Microscaling (MX) v1.0
+revision of it (PaperTrace "02 · DeepSeek-V4: 压缩注意力撑起 1M 上下文" §3.3: FP4 (MXFP4) on
+the indexer's QK path, with 1x32 sub-blocks carrying their own scale factors).  The format is the OCP Microscaling (MX) v1.0
 one: 32 elements share one E8M0 scale X = 2^(e - 127); each element is FP4 E2M1 (sign bit
 3, exponent bits 2..1 with bias 1, mantissa bit 0; values 0, 0.5, 1, 1.5, 2, 3, 4, 6).
 Encoding follows the MX conversion rule: X = 2^(floor(log2(max |v|)) - 2) (2 is E2M1's

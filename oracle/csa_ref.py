@@ -231,7 +231,7 @@ def store_kv(y, dims: Dims):
 
 def store_index_keys(k, dims: Dims):
     """Round indexer keys to storage: float32, E4M3 with unit scale, or MXFP4 (the pages'
-    later FP4 indexer path, reading notes §3.3-3.4).  Returns (values, bytes); for MXFP4 the
+    later FP4 indexer path, [PT] §3.3).  Returns (values, bytes); for MXFP4 the
     bytes are the packed element codes followed by the block scale codes, per key."""
     k = np.asarray(k, np.float64)
     if dims.idx_fmt == "f32":
@@ -379,7 +379,7 @@ def index_scores(qI, w, KI):
 
 def stored_scores(scores, dims: Dims):
     """The scores top-k selects from: as computed, or with an MXFP4 QK path the pages' BF16
-    index scores (reading notes §3.4: scores drop from FP32 to BF16 with the FP4 indexer),
+    index scores ([PT] §3.3: scores drop from FP32 to BF16 with the FP4 indexer),
     rounded to nearest even from the exact value."""
     if dims.idx_fmt == "mxfp4":
         return codecs.bf16_round_nearest(scores)

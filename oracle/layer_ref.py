@@ -12,9 +12,10 @@ Sources:
        (HCA uses the same two projections).
   [DD] "DeepSeek-V4 架构设计深度解析" (blog.sysu-sam.com), stage three: g = 16 (Pro) / 8
        (Flash) groups, each projected to d_g = 1024.
-  [EX] "DeepSeek V4 架构解读: CSA、HCA、mHC 与 Muon" (researchpapers.dev), §2.2: the query
-       up-projection of Pro is 1536 x 128 x 512 (so d_c = 1536), the grouped output
-       projection about 1.8e8 parameters against about 4.7e8 ungrouped.
+  [PT] "02 · DeepSeek-V4: 压缩注意力撑起 1M 上下文" (PaperTrace, yayajjiang.github.io), §1:
+       the query up-projection of Pro is 1536 x 128 x 512 (so d_c = 1536), about 1.0e8
+       parameters; §2.2: g = 16 (Pro) / 8 (Flash), d_g = 1024, the grouped output projection
+       about 1.8e8 parameters against about 4.7e8 ungrouped.
 
 Weights follow the convention of ``csa_ref.project``: a matrix W in R^{a x b} is stored
 transposed, [b][a], one row per output column.

@@ -67,6 +67,12 @@ def test_invalid_dims_are_rejected_on_the_host():
                                     ctypes.byref(out))
         assert st == 1, over
         assert lib.csa_last_error().decode()
+    # HCA too: a window shorter than m' would leave the open block's older tokens unseen
+    d = L.Dims.from_config(synth.config("c5"), n_win=64)
+    out = ctypes.c_size_t(0)
+    assert lib.csa_workspace_size(ctypes.byref(d.struct()), L.OP_ATTEND, 1, 1, 1, 1, 0,
+                                  ctypes.byref(out)) == 1
+    assert "n_win" in lib.csa_last_error().decode()
     # an unbuilt combination: quantized rows need c = 512
     d = L.Dims.from_config(synth.config("c2"), c=256)
     out = ctypes.c_size_t(0)
