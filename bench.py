@@ -167,6 +167,37 @@ def kernel_time_us(fns, reps=20, rounds=5):
 # ----------------------------------------------------------------------------- CPU baseline
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where it is not readable)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline_keys_and_queries(cfg, sc, qs, N):
+    """Indexer keys of sequence 0 and the indexer queries, decoded as the oracle reads them
+    (E4M3, or MXFP4 element codes and block scales)."""
+    import numpy as np
+
+    from oracle import codecs
+    if cfg["idx_fmt"] == "mxfp4":
+        cI, nh = cfg["c_I"], cfg["n_hI"]
+        kb = sc["ki"][0].numpy()
+        ki = codecs.mxfp4_decode(kb[:N * cI // 2].reshape(N, cI // 2), kb[N * cI // 2:].reshape(N, cI // 32))
+        qb = qs["qI"].numpy()
+        Q = qb.shape[0]
+        qI = codecs.mxfp4_decode(qb[:, :nh * cI // 2].reshape(Q, nh, cI // 2),
+                                 qb[:, nh * cI // 2:].reshape(Q, nh, cI // 32))
+        return ki, qI
+    if cfg["idx_fmt"] == "f32":
+        return sc["ki"][0].numpy().astype(np.float64), qs["qI"].float().numpy().astype(np.float64)
+    return codecs.e4m3_decode(sc["ki"][0].numpy()), codecs.e4m3_decode(qs["qI"].numpy())
+
+
 def cpu_baseline(cfg, seconds):
     """The oracle, untuned, on a bounded sample of the same decode step: single queries
     (compress of the new token: every projection and its window row; indexer over all visible
@@ -184,7 +215,7 @@ def cpu_baseline(cfg, seconds):
         threads = os.cpu_count() or 1
     od = R.Dims(d=cfg["d"], c=cfg["c"], rope_dim=cfg["rope_dim"], n_h=cfg["n_h"], c_I=cfg["c_I"],
                 n_hI=cfg["n_hI"], m=cfg["m"], dual=cfg["dual"], top_k=cfg["top_k"],
-                n_win=cfg["n_win"], kv_fmt="q", idx_fmt="e4m3")
+                n_win=cfg["n_win"], kv_fmt="q", idx_fmt=cfg["idx_fmt"] if cfg["dual"] else "e4m3")
     N = cfg["prefix"] // cfg["m"]
     tau = cfg["prefix"]
     W = synth.weights(cfg, device="cpu")
@@ -199,10 +230,9 @@ def cpu_baseline(cfg, seconds):
                                codecs.bf16_decode(b[:, c - r:].copy().view("<u2"))], axis=1)
     entries = dec(sc["kv"][0].numpy())
     win = dec(sc["win"][0].numpy())
-    ki = codecs.e4m3_decode(sc["ki"][0].numpy()) if cfg["dual"] else None
-    qs = synth.queries(cfg, 8, device="cpu")
+    qs = synth.queries(cfg, 8, device="cpu", mx_codes=(125, 127))
     q = qs["q"].float().numpy().astype(np.float64)
-    qI = codecs.e4m3_decode(qs["qI"].numpy()) if cfg["dual"] else [None] * 8
+    ki, qI = cpu_baseline_keys_and_queries(cfg, sc, qs, N) if cfg["dual"] else (None, [None] * 8)
     w = qs["w"].float().numpy().astype(np.float64) if cfg["dual"] else [None] * 8
     h = synth.hidden(cfg, 0, tau, tau + 1, device="cpu").float().numpy().astype(np.float64)
     paths = (("kv_a", "kv_b", "z_a", "z_b", "ki_a", "ki_b", "zi_a", "zi_b") if cfg["dual"]
@@ -226,8 +256,10 @@ def cpu_baseline(cfg, seconds):
     what = (f"indexer over {N} entries, top-{cfg['top_k']}, attention over {cfg['top_k']}+{cfg['n_win']} rows"
             if cfg["dual"] else f"dense attention over {N}+{cfg['n_win']} rows")
     return {"value": round(n / el, 2), "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{n} single-query decode steps of the same workload (compress of the new "
-                      f"token, {what}), synthetic inputs of the same shapes, {el:.1f} s"}
+                      f"token, {what}{', MXFP4 indexer keys and queries, BF16 scores' if cfg['idx_fmt'] == 'mxfp4' and cfg['dual'] else ''}), "
+                      f"synthetic inputs of the same shapes, {el:.1f} s"}
 
 
 def cpu_baseline_prefill(cfg, seconds):
@@ -257,16 +289,14 @@ def cpu_baseline_prefill(cfg, seconds):
     if cfg["kv_fmt"] == "f32":
         entries = sc["kv"][0].numpy().view(np.float32).astype(np.float64)
         win = sc["win"][0].numpy().view(np.float32).astype(np.float64)
-        ki = sc["ki"][0].numpy().astype(np.float64)
     else:
         entries = np.concatenate([codecs.e4m3_decode(sc["kv"][0].numpy()[:, :c - r]),
                                   codecs.bf16_decode(sc["kv"][0].numpy()[:, c - r:].copy().view("<u2"))], 1)
         win = np.concatenate([codecs.e4m3_decode(sc["win"][0].numpy()[:, :c - r]),
                               codecs.bf16_decode(sc["win"][0].numpy()[:, c - r:].copy().view("<u2"))], 1)
-        ki = codecs.e4m3_decode(sc["ki"][0].numpy())
-    qs = synth.queries(cfg, 8, device="cpu")
+    qs = synth.queries(cfg, 8, device="cpu", mx_codes=(125, 127))
+    ki, qI = cpu_baseline_keys_and_queries(cfg, sc, qs, N)
     q = qs["q"].float().numpy().astype(np.float64)
-    qI = qs["qI"].float().numpy().astype(np.float64) if cfg["idx_fmt"] == "f32" else codecs.e4m3_decode(qs["qI"].numpy())
     w = qs["w"].float().numpy().astype(np.float64)
     t0 = time.perf_counter()
     H = synth.hidden(cfg, 0, p0, p0 + 64, device="cpu").float().numpy().astype(np.float64)
@@ -283,7 +313,7 @@ def cpu_baseline_prefill(cfg, seconds):
             break
     t_q = (time.perf_counter() - t1) / n
     return {"value": round(1.0 / (t_comp + t_q), 2), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"compression of 64 chunk tokens plus {n} single-query steps against the "
                       f"{N}-entry prefix (synthetic inputs of the workload's shapes); per-token cost "
                       f"= compress share + one query"}
@@ -300,25 +330,39 @@ def run_decode(args, cfg):
 
     dev = "cuda:0"
     calibration_copy()
-    B, tau, k = cfg["B"], cfg["prefix"], cfg["top_k"]
+    B, k, m = cfg["B"], cfg["top_k"], cfg["m"]
     dual = cfg["dual"]
     dims = L.Dims.from_config(cfg)
     W = synth.weights(cfg, device=dev)
     lw = lib_weights(L, W, dual)
-    N = tau // cfg["m"]
-    t_build = time.perf_counter()
-    base = build_cache(L, synth, cfg, dims, lw, dev, B, tau, N, cfg["n_win"])
-    t_build = time.perf_counter() - t_build
+    N = cfg["prefix"] // m          # entry capacity per sequence
+    steps = args.steps or 200
+    warm = args.warmup if args.warmup is not None else 10
     # Enough rotating copies that the tensor a launch streams (indexer keys, or the whole cache
     # for the dense variant) is not still held by the 256 MB last-level cache from an earlier
     # step: the set that rotates between two uses of a copy is at least twice that size.
     streamed = B * N * (cfg["c_I"] if dual else synth.row_bytes(cfg))
     copies = args.copies or min(16, max(3, -(-2 * MALL_BYTES // streamed) + 1))
+    G = copies
+    # Step s runs on copy s % G at position tau_start + s // G: every copy advances one token
+    # per cycle, so one step in m completes (and stores) an entry.  The prefix stops `room`
+    # entries short of the capacity, which leaves room for every entry the steps complete.
+    cycles = -(-(warm + steps) // G)
+    room = cycles // m + 1
+    N0 = N - room
+    tau_start = m * N0
+    tau = tau_start
+    t_build = time.perf_counter()
+    base = build_cache(L, synth, cfg, dims, lw, dev, B, tau_start, N, cfg["n_win"])
+    t_build = time.perf_counter() - t_build
     caches = [base] + [clone_cache(base) for _ in range(copies - 1)]
 
-    H1 = torch.stack([synth.hidden(cfg, b, tau, tau + 1, device=dev) for b in range(B)])
-    qs = synth.queries(cfg, B, device=dev, tag="decode")
-    pos0 = torch.full((B,), tau, dtype=torch.int32, device=dev)
+    # per cycle: the new token of each sequence (its hidden state) and its position
+    Hc = [torch.stack([synth.hidden(cfg, b, tau_start + c, tau_start + c + 1, device=dev) for b in range(B)])
+          for c in range(cycles)]
+    posc = [torch.full((B,), tau_start + c, dtype=torch.int32, device=dev) for c in range(cycles)]
+    H1, pos0 = Hc[0], posc[0]
+    qs = synth.queries(cfg, B, device=dev, tag="decode", mx_codes=(125, 127))
     q_seq = torch.arange(B, dtype=torch.int32, device=dev)
     q_pos = torch.full((B,), tau, dtype=torch.int32, device=dev)
     ws_c = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_COMPRESS, B=B, T=1)), dtype=torch.uint8, device=dev)
@@ -363,42 +407,46 @@ def run_decode(args, cfg):
         def k_oproj(c):
             L.csa_output_project(dims, pw, out, B, y, ws_o)
 
-    def step(c):
-        # one pass of the whole path through the library's forward entry point
+    def step(s):
+        # step s: one pass of the whole path through the library's forward entry point, on
+        # copy s % G at position tau_start + s // G
+        c, cyc = caches[s % G], s // G
         if args.layer:
             k_qproj(c)
-            L.csa_forward(dims, lw, c, H1, 1, pos0, q_l, qI_l, w_l, W["gamma_q"], W["sink"], out,
+            L.csa_forward(dims, lw, c, Hc[cyc], 1, posc[cyc], q_l, qI_l, w_l, W["gamma_q"], W["sink"], out,
                           idx if dual else None, ws_f)
             k_oproj(c)
             return
-        L.csa_forward(dims, lw, c, H1, 1, pos0, qs["q"], qs["qI"] if dual else None,
+        L.csa_forward(dims, lw, c, Hc[cyc], 1, posc[cyc], qs["q"], qs["qI"] if dual else None,
                       qs["w"] if dual else None, W["gamma_q"], W["sink"], out,
                       idx if dual else None, ws_f)
 
-    step(caches[0])
-    torch.cuda.synchronize()
-    ref = (y.clone() if args.layer else out.clone(), idx.clone() if dual else None)
-    steps = args.steps or 200
-    warm = args.warmup if args.warmup is not None else 10
-    G = len(caches)
-    cycle = capture(lambda: [step(c) for c in caches])
-    tails = {r: capture(lambda r=r: [step(caches[i]) for i in range(r)])
-             for r in {warm % G, steps % G} if r}
+    def graphs(s0, s1):
+        # steps s0 .. s1 - 1 in graphs of at most one cycle each (a decode loop over the copies
+        # captured once per cycle), cut at cycle boundaries
+        gs, s = [], s0
+        while s < s1:
+            e = min(s1, (s // G + 1) * G)
+            gs.append(capture(lambda s=s, e=e: [step(i) for i in range(s, e)]))
+            s = e
+        return gs
 
-    def run_steps(n):
-        for _ in range(n // G):
-            cycle.replay()
-        if n % G:
-            tails[n % G].replay()
-
+    g_warm, g_timed = graphs(0, warm), graphs(warm, warm + steps)
     torch.cuda.synchronize()
-    run_steps(warm)
+    for g in g_warm:
+        g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run_steps(steps)
+    for g in g_timed:
+        g.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ok = torch.equal(y if args.layer else out, ref[0]) and (not dual or torch.equal(idx, ref[1]))
+    # the last step again, eagerly: a step at a position a copy has already taken recomputes
+    # exactly what it wrote then, so the graph's output must be reproduced bit for bit
+    got = (y.clone() if args.layer else out.clone(), idx.clone() if dual else None)
+    step(warm + steps - 1)
+    torch.cuda.synchronize()
+    ok = torch.equal(y if args.layer else out, got[0]) and (not dual or torch.equal(idx, got[1]))
 
     # per-kernel launch durations (same inputs and grids, rotating cache copies)
     kt = {name: kernel_time_us([lambda c=c, f=f: f(c) for c in caches])
@@ -460,9 +508,11 @@ def run_decode(args, cfg):
                             "frac": round(wo / to / HBM_PEAK, 4)}}
         desc += (f"; whole attention layer: query-side projections (d_c {cfg['d_c']}) before the path and the "
                  f"grouped output projection (g {cfg['g']}, d_g {cfg['d_g']}) after it")
-    res["config"] = {"workload": f"{cfg['name']}: {desc}", "global_batch": B, "seq_len": tau,
-                     "parallelism": "single GPU", "launch": f"HIP graphs of {len(caches)} steps (one per cache copy)",
-                     "cache_copies": len(caches)}
+    res["config"] = {"workload": f"{cfg['name']}: {desc}", "global_batch": B, "seq_len": cfg["prefix"],
+                     "positions": f"{tau_start} .. {tau_start + cycles - 1} (each copy advances one token per "
+                                  f"cycle; one step in {m} completes an entry)",
+                     "parallelism": "single GPU", "launch": f"HIP graphs of {G} steps (one per cache copy)",
+                     "cache_copies": G}
     if not args.no_cpu and not args.layer:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     return res, ok
@@ -486,7 +536,7 @@ def run_prefill(args, cfg):
         L.Cache(dims, B=1, cap=cap, win_cap=win_cap, device=dev)
     t_build = time.perf_counter() - t_build
     H = synth.hidden(cfg, 0, p0, p0 + T, device=dev).unsqueeze(0).contiguous()
-    qs = synth.queries(cfg, T, device=dev, tag="prefill")
+    qs = synth.queries(cfg, T, device=dev, tag="prefill", mx_codes=(125, 127))
     pos0 = torch.full((1,), p0, dtype=torch.int32, device=dev)
     dt = torch.float32 if cfg["act"] == "f32" else torch.bfloat16
     out = torch.empty((T, cfg["n_h"], cfg["c"]), dtype=dt, device=dev)

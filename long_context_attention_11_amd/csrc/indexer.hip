@@ -7,10 +7,12 @@
 // bf16 exactly, products are exact and accumulate in float32.  (The fp8 MFMA forms accumulate
 // with fewer bits: measured errors of ~2^-16 of sum|a_k b_k|, which top-k selection cannot
 // tolerate.)  With MXFP4 keys and queries (the FP4 indexer path, PaperTrace §3.3) the
-// codes and scales go to the block-scaled FP4 MFMA as stored; measured on gfx950 it returns
-// the float32 rounding of the exact dot, exactly the dot for these operands.  The ReLU, the
-// head weight and the sum over heads are fused into the MFMA epilogue; the FP4 path sums in
-// float64 and stores the BF16 score rounded once.
+// codes and scales go to the block-scaled FP4 MFMA as stored.  Its float32 result is the
+// exact dot whenever that fits a float32 significand, which the block scales decide: each
+// tile checks them, and a tile whose (head, key) pairs could overflow the significand
+// contracts each 32-element block on its own and adds the four exact block terms in float64.
+// The ReLU, the head weight and the sum over heads are fused into the MFMA epilogue; the FP4
+// path sums in float64 and stores the BF16 score rounded once.
 #include "csa_internal.h"
 
 namespace csa {
@@ -43,6 +45,27 @@ __device__ __forceinline__ f32x4 mfma_fp4(const uint4& a, int sa, const uint4& b
   const i32x8 bv = {(int32_t)b.x, (int32_t)b.y, (int32_t)b.z, (int32_t)b.w, 0, 0, 0, 0};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, sa,
                                                           0, sb);
+}
+
+// When the 16x16x128 FP4 MFMA's float32 result is exact.  A 32-element block's sum of E2M1
+// products is an integer multiple of 2^-2 below 32 * 36 (|product| <= 6 * 6), scaled by the
+// product of the two block scales 2^p_b, p_b = (code_q - 127) + (code_k - 127).  In units of
+// 2^(min_b p_b - 2) the four-block sum stays below 4 * 4608 * 2^D, D = max_b p_b - min_b p_b,
+// which fits the 24-bit float32 significand for D <= 9; gfx950 then returns it exactly.  D is
+// at most the query head's code spread plus the key's.
+constexpr int FP4_EXACT_SPREAD = 9;
+
+// Largest minus smallest of the four scale codes of one row, where lane group g (l >> 4) holds
+// block g's code and the 16 lanes of a group hold 16 rows (the layout of an FP4 MFMA operand).
+__device__ __forceinline__ int code_spread(int code) {
+  int mx = code, mn = code;
+  int o = __float_as_int(lane_xor16(__int_as_float(mx)));
+  int p = __float_as_int(lane_xor16(__int_as_float(mn)));
+  mx = max(mx, o);
+  mn = min(mn, p);
+  o = __float_as_int(lane_xor32(__int_as_float(mx)));
+  p = __float_as_int(lane_xor32(__int_as_float(mn)));
+  return max(mx, o) - min(mn, p);
 }
 
 // ReLU of an MFMA result as one integer max on its bits: negative floats (and -0) are
@@ -234,6 +257,46 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
 // block g of a row (16 element bytes and one scale code), which is exactly the lane's share
 // of a block-scaled MFMA operand, so the codes go to the matrix cores as loaded: one
 // 16x16x128 MFMA per head tile covers all 128 dims.  Scores are bfloat16.
+// The same head sum for a tile whose block scales may span more octaves than a float32 sum
+// holds: block blk is contracted alone (the key operand's other blocks zeroed; zeroing the
+// query operand instead would be loop-invariant, and the compiler would keep all sixteen
+// masked copies live), where its sum is exact, and the dot is the float64 sum of the four
+// block terms in block order.
+template <int HT>
+__device__ __forceinline__ double head_sum_f64_blocks(const uint4 (&qa)[HT], const int (&qs)[HT],
+                                                      const double (&W)[HT][4], const uint4& b, int bs,
+                                                      int g) {
+  // (scheduling fences keep one head tile's MFMAs in flight at a time: the path is rare, and
+  // hoisting all of them would raise the register use of the common path around it)
+  uint4 bm[4];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) bm[blk] = g == blk ? b : make_uint4(0u, 0u, 0u, 0u);
+  double part = 0.0;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) acc[blk] = mfma_fp4(qa[ht], qs[ht], bm[blk], bs);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double dot = (((double)acc[0][e] + (double)acc[1][e]) + (double)acc[2][e]) + (double)acc[3][e];
+      part = fma(W[ht][e], fmax(dot, 0.0), part);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  return part;
+}
+
+// Largest scale-code spread over a query's NH heads (every lane of the wave gets it).
+template <int HT>
+__device__ __forceinline__ int query_code_spread(const int (&qs)[HT]) {
+  int sp = 0;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) sp = max(sp, code_spread(qs[ht]));
+  return wave_allreduce(sp, [](int x, int y) { return max(x, y); });
+}
+
 template <int NH, int QPW>
 __device__ __forceinline__ void indexer_fp4_body(const IndexerArgs& ia, int bx, int by) {
   constexpr int KC = IX_CI / 2, KS = IX_CI / 32;  // element bytes, scale codes per row
@@ -276,8 +339,9 @@ __device__ __forceinline__ void indexer_fp4_body(const IndexerArgs& ia, int bx, 
   __builtin_amdgcn_sched_barrier(0);
 
   double W[QPW][HT][4];
+  int sq[QPW];
 #pragma unroll
-  for (int qq = 0; qq < QPW; ++qq)
+  for (int qq = 0; qq < QPW; ++qq) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const uint2 w4 = wraw[qq][ht];
@@ -286,6 +350,8 @@ __device__ __forceinline__ void indexer_fp4_body(const IndexerArgs& ia, int bx, 
       W[qq][ht][2] = bf16_bits_to_f32(w4.y & 0xffffu);
       W[qq][ht][3] = bf16_bits_to_f32(w4.y >> 16);
     }
+    sq[qq] = query_code_spread<HT>(qs[qq]);
+  }
   const int rounds = (c_hi - w_lo + stride * DEPTH - 1) / (stride * DEPTH);
   int it = 0;
   do {  // rounds >= 1 since w_lo < c_hi
@@ -296,9 +362,13 @@ __device__ __forceinline__ void indexer_fp4_body(const IndexerArgs& ia, int bx, 
       const uint4 b = kc[i];
       const int bs = ks[i];
       load_tile(s0 + stride * DEPTH, kc[i], ks[i]);
+      const int sk = code_spread(bs);
 #pragma unroll
       for (int qq = 0; qq < QPW; ++qq) {
-        double part = head_sum_f64<HT>(qa[qq], qs[qq], W[qq], b, bs);
+        // wave-uniform: every (head, key) pair of the tile sums exactly in float32
+        const bool fast = __ballot(sq[qq] + sk > FP4_EXACT_SPREAD) == 0;
+        double part = fast ? head_sum_f64<HT>(qa[qq], qs[qq], W[qq], b, bs)
+                           : head_sum_f64_blocks<HT>(qa[qq], qs[qq], W[qq], b, bs, g);
         part += lane_xor32_d(part);
         part += lane_xor16_d(part);
         const int s = s0 + col;
@@ -512,6 +582,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   uint4 qa[2][HT];
   int qs[2][HT];
   double W[2][HT][4];
+  int sq[2];
 #pragma unroll
   for (int qq = 0; qq < 2; ++qq) {
     const int qr = qt0 + 2 * wave + qq;
@@ -529,6 +600,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       W[qq][ht][2] = bf16_bits_to_f32(w4.y & 0xffffu);
       W[qq][ht][3] = bf16_bits_to_f32(w4.y >> 16);
     }
+    sq[qq] = query_code_spread<HT>(qs[qq]);
   }
 
   // stage loader: thread t moves element bytes 16 (t % 4) .. +15 of entry t / 4 of the stage;
@@ -565,11 +637,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // the stage's key operands: the lane's block of entry 16t + col, read once per tile
     uint4 b[NT];
     int bs[NT];
+    // bit t: tile t holds a (head, key) pair of either query whose float32 sum may be inexact
+    uint32_t slow = 0;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int r = t * 16 + col;
       b[t] = *reinterpret_cast<const uint4*>(kb + r * IF_RS + g * 16);
       bs[t] = sb[r * KS + g];
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int sk = code_spread(bs[t]);
+      slow |= (__ballot(max(sq[0], sq[1]) + sk > FP4_EXACT_SPREAD) != 0 ? 1u : 0u) << t;
     }
     f32x4 acc[2][HT];
     auto mm = [&](int u, f32x4 (&a)[HT]) {
@@ -583,12 +662,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int u = 0; u < NU; ++u) {
       if (u + 1 < NU) mm(u + 1, acc[(u + 1) & 1]);
       const int qq = u & 1, t = (u >> 1) & 3;
-      // the head sum of head_sum_f64, in the same order
       double p = 0.0;
+      if (!((slow >> (u >> 1)) & 1u)) {
+        // the head sum of head_sum_f64, in the same order
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
+        for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p = fma(W[qq][ht][e], (double)relu(acc[u & 1][ht][e]), p);
+          for (int e = 0; e < 4; ++e) p = fma(W[qq][ht][e], (double)relu(acc[u & 1][ht][e]), p);
+      } else {
+        p = head_sum_f64_blocks<HT>(qa[qq], qs[qq], W[qq], b[u >> 1], bs[u >> 1], g);
+      }
       part[t][qq] = p;
       if ((u & 7) != 7) continue;
       // a 64-entry run is complete: reduce-scatter over the lane groups as in k_indexer_tile,

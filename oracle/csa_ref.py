@@ -57,6 +57,8 @@ __all__ = [
     "visible_entries",
     "window_positions",
     "index_scores",
+    "bf16_index_scores",
+    "scores_for_topk",
     "topk",
     "attention_weights",
     "attend",
@@ -378,12 +380,77 @@ def index_scores(qI, w, KI):
 
 
 def stored_scores(scores, dims: Dims):
-    """The scores top-k selects from: as computed, or with an MXFP4 QK path the pages' BF16
-    index scores ([PT] §3.3: scores drop from FP32 to BF16 with the FP4 indexer),
-    rounded to nearest even from the exact value."""
+    """The scores top-k selects from, given float64 scores: as computed, or with an MXFP4 QK
+    path their rounding to the nearest bfloat16.  Exact when the float64 scores are; for the
+    MXFP4 path ``scores_for_topk`` gives the rounding of the exact score in every case."""
     if dims.idx_fmt == "mxfp4":
         return codecs.bf16_round_nearest(scores)
     return np.asarray(scores, np.float64)
+
+
+def _fraction_score(qI, w, k):
+    """sum_h w_h ReLU(q_h . k) in exact rational arithmetic (every float is a dyadic rational)."""
+    from fractions import Fraction
+    total = Fraction(0)
+    kf = [Fraction(float(x)) for x in k]
+    for h in range(qI.shape[0]):
+        dot = sum((Fraction(float(a)) * b for a, b in zip(qI[h], kf)), Fraction(0))
+        if dot > 0:
+            total += Fraction(float(w[h])) * dot
+    return total
+
+
+def _bf16_of_fraction(x) -> float:
+    """The bfloat16 value nearest to the rational x, ties to the even significand."""
+    from fractions import Fraction
+    if x == 0:
+        return 0.0
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()  # 2^e <= a < 2^(e+2)
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    # a = f 2^e with f in [1, 2): keep 8 significant bits, round half to even
+    n = round(a / Fraction(2) ** (e - 7))          # Python rounds a Fraction half to even
+    v = math.ldexp(float(n), e - 7)
+    return -v if x < 0 else v
+
+
+def bf16_index_scores(qI, w, KI):
+    """The pages' BF16 index scores of the FP4 indexer path ([PT] §3.3: with the QK path in
+    FP4 the scores drop from FP32 to BF16): each exact score sum_h w_h ReLU(q_h . K_s)
+    rounded once to the nearest bfloat16, ties to even.
+
+    float64 holds the score exactly only while its terms span few enough octaves (MXFP4
+    block scales can span many), so each score is first evaluated in float64 with a bound on
+    that evaluation's error: a sum of n exactly representable products carries at most
+    gamma_n = n u / (1 - n u) (u = 2^-53) times the sum of the terms' magnitudes, whatever the
+    order, and the ReLU and the head weights add the head count to n.  When both ends of that
+    interval round to the same bfloat16, so does the exact score (rounding is monotonic);
+    otherwise the score is recomputed in exact rational arithmetic and rounded from there."""
+    qI = np.asarray(qI, np.float64)
+    w = np.asarray(w, np.float64)
+    KI = np.asarray(KI, np.float64)
+    s = index_scores(qI, w, KI)
+    mag = (np.abs(KI) @ np.abs(qI).T) @ np.abs(w)
+    n = qI.shape[-1] + qI.shape[0] + 2
+    err = 2.0 * n * 2.0 ** -53 * mag
+    err = err + 2.0 ** -52 * (np.abs(s) + err)   # the rounding of s -/+ err itself
+    lo = codecs.bf16_round_nearest(s - err)
+    hi = codecs.bf16_round_nearest(s + err)
+    out = codecs.bf16_round_nearest(s)
+    for j in np.flatnonzero(lo != hi):
+        out[j] = _bf16_of_fraction(_fraction_score(qI, w, KI[j]))
+    return out
+
+
+def scores_for_topk(qI, w, KI, dims: Dims):
+    """The scores top-k selects from for one query: float64 scores (exact for E4M3 and for
+    float32 inputs of these sizes), or with an MXFP4 QK path the BF16 scores."""
+    if dims.idx_fmt == "mxfp4":
+        return bf16_index_scores(qI, w, KI)
+    return index_scores(qI, w, KI)
 
 
 def topk(scores, k: int) -> np.ndarray:
@@ -449,7 +516,7 @@ def query_step(tau: int, q, qI, w, gamma_q, sink, entries, ki, raw_of, n_entries
         if dims.top_k == 0:
             sel = np.arange(V)
         else:
-            scores = stored_scores(index_scores(qI, w, ki[:V]), dims)
+            scores = scores_for_topk(qI, w, ki[:V], dims)
             sel = topk(scores, dims.top_k)
     sel = np.asarray(sel, dtype=np.int64)
     keys = np.concatenate([np.asarray(entries)[sel], raw_of(window_positions(tau, dims.n_win))], axis=0)

@@ -103,13 +103,22 @@ def randn(shape, std, device, *ids) -> torch.Tensor:
     return torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
 
 
-def mxfp4_random(rows: int, n: int, device, *ids):
+def mxfp4_random(rows: int, n: int, device, *ids, lo: int = 100, hi: int = 140):
     """Random MXFP4 rows (n elements each): uniformly drawn element bytes [rows][n / 2] (two
-    E2M1 codes each) and block scale codes [rows][n / 32] in 124 .. 127 (2^-3 .. 1).  Drawn
+    E2M1 codes each) and block scale codes [rows][n / 32] uniform in lo .. hi (by default
+    2^-27 .. 2^13, so the blocks of one row often lie many octaves apart).  One block in 16
+    is all zeros with scale code 127 (what an all-zero block gets), and in one row in 8 the
+    last block's code is pulled 12 octaves below the row's first (clamped at lo).  Drawn
     directly as codes, so both sides decode the same bytes and no encoding is involved."""
     g = generator(device, *ids)
+    nb = n // 32
     codes = torch.randint(0, 256, (rows, n // 2), generator=g, device=device, dtype=torch.int32)
-    scales = torch.randint(124, 128, (rows, n // 32), generator=g, device=device, dtype=torch.int32)
+    scales = torch.randint(lo, hi + 1, (rows, nb), generator=g, device=device, dtype=torch.int32)
+    zero = torch.rand((rows, nb), generator=g, device=device) < 1.0 / 16
+    far = torch.rand((rows,), generator=g, device=device) < 1.0 / 8
+    scales[:, -1] = torch.where(far, (scales[:, 0] - 12).clamp(min=lo), scales[:, -1])
+    scales = torch.where(zero, torch.full_like(scales, 127), scales)
+    codes = codes.view(rows, nb, 16).masked_fill(zero.unsqueeze(-1), 0).view(rows, n // 2)
     return codes.to(torch.uint8), scales.to(torch.uint8)
 
 
@@ -170,14 +179,17 @@ def hidden(cfg: dict, seq: int, t0: int, t1: int, seed: int = SEED, device="cpu"
     return torch.cat(parts, 0)
 
 
-def queries(cfg: dict, Q: int, seed: int = SEED, device="cpu", tag="q") -> dict:
+def queries(cfg: dict, Q: int, seed: int = SEED, device="cpu", tag="q", mx_codes=(100, 140)) -> dict:
     """Per-query inputs: q [Q][n_h][c] (activation type), qI [Q][n_hI][c_I] (index format),
     w [Q][n_hI] (activation type).  All N(0,1), except MXFP4 q^I: random codes
-    (mxfp4_random), laid out per query as element bytes then scale codes."""
+    (mxfp4_random, scale codes in the range ``mx_codes``; (125, 127) is the range the MX
+    scale rule gives blocks of N(0,1) values), laid out per query as element bytes then scale
+    codes."""
     out = {"q": _store(randn((Q, cfg["n_h"], cfg["c"]), 1.0, device, seed, tag, "q"), cfg["act"])}
     if cfg["dual"] and cfg["idx_fmt"] == "mxfp4":
         # per query: n_hI rows of element bytes, then n_hI rows of scale codes
-        codes, scales = mxfp4_random(Q * cfg["n_hI"], cfg["c_I"], device, seed, tag, "qI4")
+        codes, scales = mxfp4_random(Q * cfg["n_hI"], cfg["c_I"], device, seed, tag, "qI4",
+                                     lo=mx_codes[0], hi=mx_codes[1])
         out["qI"] = torch.cat([codes.view(Q, -1), scales.view(Q, -1)], dim=1).contiguous()
     elif cfg["dual"]:
         out["qI"] = _store(randn((Q, cfg["n_hI"], cfg["c_I"]), 1.0, device, seed, tag, "qI"),

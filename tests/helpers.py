@@ -120,6 +120,35 @@ def check_topk(gpu_idx: np.ndarray, scores: np.ndarray, k: int, what: str = "") 
     return False
 
 
+# The MXFP4 indexer's stated bound: its BF16 score is the exact score rounded once unless the
+# exact score lies within this many times sum_h |w_h| sum_u |q_hu k_u| of a rounding midpoint
+# (dots are exact; the float64 head sum and the float64 sum of block terms where the block
+# scales span many octaves round at most a few dozen times, each by 2^-53 of that sum).
+BF16_SCORE_BAND = 2.0 ** -44
+
+
+def check_bf16_scores(got: np.ndarray, qI: np.ndarray, w: np.ndarray, KI: np.ndarray, what: str = ""):
+    """BF16 index scores of the MXFP4 path ([V]) against the oracle's exact ones for one query.
+    Every score must equal the oracle's, except where the exact score lies within the stated
+    band of a midpoint between two bfloat16 values; there either neighbour is accepted.
+    Returns the scores the selection is checked against: the oracle's, with any such
+    legitimately different GPU value in its place."""
+    ref = R.bf16_index_scores(qI, w, KI)
+    bad = np.flatnonzero(got != ref)
+    if len(bad) == 0:
+        return ref
+    s = R.index_scores(qI, w, KI[bad])
+    mag = (np.abs(KI[bad]) @ np.abs(qI).T) @ np.abs(w)
+    band = (BF16_SCORE_BAND + 2.0 ** -40) * mag   # plus the float64 evaluation of s itself
+    lo, hi = codecs.bf16_round_nearest(s - band), codecs.bf16_round_nearest(s + band)
+    ok = (lo != hi) & ((got[bad] == lo) | (got[bad] == hi))
+    assert ok.all(), (f"{what}: {int((~ok).sum())} bf16 scores differ from the exact score's rounding "
+                      f"outside the stated band; first at {bad[~ok][:3]}: {got[bad[~ok][:3]]} vs {ref[bad[~ok][:3]]}")
+    out = ref.copy()
+    out[bad] = got[bad]
+    return out
+
+
 def assert_close_q(got: np.ndarray, ref: np.ndarray, what: str = ""):
     d = np.abs(got - ref)
     mx = d.max()

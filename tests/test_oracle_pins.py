@@ -427,6 +427,67 @@ def test_index_scores_closed_form_and_exactness():
         assert abs(s[j] - ref) <= 1e-12 * (1 + abs(ref))
 
 
+def _bf16_nearest_exact(x: Fraction) -> float:
+    """Nearest bfloat16 to the rational x (ties to the even bit pattern), by comparing exact
+    distances to the bfloat16 values around x's float64 rounding."""
+    c = np.float32(float(x))
+    bits = int(np.array([c], np.float32).view(np.uint32)[0]) >> 16
+    cands = []
+    for b in (bits - 1, bits, bits + 1):
+        if 0 <= b < 0x10000 and (b & 0x7F80) != 0x7F80:
+            cands.append((b, float(np.array([b << 16], np.uint32).view(np.float32)[0])))
+    best = min(cands, key=lambda bv: (abs(Fraction(bv[1]) - x), bv[0] & 1))
+    return best[1]
+
+
+def _mx(rng, shape, lo, hi):
+    """Random MXFP4 rows: element codes, scale codes in lo .. hi, decoded exactly."""
+    codes = rng.integers(0, 16, shape).astype(np.uint8)
+    scales = rng.integers(lo, hi + 1, shape[:-1] + (shape[-1] // 32,)).astype(np.uint8)
+    return codecs.mxfp4_decode(codecs.mxfp4_pack(codes), scales)
+
+
+def test_bf16_index_scores_are_the_exact_score_rounded_once():
+    """BF16 scores of the FP4 path: the exact score rounded once, even where the block scales
+    span far more octaves than float64 holds (scale codes 80 .. 150: products of block scales
+    from 2^-94 to 2^46)."""
+    rng = np.random.default_rng(71)
+    qI = _mx(rng, (4, 128), 80, 150)
+    w = codecs.bf16_decode(codecs.bf16_encode(rng.standard_normal(4)))
+    K = _mx(rng, (40, 128), 80, 150)
+    K[3, 32:64] = 0.0                        # an all-zero block
+    got = R.bf16_index_scores(qI, w, K)
+    for j in range(K.shape[0]):
+        exact = Fraction(0)
+        for h in range(4):
+            dot = sum((Fraction(float(a)) * Fraction(float(b)) for a, b in zip(qI[h], K[j])), Fraction(0))
+            exact += Fraction(float(w[h])) * max(dot, Fraction(0))
+        assert got[j] == _bf16_nearest_exact(exact), j
+
+
+def test_bf16_index_scores_decide_near_midpoints_exactly():
+    """Crafted scores 1 + 2^-8 +- 2^-70: the first block gives the midpoint between the
+    bfloat16 values 1 and 1 + 2^-7, a block 62 octaves further down decides the side.  float64
+    drops the small term and rounds the tie to even (1.0) both times; the exact rounding goes
+    up for + and down for -, and an exact tie goes to the even value."""
+    def row(vals_by_block, scale_codes):
+        codes = np.zeros(128, np.uint8)
+        for blk, elems in vals_by_block.items():
+            for i, code in elems:
+                codes[32 * blk + i] = code
+        return codecs.mxfp4_decode(codecs.mxfp4_pack(codes[None]), np.array([scale_codes], np.uint8))[0]
+    # E2M1 code 2 is 1.0, code 10 is -1.0
+    q = row({0: [(0, 2)], 1: [(0, 2)], 2: [(0, 2)]}, [127, 123, 87, 127])    # 1, 2^-4, 2^-40
+    k_up = row({0: [(0, 2)], 1: [(0, 2)], 2: [(0, 2)]}, [127, 123, 97, 127])   # 1, 2^-4, 2^-30
+    k_dn = row({0: [(0, 2)], 1: [(0, 2)], 2: [(0, 10)]}, [127, 123, 97, 127])
+    k_tie = row({0: [(0, 2)], 1: [(0, 2)]}, [127, 123, 127, 127])
+    K = np.stack([k_up, k_dn, k_tie])
+    f64 = R.index_scores(q[None], np.ones(1), K)
+    assert np.all(codecs.bf16_round_nearest(f64) == 1.0)          # what float64 would give
+    got = R.bf16_index_scores(q[None], np.ones(1), K)
+    assert got[0] == 1.0 + 2.0 ** -7 and got[1] == 1.0 and got[2] == 1.0
+
+
 def _topk_bruteforce(scores, k):
     V = len(scores)
     if V <= k:
