@@ -292,6 +292,30 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
                 int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * csa_forward for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Arguments and results are those of
+ * csa_forward; the workspace is a static device array of CSA_NOALLOC_SCRATCH_BYTES inside the
+ * library (one per GPU, held from the first call on that GPU until the process ends), so the
+ * call allocates nothing.  The device current at the call is the one used; `stream` must
+ * belong to it.  Calls that overlap in time on one GPU share that array and race; calls in
+ * stream order do not (nothing in the array has to survive from one call to the next, and
+ * nothing in it has to start zeroed).
+ * Errors: as csa_forward; WORKSPACE_TOO_SMALL (before any HIP call) when the call needs more
+ * workspace than the array holds (csa_workspace_size with op FORWARD tells; decode steps of one
+ * token per sequence need a few MiB, prefill chunks of some thousand tokens fit, longer chunks
+ * need csa_forward); HIP_ERROR when the array's device address cannot be looked up.
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int csa_forward_noalloc(const csa_dims* dims, const csa_weights* w, const csa_cache* cache,
+                        const void* H, int32_t T, const int32_t* pos0, const void* q, const void* qI,
+                        const void* wI, const float* gamma_q, const float* sink, void* out,
+                        int32_t* idx_out, hipStream_t stream);
+
+/* Size of csa_forward_noalloc's static scratch (CSA_NOALLOC_SCRATCH_BYTES). */
+size_t csa_noalloc_scratch_bytes(void);
+
+/*
  * The projections around the attention core: the low-rank query path before it (reading
  * notes "DeepSeekV4技术报告阅读笔记" §2.3.2 eqs. 13-15 and §2.3.3 eq. 18: one latent
  * c^Q = h W^DQ of width d_c feeds both the attention queries q = c^Q W^UQ and the indexer

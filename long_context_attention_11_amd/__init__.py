@@ -19,7 +19,8 @@ __all__ = [
     "csa_abi_version", "csa_row_bytes", "csa_state_width", "csa_state_rows",
     "csa_workspace_size", "csa_compress", "csa_index_topk", "csa_attend", "csa_forward",
     "csa_index_scores", "csa_topk", "csa_topk_workspace_size", "ProjWeights", "csa_query_project",
-    "csa_query_project_workspace_size", "csa_output_project", "csa_output_project_workspace_size", "OP_COMPRESS", "OP_INDEX_TOPK", "OP_ATTEND", "OP_FORWARD",
+    "csa_query_project_workspace_size", "csa_output_project", "csa_output_project_workspace_size",
+    "csa_forward_noalloc", "csa_noalloc_scratch_bytes", "OP_COMPRESS", "OP_INDEX_TOPK", "OP_ATTEND", "OP_FORWARD",
     "FMT_F32", "FMT_BF16", "FMT_E4M3", "FMT_E4M3_BF16", "FMT_MXFP4", "EXPORTED_SYMBOLS",
 ]
 
@@ -32,7 +33,8 @@ EXPORTED_SYMBOLS = (
     "csa_state_width", "csa_state_rows", "csa_workspace_size", "csa_compress",
     "csa_index_topk", "csa_attend", "csa_forward", "csa_index_scores", "csa_topk",
     "csa_topk_workspace_size", "csa_query_project", "csa_query_project_workspace_size",
-    "csa_output_project", "csa_output_project_workspace_size",
+    "csa_output_project", "csa_output_project_workspace_size", "csa_forward_noalloc",
+    "csa_noalloc_scratch_bytes",
 )
 
 
@@ -110,6 +112,11 @@ def load():
     lib.csa_forward.restype = ctypes.c_int
     lib.csa_forward.argtypes = [dims_p, ctypes.POINTER(_Weights), ctypes.POINTER(_Cache), P, I32, P,
                                 P, P, P, P, P, P, P, P, SZ, P]
+    lib.csa_forward_noalloc.restype = ctypes.c_int
+    lib.csa_forward_noalloc.argtypes = [dims_p, ctypes.POINTER(_Weights), ctypes.POINTER(_Cache), P, I32, P,
+                                        P, P, P, P, P, P, P, P]
+    lib.csa_noalloc_scratch_bytes.restype = SZ
+    lib.csa_noalloc_scratch_bytes.argtypes = []
     pw_p = ctypes.POINTER(_ProjWeights)
     lib.csa_query_project_workspace_size.restype = SZ
     lib.csa_query_project_workspace_size.argtypes = [dims_p, pw_p, I32]
@@ -334,6 +341,19 @@ def csa_forward(dims: Dims, w: Weights, cache: Cache, H, T: int, pos0, q, qI, wI
                               ctypes.byref(cache.struct()), _ptr(H), T, _ptr(pos0), _ptr(q),
                               _ptr(qI), _ptr(wI), _ptr(gamma_q), _ptr(sink), _ptr(out),
                               _ptr(idx_out), wp, wn, _stream(stream)))
+
+
+def csa_forward_noalloc(dims: Dims, w: Weights, cache: Cache, H, T: int, pos0, q, qI, wI, gamma_q, sink,
+                        out, idx_out=None, stream=None):
+    """csa_forward on the library's static scratch: no workspace argument, nothing allocated."""
+    _check(load().csa_forward_noalloc(ctypes.byref(dims.struct()), ctypes.byref(w.struct()),
+                                      ctypes.byref(cache.struct()), _ptr(H), T, _ptr(pos0), _ptr(q),
+                                      _ptr(qI), _ptr(wI), _ptr(gamma_q), _ptr(sink), _ptr(out),
+                                      _ptr(idx_out), _stream(stream)))
+
+
+def csa_noalloc_scratch_bytes() -> int:
+    return load().csa_noalloc_scratch_bytes()
 
 
 class ProjWeights:

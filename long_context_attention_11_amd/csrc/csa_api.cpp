@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "csa_internal.h"
@@ -350,11 +351,10 @@ int csa_attend(const csa_dims* dims, const csa_cache* cache, const void* q, cons
   return CSA_OK;
 }
 
-int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cache, const void* H,
-                int32_t T, const int32_t* pos0, const void* q, const void* qI, const void* wI,
-                const float* gamma_q, const float* sink, void* out, int32_t* idx_out, void* ws,
-                size_t ws_bytes, hipStream_t stream) {
-  g_last_error.clear();
+// The host-side checks of a forward call, and the least workspace it can run in (*min_ws).
+static int forward_checks(const csa_dims* dims, const csa_weights* w, const csa_cache* cache,
+                          const void* H, int32_t T, const int32_t* pos0, const void* q, const void* qI,
+                          const void* wI, void* out, int32_t* idx_out, size_t* min_ws) {
   int st = check_dims(dims);
   if (st) return st;
   const csa_dims& d = *dims;
@@ -370,15 +370,32 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
     return fail(CSA_ERR_UNSUPPORTED, "cap exceeds the entries the top-k kernels handle for this top_k");
   if ((st = attend_checks(d, *cache, d.dual != 0))) return st;
   const int32_t Qn = cache->B * T;
+  Layout L;
+  L.add(0, 2 * sizeof(int32_t) * (size_t)Qn);
+  L.add(1, (d.dual && !idx_out) ? sizeof(int32_t) * (size_t)Qn * d.top_k : 0);
+  size_t min_phase = std::max(compress_ws(d, cache->B, T), attend_workspace_bytes(d, Qn, cache->cap, d.dual ? 0 : 1));
+  if (d.dual) min_phase = std::max(min_phase, index_ws(d, 1, cache->cap));
+  *min_ws = L.total + min_phase;
+  return CSA_OK;
+}
+
+int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cache, const void* H,
+                int32_t T, const int32_t* pos0, const void* q, const void* qI, const void* wI,
+                const float* gamma_q, const float* sink, void* out, int32_t* idx_out, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  size_t min_ws = 0;
+  int st = forward_checks(dims, w, cache, H, T, pos0, q, qI, wI, out, idx_out, &min_ws);
+  if (st) return st;
+  const csa_dims& d = *dims;
+  if (!ws || ws_bytes < min_ws)
+    return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "forward needs at least " + std::to_string(min_ws) + " bytes of workspace");
+  const int32_t Qn = cache->B * T;
   // fixed part of the workspace, then the largest query chunk the rest allows
   Layout L;
   L.add(0, 2 * sizeof(int32_t) * (size_t)Qn);
   L.add(1, (d.dual && !idx_out) ? sizeof(int32_t) * (size_t)Qn * d.top_k : 0);
   const size_t fixed = L.total;
-  size_t min_phase = std::max(compress_ws(d, cache->B, T), attend_workspace_bytes(d, Qn, cache->cap, d.dual ? 0 : 1));
-  if (d.dual) min_phase = std::max(min_phase, index_ws(d, 1, cache->cap));
-  if (!ws || ws_bytes < fixed + min_phase)
-    return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "forward needs at least " + std::to_string(fixed + min_phase) + " bytes of workspace");
   int32_t* q_seq = (int32_t*)((char*)ws + L.off[0]);
   int32_t* q_pos = q_seq + Qn;
   int32_t* idx = idx_out ? idx_out : (int32_t*)((char*)ws + L.off[1]);
@@ -449,6 +466,68 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
                     phase_ws, stream);
   if (e != hipSuccess) return hip_fail(e, "attend launch");
   return CSA_OK;
+}
+
+// ------------------------------------------------------------------ forward without allocation
+
+}  // extern "C"
+
+// Scratch of csa_forward_noalloc: a file-scope device array, one copy per GPU, held from the
+// library's load until the process ends.  In host code `scratch` names a host-side stand-in,
+// not a device address; the device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) uint8_t scratch[CSA_NOALLOC_SCRATCH_BYTES];
+
+namespace csa {
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SCRATCH_MAX_DEVICES];   // device address of `scratch` per device, once looked up
+
+// The current device's copy of `scratch` (looked up on the first call on that device, with
+// that device current, and kept).
+int device_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+    return fail(CSA_ERR_UNSUPPORTED, "device index beyond the scratch table (" + std::to_string(dev) + ")");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return CSA_OK;
+}
+
+}  // namespace
+}  // namespace csa
+
+extern "C" {
+
+size_t csa_noalloc_scratch_bytes(void) { return CSA_NOALLOC_SCRATCH_BYTES; }
+
+int csa_forward_noalloc(const csa_dims* dims, const csa_weights* w, const csa_cache* cache,
+                        const void* H, int32_t T, const int32_t* pos0, const void* q, const void* qI,
+                        const void* wI, const float* gamma_q, const float* sink, void* out,
+                        int32_t* idx_out, hipStream_t stream) {
+  g_last_error.clear();
+  size_t min_ws = 0;
+  int st = forward_checks(dims, w, cache, H, T, pos0, q, qI, wI, out, idx_out, &min_ws);
+  if (st) return st;
+  if (min_ws > CSA_NOALLOC_SCRATCH_BYTES)
+    return fail(CSA_ERR_WORKSPACE_TOO_SMALL,
+                "csa_forward_noalloc: this call needs at least " + std::to_string(min_ws) +
+                    " bytes of scratch, more than the static " + std::to_string((size_t)CSA_NOALLOC_SCRATCH_BYTES) +
+                    "; call csa_forward with a workspace instead");
+  void* ws = nullptr;
+  if ((st = device_scratch(&ws))) return st;
+  st = csa_forward(dims, w, cache, H, T, pos0, q, qI, wI, gamma_q, sink, out, idx_out, ws,
+                   CSA_NOALLOC_SCRATCH_BYTES, stream);
+  return st;
 }
 
 // ------------------------------------------------------------------ projections around the path

@@ -113,6 +113,13 @@ def test_null_and_workspace_errors_without_a_device():
     assert lib.csa_forward(ctypes.byref(ds), ctypes.byref(w), ctypes.byref(cache), fake, 64, fake,
                            fake, fake, fake, None, None, fake, None, fake, 1 << 30, None) == 1
     assert lib.csa_status_string(3) == b"workspace too small"
+    # the allocation-free forward: a 32768-token chunk needs more than its static scratch, which
+    # it reports before any HIP call
+    big = L._Cache(1, 270336, 32768 + 128, fake, fake, fake, fake, fake, fake)
+    st = lib.csa_forward_noalloc(ctypes.byref(ds), ctypes.byref(w), ctypes.byref(big), fake, 32768, fake,
+                                 fake, fake, fake, None, None, fake, fake, None)
+    assert st == 3 and b"static" in lib.csa_last_error()
+    assert L.csa_noalloc_scratch_bytes() == 64 << 20
 
 
 def test_workspace_sizes_are_consistent():
