@@ -38,6 +38,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12        # bytes/s, MI355X HBM3E
 BF16_PEAK = 2.5e15       # dense bf16 MFMA FLOP/s
+FP8_PEAK = 5.0e15        # dense fp8 MFMA FLOP/s
+FP4_PEAK = 10.1e15       # dense fp4 (MXFP4) MFMA FLOP/s
 MALL_BYTES = 256 << 20   # MI355X last-level (Infinity) cache
 CAL_BYTES = 256 << 20    # plain device copy that calibrates the FETCH_SIZE / WRITE_SIZE counters
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_c2_traffic.txt")
@@ -93,6 +95,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="with the default c2 workload, skip the c3 decode, c4a prefill and batch-series runs")
     return ap.parse_args()
 
 
@@ -483,6 +487,16 @@ def run_decode(args, cfg):
                            "achieved": round(alg / dur / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                            "frac": round(alg / dur / HBM_PEAK, 4), "traffic": None,
                            "alg_bytes_per_launch": alg, "avg_launch_us": round(kt["attend"], 2)}
+    if dual:
+        rows = k + cfg["n_win"]
+        at_bytes = B * (rows * synth_row_bytes(cfg) + 2 * 2 * cfg["n_h"] * cfg["c"] + 4 * k)
+        at_flops = B * 2.0 * 2.0 * cfg["n_h"] * cfg["c"] * rows
+        t_at = kt["attend"] * 1e-6
+        res["roofline_attention"] = {
+            "bound": "hbm", "kernel": "attention (csa_attend: k_attend_hs + combine)",
+            "achieved": round(at_bytes / t_at / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+            "frac": round(at_bytes / t_at / HBM_PEAK, 4), "alg_bytes_per_launch": at_bytes,
+            "mfma_frac": round(at_flops / t_at / BF16_PEAK, 4), "avg_launch_us": round(kt["attend"], 2)}
     res["kernels_us"] = {k_: round(v, 2) for k_, v in kt.items()}
     res["graph_replay_matches_eager"] = bool(ok)
     res["cache_build_s"] = round(t_build, 2)
@@ -516,6 +530,50 @@ def run_decode(args, cfg):
     if not args.no_cpu and not args.layer:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     return res, ok
+
+
+def prefill_rooflines(L, cfg, dims, cache, qs, W, idx, out, p0, T, q_chunk, ws):
+    """The chunk's dominant kernels timed on their own with the forward's grids: the indexer
+    on its first q_chunk queries (the forward runs it chunk by chunk, as csa_index_scores_grouped
+    does), and the attention over all T queries with the forward's selection."""
+    import torch
+    m, cap = cfg["m"], cache.cap
+    Qc = q_chunk
+    fp4 = cfg["idx_fmt"] == "mxfp4"
+    q_seq = torch.zeros(Qc, dtype=torch.int32, device="cuda")
+    q_pos = torch.arange(p0, p0 + Qc, dtype=torch.int32, device="cuda")
+    scores = torch.empty((Qc, cap), dtype=torch.bfloat16 if fp4 else torch.float32, device="cuda")
+    qI = qs["qI"][:Qc].contiguous()
+    wI = qs["w"][:Qc].contiguous()
+    t_ix = kernel_time_us([lambda: L.csa_index_scores_grouped(dims, cache, qI, wI, q_seq, q_pos, Qc, scores, cap)],
+                          reps=5, rounds=3)
+    del scores
+    flops = 2.0 * cfg["n_hI"] * cfg["c_I"] * sum(min((p0 + t) // m, cap) for t in range(Qc))
+    peak = FP4_PEAK if fp4 else BF16_PEAK
+    ix = {"bound": "mfma", "kernel": "k_indexer_tile_fp4" if fp4 else "k_indexer_tile", "queries_per_launch": Qc,
+          "achieved": round(flops / (t_ix * 1e-6) / 1e12, 1), "peak": peak / 1e12, "unit": "TFLOP/s",
+          "frac": round(flops / (t_ix * 1e-6) / peak, 4), "traffic": None,
+          "alg_flop_per_launch": flops, "avg_launch_us": round(t_ix, 1),
+          "contraction": "MXFP4 block-scaled MFMA" if fp4 else "bf16 MFMA on E4M3 widened exactly (fp8 MFMA inexact)"}
+    if not fp4:
+        ix["frac_of_fp8_peak"] = round(flops / (t_ix * 1e-6) / FP8_PEAK, 4)
+    q_seq_all = torch.zeros(T, dtype=torch.int32, device="cuda")
+    q_pos_all = torch.arange(p0, p0 + T, dtype=torch.int32, device="cuda")
+    # (the forward's workspace holds the sparse attention's partials)
+    t_at = kernel_time_us([lambda: L.csa_attend(dims, cache, qs["q"], W["gamma_q"], W["sink"], q_seq_all, q_pos_all,
+                                                T, idx, out, ws)], reps=5, rounds=3)
+    rows = cfg["top_k"] + cfg["n_win"]
+    at_bytes = T * (rows * synth_row_bytes(cfg) + 2 * 2 * cfg["n_h"] * cfg["c"] + 4 * cfg["top_k"])
+    at_flops = T * 2.0 * 2.0 * cfg["n_h"] * cfg["c"] * rows
+    at = {"bound": "mfma", "kernel": "k_attend_hs (prefill)", "achieved": round(at_flops / (t_at * 1e-6) / 1e12, 1),
+          "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s", "frac": round(at_flops / (t_at * 1e-6) / BF16_PEAK, 4),
+          "alg_flop_per_launch": at_flops, "alg_bytes_per_launch": at_bytes,
+          "hbm_frac_without_reuse": round(at_bytes / (t_at * 1e-6) / HBM_PEAK, 4), "avg_launch_us": round(t_at, 1)}
+    return {"roofline": ix, "roofline_attention": at}
+
+
+def synth_row_bytes(cfg):
+    return cfg["c"] - cfg["rope_dim"] + 2 * cfg["rope_dim"] if cfg["kv_fmt"] != "f32" else 4 * cfg["c"]
 
 
 def run_prefill(args, cfg):
@@ -599,6 +657,8 @@ def run_prefill(args, cfg):
         Vs = [min((p0 + t) // cfg["m"], cap) for t in range(T)]
         flops = 2.0 * cfg["n_hI"] * cfg["c_I"] * sum(Vs)
         res["indexer_tflop_per_step"] = round(flops / 1e12, 2)
+        if not args.layer:
+            res.update(prefill_rooflines(L, cfg, dims, cache, qs, W, idx, out, p0, T, q_chunk, ws))
     if args.layer:
         d, dc, nq = cfg["d"], cfg["d_c"], cfg["n_h"] * cfg["c"]
         res["projection_tflop_per_step"] = round(2.0 * T * (d * (dc + cfg["n_hI"]) + dc * (nq + cfg["n_hI"] * cfg["c_I"])
@@ -608,6 +668,52 @@ def run_prefill(args, cfg):
     if not args.no_cpu and cfg["name"] != "c1" and not args.layer:
         res["cpu_baseline"] = cpu_baseline_prefill(cfg, args.cpu_seconds)
     return res, True
+
+
+def attention_batch_series(cfg, batches=(16, 32, 64, 128, 256), reps=20):
+    """Decode attention (csa_attend, the launches the step runs) at the Flash shape for B
+    queries, each over its own sequence: 512 selected entries drawn at random (a fresh draw
+    per launch) plus the 128-row window.  Caches large enough (capacity up to 262144 entries
+    per sequence, at most ~20 GB) that the rows a launch gathers were not fetched by the
+    launches just before it, so the bytes come from HBM.  Shows where the latency floor of a
+    small batch gives way to the bandwidth bound."""
+    import torch
+
+    import long_context_attention_11_amd as L
+    import synth
+    dims = L.Dims.from_config(cfg)
+    k, nw, rb = cfg["top_k"], cfg["n_win"], synth_row_bytes(cfg)
+    r = cfg["c"] - cfg["rope_dim"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    out_rows = []
+    for B in batches:
+        cap = max(4096, min(262144, (20 << 30) // (B * rb)))
+        cache = L.Cache(dims, B=B, cap=cap, win_cap=nw, device="cuda")
+        for t in (cache.kv, cache.win):
+            t.copy_(torch.randint(0, 0x60, tuple(t.shape), generator=g, device="cuda", dtype=torch.uint8))
+            t.view(t.shape[0], t.shape[1], rb)[:, :, r + 1::2] = 0x3F   # bf16 RoPE dims of magnitude ~1
+        tau = 4 * cap
+        cache.n_entries.fill_(cap)
+        cache.win_pos.copy_(torch.arange(tau - nw + 1, tau + 1, dtype=torch.int32, device="cuda")
+                            .roll((tau + 1) % nw).repeat(B, 1))
+        qs = synth.queries(cfg, B, device="cuda", tag="series")
+        W = {"gamma_q": torch.ones(cfg["c"], device="cuda"),
+             "sink": synth.randn((cfg["n_h"],), 0.1 ** 0.5, "cuda", 0, "sink")}
+        q_seq = torch.arange(B, dtype=torch.int32, device="cuda")
+        q_pos = torch.full((B,), tau, dtype=torch.int32, device="cuda")
+        idxs = [torch.sort(torch.randint(0, cap, (B, k), generator=g, device="cuda", dtype=torch.int32), 1).values
+                for _ in range(reps)]
+        out = torch.empty((B, cfg["n_h"], cfg["c"]), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_ATTEND, Q=B, cap=cap)), dtype=torch.uint8, device="cuda")
+        us = kernel_time_us([lambda i=i: L.csa_attend(dims, cache, qs["q"], W["gamma_q"], W["sink"], q_seq, q_pos, B,
+                                                      idxs[i], out, ws) for i in range(reps)], reps=reps)
+        byt = B * ((k + nw) * rb + 2 * 2 * cfg["n_h"] * cfg["c"] + 4 * k)
+        out_rows.append({"B": B, "us": round(us, 2), "alg_bytes": byt, "GB_s": round(byt / us / 1e3, 1),
+                         "frac_hbm": round(byt / (us * 1e-6) / HBM_PEAK, 4), "cache_entries_per_seq": cap})
+        del cache, idxs, out, ws
+        torch.cuda.empty_cache()
+    return out_rows
 
 
 def main():
@@ -625,6 +731,26 @@ def main():
         res, ok = run_decode(args, cfg)
     else:
         res, ok = run_prefill(args, cfg)
+    if args.config == "c2" and not args.layer and not args.no_extra:
+        # the rest of the metric in the same run: decode at 1M context (Pro shape), prefill
+        # tokens/s after a 1M-token prefix, and the decode attention's batch series
+        print(f"[bench] c2 done ({res['value']} queries/s); c3 decode", file=sys.stderr, flush=True)
+        extra = {}
+        sub = argparse.Namespace(**{**vars(args), "steps": 20, "warmup": 5, "no_cpu": True, "copies": None})
+        r3, ok3 = run_decode(sub, synth.config("c3"))
+        extra["c3_decode"] = {k_: r3[k_] for k_ in ("metric", "value", "unit", "ms_per_step", "roofline",
+                                                    "roofline_attention", "kernels_us", "graph_replay_matches_eager")}
+        extra["c3_decode"]["workload"] = r3["config"]["workload"]
+        print(f"[bench] c3 done ({r3['value']} queries/s); c4a prefill", file=sys.stderr, flush=True)
+        sub = argparse.Namespace(**{**vars(args), "steps": 3, "warmup": 1, "no_cpu": True})
+        r4, _ = run_prefill(sub, synth.config("c4a"))
+        extra["c4a_prefill"] = {k_: r4[k_] for k_ in ("metric", "value", "unit", "ms_per_step", "roofline",
+                                                      "roofline_attention", "indexer_tflop_per_step")}
+        extra["c4a_prefill"]["workload"] = r4["config"]["workload"]
+        print(f"[bench] c4a done ({r4['value']} tokens/s); attention batch series", file=sys.stderr, flush=True)
+        extra["decode_attention_batch_series"] = attention_batch_series(synth.config("c2"))
+        res["extra"] = extra
+        ok = ok and ok3
     print(json.dumps(res), flush=True)
     if not ok:
         sys.exit(1)

@@ -244,6 +244,18 @@ int csa_index_scores(const csa_dims* dims, const csa_cache* cache, const void* q
                      void* scores, int64_t ld, hipStream_t stream);
 
 /*
+ * csa_index_scores for queries laid out as a prefill chunk's are (query b*T + t is token t of
+ * sequence b, T a multiple of 16): every aligned group of 16 queries (0-15, 16-31, ...)
+ * belongs to one sequence, which the caller guarantees (it cannot be checked on the host).
+ * The scores are those of csa_index_scores, bit for bit; the kernel shares each key tile
+ * among a group's 16 queries (the indexer csa_forward runs on a chunk of such queries).
+ * Errors: as csa_index_scores.
+ */
+int csa_index_scores_grouped(const csa_dims* dims, const csa_cache* cache, const void* qI,
+                             const void* w, const int32_t* q_seq, const int32_t* q_pos, int32_t Q,
+                             void* scores, int64_t ld, hipStream_t stream);
+
+/*
  * The top-k selection on its own (reading notes eq. 17) over scores [Q][ld] as written by
  * csa_index_scores (float32, or bfloat16 with idx_fmt MXFP4): idx_out[Q][top_k] as in csa_index_topk.  ws as csa_workspace_size(
  * INDEX_TOPK) minus the score buffer: csa_topk_workspace_size(), which is 0 for caches of

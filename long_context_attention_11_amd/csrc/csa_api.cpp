@@ -292,6 +292,23 @@ int csa_index_scores(const csa_dims* dims, const csa_cache* cache, const void* q
   return CSA_OK;
 }
 
+int csa_index_scores_grouped(const csa_dims* dims, const csa_cache* cache, const void* qI, const void* w,
+                             const int32_t* q_seq, const int32_t* q_pos, int32_t Q, void* scores,
+                             int64_t ld, hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!dims->dual) return fail(CSA_ERR_INVALID_ARGUMENT, "HCA (dual = 0) has no indexer");
+  if ((st = check_cache(dims, cache, false))) return st;
+  if (!qI || !w || !q_seq || !q_pos || !scores)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "qI, w, q_seq, q_pos and scores must be set");
+  if (Q < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "Q must be >= 1");
+  if (ld < cache->cap) return fail(CSA_ERR_INVALID_ARGUMENT, "ld must be >= cap");
+  hipError_t e = launch_indexer(*dims, *cache, qI, w, q_seq, q_pos, Q, scores, ld, true, stream);
+  if (e != hipSuccess) return hip_fail(e, "indexer launch");
+  return CSA_OK;
+}
+
 size_t csa_topk_workspace_size(const csa_dims* dims, int32_t Q, int32_t cap) {
   if (check_dims(dims) != CSA_OK || Q < 1 || cap < 1) return 0;
   return topk_workspace_bytes(*dims, Q, cap);

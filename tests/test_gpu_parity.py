@@ -440,6 +440,28 @@ def test_q_forward_decode_steps(idx_fmt):
             assert_close_q(go, o_ref, f"decode out seq {b} tau={tau}")
 
 
+@pytest.mark.parametrize("idx_fmt", ["e4m3", "mxfp4"])
+def test_index_scores_grouped_equals_plain(idx_fmt):
+    """csa_index_scores_grouped (key tiles shared by 16 queries of one sequence, the prefill
+    kernel) gives the scores of csa_index_scores bit for bit: 48 queries in three groups over
+    two sequences of 3001 entries (ragged tail), positions spread so the visible counts differ
+    within a group."""
+    cfg = _qcfg(idx_fmt=idx_fmt)
+    N = 3001
+    seqs = [0] * 32 + [1] * 16
+    taus = [(b, 4 * 100 + 97 * i) for i, b in enumerate(seqs)]
+    dims, cache, qs, W, q_seq, q_pos = _synthetic_decode_setup(cfg, 2, N, 128, taus, seed=13)
+    Q = len(taus)
+    sdt = torch.bfloat16 if idx_fmt == "mxfp4" else torch.float32
+    a = torch.zeros((Q, N), dtype=sdt, device=DEV)
+    b = torch.zeros((Q, N), dtype=sdt, device=DEV)
+    L.csa_index_scores(dims, cache, qs["qI"], qs["w"], q_seq, q_pos, Q, a, N)
+    L.csa_index_scores_grouped(dims, cache, qs["qI"], qs["w"], q_seq, q_pos, Q, b, N)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16) if idx_fmt == "mxfp4" else a.view(torch.int32),
+                       b.view(torch.int16) if idx_fmt == "mxfp4" else b.view(torch.int32))
+
+
 def test_deterministic_repeat():
     """Two runs of index + top-k + attend on the same inputs give identical bits."""
     cfg = _qcfg()
