@@ -94,6 +94,8 @@ def parse():
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2fp4", "c3", "c4a", "c4afp4", "c4b", "c4bfp4", "c5"])
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--paged", action="store_true",
+                    help="decode on a paged cache (128-token pages dealt over a shuffled pool)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-extra", action="store_true",
                     help="with the default c2 workload, skip the c3 decode, c4a prefill and batch-series runs")
@@ -111,10 +113,21 @@ def lib_weights(L, W, dual):
                      W["gamma_kv"])
 
 
-def build_cache(L, synth, cfg, dims, lw, dev, B, n_tokens, cap, win_cap, chunk=8192):
-    """Compress n_tokens synthetic tokens of each sequence into a fresh cache (untimed)."""
+PAGE_TOKENS = 128   # one page holds 32 CSA entries or 1 HCA entry
+
+
+def build_cache(L, synth, cfg, dims, lw, dev, B, n_tokens, cap, win_cap, chunk=8192, paged=False):
+    """Compress n_tokens synthetic tokens of each sequence into a fresh cache (untimed).
+    Paged: every sequence's pages are dealt at random over one pool (a seeded permutation)."""
     import torch
-    cache = L.Cache(dims, B=B, cap=cap, win_cap=win_cap, device=dev)
+    if paged:
+        E = PAGE_TOKENS // cfg["m"]
+        mb = -(-cap // E)
+        perm = torch.randperm(B * mb, generator=torch.Generator().manual_seed(7)).to(torch.int32)
+        cache = L.Cache(dims, B=B, cap=cap, win_cap=win_cap, device=dev, block_table=perm.view(B, mb).to(dev),
+                        page_tokens=PAGE_TOKENS, n_pages=B * mb)
+    else:
+        cache = L.Cache(dims, B=B, cap=cap, win_cap=win_cap, device=dev)
     chunk = min(chunk, n_tokens)
     ws = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_COMPRESS, B=B, T=chunk)), dtype=torch.uint8, device=dev)
     for t0 in range(0, n_tokens, chunk):
@@ -357,7 +370,8 @@ def run_decode(args, cfg):
     tau_start = m * N0
     tau = tau_start
     t_build = time.perf_counter()
-    base = build_cache(L, synth, cfg, dims, lw, dev, B, tau_start, N, cfg["n_win"])
+    paged = getattr(args, "paged", False)
+    base = build_cache(L, synth, cfg, dims, lw, dev, B, tau_start, N, cfg["n_win"], paged=paged)
     t_build = time.perf_counter() - t_build
     caches = [base] + [clone_cache(base) for _ in range(copies - 1)]
 
@@ -477,7 +491,7 @@ def run_decode(args, cfg):
         res["roofline"] = {"bound": "hbm", "kernel": f"indexer ({kname})",
                            "achieved": round(alg / dur / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                            "frac": round(alg / dur / HBM_PEAK, 4),
-                           "traffic": measured_traffic() if cfg["name"] == "c2" else None,
+                           "traffic": measured_traffic() if cfg["name"] == "c2" and not paged else None,
                            "alg_bytes_per_launch": alg, "avg_launch_us": round(kt["index_scores"], 2)}
     else:
         rows = N + cfg["n_win"]
@@ -508,6 +522,9 @@ def run_decode(args, cfg):
                   "128 heads x 512, indexer 64x128, top-k 1024, n_win 128",
             "c5": "HCA decode, 8 seqs x 1048576-token context (8192 entries, m'=128), d=4096, "
                   "64 heads x 512, dense, n_win 128"}[cfg["name"]]
+    if paged:
+        desc += (f"; paged cache: {PAGE_TOKENS}-token pages ({PAGE_TOKENS // m} entries) dealt over a shuffled "
+                 f"pool through a per-sequence block table")
     if args.layer:
         # the projections stream their weights once per step: HBM-bound at decode
         d, dc, nq = cfg["d"], cfg["d_c"], cfg["n_h"] * cfg["c"]
@@ -741,7 +758,16 @@ def main():
         extra["c3_decode"] = {k_: r3[k_] for k_ in ("metric", "value", "unit", "ms_per_step", "roofline",
                                                     "roofline_attention", "kernels_us", "graph_replay_matches_eager")}
         extra["c3_decode"]["workload"] = r3["config"]["workload"]
-        print(f"[bench] c3 done ({r3['value']} queries/s); c4a prefill", file=sys.stderr, flush=True)
+        print(f"[bench] c3 done ({r3['value']} queries/s); c2 decode on a paged cache", file=sys.stderr, flush=True)
+        sub = argparse.Namespace(**{**vars(args), "steps": 20, "warmup": 5, "no_cpu": True, "copies": None,
+                                    "paged": True})
+        rp, okp = run_decode(sub, cfg)
+        extra["c2_decode_paged"] = {k_: rp[k_] for k_ in ("metric", "value", "unit", "ms_per_step", "roofline",
+                                                          "roofline_attention", "kernels_us",
+                                                          "graph_replay_matches_eager")}
+        extra["c2_decode_paged"]["workload"] = rp["config"]["workload"]
+        ok3 = ok3 and okp
+        print(f"[bench] paged c2 done ({rp['value']} queries/s); c4a prefill", file=sys.stderr, flush=True)
         sub = argparse.Namespace(**{**vars(args), "steps": 3, "warmup": 1, "no_cpu": True})
         r4, _ = run_prefill(sub, synth.config("c4a"))
         extra["c4a_prefill"] = {k_: r4[k_] for k_ in ("metric", "value", "unit", "ms_per_step", "roofline",

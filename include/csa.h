@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -135,7 +135,8 @@ typedef struct csa_weights {
 /*
  * Per-sequence cache, all caller-owned device memory.
  *   B        number of sequences.
- *   cap      entry capacity per sequence; entries past it are not stored.
+ *   cap      entry capacity per sequence; entries past it are not stored.  With a block
+ *            table, the logical capacity: at most max_blocks * page_tokens / m.
  *   win_cap  window ring rows per sequence, >= n_win.  Token j's raw row sits in slot
  *            j % win_cap.  A compress call of T tokens needs win_cap >= T + n_win - 1 for
  *            the chunk's own queries to find their window rows.
@@ -150,6 +151,24 @@ typedef struct csa_weights {
  *                                  HCA; P = 4c + 4c_I for CSA, 2c for HCA), slot j % S, so
  *                                  that a block split across calls still folds.
  * Successive csa_compress calls on a sequence must cover consecutive positions.
+ *
+ * Paged layout (PaperTrace "02 · DeepSeek-V4: 压缩注意力撑起 1M 上下文" §3.3, KV-cache
+ * paragraph: compressed entries are kept in blocks of lcm(m, m') = 128 raw tokens, and each
+ * request holds one fixed-size state block for the window KV and the uncompressed tail).
+ * With block_table set, kv and ki are pools of n_pages pages instead of per-sequence runs:
+ *   page_tokens  raw tokens per page (128 = lcm(4, 128) serves CSA and HCA layers with one
+ *                table); a multiple of m, so a page holds E = page_tokens / m entries.
+ *   block_table  [B][max_blocks] int32 device array: logical page j of sequence b (its
+ *                entries j E .. j E + E - 1) is pool page block_table[b][j].  Page ids are not
+ *                validated (they live in device memory); they are clamped to [0, n_pages).
+ *   kv           [n_pages][E][row_bytes]; entry i of sequence b at page
+ *                block_table[b][i / E], row i % E.
+ *   ki           E4M3 / F32: [n_pages][E][c_I]; MXFP4: per page E rows of c_I / 2 element
+ *                bytes, then E rows of c_I / 32 scale codes.
+ *   win, win_pos, state, n_entries stay per sequence: they are the request's state block.
+ * The table is read, never written: the caller maps pages before a call writes into them.
+ * With block_table NULL (max_blocks, page_tokens and n_pages ignored) the layout is the
+ * contiguous one above.
  */
 typedef struct csa_cache {
   int32_t B;
@@ -161,6 +180,10 @@ typedef struct csa_cache {
   void* win;
   int32_t* win_pos;
   float* state;
+  const int32_t* block_table;
+  int32_t max_blocks;
+  int32_t page_tokens;
+  int32_t n_pages;
 } csa_cache;
 
 /* Version of this header the library was built from (CSA_ABI_VERSION). */

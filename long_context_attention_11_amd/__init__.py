@@ -64,7 +64,12 @@ class _ProjWeights(ctypes.Structure):
 class _Cache(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("cap", ctypes.c_int32), ("win_cap", ctypes.c_int32),
                 ("kv", ctypes.c_void_p), ("ki", ctypes.c_void_p), ("n_entries", ctypes.c_void_p),
-                ("win", ctypes.c_void_p), ("win_pos", ctypes.c_void_p), ("state", ctypes.c_void_p)]
+                ("win", ctypes.c_void_p), ("win_pos", ctypes.c_void_p), ("state", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int32),
+                ("page_tokens", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
+
+
+ABI_VERSION = 2   # the csa.h version these structures follow
 
 
 _lib = None
@@ -86,6 +91,9 @@ def load():
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     dims_p = ctypes.POINTER(_Dims)
     lib.csa_abi_version.restype = ctypes.c_int
+    if lib.csa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} was built from csa.h version {lib.csa_abi_version()}, "
+                           f"the binding expects {ABI_VERSION}: rebuild it")
     lib.csa_status_string.restype = ctypes.c_char_p
     lib.csa_status_string.argtypes = [ctypes.c_int]
     lib.csa_last_error.restype = ctypes.c_char_p
@@ -218,9 +226,18 @@ def csa_workspace_size(dims: Dims, op: int, B: int = 1, T: int = 1, Q: int = 1, 
 
 
 class Cache:
-    """Caller-owned cache tensors for ``B`` sequences (see csa_cache in csa.h)."""
+    """Caller-owned cache tensors for ``B`` sequences (see csa_cache in csa.h).
 
-    def __init__(self, dims: Dims, B: int, cap: int, win_cap: int, device="cuda"):
+    Contiguous by default: ``kv`` [B][cap][row_bytes], ``ki`` per sequence.  With
+    ``block_table`` ([B][max_blocks] int32 on the device) the cache is paged: ``kv`` and ``ki``
+    are pools of ``n_pages`` pages of ``page_tokens / m`` entries each (``kv``
+    [n_pages][E][row_bytes]; ``ki`` [n_pages][E][c_I] bytes, or for MXFP4 per page E rows of
+    element bytes then E rows of scale codes), and logical page j of sequence b is pool page
+    ``block_table[b][j]``.  The window ring, its positions, the projection state and the entry
+    counts stay per sequence."""
+
+    def __init__(self, dims: Dims, B: int, cap: int, win_cap: int, device="cuda",
+                 block_table=None, page_tokens: int = 128, n_pages: int = 0):
         import torch
         self.dims, self.B, self.cap, self.win_cap = dims, B, cap, win_cap
         rb = csa_row_bytes(dims)
@@ -228,15 +245,26 @@ class Cache:
             raise CsaError(1, load().csa_last_error().decode())
         self.row_bytes = rb
         u8 = dict(dtype=torch.uint8, device=device)
-        self.kv = torch.zeros((B, cap, rb), **u8)
+        self.block_table = block_table
+        if block_table is not None:
+            if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+                raise ValueError("block_table must be an int32 [B][max_blocks] tensor")
+            self.block_table = block_table.contiguous()
+            self.max_blocks, self.page_tokens, self.n_pages = block_table.shape[1], page_tokens, n_pages
+            groups, rows = n_pages, page_tokens // dims.m      # pool: n_pages groups of E rows
+        else:
+            self.max_blocks, self.page_tokens, self.n_pages = 0, 0, 0
+            groups, rows = B, cap                              # one group of cap rows per sequence
+        self.kv = torch.zeros((groups, rows, rb), **u8)
         if dims.dual and dims.idx_fmt == "mxfp4":
-            # per sequence: cap rows of c_I / 2 element bytes, then cap rows of c_I / 32 scales
-            self.ki = torch.zeros((B, cap * (dims.c_I // 2 + dims.c_I // 32)), **u8)
+            # per group: rows of c_I / 2 element bytes, then rows of c_I / 32 scale codes
+            self.ki = torch.zeros((groups, rows * (dims.c_I // 2 + dims.c_I // 32)), **u8)
         elif dims.dual:
             kib = dims.c_I * (4 if dims.idx_fmt == "f32" else 1)
-            self.ki = torch.zeros((B, cap, kib), **u8)
+            self.ki = torch.zeros((groups, rows, kib), **u8)
         else:
             self.ki = None
+        self._rows = rows
         self.n_entries = torch.zeros(B, dtype=torch.int32, device=device)
         self.win = torch.zeros((B, win_cap, rb), **u8)
         self.win_pos = torch.full((B, win_cap), -1, dtype=torch.int32, device=device)
@@ -245,15 +273,16 @@ class Cache:
 
     @property
     def ki_codes(self):
-        """MXFP4 keys: the element bytes, a [B][cap][c_I / 2] view of ki."""
-        n = self.cap * (self.dims.c_I // 2)
-        return self.ki[:, :n].view(self.B, self.cap, self.dims.c_I // 2)
+        """MXFP4 keys: the element bytes, a [groups][rows][c_I / 2] view of ki (groups are
+        sequences of cap rows, or pool pages)."""
+        n = self._rows * (self.dims.c_I // 2)
+        return self.ki[:, :n].view(self.ki.shape[0], self._rows, self.dims.c_I // 2)
 
     @property
     def ki_scales(self):
-        """MXFP4 keys: the block scale codes, a [B][cap][c_I / 32] view of ki."""
-        n = self.cap * (self.dims.c_I // 2)
-        return self.ki[:, n:].view(self.B, self.cap, self.dims.c_I // 32)
+        """MXFP4 keys: the block scale codes, a [groups][rows][c_I / 32] view of ki."""
+        n = self._rows * (self.dims.c_I // 2)
+        return self.ki[:, n:].view(self.ki.shape[0], self._rows, self.dims.c_I // 32)
 
     def reset(self):
         self.n_entries.zero_()
@@ -262,7 +291,8 @@ class Cache:
 
     def struct(self) -> _Cache:
         return _Cache(self.B, self.cap, self.win_cap, _ptr(self.kv), _ptr(self.ki),
-                      _ptr(self.n_entries), _ptr(self.win), _ptr(self.win_pos), _ptr(self.state))
+                      _ptr(self.n_entries), _ptr(self.win), _ptr(self.win_pos), _ptr(self.state),
+                      _ptr(self.block_table), self.max_blocks, self.page_tokens, self.n_pages)
 
 
 class Weights:

@@ -34,7 +34,7 @@ struct AttendArgs {
   int Q, n_h;
   const int32_t* idx;         // [Q][k] or null (dense)
   int k;
-  const uint8_t* kv;          // [B][cap][576]
+  const uint8_t* kv;          // [B][cap][576], or a pool of pages (rm)
   const uint8_t* win;         // [B][win_cap][576]
   const int32_t* win_pos;     // [B][win_cap]
   const int32_t* n_entries;   // [B]
@@ -43,6 +43,7 @@ struct AttendArgs {
   float eps;
   double log2_base;
   int splits, tiles_per_split;
+  RowMap rm;                  // where a sequence's entries live
   uint16_t* out;              // [Q][n_h][512] bf16 (splits == 1)
   uint16_t* part_o;           // [Q][n_h][splits][512] bf16 (splits > 1)
   float* part_ml;             // [Q][n_h][splits][2]
@@ -151,13 +152,16 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
 }
 
-template <bool SPARSE>
+template <bool SPARSE, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_attend_hs(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t Ks[HS_ROWS * HS_PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t PsT[16 * HS_PLD];
   __shared__ float redm[4][16], reds[4][16];
-  __shared__ int ridx[SPARSE ? HS_MAX_ROWS : 1];
+  // entry rows of the workgroup's part: index-list entries, or with a paged cache the pool
+  // rows they live in (-1: not a visible entry)
+  constexpr int NRIDX = (SPARSE || PAGED) ? HS_MAX_ROWS : 1;
+  __shared__ int ridx[NRIDX];
   __shared__ float rope_cs[AR];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -183,7 +187,7 @@ void k_attend_hs(AttendArgs a) {
   // are read through a valid stand-in address and replaced afterwards, so that no load sits
   // in a branch.
   int s01[HS_DEPTH] = {};
-  int rid[HS_IPT];
+  int rid[HS_IPT] = {};
   auto rid_row = [&](int i) { const int f = 64 * i + lane; return r_lo + (f >> 4) * HS_ROWS + wave * 16 + (f & 15); };
   if constexpr (SPARSE) {
 #pragma unroll
@@ -210,11 +214,23 @@ void k_attend_hs(AttendArgs a) {
   const int w0 = max(0, tau - a.n_win + 1);
   // entries visible at tau; with an index list it is needed only when the rows are widened
   int V = 0;
-  if constexpr (!SPARSE) V = max(0, min(tau / a.m, a.n_entries[seq]));
+  if constexpr (!SPARSE || PAGED) V = max(0, min(tau / a.m, a.n_entries[seq]));
   const int nsel = SPARSE ? a.k : V;
   const int nrows = nsel + (tau - w0 + 1);
   const int r_hi = min(nrows, r_lo + a.tiles_per_split * HS_ROWS);
-  const uint8_t* kvseq = a.kv + (size_t)seq * a.cap * AROWB;
+  // paged: row numbers are pool rows (kv is the pool), looked up once per entry here, so
+  // that the loop below reads them from LDS like an index list; entries past the visible
+  // ones become -1, and only window rows then need the visibility test
+  const uint8_t* kvseq = PAGED ? a.kv : a.kv + (size_t)seq * a.cap * AROWB;
+  if constexpr (PAGED) {
+    auto pool_row = [&](int e) {
+      return e >= 0 && e < min(V, a.cap) ? page_of(a.rm, seq, e) * a.rm.epp + e % a.rm.epp : -1;
+    };
+#pragma unroll
+    for (int t = 0; t < HS_DEPTH; ++t) s01[t] = pool_row(SPARSE ? s01[t] : r_lo + t * HS_ROWS + myrow);
+#pragma unroll
+    for (int i = 0; i < HS_IPT; ++i) rid[i] = pool_row(SPARSE ? rid[i] : rid_row(i));
+  }
   const uint8_t* winseq = a.win + (size_t)seq * a.win_cap * AROWB;
   const int32_t* wpseq = a.win_pos + (size_t)seq * a.win_cap;
 
@@ -230,8 +246,8 @@ void k_attend_hs(AttendArgs a) {
     constexpr int b = decltype(bconst)::value;
     const int r = t0 + myrow;
     const bool in = r < r_hi, ent = r < nsel;
-    const int s = SPARSE ? s_in : r;
-    const bool ok_a = in && ent && s >= 0 && s < a.cap;
+    const int s = (SPARSE || PAGED) ? s_in : r;
+    const bool ok_a = in && ent && s >= 0 && (PAGED || s < a.cap);
     const int slot = (ent ? 0 : w0 + (r - nsel)) % a.win_cap;
     const uint8_t* src = ent ? kvseq + (size_t)(ok_a ? s : 0) * AROWB
                              : (in ? winseq + (size_t)slot * AROWB : kvseq);
@@ -252,7 +268,7 @@ void k_attend_hs(AttendArgs a) {
   if constexpr (HS_DEPTH > 1) gather(r_lo + HS_ROWS, s01[HS_DEPTH - 1], std::integral_constant<int, HS_DEPTH - 1>{});
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (SPARSE) V = max(0, min(tau / a.m, a.n_entries[seq]));
+  if constexpr (SPARSE && !PAGED) V = max(0, min(tau / a.m, a.n_entries[seq]));
 
   // ---- LDS: the normalised query rows (RMSNorm over a head's 512 dims, whose 16 threads
   // hold 32 dims each, times the norm weights; in the tile buffer, pitch HS_PITCH), this
@@ -271,7 +287,7 @@ void k_attend_hs(AttendArgs a) {
     *reinterpret_cast<uint4*>(qd + 32) = norm_q8(qr2, inv, gq[4], gq[5]);
     *reinterpret_cast<uint4*>(qd + 48) = norm_q8(qr3, inv, gq[6], gq[7]);
   }
-  if constexpr (SPARSE) {
+  if constexpr (SPARSE || PAGED) {
 #pragma unroll
     for (int i = 0; i < HS_IPT; ++i) ridx[min(rid_row(i) - r_lo, HS_MAX_ROWS - 1)] = rid[i];
   }
@@ -302,8 +318,8 @@ void k_attend_hs(AttendArgs a) {
     // the entry index of this lane's row in the tile after next, read before this tile's
     // LDS writes so that waiting for it does not wait for them
     const int tn = t0 + HS_DEPTH * HS_ROWS;
-    const int s_next = SPARSE ? ridx[min(max(tn + myrow - r_lo, 0), SPARSE ? HS_MAX_ROWS - 1 : 0)] : 0;
-    const bool ok = (chk[b] == 1 && sv[b] < V) || (chk[b] >= 2 && wpv[b] == chk[b] - 2);
+    const int s_next = (SPARSE || PAGED) ? ridx[min(max(tn + myrow - r_lo, 0), NRIDX - 1)] : 0;
+    const bool ok = (chk[b] == 1 && (PAGED || sv[b] < V)) || (chk[b] >= 2 && wpv[b] == chk[b] - 2);
     const uint64_t okm = __ballot(ok);   // bit r of the low 16: row 16w + r is valid
     // ---- widen, write the V tile, and contract Q.K for this wave's 16 rows (four
     // independent accumulation chains, added at the end)
@@ -486,7 +502,7 @@ __global__ __launch_bounds__(64) void k_attend_f32(const float* __restrict__ qv,
                                                    const float* __restrict__ win,
                                                    const int32_t* __restrict__ win_pos,
                                                    const int32_t* __restrict__ n_entries,
-                                                   int cap, int win_cap, int m, int n_win, int c,
+                                                   RowMap rm, int win_cap, int m, int n_win, int c,
                                                    int r, float scale, float eps, double log2_base,
                                                    float* __restrict__ out) {
   __shared__ float qs[1024];
@@ -525,7 +541,7 @@ __global__ __launch_bounds__(64) void k_attend_f32(const float* __restrict__ qv,
     const float* p = nullptr;
     if (j < nsel) {
       int s = idx ? idx[(size_t)q * k + j] : j;
-      if (s >= 0 && s < V) p = kv + ((size_t)seq * cap + s) * c;
+      if (s >= 0 && s < min(V, rm.cap)) p = kv + row_of(rm, seq, s) * c;
     } else {
       const int pos = w0 + (j - nsel);
       const int slot = pos % win_cap;
@@ -632,7 +648,7 @@ hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
   if (d.kv_fmt == CSA_FMT_F32) {
     hipLaunchKernelGGL(k_attend_f32, dim3(Q * d.n_h), dim3(64), 0, s, (const float*)q, gamma_q,
                        sink, q_seq, q_pos, d.n_h, idx, d.top_k, (const float*)c.kv,
-                       (const float*)c.win, c.win_pos, c.n_entries, c.cap, c.win_cap, d.m,
+                       (const float*)c.win, c.win_pos, c.n_entries, row_map(d, c), c.win_cap, d.m,
                        d.n_win, d.c, d.rope_dim, scale, d.rms_eps, std::log2((double)d.rope_base),
                        (float*)out);
     return hipGetLastError();
@@ -652,6 +668,7 @@ hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
   a.win_pos = c.win_pos;
   a.n_entries = c.n_entries;
   a.cap = c.cap;
+  a.rm = row_map(d, c);
   a.win_cap = c.win_cap;
   a.m = d.m;
   a.n_win = d.n_win;
@@ -666,10 +683,13 @@ hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
   const size_t po = ((size_t)Q * d.n_h * p.splits * AC * sizeof(uint16_t) + 255) / 256 * 256;
   a.part_ml = p.splits > 1 ? (float*)((char*)ws + po) : nullptr;
   const dim3 grid(Q * (d.n_h / 16) * p.splits);
-  if (idx)
-    hipLaunchKernelGGL(k_attend_hs<true>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_attend_hs<false>, grid, dim3(256), 0, s, a);
+  if (a.rm.bt) {
+    if (idx) hipLaunchKernelGGL((k_attend_hs<true, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attend_hs<false, true>), grid, dim3(256), 0, s, a);
+  } else {
+    if (idx) hipLaunchKernelGGL((k_attend_hs<true, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attend_hs<false, false>), grid, dim3(256), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   hipLaunchKernelGGL(k_attend_combine, dim3(Q * d.n_h), dim3(256), 0, s, a);

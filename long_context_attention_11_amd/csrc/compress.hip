@@ -295,6 +295,7 @@ FoldArgs fold_args(const csa_dims& d, const csa_weights& w, const csa_cache& c, 
   a.cap = c.cap;
   a.win_cap = c.win_cap;
   a.rowB = (int)row_bytes(d);
+  a.rm = row_map(d, c);
   a.kv = (uint8_t*)c.kv;
   a.ki = (uint8_t*)c.ki;
   a.win = (uint8_t*)c.win;

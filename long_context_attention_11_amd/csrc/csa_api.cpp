@@ -79,6 +79,20 @@ int check_cache(const csa_dims* d, const csa_cache* c, bool need_state) {
   const size_t rb = row_bytes(*d);
   if ((size_t)c->cap * rb > (size_t)1 << 40)
     return fail(CSA_ERR_INVALID_ARGUMENT, "cache capacity overflows");
+  if (c->block_table) {
+    if (c->page_tokens < d->m || c->page_tokens % d->m)
+      return fail(CSA_ERR_INVALID_ARGUMENT, "page_tokens must be a positive multiple of m");
+    if (c->max_blocks < 1 || c->n_pages < 1)
+      return fail(CSA_ERR_INVALID_ARGUMENT, "a paged cache needs max_blocks >= 1 and n_pages >= 1");
+    const int64_t epp = c->page_tokens / d->m;
+    if ((int64_t)c->cap > (int64_t)c->max_blocks * epp)
+      return fail(CSA_ERR_INVALID_ARGUMENT, "cap exceeds max_blocks * page_tokens / m");
+    if ((size_t)c->n_pages * (size_t)epp * rb > (size_t)1 << 40)
+      return fail(CSA_ERR_INVALID_ARGUMENT, "page pool size overflows");
+    // the quantized decode indexer scores 16-entry tiles that must not straddle a page
+    if (d->dual && d->idx_fmt != CSA_FMT_F32 && epp % 16)
+      return fail(CSA_ERR_UNSUPPORTED, "a paged CSA cache with quantized keys needs page_tokens / m % 16 == 0");
+  }
   return CSA_OK;
 }
 

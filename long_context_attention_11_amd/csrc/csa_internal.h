@@ -99,6 +99,46 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ----------------------------------------------------------------------------- cache rows
+
+// Where a cache's entries live: cap rows per sequence in one run, or pages of epp entries
+// found through a per-sequence block table (bt[seq * max_blocks + j] = pool page of the
+// sequence's entries j epp .. j epp + epp - 1).
+struct RowMap {
+  const int32_t* bt;   // null: contiguous
+  int32_t max_blocks, epp, n_pages, cap;
+};
+
+// Pool page of entry i of sequence seq (paged maps only), clamped to the pool.
+__device__ __forceinline__ int page_of(const RowMap& rm, int seq, int i) {
+  const int p = rm.bt[(int64_t)seq * rm.max_blocks + min(i / rm.epp, rm.max_blocks - 1)];
+  return min(max(p, 0), rm.n_pages - 1);
+}
+// Row of entry i of sequence seq in its tensor (row-major rows of one width).
+__device__ __forceinline__ int64_t row_of(const RowMap& rm, int seq, int i) {
+  if (!rm.bt) return (int64_t)seq * rm.cap + i;
+  return (int64_t)page_of(rm, seq, i) * rm.epp + i % rm.epp;
+}
+// MXFP4 keys are stored in groups: a group of n rows holds n rows of element bytes, then n
+// rows of scale codes; a group is a sequence (n = cap) or a page (n = epp).  Byte offsets of
+// entry i's element bytes and scale codes (rows of ce and cs bytes).
+__device__ __forceinline__ void mx_offsets(const RowMap& rm, int seq, int i, int ce, int cs,
+                                           int64_t& codes, int64_t& scales) {
+  int64_t g0;
+  int n, r;
+  if (!rm.bt) {
+    g0 = (int64_t)seq * rm.cap;
+    n = rm.cap;
+    r = i;
+  } else {
+    g0 = (int64_t)page_of(rm, seq, i) * rm.epp;
+    n = rm.epp;
+    r = i % rm.epp;
+  }
+  codes = g0 * (ce + cs) + (int64_t)r * ce;
+  scales = g0 * (ce + cs) + (int64_t)n * ce + (int64_t)r * cs;
+}
+
 // ----------------------------------------------------------------------------- wave helpers
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -247,6 +287,17 @@ hipError_t launch_reduce_partials(const float* P, int32_t ksplit, int64_t n, flo
                                   hipStream_t s);
 hipError_t launch_query_meta(int32_t B, int32_t T, const int32_t* pos0, int32_t* q_seq,
                              int32_t* q_pos, hipStream_t s);
+
+// The row map of a cache (host).
+inline RowMap row_map(const csa_dims& d, const csa_cache& c) {
+  RowMap rm;
+  rm.bt = c.block_table;
+  rm.max_blocks = c.block_table ? c.max_blocks : 0;
+  rm.epp = c.block_table ? c.page_tokens / d.m : 0;
+  rm.n_pages = c.block_table ? c.n_pages : 0;
+  rm.cap = c.cap;
+  return rm;
+}
 
 // Planning helpers shared by the API and the launchers (pure host arithmetic).
 int32_t project_ksplit(const csa_dims& d, int32_t M);

@@ -27,6 +27,7 @@ struct FoldArgs {
   double log2_base;
   int kv_fmt, idx_fmt;
   int cap, win_cap, rowB;
+  RowMap rm;             // where entry i of a sequence lives in kv and ki
   uint8_t* kv;
   uint8_t* ki;
   uint8_t* win;
@@ -181,7 +182,7 @@ __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, f
       x1 = fold_column<PART>(a, b, p0, i, u + 1, a.c + u + 1, 0, a.bias, a.bias, a.c, u + 1);
     }
   }
-  uint8_t* dst = a.kv + ((size_t)b * a.cap + i) * a.rowB;
+  uint8_t* dst = a.kv + row_of(a.rm, b, i) * a.rowB;
   finalize_store<NW>(a, x0, x1, (int64_t)a.m * i, dst, red);
   // indexer key: same fold with its own columns and biases; stored as folded
   if (a.dual && u < a.cI) {
@@ -191,7 +192,7 @@ __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, f
     float k0 = fold_column<PART>(a, b, p0, i, base + u, base + 2 * a.cI + u, a.cI, BIa, BIb, a.cI, u);
     float k1 = fold_column<PART>(a, b, p0, i, base + u + 1, base + 2 * a.cI + u + 1, a.cI, BIa, BIb, a.cI, u + 1);
     if (a.idx_fmt == CSA_FMT_F32) {
-      float* kd = reinterpret_cast<float*>(a.ki) + ((size_t)b * a.cap + i) * a.cI;
+      float* kd = reinterpret_cast<float*>(a.ki) + row_of(a.rm, b, i) * a.cI;
       kd[u] = k0;
       kd[u + 1] = k1;
     } else if (a.idx_fmt == CSA_FMT_MXFP4) {
@@ -204,12 +205,12 @@ __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, f
         frexpf(amax, &ex);   // amax = f 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
         e = min(127, max(-127, ex - 1 - 2));
       }
-      const size_t krow = (size_t)a.cI / 2 + a.cI / 32;
-      uint8_t* kseq = a.ki + (size_t)b * a.cap * krow;
-      kseq[(size_t)i * (a.cI / 2) + t] = (uint8_t)(e2m1_code(ldexpf(k0, -e)) | (e2m1_code(ldexpf(k1, -e)) << 4));
-      if ((t & 15) == 0) kseq[(size_t)a.cap * (a.cI / 2) + (size_t)i * (a.cI / 32) + (t >> 4)] = (uint8_t)(e + 127);
+      int64_t oc, os;
+      mx_offsets(a.rm, b, i, a.cI / 2, a.cI / 32, oc, os);
+      a.ki[oc + t] = (uint8_t)(e2m1_code(ldexpf(k0, -e)) | (e2m1_code(ldexpf(k1, -e)) << 4));
+      if ((t & 15) == 0) a.ki[os + (t >> 4)] = (uint8_t)(e + 127);
     } else {
-      uint8_t* kd = a.ki + ((size_t)b * a.cap + i) * a.cI;
+      uint8_t* kd = a.ki + row_of(a.rm, b, i) * a.cI;
       *reinterpret_cast<uint16_t*>(kd + u) = (uint16_t)(f32_to_e4m3(k0) | (f32_to_e4m3(k1) << 8));
     }
   }

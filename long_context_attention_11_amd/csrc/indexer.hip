@@ -128,7 +128,38 @@ struct IndexerArgs {
   void* scores;           // float32, or bfloat16 with MXFP4
   int64_t ld;
   int chunk;
+  RowMap rm;              // where a sequence's keys live (contiguous or paged)
 };
+
+// Paged keys in the decode bodies: a wave scans tiles s0 = w_lo + 64 j, each inside one page
+// (pages hold a multiple of 16 entries and tiles start at multiples of 16).  A tile past the
+// end reads the last 16-aligned tile's entries instead (s is clamped to c_hi - 1), so tile j
+// is found at t0 = min(s0, (c_hi - 1) & ~15).  Lane j of the wave looks up tile j's page and
+// the row of t0 in it once, before any key is requested; a key row is then two lane reads
+// and an add.  (The chunk is capped so that a wave's tiles, prefetched ones past the end
+// included, number at most 64.)
+struct WavePages {
+  int page, r0;
+};
+__device__ __forceinline__ WavePages wave_pages(const RowMap& rm, int seq, int w_lo, int c_hi, int lane) {
+  if (!rm.bt) return {0, 0};
+  const int t0 = min(w_lo + 64 * lane, (c_hi - 1) & ~15);
+  return {page_of(rm, seq, t0), t0 % rm.epp};
+}
+// Entry s of the tile at s0: the first row of its group (a sequence's cap rows, or a page's
+// epp rows) and its row within the group.
+__device__ __forceinline__ void tile_loc(const RowMap& rm, int seq, const WavePages& wp, int w_lo, int c_hi,
+                                         int s0, int s, int64_t& g0, int& r) {
+  if (!rm.bt) {
+    g0 = (int64_t)seq * rm.cap;
+    r = s;
+    return;
+  }
+  const int j = __builtin_amdgcn_readfirstlane((s0 - w_lo) >> 6);
+  const int t0 = min(s0, (c_hi - 1) & ~15);
+  g0 = (int64_t)__builtin_amdgcn_readlane(wp.page, j) * rm.epp;
+  r = __builtin_amdgcn_readlane(wp.r0, j) + (s - t0);
+}
 
 // The part of a workgroup's work every indexer body shares: its queries' visible ranges and
 // the wave's first tile of the chunk.  Returns false when the wave has nothing to score.
@@ -159,7 +190,6 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
   const uint16_t* __restrict__ wI = ia.wI;
   const int Q = ia.Q;
   const uint8_t* __restrict__ ki = ia.ki;
-  const int cap = ia.cap;
   float* __restrict__ scores = static_cast<float*>(ia.scores);
   const int64_t ld = ia.ld;
   constexpr int HT = NH / 16;
@@ -171,7 +201,7 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
   if (!indexer_range<QPW>(ia, bx, by, wave, seq, V, c_hi, w_lo)) return;
   const int stride = 64;  // 4 waves x 16 entries
 
-  const uint8_t* kseq = ki + (size_t)seq * cap * IX_CI;
+  const WavePages wp = wave_pages(ia.rm, seq, w_lo, c_hi, lane);
   // Prologue: the query operands (q^I rows, head weights) and the first DEPTH tiles of keys
   // are all requested before anything waits, so their latencies overlap.  The ring holds
   // DEPTH tiles (16 entries x 128 B per wave, 32 B per lane); waits count outstanding loads
@@ -192,7 +222,10 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
   uint4 rk[DEPTH][2];
   auto load_tile = [&](int s0, uint4 (&r)[2]) {
     const int s = min(s0 + col, c_hi - 1);
-    const uint8_t* src = kseq + (size_t)s * IX_CI + g * 32;
+    int64_t g0;
+    int ri;
+    tile_loc(ia.rm, seq, wp, w_lo, c_hi, s0, s, g0, ri);
+    const uint8_t* src = ki + (g0 + ri) * IX_CI + g * 32;
     r[0] = *reinterpret_cast<const uint4*>(src);
     r[1] = *reinterpret_cast<const uint4*>(src + 16);
   };
@@ -310,8 +343,10 @@ __device__ __forceinline__ void indexer_fp4_body(const IndexerArgs& ia, int bx, 
   const int stride = 64;  // 4 waves x 16 entries
   uint16_t* __restrict__ scores = static_cast<uint16_t*>(ia.scores);
 
-  const uint8_t* kcode = ia.ki + (size_t)seq * ia.cap * (KC + KS);
-  const uint8_t* kscale = kcode + (size_t)ia.cap * KC;
+  const WavePages wp = wave_pages(ia.rm, seq, w_lo, c_hi, lane);
+  // a group of n rows (a sequence's cap, or a page's epp) holds n rows of element bytes, then
+  // n rows of scale codes
+  const int64_t gn = ia.rm.bt ? ia.rm.epp : ia.cap;
   uint4 qa[QPW][HT];
   int qs[QPW][HT];
   uint2 wraw[QPW][HT];
@@ -331,8 +366,12 @@ __device__ __forceinline__ void indexer_fp4_body(const IndexerArgs& ia, int bx, 
   int ks[DEPTH];
   auto load_tile = [&](int s0, uint4& c, int& sc) {
     const int s = min(s0 + col, c_hi - 1);
-    c = *reinterpret_cast<const uint4*>(kcode + (size_t)s * KC + g * 16);
-    sc = kscale[(size_t)s * KS + g];
+    int64_t g0;
+    int r;
+    tile_loc(ia.rm, seq, wp, w_lo, c_hi, s0, s, g0, r);
+    const uint8_t* grp = ia.ki + g0 * (KC + KS);
+    c = *reinterpret_cast<const uint4*>(grp + r * KC + g * 16);
+    sc = grp[gn * KC + r * KS + g];
   };
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) load_tile(w_lo + stride * i, kc[i], ks[i]);
@@ -403,7 +442,7 @@ constexpr int IT_LD = 272;      // LDS bytes per entry row: 128 dims in bf16 + 1
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_indexer_tile(
     const uint8_t* __restrict__ qI, const uint16_t* __restrict__ wI,
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int Q,
-    const uint8_t* __restrict__ ki, int cap, const int32_t* __restrict__ n_entries, int m,
+    const uint8_t* __restrict__ ki, RowMap rm, const int32_t* __restrict__ n_entries, int m,
     float* __restrict__ scores, int64_t ld, int chunk) {
   constexpr int NH = 64, HT = NH / 16;
   __shared__ __align__(16) uint8_t kbuf[2][IT_STAGE * IT_LD];
@@ -446,14 +485,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // stage loader: thread t moves dims 8p .. 8p+7 and 64+8p .. 64+8p+7 (p = t % 8) of entry
   // t / 8 of the stage, widened to bf16; the 8 threads of an entry write two contiguous
   // 128-byte runs, which keeps the LDS writes free of bank conflicts
-  const uint8_t* kseq = ki + (size_t)seq * cap * IX_CI;
+  // (a paged cache costs one block-table read per entry, hidden behind a stage of MFMAs)
   const int le = tid >> 3, lp = (tid & 7) * 8;
   constexpr int RPT = IT_STAGE / 64;  // entries per thread per stage
   auto gload = [&](int st, uint4 (&v)[RPT]) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
       const int e = min(e_lo + st * IT_STAGE + 64 * r + le, e_hi - 1);
-      const uint8_t* src = kseq + (size_t)e * IX_CI + lp;
+      const uint8_t* src = ki + row_of(rm, seq, e) * IX_CI + lp;
       const uint2 a = *reinterpret_cast<const uint2*>(src);
       const uint2 b = *reinterpret_cast<const uint2*>(src + 64);
       v[r] = make_uint4(a.x, a.y, b.x, b.y);
@@ -559,7 +598,7 @@ constexpr int IF_RS = 80;      // LDS bytes per entry row: 64 element bytes + 16
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_indexer_tile_fp4(
     const uint8_t* __restrict__ qI, const uint16_t* __restrict__ wI,
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int Q,
-    const uint8_t* __restrict__ ki, int cap, const int32_t* __restrict__ n_entries, int m,
+    const uint8_t* __restrict__ ki, RowMap rm, const int32_t* __restrict__ n_entries, int m,
     uint16_t* __restrict__ scores, int64_t ld, int chunk) {
   constexpr int NH = 64, HT = NH / 16, KC = IX_CI / 2, KS = IX_CI / 32;
   __shared__ __align__(16) uint8_t kbuf[2][IF_STAGE * IF_RS];
@@ -605,15 +644,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // stage loader: thread t moves element bytes 16 (t % 4) .. +15 of entry t / 4 of the stage;
   // threads t < IF_STAGE also move entry t's scale codes (clamped past the end, unused there)
-  const uint8_t* kcode = ki + (size_t)seq * cap * (KC + KS);
-  const uint8_t* kscale = kcode + (size_t)cap * KC;
   const int le = tid >> 2, lp = (tid & 3) * 16;
   auto gload = [&](int st, uint4& v, uint32_t& sv) {
     const int e = min(e_lo + st * IF_STAGE + le, e_hi - 1);
-    v = *reinterpret_cast<const uint4*>(kcode + (size_t)e * KC + lp);
+    int64_t oc, os;
+    mx_offsets(rm, seq, e, KC, KS, oc, os);
+    v = *reinterpret_cast<const uint4*>(ki + oc + lp);
     if (tid < IF_STAGE) {
       const int es = min(e_lo + st * IF_STAGE + tid, e_hi - 1);
-      sv = *reinterpret_cast<const uint32_t*>(kscale + (size_t)es * KS);
+      mx_offsets(rm, seq, es, KC, KS, oc, os);
+      sv = *reinterpret_cast<const uint32_t*>(ki + os);
     }
   };
   auto lstore = [&](int buf, const uint4& v, uint32_t sv) {
@@ -703,7 +743,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // float32 indexer (fp32 formats): one thread per (query, entry).
 __global__ __launch_bounds__(256) void k_indexer_f32(
     const float* __restrict__ qI, const float* __restrict__ wI, const int32_t* __restrict__ q_seq,
-    const int32_t* __restrict__ q_pos, int Q, const float* __restrict__ ki, int cap,
+    const int32_t* __restrict__ q_pos, int Q, const float* __restrict__ ki, RowMap rm,
     const int32_t* __restrict__ n_entries, int m, int nh, int cI, float* __restrict__ scores,
     int64_t ld) {
   const int q = blockIdx.y;
@@ -712,7 +752,7 @@ __global__ __launch_bounds__(256) void k_indexer_f32(
   const int seq = q_seq ? q_seq[q] : q;
   const int V = max(0, min(q_pos[q] / m, n_entries[seq]));
   if (s >= V) return;
-  const float* k = ki + ((size_t)seq * cap + s) * cI;
+  const float* k = ki + row_of(rm, seq, s) * cI;
   float acc = 0.f;
   for (int h = 0; h < nh; ++h) {
     const float* qh = qI + ((size_t)q * nh + h) * cI;
@@ -729,6 +769,7 @@ hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI,
                           const int32_t* q_seq, const int32_t* q_pos, int32_t Q, void* scores,
                           int64_t ld, bool tiled, hipStream_t s) {
   const bool fp4 = d.idx_fmt == CSA_FMT_MXFP4;
+  const RowMap rm = row_map(d, c);
   if (tiled && (fp4 || d.idx_fmt == CSA_FMT_E4M3) && d.n_hI == 64 && Q >= IT_Q) {
     // every aligned group of IT_Q queries belongs to one sequence (the caller guarantees it)
     const int ntile = (Q + IT_Q - 1) / IT_Q;
@@ -739,18 +780,18 @@ hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI,
     dim3 grid(ntile, (c.cap + chunk - 1) / chunk);
     if (fp4)
       hipLaunchKernelGGL(k_indexer_tile_fp4, grid, dim3(512), 0, s, (const uint8_t*)qI,
-                         (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki, c.cap,
+                         (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki, rm,
                          c.n_entries, d.m, static_cast<uint16_t*>(scores), ld, chunk);
     else
       hipLaunchKernelGGL(k_indexer_tile, grid, dim3(512), 0, s, (const uint8_t*)qI,
-                         (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki, c.cap,
+                         (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki, rm,
                          c.n_entries, d.m, static_cast<float*>(scores), ld, chunk);
     return hipGetLastError();
   }
   if (d.idx_fmt == CSA_FMT_F32) {
     dim3 grid((c.cap + 255) / 256, Q);
     hipLaunchKernelGGL(k_indexer_f32, grid, dim3(256), 0, s, (const float*)qI, (const float*)w,
-                       q_seq, q_pos, Q, (const float*)c.ki, c.cap, c.n_entries, d.m, d.n_hI,
+                       q_seq, q_pos, Q, (const float*)c.ki, rm, c.n_entries, d.m, d.n_hI,
                        d.c_I, static_cast<float*>(scores), ld);
     return hipGetLastError();
   }
@@ -760,9 +801,12 @@ hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI,
   const int per_q = std::max(1, target_wgs / std::max(Q, 1));
   int chunk = (c.cap + per_q - 1) / per_q;
   chunk = std::max(256, (chunk + 255) / 256 * 256);
+  // paged keys: a wave's tiles (64 entries apart, 4 prefetched past the end) must number at
+  // most 64, one page id per lane
+  if (rm.bt) chunk = std::min(chunk, 2048);
   const int nchunk = (c.cap + chunk - 1) / chunk;
   const IndexerArgs ia{(const uint8_t*)qI, (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki,
-                       c.cap, c.n_entries, d.m, scores, ld, chunk};
+                       c.cap, c.n_entries, d.m, scores, ld, chunk, rm};
   dim3 grid(Q, nchunk);
 #define IX_LAUNCH(NHV)                                                                          \
   if (fp4) hipLaunchKernelGGL((k_indexer_fp4<NHV, 1>), grid, dim3(256), 0, s, ia);                \

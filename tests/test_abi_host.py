@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), f"libcsa.so does not export {name}"
     assert set(L.EXPORTED_SYMBOLS) == set(declared)
-    assert L.csa_abi_version() == 1
+    assert L.csa_abi_version() == L.ABI_VERSION == 2
 
 
 def _lib():
@@ -120,6 +120,42 @@ def test_null_and_workspace_errors_without_a_device():
                                  fake, fake, fake, None, None, fake, fake, None)
     assert st == 3 and b"static" in lib.csa_last_error()
     assert L.csa_noalloc_scratch_bytes() == 64 << 20
+
+
+def test_paged_cache_arguments_are_checked_on_the_host():
+    """A block table brings page_tokens, max_blocks and n_pages, checked before any launch."""
+    lib = _lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: checks fail before any launch
+    w = L._Weights(fake, fake, fake, fake, None)
+
+    def attend(cfg, cache):
+        ds = L.Dims.from_config(cfg).struct()
+        return lib.csa_attend(ctypes.byref(ds), ctypes.byref(cache), fake, None, None, fake, fake, 1,
+                              None, fake, fake, 1 << 30, None)
+
+    def paged(cap, max_blocks, page_tokens, n_pages):
+        return L._Cache(2, cap, 128, fake, fake, fake, fake, fake, fake, fake, max_blocks, page_tokens, n_pages)
+
+    c2, c5 = synth.config("c2"), synth.config("c5")
+    # HCA: a page must hold whole entries of m' = 128 tokens, the table must reach cap
+    for cache, msg in ((paged(64, 64, 100, 128), b"multiple of m"),
+                       (paged(65, 64, 128, 128), b"cap exceeds"),
+                       (paged(64, 0, 128, 128), b"max_blocks"),
+                       (paged(64, 64, 128, 0), b"n_pages")):
+        assert attend(c5, cache) == 1
+        assert msg in lib.csa_last_error()
+    # CSA with quantized keys: a page must hold a multiple of 16 entries
+    ds = L.Dims.from_config(c2).struct()
+    bad = paged(64, 32, 8, 64)                                # 2 entries per page
+    assert lib.csa_index_topk(ctypes.byref(ds), ctypes.byref(bad), fake, fake, fake, fake, 1, fake,
+                              None, fake, 1 << 30, None) == 2
+    assert b"% 16" in lib.csa_last_error()
+    # float32 keys take any page size that is a multiple of m: the cache passes its checks and
+    # the call fails on T = 0, which is checked after them
+    d1 = L.Dims.from_config(synth.config("c1")).struct()
+    assert lib.csa_compress(ctypes.byref(d1), ctypes.byref(w), ctypes.byref(paged(64, 64, 4, 128)), fake, 0,
+                            fake, fake, 1 << 30, None) == 1
+    assert b"T must" in lib.csa_last_error()
 
 
 def test_workspace_sizes_are_consistent():

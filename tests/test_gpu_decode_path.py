@@ -23,6 +23,7 @@ from helpers import (assert_close_q, check_bf16_scores, check_stored_codes, chec
                      qI_host)
 from oracle import codecs
 from oracle import csa_ref as R
+from paging import logical, paged_cache, store_logical
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -40,7 +41,7 @@ def _mx_encode_rows(x: np.ndarray):
     return codecs.mxfp4_pack(c), s
 
 
-def _decode_path(name, idx_fmt="e4m3", realistic_mx=False, seed=51):
+def _decode_path(name, idx_fmt="e4m3", realistic_mx=False, seed=51, paged=False):
     cfg = synth.config(name, idx_fmt=idx_fmt)
     dims = L.Dims.from_config(cfg)
     od = oracle_dims(cfg)
@@ -49,19 +50,22 @@ def _decode_path(name, idx_fmt="e4m3", realistic_mx=False, seed=51):
     N0 = N - 8                      # complete entries before the steps
     tau0 = m * N0
     steps = m
-    print(f"decode path {name} idx={idx_fmt} realistic_mx={realistic_mx}: B={B} N0={N0} k={k}", flush=True)
+    print(f"decode path {name} idx={idx_fmt} realistic_mx={realistic_mx} paged={paged}: B={B} N0={N0} k={k}",
+          flush=True)
 
-    cache = L.Cache(dims, B=B, cap=N, win_cap=nw)
+    cache = paged_cache(dims, B, N, nw, seed=seed) if paged else L.Cache(dims, B=B, cap=N, win_cap=nw)
     sc = synth.synthetic_cache(cfg, B, N, nw, seed=seed, device=DEV)
-    cache.kv.copy_(sc["kv"])
     cache.win.copy_(sc["win"])
     if idx_fmt == "mxfp4" and realistic_mx:
         # keys as the MX rule encodes N(0, 0.25) values (scale codes near those a fold gives)
         kx = synth.randn((B, N, cfg["c_I"]), 0.5, "cpu", seed, "ckx").numpy().astype(np.float64)
         el, scl = _mx_encode_rows(kx.reshape(B * N, -1))
-        cache.ki.copy_(torch.cat([torch.from_numpy(el).view(B, -1), torch.from_numpy(scl).view(B, -1)], 1))
+        ki0 = torch.cat([torch.from_numpy(el).view(B, -1), torch.from_numpy(scl).view(B, -1)], 1)
     else:
-        cache.ki.copy_(sc["ki"].view(torch.uint8).reshape(cache.ki.shape))
+        ki0 = sc["ki"].view(torch.uint8)
+    store_logical(cache, kv=sc["kv"], ki=ki0)
+    pool = cache
+    cache = logical(pool)
     cache.n_entries.fill_(N0)
     wp = np.full((B, nw), -1, dtype=np.int32)
     for j in range(tau0 - nw, tau0):
@@ -104,13 +108,14 @@ def _decode_path(name, idx_fmt="e4m3", realistic_mx=False, seed=51):
         rows = [b * steps + t for b in range(B)]
         out = torch.zeros((B, cfg["n_h"], cfg["c"]), dtype=torch.bfloat16, device=DEV)
         idx = torch.full((B, k), -7, dtype=torch.int32, device=DEV)
-        L.csa_forward(dims, lw, cache, Hs[:, 2 * m + t:2 * m + t + 1].contiguous(), 1, _i32([tau0 + t] * B),
+        L.csa_forward(dims, lw, pool, Hs[:, 2 * m + t:2 * m + t + 1].contiguous(), 1, _i32([tau0 + t] * B),
                       qs["q"][rows].contiguous(), qs["qI"][rows].contiguous(), qs["w"][rows].contiguous(),
                       W["gamma_q"], W["sink"], out, idx, ws)
         outs.append(out)
         idxs.append(idx)
     torch.cuda.synchronize()
     print(f"decode path {name}: {steps} steps ran, checking", flush=True)
+    cache = logical(pool)
 
     q, qI, w = host64(qs["q"]), qI_host(qs["qI"], cfg), host64(qs["w"])
     sink = host64(W["sink"])
@@ -194,3 +199,14 @@ def test_c2_forward_decode_path_full_size_mxfp4_mx_rule_inputs():
 def test_c3_forward_decode_path_full_size():
     """Pro decode at full size (4 x 262144 entries, 128 heads, k = 1024) through csa_forward."""
     _decode_path("c3")
+
+
+def test_c2_forward_decode_path_full_size_paged():
+    """Flash decode at full size through csa_forward on a paged cache (128-token pages of 32
+    entries, shuffled over the pool): the new entry and key are written through the table."""
+    _decode_path("c2", paged=True)
+
+
+def test_c2_forward_decode_path_full_size_mxfp4_paged():
+    """The same with MXFP4 keys, wide block scales, paged."""
+    _decode_path("c2", idx_fmt="mxfp4", paged=True)

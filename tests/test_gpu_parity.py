@@ -16,6 +16,7 @@ from helpers import (assert_close_f32, assert_close_q, check_bf16_scores, check_
                      keys_of, qI_host, check_stored_mxfp4)
 from oracle import codecs
 from oracle import csa_ref as R
+from paging import logical, paged_cache, store_logical
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -79,10 +80,12 @@ def _check_cache_vs_oracle(cfg, cache, b, comp, n_tokens, what):
 # ----------------------------------------------------------------------------- config 1
 
 
-def test_c1_forward_matches_oracle():
+@pytest.mark.parametrize("paged", [False, True])
+def test_c1_forward_matches_oracle(paged):
     """Tiny fp32 prefill (n=256, d=256, m=4, c=64, 4 heads, k=8, n_win=16): every query.  The
     queries come from the hidden states through the low-rank query path (eqs. 13-15 and 18,
-    d_c = 64), computed in float64 and handed to both sides as the same float32 arrays."""
+    d_c = 64), computed in float64 and handed to both sides as the same float32 arrays.
+    Paged: 8-token pages (2 entries each) in a shuffled pool."""
     cfg = synth.config("c1")
     dims = L.Dims.from_config(cfg)
     od = oracle_dims(cfg)
@@ -96,7 +99,8 @@ def test_c1_forward_matches_oracle():
     qs = {"q": f32(cQ @ PW["w_uq"].T, (T, cfg["n_h"], cfg["c"])),        # eq. 18
           "qI": f32(cQ @ PW["w_iuq"].T, (T, cfg["n_hI"], cfg["c_I"])),   # eq. 14
           "w": f32(hn @ PW["w_w"].T, (T, cfg["n_hI"]))}                  # eq. 15
-    cache = L.Cache(dims, B=1, cap=T // m, win_cap=T + cfg["n_win"])
+    cache = (paged_cache(dims, 1, T // m, T + cfg["n_win"], seed=1, page_tokens=8) if paged
+             else L.Cache(dims, B=1, cap=T // m, win_cap=T + cfg["n_win"]))
     out = torch.zeros((T, cfg["n_h"], cfg["c"]), dtype=torch.float32, device=DEV)
     idx = torch.zeros((T, k), dtype=torch.int32, device=DEV)
     ws = _ws(L.csa_workspace_size(dims, L.OP_FORWARD, B=1, T=T, cap=cache.cap))
@@ -106,7 +110,7 @@ def test_c1_forward_matches_oracle():
 
     OW = oracle_weights(W)
     comp = R.compress_sequence(host64(H), OW, od)
-    _check_cache_vs_oracle(cfg, cache, 0, comp, T, "c1")
+    _check_cache_vs_oracle(cfg, logical(cache), 0, comp, T, "c1")
     q, qI, w = host64(qs["q"]), host64(qs["qI"]), host64(qs["w"])
     sink = host64(W["sink"])
     gi, go = idx.cpu().numpy(), out.cpu().numpy().astype(np.float64)
@@ -122,17 +126,20 @@ def test_c1_forward_matches_oracle():
     assert ties <= 2
 
 
-def test_c1_chunked_compress_equals_whole():
+@pytest.mark.parametrize("paged", [False, True])
+def test_c1_chunked_compress_equals_whole(paged):
     """Ragged chunks (not multiples of m, a single token, a block split across calls) build the
-    same cache as the whole-sequence oracle: the projection state carries across calls."""
+    same cache as the whole-sequence oracle: the projection state carries across calls.
+    Paged: 4-token pages (one entry each)."""
     cfg = synth.config("c1")
     dims = L.Dims.from_config(cfg)
     od = oracle_dims(cfg)
     B, n = 2, 203
     W = synth.weights(cfg, seed=3, device=DEV)
     Hs = torch.stack([synth.hidden(cfg, b, 0, n, seed=3, device=DEV) for b in range(B)])
-    cache = L.Cache(dims, B=B, cap=64, win_cap=32)
+    cache = paged_cache(dims, B, 64, 32, seed=3, page_tokens=4) if paged else L.Cache(dims, B=B, cap=64, win_cap=32)
     _compress_chunks(dims, W, cache, Hs, [5, 1, 2, 50, 3, 142])
+    cache = logical(cache)
     OW = oracle_weights(W)
     for b in range(B):
         comp = R.compress_sequence(host64(Hs[b]), OW, od)
@@ -189,31 +196,33 @@ def test_q_compress_single_token_steps(idx_fmt):
     assert flips < 50
 
 
-def test_hca_compress_matches_oracle():
-    """HCA (m'=128, single path, no indexer): 2 sequences x 300 tokens in chunks."""
+@pytest.mark.parametrize("paged", [False, True])
+def test_hca_compress_matches_oracle(paged):
+    """HCA (m'=128, single path, no indexer): 2 sequences x 300 tokens in chunks; paged: one
+    entry per 128-token page."""
     cfg = synth.config("c5")
     dims = L.Dims.from_config(cfg)
     od = oracle_dims(cfg)
     B, n = 2, 300
     W = synth.weights(cfg, seed=6, device=DEV)
     Hs = torch.stack([synth.hidden(cfg, b, 0, n, seed=6, device=DEV) for b in range(B)])
-    cache = L.Cache(dims, B=B, cap=8, win_cap=128)
+    cache = paged_cache(dims, B, 8, 128, seed=6) if paged else L.Cache(dims, B=B, cap=8, win_cap=128)
     _compress_chunks(dims, W, cache, Hs, [100, 1, 127, 72])
+    cache = logical(cache)
     OW = oracle_weights(W)
     for b in range(B):
         comp = R.compress_sequence(host64(Hs[b]), OW, od)
         _check_cache_vs_oracle(cfg, cache, b, comp, n, f"hca seq {b}")
 
 
-def _synthetic_decode_setup(cfg, B, N, R_win, taus, seed=11, sink=True, n_entries=None):
-    """Synthetic cache + one query per listed (seq, tau)."""
+def _synthetic_decode_setup(cfg, B, N, R_win, taus, seed=11, sink=True, n_entries=None, paged=False):
+    """Synthetic cache (contiguous, or paged through a shuffled block table) + one query per
+    listed (seq, tau)."""
     dims = L.Dims.from_config(cfg)
-    cache = L.Cache(dims, B=B, cap=N, win_cap=R_win)
+    cache = paged_cache(dims, B, N, R_win, seed=seed) if paged else L.Cache(dims, B=B, cap=N, win_cap=R_win)
     sc = synth.synthetic_cache(cfg, B, N, R_win, seed=seed, device=DEV)
-    cache.kv.copy_(sc["kv"])
     cache.win.copy_(sc["win"])
-    if cfg["dual"]:
-        cache.ki.copy_(sc["ki"].view(torch.uint8).reshape(cache.ki.shape))
+    store_logical(cache, kv=sc["kv"], ki=sc["ki"].view(torch.uint8) if cfg["dual"] else None)
     ne = n_entries if n_entries is not None else [N] * B
     cache.n_entries.copy_(_i32(ne))
     # ring positions: the R_win tokens ending at each sequence's largest query position
@@ -269,9 +278,10 @@ def _run_index_attend_and_check(cfg, dims, cache, qs, W, q_seq, q_pos, taus, che
     gs = scores.float().cpu().numpy().astype(np.float64) if scores is not None else None
     per_seq = {}
     stats = []
+    lc = logical(cache)
     for i, (b, tau) in enumerate(taus):
         if b not in per_seq:
-            per_seq[b] = _oracle_cache(cfg, cache, b)
+            per_seq[b] = _oracle_cache(cfg, lc, b)
         entries, ki, raw_of = per_seq[b]
         ne = int(cache.n_entries[b])
         o_ref, sel, sc = R.query_step(tau, q[i], None if qI is None else qI[i], None if w is None else w[i],
@@ -327,13 +337,14 @@ def test_hca_dense_attend_small():
     _run_index_attend_and_check(cfg, dims, cache, qs, W, q_seq, q_pos, taus)
 
 
-@pytest.mark.parametrize("idx_fmt", ["e4m3", "mxfp4"])
-def test_q_forward_end_to_end(idx_fmt):
+@pytest.mark.parametrize("idx_fmt,paged", [("e4m3", False), ("mxfp4", False), ("e4m3", True), ("mxfp4", True)])
+def test_q_forward_end_to_end(idx_fmt, paged):
     """Compress a 600-token prefix in chunks, then a 96-token forward chunk (compress +
     index + top-k + attend) on 2 sequences; the oracle builds its own cache from the same
     hidden states.  Queries whose selection differs only through ties or a stored-code flip
     are checked for validity on the GPU's selection.  The chunk's queries take the tiled
-    (prefill) indexer, with E4M3 or MXFP4 keys."""
+    (prefill) indexer, with E4M3 or MXFP4 keys; the cache is contiguous or paged (128-token
+    pages in a shuffled pool)."""
     cfg = _qcfg(idx_fmt=idx_fmt)
     dims = L.Dims.from_config(cfg)
     od = oracle_dims(cfg)
@@ -341,7 +352,7 @@ def test_q_forward_end_to_end(idx_fmt):
     k = cfg["top_k"]
     W = synth.weights(cfg, seed=21, device=DEV)
     Hs = torch.stack([synth.hidden(cfg, b, 0, n0 + T, seed=21, device=DEV) for b in range(B)])
-    cache = L.Cache(dims, B=B, cap=256, win_cap=T + 128)
+    cache = paged_cache(dims, B, 256, T + 128, seed=21) if paged else L.Cache(dims, B=B, cap=256, win_cap=T + 128)
     _compress_chunks(dims, W, cache, Hs[:, :n0].contiguous(), [256, 3, 341])
     qs = synth.queries(cfg, B * T, seed=21, device=DEV)
     out = torch.zeros((B * T, cfg["n_h"], cfg["c"]), dtype=torch.bfloat16, device=DEV)
@@ -350,6 +361,7 @@ def test_q_forward_end_to_end(idx_fmt):
     L.csa_forward(dims, lib_weights(W, True), cache, Hs[:, n0:].contiguous(), T, _i32([n0] * B),
                   qs["q"], qs["qI"], qs["w"], W["gamma_q"], W["sink"], out, idx, ws)
     torch.cuda.synchronize()
+    cache = logical(cache)
     OW = oracle_weights(W)
     q, qI, w = host64(qs["q"]), qI_host(qs["qI"], cfg), host64(qs["w"])
     sink = host64(W["sink"])
@@ -381,12 +393,13 @@ def test_q_forward_end_to_end(idx_fmt):
             assert_close_q(go[i], o_ref, f"e2e out seq {b} tau={tau}")
 
 
-@pytest.mark.parametrize("idx_fmt", ["e4m3", "mxfp4"])
-def test_q_forward_decode_steps(idx_fmt):
+@pytest.mark.parametrize("idx_fmt,paged", [("e4m3", False), ("mxfp4", False), ("mxfp4", True)])
+def test_q_forward_decode_steps(idx_fmt, paged):
     """Nine one-token forward steps (tau = 600 .. 608, two of them completing an entry) on a
     cache whose capacity spans two top-k segments: the path that scores before compressing
     and runs the projection step inside the top-k threshold launch.  Outputs, selections and
-    the cache afterwards are checked against the oracle as in the chunked test."""
+    the cache afterwards are checked against the oracle as in the chunked test; the cache is
+    contiguous or paged."""
     cfg = _qcfg(idx_fmt=idx_fmt)
     dims = L.Dims.from_config(cfg)
     od = oracle_dims(cfg)
@@ -395,7 +408,7 @@ def test_q_forward_decode_steps(idx_fmt):
     W = synth.weights(cfg, seed=23, device=DEV)
     lw = lib_weights(W, True)
     Hs = torch.stack([synth.hidden(cfg, b, 0, n0 + steps, seed=23, device=DEV) for b in range(B)])
-    cache = L.Cache(dims, B=B, cap=16384, win_cap=128)
+    cache = paged_cache(dims, B, 16384, 128, seed=23) if paged else L.Cache(dims, B=B, cap=16384, win_cap=128)
     _compress_chunks(dims, W, cache, Hs[:, :n0].contiguous(), [256, 344])
     qs = synth.queries(cfg, B * steps, seed=23, device=DEV)
     ws = _ws(L.csa_workspace_size(dims, L.OP_FORWARD, B=B, T=1, cap=cache.cap))
@@ -410,6 +423,7 @@ def test_q_forward_decode_steps(idx_fmt):
         outs.append(out)
         idxs.append(idx)
     torch.cuda.synchronize()
+    cache = logical(cache)
     OW = oracle_weights(W)
     q, qI, w = host64(qs["q"]), qI_host(qs["qI"], cfg), host64(qs["w"])
     sink = host64(W["sink"])
@@ -484,7 +498,7 @@ def test_deterministic_repeat():
 # ----------------------------------------------------------------------------- full sizes
 
 
-def _decode_full(name, B=None, check_scores_for=2, **over):
+def _decode_full(name, B=None, check_scores_for=2, paged=False, **over):
     """A decode step of a full-size configuration on a synthetic cache: every query's
     selection (under the tie rule) and output are checked against the oracle."""
     cfg = synth.config(name, **over)
@@ -492,7 +506,7 @@ def _decode_full(name, B=None, check_scores_for=2, **over):
     N = cfg["prefix"] // cfg["m"]
     tau = cfg["prefix"]
     taus = [(b, tau) for b in range(B)]
-    dims, cache, qs, W, q_seq, q_pos = _synthetic_decode_setup(cfg, B, N, cfg["n_win"], taus, seed=31)
+    dims, cache, qs, W, q_seq, q_pos = _synthetic_decode_setup(cfg, B, N, cfg["n_win"], taus, seed=31, paged=paged)
     stats = _run_index_attend_and_check(cfg, dims, cache, qs, W, q_seq, q_pos, taus,
                                         check_scores=True)
     return stats
@@ -523,6 +537,28 @@ def test_c3_decode_full_size_mxfp4():
 def test_c5_hca_decode_full_size():
     """HCA decode, 8 sequences x 8192 entries (1M tokens, m'=128), dense attention."""
     _decode_full("c5")
+
+
+def test_c2_decode_full_size_paged():
+    """Flash decode at full size on a paged cache: 128-token pages (32 entries) in a shuffled
+    pool, one block table per sequence."""
+    _decode_full("c2", paged=True)
+
+
+def test_c2_decode_full_size_mxfp4_paged():
+    """The same with MXFP4 keys (per page: 32 rows of element bytes, then 32 rows of scales)."""
+    _decode_full("c2", idx_fmt="mxfp4", paged=True)
+
+
+def test_c3_decode_full_size_paged():
+    """Pro decode at full size on a paged cache (8192 pages per sequence)."""
+    _decode_full("c3", paged=True)
+
+
+def test_c5_hca_decode_full_size_paged():
+    """HCA dense decode on a paged cache: a 128-token page holds one HCA entry, so every
+    entry is looked up in the block table."""
+    _decode_full("c5", paged=True)
 
 
 @pytest.mark.parametrize("idx_fmt", ["e4m3", "mxfp4"])
