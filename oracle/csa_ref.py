@@ -28,6 +28,10 @@ Pins (what each function is checked against, in tests/test_oracle_*.py):
                 path switched off reduces to dense causal MQA (torch SDPA in float64);
                 sink limits and sum of weights < 1 ([RN] §2.5.4 eq. 27)
   codecs        the E4M3 and bfloat16 formats against their bit definitions and torch casts
+  CSA2          the single-path fold without bias (closed forms; no token of another block
+                reaches an entry); index keys from the entry (linear in the normalised entry,
+                blind to the entry's scale and position); MXFP4 main rows (worked blocks);
+                m = 1 with every entry selected reduces to dense causal MQA
 The learned meaning of the weights (whether trained values make a good model) cannot be
 checked without trained weights: that part is parity unpinned and out of scope.
 """
@@ -51,6 +55,7 @@ __all__ = [
     "finalize_kv",
     "store_kv",
     "store_index_keys",
+    "index_keys_from_entries",
     "compress_sequence",
     "compress_entries",
     "raw_rows",
@@ -77,10 +82,14 @@ class Dims:
     c_I      indexer key / query width                    ([RN] §2.3.2)
     n_hI     indexer heads                                ([RN] §2.3.2)
     m        tokens per compressed entry (m for CSA, m' for HCA)
-    dual     True: overlapping a|b compression (CSA); False: single path (HCA, [RN] §2.4)
-    top_k    entries kept per query; 0 means every visible entry (HCA, [RN] eq. 26)
+    dual     True: overlapping a|b compression (CSA); False: single path (HCA, [RN] §2.4,
+             and CSA2)
+    top_k    entries kept per query; 0 means every visible entry (HCA, [RN] eq. 26).  A
+             single-path layer with top_k > 0 is CSA2 ([PT] §6.4, V4.1-Flash paragraph):
+             no overlapping windows, no in-block bias, index keys projected from the entry
     n_win    sliding-window length over uncompressed tokens ([RN] §2.5.3; [PT] §2.4)
-    kv_fmt   "f32" or "q" (E4M3 for the non-RoPE dims, bfloat16 for the RoPE dims)
+    kv_fmt   "f32", "q" (E4M3 for the non-RoPE dims, bfloat16 for the RoPE dims) or "q4"
+             (MXFP4 for the non-RoPE dims, bfloat16 for the RoPE dims: CSA2's FP4 main KV)
     idx_fmt  "f32", "e4m3" or "mxfp4" (indexer keys and queries)
     """
 
@@ -162,11 +171,15 @@ def csa_fold(Ca, Cb, Za, Zb, Ba, Bb, m: int, prev_b=None, return_weights: bool =
 def hca_fold(C, Z, B, m: int, return_weights: bool = False):
     """Heavily-compressed fold ([RN] §2.4.1 eqs. 22-23): each of the n // m blocks of m
     tokens is soft-maxed per column over its own m logits Z + B (B in R^{m x c}) and summed.
-    Blocks do not overlap and there is no second path."""
+    Blocks do not overlap and there is no second path.
+
+    CSA2's compression ([PT] §6.4, V4.1-Flash paragraph: eqs. 9-12 without the overlapping
+    windows and the in-block positional bias) is read as this fold with m = 4 and no bias:
+    pass B = None."""
     C, Z = np.asarray(C, np.float64), np.asarray(Z, np.float64)
     n, c = C.shape
     nb = n // m
-    logits = Z[: nb * m].reshape(nb, m, c) + B
+    logits = Z[: nb * m].reshape(nb, m, c) + (0.0 if B is None else B)
     S = softmax_columns(logits, axis=1)
     out = np.sum(S * C[: nb * m].reshape(nb, m, c), axis=1)
     return (out, S) if return_weights else out
@@ -224,6 +237,17 @@ def store_kv(y, dims: Dims):
     if dims.kv_fmt == "f32":
         v = codecs.to_f32(y)
         return v, v.astype(np.float32).view(np.uint8).reshape(y.shape[:-1] + (4 * c,))
+    if dims.kv_fmt == "q4":
+        # CSA2's FP4 main KV ([PT] §6.4: main KV from FP8 down to FP4).  Reading: the dims
+        # that were E4M3 become MXFP4 (blocks of 32 sharing an E8M0 scale, the OCP MX rule
+        # as for the FP4 indexer keys); the RoPE dims stay bfloat16.  Bytes: packed element
+        # codes, then the block scale codes, then the bfloat16 dims.
+        codes, scales = codecs.mxfp4_encode(y[..., : c - r])
+        packed = codecs.mxfp4_pack(codes)
+        rope = codecs.bf16_encode(y[..., c - r :])
+        vals = np.concatenate([codecs.mxfp4_decode(packed, scales), codecs.bf16_decode(rope)], axis=-1)
+        rope_b = rope.astype("<u2").view(np.uint8).reshape(y.shape[:-1] + (2 * r,))
+        return vals, np.concatenate([packed, scales, rope_b], axis=-1)
     nope = codecs.e4m3_encode(y[..., : c - r])
     rope = codecs.bf16_encode(y[..., c - r :])
     vals = np.concatenate([codecs.e4m3_decode(nope), codecs.bf16_decode(rope)], axis=-1)
@@ -247,6 +271,16 @@ def store_index_keys(k, dims: Dims):
     return codecs.e4m3_decode(code), code
 
 
+def index_keys_from_entries(pre, W_ik, gamma, dims: Dims):
+    """CSA2's indexer keys, projected from the main KV entries ([PT] §6.4, V4.1-Flash
+    paragraph: the index keys are no longer compressed on their own but projected from the
+    main entry).  Reading: K^I_s = RMSNorm(C^Comp_s) . W^IK with W^IK in R^{c x c_I}, taken
+    from the normalised entry before RoPE (the key then carries no position, as the V4
+    indexer keys carry none) and before the entry is rounded to storage.  ``W_ik`` is
+    W^IK transposed: [c_I][c]."""
+    return rmsnorm(pre, gamma, dims.eps) @ np.asarray(W_ik, np.float64).T
+
+
 def _paths(H, W):
     """Projections of every path listed in the weight dict W (arrays [width][d])."""
     return {name: project(H, W[name]) for name in W["paths"]}
@@ -259,6 +293,8 @@ def compress_sequence(H, W, dims: Dims):
       CSA: "kv_a","kv_b","z_a","z_b" [c][d]; "ki_a","ki_b","zi_a","zi_b" [c_I][d];
            "B_a","B_b" [m][c]; "BI_a","BI_b" [m][c_I]; "gamma_kv" [c] or None.
       HCA: "kv","z" [c][d]; "B" [m][c]; "gamma_kv".
+      CSA2 (single path, top_k > 0): "kv","z" [c][d]; "B" None (no bias); "w_ik" [c_I][c];
+           "gamma_kv".
     Returns a dict with
       "entry_pre"  [n//m][c]    folded entries before RMSNorm/RoPE (float64)
       "entry_fin"  [n//m][c]    finalized entries (before rounding to storage)
@@ -285,8 +321,12 @@ def compress_sequence(H, W, dims: Dims):
         out["ki"], out["ki_bytes"] = store_index_keys(ki, dims)
     else:
         C, Z = project(H, W["kv"]), project(H, W["z"])
-        pre = hca_fold(C, Z, W["B"], m)
+        pre = hca_fold(C, Z, W.get("B"), m)
         raw_src = C
+        if dims.top_k > 0:
+            ki = index_keys_from_entries(pre, W["w_ik"], W.get("gamma_kv"), dims)
+            out["ki_pre"] = ki
+            out["ki"], out["ki_bytes"] = store_index_keys(ki, dims)
     pos_e = m * np.arange(nb)
     fin = finalize_kv(pre, pos_e, W.get("gamma_kv"), dims)
     out["entry_pre"], out["entry_fin"] = pre, fin
@@ -328,7 +368,7 @@ def compress_entries(H_of, entries, W, dims: Dims):
             rows["ki_pre"].append(k[0])
         else:
             cur = H_of(m * i, m * (i + 1))
-            e = hca_fold(project(cur, W["kv"]), project(cur, W["z"]), W["B"], m)
+            e = hca_fold(project(cur, W["kv"]), project(cur, W["z"]), W.get("B"), m)
             rows["entry_pre"].append(e[0])
     out = {"entry_pre": np.array(rows["entry_pre"])}
     pos_e = m * np.asarray(entries, np.float64)
@@ -336,6 +376,9 @@ def compress_entries(H_of, entries, W, dims: Dims):
     out["entry"], out["entry_bytes"] = store_kv(out["entry_fin"], dims)
     if dims.dual:
         out["ki_pre"] = np.array(rows["ki_pre"])
+    elif dims.top_k > 0:
+        out["ki_pre"] = index_keys_from_entries(out["entry_pre"], W["w_ik"], W.get("gamma_kv"), dims)
+    if "ki_pre" in out:
         out["ki"], out["ki_bytes"] = store_index_keys(out["ki_pre"], dims)
     return out
 
