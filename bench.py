@@ -91,7 +91,8 @@ def parse():
     ap.add_argument("--layer", action="store_true",
                     help="time the whole attention layer: the query-side projections before the path "
                          "and the grouped output projection after it included (bf16 configurations)")
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2fp4", "c3", "c4a", "c4afp4", "c4b", "c4bfp4", "c5"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2fp4", "c3", "c4a", "c4afp4", "c4b", "c4bfp4", "c5",
+                                                       "c6", "c6fp4"])
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--paged", action="store_true",
@@ -104,6 +105,9 @@ def parse():
 
 def lib_weights(L, W, dual):
     import torch
+    if W.get("w_ik") is not None:   # CSA2: single path, no bias, entry-to-key projection
+        return L.Weights(torch.stack([W["kv"], W["z"]]).contiguous(), None, W["w_ik"].contiguous(), None,
+                         W["gamma_kv"])
     if dual:
         return L.Weights(torch.stack([W["kv_a"], W["kv_b"], W["z_a"], W["z_b"]]).contiguous(),
                          torch.stack([W["B_a"], W["B_b"]]).contiguous(),
@@ -230,9 +234,10 @@ def cpu_baseline(cfg, seconds):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
+    idx = cfg["top_k"] > 0
     od = R.Dims(d=cfg["d"], c=cfg["c"], rope_dim=cfg["rope_dim"], n_h=cfg["n_h"], c_I=cfg["c_I"],
                 n_hI=cfg["n_hI"], m=cfg["m"], dual=cfg["dual"], top_k=cfg["top_k"],
-                n_win=cfg["n_win"], kv_fmt="q", idx_fmt=cfg["idx_fmt"] if cfg["dual"] else "e4m3")
+                n_win=cfg["n_win"], kv_fmt=cfg["kv_fmt"], idx_fmt=cfg["idx_fmt"] if idx else "e4m3")
     N = cfg["prefix"] // cfg["m"]
     tau = cfg["prefix"]
     W = synth.weights(cfg, device="cpu")
@@ -243,14 +248,18 @@ def cpu_baseline(cfg, seconds):
     c, r = cfg["c"], cfg["rope_dim"]
 
     def dec(b):
+        if cfg["kv_fmt"] == "q4":   # bf16 RoPE dims, MXFP4 element bytes and scale codes
+            ne = (c - r) // 2
+            return np.concatenate([codecs.mxfp4_decode(b[:, 2 * r:2 * r + ne], b[:, 2 * r + ne:2 * r + ne + (c - r) // 32]),
+                                   codecs.bf16_decode(b[:, :2 * r].copy().view("<u2"))], axis=1)
         return np.concatenate([codecs.e4m3_decode(b[:, :c - r]),
                                codecs.bf16_decode(b[:, c - r:].copy().view("<u2"))], axis=1)
     entries = dec(sc["kv"][0].numpy())
     win = dec(sc["win"][0].numpy())
     qs = synth.queries(cfg, 8, device="cpu", mx_codes=(125, 127))
     q = qs["q"].float().numpy().astype(np.float64)
-    ki, qI = cpu_baseline_keys_and_queries(cfg, sc, qs, N) if cfg["dual"] else (None, [None] * 8)
-    w = qs["w"].float().numpy().astype(np.float64) if cfg["dual"] else [None] * 8
+    ki, qI = cpu_baseline_keys_and_queries(cfg, sc, qs, N) if idx else (None, [None] * 8)
+    w = qs["w"].float().numpy().astype(np.float64) if idx else [None] * 8
     h = synth.hidden(cfg, 0, tau, tau + 1, device="cpu").float().numpy().astype(np.float64)
     paths = (("kv_a", "kv_b", "z_a", "z_b", "ki_a", "ki_b", "zi_a", "zi_b") if cfg["dual"]
              else ("kv", "z"))
@@ -271,11 +280,13 @@ def cpu_baseline(cfg, seconds):
         if el >= seconds:
             break
     what = (f"indexer over {N} entries, top-{cfg['top_k']}, attention over {cfg['top_k']}+{cfg['n_win']} rows"
-            if cfg["dual"] else f"dense attention over {N}+{cfg['n_win']} rows")
+            if idx else f"dense attention over {N}+{cfg['n_win']} rows")
+    if cfg["kv_fmt"] == "q4":
+        what += ", MXFP4 main rows"
     return {"value": round(n / el, 2), "unit": "queries/s", "cores": int(threads), "kind": "oracle",
             "cpu_model": cpu_model(),
             "sample": f"{n} single-query decode steps of the same workload (compress of the new "
-                      f"token, {what}{', MXFP4 indexer keys and queries, BF16 scores' if cfg['idx_fmt'] == 'mxfp4' and cfg['dual'] else ''}), "
+                      f"token, {what}{', MXFP4 indexer keys and queries, BF16 scores' if cfg['idx_fmt'] == 'mxfp4' and idx else ''}), "
                       f"synthetic inputs of the same shapes, {el:.1f} s"}
 
 
@@ -348,17 +359,17 @@ def run_decode(args, cfg):
     dev = "cuda:0"
     calibration_copy()
     B, k, m = cfg["B"], cfg["top_k"], cfg["m"]
-    dual = cfg["dual"]
+    has_idx = cfg["top_k"] > 0      # CSA and CSA2 score and select; HCA attends densely
     dims = L.Dims.from_config(cfg)
     W = synth.weights(cfg, device=dev)
-    lw = lib_weights(L, W, dual)
+    lw = lib_weights(L, W, cfg["dual"])
     N = cfg["prefix"] // m          # entry capacity per sequence
     steps = args.steps or 200
     warm = args.warmup if args.warmup is not None else 10
     # Enough rotating copies that the tensor a launch streams (indexer keys, or the whole cache
     # for the dense variant) is not still held by the 256 MB last-level cache from an earlier
     # step: the set that rotates between two uses of a copy is at least twice that size.
-    streamed = B * N * (cfg["c_I"] if dual else synth.row_bytes(cfg))
+    streamed = B * N * (cfg["c_I"] if has_idx else synth.row_bytes(cfg))
     copies = args.copies or min(16, max(3, -(-2 * MALL_BYTES // streamed) + 1))
     G = copies
     # Step s runs on copy s % G at position tau_start + s // G: every copy advances one token
@@ -386,7 +397,7 @@ def run_decode(args, cfg):
     ws_c = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_COMPRESS, B=B, T=1)), dtype=torch.uint8, device=dev)
     ws_a = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_ATTEND, Q=B, cap=N)), dtype=torch.uint8, device=dev)
     out = torch.empty((B, cfg["n_h"], cfg["c"]), dtype=torch.bfloat16, device=dev)
-    if dual:
+    if has_idx:
         ws_t = torch.empty(max(1, L.csa_topk_workspace_size(dims, B, N)), dtype=torch.uint8, device=dev)
         scores = torch.empty((B, N), dtype=torch.bfloat16 if dims.idx_fmt == "mxfp4" else torch.float32,
                              device=dev)
@@ -402,9 +413,9 @@ def run_decode(args, cfg):
         L.csa_topk(dims, c, q_seq, q_pos, B, scores, N, idx, ws_t)
 
     def k_attend(c):
-        L.csa_attend(dims, c, qs["q"], W["gamma_q"], W["sink"], q_seq, q_pos, B, idx if dual else None, out, ws_a)
+        L.csa_attend(dims, c, qs["q"], W["gamma_q"], W["sink"], q_seq, q_pos, B, idx if has_idx else None, out, ws_a)
 
-    phases = [k_compress, k_index, k_topk, k_attend] if dual else [k_compress, k_attend]
+    phases = [k_compress, k_index, k_topk, k_attend] if has_idx else [k_compress, k_attend]
     ws_f = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_FORWARD, B=B, T=1, cap=N)), dtype=torch.uint8, device=dev)
 
     if args.layer:
@@ -413,8 +424,8 @@ def run_decode(args, cfg):
         pw = L.ProjWeights(**PW)
         h = H1.reshape(B, cfg["d"])
         q_l = torch.empty_like(qs["q"])
-        qI_l = torch.empty_like(qs["qI"]) if dual else None
-        w_l = torch.empty_like(qs["w"]) if dual else None
+        qI_l = torch.empty_like(qs["qI"]) if has_idx else None
+        w_l = torch.empty_like(qs["w"]) if has_idx else None
         y = torch.empty((B, cfg["d"]), dtype=torch.bfloat16, device=dev)
         ws_q = torch.empty(max(1, L.csa_query_project_workspace_size(dims, pw, B)), dtype=torch.uint8, device=dev)
         ws_o = torch.empty(max(1, L.csa_output_project_workspace_size(dims, pw, B)), dtype=torch.uint8, device=dev)
@@ -432,12 +443,12 @@ def run_decode(args, cfg):
         if args.layer:
             k_qproj(c)
             L.csa_forward(dims, lw, c, Hc[cyc], 1, posc[cyc], q_l, qI_l, w_l, W["gamma_q"], W["sink"], out,
-                          idx if dual else None, ws_f)
+                          idx if has_idx else None, ws_f)
             k_oproj(c)
             return
-        L.csa_forward(dims, lw, c, Hc[cyc], 1, posc[cyc], qs["q"], qs["qI"] if dual else None,
-                      qs["w"] if dual else None, W["gamma_q"], W["sink"], out,
-                      idx if dual else None, ws_f)
+        L.csa_forward(dims, lw, c, Hc[cyc], 1, posc[cyc], qs["q"], qs["qI"] if has_idx else None,
+                      qs["w"] if has_idx else None, W["gamma_q"], W["sink"], out,
+                      idx if has_idx else None, ws_f)
 
     def graphs(s0, s1):
         # steps s0 .. s1 - 1 in graphs of at most one cycle each (a decode loop over the copies
@@ -461,28 +472,31 @@ def run_decode(args, cfg):
     wall = time.perf_counter() - t0
     # the last step again, eagerly: a step at a position a copy has already taken recomputes
     # exactly what it wrote then, so the graph's output must be reproduced bit for bit
-    got = (y.clone() if args.layer else out.clone(), idx.clone() if dual else None)
+    got = (y.clone() if args.layer else out.clone(), idx.clone() if has_idx else None)
     step(warm + steps - 1)
     torch.cuda.synchronize()
-    ok = torch.equal(y if args.layer else out, got[0]) and (not dual or torch.equal(idx, got[1]))
+    ok = torch.equal(y if args.layer else out, got[0]) and (not has_idx or torch.equal(idx, got[1]))
 
     # per-kernel launch durations (same inputs and grids, rotating cache copies)
     kt = {name: kernel_time_us([lambda c=c, f=f: f(c) for c in caches])
-          for name, f in zip(["compress", "index_scores", "topk", "attend"] if dual else ["compress", "attend"], phases)}
+          for name, f in zip(["compress", "index_scores", "topk", "attend"] if has_idx else ["compress", "attend"], phases)}
     if args.layer:
         kt["q_proj"] = kernel_time_us([lambda c=c: k_qproj(c) for c in caches])
         kt["o_proj"] = kernel_time_us([lambda c=c: k_oproj(c) for c in caches])
     res = {
-        "metric": ("CSA decode queries/s (Flash-shaped, 128K context, batch 16)" if cfg["name"] == "c2" and not args.layer
-                   else f"CSA {'attention-layer ' if args.layer else ''}decode queries/s ({cfg['name']})"),
+        "metric": ("CSA decode queries/s (Flash-shaped, 128K context, batch 16)"
+                   if cfg["name"] == "c2" and not args.layer and not paged
+                   else f"CSA {'attention-layer ' if args.layer else ''}decode queries/s ({cfg['name']}"
+                        f"{', paged cache' if paged else ''})"),
         "value": round(B * steps / wall, 1), "unit": "queries/s", "n_gpus": 1, "steps": steps,
         "warmup": warm, "ms_per_step": round(wall / steps * 1e3, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": ("MXFP4 MFMA indexer, bf16 index scores; bf16 MFMA on E4M3/bf16 KV storage, fp32 accumulate"
-                  if cfg["idx_fmt"] == "mxfp4" else "bf16 MFMA on E4M3/bf16 storage, fp32 accumulate"),
+        "dtype": (("MXFP4 MFMA indexer, bf16 index scores; " if cfg["idx_fmt"] == "mxfp4" else "")
+                  + ("bf16 MFMA on MXFP4/bf16 KV storage" if cfg["kv_fmt"] == "q4" else "bf16 MFMA on E4M3/bf16 KV storage")
+                  + ", fp32 accumulate"),
         "data": "synthetic (seeded N(0,1) hidden states and queries, N(0,1/fan_in) weights)",
     }
-    if dual:
+    if has_idx:
         key_bytes = cfg["c_I"] // 2 + cfg["c_I"] // 32 if cfg["idx_fmt"] == "mxfp4" else cfg["c_I"]
         bytes_per_query = N * key_bytes + cfg["n_hI"] * key_bytes + 2 * cfg["n_hI"]
         alg = B * bytes_per_query
@@ -501,7 +515,7 @@ def run_decode(args, cfg):
                            "achieved": round(alg / dur / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                            "frac": round(alg / dur / HBM_PEAK, 4), "traffic": None,
                            "alg_bytes_per_launch": alg, "avg_launch_us": round(kt["attend"], 2)}
-    if dual:
+    if has_idx:
         rows = k + cfg["n_win"]
         at_bytes = B * (rows * synth_row_bytes(cfg) + 2 * 2 * cfg["n_h"] * cfg["c"] + 4 * k)
         at_flops = B * 2.0 * 2.0 * cfg["n_h"] * cfg["c"] * rows
@@ -521,14 +535,18 @@ def run_decode(args, cfg):
             "c3": "Pro-shaped CSA decode, 4 seqs x 1048576-token context (262144 entries), d=7168, "
                   "128 heads x 512, indexer 64x128, top-k 1024, n_win 128",
             "c5": "HCA decode, 8 seqs x 1048576-token context (8192 entries, m'=128), d=4096, "
-                  "64 heads x 512, dense, n_win 128"}[cfg["name"]]
+                  "64 heads x 512, dense, n_win 128",
+            "c6": "CSA2 decode (single-path fold with m=4 and no bias, index keys projected from the "
+                  "entry, MXFP4 main KV rows of 384 B), 16 seqs x 131072-token context (32768 entries), "
+                  "d=4096, 64 heads x 512, indexer 64x128, top-k 512, n_win 128",
+            "c6fp4": "CSA2 decode as c6, with the indexer's keys and queries in MXFP4"}[cfg["name"]]
     if paged:
         desc += (f"; paged cache: {PAGE_TOKENS}-token pages ({PAGE_TOKENS // m} entries) dealt over a shuffled "
                  f"pool through a per-sequence block table")
     if args.layer:
         # the projections stream their weights once per step: HBM-bound at decode
         d, dc, nq = cfg["d"], cfg["d_c"], cfg["n_h"] * cfg["c"]
-        wq = 2 * (dc * d + nq * dc + ((cfg["n_hI"] * cfg["c_I"] * dc + cfg["n_hI"] * d) if dual else 0))
+        wq = 2 * (dc * d + nq * dc + ((cfg["n_hI"] * cfg["c_I"] * dc + cfg["n_hI"] * d) if has_idx else 0))
         wo = 2 * (nq * cfg["d_g"] + d * cfg["g"] * cfg["d_g"])
         tq, to = kt["q_proj"] * 1e-6, kt["o_proj"] * 1e-6
         res["roofline_projections"] = {
@@ -590,7 +608,8 @@ def prefill_rooflines(L, cfg, dims, cache, qs, W, idx, out, p0, T, q_chunk, ws):
 
 
 def synth_row_bytes(cfg):
-    return cfg["c"] - cfg["rope_dim"] + 2 * cfg["rope_dim"] if cfg["kv_fmt"] != "f32" else 4 * cfg["c"]
+    import synth
+    return synth.row_bytes(cfg)
 
 
 def run_prefill(args, cfg):
@@ -744,7 +763,7 @@ def main():
     import synth
     torch.cuda.set_device(0)
     cfg = synth.config(args.config)
-    if args.config in ("c2", "c2fp4", "c3", "c5"):
+    if args.config in ("c2", "c2fp4", "c3", "c5", "c6", "c6fp4"):
         res, ok = run_decode(args, cfg)
     else:
         res, ok = run_prefill(args, cfg)
@@ -767,7 +786,15 @@ def main():
                                                           "graph_replay_matches_eager")}
         extra["c2_decode_paged"]["workload"] = rp["config"]["workload"]
         ok3 = ok3 and okp
-        print(f"[bench] paged c2 done ({rp['value']} queries/s); c4a prefill", file=sys.stderr, flush=True)
+        print(f"[bench] paged c2 done ({rp['value']} queries/s); c6 (CSA2) decode", file=sys.stderr, flush=True)
+        sub = argparse.Namespace(**{**vars(args), "steps": 20, "warmup": 5, "no_cpu": True, "copies": None,
+                                    "paged": False})
+        r6, ok6 = run_decode(sub, synth.config("c6"))
+        extra["c6_decode"] = {k_: r6[k_] for k_ in ("metric", "value", "unit", "ms_per_step", "roofline",
+                                                    "roofline_attention", "kernels_us", "graph_replay_matches_eager")}
+        extra["c6_decode"]["workload"] = r6["config"]["workload"]
+        ok3 = ok3 and ok6
+        print(f"[bench] c6 done ({r6['value']} queries/s); c4a prefill", file=sys.stderr, flush=True)
         sub = argparse.Namespace(**{**vars(args), "steps": 3, "warmup": 1, "no_cpu": True})
         r4, _ = run_prefill(sub, synth.config("c4a"))
         extra["c4a_prefill"] = {k_: r4[k_] for k_ in ("metric", "value", "unit", "ms_per_step", "roofline",

@@ -6,7 +6,9 @@
  *      softmax taken per column over 2m weighted projections with a learned positional bias
  *      (reading notes "DeepSeekV4技术报告阅读笔记", zouxinn.github.io, §2.3.1 eqs. 9-12;
  *      PaperTrace "02 · DeepSeek-V4: 压缩注意力撑起 1M 上下文" §2.1), or the single-path,
- *      non-overlapping variant with m' tokens per entry (reading notes §2.4.1 eqs. 20-23);
+ *      non-overlapping variant with m' tokens per entry (reading notes §2.4.1 eqs. 20-23),
+ *      which with m = 4, no bias and an indexer is the CSA2 layer (PaperTrace §6.4,
+ *      V4.1-Flash paragraph);
  *   2. lightning-indexer scores I_{t,s} = sum_h w_{t,h} ReLU(q^I_{t,h} . K^I_s)
  *      (reading notes §2.3.2 eq. 16);
  *   3. per-query top-k over the visible entries (reading notes eq. 17);
@@ -57,7 +59,9 @@ typedef enum csa_format {
   CSA_FMT_BF16 = 1,       /* bfloat16 */
   CSA_FMT_E4M3 = 2,       /* OCP FP8 E4M3 (e4m3fn), unit scale */
   CSA_FMT_E4M3_BF16 = 3,  /* KV rows: c - rope_dim E4M3 bytes, then rope_dim bfloat16 */
-  CSA_FMT_MXFP4 = 4       /* OCP MX FP4: blocks of 32 E2M1 elements sharing one E8M0 scale */
+  CSA_FMT_MXFP4 = 4,      /* OCP MX FP4: blocks of 32 E2M1 elements sharing one E8M0 scale */
+  CSA_FMT_MXFP4_BF16 = 5  /* KV rows (CSA2's FP4 main KV): rope_dim bfloat16, then the other
+                             dims as MXFP4 element bytes, then their scale codes, zero-padded */
 } csa_format;
 
 /* Operation selector for csa_workspace_size(). */
@@ -75,8 +79,11 @@ typedef enum csa_op {
  *   rope_dim  trailing dims under RoPE (the pages use 64); even, <= c.
  *   n_h       query heads; n_hI, c_I indexer heads and width (reading notes §2.3.2).
  *   m         tokens per entry: m for CSA (pages: 4), m' for HCA (pages: 128).
- *   dual      1 = CSA (a|b overlapping fold, indexer, top-k); 0 = HCA (single path, dense).
- *   top_k     entries kept per query (pages: 512 Flash, 1024 Pro); 0 with dual = 0.
+ *   dual      1 = CSA (a|b overlapping fold, indexer, top-k); 0 = single path: HCA with
+ *             top_k = 0 (dense), CSA2 with top_k > 0 (PaperTrace §6.4, V4.1-Flash paragraph:
+ *             no overlapping windows and no in-block bias; the index keys are projected from
+ *             the main entry, K^I = RMSNorm(entry) . W^IK, before RoPE and storage).
+ *   top_k     entries kept per query (pages: 512 Flash, 1024 Pro); 0 = dense (HCA).
  *   n_win     sliding-window length (pages: 128); the window of a query at tau covers
  *             positions max(0, tau - n_win + 1) .. tau, the query's own token included.
  *             n_win >= m is required (INVALID_ARGUMENT otherwise), for CSA and HCA alike: a
@@ -86,9 +93,13 @@ typedef enum csa_op {
  *   rms_eps   RMSNorm epsilon (1e-6).
  *   act_fmt   F32 or BF16: hidden states, projection weights, queries q, indexer weights w,
  *             and the attention output.
- *   kv_fmt    F32 (c floats per row) or E4M3_BF16 (c - rope_dim + 2 * rope_dim bytes per row:
+ *   kv_fmt    F32 (c floats per row), E4M3_BF16 (c - rope_dim + 2 * rope_dim bytes per row:
  *             RoPE dims kept in BF16, the rest in FP8, as the explainer's key-numbers table and
- *             PaperTrace §2.5 state).
+ *             PaperTrace §2.5 state) or MXFP4_BF16 (CSA2's FP4 main KV, PaperTrace §6.4: the
+ *             FP8 dims become MXFP4 under the MX rule below, the RoPE dims stay BF16; for
+ *             c = 512, rope_dim = 64 a 384-byte row: 128 bytes of BF16 RoPE dims, 224 bytes
+ *             of E2M1 codes for dims 0..447 (dim 2i in the low nibble), 14 scale codes, 18
+ *             zero bytes, so that a row fills three 128-byte lines).
  *   idx_fmt   F32, E4M3 or MXFP4: indexer keys K^I and indexer queries q^I.  MXFP4 is the
  *             pages' later FP4 indexer path (PaperTrace §3.3: 1x32 sub-blocks with their own
  *             scales) in the OCP MX v1.0 format: per block of 32 dims one E8M0
@@ -116,12 +127,15 @@ typedef struct csa_dims {
  * Compression weights, stored transposed (row u of a [width][d] matrix is column u of the
  * pages' W in R^{d x width}), in act_fmt.
  *   CSA: w_kv  [4][c][d]   = W^{aKV}, W^{bKV}, W^{aZ}, W^{bZ}       (reading notes eqs. 9-10)
- *        w_idx [4][c_I][d] = the same four for the indexer keys   (K^IComp: "the same
- *                            compression, smaller output width", deep dive §3.2)
+ *        w_idx [4][c_I][d] = the same four for the indexer keys   (K^IComp: the deep dive,
+ *                            §3.2, compresses the keys the same way at a smaller width)
  *        bias     [2][m][c]   = B^a, B^b (float32)                 (eq. 11)
  *        bias_idx [2][m][c_I] = the indexer's B^a, B^b (float32)
  *   HCA: w_kv  [2][c][d]   = W^{KV}, W^{Z}                          (eqs. 20-21)
  *        w_idx = NULL, bias [m][c] = B (float32) (eq. 22), bias_idx = NULL
+ *   CSA2 (dual = 0, top_k > 0): w_kv [2][c][d] = W^{KV}, W^{Z}; bias = NULL (no in-block
+ *        bias; a bias, if given, is added as for HCA); w_idx [c_I][c] = W^IK transposed, the
+ *        projection of the normalised entry onto the index key; bias_idx = NULL.
  *   gamma_kv [c] float32 RMSNorm weight of the KV head, or NULL for ones.
  */
 typedef struct csa_weights {
@@ -141,14 +155,15 @@ typedef struct csa_weights {
  *            j % win_cap.  A compress call of T tokens needs win_cap >= T + n_win - 1 for
  *            the chunk's own queries to find their window rows.
  *   kv       [B][cap][row_bytes]   finalized entries (RMSNorm, RoPE at position m*i).
- *   ki       [B][cap][c_I]         indexer keys in idx_fmt (CSA only; NULL for HCA).
+ *   ki       [B][cap][c_I]         indexer keys in idx_fmt (CSA and CSA2; NULL for HCA).
  *   n_entries[B] int32             complete entries; written by csa_compress.
- *   win      [B][win_cap][row_bytes] raw window rows: the a-path row C^a_j (HCA: C_j),
- *                                  finalized at position j.
+ *   win      [B][win_cap][row_bytes] raw window rows: the a-path row C^a_j (HCA, CSA2:
+ *                                  C_j), finalized at position j, in kv_fmt.
  *   win_pos  [B][win_cap] int32    position held by each ring slot, -1 when empty; the
  *                                  caller fills it with -1 before a sequence's first call.
  *   state    [B][S][P] float32     projections of the last S tokens (S = 2m for CSA, m for
- *                                  HCA; P = 4c + 4c_I for CSA, 2c for HCA), slot j % S, so
+ *                                  HCA and CSA2; P = 4c + 4c_I for CSA, 2c for HCA and
+ *                                  CSA2), slot j % S, so
  *                                  that a block split across calls still folds.
  * Successive csa_compress calls on a sequence must cover consecutive positions.
  *
@@ -247,7 +262,7 @@ int csa_compress(const csa_dims* dims, const csa_weights* w, const csa_cache* ca
  *           s >= V are left untouched): float32, or with idx_fmt MXFP4 bfloat16, the pages'
  *           BF16 index scores of the FP4 path (PaperTrace §3.3), each the exact score
  *           rounded to nearest even.
- * Errors: INVALID_ARGUMENT (null pointer, Q < 1, dual = 0 or top_k < 1), UNSUPPORTED
+ * Errors: INVALID_ARGUMENT (null pointer, Q < 1, top_k = 0), UNSUPPORTED
  * (V could exceed what the selection kernels handle for this top_k), WORKSPACE_TOO_SMALL,
  * HIP_ERROR.
  */
@@ -309,9 +324,11 @@ int csa_attend(const csa_dims* dims, const csa_cache* cache, const void* q,
                size_t ws_bytes, hipStream_t stream);
 
 /*
- * The whole path for a chunk of T new tokens per sequence: csa_compress, then (CSA)
+ * The whole path for a chunk of T new tokens per sequence: csa_compress, then (CSA, CSA2)
  * csa_index_topk and csa_attend with the new tokens as queries (query b*T + t sits at
- * position pos0[b] + t), or (HCA) dense csa_attend.
+ * position pos0[b] + t), or (HCA) dense csa_attend.  A CSA2 layer that reuses an earlier
+ * layer's KV and top-k (PaperTrace §6.4) runs no forward of its own: it calls csa_attend on
+ * that layer's cache with that layer's idx_out and its own queries.
  *   q, qI, w  per-query inputs as in csa_index_topk / csa_attend, Q = B*T.
  *   idx_out   [Q][top_k] int32 receiving the selection, or NULL (CSA: then it lives in ws).
  * The indexer works on q_chunk queries at a time, the largest that fits ws_bytes.
@@ -366,8 +383,8 @@ size_t csa_noalloc_scratch_bytes(void);
 typedef struct csa_proj_weights {
   const void* w_dq;   /* [d_c][d] bf16: W^DQ */
   const void* w_uq;   /* [n_h * c][d_c] bf16: W^UQ */
-  const void* w_iuq;  /* [n_hI * c_I][d_c] bf16: W^IUQ (CSA; not read when dual = 0) */
-  const void* w_w;    /* [n_hI][d] bf16: W^w (CSA; not read when dual = 0) */
+  const void* w_iuq;  /* [n_hI * c_I][d_c] bf16: W^IUQ (CSA, CSA2; not read when top_k = 0) */
+  const void* w_w;    /* [n_hI][d] bf16: W^w (CSA, CSA2; not read when top_k = 0) */
   const void* w_og;   /* [g][d_g][n_h * c / g] bf16: group i's map at w_og + i d_g (n_h c / g) */
   const void* w_o;    /* [d][g * d_g] bf16: the map of the concatenated groups to d */
   int32_t d_c;        /* latent width, a multiple of 64 */
@@ -387,8 +404,8 @@ size_t csa_query_project_workspace_size(const csa_dims* dims, const csa_proj_wei
  *   q   [T][n_h][c] bf16 out: the attention queries, as csa_attend reads them.
  *   qI  [T] rows out in the indexer's format (idx_fmt E4M3: [n_hI][c_I] codes; MXFP4: n_hI
  *       rows of c_I / 2 element bytes then n_hI rows of c_I / 32 scale codes, the encoding
- *       of the keys), as csa_index_topk reads them.  CSA only; NULL when dual = 0.
- *   w   [T][n_hI] bf16 out: the indexer head weights.  CSA only; NULL when dual = 0.
+ *       of the keys), as csa_index_topk reads them.  NULL when top_k = 0 (HCA).
+ *   w   [T][n_hI] bf16 out: the indexer head weights.  NULL when top_k = 0 (HCA).
  * c^Q is held in bf16 between the two products; accumulation is float32.  ws (device,
  * csa_query_project_workspace_size bytes) holds c^Q and split-K partial sums.
  * Errors: INVALID_ARGUMENT (null pointer, T < 1), UNSUPPORTED (formats or widths outside the

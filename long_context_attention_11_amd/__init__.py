@@ -21,11 +21,11 @@ __all__ = [
     "csa_index_scores", "csa_topk", "csa_topk_workspace_size", "ProjWeights", "csa_query_project",
     "csa_query_project_workspace_size", "csa_output_project", "csa_output_project_workspace_size",
     "csa_forward_noalloc", "csa_noalloc_scratch_bytes", "csa_index_scores_grouped", "OP_COMPRESS", "OP_INDEX_TOPK", "OP_ATTEND", "OP_FORWARD",
-    "FMT_F32", "FMT_BF16", "FMT_E4M3", "FMT_E4M3_BF16", "FMT_MXFP4", "EXPORTED_SYMBOLS",
+    "FMT_F32", "FMT_BF16", "FMT_E4M3", "FMT_E4M3_BF16", "FMT_MXFP4", "FMT_MXFP4_BF16", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-FMT_F32, FMT_BF16, FMT_E4M3, FMT_E4M3_BF16, FMT_MXFP4 = 0, 1, 2, 3, 4
+FMT_F32, FMT_BF16, FMT_E4M3, FMT_E4M3_BF16, FMT_MXFP4, FMT_MXFP4_BF16 = 0, 1, 2, 3, 4, 5
 OP_COMPRESS, OP_INDEX_TOPK, OP_ATTEND, OP_FORWARD = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = (
@@ -147,13 +147,15 @@ def _check(status: int):
 
 # ----------------------------------------------------------------------------- structures
 
-_FMT = {"f32": FMT_F32, "bf16": FMT_BF16, "e4m3": FMT_E4M3, "q": FMT_E4M3_BF16, "mxfp4": FMT_MXFP4}
+_FMT = {"f32": FMT_F32, "bf16": FMT_BF16, "e4m3": FMT_E4M3, "q": FMT_E4M3_BF16, "mxfp4": FMT_MXFP4,
+        "q4": FMT_MXFP4_BF16}
 
 
 @dataclass
 class Dims:
-    """Layer shape and formats (mirrors csa_dims).  ``kv_fmt``: "f32" or "q" (E4M3 + bf16
-    RoPE dims); ``idx_fmt``: "f32", "e4m3" or "mxfp4"; ``act``: "f32" or "bf16"."""
+    """Layer shape and formats (mirrors csa_dims).  ``kv_fmt``: "f32", "q" (E4M3 + bf16
+    RoPE dims) or "q4" (MXFP4 + bf16 RoPE dims); ``idx_fmt``: "f32", "e4m3" or "mxfp4";
+    ``act``: "f32" or "bf16".  dual = False with top_k > 0 is a CSA2 layer."""
     d: int
     c: int
     rope_dim: int
@@ -256,10 +258,10 @@ class Cache:
             self.max_blocks, self.page_tokens, self.n_pages = 0, 0, 0
             groups, rows = B, cap                              # one group of cap rows per sequence
         self.kv = torch.zeros((groups, rows, rb), **u8)
-        if dims.dual and dims.idx_fmt == "mxfp4":
+        if dims.top_k > 0 and dims.idx_fmt == "mxfp4":
             # per group: rows of c_I / 2 element bytes, then rows of c_I / 32 scale codes
             self.ki = torch.zeros((groups, rows * (dims.c_I // 2 + dims.c_I // 32)), **u8)
-        elif dims.dual:
+        elif dims.top_k > 0:
             kib = dims.c_I * (4 if dims.idx_fmt == "f32" else 1)
             self.ki = torch.zeros((groups, rows, kib), **u8)
         else:

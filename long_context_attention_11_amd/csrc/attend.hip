@@ -143,16 +143,34 @@ __device__ __forceinline__ int hs_sigma(int p) {
   return (p & ~15) + 8 * ((p >> 3) & 1) + 2 * (p & 3) + ((p >> 2) & 1);
 }
 
-// First dim of MFMA step ks for lane group g (the dim pairing above).
+// Row formats.  FMT 0: E4M3_BF16 rows as above.  FMT 1: MXFP4_BF16 rows (CSA2's FP4 main
+// KV, 384 bytes): six 64-byte pieces, 0 and 1 the bf16 RoPE dims (lane group g of piece i:
+// dims 448 + 32i + 8g ..), 2 .. 4 and the first half of 5 the E2M1 codes (lane group g of
+// piece i: the 32 dims of block 4(i - 2) + g), the third quarter of 5 the 14 scale codes.
+// Each code piece widens (exactly, by the hardware's scaled FP4 conversion) into four
+// 8-dim MFMA slices; piece 5 feeds its four steps from lane groups 0 and 1 only (the others
+// contribute zeros), so a row takes 18 MFMA steps instead of 16.
+template <int FMT> struct RowFmt;
+template <> struct RowFmt<0> { static constexpr int BYTES = 576, PIECES = 9, KSTEPS = 16; };
+template <> struct RowFmt<1> { static constexpr int BYTES = 384, PIECES = 6, KSTEPS = 18; };
+
+// First dim of MFMA step ks for lane group g (the dim pairings above).
+template <int FMT>
 __device__ __forceinline__ int hs_dim(int ks, int g) {
-  return ks < 14 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : ANOPE + 32 * (ks - 14) + 8 * g;
+  if constexpr (FMT == 0) {
+    return ks < 14 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : ANOPE + 32 * (ks - 14) + 8 * g;
+  } else {
+    if (ks < 2) return ANOPE + 32 * ks + 8 * g;
+    if (ks < 14) return 32 * (4 * ((ks - 2) >> 2) + g) + 8 * ((ks - 2) & 3);
+    return g < 2 ? 32 * (12 + g) + 8 * (ks - 14) : 0;   // g >= 2: zero key operand
+  }
 }
 
 __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
 }
 
-template <bool SPARSE, bool PAGED>
+template <bool SPARSE, bool PAGED, int FMT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_attend_hs(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t Ks[HS_ROWS * HS_PITCH];
@@ -221,7 +239,8 @@ void k_attend_hs(AttendArgs a) {
   // paged: row numbers are pool rows (kv is the pool), looked up once per entry here, so
   // that the loop below reads them from LDS like an index list; entries past the visible
   // ones become -1, and only window rows then need the visibility test
-  const uint8_t* kvseq = PAGED ? a.kv : a.kv + (size_t)seq * a.cap * AROWB;
+  constexpr int ROWB = RowFmt<FMT>::BYTES, NPIECE = RowFmt<FMT>::PIECES, NKS = RowFmt<FMT>::KSTEPS;
+  const uint8_t* kvseq = PAGED ? a.kv : a.kv + (size_t)seq * a.cap * ROWB;
   if constexpr (PAGED) {
     auto pool_row = [&](int e) {
       return e >= 0 && e < min(V, a.cap) ? page_of(a.rm, seq, e) * a.rm.epp + e % a.rm.epp : -1;
@@ -231,14 +250,14 @@ void k_attend_hs(AttendArgs a) {
 #pragma unroll
     for (int i = 0; i < HS_IPT; ++i) rid[i] = pool_row(SPARSE ? rid[i] : rid_row(i));
   }
-  const uint8_t* winseq = a.win + (size_t)seq * a.win_cap * AROWB;
+  const uint8_t* winseq = a.win + (size_t)seq * a.win_cap * ROWB;
   const int32_t* wpseq = a.win_pos + (size_t)seq * a.win_cap;
 
   // ---- row gather: lane (row, g) loads bytes 64i + 16g .. +15 of the row (i < 9; pieces
   // 0..6 hold E4M3 dims, 7 and 8 bf16 RoPE dims) and the position its window slot holds.
   // Loads are unconditional: masked rows read row 0 of the sequence and are zeroed at
   // widening.
-  uint4 pre[HS_DEPTH][9];
+  uint4 pre[HS_DEPTH][NPIECE];
   int chk[HS_DEPTH], wpv[HS_DEPTH], sv[HS_DEPTH];   // chk: 1 entry row, 0 masked, else window position + 2
   // source row of this lane for the tile at t0 (plus its window-slot position load and the
   // facts its validity is decided from)
@@ -249,8 +268,8 @@ void k_attend_hs(AttendArgs a) {
     const int s = (SPARSE || PAGED) ? s_in : r;
     const bool ok_a = in && ent && s >= 0 && (PAGED || s < a.cap);
     const int slot = (ent ? 0 : w0 + (r - nsel)) % a.win_cap;
-    const uint8_t* src = ent ? kvseq + (size_t)(ok_a ? s : 0) * AROWB
-                             : (in ? winseq + (size_t)slot * AROWB : kvseq);
+    const uint8_t* src = ent ? kvseq + (size_t)(ok_a ? s : 0) * ROWB
+                             : (in ? winseq + (size_t)slot * ROWB : kvseq);
     wpv[b] = wpseq[slot];
     chk[b] = ent ? (ok_a ? 1 : 0) : (in ? w0 + (r - nsel) + 2 : 0);
     sv[b] = s;
@@ -262,7 +281,7 @@ void k_attend_hs(AttendArgs a) {
   auto gather = [&](int t0, int s_in, auto bconst) {
     const uint8_t* src = gather_src(t0, s_in, bconst);
 #pragma unroll
-    for (int i = 0; i < 9; ++i) gather_piece(src, i, bconst);
+    for (int i = 0; i < NPIECE; ++i) gather_piece(src, i, bconst);
   };
   gather(r_lo, s01[0], std::integral_constant<int, 0>{});
   if constexpr (HS_DEPTH > 1) gather(r_lo + HS_ROWS, s01[HS_DEPTH - 1], std::integral_constant<int, HS_DEPTH - 1>{});
@@ -295,13 +314,15 @@ void k_attend_hs(AttendArgs a) {
   lds_barrier();
 
   // ---- bf16 B operands of Q.K, with RoPE at tau on dims 448..511 (steps 14 and 15)
-  bf16x8 Qop[16];
+  bf16x8 Qop[NKS];
   {
     const uint8_t* qs = Ks + col * HS_PITCH;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qs + 2 * hs_dim(ks, g));
-      Qop[ks] = __builtin_bit_cast(bf16x8, ks < 14 ? v : rope_q8(v, hs_dim(ks, g), rope_cs));
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int d0 = hs_dim<FMT>(ks, g);
+      const uint4 v = *reinterpret_cast<const uint4*>(qs + 2 * d0);
+      const bool rope = FMT == 0 ? ks >= 14 : ks < 2;
+      Qop[ks] = __builtin_bit_cast(bf16x8, rope ? rope_q8(v, d0, rope_cs) : v);
     }
   }
   lds_barrier();   // the tile buffer is rewritten next
@@ -327,6 +348,45 @@ void k_attend_hs(AttendArgs a) {
     uint8_t* const Kb = Ks;
     uint16_t* const Pb = PsT;
     uint8_t* wrow = Kb + hs_sigma(myrow) * HS_PITCH;
+    if constexpr (FMT == 1) {
+      // the row's scale codes, from its lane group 2 (piece 5): code piece i of lane group g
+      // takes byte g of dword i - 2
+      typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+      const int sl = ((lane & 15) + 32) << 2;
+      const uint32_t scw[4] = {(uint32_t)__builtin_amdgcn_ds_bpermute(sl, (int)pre[b][5].x),
+                               (uint32_t)__builtin_amdgcn_ds_bpermute(sl, (int)pre[b][5].y),
+                               (uint32_t)__builtin_amdgcn_ds_bpermute(sl, (int)pre[b][5].z),
+                               (uint32_t)__builtin_amdgcn_ds_bpermute(sl, (int)pre[b][5].w)};
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        uint4 v = pre[b][i];
+        if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
+        if (i < 2) {
+          *reinterpret_cast<uint4*>(wrow + 16 * (56 + 4 * i + g)) = v;
+          Sp[i & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), Qop[i], Sp[i & 3], 0, 0, 0);
+        } else {
+          const bool has = i < 5 || g < 2;   // piece 5: codes in lane groups 0, 1 only
+          if (!has) v = make_uint4(0u, 0u, 0u, 0u);
+          int code = (scw[i - 2] >> (8 * g)) & 0xff;
+          if (!ok || !has) code = 127;       // masked rows: scale 1 on zero codes
+          const float scale = __int_as_float(code ? code << 23 : 0x00400000);   // 2^(code - 127)
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+          const int blk = 4 * (i - 2) + g;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 0);
+            const bf2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 1);
+            const bf2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 2);
+            const bf2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 3);
+            const uint4 cw = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                                        __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+            if (has) *reinterpret_cast<uint4*>(wrow + 64 * blk + 16 * j) = cw;
+            const int ks = 2 + 4 * (i - 2) + j;
+            Sp[ks & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cw), Qop[ks], Sp[ks & 3], 0, 0, 0);
+          }
+        }
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < 9; ++i) {
       uint4 v = pre[b][i];
@@ -347,6 +407,7 @@ void k_attend_hs(AttendArgs a) {
         *reinterpret_cast<uint4*>(wrow + 16 * (56 + 4 * (i - 7) + g)) = v;
         Sp[(7 + i) & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), Qop[7 + i], Sp[(7 + i) & 3], 0, 0, 0);
       }
+    }
     }
     f32x4 S = (Sp[0] + Sp[1]) + (Sp[2] + Sp[3]);
     // the tile after next goes into the registers just consumed; its nine loads are spread
@@ -401,7 +462,7 @@ void k_attend_hs(AttendArgs a) {
         const s16x4 hi = lds_read_tr16(va + HS_PITCH);
         const bf16x8 Av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Bp, O[dt], 0, 0, 0);
-        if (kc * 8 + dt < 9) gather_piece(nsrc, kc * 8 + dt, bconst);
+        if (kc * 8 + dt < NPIECE) gather_piece(nsrc, kc * 8 + dt, bconst);
       }
     }
     lds_barrier();   // the next tile rewrites the row and probability buffers
@@ -683,13 +744,20 @@ hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
   const size_t po = ((size_t)Q * d.n_h * p.splits * AC * sizeof(uint16_t) + 255) / 256 * 256;
   a.part_ml = p.splits > 1 ? (float*)((char*)ws + po) : nullptr;
   const dim3 grid(Q * (d.n_h / 16) * p.splits);
-  if (a.rm.bt) {
-    if (idx) hipLaunchKernelGGL((k_attend_hs<true, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attend_hs<false, true>), grid, dim3(256), 0, s, a);
-  } else {
-    if (idx) hipLaunchKernelGGL((k_attend_hs<true, false>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attend_hs<false, false>), grid, dim3(256), 0, s, a);
+#define ATT_LAUNCH(F)                                                                         \
+  if (a.rm.bt) {                                                                              \
+    if (idx) hipLaunchKernelGGL((k_attend_hs<true, true, F>), grid, dim3(256), 0, s, a);      \
+    else hipLaunchKernelGGL((k_attend_hs<false, true, F>), grid, dim3(256), 0, s, a);         \
+  } else {                                                                                    \
+    if (idx) hipLaunchKernelGGL((k_attend_hs<true, false, F>), grid, dim3(256), 0, s, a);     \
+    else hipLaunchKernelGGL((k_attend_hs<false, false, F>), grid, dim3(256), 0, s, a);        \
   }
+  if (d.kv_fmt == CSA_FMT_MXFP4_BF16) {
+    ATT_LAUNCH(1)
+  } else {
+    ATT_LAUNCH(0)
+  }
+#undef ATT_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   hipLaunchKernelGGL(k_attend_combine, dim3(Q * d.n_h), dim3(256), 0, s, a);

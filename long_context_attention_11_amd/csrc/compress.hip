@@ -148,7 +148,8 @@ __global__ __launch_bounds__(64) void k_project_step(ProjectStepArgs a, int unit
 template <bool PART>
 __global__ __launch_bounds__(256) void k_fold(FoldArgs a) {
   __shared__ float red[4];
-  fold_block<4, PART>(a, blockIdx.x, blockIdx.y, red);
+  __shared__ float ybuf[512], kbuf[512];   // CSA2's index keys (c, c_I <= 512)
+  fold_block<4, PART>(a, blockIdx.x, blockIdx.y, red, ybuf, kbuf);
 }
 
 // Keep the projections of the last S tokens of each sequence: slot j % S.
@@ -202,7 +203,13 @@ hipError_t launch_query_meta(int32_t B, int32_t T, const int32_t* pos0, int32_t*
 int32_t state_width(const csa_dims& d) { return d.dual ? 4 * d.c + 4 * d.c_I : 2 * d.c; }
 int32_t state_rows(const csa_dims& d) { return d.dual ? 2 * d.m : d.m; }
 size_t row_bytes(const csa_dims& d) {
-  return d.kv_fmt == CSA_FMT_F32 ? (size_t)4 * d.c : (size_t)(d.c - d.rope_dim) + 2 * (size_t)d.rope_dim;
+  if (d.kv_fmt == CSA_FMT_F32) return (size_t)4 * d.c;
+  if (d.kv_fmt == CSA_FMT_MXFP4_BF16) {
+    // bf16 RoPE dims, E2M1 codes and E8M0 scales, padded to whole 128-byte lines
+    const size_t n = 2 * (size_t)d.rope_dim + (size_t)(d.c - d.rope_dim) / 2 + (size_t)(d.c - d.rope_dim) / 32;
+    return (n + 127) / 128 * 128;
+  }
+  return (size_t)(d.c - d.rope_dim) + 2 * (size_t)d.rope_dim;
 }
 
 int32_t project_ksplit(const csa_dims& d, int32_t M) {
@@ -283,10 +290,13 @@ FoldArgs fold_args(const csa_dims& d, const csa_weights& w, const csa_cache& c, 
   a.dual = d.dual;
   a.c = d.c;
   a.r = d.rope_dim;
-  a.cI = d.dual ? d.c_I : 0;
+  a.cI = has_indexer(d) ? d.c_I : 0;
   a.pos0 = pos0;
   a.bias = w.bias;
   a.bias_idx = w.bias_idx;
+  a.keys_entry = keys_from_entry(d);
+  a.w_ik = a.keys_entry ? w.w_idx : nullptr;
+  a.act_f32 = d.act_fmt == CSA_FMT_F32;
   a.gamma = w.gamma_kv;
   a.eps = d.rms_eps;
   a.log2_base = std::log2((double)d.rope_base);

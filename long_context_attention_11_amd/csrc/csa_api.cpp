@@ -27,6 +27,17 @@ int fail(int code, const std::string& msg) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+int check_weights(const csa_dims& d, const csa_weights* w) {
+  if (!w || !w->w_kv) return fail(CSA_ERR_INVALID_ARGUMENT, "weights: w_kv is required");
+  if (d.dual && (!w->bias || !w->w_idx || !w->bias_idx))
+    return fail(CSA_ERR_INVALID_ARGUMENT, "CSA weights: bias, w_idx and bias_idx are required");
+  if (!d.dual && !has_indexer(d) && !w->bias)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "HCA weights: bias is required");
+  if (keys_from_entry(d) && !w->w_idx)
+    return fail(CSA_ERR_INVALID_ARGUMENT, "CSA2 weights: w_idx (the index-key projection) is required");
+  return CSA_OK;
+}
+
 // Checks the dims on their own.  Returns CSA_OK or an error (message set).
 int check_dims(const csa_dims* d) {
   if (!d) return fail(CSA_ERR_INVALID_ARGUMENT, "dims is NULL");
@@ -39,28 +50,29 @@ int check_dims(const csa_dims* d) {
   if (d->n_win < d->m)
     return fail(CSA_ERR_INVALID_ARGUMENT, "n_win must be >= m so the window covers the open block");
   if (d->dual != 0 && d->dual != 1) return fail(CSA_ERR_INVALID_ARGUMENT, "dual must be 0 or 1");
-  if (d->dual) {
-    if (d->c_I < 2 || (d->c_I & 1) || d->n_hI < 1)
-      return fail(CSA_ERR_INVALID_ARGUMENT, "CSA needs c_I >= 2 (even) and n_hI >= 1");
-    if (d->top_k < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "CSA needs top_k >= 1");
-  } else if (d->top_k != 0) {
-    return fail(CSA_ERR_INVALID_ARGUMENT, "HCA (dual = 0) is dense: top_k must be 0");
-  }
+  if (d->top_k < 0) return fail(CSA_ERR_INVALID_ARGUMENT, "top_k must be >= 0");
+  if (d->dual && d->top_k < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "CSA needs top_k >= 1");
+  const bool idx = has_indexer(*d);
+  if (idx && (d->c_I < 2 || (d->c_I & 1) || d->n_hI < 1))
+    return fail(CSA_ERR_INVALID_ARGUMENT, "an indexer needs c_I >= 2 (even) and n_hI >= 1");
+  if (keys_from_entry(*d) && d->c_I > 512)
+    return fail(CSA_ERR_UNSUPPORTED, "CSA2 index keys are built for c_I <= 512");
   if (!(d->rope_base > 0.f) || !(d->rms_eps >= 0.f))
     return fail(CSA_ERR_INVALID_ARGUMENT, "rope_base must be > 0 and rms_eps >= 0");
   if (d->c > 512) return fail(CSA_ERR_UNSUPPORTED, "c > 512 is not built");
   const bool f32 = d->act_fmt == CSA_FMT_F32 && d->kv_fmt == CSA_FMT_F32 &&
-                   (!d->dual || d->idx_fmt == CSA_FMT_F32);
-  const bool q = d->act_fmt == CSA_FMT_BF16 && d->kv_fmt == CSA_FMT_E4M3_BF16 &&
-                 (!d->dual || d->idx_fmt == CSA_FMT_E4M3 || d->idx_fmt == CSA_FMT_MXFP4);
+                   (!idx || d->idx_fmt == CSA_FMT_F32);
+  const bool q = d->act_fmt == CSA_FMT_BF16 &&
+                 (d->kv_fmt == CSA_FMT_E4M3_BF16 || d->kv_fmt == CSA_FMT_MXFP4_BF16) &&
+                 (!idx || d->idx_fmt == CSA_FMT_E4M3 || d->idx_fmt == CSA_FMT_MXFP4);
   if (!f32 && !q)
     return fail(CSA_ERR_UNSUPPORTED,
-                "supported formats: all F32, or act BF16 + kv E4M3_BF16 + idx E4M3 or MXFP4");
+                "supported formats: all F32, or act BF16 + kv E4M3_BF16 or MXFP4_BF16 + idx E4M3 or MXFP4");
   if (q) {
     if (d->c != 512 || d->rope_dim != 64)
-      return fail(CSA_ERR_UNSUPPORTED, "E4M3_BF16 rows are built for c = 512, rope_dim = 64");
+      return fail(CSA_ERR_UNSUPPORTED, "quantized KV rows are built for c = 512, rope_dim = 64");
     if (d->n_h % 16) return fail(CSA_ERR_UNSUPPORTED, "n_h must be a multiple of 16");
-    if (d->dual && (d->c_I != 128 || (d->n_hI != 16 && d->n_hI != 32 && d->n_hI != 64)))
+    if (idx && (d->c_I != 128 || (d->n_hI != 16 && d->n_hI != 32 && d->n_hI != 64)))
       return fail(CSA_ERR_UNSUPPORTED, "the quantized indexer is built for c_I = 128, n_hI in {16, 32, 64}");
     if (d->d % 64) return fail(CSA_ERR_UNSUPPORTED, "bf16 projection needs d % 64 == 0");
   }
@@ -74,7 +86,7 @@ int check_cache(const csa_dims* d, const csa_cache* c, bool need_state) {
   if (c->win_cap < d->n_win) return fail(CSA_ERR_INVALID_ARGUMENT, "win_cap must be >= n_win");
   if (!c->kv || !c->n_entries || !c->win || !c->win_pos)
     return fail(CSA_ERR_INVALID_ARGUMENT, "cache kv, n_entries, win and win_pos must be set");
-  if (d->dual && !c->ki) return fail(CSA_ERR_INVALID_ARGUMENT, "CSA cache needs ki");
+  if (has_indexer(*d) && !c->ki) return fail(CSA_ERR_INVALID_ARGUMENT, "a cache with an indexer needs ki");
   if (need_state && !c->state) return fail(CSA_ERR_INVALID_ARGUMENT, "cache state is NULL");
   const size_t rb = row_bytes(*d);
   if ((size_t)c->cap * rb > (size_t)1 << 40)
@@ -90,7 +102,7 @@ int check_cache(const csa_dims* d, const csa_cache* c, bool need_state) {
     if ((size_t)c->n_pages * (size_t)epp * rb > (size_t)1 << 40)
       return fail(CSA_ERR_INVALID_ARGUMENT, "page pool size overflows");
     // the quantized decode indexer scores 16-entry tiles that must not straddle a page
-    if (d->dual && d->idx_fmt != CSA_FMT_F32 && epp % 16)
+    if (has_indexer(*d) && d->idx_fmt != CSA_FMT_F32 && epp % 16)
       return fail(CSA_ERR_UNSUPPORTED, "a paged CSA cache with quantized keys needs page_tokens / m % 16 == 0");
   }
   return CSA_OK;
@@ -178,7 +190,7 @@ int csa_workspace_size(const csa_dims* dims, int32_t op, int32_t B, int32_t T, i
       *bytes = compress_ws(d, B, T);
       return CSA_OK;
     case CSA_OP_INDEX_TOPK:
-      if (!d.dual) return fail(CSA_ERR_INVALID_ARGUMENT, "HCA has no indexer");
+      if (!has_indexer(d)) return fail(CSA_ERR_INVALID_ARGUMENT, "HCA has no indexer");
       if (Q < 1 || cap < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "Q and cap must be positive");
       *bytes = index_ws(d, Q, cap);
       return CSA_OK;
@@ -192,12 +204,13 @@ int csa_workspace_size(const csa_dims* dims, int32_t op, int32_t B, int32_t T, i
       const int32_t Qc = (q_chunk > 0 && q_chunk < Qn) ? q_chunk : Qn;
       Layout L;
       L.add(0, 2 * sizeof(int32_t) * (size_t)Qn);                 // q_seq, q_pos
-      L.add(1, d.dual ? sizeof(int32_t) * (size_t)Qn * d.top_k : 0);  // idx
+      L.add(1, has_indexer(d) ? sizeof(int32_t) * (size_t)Qn * d.top_k : 0);  // idx
       size_t phase = compress_ws(d, B, T);
-      if (d.dual) phase = std::max(phase, index_ws(d, Qc, cap));
+      if (has_indexer(d)) phase = std::max(phase, index_ws(d, Qc, cap));
       if (d.dual && T == 1)
         phase = std::max(phase, align_up(index_ws_carry(d, Qn, cap), 256) + project_part_bytes(d, B));
-      phase = std::max(phase, attend_workspace_bytes(d, Qn, cap, d.dual ? 0 : 1));  // forward attends a CSA layer sparsely
+      // forward attends a layer with an indexer sparsely
+      phase = std::max(phase, attend_workspace_bytes(d, Qn, cap, has_indexer(d) ? 0 : 1));
       L.add(2, phase);
       *bytes = L.total;
       return CSA_OK;
@@ -215,8 +228,7 @@ int csa_compress(const csa_dims* dims, const csa_weights* w, const csa_cache* ca
   if (st) return st;
   const csa_dims& d = *dims;
   if ((st = check_cache(dims, cache, true))) return st;
-  if (!w || !w->w_kv || !w->bias || (d.dual && (!w->w_idx || !w->bias_idx)))
-    return fail(CSA_ERR_INVALID_ARGUMENT, "weights: w_kv and bias (and w_idx, bias_idx for CSA) are required");
+  if ((st = check_weights(d, w))) return st;
   if (!H || !pos0) return fail(CSA_ERR_INVALID_ARGUMENT, "H and pos0 must be set");
   if (T < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "T must be >= 1");
   const int32_t M = cache->B * T;
@@ -277,7 +289,7 @@ int csa_index_topk(const csa_dims* dims, const csa_cache* cache, const void* qI,
   int st = check_dims(dims);
   if (st) return st;
   const csa_dims& d = *dims;
-  if (!d.dual) return fail(CSA_ERR_INVALID_ARGUMENT, "HCA (dual = 0) has no indexer");
+  if (!has_indexer(d)) return fail(CSA_ERR_INVALID_ARGUMENT, "HCA (top_k = 0) has no indexer");
   if ((st = check_cache(dims, cache, false))) return st;
   if (!qI || !w || !q_seq || !q_pos || !idx_out)
     return fail(CSA_ERR_INVALID_ARGUMENT, "qI, w, q_seq, q_pos and idx_out must be set");
@@ -295,7 +307,7 @@ int csa_index_scores(const csa_dims* dims, const csa_cache* cache, const void* q
   g_last_error.clear();
   int st = check_dims(dims);
   if (st) return st;
-  if (!dims->dual) return fail(CSA_ERR_INVALID_ARGUMENT, "HCA (dual = 0) has no indexer");
+  if (!has_indexer(*dims)) return fail(CSA_ERR_INVALID_ARGUMENT, "HCA (top_k = 0) has no indexer");
   if ((st = check_cache(dims, cache, false))) return st;
   if (!qI || !w || !q_seq || !q_pos || !scores)
     return fail(CSA_ERR_INVALID_ARGUMENT, "qI, w, q_seq, q_pos and scores must be set");
@@ -312,7 +324,7 @@ int csa_index_scores_grouped(const csa_dims* dims, const csa_cache* cache, const
   g_last_error.clear();
   int st = check_dims(dims);
   if (st) return st;
-  if (!dims->dual) return fail(CSA_ERR_INVALID_ARGUMENT, "HCA (dual = 0) has no indexer");
+  if (!has_indexer(*dims)) return fail(CSA_ERR_INVALID_ARGUMENT, "HCA (top_k = 0) has no indexer");
   if ((st = check_cache(dims, cache, false))) return st;
   if (!qI || !w || !q_seq || !q_pos || !scores)
     return fail(CSA_ERR_INVALID_ARGUMENT, "qI, w, q_seq, q_pos and scores must be set");
@@ -334,7 +346,7 @@ int csa_topk(const csa_dims* dims, const csa_cache* cache, const int32_t* q_seq,
   g_last_error.clear();
   int st = check_dims(dims);
   if (st) return st;
-  if (!dims->dual) return fail(CSA_ERR_INVALID_ARGUMENT, "HCA (dual = 0) has no top-k");
+  if (!has_indexer(*dims)) return fail(CSA_ERR_INVALID_ARGUMENT, "HCA (top_k = 0) has no top-k");
   if ((st = check_cache(dims, cache, false))) return st;
   if (!q_seq || !q_pos || !scores || !idx_out)
     return fail(CSA_ERR_INVALID_ARGUMENT, "q_seq, q_pos, scores and idx_out must be set");
@@ -390,22 +402,22 @@ static int forward_checks(const csa_dims* dims, const csa_weights* w, const csa_
   if (st) return st;
   const csa_dims& d = *dims;
   if ((st = check_cache(dims, cache, true))) return st;
-  if (!w || !w->w_kv || !w->bias || (d.dual && (!w->w_idx || !w->bias_idx)))
-    return fail(CSA_ERR_INVALID_ARGUMENT, "weights: w_kv and bias (and w_idx, bias_idx for CSA) are required");
+  if ((st = check_weights(d, w))) return st;
   if (!H || !pos0 || !q || !out) return fail(CSA_ERR_INVALID_ARGUMENT, "H, pos0, q and out must be set");
-  if (d.dual && (!qI || !wI)) return fail(CSA_ERR_INVALID_ARGUMENT, "CSA forward needs qI and wI");
+  if (has_indexer(d) && (!qI || !wI)) return fail(CSA_ERR_INVALID_ARGUMENT, "a forward with an indexer needs qI and wI");
   if (T < 1) return fail(CSA_ERR_INVALID_ARGUMENT, "T must be >= 1");
   if (cache->win_cap < T + d.n_win - 1)
     return fail(CSA_ERR_INVALID_ARGUMENT, "win_cap must be >= T + n_win - 1 for the chunk's queries");
-  if (d.dual && cache->cap > topk_max_visible(d))
+  if (has_indexer(d) && cache->cap > topk_max_visible(d))
     return fail(CSA_ERR_UNSUPPORTED, "cap exceeds the entries the top-k kernels handle for this top_k");
-  if ((st = attend_checks(d, *cache, d.dual != 0))) return st;
+  if ((st = attend_checks(d, *cache, has_indexer(d)))) return st;
   const int32_t Qn = cache->B * T;
   Layout L;
   L.add(0, 2 * sizeof(int32_t) * (size_t)Qn);
-  L.add(1, (d.dual && !idx_out) ? sizeof(int32_t) * (size_t)Qn * d.top_k : 0);
-  size_t min_phase = std::max(compress_ws(d, cache->B, T), attend_workspace_bytes(d, Qn, cache->cap, d.dual ? 0 : 1));
-  if (d.dual) min_phase = std::max(min_phase, index_ws(d, 1, cache->cap));
+  L.add(1, (has_indexer(d) && !idx_out) ? sizeof(int32_t) * (size_t)Qn * d.top_k : 0);
+  size_t min_phase = std::max(compress_ws(d, cache->B, T),
+                              attend_workspace_bytes(d, Qn, cache->cap, has_indexer(d) ? 0 : 1));
+  if (has_indexer(d)) min_phase = std::max(min_phase, index_ws(d, 1, cache->cap));
   *min_ws = L.total + min_phase;
   return CSA_OK;
 }
@@ -425,7 +437,7 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
   // fixed part of the workspace, then the largest query chunk the rest allows
   Layout L;
   L.add(0, 2 * sizeof(int32_t) * (size_t)Qn);
-  L.add(1, (d.dual && !idx_out) ? sizeof(int32_t) * (size_t)Qn * d.top_k : 0);
+  L.add(1, (has_indexer(d) && !idx_out) ? sizeof(int32_t) * (size_t)Qn * d.top_k : 0);
   const size_t fixed = L.total;
   int32_t* q_seq = (int32_t*)((char*)ws + L.off[0]);
   int32_t* q_pos = q_seq + Qn;
@@ -465,7 +477,7 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
   if (st) return st;
   // largest query chunk whose scores and candidates fit
   int32_t Qc = Qn;
-  if (d.dual) {
+  if (has_indexer(d)) {
     while (Qc > 1 && index_ws(d, Qc, cache->cap) > phase_bytes) Qc = (Qc + 1) / 2;
     // Query q is token q % T of sequence q / T.  With T and the chunk a multiple of 16, every
     // aligned group of 16 queries of a chunk is one sequence and the indexer can tile them.
@@ -480,7 +492,7 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
     e = launch_query_meta(cache->B, T, pos0, q_seq, q_pos, stream);
     if (e != hipSuccess) return hip_fail(e, "query metadata launch");
   }
-  if (d.dual) {
+  if (has_indexer(d)) {
     const bool tiled = T % 16 == 0 && Qc % 16 == 0;
     const size_t qI_row = d.idx_fmt == CSA_FMT_MXFP4 ? (size_t)d.n_hI * (d.c_I / 2 + d.c_I / 32)
                                                       : (size_t)d.n_hI * d.c_I * (d.idx_fmt == CSA_FMT_F32 ? 4 : 1);
@@ -493,7 +505,7 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
       if (st) return st;
     }
   }
-  e = launch_attend(d, *cache, q, gamma_q, sink, qs_, qp_, Qn, d.dual ? idx : nullptr, out,
+  e = launch_attend(d, *cache, q, gamma_q, sink, qs_, qp_, Qn, has_indexer(d) ? idx : nullptr, out,
                     phase_ws, stream);
   if (e != hipSuccess) return hip_fail(e, "attend launch");
   return CSA_OK;
@@ -589,7 +601,7 @@ int csa_query_project(const csa_dims* dims, const csa_proj_weights* pw, const vo
   if (st) return st;
   if (!h || !q || !pw->w_dq || !pw->w_uq)
     return fail(CSA_ERR_INVALID_ARGUMENT, "h, q, w_dq and w_uq must be set");
-  if (dims->dual && (!qI || !w || !pw->w_iuq || !pw->w_w))
+  if (has_indexer(*dims) && (!qI || !w || !pw->w_iuq || !pw->w_w))
     return fail(CSA_ERR_INVALID_ARGUMENT, "CSA needs qI, w, w_iuq and w_w");
   const size_t need = csa::query_project_ws_bytes(*dims, pw->d_c, T);
   if (!ws || ws_bytes < need)

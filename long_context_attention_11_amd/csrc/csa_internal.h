@@ -288,6 +288,11 @@ hipError_t launch_reduce_partials(const float* P, int32_t ksplit, int64_t n, flo
 hipError_t launch_query_meta(int32_t B, int32_t T, const int32_t* pos0, int32_t* q_seq,
                              int32_t* q_pos, hipStream_t s);
 
+// Layer kinds: CSA (dual), HCA (single path, dense) and CSA2 (single path with an indexer
+// whose keys are projected from the main entry).
+inline bool has_indexer(const csa_dims& d) { return d.top_k > 0; }
+inline bool keys_from_entry(const csa_dims& d) { return !d.dual && d.top_k > 0; }
+
 // The row map of a cache (host).
 inline RowMap row_map(const csa_dims& d, const csa_cache& c) {
   RowMap rm;

@@ -3,7 +3,8 @@
 //
 // Sources: reading notes "DeepSeekV4技术报告阅读笔记" (zouxinn.github.io) §2.3.1 eqs. 11-12 (CSA
 // fold), §2.4.1 eqs. 22-23 (HCA fold), §2.5.1-2.5.2 (RMSNorm, partial RoPE); PaperTrace "02 ·
-// DeepSeek-V4: 压缩注意力撑起 1M 上下文" §2.5 (RoPE dims in BF16, the rest FP8).
+// DeepSeek-V4: 压缩注意力撑起 1M 上下文" §2.5 (RoPE dims in BF16, the rest FP8) and §6.4
+// (CSA2: single-path fold without bias, index keys from the entry, FP4 main KV).
 #pragma once
 
 #include "csa_internal.h"
@@ -20,8 +21,11 @@ struct FoldArgs {
   int S, NP;
   int T, m, dual, c, r, cI;
   const int32_t* pos0;
-  const float* bias;     // CSA [2][m][c], HCA [m][c]
+  const float* bias;     // CSA [2][m][c], HCA [m][c], CSA2 null (no bias)
   const float* bias_idx; // CSA [2][m][cI]
+  const void* w_ik;      // CSA2: [cI][c] projection of the normalised entry onto its key
+  int act_f32;           // w_ik in float32 (else bfloat16)
+  int keys_entry;        // CSA2: the index key is projected from the entry
   const float* gamma;    // [c] or null
   float eps;
   double log2_base;
@@ -68,20 +72,21 @@ __device__ __forceinline__ float fold_column(const FoldArgs& a, int b, int p0, i
   const int m = a.m;
   const int ja = m * i, jb = m * (i - 1);
   const bool has_b = a.dual && i > 0;
+  auto bias = [&](const float* B, int r) { return B ? B[r * bstride_col + u] : 0.f; };
   float mx = -INFINITY;
-  for (int r = 0; r < m; ++r) mx = fmaxf(mx, proj<PART>(a, b, p0, ja + r, colZa) + Ba[r * bstride_col + u]);
+  for (int r = 0; r < m; ++r) mx = fmaxf(mx, proj<PART>(a, b, p0, ja + r, colZa) + bias(Ba, r));
   if (has_b)
     for (int r = 0; r < m; ++r)
-      mx = fmaxf(mx, proj<PART>(a, b, p0, jb + r, colZa + boff) + Bb[r * bstride_col + u]);
+      mx = fmaxf(mx, proj<PART>(a, b, p0, jb + r, colZa + boff) + bias(Bb, r));
   float den = 0.f, num = 0.f;
   for (int r = 0; r < m; ++r) {
-    float e = expf(proj<PART>(a, b, p0, ja + r, colZa) + Ba[r * bstride_col + u] - mx);
+    float e = expf(proj<PART>(a, b, p0, ja + r, colZa) + bias(Ba, r) - mx);
     den += e;
     num = fmaf(e, proj<PART>(a, b, p0, ja + r, colCa), num);
   }
   if (has_b)
     for (int r = 0; r < m; ++r) {
-      float e = expf(proj<PART>(a, b, p0, jb + r, colZa + boff) + Bb[r * bstride_col + u] - mx);
+      float e = expf(proj<PART>(a, b, p0, jb + r, colZa + boff) + bias(Bb, r) - mx);
       den += e;
       num = fmaf(e, proj<PART>(a, b, p0, jb + r, colCa + boff), num);
     }
@@ -104,11 +109,33 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
+// MXFP4 encoding of a 32-dim block held by the 16 threads of one DPP row, two dims each:
+// the row's largest magnitude sets the scale exponent e (the MX rule: floor(log2 max) - 2,
+// 0 for an all-zero block), and each thread's two dims become one byte (first dim in the
+// low nibble).  Returns the byte; *e_out the exponent (scale code e + 127).
+__device__ __forceinline__ uint8_t mx_encode_pair(float v0, float v1, int* e_out) {
+  const float amax = __int_as_float(row_allreduce(__float_as_int(fmaxf(fabsf(v0), fabsf(v1))), MaxBits()));
+  int e = 0;
+  if (amax > 0.f) {
+    int ex;
+    frexpf(amax, &ex);   // amax = f 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
+    e = min(127, max(-127, ex - 1 - 2));
+  }
+  *e_out = e;
+  return (uint8_t)(e2m1_code(ldexpf(v0, -e)) | (e2m1_code(ldexpf(v1, -e)) << 4));
+}
+
+// Byte offsets inside an MXFP4_BF16 row (c = 512, r = 64): RoPE dims first, then the codes
+// of dims 0 .. c - r - 1, then one scale code per 32 of them, zero padding to MXR_BYTES.
+constexpr int MXR_CODES = 128, MXR_SCALES = 352, MXR_PAD = 366, MXR_BYTES = 384;
+
 // RMSNorm over c columns (each thread holds columns 2t, 2t+1), RoPE at pos on the last r
-// columns, then store the row in its format.  Threads with 2t >= c hold zeros.
+// columns, then store the row in its format.  Threads with 2t >= c hold zeros.  With ybuf
+// set, the normalised row before RoPE is also left there (ybuf[u], c floats of LDS; the
+// caller synchronises before reading it).
 template <int NW>
 __device__ __forceinline__ void finalize_store(const FoldArgs& a, float x0, float x1, int64_t pos,
-                                               uint8_t* dst, float* red) {
+                                               uint8_t* dst, float* red, float* ybuf = nullptr) {
   const int t = threadIdx.x, u = 2 * t;
   const bool act = u < a.c;
   float ss = block_sum<NW>(act ? x0 * x0 + x1 * x1 : 0.f, red);
@@ -116,6 +143,10 @@ __device__ __forceinline__ void finalize_store(const FoldArgs& a, float x0, floa
   if (!act) return;
   float g0 = a.gamma ? a.gamma[u] : 1.f, g1 = a.gamma ? a.gamma[u + 1] : 1.f;
   float y0 = g0 * (x0 * inv), y1 = g1 * (x1 * inv);
+  if (ybuf) {
+    ybuf[u] = y0;
+    ybuf[u + 1] = y1;
+  }
   const int rs = a.c - a.r;
   if (u >= rs) {
     float cs, sn;
@@ -127,6 +158,20 @@ __device__ __forceinline__ void finalize_store(const FoldArgs& a, float x0, floa
   if (a.kv_fmt == CSA_FMT_F32) {
     float2 v = make_float2(y0, y1);
     *reinterpret_cast<float2*>(dst + 4 * u) = v;
+  } else if (a.kv_fmt == CSA_FMT_MXFP4_BF16) {
+    if (u < rs) {
+      // dims 32k .. 32k + 31 are the 16 threads of DPP row k (rs is a multiple of 32)
+      int e;
+      dst[MXR_CODES + t] = mx_encode_pair(y0, y1, &e);
+      if ((t & 15) == 0) dst[MXR_SCALES + (t >> 4)] = (uint8_t)(e + 127);
+      if (t == 0) {
+        *reinterpret_cast<uint16_t*>(dst + MXR_PAD) = 0;
+        *reinterpret_cast<uint4*>(dst + MXR_PAD + 2) = make_uint4(0u, 0u, 0u, 0u);
+      }
+    } else {
+      const uint32_t bits = f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16);
+      *reinterpret_cast<uint32_t*>(dst + 2 * (u - rs)) = bits;
+    }
   } else if (u < rs) {
     uint32_t code = f32_to_e4m3(y0) | (f32_to_e4m3(y1) << 8);
     *reinterpret_cast<uint16_t*>(dst + u) = (uint16_t)code;
@@ -136,12 +181,62 @@ __device__ __forceinline__ void finalize_store(const FoldArgs& a, float x0, floa
   }
 }
 
+// Keys 2t and 2t + 1 of entry i of sequence b, stored in the index format (thread t, 2t < cI).
+__device__ __forceinline__ void store_key_pair(const FoldArgs& a, int b, int i, float k0, float k1) {
+  const int t = threadIdx.x, u = 2 * t;
+  if (a.idx_fmt == CSA_FMT_F32) {
+    float* kd = reinterpret_cast<float*>(a.ki) + row_of(a.rm, b, i) * a.cI;
+    kd[u] = k0;
+    kd[u + 1] = k1;
+  } else if (a.idx_fmt == CSA_FMT_MXFP4) {
+    // a block of 32 dims is the 16 threads of one DPP row
+    int e;
+    const uint8_t byte = mx_encode_pair(k0, k1, &e);
+    int64_t oc, os;
+    mx_offsets(a.rm, b, i, a.cI / 2, a.cI / 32, oc, os);
+    a.ki[oc + t] = byte;
+    if ((t & 15) == 0) a.ki[os + (t >> 4)] = (uint8_t)(e + 127);
+  } else {
+    uint8_t* kd = a.ki + row_of(a.rm, b, i) * a.cI;
+    *reinterpret_cast<uint16_t*>(kd + u) = (uint16_t)(f32_to_e4m3(k0) | (f32_to_e4m3(k1) << 8));
+  }
+}
+
+// CSA2's index key of entry i: K^I = y . W^IK over the normalised entry y (ybuf, before RoPE),
+// float32 sums over the c dims in order, two threads per key (halves of the dims, added
+// together), then stored in the index format.  kbuf: LDS [cI].  Every thread of the block
+// calls it (it synchronises).
+template <int NW>
+__device__ __forceinline__ void entry_key(const FoldArgs& a, int b, int i, const float* ybuf, float* kbuf) {
+  const int t = threadIdx.x;
+  __syncthreads();   // ybuf complete
+  const int half = a.c / 2;
+  for (int o2 = t; o2 < 2 * a.cI; o2 += 64 * NW) {
+    const int o = o2 >> 1, h = o2 & 1;
+    float acc = 0.f;
+    if (a.act_f32) {
+      const float* wr = static_cast<const float*>(a.w_ik) + (size_t)o * a.c + h * half;
+      for (int v = 0; v < half; ++v) acc = fmaf(ybuf[h * half + v], wr[v], acc);
+    } else {
+      const uint16_t* wr = static_cast<const uint16_t*>(a.w_ik) + (size_t)o * a.c + h * half;
+      for (int v = 0; v < half; ++v) acc = fmaf(ybuf[h * half + v], bf16_bits_to_f32(wr[v]), acc);
+    }
+    // pairs (2o, 2o + 1) are adjacent lanes of one wave
+    const float other = __shfl_xor(acc, 1);
+    if (h == 0) kbuf[o] = acc + other;
+  }
+  __syncthreads();
+  if (2 * t < a.cI) store_key_pair(a, b, i, kbuf[2 * t], kbuf[2 * t + 1]);
+}
+
 // Block (slot, b) of the fold: slot < T the raw window row of token pos0[b] + slot, otherwise
 // the entry slot - T past pos0[b] / m (when its block completes in this chunk).  Threads hold
 // columns 2t, 2t + 1; a block of NW waves (NW >= 4; those past the c columns hold zeros).
-// red: LDS [NW].
+// red: LDS [NW]; ybuf, kbuf: LDS [c] and [cI] for CSA2's index keys (null where the fold
+// never serves a CSA2 layer).
 template <int NW, bool PART>
-__device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, float* red) {
+__device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, float* red,
+                                           float* ybuf = nullptr, float* kbuf = nullptr) {
   const int t = threadIdx.x;
   const int p0 = a.pos0[b];
   const int u = 2 * t;
@@ -183,36 +278,20 @@ __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, f
     }
   }
   uint8_t* dst = a.kv + row_of(a.rm, b, i) * a.rowB;
-  finalize_store<NW>(a, x0, x1, (int64_t)a.m * i, dst, red);
-  // indexer key: same fold with its own columns and biases; stored as folded
+  const bool ek = a.keys_entry && ybuf;
+  finalize_store<NW>(a, x0, x1, (int64_t)a.m * i, dst, red, ek ? ybuf : nullptr);
+  if (ek) {
+    entry_key<NW>(a, b, i, ybuf, kbuf);
+    return;
+  }
+  // CSA indexer key: same fold with its own columns and biases; stored as folded
   if (a.dual && u < a.cI) {
     const int base = 4 * a.c;
     const float* BIa = a.bias_idx;
     const float* BIb = a.bias_idx + a.m * a.cI;
     float k0 = fold_column<PART>(a, b, p0, i, base + u, base + 2 * a.cI + u, a.cI, BIa, BIb, a.cI, u);
     float k1 = fold_column<PART>(a, b, p0, i, base + u + 1, base + 2 * a.cI + u + 1, a.cI, BIa, BIb, a.cI, u + 1);
-    if (a.idx_fmt == CSA_FMT_F32) {
-      float* kd = reinterpret_cast<float*>(a.ki) + row_of(a.rm, b, i) * a.cI;
-      kd[u] = k0;
-      kd[u + 1] = k1;
-    } else if (a.idx_fmt == CSA_FMT_MXFP4) {
-      // a block of 32 dims is the 16 threads of one DPP row: its largest magnitude sets the
-      // scale, then each thread encodes its two elements into one byte
-      const float amax = __int_as_float(row_allreduce(__float_as_int(fmaxf(fabsf(k0), fabsf(k1))), MaxBits()));
-      int e = 0;
-      if (amax > 0.f) {
-        int ex;
-        frexpf(amax, &ex);   // amax = f 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
-        e = min(127, max(-127, ex - 1 - 2));
-      }
-      int64_t oc, os;
-      mx_offsets(a.rm, b, i, a.cI / 2, a.cI / 32, oc, os);
-      a.ki[oc + t] = (uint8_t)(e2m1_code(ldexpf(k0, -e)) | (e2m1_code(ldexpf(k1, -e)) << 4));
-      if ((t & 15) == 0) a.ki[os + (t >> 4)] = (uint8_t)(e + 127);
-    } else {
-      uint8_t* kd = a.ki + row_of(a.rm, b, i) * a.cI;
-      *reinterpret_cast<uint16_t*>(kd + u) = (uint16_t)(f32_to_e4m3(k0) | (f32_to_e4m3(k1) << 8));
-    }
+    store_key_pair(a, b, i, k0, k1);
   }
 }
 

@@ -16,6 +16,9 @@ Workload shapes follow the five layer configurations the attention path is measu
   c4b  the same after a 262144-token prefix
   c2fp4, c4afp4, c4bfp4  c2, c4a and c4b with the indexer's keys and queries in MXFP4
   c5   HCA decode: 8 x 1048576 tokens, m'=128 (8192 entries), dense, 64 heads
+  c6   CSA2 (the V4.1-Flash layer): c2's shape with the single-path fold (m=4, no bias),
+       index keys projected from the entry and MXFP4 main KV rows; c6fp4 with MXFP4 indexer
+       keys and queries; c1v2 the same layer kind at c1's tiny fp32 shape
 Value distributions: hidden states N(0,1); projection weights N(0, 1/fan_in); positional
 biases and sink logits N(0, 0.1) (second argument read as the variance); queries, indexer
 queries and indexer head weights N(0,1).  Synthetic cache rows (used where a decode stage is
@@ -69,6 +72,16 @@ CONFIGS = {
     "c5": dict(name="c5", B=8, prefix=1048576, T=1, d=4096, c=512, rope_dim=64, n_h=64, c_I=0,
                n_hI=0, m=128, dual=False, top_k=0, n_win=128, kv_fmt="q", idx_fmt="e4m3",
                act="bf16", sink=True, **_BASE, **_FLASH_PROJ),
+    # CSA2 (PaperTrace §6.4, V4.1-Flash paragraph) at the Flash decode shape
+    "c6": dict(name="c6", B=16, prefix=131072, T=1, d=4096, c=512, rope_dim=64, n_h=64, c_I=128,
+               n_hI=64, m=4, dual=False, top_k=512, n_win=128, kv_fmt="q4", idx_fmt="e4m3",
+               act="bf16", sink=True, **_BASE, **_FLASH_PROJ),
+    "c6fp4": dict(name="c6fp4", B=16, prefix=131072, T=1, d=4096, c=512, rope_dim=64, n_h=64, c_I=128,
+                  n_hI=64, m=4, dual=False, top_k=512, n_win=128, kv_fmt="q4", idx_fmt="mxfp4",
+                  act="bf16", sink=True, **_BASE, **_FLASH_PROJ),
+    "c1v2": dict(name="c1v2", B=1, prefix=0, T=256, d=256, c=64, rope_dim=16, n_h=4, c_I=16, n_hI=2,
+                 m=4, dual=False, top_k=8, n_win=16, kv_fmt="f32", idx_fmt="f32", act="f32",
+                 sink=True, **_BASE),
 }
 
 
@@ -80,10 +93,14 @@ def config(name: str, **over) -> dict:
 
 
 def row_bytes(cfg: dict) -> int:
-    """Bytes of one stored KV row: 4c for fp32, (c - r) E4M3 + r bf16 otherwise."""
+    """Bytes of one stored KV row: 4c for fp32, (c - r) E4M3 + r bf16 for "q", and for "q4"
+    r bf16 + (c - r) / 2 element bytes + (c - r) / 32 scale codes padded to 128 bytes."""
+    c, r = cfg["c"], cfg["rope_dim"]
     if cfg["kv_fmt"] == "f32":
-        return 4 * cfg["c"]
-    return cfg["c"] - cfg["rope_dim"] + 2 * cfg["rope_dim"]
+        return 4 * c
+    if cfg["kv_fmt"] == "q4":
+        return -(-(2 * r + (c - r) // 2 + (c - r) // 32) // 128) * 128
+    return c - r + 2 * r
 
 
 def _seed_of(*ids) -> int:
@@ -103,16 +120,24 @@ def randn(shape, std, device, *ids) -> torch.Tensor:
     return torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
 
 
-def mxfp4_random(rows: int, n: int, device, *ids, lo: int = 100, hi: int = 140):
+def mxfp4_random(rows: int, n: int, device, *ids, lo: int = 100, hi: int = 140, mag_max: int = 7):
     """Random MXFP4 rows (n elements each): uniformly drawn element bytes [rows][n / 2] (two
     E2M1 codes each) and block scale codes [rows][n / 32] uniform in lo .. hi (by default
     2^-27 .. 2^13, so the blocks of one row often lie many octaves apart).  One block in 16
     is all zeros with scale code 127 (what an all-zero block gets), and in one row in 8 the
     last block's code is pulled 12 octaves below the row's first (clamped at lo).  Drawn
-    directly as codes, so both sides decode the same bytes and no encoding is involved."""
+    directly as codes, so both sides decode the same bytes and no encoding is involved.
+    ``mag_max`` < 7 caps each element's magnitude code (E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4,
+    6 have codes 0 .. 7), keeping the sign uniform."""
     g = generator(device, *ids)
     nb = n // 32
-    codes = torch.randint(0, 256, (rows, n // 2), generator=g, device=device, dtype=torch.int32)
+    if mag_max >= 7:
+        codes = torch.randint(0, 256, (rows, n // 2), generator=g, device=device, dtype=torch.int32)
+    else:
+        mag = torch.randint(0, mag_max + 1, (rows, n), generator=g, device=device, dtype=torch.int32)
+        sign = torch.randint(0, 2, (rows, n), generator=g, device=device, dtype=torch.int32)
+        nib = (sign << 3) | mag
+        codes = nib[:, 0::2] | (nib[:, 1::2] << 4)
     scales = torch.randint(lo, hi + 1, (rows, nb), generator=g, device=device, dtype=torch.int32)
     zero = torch.rand((rows, nb), generator=g, device=device) < 1.0 / 16
     far = torch.rand((rows,), generator=g, device=device) < 1.0 / 8
@@ -136,7 +161,8 @@ def weights(cfg: dict, seed: int = SEED, device="cpu") -> dict:
     """Projection weights (rows = output features, [width][d]), biases, gamma and sink.
 
     CSA: kv_a kv_b z_a z_b [c][d]; ki_a ki_b zi_a zi_b [c_I][d]; B_a B_b [m][c];
-         BI_a BI_b [m][c_I].  HCA: kv z [c][d]; B [m][c].
+         BI_a BI_b [m][c_I].  HCA: kv z [c][d]; B [m][c].  CSA2: kv z [c][d]; B None (no
+         bias); w_ik [c_I][c] (N(0, 1/c)), the projection of the normalised entry.
     Weights are stored in the activation type (fp32 or bf16); biases, gamma (ones) and the
     sink are fp32.
     """
@@ -155,6 +181,9 @@ def weights(cfg: dict, seed: int = SEED, device="cpu") -> dict:
         W["B_b"] = randn((m, c), std_b, device, seed, "b", "b")
         W["BI_a"] = randn((m, cI), std_b, device, seed, "b", "ia")
         W["BI_b"] = randn((m, cI), std_b, device, seed, "b", "ib")
+    elif cfg["top_k"] > 0:
+        W["B"] = None
+        W["w_ik"] = _store(randn((cI, c), 1.0 / math.sqrt(c), device, seed, "w", "ik"), act)
     else:
         W["B"] = randn((m, c), std_b, device, seed, "b", "hca")
     W["gamma_kv"] = torch.ones(c, device=device, dtype=torch.float32)
@@ -186,15 +215,16 @@ def queries(cfg: dict, Q: int, seed: int = SEED, device="cpu", tag="q", mx_codes
     scale rule gives blocks of N(0,1) values), laid out per query as element bytes then scale
     codes."""
     out = {"q": _store(randn((Q, cfg["n_h"], cfg["c"]), 1.0, device, seed, tag, "q"), cfg["act"])}
-    if cfg["dual"] and cfg["idx_fmt"] == "mxfp4":
+    idx = cfg["top_k"] > 0
+    if idx and cfg["idx_fmt"] == "mxfp4":
         # per query: n_hI rows of element bytes, then n_hI rows of scale codes
         codes, scales = mxfp4_random(Q * cfg["n_hI"], cfg["c_I"], device, seed, tag, "qI4",
                                      lo=mx_codes[0], hi=mx_codes[1])
         out["qI"] = torch.cat([codes.view(Q, -1), scales.view(Q, -1)], dim=1).contiguous()
-    elif cfg["dual"]:
+    elif idx:
         out["qI"] = _store(randn((Q, cfg["n_hI"], cfg["c_I"]), 1.0, device, seed, tag, "qI"),
                            cfg["idx_fmt"])
-    if cfg["dual"]:
+    if idx:
         out["w"] = _store(randn((Q, cfg["n_hI"]), 1.0, device, seed, tag, "w"), cfg["act"])
     return out
 
@@ -212,16 +242,26 @@ def synthetic_cache(cfg: dict, B: int, N: int, R: int, seed: int = SEED, device=
         x = randn((B, n, c), 1.0, device, seed, *ids)
         if cfg["kv_fmt"] == "f32":
             return x.contiguous().view(torch.uint8).reshape(B, n, 4 * c)
+        if cfg["kv_fmt"] == "q4":
+            # the library's MXFP4_BF16 row: bf16 RoPE dims, element bytes, scale codes, zero
+            # pad.  Drawn as codes: scale codes 125 .. 127 (the ones the MX rule gives blocks of
+            # N(0,1) values) and element magnitudes up to 3 (code 5), so that rows have about
+            # the RMS (1) and the range of an RMS-normalised row
+            rope = x[..., c - r:].to(torch.bfloat16).contiguous().view(torch.uint8)
+            el, sc = mxfp4_random(B * n, c - r, device, seed, *ids, "q4", lo=125, hi=127, mag_max=5)
+            pad = torch.zeros((B, n, row_bytes(cfg) - rope.shape[-1] - el.shape[-1] - sc.shape[-1]),
+                              dtype=torch.uint8, device=device)
+            return torch.cat([rope, el.view(B, n, -1), sc.view(B, n, -1), pad], dim=-1).contiguous()
         nope = _store(x[..., : c - r], "e4m3")
         rope = x[..., c - r:].to(torch.bfloat16).contiguous().view(torch.uint8)
         return torch.cat([nope, rope], dim=-1).contiguous()
 
     out = {"kv": rows(N, "ckv"), "win": rows(R, "cwin")}
-    if cfg["dual"] and cfg["idx_fmt"] == "mxfp4":
+    if cfg["top_k"] > 0 and cfg["idx_fmt"] == "mxfp4":
         # per sequence: N rows of element bytes, then N rows of scale codes
         codes, scales = mxfp4_random(B * N, cfg["c_I"], device, seed, "cki4")
         out["ki"] = torch.cat([codes.view(B, -1), scales.view(B, -1)], dim=1).contiguous()
-    elif cfg["dual"]:
+    elif cfg["top_k"] > 0:
         out["ki"] = _store(randn((B, N, cfg["c_I"]), 0.5, device, seed, "cki"), cfg["idx_fmt"])
     return out
 

@@ -36,7 +36,8 @@ def oracle_dims(cfg: dict, **over) -> R.Dims:
 
 
 def lib_weights(W: dict, dual: bool) -> L.Weights:
-    """Pack synthetic weights (synth.weights) into the ABI layout."""
+    """Pack synthetic weights (synth.weights) into the ABI layout (CSA2: no bias, w_idx the
+    entry-to-key projection)."""
     if dual:
         w_kv = torch.stack([W["kv_a"], W["kv_b"], W["z_a"], W["z_b"]]).contiguous()
         w_idx = torch.stack([W["ki_a"], W["ki_b"], W["zi_a"], W["zi_b"]]).contiguous()
@@ -44,6 +45,8 @@ def lib_weights(W: dict, dual: bool) -> L.Weights:
         bias_idx = torch.stack([W["BI_a"], W["BI_b"]]).contiguous()
         return L.Weights(w_kv, bias, w_idx, bias_idx, W["gamma_kv"])
     w_kv = torch.stack([W["kv"], W["z"]]).contiguous()
+    if W.get("w_ik") is not None:
+        return L.Weights(w_kv, None, W["w_ik"].contiguous(), None, W["gamma_kv"])
     return L.Weights(w_kv, W["B"].contiguous(), None, None, W["gamma_kv"])
 
 
@@ -67,6 +70,12 @@ def decode_rows(rows_u8: np.ndarray, cfg: dict) -> np.ndarray:
     rows_u8 = np.ascontiguousarray(rows_u8)
     if cfg["kv_fmt"] == "f32":
         return rows_u8.view(np.float32).astype(np.float64)
+    if cfg["kv_fmt"] == "q4":
+        # the library's MXFP4_BF16 row: r bf16 RoPE dims, (c - r) / 2 element bytes, scales
+        ne, ns = (c - r) // 2, (c - r) // 32
+        rope = codecs.bf16_decode(rows_u8[..., : 2 * r].copy().view("<u2"))
+        nope = codecs.mxfp4_decode(rows_u8[..., 2 * r: 2 * r + ne], rows_u8[..., 2 * r + ne: 2 * r + ne + ns])
+        return np.concatenate([nope, rope], axis=-1)
     nope = codecs.e4m3_decode(rows_u8[..., : c - r])
     rope = codecs.bf16_decode(rows_u8[..., c - r:].copy().view("<u2"))
     return np.concatenate([nope, rope], axis=-1)

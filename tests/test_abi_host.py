@@ -58,7 +58,8 @@ def test_invalid_dims_are_rejected_on_the_host():
         dict(rope_dim=70),               # rope_dim > c
         dict(top_k=0),                   # CSA needs top_k
         dict(n_win=2),                   # n_win < m
-        dict(dual=False),                # HCA with top_k > 0
+        dict(top_k=-1),                  # negative top_k
+        dict(dual=False, c_I=0),         # CSA2 (single path with top_k > 0) without index keys
     ]
     for over in bad:
         d = L.Dims.from_config(synth.config("c1"), **over)
@@ -67,6 +68,13 @@ def test_invalid_dims_are_rejected_on_the_host():
                                     ctypes.byref(out))
         assert st == 1, over
         assert lib.csa_last_error().decode()
+    # CSA2 (single path with an indexer) is a valid layer at both shapes, with FP4 main rows
+    for name in ("c1v2", "c6", "c6fp4"):
+        d = L.Dims.from_config(synth.config(name))
+        out = ctypes.c_size_t(0)
+        assert lib.csa_workspace_size(ctypes.byref(d.struct()), L.OP_FORWARD, 2, 1, 1, 64, 0,
+                                      ctypes.byref(out)) == 0, lib.csa_last_error()
+    assert L.csa_row_bytes(L.Dims.from_config(synth.config("c6"))) == 384 == synth.row_bytes(synth.config("c6"))
     # HCA too: a window shorter than m' would leave the open block's older tokens unseen
     d = L.Dims.from_config(synth.config("c5"), n_win=64)
     out = ctypes.c_size_t(0)
@@ -113,6 +121,12 @@ def test_null_and_workspace_errors_without_a_device():
     assert lib.csa_forward(ctypes.byref(ds), ctypes.byref(w), ctypes.byref(cache), fake, 64, fake,
                            fake, fake, fake, None, None, fake, None, fake, 1 << 30, None) == 1
     assert lib.csa_status_string(3) == b"workspace too small"
+    # CSA2 needs its entry-to-key projection in w_idx (and takes no bias)
+    d6 = L.Dims.from_config(synth.config("c6")).struct()
+    no_ik = L._Weights(fake, None, None, None, None)
+    assert lib.csa_compress(ctypes.byref(d6), ctypes.byref(no_ik), ctypes.byref(cache), fake, 4, fake,
+                            fake, 1 << 30, None) == 1
+    assert b"w_idx" in lib.csa_last_error()
     # the allocation-free forward: a 32768-token chunk needs more than its static scratch, which
     # it reports before any HIP call
     big = L._Cache(1, 270336, 32768 + 128, fake, fake, fake, fake, fake, fake)
