@@ -231,8 +231,7 @@ void k_attend_hs(AttendArgs a) {
 
   const int w0 = max(0, tau - a.n_win + 1);
   // entries visible at tau; with an index list it is needed only when the rows are widened
-  int V = 0;
-  if constexpr (!SPARSE || PAGED) V = max(0, min(tau / a.m, a.n_entries[seq]));
+  const int V = max(0, min(tau / a.m, a.n_entries[seq]));
   const int nsel = SPARSE ? a.k : V;
   const int nrows = nsel + (tau - w0 + 1);
   const int r_hi = min(nrows, r_lo + a.tiles_per_split * HS_ROWS);
@@ -255,9 +254,16 @@ void k_attend_hs(AttendArgs a) {
 
   // ---- row gather: lane (row, g) loads bytes 64i + 16g .. +15 of the row (i < 9; pieces
   // 0..6 hold E4M3 dims, 7 and 8 bf16 RoPE dims) and the position its window slot holds.
-  // Loads are unconditional: masked rows read row 0 of the sequence and are zeroed at
-  // widening.
+  // Rows past the part's end and entries that are not visible are not loaded at all: their
+  // lanes keep the values of an earlier row (finite, or the zeros they start with), and the
+  // softmax gives them weight 0.  Window rows always load (a slot holding another position
+  // is a finite row too) and are masked by the position check.
   uint4 pre[HS_DEPTH][NPIECE];
+#pragma unroll
+  for (int t = 0; t < HS_DEPTH; ++t)
+#pragma unroll
+    for (int i = 0; i < NPIECE; ++i) pre[t][i] = make_uint4(0u, 0u, 0u, 0u);
+  bool ldk[HS_DEPTH];   // whether this lane's row of the tile is loaded
   int chk[HS_DEPTH], wpv[HS_DEPTH], sv[HS_DEPTH];   // chk: 1 entry row, 0 masked, else window position + 2
   // source row of this lane for the tile at t0 (plus its window-slot position load and the
   // facts its validity is decided from)
@@ -266,17 +272,19 @@ void k_attend_hs(AttendArgs a) {
     const int r = t0 + myrow;
     const bool in = r < r_hi, ent = r < nsel;
     const int s = (SPARSE || PAGED) ? s_in : r;
-    const bool ok_a = in && ent && s >= 0 && (PAGED || s < a.cap);
+    const bool ok_a = in && ent && s >= 0 && (PAGED || (s < a.cap && s < V));
     const int slot = (ent ? 0 : w0 + (r - nsel)) % a.win_cap;
     const uint8_t* src = ent ? kvseq + (size_t)(ok_a ? s : 0) * ROWB
                              : (in ? winseq + (size_t)slot * ROWB : kvseq);
     wpv[b] = wpseq[slot];
     chk[b] = ent ? (ok_a ? 1 : 0) : (in ? w0 + (r - nsel) + 2 : 0);
     sv[b] = s;
+    ldk[b] = ent ? ok_a : in;
     return src;
   };
   auto gather_piece = [&](const uint8_t* src, int i, auto bconst) {
-    pre[decltype(bconst)::value][i] = *reinterpret_cast<const uint4*>(src + 64 * i + 16 * g);
+    constexpr int b = decltype(bconst)::value;
+    if (ldk[b]) pre[b][i] = *reinterpret_cast<const uint4*>(src + 64 * i + 16 * g);
   };
   auto gather = [&](int t0, int s_in, auto bconst) {
     const uint8_t* src = gather_src(t0, s_in, bconst);
@@ -287,7 +295,6 @@ void k_attend_hs(AttendArgs a) {
   if constexpr (HS_DEPTH > 1) gather(r_lo + HS_ROWS, s01[HS_DEPTH - 1], std::integral_constant<int, HS_DEPTH - 1>{});
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (SPARSE && !PAGED) V = max(0, min(tau / a.m, a.n_entries[seq]));
 
   // ---- LDS: the normalised query rows (RMSNorm over a head's 512 dims, whose 16 threads
   // hold 32 dims each, times the norm weights; in the tile buffer, pitch HS_PITCH), this
@@ -360,7 +367,6 @@ void k_attend_hs(AttendArgs a) {
 #pragma unroll
       for (int i = 0; i < 6; ++i) {
         uint4 v = pre[b][i];
-        if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
         if (i < 2) {
           *reinterpret_cast<uint4*>(wrow + 16 * (56 + 4 * i + g)) = v;
           Sp[i & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), Qop[i], Sp[i & 3], 0, 0, 0);
@@ -389,8 +395,7 @@ void k_attend_hs(AttendArgs a) {
     } else {
 #pragma unroll
     for (int i = 0; i < 9; ++i) {
-      uint4 v = pre[b][i];
-      if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
+      const uint4 v = pre[b][i];
       if (i < 7) {
         uint32_t x[8];
         e4m3x4_to_bf16x4(v.x, x[0], x[1]);
@@ -428,11 +433,11 @@ void k_attend_hs(AttendArgs a) {
     lds_barrier();
     const float m_tile = fmaxf(fmaxf(redm[0][col], redm[1][col]), fmaxf(redm[2][col], redm[3][col]));
     const float m_new = fmaxf(m_run, m_tile);
-    const float alpha = exp2f(m_run - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float ls = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      S[e] = exp2f(S[e] - m_new);
+      S[e] = __builtin_amdgcn_exp2f(S[e] - m_new);
       ls += S[e];
     }
     // every wave holds the same running max, so each keeps the sum over its own rows and
