@@ -26,6 +26,14 @@ HIP_FLAGS = [
 ]
 
 
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer (device code is unaffected): the
+# checks, planning and dispatch code of the C ABI, for the host sanitizer test.
+HOST_SANITIZE = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g",
+]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -33,15 +41,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library needs ROCm's hipcc")
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+def build(verbose: bool = False, jobs: int = 4, out: str = LIB, host_sanitize: bool = False) -> str:
+    """Compile every source for gfx950 and link ``out`` (the in-tree libcsa.so by default).
+    host_sanitize builds the host code with the sanitizers (a separate library, for tests)."""
     cc = hipcc()
+    extra = HOST_SANITIZE if host_sanitize else []
     tmp = tempfile.mkdtemp(prefix="csa_build_")
     try:
         objs, procs = [], []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"]
-            cmd = [cc, *HIP_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *HIP_FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -50,17 +61,17 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
                 _wait(procs.pop(0), verbose)
         for p in procs:
             _wait(p, verbose)
-        out_tmp = LIB + ".tmp"
-        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", out_tmp]
+        out_tmp = out + ".tmp"
+        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *extra, *objs, "-o", out_tmp]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
         if r.returncode:
             raise RuntimeError("link failed:\n" + r.stdout)
-        os.replace(out_tmp, LIB)
+        os.replace(out_tmp, out)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB
+    return out
 
 
 def _wait(item, verbose):

@@ -574,15 +574,28 @@ def test_c5_hca_decode_full_size_paged():
     _decode_full("c5", paged=True)
 
 
-@pytest.mark.parametrize("idx_fmt", ["e4m3", "mxfp4"])
-def test_c4_prefill_full_size_sampled(idx_fmt):
+def _prefill_sample(T, m, seed=0):
+    """256 query rows of a T-token chunk: the first and last 32, 32 at positions = 0 and 32 at
+    positions = m - 1 (mod m) spread over the chunk, and 128 more drawn at random."""
+    rng = np.random.default_rng(seed)
+    first, last = list(range(32)), list(range(T - 32, T))
+    mid = np.arange(32, T - 32)
+    at0 = rng.choice(mid[mid % m == 0], 32, replace=False).tolist()
+    at3 = rng.choice(mid[mid % m == m - 1], 32, replace=False).tolist()
+    rest = np.setdiff1d(mid, at0 + at3)
+    return sorted(set(first + last + at0 + at3 + rng.choice(rest, 128, replace=False).tolist()))
+
+
+@pytest.mark.parametrize("name,idx_fmt", [("c4a", "e4m3"), ("c4a", "mxfp4"), ("c4b", "e4m3")])
+def test_c4_prefill_full_size_sampled(name, idx_fmt):
     """Flash chunked prefill at full size: a 32768-token chunk after a 1048576-token prefix
-    (262144 entries).  The prefix cache, its window ring and the projection state of the
-    block before the chunk (zeros) are inputs given to both sides; csa_forward compresses the
-    chunk (8192 new entries), scores every query against up to 270335 entries, selects 512 and
-    attends.  Sampled queries across the chunk are checked against the oracle, which folds
-    the chunk's entries from the same hidden states.  Indexer keys in E4M3 or MXFP4."""
-    cfg = dict(synth.config("c4a"), idx_fmt=idx_fmt)
+    (c4a: 262144 entries) or a 262144-token prefix (c4b: 65536 entries).  The prefix cache,
+    its window ring and the projection state of the block before the chunk (zeros) are inputs
+    given to both sides; csa_forward compresses the chunk (8192 new entries), scores every
+    query against all visible entries, selects 512 and attends.  256 stratified query rows of
+    the chunk are checked against the oracle, which folds the chunk's entries from the same
+    hidden states; every new entry and key is checked.  Indexer keys in E4M3 or MXFP4."""
+    cfg = dict(synth.config(name), idx_fmt=idx_fmt)
     dims = L.Dims.from_config(cfg)
     od = oracle_dims(cfg)
     m, k, T, p0 = cfg["m"], cfg["top_k"], cfg["T"], cfg["prefix"]
@@ -651,8 +664,7 @@ def test_c4_prefill_full_size_sampled(idx_fmt):
     q, qI, w = host64(qs["q"]), qI_host(qs["qI"], cfg), host64(qs["w"])
     sink = host64(W["sink"])
     gi, go = idx.cpu().numpy(), host64(out)
-    sample = [0, 1, 2, 3, 4, 5, 127, 128, 1000, 4097, 16383, 20000, 32766, 32767]
-    for t in sample:
+    for t in _prefill_sample(T, m):
         tau = p0 + t
         o_ref, sel, sc = R.query_step(tau, q[t], qI[t], w[t], None, sink, entries, ki, raw_of, cap, od)
         try:
