@@ -207,7 +207,7 @@ int csa_workspace_size(const csa_dims* dims, int32_t op, int32_t B, int32_t T, i
       L.add(1, has_indexer(d) ? sizeof(int32_t) * (size_t)Qn * d.top_k : 0);  // idx
       size_t phase = compress_ws(d, B, T);
       if (has_indexer(d)) phase = std::max(phase, index_ws(d, Qc, cap));
-      if (d.dual && T == 1)
+      if (has_indexer(d) && T == 1)
         phase = std::max(phase, align_up(index_ws_carry(d, Qn, cap), 256) + project_part_bytes(d, B));
       // forward attends a layer with an indexer sparsely
       phase = std::max(phase, attend_workspace_bytes(d, Qn, cap, has_indexer(d) ? 0 : 1));
@@ -455,7 +455,7 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
   // With T = 1, query i is token pos0[i] of sequence i, so the kernels take the sequence as
   // the query index (null q_seq) and pos0 as q_pos.
   const size_t ix_bytes = align_up(index_ws_carry(d, Qn, cache->cap), 256);
-  if (d.dual && project_step_ok(d, T) && topk_can_carry(*cache) &&
+  if (has_indexer(d) && project_step_ok(d, T) && topk_can_carry(*cache) &&
       ix_bytes + project_part_bytes(d, cache->B) <= phase_bytes) {
     float* part = (float*)((char*)phase_ws + ix_bytes);
     const ProjectStepArgs pa = project_step_args(d, *w, *cache, H, part);

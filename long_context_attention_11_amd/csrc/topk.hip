@@ -612,13 +612,15 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_final(FinalArgs fa) {
 
 // The final pass and a one-token fold in one launch (independent: blocks [0, Q) select, the
 // rest fold with 1024-thread blocks, whose columns past c hold zeros).
-template <bool BF>
+// EK: the fold projects CSA2 index keys from the entries (LDS for the entry row and key).
+template <bool BF, bool EK>
 __global__ __launch_bounds__(TK_THREADS) void k_topk_final_fold(FinalArgs fa, int Q, FoldArgs fo, int fx) {
   __shared__ FinalShared fs;
   __shared__ float red[TK_WAVES];
+  __shared__ float ybuf[EK ? 512 : 1], kbuf[EK ? 512 : 1];
   const int b = blockIdx.x;
   if (b < Q) topk_final_body<BF>(fa, b, fs);
-  else fold_block<TK_WAVES, true>(fo, (b - Q) % fx, (b - Q) / fx, red);
+  else fold_block<TK_WAVES, true>(fo, (b - Q) % fx, (b - Q) / fx, red, EK ? ybuf : nullptr, EK ? kbuf : nullptr);
 }
 
 // ----------------------------------------------------------------------- one-launch rows
@@ -891,7 +893,10 @@ hipError_t launch_topk_t(const csa_dims& d, const csa_cache& c, const int32_t* q
   if (fold) {
     if (!fold->part) return hipErrorInvalidValue;   // the carried fold is a one-token step's
     const int fx = fold_grid_x(*fold);
-    hipLaunchKernelGGL(k_topk_final_fold<BF>, dim3(Q + fx * c.B), dim3(TK_THREADS), 0, s, fin, Q, *fold, fx);
+    if (fold->keys_entry)
+      hipLaunchKernelGGL((k_topk_final_fold<BF, true>), dim3(Q + fx * c.B), dim3(TK_THREADS), 0, s, fin, Q, *fold, fx);
+    else
+      hipLaunchKernelGGL((k_topk_final_fold<BF, false>), dim3(Q + fx * c.B), dim3(TK_THREADS), 0, s, fin, Q, *fold, fx);
   } else {
     hipLaunchKernelGGL(k_topk_final<BF>, dim3(Q), dim3(TK_THREADS), 0, s, fin);
   }
