@@ -230,7 +230,7 @@ void k_attend_hs(AttendArgs a) {
   __builtin_amdgcn_sched_barrier(0);
 
   const int w0 = max(0, tau - a.n_win + 1);
-  // entries visible at tau; with an index list it is needed only when the rows are widened
+  // entries visible at tau
   const int V = max(0, min(tau / a.m, a.n_entries[seq]));
   const int nsel = SPARSE ? a.k : V;
   const int nrows = nsel + (tau - w0 + 1);
@@ -282,14 +282,13 @@ void k_attend_hs(AttendArgs a) {
     ldk[b] = ent ? ok_a : in;
     return src;
   };
-  auto gather_piece = [&](const uint8_t* src, int i, auto bconst) {
-    constexpr int b = decltype(bconst)::value;
-    if (ldk[b]) pre[b][i] = *reinterpret_cast<const uint4*>(src + 64 * i + 16 * g);
-  };
   auto gather = [&](int t0, int s_in, auto bconst) {
+    constexpr int b = decltype(bconst)::value;
     const uint8_t* src = gather_src(t0, s_in, bconst);
+    if (ldk[b]) {
 #pragma unroll
-    for (int i = 0; i < NPIECE; ++i) gather_piece(src, i, bconst);
+      for (int i = 0; i < NPIECE; ++i) pre[b][i] = *reinterpret_cast<const uint4*>(src + 64 * i + 16 * g);
+    }
   };
   gather(r_lo, s01[0], std::integral_constant<int, 0>{});
   if constexpr (HS_DEPTH > 1) gather(r_lo + HS_ROWS, s01[HS_DEPTH - 1], std::integral_constant<int, HS_DEPTH - 1>{});
@@ -349,6 +348,7 @@ void k_attend_hs(AttendArgs a) {
     const int s_next = (SPARSE || PAGED) ? ridx[min(max(tn + myrow - r_lo, 0), NRIDX - 1)] : 0;
     const bool ok = (chk[b] == 1 && (PAGED || sv[b] < V)) || (chk[b] >= 2 && wpv[b] == chk[b] - 2);
     const uint64_t okm = __ballot(ok);   // bit r of the low 16: row 16w + r is valid
+
     // ---- widen, write the V tile, and contract Q.K for this wave's 16 rows (four
     // independent accumulation chains, added at the end)
     f32x4 Sp[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
@@ -415,9 +415,10 @@ void k_attend_hs(AttendArgs a) {
     }
     }
     f32x4 S = (Sp[0] + Sp[1]) + (Sp[2] + Sp[3]);
-    // the tile after next goes into the registers just consumed; its nine loads are spread
-    // over the P.V steps below, so that the vector memory unit works while LDS and MFMA do
-    const uint8_t* nsrc = gather_src(tn, s_next, bconst);
+    // the tile after next goes into the registers just consumed, its loads in flight during
+    // the softmax and P.V (one predicated block: per-load branches would split P.V's LDS
+    // reads and MFMAs into separately scheduled pieces)
+    gather(tn, s_next, bconst);
 
     // ---- online softmax: lane holds head col, rows 16w + 4g + e
     float mx = NEG_BIG;
@@ -467,7 +468,6 @@ void k_attend_hs(AttendArgs a) {
         const s16x4 hi = lds_read_tr16(va + HS_PITCH);
         const bf16x8 Av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Bp, O[dt], 0, 0, 0);
-        if (kc * 8 + dt < NPIECE) gather_piece(nsrc, kc * 8 + dt, bconst);
       }
     }
     lds_barrier();   // the next tile rewrites the row and probability buffers
@@ -508,29 +508,31 @@ void k_attend_hs(AttendArgs a) {
   }
 }
 
-// Merge split partials (already rotated back): one workgroup of 256 threads per (query, head),
-// 2 dims per thread.
-// Splits are taken 8 at a time (all loads of a chunk in flight), merged with a running max.
+// Merge split partials (already rotated back): one wave per (query, head), 8 dims per lane,
+// four (query, head) pairs per workgroup.  Splits are taken 8 at a time (all loads of a chunk
+// in flight), merged with a running max.
 constexpr int COMB_MAX = 256;  // most splits a plan uses
+constexpr int COMB_WAVES = 4;
 
-__global__ __launch_bounds__(256) void k_attend_combine(AttendArgs a) {
-  const int qh = blockIdx.x;
+__global__ __launch_bounds__(64 * COMB_WAVES) void k_attend_combine(AttendArgs a) {
+  const int qh = blockIdx.x * COMB_WAVES + (threadIdx.x >> 6);
+  if (qh >= a.Q * a.n_h) return;
   const int h = qh % a.n_h;
-  const int d = 2 * threadIdx.x;
+  const int d = 8 * (threadIdx.x & 63);
   const float* ml = a.part_ml + (size_t)qh * a.splits * 2;
   const uint16_t* po = a.part_o + (size_t)qh * a.splits * AC + d;
   const float sink2 = a.sink ? a.sink[h] * LOG2E : NEG_BIG;
   float M = a.sink ? sink2 : NEG_BIG;
   float Lsum = a.sink ? 1.0f : 0.f;   // the sink's term exp2(sink2 - M) with M = sink2
-  float y0 = 0.f, y1 = 0.f;
+  float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < a.splits; s0 += 8) {
-    float2 mls[8], ov[8];
+    float2 mls[8];
+    uint4 ov[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int s = min(s0 + i, a.splits - 1);
       mls[i] = *reinterpret_cast<const float2*>(ml + 2 * s);
-      const uint32_t pk = *reinterpret_cast<const uint32_t*>(po + (size_t)s * AC);
-      ov[i] = make_float2(bf16_bits_to_f32(pk & 0xffffu), bf16_bits_to_f32(pk >> 16));
+      ov[i] = *reinterpret_cast<const uint4*>(po + (size_t)s * AC);
     }
     float Mc = M;
 #pragma unroll
@@ -538,20 +540,26 @@ __global__ __launch_bounds__(256) void k_attend_combine(AttendArgs a) {
       if (s0 + i < a.splits) Mc = fmaxf(Mc, mls[i].x);
     const float r = exp2f(M - Mc);
     Lsum *= r;
-    y0 *= r;
-    y1 *= r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] *= r;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (s0 + i >= a.splits) break;
       const float f = exp2f(mls[i].x - Mc);
       Lsum = fmaf(mls[i].y, f, Lsum);
-      y0 = fmaf(ov[i].x, f, y0);
-      y1 = fmaf(ov[i].y, f, y1);
+      const uint32_t w[4] = {ov[i].x, ov[i].y, ov[i].z, ov[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y[2 * j] = fmaf(bf16_bits_to_f32(w[j] & 0xffffu), f, y[2 * j]);
+        y[2 * j + 1] = fmaf(bf16_bits_to_f32(w[j] >> 16), f, y[2 * j + 1]);
+      }
     }
     M = Mc;
   }
   const float invL = Lsum > 0.f ? 1.0f / Lsum : 0.f;
-  *reinterpret_cast<uint32_t*>(a.out + (size_t)qh * AC + d) = pack_bf16x2(y0 * invL, y1 * invL);
+  *reinterpret_cast<uint4*>(a.out + (size_t)qh * AC + d) =
+      make_uint4(pack_bf16x2(y[0] * invL, y[1] * invL), pack_bf16x2(y[2] * invL, y[3] * invL),
+                 pack_bf16x2(y[4] * invL, y[5] * invL), pack_bf16x2(y[6] * invL, y[7] * invL));
 }
 
 // float32 rows (fp32 formats): one workgroup of 64 threads per (query, head); exact
@@ -765,7 +773,7 @@ hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
 #undef ATT_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL(k_attend_combine, dim3(Q * d.n_h), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_attend_combine, dim3((Q * d.n_h + COMB_WAVES - 1) / COMB_WAVES), dim3(64 * COMB_WAVES), 0, s, a);
   return hipGetLastError();
 }
 

@@ -342,6 +342,42 @@ def test_q_attend_no_sink_and_masked_window():
     _run_index_attend_and_check(cfg, dims, cache, qs, W, q_seq, q_pos, taus)
 
 
+def test_q_attend_skips_indices_past_visible():
+    """A caller's index list holding -1 slots, duplicates and indices at or past the visible
+    count V (rows past n_entries hold NaN bytes in every field): only the slots below V count,
+    each as one key, and no NaN of a row that is not visible reaches the output."""
+    cfg = _qcfg()
+    N, k = 3000, cfg["top_k"]
+    taus = [(0, 4 * 1500 + 1), (1, 4 * 2999 + 3)]   # V = 1500 (n_entries 2000), V = 2999
+    dims, cache, qs, W, q_seq, q_pos = _synthetic_decode_setup(cfg, 2, N, 128, taus, n_entries=[2000, 3000])
+    cache.kv.view(2, N, -1)[0, 2000:] = 0xFF          # NaN as E4M3 and as bf16
+    rng = np.random.default_rng(5)
+    idx = np.empty((2, k), dtype=np.int32)
+    for i, (b, tau) in enumerate(taus):
+        V = R.visible_entries(tau, cfg["m"], int(cache.n_entries[b]))
+        row = rng.choice(V, size=k, replace=False).astype(np.int32)
+        bad = rng.choice(k, size=96, replace=False)
+        row[bad[:40]] = rng.integers(V, N, size=40)     # invisible (NaN rows for sequence 0)
+        row[bad[40:60]] = -1
+        row[bad[60:96]] = row[(bad[60:96] + 1) % k]     # duplicates of other slots
+        idx[i] = row
+    out = torch.zeros((2, cfg["n_h"], cfg["c"]), dtype=torch.bfloat16, device=DEV)
+    ws = _ws(L.csa_workspace_size(dims, L.OP_ATTEND, Q=2, cap=cache.cap))
+    L.csa_attend(dims, cache, qs["q"], W["gamma_q"], W["sink"], q_seq, q_pos, 2, _i32(idx), out, ws)
+    torch.cuda.synchronize()
+    go = host64(out)
+    assert np.all(np.isfinite(go))
+    od = oracle_dims(cfg)
+    q, sink = host64(qs["q"]), host64(W["sink"])
+    for i, (b, tau) in enumerate(taus):
+        entries, ki, raw_of = _oracle_cache(cfg, cache, b)
+        V = R.visible_entries(tau, cfg["m"], int(cache.n_entries[b]))
+        sel = idx[i][(idx[i] >= 0) & (idx[i] < V)]
+        o_ref = R.query_step(tau, q[i], None, None, None, sink, entries, ki, raw_of, int(cache.n_entries[b]), od,
+                             sel=sel)[0]
+        assert_close_q(go[i], o_ref, f"past-visible indices seq {b}")
+
+
 def test_hca_dense_attend_small():
     """HCA dense attention (idx = NULL) over up to 300 entries + the window."""
     cfg = synth.config("c5")
