@@ -429,14 +429,14 @@ __global__ __launch_bounds__(256) void k_indexer_fp4(IndexerArgs ia) {
 
 // Prefill-shaped indexer: a workgroup of 8 waves scores IT_Q = 16 queries of ONE sequence
 // (2 per wave) against that sequence's entries [e_lo, e_hi).  Keys are shared by every query
-// of the tile, so they are staged once through LDS (64-entry stages, double buffered, one
-// 16-byte load per thread per stage, widened to bf16 once while staging) instead of being
+// of the tile, so they are staged once through LDS (256-entry stages, double buffered, four
+// 16-byte loads per thread per stage, widened to bf16 once while staging) instead of being
 // fetched and widened per query.  Each wave keeps its two queries' q^I (64 heads, widened to
 // bf16) in registers; per 16-entry tile it reads the keys from LDS and runs 2 x 4 head tiles
 // x 4 K-steps of bf16 MFMA, with the same operand mapping and epilogue order as
 // k_indexer_bf16 (so the scores are identical).
 constexpr int IT_Q = 16;        // queries per workgroup
-constexpr int IT_STAGE = 64;    // entries per LDS stage
+constexpr int IT_STAGE = 256;   // entries per LDS stage (one barrier per 16 tiles)
 constexpr int IT_LD = 272;      // LDS bytes per entry row: 128 dims in bf16 + 16 pad (spreads the banks)
 
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_indexer_tile(
