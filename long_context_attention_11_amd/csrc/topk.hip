@@ -369,6 +369,7 @@ struct FilterArgs {
   const int32_t* q_pos;
   const int32_t* n_entries;
   int m, k, cs, nseg;
+  int spw;                // segments per workgroup (consecutive; one sample and threshold)
   int32_t* cand_idx;
   uint32_t* cand_key;
   int32_t* cand_cnt;
@@ -383,9 +384,11 @@ struct FilterArgs {
 // the passing scores are compacted with wave ballots and lane counts below the lane.  Reads
 // of a segment start at min(c0, L - TK_SEG), L = max(V, TK_SEG) <= the row stride (these
 // rows are longer than TK_SEG), so every read stays in the row; elements outside [c0, V) are
-// masked.
+// masked.  A workgroup filters segments seg0 .. seg0 + n - 1 of the row against one threshold
+// (the sample is the same for every segment of a row), the next segment's loads in flight
+// while one is compacted.
 template <bool BF>
-__device__ __forceinline__ void topk_filter_body(const FilterArgs& fa, int q, int seg, TopkShared& sh) {
+__device__ __forceinline__ void topk_filter_body(const FilterArgs& fa, int q, int seg0, int n, TopkShared& sh) {
   const int k = fa.k, cs = fa.cs, nseg = fa.nseg;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -398,11 +401,14 @@ __device__ __forceinline__ void topk_filter_body(const FilterArgs& fa, int q, in
   float smp[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) smp[i] = row[bs + i];
-  const int c0 = seg * TK_SEG;
-  const int a0 = min(c0, L - TK_SEG) + 512 * w;
+  const int nlast = min(seg0 + n, nseg) - 1;
+  auto seg_base = [&](int seg) { return min(seg * TK_SEG, L - TK_SEG) + 512 * w; };
   float sv[8];
+  {
+    const int a0 = seg_base(seg0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) sv[i] = row[a0 + 64 * i + lane];
+    for (int i = 0; i < 8; ++i) sv[i] = row[a0 + 64 * i + lane];
+  }
   uint32_t lo = 0u, span = 0xffffffffu;   // every score passes
   if (!take_all) {   // uniform
 #pragma unroll
@@ -426,44 +432,58 @@ __device__ __forceinline__ void topk_filter_body(const FilterArgs& fa, int q, in
     __syncthreads();
     if (scale > 0.f) pass_interval(fmn + (float)sh.sel_bin / scale, lo, span);
   }
-  const int vlo = max(0, c0 - a0), vspan = max(0, min(512, V - a0) - vlo);   // uniform
-  bool p[8];
-  uint64_t bal[8];
-  int cnt = 0;
+  for (int seg = seg0; seg <= nlast; ++seg) {
+    const int c0 = seg * TK_SEG;
+    const int a0 = seg_base(seg);
+    const int vlo = max(0, c0 - a0), vspan = max(0, min(512, V - a0) - vlo);   // uniform
+    bool p[8];
+    uint64_t bal[8];
+    int cnt = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    p[i] = __float_as_uint(sv[i]) - lo <= span && (uint32_t)(64 * i + lane - vlo) < (uint32_t)vspan;
-    bal[i] = __ballot(p[i]);
-    cnt += __popcll(bal[i]);
-  }
-  if (lane == 0) sh.scan[w] = cnt;
-  __syncthreads();
-  const int sw = sh.scan[lane & 15];
-  const int before = __builtin_amdgcn_readfirstlane(row_allreduce((lane & 15) < w ? sw : 0, OpAdd()));
-  const int total = row_allreduce(sw, OpAdd());   // every lane of the row takes part
-  int32_t* ci = fa.cand_idx + ((size_t)q * nseg + seg) * cs;
-  uint32_t* ck = fa.cand_key + ((size_t)q * nseg + seg) * cs;
-  uint32_t base = (uint32_t)before;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (p[i]) {
-      const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[i] >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal[i], base));
-      if (pos < cs) {
-        ci[pos] = a0 + 64 * i + lane;
-        ck[pos] = score_key(sv[i]);
-      }
+    for (int i = 0; i < 8; ++i) {
+      p[i] = __float_as_uint(sv[i]) - lo <= span && (uint32_t)(64 * i + lane - vlo) < (uint32_t)vspan;
+      bal[i] = __ballot(p[i]);
+      cnt += __popcll(bal[i]);
     }
-    base += (uint32_t)__popcll(bal[i]);
+    // the passing scores' keys are taken now, so that the next segment can be loaded into sv
+    uint32_t kv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kv[i] = score_key(sv[i]);
+    if (seg < nlast) {
+      const int a1 = seg_base(seg + 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sv[i] = row[a1 + 64 * i + lane];
+    }
+    if (lane == 0) sh.scan[w] = cnt;
+    __syncthreads();
+    const int sw = sh.scan[lane & 15];
+    const int before = __builtin_amdgcn_readfirstlane(row_allreduce((lane & 15) < w ? sw : 0, OpAdd()));
+    const int total = row_allreduce(sw, OpAdd());   // every lane of the row takes part
+    __syncthreads();   // sh.scan is rewritten by the next segment
+    int32_t* ci = fa.cand_idx + ((size_t)q * nseg + seg) * cs;
+    uint32_t* ck = fa.cand_key + ((size_t)q * nseg + seg) * cs;
+    uint32_t base = (uint32_t)before;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (p[i]) {
+        const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[i] >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)bal[i], base));
+        if (pos < cs) {
+          ci[pos] = a0 + 64 * i + lane;
+          ck[pos] = kv[i];
+        }
+      }
+      base += (uint32_t)__popcll(bal[i]);
+    }
+    if (tid == 0) fa.cand_cnt[(size_t)q * nseg + seg] = total;
+    if (tid == 0 && seg == 0) fa.vis[q] = V;
   }
-  if (tid == 0) fa.cand_cnt[(size_t)q * nseg + seg] = total;
-  if (tid == 0 && seg == 0) fa.vis[q] = V;
 }
 
 template <bool BF>
 __global__ __launch_bounds__(TK_THREADS) void k_topk_filter(FilterArgs fa) {
   __shared__ TopkShared sh;
-  topk_filter_body<BF>(fa, blockIdx.x, blockIdx.y, sh);
+  topk_filter_body<BF>(fa, blockIdx.x, blockIdx.y * fa.spw, fa.spw, sh);
 }
 
 // The threshold pass and a one-token projection in one launch (they are independent), so the
@@ -478,7 +498,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_filter_project(FilterArgs f
   const int nf = Q * fa.nseg;
   const int b = blockIdx.x, wave = threadIdx.x >> 6;
   if (b < nf) {
-    topk_filter_body<BF>(fa, b % Q, b / Q, sh);
+    topk_filter_body<BF>(fa, b % Q, b / Q, 1, sh);
   } else if (wave < upb) {
     const int u = upb * (b - nf) + wave;
     if (u < units) project_unit<2>(pa, u);
@@ -877,7 +897,11 @@ hipError_t launch_topk_t(const csa_dims& d, const csa_cache& c, const int32_t* q
   uint32_t* ck = (uint32_t*)(ci + (size_t)Q * nseg * cs);
   int32_t* cc = (int32_t*)(ck + (size_t)Q * nseg * cs);
   int32_t* fvis = cc + (size_t)Q * nseg;   // the counts the threshold pass filtered with
-  const FilterArgs fa{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, cs, nseg, ci, ck, cc, fvis};
+  // segments per threshold workgroup: one while that still leaves a few workgroups per CU
+  // (decode), four on long prefill batches (the sample and its histogram are then taken once
+  // per four segments)
+  const int spw = (int64_t)Q * nseg >= 16 * 256 ? 4 : 1;
+  const FilterArgs fa{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, cs, nseg, spw, ci, ck, cc, fvis};
   if (step) {
     const int units = project_units(step->NP, step->M, 2);
     const int upb = carry_units_per_block(Q * nseg, units);
@@ -885,7 +909,7 @@ hipError_t launch_topk_t(const csa_dims& d, const csa_cache& c, const int32_t* q
     hipLaunchKernelGGL(k_topk_filter_project<BF>, dim3(Q * nseg + (units + upb - 1) / upb), dim3(TK_THREADS), 0, s,
                        fa, Q, *step, units, upb);
   } else {
-    hipLaunchKernelGGL(k_topk_filter<BF>, dim3(Q, nseg), dim3(TK_THREADS), 0, s, fa);
+    hipLaunchKernelGGL(k_topk_filter<BF>, dim3(Q, (nseg + spw - 1) / spw), dim3(TK_THREADS), 0, s, fa);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -768,3 +768,36 @@ def test_topk_exact_on_crafted_scores(fmt):
             got = gi[i][gi[i] >= 0]
             assert np.array_equal(got, ref), f"k={k} cap={cap} V={V} kind={i % 5}"
             assert np.all(gi[i][len(got):] == -1)
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16"])
+def test_topk_exact_many_long_rows(fmt):
+    """Enough long rows that each threshold workgroup filters several segments against one
+    sample (400 rows x 11 segments of 8192, the last group of segments ragged): random rows,
+    integer ties and falling ramps (the whole-row fallback), visible counts from k to the row
+    length.  The selection must equal the oracle's exactly."""
+    k, cap, Q = 512, 90001, 400
+    cfg = _qcfg(top_k=k, idx_fmt="mxfp4" if fmt == "bf16" else "e4m3")
+    dims = L.Dims.from_config(cfg)
+    m = cfg["m"]
+    cache = L.Cache(dims, B=1, cap=cap, win_cap=128)
+    cache.n_entries.fill_(cap)
+    rng = np.random.default_rng(77)
+    sc = rng.standard_normal((Q, cap)).astype(np.float32)
+    sc[1::7] = rng.integers(-3, 4, (len(range(1, Q, 7)), cap)).astype(np.float32)
+    sc[3::11] = -np.arange(cap, dtype=np.float32) * 1e-3
+    Vs = rng.integers(k, cap + 1, Q)
+    Vs[:4] = [k, k + 1, cap - 1, cap]
+    pos = [int(m * V + (i % m)) for i, V in enumerate(Vs)]
+    scores = torch.from_numpy(sc).to(DEV)
+    if fmt == "bf16":
+        scores = scores.to(torch.bfloat16)
+        sc = scores.float().cpu().numpy()
+    idx = torch.full((Q, k), -7, dtype=torch.int32, device=DEV)
+    ws = _ws(L.csa_topk_workspace_size(dims, Q, cap))
+    L.csa_topk(dims, cache, _i32([0] * Q), _i32(pos), Q, scores, cap, idx, ws)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    for i in range(Q):
+        ref = R.topk(sc[i, :Vs[i]].astype(np.float64), k)
+        assert np.array_equal(gi[i], ref), f"row {i} V={Vs[i]}"
