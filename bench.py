@@ -580,15 +580,25 @@ def prefill_rooflines(L, cfg, dims, cache, qs, W, idx, out, p0, T, q_chunk, ws):
     scores = torch.empty((Qc, cap), dtype=torch.bfloat16 if fp4 else torch.float32, device="cuda")
     qI = qs["qI"][:Qc].contiguous()
     wI = qs["w"][:Qc].contiguous()
-    t_ix = kernel_time_us([lambda: L.csa_index_scores_grouped(dims, cache, qI, wI, q_seq, q_pos, Qc, scores, cap)],
-                          reps=5, rounds=3)
+    t_scores = kernel_time_us([lambda: L.csa_index_scores_grouped(dims, cache, qI, wI, q_seq, q_pos, Qc, scores, cap)],
+                              reps=5, rounds=3)
     del scores
     flops = 2.0 * cfg["n_hI"] * cfg["c_I"] * sum(min((p0 + t) // m, cap) for t in range(Qc))
     peak = FP4_PEAK if fp4 else BF16_PEAK
-    ix = {"bound": "mfma", "kernel": "k_indexer_tile_fp4" if fp4 else "k_indexer_tile", "queries_per_launch": Qc,
+    if fp4:
+        t_ix, kname = t_scores, "k_indexer_tile_fp4"
+    else:
+        # the forward's own path: the indexer that thresholds its scores, then the selection
+        # from its lists (the launch pair csa_index_topk_grouped makes; the selection is ~1 %)
+        idx_c = torch.empty((Qc, cfg["top_k"]), dtype=torch.int32, device="cuda")
+        t_ix = kernel_time_us([lambda: L.csa_index_topk_grouped(dims, cache, qI, wI, q_seq, q_pos, Qc, idx_c, None, ws)],
+                              reps=5, rounds=3)
+        kname = "k_indexer_tile<true> (own threshold) + k_topk_final"
+        del idx_c
+    ix = {"bound": "mfma", "kernel": kname, "queries_per_launch": Qc,
           "achieved": round(flops / (t_ix * 1e-6) / 1e12, 1), "peak": peak / 1e12, "unit": "TFLOP/s",
           "frac": round(flops / (t_ix * 1e-6) / peak, 4), "traffic": None,
-          "alg_flop_per_launch": flops, "avg_launch_us": round(t_ix, 1),
+          "alg_flop_per_launch": flops, "avg_launch_us": round(t_ix, 1), "scores_only_kernel_us": round(t_scores, 1),
           "contraction": "MXFP4 block-scaled MFMA" if fp4 else "bf16 MFMA on E4M3 widened exactly (fp8 MFMA inexact)"}
     if not fp4:
         ix["frac_of_fp8_peak"] = round(flops / (t_ix * 1e-6) / FP8_PEAK, 4)

@@ -272,6 +272,24 @@ int csa_index_topk(const csa_dims* dims, const csa_cache* cache, const void* qI,
                    hipStream_t stream);
 
 /*
+ * csa_index_topk for queries laid out as a prefill chunk's are (every aligned group of 16
+ * queries belongs to one sequence, as for csa_index_scores_grouped; the caller guarantees
+ * it).  The selection is csa_index_topk's, index for index.  With E4M3 keys and 64 indexer
+ * heads the indexer shares key tiles among a group's queries and also takes each query's
+ * threshold itself: from a sample of the group's scores it keeps, per query, every score at
+ * or above the sample's r-th largest (r set for about 3072 of the row), and the selection
+ * runs on those lists (an upper set of the row, so they hold the top k whenever they number
+ * at least k; otherwise, or when they overflow, on the whole row).  This is the indexer and
+ * selection csa_forward runs on a chunk of such queries.  ws: as csa_index_topk
+ * (csa_workspace_size(INDEX_TOPK) covers both).
+ * Errors: as csa_index_topk.
+ */
+int csa_index_topk_grouped(const csa_dims* dims, const csa_cache* cache, const void* qI,
+                           const void* w, const int32_t* q_seq, const int32_t* q_pos, int32_t Q,
+                           int32_t* idx_out, void* scores_out, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/*
  * The indexer on its own (reading notes eq. 16): scores[q][s] for s < V of each query, in
  * float32 (bfloat16 with idx_fmt MXFP4, as in csa_index_topk), row stride ld (>= the largest V; cache->cap always works).  Entries s >= V are
  * left untouched.  csa_index_topk = csa_index_scores + csa_topk.

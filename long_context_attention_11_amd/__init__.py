@@ -20,7 +20,8 @@ __all__ = [
     "csa_workspace_size", "csa_compress", "csa_index_topk", "csa_attend", "csa_forward",
     "csa_index_scores", "csa_topk", "csa_topk_workspace_size", "ProjWeights", "csa_query_project",
     "csa_query_project_workspace_size", "csa_output_project", "csa_output_project_workspace_size",
-    "csa_forward_noalloc", "csa_noalloc_scratch_bytes", "csa_index_scores_grouped", "OP_COMPRESS", "OP_INDEX_TOPK", "OP_ATTEND", "OP_FORWARD",
+    "csa_forward_noalloc", "csa_noalloc_scratch_bytes", "csa_index_scores_grouped", "csa_index_topk_grouped",
+    "OP_COMPRESS", "OP_INDEX_TOPK", "OP_ATTEND", "OP_FORWARD",
     "FMT_F32", "FMT_BF16", "FMT_E4M3", "FMT_E4M3_BF16", "FMT_MXFP4", "FMT_MXFP4_BF16", "EXPORTED_SYMBOLS",
 ]
 
@@ -34,7 +35,7 @@ EXPORTED_SYMBOLS = (
     "csa_index_topk", "csa_attend", "csa_forward", "csa_index_scores", "csa_topk",
     "csa_topk_workspace_size", "csa_query_project", "csa_query_project_workspace_size",
     "csa_output_project", "csa_output_project_workspace_size", "csa_forward_noalloc",
-    "csa_noalloc_scratch_bytes", "csa_index_scores_grouped",
+    "csa_noalloc_scratch_bytes", "csa_index_scores_grouped", "csa_index_topk_grouped",
 )
 
 
@@ -109,6 +110,8 @@ def load():
     lib.csa_compress.argtypes = [dims_p, ctypes.POINTER(_Weights), ctypes.POINTER(_Cache), P, I32, P, P, SZ, P]
     lib.csa_index_topk.restype = ctypes.c_int
     lib.csa_index_topk.argtypes = [dims_p, ctypes.POINTER(_Cache), P, P, P, P, I32, P, P, P, SZ, P]
+    lib.csa_index_topk_grouped.restype = ctypes.c_int
+    lib.csa_index_topk_grouped.argtypes = [dims_p, ctypes.POINTER(_Cache), P, P, P, P, I32, P, P, P, SZ, P]
     lib.csa_index_scores.restype = ctypes.c_int
     lib.csa_index_scores.argtypes = [dims_p, ctypes.POINTER(_Cache), P, P, P, P, I32, P, ctypes.c_int64, P]
     lib.csa_index_scores_grouped.restype = ctypes.c_int
@@ -338,6 +341,17 @@ def csa_index_topk(dims: Dims, cache: Cache, qI, w, q_seq, q_pos, Q: int, idx_ou
     _check(load().csa_index_topk(ctypes.byref(dims.struct()), ctypes.byref(cache.struct()),
                                  _ptr(qI), _ptr(w), _ptr(q_seq), _ptr(q_pos), Q, _ptr(idx_out),
                                  _ptr(scores_out), wp, wn, _stream(stream)))
+
+
+def csa_index_topk_grouped(dims: Dims, cache: Cache, qI, w, q_seq, q_pos, Q: int, idx_out,
+                           scores_out=None, ws=None, stream=None):
+    """csa_index_topk for a prefill chunk's query layout (aligned groups of 16 queries of one
+    sequence)."""
+    _check_scores(dims, scores_out)
+    wp, wn = _ws(ws)
+    _check(load().csa_index_topk_grouped(ctypes.byref(dims.struct()), ctypes.byref(cache.struct()),
+                                         _ptr(qI), _ptr(w), _ptr(q_seq), _ptr(q_pos), Q, _ptr(idx_out),
+                                         _ptr(scores_out), wp, wn, _stream(stream)))
 
 
 def csa_index_scores(dims: Dims, cache: Cache, qI, w, q_seq, q_pos, Q: int, scores, ld: int,

@@ -130,9 +130,11 @@ size_t compress_ws(const csa_dims& d, int32_t B, int32_t T) {
   return (size_t)(ks + (ks > 1 ? 1 : 0)) * M * state_width(d) * sizeof(float);
 }
 
-// scores [q][cap] + top-k candidates for `Qc` queries
+// scores [q][cap] + top-k candidates for `Qc` queries (through the top-k passes, or lists the
+// prefill indexer fills itself)
 size_t index_ws(const csa_dims& d, int32_t Qc, int32_t cap) {
-  return align_up((size_t)Qc * cap * sizeof(float), 256) + topk_workspace_bytes(d, Qc, cap);
+  return align_up((size_t)Qc * cap * sizeof(float), 256) +
+         std::max(topk_workspace_bytes(d, Qc, cap), indexer_cand_bytes(d, Qc, cap));
 }
 
 // The same through the threshold + final passes, whose launches carry a one-token step.
@@ -275,6 +277,18 @@ static int index_topk_impl(const csa_dims& d, const csa_cache& c, const void* qI
     return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "index_topk needs " + std::to_string(need) + " bytes of workspace");
   void* scores = scores_out ? scores_out : ws;
   void* tws = (char*)ws + sc_bytes;
+  if (tiled && !step && !fold && indexer_cand_applies(d, Q)) {
+    // the prefill indexer thresholds its own scores; the final selection reads its lists
+    if (!ws || sc_bytes + indexer_cand_bytes(d, Q, c.cap) > ws_bytes)
+      return fail(CSA_ERR_WORKSPACE_TOO_SMALL, "index_topk needs " + std::to_string(sc_bytes + indexer_cand_bytes(d, Q, c.cap)) +
+                                                   " bytes of workspace");
+    CandLists cl;
+    hipError_t e = launch_indexer_cand(d, c, qI, w, q_seq, q_pos, Q, (float*)scores, c.cap, tws, &cl, stream);
+    if (e != hipSuccess) return hip_fail(e, "indexer launch");
+    e = launch_topk_final_lists(d, c, Q, (const float*)scores, c.cap, cl, idx_out, stream);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    return CSA_OK;
+  }
   hipError_t e = launch_indexer(d, c, qI, w, q_seq, q_pos, Q, scores, c.cap, tiled, stream);
   if (e != hipSuccess) return hip_fail(e, "indexer launch");
   e = launch_topk(d, c, q_seq, q_pos, Q, scores, c.cap, idx_out, tws, stream, step, fold);
@@ -282,9 +296,9 @@ static int index_topk_impl(const csa_dims& d, const csa_cache& c, const void* qI
   return CSA_OK;
 }
 
-int csa_index_topk(const csa_dims* dims, const csa_cache* cache, const void* qI, const void* w,
-                   const int32_t* q_seq, const int32_t* q_pos, int32_t Q, int32_t* idx_out,
-                   void* scores_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+static int index_topk_entry(const csa_dims* dims, const csa_cache* cache, const void* qI, const void* w,
+                            const int32_t* q_seq, const int32_t* q_pos, int32_t Q, int32_t* idx_out,
+                            void* scores_out, void* ws, size_t ws_bytes, bool grouped, hipStream_t stream) {
   g_last_error.clear();
   int st = check_dims(dims);
   if (st) return st;
@@ -298,7 +312,19 @@ int csa_index_topk(const csa_dims* dims, const csa_cache* cache, const void* qI,
     return fail(CSA_ERR_UNSUPPORTED, "cap exceeds the entries the top-k kernels handle for this top_k (" +
                                          std::to_string(topk_max_visible(d)) + ")");
   return index_topk_impl(d, *cache, qI, w, q_seq, q_pos, Q, idx_out, scores_out, ws, ws_bytes,
-                         false, stream);
+                         grouped, stream);
+}
+
+int csa_index_topk(const csa_dims* dims, const csa_cache* cache, const void* qI, const void* w,
+                   const int32_t* q_seq, const int32_t* q_pos, int32_t Q, int32_t* idx_out,
+                   void* scores_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return index_topk_entry(dims, cache, qI, w, q_seq, q_pos, Q, idx_out, scores_out, ws, ws_bytes, false, stream);
+}
+
+int csa_index_topk_grouped(const csa_dims* dims, const csa_cache* cache, const void* qI, const void* w,
+                           const int32_t* q_seq, const int32_t* q_pos, int32_t Q, int32_t* idx_out,
+                           void* scores_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return index_topk_entry(dims, cache, qI, w, q_seq, q_pos, Q, idx_out, scores_out, ws, ws_bytes, true, stream);
 }
 
 int csa_index_scores(const csa_dims* dims, const csa_cache* cache, const void* qI, const void* w,

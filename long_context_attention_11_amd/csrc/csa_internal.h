@@ -266,6 +266,32 @@ hipError_t launch_state_update(const csa_dims& d, const csa_cache& c, int32_t T,
 hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
                           const int32_t* q_seq, const int32_t* q_pos, int32_t Q, void* scores,
                           int64_t ld_scores, bool tiled, hipStream_t s);
+// Candidates the final top-k selection holds: a query whose candidate lists total more (or
+// fewer than k) is selected from its whole score row instead.
+constexpr int TOPK_FINAL_CAND = 8192;
+
+// A query's candidate lists, one per segment of its row (entries at or above one threshold,
+// in index order), as the final top-k selection reads them.
+struct CandLists {
+  int32_t* idx;   // [Q][nseg][cs] entry indices
+  uint32_t* key;  // [Q][nseg][cs] their order-preserving score keys
+  int32_t* cnt;   // [Q][nseg] entries that passed (more than cs: the list overflowed)
+  int32_t* vis;   // [Q] the visible count each query was scored with
+  int nseg, cs;
+};
+// The prefill indexer that thresholds its own scores (tiled, E4M3 keys, 64 heads): every
+// visible score goes to `scores` (row stride ld) as with launch_indexer, and the entries at or
+// above a per-query threshold to candidate lists in ws (indexer_cand_bytes), described in
+// *cl; the final selection then needs no threshold pass.
+bool indexer_cand_applies(const csa_dims& d, int32_t Q);
+size_t indexer_cand_bytes(const csa_dims& d, int32_t Q, int32_t cap);
+hipError_t launch_indexer_cand(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
+                               const int32_t* q_seq, const int32_t* q_pos, int32_t Q, float* scores,
+                               int64_t ld_scores, void* ws, CandLists* cl, hipStream_t s);
+// The final top-k selection from such lists (float32 scores).
+hipError_t launch_topk_final_lists(const csa_dims& d, const csa_cache& c, int32_t Q,
+                                   const float* scores, int64_t ld_scores, const CandLists& cl,
+                                   int32_t* idx, hipStream_t s);
 // Rows longer than one top-k segment (topk_can_carry) can take the threshold + final passes,
 // whose launches carry other work: with step non-null (only where topk_can_carry_step allows
 // it) the threshold pass also runs that one-token projection step, and with fold non-null the

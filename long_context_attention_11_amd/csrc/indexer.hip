@@ -439,27 +439,54 @@ constexpr int IT_Q = 16;        // queries per workgroup
 constexpr int IT_STAGE = 256;   // entries per LDS stage (one barrier per 16 tiles)
 constexpr int IT_LD = 272;      // LDS bytes per entry row: 128 dims in bf16 + 16 pad (spreads the banks)
 
+// With CAND the kernel also thresholds its own scores: before the main pass it scores a
+// sample of IT_SMP entries shared by the tile's queries (IT_SMP_RUNS evenly spaced runs of 64
+// below the smallest visible count of the tile), writes those scores to their places in the
+// rows, reads each query's sample back and takes its r-th largest, r chosen so that about
+// IT_TARGET of the row's V scores are expected at or above it (every score passes when
+// V <= TOPK_FINAL_CAND).  The main pass then appends, besides storing every score, the
+// entries at or above the threshold to the query's list for this workgroup's segment of the
+// row (wave ballots, index order).  The lists of all segments hold every score at or above one
+// threshold, an upper set of the row, so when they hold at least k entries they hold the top k.
+constexpr int IT_SMP_RUNS = 16, IT_SMP = IT_SMP_RUNS * 64;
+constexpr int IT_TARGET = 3072;
+constexpr int IT_STAGE_CAND = 128;   // the thresholding kernel's stage (its registers fit no larger)
+
+template <bool CAND, int STG>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_indexer_tile(
     const uint8_t* __restrict__ qI, const uint16_t* __restrict__ wI,
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int Q,
     const uint8_t* __restrict__ ki, RowMap rm, const int32_t* __restrict__ n_entries, int m,
-    float* __restrict__ scores, int64_t ld, int chunk) {
+    float* __restrict__ scores, int64_t ld, int chunk, CandLists cl) {
   constexpr int NH = 64, HT = NH / 16;
-  __shared__ __align__(16) uint8_t kbuf[2][IT_STAGE * IT_LD];
+  static_assert(IT_SMP % STG == 0, "the sample is whole stages");
+  __shared__ __align__(16) uint8_t kbuf[2][STG * IT_LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int qt0 = blockIdx.x * IT_Q;
   const int seq = q_seq ? q_seq[qt0] : qt0;
   const int nent = n_entries[seq];
-  // visible entries of the tile's queries (clamped duplicates past Q store nothing)
-  int Vmax = 0;
+  // visible entries of the tile's queries (clamped duplicates past Q store nothing); the
+  // smallest and largest over the real ones
+  int Vmax = 0, Vmin = 0x7fffffff;
   for (int i = 0; i < IT_Q; ++i) {
     const int q = min(qt0 + i, Q - 1);
-    Vmax = max(Vmax, max(0, min(q_pos[q] / m, nent)));
+    const int v = max(0, min(q_pos[q] / m, nent));
+    Vmax = max(Vmax, v);
+    if (qt0 + i < Q) Vmin = min(Vmin, v);
   }
-  const int e_lo = blockIdx.y * chunk;
+  const int seg = blockIdx.y, nseg = gridDim.y;
+  if constexpr (CAND) {
+    if (seg == 0 && tid < IT_Q && qt0 + tid < Q) cl.vis[qt0 + tid] = max(0, min(q_pos[qt0 + tid] / m, nent));
+  }
+  const int e_lo = seg * chunk;
   const int e_hi = min(e_lo + chunk, Vmax);
-  if (e_lo >= e_hi) return;  // uniform over the workgroup
+  if (e_lo >= e_hi) {  // uniform over the workgroup
+    if constexpr (CAND) {
+      if (tid < IT_Q && qt0 + tid < Q) cl.cnt[(size_t)(qt0 + tid) * nseg + seg] = 0;
+    }
+    return;
+  }
 
   int V[2];
   bf16x8 A[2][HT][4];
@@ -485,13 +512,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // stage loader: thread t moves dims 8p .. 8p+7 and 64+8p .. 64+8p+7 (p = t % 8) of entry
   // t / 8 of the stage, widened to bf16; the 8 threads of an entry write two contiguous
   // 128-byte runs, which keeps the LDS writes free of bank conflicts
-  // (a paged cache costs one block-table read per entry, hidden behind a stage of MFMAs)
+  // (a paged cache costs one block-table read per entry, hidden behind a stage of MFMAs).
+  // entry_of maps a position in the pass (st * STG + ...) to the entry it scores.
   const int le = tid >> 3, lp = (tid & 7) * 8;
-  constexpr int RPT = IT_STAGE / 64;  // entries per thread per stage
-  auto gload = [&](int st, uint4 (&v)[RPT]) {
+  constexpr int RPT = STG / 64;  // entries per thread per stage
+  auto gload = [&](auto entry_of, int st, uint4 (&v)[RPT]) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-      const int e = min(e_lo + st * IT_STAGE + 64 * r + le, e_hi - 1);
+      const int e = entry_of(st * STG + 64 * r + le);
       const uint8_t* src = ki + row_of(rm, seq, e) * IX_CI + lp;
       const uint2 a = *reinterpret_cast<const uint2*>(src);
       const uint2 b = *reinterpret_cast<const uint2*>(src + 64);
@@ -511,75 +539,166 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       *reinterpret_cast<uint4*>(dst + 128) = make_uint4(b[4], b[5], b[6], b[7]);
     }
   };
-  const int nst = (e_hi - e_lo + IT_STAGE - 1) / IT_STAGE;
-  uint4 nxt[RPT];
-  gload(0, nxt);
-  lstore(0, nxt);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    if (st + 1 < nst) gload(st + 1, nxt);
+  // Scores of the 64 entries of one sub-stage (kb) for this wave's two queries: lane (col, g)
+  // receives entry 16 g + col's.
+  auto score_sub = [&](const uint8_t* kb, float (&tot)[2]) {
+    // per lane partial head sums: part[t][qq] for tile t of the sub-stage, query qq (the
+    // lane's 4 heads of each head tile); reduced over the 4 lane groups once per 64 entries
+    float part[4][2];
 #pragma unroll
-    for (int sub = 0; sub < RPT; ++sub) {
-      const uint8_t* kb = kbuf[st & 1] + sub * 64 * IT_LD;
-      // per lane partial head sums: part[t][qq] for tile t of the stage, query qq (the lane's
-      // 4 heads of each head tile); reduced over the 4 lane groups once per 64 entries
-      float part[4][2];
+    for (int t = 0; t < 4; ++t) {
+      // dims g*32 + ks*8 .. +7 (the mapping e4m3x32_to_ops gives the q^I operands)
+      const uint8_t* row = kb + (t * 16 + col) * IT_LD + g * 64;
+      bf16x8 Bop[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        // dims g*32 + ks*8 .. +7 (the mapping e4m3x32_to_ops gives the q^I operands)
-        const uint8_t* row = kb + (t * 16 + col) * IT_LD + g * 64;
-        bf16x8 Bop[4];
+      for (int ks = 0; ks < 4; ++ks) Bop[ks] = *reinterpret_cast<const bf16x8*>(row + 16 * ks);
+      // K-step outermost: the 8 accumulators are independent, so consecutive MFMAs never
+      // wait on each other's results
+      f32x4 acc[2][HT];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) Bop[ks] = *reinterpret_cast<const bf16x8*>(row + 16 * ks);
-        // K-step outermost: the 8 accumulators are independent, so consecutive MFMAs never
-        // wait on each other's results
-        f32x4 acc[2][HT];
+      for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) acc[qq][ht] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht) acc[qq][ht] = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht)
-              acc[qq][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[qq][ht][ks], Bop[ks], acc[qq][ht], 0, 0, 0);
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-          float p = 0.f;
-#pragma unroll
           for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) p = fmaf(W[qq][ht][e], relu(acc[qq][ht][e]), p);
-          part[t][qq] = p;
-        }
-      }
-      // Reduce-scatter over the lane groups g = lane >> 4: after the exchange with lane ^ 32
-      // a lane keeps tiles {0,1} (g < 2) or {2,3}; after lane ^ 16 it keeps tile g.  Lane
-      // (col, g) then holds entry t*16 + col of tile t = g, summed over all 64 heads, and the
-      // 64 lanes store one contiguous run of 64 scores per query.
-      const bool hi2 = g >= 2, odd = g & 1;
-      float r1[2][2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-          const float keep = hi2 ? part[2 + j][qq] : part[j][qq];
-          const float send = hi2 ? part[j][qq] : part[2 + j][qq];
-          r1[j][qq] = keep + lane_xor32(send);
-        }
-      const int s = e_lo + st * IT_STAGE + sub * 64 + g * 16 + col;
+            acc[qq][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[qq][ht][ks], Bop[ks], acc[qq][ht], 0, 0, 0);
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
-        const float keep = odd ? r1[1][qq] : r1[0][qq];
-        const float send = odd ? r1[0][qq] : r1[1][qq];
-        const float total = keep + lane_xor16(send);
-        if (s < min(V[qq], e_hi)) scores[(size_t)(qt0 + 2 * wave + qq) * ld + s] = total;
+        float p = 0.f;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p = fmaf(W[qq][ht][e], relu(acc[qq][ht][e]), p);
+        part[t][qq] = p;
+      }
+    }
+    // Reduce-scatter over the lane groups g = lane >> 4: after the exchange with lane ^ 32
+    // a lane keeps tiles {0,1} (g < 2) or {2,3}; after lane ^ 16 it keeps tile g.  Lane
+    // (col, g) then holds entry t*16 + col of tile t = g, summed over all 64 heads.
+    const bool hi2 = g >= 2, odd = g & 1;
+    float r1[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const float keep = hi2 ? part[2 + j][qq] : part[j][qq];
+        const float send = hi2 ? part[j][qq] : part[2 + j][qq];
+        r1[j][qq] = keep + lane_xor32(send);
+      }
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const float keep = odd ? r1[1][qq] : r1[0][qq];
+      const float send = odd ? r1[0][qq] : r1[1][qq];
+      tot[qq] = keep + lane_xor16(send);
+    }
+  };
+  uint4 nxt[RPT];
+  auto main_entry = [&](int v) { return min(e_lo + v, e_hi - 1); };
+
+  // ---- CAND: the sample and the thresholds (thr = 0 takes every score)
+  uint32_t thr[2] = {0u, 0u};
+  int ccount[2] = {0, 0};
+  if constexpr (CAND) {
+    int vbig = 0;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) vbig = max(vbig, V[qq]);
+    const bool need = __syncthreads_or(vbig > TOPK_FINAL_CAND) != 0;
+    const int span = max(Vmin - 64, 0);
+    auto sample_entry = [&](int v) {
+      return min((int)((int64_t)(v >> 6) * span / (IT_SMP_RUNS - 1)) + (v & 63), Vmax - 1);
+    };
+    if (need) {   // uniform
+      gload(sample_entry, 0, nxt);
+      lstore(0, nxt);
+      __syncthreads();
+      for (int st = 0; st < IT_SMP / STG; ++st) {
+        if (st + 1 < IT_SMP / STG) gload(sample_entry, st + 1, nxt);
+#pragma unroll
+        for (int sub = 0; sub < RPT; ++sub) {
+          float tot[2];
+          score_sub(kbuf[st & 1] + sub * 64 * IT_LD, tot);
+          // the sample scores go to their places in the rows (the main pass stores the same
+          // values there again), from where this wave reads them back
+          const int e = sample_entry(st * STG + sub * 64 + g * 16 + col);
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq)
+            if (qt0 + 2 * wave + qq < Q) scores[(size_t)(qt0 + 2 * wave + qq) * ld + e] = tot[qq];
+        }
+        if (st + 1 < IT_SMP / STG) lstore((st + 1) & 1, nxt);
+        __syncthreads();
+      }
+      // the wave's own stores are complete and visible to its lanes before they are read back
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const int q = qt0 + 2 * wave + qq;
+        if (V[qq] <= TOPK_FINAL_CAND) continue;   // uniform: every score passes
+        uint32_t kk[IT_SMP / 64];
+#pragma unroll
+        for (int i = 0; i < IT_SMP / 64; ++i) kk[i] = score_key(scores[(size_t)q * ld + sample_entry(lane + 64 * i)]);
+        const int r = min(IT_SMP, max(1, (int)(((int64_t)IT_TARGET * IT_SMP + V[qq] - 1) / V[qq])));
+        // the largest key t with at least r sample keys >= t: the sample's r-th largest
+        uint32_t lo = 0u, hi = 0xffffffffu;
+        while (lo < hi) {   // uniform
+          const uint32_t mid = lo + ((hi - lo) >> 1) + 1u;
+          int cnt = 0;
+#pragma unroll
+          for (int i = 0; i < IT_SMP / 64; ++i) cnt += __popcll(__ballot(kk[i] >= mid));
+          if (cnt >= r) lo = mid;
+          else hi = mid - 1u;
+        }
+        thr[qq] = __builtin_amdgcn_readfirstlane(lo);
+      }
+    }
+  }
+
+  // ---- main pass over the segment's entries
+  const int nst = (e_hi - e_lo + STG - 1) / STG;
+  gload(main_entry, 0, nxt);
+  lstore(0, nxt);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    if (st + 1 < nst) gload(main_entry, st + 1, nxt);
+#pragma unroll
+    for (int sub = 0; sub < RPT; ++sub) {
+      float tot[2];
+      score_sub(kbuf[st & 1] + sub * 64 * IT_LD, tot);
+      // the 64 lanes store one contiguous run of 64 scores per query
+      const int s = e_lo + st * STG + sub * 64 + g * 16 + col;
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const bool vis = s < min(V[qq], e_hi);
+        if (vis) scores[(size_t)(qt0 + 2 * wave + qq) * ld + s] = tot[qq];
+        if constexpr (CAND) {
+          const uint32_t key = score_key(tot[qq]);
+          const bool pass = vis && key >= thr[qq];
+          const uint64_t bal = __ballot(pass);
+          if (pass) {
+            const int pos = ccount[qq] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (pos < cl.cs) {
+              const size_t at = ((size_t)(qt0 + 2 * wave + qq) * nseg + seg) * cl.cs + pos;
+              cl.idx[at] = s;
+              cl.key[at] = key;
+            }
+          }
+          ccount[qq] = __builtin_amdgcn_readfirstlane(ccount[qq] + (int)__popcll(bal));
+        }
       }
     }
     if (st + 1 < nst) lstore((st + 1) & 1, nxt);
     __syncthreads();
+  }
+  if constexpr (CAND) {
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+      if (lane == 0 && qt0 + 2 * wave + qq < Q) cl.cnt[(size_t)(qt0 + 2 * wave + qq) * nseg + seg] = ccount[qq];
   }
 }
 
@@ -765,6 +884,59 @@ __global__ __launch_bounds__(256) void k_indexer_f32(
 
 }  // namespace
 
+// The tiled launch shape: nsplit workgroups per group of IT_Q queries (about one workgroup
+// per CU overall), each scoring a chunk of the row (a multiple of the stage).
+static void tile_shape(int32_t Q, int32_t cap, int stage, int* chunk, int* nchunk) {
+  const int ntile = (Q + IT_Q - 1) / IT_Q;
+  const int nsplit = std::max(1, (256 + ntile - 1) / ntile);
+  int ch = (cap + nsplit - 1) / nsplit;
+  ch = (ch + stage - 1) / stage * stage;
+  *chunk = ch;
+  *nchunk = (cap + ch - 1) / ch;
+}
+
+// Candidate-list capacity per segment: the final pass holds TOPK_FINAL_CAND candidates in all;
+// each segment's list takes up to four times its even share (at least 1024).
+static int cand_cs(int nseg) {
+  return std::min(TOPK_FINAL_CAND, std::max(1024, 4 * TOPK_FINAL_CAND / nseg));
+}
+
+bool indexer_cand_applies(const csa_dims& d, int32_t Q) {
+  return d.idx_fmt == CSA_FMT_E4M3 && d.n_hI == 64 && d.c_I == IX_CI && Q >= IT_Q;
+}
+
+size_t indexer_cand_bytes(const csa_dims& d, int32_t Q, int32_t cap) {
+  if (!indexer_cand_applies(d, Q)) return 0;
+  int chunk, nseg;
+  tile_shape(Q, cap, IT_STAGE_CAND, &chunk, &nseg);
+  const size_t n = (size_t)Q * nseg;
+  const size_t list = ((n * cand_cs(nseg) * 4) + 255) / 256 * 256;
+  return 2 * list + (n * 4 + 255) / 256 * 256 + ((size_t)Q * 4 + 255) / 256 * 256;
+}
+
+hipError_t launch_indexer_cand(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
+                               const int32_t* q_seq, const int32_t* q_pos, int32_t Q, float* scores,
+                               int64_t ld, void* ws, CandLists* cl, hipStream_t s) {
+  if (!indexer_cand_applies(d, Q)) return hipErrorInvalidValue;
+  int chunk, nseg;
+  tile_shape(Q, c.cap, IT_STAGE_CAND, &chunk, &nseg);
+  const int cs = cand_cs(nseg);
+  const size_t n = (size_t)Q * nseg;
+  const size_t list = ((n * cs * 4) + 255) / 256 * 256;
+  char* p = static_cast<char*>(ws);
+  cl->idx = reinterpret_cast<int32_t*>(p);
+  cl->key = reinterpret_cast<uint32_t*>(p + list);
+  cl->cnt = reinterpret_cast<int32_t*>(p + 2 * list);
+  cl->vis = reinterpret_cast<int32_t*>(p + 2 * list + (n * 4 + 255) / 256 * 256);
+  cl->nseg = nseg;
+  cl->cs = cs;
+  const dim3 grid((Q + IT_Q - 1) / IT_Q, nseg);
+  hipLaunchKernelGGL((k_indexer_tile<true, IT_STAGE_CAND>), grid, dim3(512), 0, s, (const uint8_t*)qI, (const uint16_t*)w,
+                     q_seq, q_pos, Q, (const uint8_t*)c.ki, row_map(d, c), c.n_entries, d.m, scores, ld,
+                     chunk, *cl);
+  return hipGetLastError();
+}
+
 hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI, const void* w,
                           const int32_t* q_seq, const int32_t* q_pos, int32_t Q, void* scores,
                           int64_t ld, bool tiled, hipStream_t s) {
@@ -772,20 +944,17 @@ hipError_t launch_indexer(const csa_dims& d, const csa_cache& c, const void* qI,
   const RowMap rm = row_map(d, c);
   if (tiled && (fp4 || d.idx_fmt == CSA_FMT_E4M3) && d.n_hI == 64 && Q >= IT_Q) {
     // every aligned group of IT_Q queries belongs to one sequence (the caller guarantees it)
-    const int ntile = (Q + IT_Q - 1) / IT_Q;
-    const int nsplit = std::max(1, (256 + ntile - 1) / ntile);
-    const int stage = fp4 ? IF_STAGE : IT_STAGE;
-    int chunk = (c.cap + nsplit - 1) / nsplit;
-    chunk = (chunk + stage - 1) / stage * stage;
-    dim3 grid(ntile, (c.cap + chunk - 1) / chunk);
+    int chunk, nchunk;
+    tile_shape(Q, c.cap, fp4 ? IF_STAGE : IT_STAGE, &chunk, &nchunk);
+    dim3 grid((Q + IT_Q - 1) / IT_Q, nchunk);
     if (fp4)
       hipLaunchKernelGGL(k_indexer_tile_fp4, grid, dim3(512), 0, s, (const uint8_t*)qI,
                          (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki, rm,
                          c.n_entries, d.m, static_cast<uint16_t*>(scores), ld, chunk);
     else
-      hipLaunchKernelGGL(k_indexer_tile, grid, dim3(512), 0, s, (const uint8_t*)qI,
+      hipLaunchKernelGGL((k_indexer_tile<false, IT_STAGE>), grid, dim3(512), 0, s, (const uint8_t*)qI,
                          (const uint16_t*)w, q_seq, q_pos, Q, (const uint8_t*)c.ki, rm,
-                         c.n_entries, d.m, static_cast<float*>(scores), ld, chunk);
+                         c.n_entries, d.m, static_cast<float*>(scores), ld, chunk, CandLists{});
     return hipGetLastError();
   }
   if (d.idx_fmt == CSA_FMT_F32) {

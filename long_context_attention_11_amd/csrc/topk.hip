@@ -42,7 +42,7 @@ constexpr int TK_WAVES = TK_THREADS / 64;
 constexpr int TK_BINS = 2048;
 constexpr int TK_SEG = 8192;     // scores per segment (E = 8)
 constexpr int TK_NS = 4096;      // threshold sample (4 per thread)
-constexpr int TK_FINAL = 8192;   // candidates the final pass holds (E = 8)
+constexpr int TK_FINAL = TOPK_FINAL_CAND;   // candidates the final pass holds (E = 8)
 constexpr int TK_MAXSEG = 1024;  // segments per row
 constexpr int TK_ROW_MAX = 65536; // rows up to this long: one workgroup per query, one launch
 constexpr int TK_MAXK = 4096;
@@ -924,6 +924,16 @@ hipError_t launch_topk_t(const csa_dims& d, const csa_cache& c, const int32_t* q
   } else {
     hipLaunchKernelGGL(k_topk_final<BF>, dim3(Q), dim3(TK_THREADS), 0, s, fin);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_final_lists(const csa_dims& d, const csa_cache& c, int32_t Q,
+                                   const float* scores, int64_t ld, const CandLists& cl,
+                                   int32_t* idx, hipStream_t s) {
+  if (cl.nseg < 1 || cl.nseg > TK_MAXSEG || d.top_k > TK_MAXK) return hipErrorInvalidValue;
+  const FinalArgs fin{scores, ld, nullptr, nullptr, c.n_entries, d.m, d.top_k, cl.nseg, cl.cs,
+                      cl.idx, cl.key, cl.cnt, cl.vis, idx};
+  hipLaunchKernelGGL(k_topk_final<false>, dim3(Q), dim3(TK_THREADS), 0, s, fin);
   return hipGetLastError();
 }
 

@@ -79,6 +79,10 @@ int main() {
   EXPECT(csa_compress(&d2, nullptr, &c, fake, 4, (const int32_t*)fake, fake, 1 << 30, nullptr) == CSA_ERR_INVALID_ARGUMENT);
   EXPECT(csa_index_topk(&d2, &c, fake, fake, (const int32_t*)fake, (const int32_t*)fake, 0, (int32_t*)fake, nullptr,
                         fake, 1 << 30, nullptr) == CSA_ERR_INVALID_ARGUMENT);
+  EXPECT(csa_index_topk_grouped(&d2, &c, fake, fake, (const int32_t*)fake, (const int32_t*)fake, 0, (int32_t*)fake,
+                                nullptr, fake, 1 << 30, nullptr) == CSA_ERR_INVALID_ARGUMENT);
+  EXPECT(csa_index_topk_grouped(&d2, &c, fake, fake, (const int32_t*)fake, (const int32_t*)fake, 16, (int32_t*)fake,
+                                nullptr, fake, 16, nullptr) == CSA_ERR_WORKSPACE_TOO_SMALL);
   EXPECT(csa_index_scores(&d2, &c, fake, fake, (const int32_t*)fake, (const int32_t*)fake, 1, fake, 8, nullptr) ==
          CSA_ERR_INVALID_ARGUMENT);
   EXPECT(csa_index_scores_grouped(&d2, &c, fake, fake, (const int32_t*)fake, (const int32_t*)fake, 1, fake, 8,

@@ -622,7 +622,8 @@ def _prefill_sample(T, m, seed=0):
     return sorted(set(first + last + at0 + at3 + rng.choice(rest, 128, replace=False).tolist()))
 
 
-@pytest.mark.parametrize("name,idx_fmt", [("c4a", "e4m3"), ("c4a", "mxfp4"), ("c4b", "e4m3")])
+@pytest.mark.parametrize("name,idx_fmt", [("c4a", "e4m3"), ("c4a", "mxfp4"), ("c4b", "e4m3"), ("mid", "e4m3"),
+                                           ("mid_ties", "e4m3")])
 def test_c4_prefill_full_size_sampled(name, idx_fmt):
     """Flash chunked prefill at full size: a 32768-token chunk after a 1048576-token prefix
     (c4a: 262144 entries) or a 262144-token prefix (c4b: 65536 entries).  The prefix cache,
@@ -630,8 +631,15 @@ def test_c4_prefill_full_size_sampled(name, idx_fmt):
     given to both sides; csa_forward compresses the chunk (8192 new entries), scores every
     query against all visible entries, selects 512 and attends.  256 stratified query rows of
     the chunk are checked against the oracle, which folds the chunk's entries from the same
-    hidden states; every new entry and key is checked.  Indexer keys in E4M3 or MXFP4."""
-    cfg = dict(synth.config(name), idx_fmt=idx_fmt)
+    hidden states; every new entry and key is checked.  Indexer keys in E4M3 or MXFP4.
+    mid: a 256-token chunk after a 48000-token prefix (about 12000 visible entries, every row
+    checked), where the prefill indexer's own threshold splits each row over 16 segments;
+    mid_ties: the same with every prefix key equal, so that every query's prefix scores tie
+    at the threshold and the candidates overflow into the whole-row selection."""
+    base = {"mid": "c4b", "mid_ties": "c4b"}.get(name, name)
+    cfg = dict(synth.config(base), idx_fmt=idx_fmt)
+    if base != name:
+        cfg.update(prefix=48000, T=256)
     dims = L.Dims.from_config(cfg)
     od = oracle_dims(cfg)
     m, k, T, p0 = cfg["m"], cfg["top_k"], cfg["T"], cfg["prefix"]
@@ -642,6 +650,8 @@ def test_c4_prefill_full_size_sampled(name, idx_fmt):
     dims, cache, _, _, _, _ = _synthetic_decode_setup(cfg, 1, cap, R_win, taus0, seed=41,
                                                       n_entries=[N0])
     cache.state.zero_()
+    if name == "mid_ties":
+        cache.ki[0, :N0] = cache.ki[0, :1].clone()
     W = synth.weights(cfg, seed=41, device=DEV)
     H = synth.hidden(cfg, 0, p0, p0 + T, seed=41, device=DEV)
     qs = synth.queries(cfg, T, seed=41, device=DEV, tag="prefill")
@@ -768,6 +778,36 @@ def test_topk_exact_on_crafted_scores(fmt):
             got = gi[i][gi[i] >= 0]
             assert np.array_equal(got, ref), f"k={k} cap={cap} V={V} kind={i % 5}"
             assert np.all(gi[i][len(got):] == -1)
+
+
+@pytest.mark.parametrize("N,taus", [(20000, "mixed"), (5003, "short"), (70000, "long")])
+def test_index_topk_grouped_equals_ungrouped(N, taus):
+    """csa_index_topk_grouped (the prefill indexer that thresholds its own scores, then the
+    selection from its lists) selects exactly what csa_index_topk does, with the same scores:
+    two sequences of 48 queries each (3 groups of 16), positions consecutive within a
+    sequence; visible counts below and above the threshold's 8192 (every score a candidate,
+    or a sampled threshold), rows split over several segments."""
+    cfg = _qcfg()
+    dims = L.Dims.from_config(cfg)
+    m, k = cfg["m"], cfg["top_k"]
+    start = {"mixed": [4 * 6000, 4 * 19000], "short": [4 * 3000, 4 * 4900], "long": [4 * 60000, 4 * 69000]}[taus]
+    Qs = 48
+    pos = [s0 + t for s0 in start for t in range(Qs)]
+    seqs = [b for b in range(2) for _ in range(Qs)]
+    dims, cache, qs, W, q_seq, q_pos = _synthetic_decode_setup(cfg, 2, N, 128, list(zip(seqs, pos)), seed=17)
+    Q = len(pos)
+    out = []
+    for fn in (L.csa_index_topk, L.csa_index_topk_grouped):
+        idx = torch.full((Q, k), -7, dtype=torch.int32, device=DEV)
+        sc = torch.zeros((Q, N), dtype=torch.float32, device=DEV)
+        ws = _ws(L.csa_workspace_size(dims, L.OP_INDEX_TOPK, Q=Q, cap=N))
+        fn(dims, cache, qs["qI"], qs["w"], q_seq, q_pos, Q, idx, sc, ws)
+        torch.cuda.synchronize()
+        out.append((idx.cpu(), sc.cpu()))
+    for i in range(Q):
+        V = R.visible_entries(pos[i], m, N)
+        assert torch.equal(out[0][1][i, :V], out[1][1][i, :V]), f"scores row {i}"
+        assert torch.equal(out[0][0][i], out[1][0][i]), f"selection row {i} (V={V})"
 
 
 @pytest.mark.parametrize("fmt", ["f32", "bf16"])
