@@ -480,6 +480,14 @@ def run_decode(args, cfg):
     # per-kernel launch durations (same inputs and grids, rotating cache copies)
     kt = {name: kernel_time_us([lambda c=c, f=f: f(c) for c in caches])
           for name, f in zip(["compress", "index_scores", "topk", "attend"] if has_idx else ["compress", "attend"], phases)}
+    if has_idx:
+        # scoring and selection in one call: the indexer, the threshold pass and the final
+        # selection, the same kernels as in the step but without the projection and the fold
+        ws_it = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_INDEX_TOPK, Q=B, cap=N)), dtype=torch.uint8,
+                            device=dev)
+        kt["index_topk"] = kernel_time_us([lambda c=c: L.csa_index_topk(dims, c, qs["qI"], qs["w"], q_seq, q_pos, B,
+                                                                         idx, None, ws_it) for c in caches])
+        del ws_it
     if args.layer:
         kt["q_proj"] = kernel_time_us([lambda c=c: k_qproj(c) for c in caches])
         kt["o_proj"] = kernel_time_us([lambda c=c: k_oproj(c) for c in caches])
@@ -506,7 +514,9 @@ def run_decode(args, cfg):
                            "achieved": round(alg / dur / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                            "frac": round(alg / dur / HBM_PEAK, 4),
                            "traffic": measured_traffic() if cfg["name"] == "c2" and not paged else None,
-                           "alg_bytes_per_launch": alg, "avg_launch_us": round(kt["index_scores"], 2)}
+                           "alg_bytes_per_launch": alg, "avg_launch_us": round(kt["index_scores"], 2),
+                           "with_selection": {"call": "csa_index_topk", "avg_us": round(kt["index_topk"], 2),
+                                              "frac_including_selection": round(alg / (kt["index_topk"] * 1e-6) / HBM_PEAK, 4)}}
     else:
         rows = N + cfg["n_win"]
         alg = B * (rows * 576 + 2 * 2 * cfg["n_h"] * cfg["c"])
