@@ -39,6 +39,21 @@ struct FoldArgs {
   int32_t* n_entries;
 };
 
+// The PU_SLICES partial sums of a one-token projection at p (slice stride `stride` floats),
+// added in slice order.  All loads are issued before the first add (the scheduling barrier
+// keeps the compiler from interleaving them with the adds, which under register pressure
+// it otherwise does, one round of memory latency per slice).
+__device__ __forceinline__ float sum_slices(const float* p, size_t stride) {
+  float x[PU_SLICES];
+#pragma unroll
+  for (int sl = 0; sl < PU_SLICES; ++sl) x[sl] = p[sl * stride];
+  __builtin_amdgcn_sched_barrier(0);
+  float v = 0.f;
+#pragma unroll
+  for (int sl = 0; sl < PU_SLICES; ++sl) v += x[sl];
+  return v;
+}
+
 // Maximum of the bit patterns of non-negative floats (ordered as the floats are).
 struct MaxBits { __device__ int operator()(int a, int b) const { return max(a, b); } };
 
@@ -49,12 +64,7 @@ struct MaxBits { __device__ int operator()(int a, int b) const { return max(a, b
 template <bool PART>
 __device__ __forceinline__ float proj(const FoldArgs& a, int b, int p0, int j, int col) {
   if constexpr (PART) {
-    if (j == p0) {
-      float v = 0.f;
-#pragma unroll
-      for (int s = 0; s < PU_SLICES; ++s) v += a.part[((size_t)s * a.B + b) * a.NP + col];
-      return v;
-    }
+    if (j == p0) return sum_slices(a.part + (size_t)b * a.NP + col, (size_t)a.B * a.NP);
   } else {
     if (a.P && j >= p0) return a.P[((size_t)b * a.T + (j - p0)) * a.NP + col];
   }
@@ -90,6 +100,89 @@ __device__ __forceinline__ float fold_column(const FoldArgs& a, int b, int p0, i
       den += e;
       num = fmaf(e, proj<PART>(a, b, p0, jb + r, colCa + boff), num);
     }
+  return num / den;
+}
+
+// The new token's summed projection in column col (its partial sums added in slice order).
+__device__ __forceinline__ float new_token_proj(const FoldArgs& a, int b, int col) {
+  return sum_slices(a.part + (size_t)b * a.NP + col, (size_t)a.B * a.NP);
+}
+
+// The same fold for the entry a one-token step completes (T = 1, partial sums in a.part):
+// entry i's block ends at the new token, p0 = M i + M - 1, so its first M - 1 rows and the
+// previous block come from the state ring and its last row from the new token's partial
+// sums.  step_load issues every load of a column (all but the new token's values, which
+// step_finish takes summed, from LDS, or sums itself) before any is used, so they take one
+// round of latency instead of one per row: a step completes an entry with one workgroup
+// per sequence, and nothing else hides that latency.  The arithmetic is fold_column's, in
+// its order.
+template <int M>
+struct StepCol {
+  float za[M], ca[M], zb[M], cb[M];
+  int colCa, colZa;
+};
+template <int M>
+__device__ __forceinline__ void step_load(const FoldArgs& a, int b, int i, int colCa, int colZa, int boff,
+                                          StepCol<M>& v) {
+  const bool has_b = a.dual && i > 0;
+  const float* st = a.state + (size_t)b * a.S * a.NP;
+  v.colCa = colCa;
+  v.colZa = colZa;
+#pragma unroll
+  for (int r = 0; r < M; ++r) {
+    if (r < M - 1) {
+      const float* row = st + (size_t)((M * i + r) % a.S) * a.NP;
+      v.za[r] = row[colZa];
+      v.ca[r] = row[colCa];
+    }
+    // the previous block's rows (read from a valid row when there is none, then ignored)
+    const float* rowb = st + (size_t)((has_b ? M * (i - 1) + r : r) % a.S) * a.NP;
+    v.zb[r] = rowb[colZa + boff];
+    v.cb[r] = rowb[colCa + boff];
+  }
+}
+// FROM_LDS: the new token's Z and C values are at pz, pc (LDS), else they are summed here; the
+// biases (a few KB, cache-resident) are read here.
+template <int M, bool FROM_LDS>
+__device__ __forceinline__ float step_finish(const FoldArgs& a, int b, int i, StepCol<M>& v, const float* pz,
+                                             const float* pc, const float* Ba, const float* Bb, int bstride_col,
+                                             int u) {
+  const bool has_b = a.dual && i > 0;
+  if constexpr (FROM_LDS) {
+    v.za[M - 1] = *pz;
+    v.ca[M - 1] = *pc;
+  } else {
+    v.za[M - 1] = new_token_proj(a, b, v.colZa);
+    v.ca[M - 1] = new_token_proj(a, b, v.colCa);
+  }
+  float ba[M], bb[M];
+#pragma unroll
+  for (int r = 0; r < M; ++r) {
+    ba[r] = Ba ? Ba[r * bstride_col + u] : 0.f;
+    bb[r] = Bb ? Bb[r * bstride_col + u] : 0.f;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < M; ++r) mx = fmaxf(mx, v.za[r] + ba[r]);
+  if (has_b) {
+#pragma unroll
+    for (int r = 0; r < M; ++r) mx = fmaxf(mx, v.zb[r] + bb[r]);
+  }
+  float den = 0.f, num = 0.f;
+#pragma unroll
+  for (int r = 0; r < M; ++r) {
+    const float e = expf(v.za[r] + ba[r] - mx);
+    den += e;
+    num = fmaf(e, v.ca[r], num);
+  }
+  if (has_b) {
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+      const float e = expf(v.zb[r] + bb[r] - mx);
+      den += e;
+      num = fmaf(e, v.cb[r], num);
+    }
+  }
   return num / den;
 }
 
@@ -138,19 +231,21 @@ __device__ __forceinline__ void finalize_store(const FoldArgs& a, float x0, floa
                                                uint8_t* dst, float* red, float* ybuf = nullptr) {
   const int t = threadIdx.x, u = 2 * t;
   const bool act = u < a.c;
+  const int rs = a.c - a.r;
+  // the norm weights and the rotation first: neither depends on the block sum, so their
+  // loads and arithmetic overlap its barriers
+  const float g0 = act && a.gamma ? a.gamma[u] : 1.f, g1 = act && a.gamma ? a.gamma[u + 1] : 1.f;
+  float cs = 1.f, sn = 0.f;
+  if (act && u >= rs) rope_cos_sin(pos, (u - rs) >> 1, a.r, a.log2_base, cs, sn);
   float ss = block_sum<NW>(act ? x0 * x0 + x1 * x1 : 0.f, red);
   float inv = 1.0f / sqrtf(ss / (float)a.c + a.eps);
   if (!act) return;
-  float g0 = a.gamma ? a.gamma[u] : 1.f, g1 = a.gamma ? a.gamma[u + 1] : 1.f;
   float y0 = g0 * (x0 * inv), y1 = g1 * (x1 * inv);
   if (ybuf) {
     ybuf[u] = y0;
     ybuf[u + 1] = y1;
   }
-  const int rs = a.c - a.r;
   if (u >= rs) {
-    float cs, sn;
-    rope_cos_sin(pos, (u - rs) >> 1, a.r, a.log2_base, cs, sn);
     float z0 = y0 * cs - y1 * sn, z1 = y0 * sn + y1 * cs;
     y0 = z0;
     y1 = z1;
@@ -181,9 +276,10 @@ __device__ __forceinline__ void finalize_store(const FoldArgs& a, float x0, floa
   }
 }
 
-// Keys 2t and 2t + 1 of entry i of sequence b, stored in the index format (thread t, 2t < cI).
-__device__ __forceinline__ void store_key_pair(const FoldArgs& a, int b, int i, float k0, float k1) {
-  const int t = threadIdx.x, u = 2 * t;
+// Keys 2t and 2t + 1 of entry i of sequence b, stored in the index format (2t < cI; pair t
+// is held by a thread whose lane is t modulo 64, so that a DPP row holds a 32-dim block).
+__device__ __forceinline__ void store_key_pair(const FoldArgs& a, int b, int i, int t, float k0, float k1) {
+  const int u = 2 * t;
   if (a.idx_fmt == CSA_FMT_F32) {
     float* kd = reinterpret_cast<float*>(a.ki) + row_of(a.rm, b, i) * a.cI;
     kd[u] = k0;
@@ -219,24 +315,49 @@ __device__ __forceinline__ void entry_key(const FoldArgs& a, int b, int i, const
       for (int v = 0; v < half; ++v) acc = fmaf(ybuf[h * half + v], wr[v], acc);
     } else {
       const uint16_t* wr = static_cast<const uint16_t*>(a.w_ik) + (size_t)o * a.c + h * half;
-      for (int v = 0; v < half; ++v) acc = fmaf(ybuf[h * half + v], bf16_bits_to_f32(wr[v]), acc);
+      if ((reinterpret_cast<uintptr_t>(wr) & 15) == 0 && half % 32 == 0) {
+        // 16-byte loads, 32 weights issued at a time; the sum keeps its order
+        const float* yb = ybuf + h * half;
+        for (int v0 = 0; v0 < half; v0 += 32) {
+          uint4 w4[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) w4[q] = *reinterpret_cast<const uint4*>(wr + v0 + 8 * q);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t ww[4] = {w4[q].x, w4[q].y, w4[q].z, w4[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int v = v0 + 8 * q + 2 * e;
+              acc = fmaf(yb[v], bf16_bits_to_f32(ww[e] & 0xffffu), acc);
+              acc = fmaf(yb[v + 1], bf16_bits_to_f32(ww[e] >> 16), acc);
+            }
+          }
+        }
+      } else {
+        for (int v = 0; v < half; ++v) acc = fmaf(ybuf[h * half + v], bf16_bits_to_f32(wr[v]), acc);
+      }
     }
     // pairs (2o, 2o + 1) are adjacent lanes of one wave
     const float other = __shfl_xor(acc, 1);
     if (h == 0) kbuf[o] = acc + other;
   }
   __syncthreads();
-  if (2 * t < a.cI) store_key_pair(a, b, i, kbuf[2 * t], kbuf[2 * t + 1]);
+  if (2 * t < a.cI) store_key_pair(a, b, i, t, kbuf[2 * t], kbuf[2 * t + 1]);
 }
 
 // Block (slot, b) of the fold: slot < T the raw window row of token pos0[b] + slot, otherwise
 // the entry slot - T past pos0[b] / m (when its block completes in this chunk).  Threads hold
 // columns 2t, 2t + 1; a block of NW waves (NW >= 4; those past the c columns hold zeros).
 // red: LDS [NW]; ybuf, kbuf: LDS [c] and [cI] for CSA2's index keys (null where the fold
-// never serves a CSA2 layer).
+// never serves a CSA2 layer); pnew: LDS [FOLD_PNEW] or null: with it, a one-token step's
+// entry first sums the new token's partial projections of the columns it reads with every
+// thread of the block (the blocks of the top-k launch have four times the threads the
+// columns need), then folds from LDS.
+constexpr int FOLD_PNEW = 2 * 512 + 2 * 128;
 template <int NW, bool PART>
 __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, float* red,
-                                           float* ybuf = nullptr, float* kbuf = nullptr) {
+                                           float* ybuf = nullptr, float* kbuf = nullptr, float* pnew = nullptr) {
   const int t = threadIdx.x;
   const int p0 = a.pos0[b];
   const int u = 2 * t;
@@ -267,15 +388,79 @@ __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, f
   const int i = p0 / a.m + (slot - a.T);
   if (a.m * (i + 1) > p0 + a.T || i >= a.cap) return;  // block not complete in this chunk
   // main KV entry: columns C^a at 0, C^b at c, Z^a at 2c, Z^b at 3c (HCA: C at 0, Z at c)
-  float x0 = 0.f, x1 = 0.f;
-  if (u < a.c) {
+  // (a one-token step with m = 4 loads each column's values at once; in blocks of 16 waves
+  // the new token's values go through LDS first, and past its size the general fold runs)
+  constexpr bool LDS_NEW = NW >= 16;
+  const int nnew = 2 * a.c + (a.dual ? 2 * a.cI : 0);
+  const bool step4 = PART && a.T == 1 && a.part && a.m == 4 && (!LDS_NEW || (pnew && nnew <= FOLD_PNEW));
+  // With threads to spare (the top-k launch's blocks) CSA's index key is folded by threads
+  // c/2 .. c/2 + cI/2 - 1 beside the entry's columns, else by threads 0 .. cI/2 - 1 after.
+  const bool keys_apart = a.dual && 64 * NW >= a.c / 2 + a.cI / 2;
+  const int kp = keys_apart ? t - a.c / 2 : t;   // this thread's key pair
+  const bool has_key = a.dual && kp >= 0 && 2 * kp < a.cI;
+  // the new token's values in LDS: C (C^a) at [0, c), Z (Z^a) at [c, 2c), then (CSA) the
+  // key's C at [2c, 2c + cI) and Z at [2c + cI, 2c + 2cI)
+  float* const pn = LDS_NEW && step4 ? pnew : nullptr;   // uniform
+  // the entry's column pair (threads u < c) or key pair (has_key)
+  const int uk = 2 * kp, kbase = 4 * a.c;
+  const float* BIa = a.bias_idx;
+  const float* BIb = a.bias_idx + a.m * a.cI;
+  const bool main_cols = u < a.c;
+  const bool key_here = keys_apart && has_key && !main_cols;
+  if (pn) {
+    for (int v = t; v < nnew; v += 64 * NW) {
+      int col;
+      if (v < 2 * a.c) col = v < a.c ? v : (a.dual ? 2 * a.c : a.c) + (v - a.c);
+      else col = 4 * a.c + (v < 2 * a.c + a.cI ? v - 2 * a.c : 2 * a.cI + (v - 2 * a.c - a.cI));
+      pn[v] = new_token_proj(a, b, col);
+    }
+    __syncthreads();
+  }
+  StepCol<4> s0, s1;
+  if (step4 && main_cols) {
     if (a.dual) {
+      step_load<4>(a, b, i, u, 2 * a.c + u, a.c, s0);
+      step_load<4>(a, b, i, u + 1, 2 * a.c + u + 1, a.c, s1);
+    } else {
+      step_load<4>(a, b, i, u, a.c + u, 0, s0);
+      step_load<4>(a, b, i, u + 1, a.c + u + 1, 0, s1);
+    }
+  } else if (step4 && key_here) {
+    step_load<4>(a, b, i, kbase + uk, kbase + 2 * a.cI + uk, a.cI, s0);
+    step_load<4>(a, b, i, kbase + uk + 1, kbase + 2 * a.cI + uk + 1, a.cI, s1);
+  }
+  auto fold_key = [&]() {
+    float k0, k1;
+    if (step4) {
+      if (!key_here) {
+        step_load<4>(a, b, i, kbase + uk, kbase + 2 * a.cI + uk, a.cI, s0);
+        step_load<4>(a, b, i, kbase + uk + 1, kbase + 2 * a.cI + uk + 1, a.cI, s1);
+      }
+      const float* kn = pn + 2 * a.c;   // the key's C, then Z (used with LDS_NEW only)
+      k0 = step_finish<4, LDS_NEW>(a, b, i, s0, kn + a.cI + uk, kn + uk, BIa, BIb, a.cI, uk);
+      k1 = step_finish<4, LDS_NEW>(a, b, i, s1, kn + a.cI + uk + 1, kn + uk + 1, BIa, BIb, a.cI, uk + 1);
+    } else {
+      k0 = fold_column<PART>(a, b, p0, i, kbase + uk, kbase + 2 * a.cI + uk, a.cI, BIa, BIb, a.cI, uk);
+      k1 = fold_column<PART>(a, b, p0, i, kbase + uk + 1, kbase + 2 * a.cI + uk + 1, a.cI, BIa, BIb, a.cI, uk + 1);
+    }
+    store_key_pair(a, b, i, kp, k0, k1);
+  };
+  float x0 = 0.f, x1 = 0.f;
+  if (main_cols) {
+    if (step4) {
+      const float* Bb = a.dual ? a.bias + a.m * a.c : nullptr;
+      x0 = step_finish<4, LDS_NEW>(a, b, i, s0, pn + a.c + u, pn + u, a.bias, Bb, a.c, u);
+      __builtin_amdgcn_sched_barrier(0);
+      x1 = step_finish<4, LDS_NEW>(a, b, i, s1, pn + a.c + u + 1, pn + u + 1, a.bias, Bb, a.c, u + 1);
+    } else if (a.dual) {
       x0 = fold_column<PART>(a, b, p0, i, u, 2 * a.c + u, a.c, a.bias, a.bias + a.m * a.c, a.c, u);
       x1 = fold_column<PART>(a, b, p0, i, u + 1, 2 * a.c + u + 1, a.c, a.bias, a.bias + a.m * a.c, a.c, u + 1);
     } else {
       x0 = fold_column<PART>(a, b, p0, i, u, a.c + u, 0, a.bias, a.bias, a.c, u);
       x1 = fold_column<PART>(a, b, p0, i, u + 1, a.c + u + 1, 0, a.bias, a.bias, a.c, u + 1);
     }
+  } else if (key_here) {
+    fold_key();
   }
   uint8_t* dst = a.kv + row_of(a.rm, b, i) * a.rowB;
   const bool ek = a.keys_entry && ybuf;
@@ -285,14 +470,7 @@ __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, f
     return;
   }
   // CSA indexer key: same fold with its own columns and biases; stored as folded
-  if (a.dual && u < a.cI) {
-    const int base = 4 * a.c;
-    const float* BIa = a.bias_idx;
-    const float* BIb = a.bias_idx + a.m * a.cI;
-    float k0 = fold_column<PART>(a, b, p0, i, base + u, base + 2 * a.cI + u, a.cI, BIa, BIb, a.cI, u);
-    float k1 = fold_column<PART>(a, b, p0, i, base + u + 1, base + 2 * a.cI + u + 1, a.cI, BIa, BIb, a.cI, u + 1);
-    store_key_pair(a, b, i, k0, k1);
-  }
+  if (!keys_apart && has_key) fold_key();
 }
 
 

@@ -638,9 +638,10 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_final_fold(FinalArgs fa, in
   __shared__ FinalShared fs;
   __shared__ float red[TK_WAVES];
   __shared__ float ybuf[EK ? 512 : 1], kbuf[EK ? 512 : 1];
+  __shared__ float pnew[FOLD_PNEW];
   const int b = blockIdx.x;
   if (b < Q) topk_final_body<BF>(fa, b, fs);
-  else fold_block<TK_WAVES, true>(fo, (b - Q) % fx, (b - Q) / fx, red, EK ? ybuf : nullptr, EK ? kbuf : nullptr);
+  else fold_block<TK_WAVES, true>(fo, (b - Q) % fx, (b - Q) / fx, red, EK ? ybuf : nullptr, EK ? kbuf : nullptr, pnew);
 }
 
 // ----------------------------------------------------------------------- one-launch rows
