@@ -186,6 +186,77 @@ __device__ __forceinline__ float step_finish(const FoldArgs& a, int b, int i, St
   return num / den;
 }
 
+// The single-path fold (HCA) of columns u and u + 1 for the entry a one-token step completes,
+// with any m: rows m i .. m i + m - 2 from the state ring, the last row the new token.  Both
+// passes read CH rows at a time with every load of a chunk issued together (one round of
+// memory latency per chunk, not per row); the arithmetic is fold_column's, in its order.
+__device__ __forceinline__ void fold_pair_rows(const FoldArgs& a, int b, int i, int u, float& x0, float& x1) {
+  constexpr int CH = 16;
+  const int m = a.m, colZ = a.c + u, colC = u;
+  const float* st = a.state + (size_t)b * a.S * a.NP;
+  const float* B = a.bias;   // [m][c] or null
+  auto bias = [&](int r, int h) { return B ? B[r * a.c + u + h] : 0.f; };
+  float zn[2], cn[2];   // the new token (row m - 1)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    zn[h] = new_token_proj(a, b, colZ + h);
+    cn[h] = new_token_proj(a, b, colC + h);
+  }
+  float mx[2] = {-INFINITY, -INFINITY};
+  for (int r0 = 0; r0 < m - 1; r0 += CH) {
+    float z[2][CH];
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const int r = min(r0 + q, m - 2);   // past the chunk's end: a repeated row, ignored
+      const float* row = st + (size_t)((m * i + r) % a.S) * a.NP;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) z[h][q] = row[colZ + h] + bias(r, h);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < CH; ++q)
+      if (r0 + q < m - 1) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) mx[h] = fmaxf(mx[h], z[h][q]);
+      }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) mx[h] = fmaxf(mx[h], zn[h] + bias(m - 1, h));
+  float den[2] = {0.f, 0.f}, num[2] = {0.f, 0.f};
+  for (int r0 = 0; r0 < m - 1; r0 += CH) {
+    float z[2][CH], cv[2][CH];
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const int r = min(r0 + q, m - 2);
+      const float* row = st + (size_t)((m * i + r) % a.S) * a.NP;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        z[h][q] = row[colZ + h] + bias(r, h);
+        cv[h][q] = row[colC + h];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < CH; ++q)
+      if (r0 + q < m - 1) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float e = expf(z[h][q] - mx[h]);
+          den[h] += e;
+          num[h] = fmaf(e, cv[h][q], num[h]);
+        }
+      }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float e = expf(zn[h] + bias(m - 1, h) - mx[h]);
+    den[h] += e;
+    num[h] = fmaf(e, cn[h], num[h]);
+  }
+  x0 = num[0] / den[0];
+  x1 = num[1] / den[1];
+}
+
 // Sum over a block of NW waves (NW >= 4); the first four partial sums are added in the same
 // order whatever NW is (the rest hold zeros in the 1024-thread launch), so the result does
 // not depend on the block size.
@@ -452,6 +523,8 @@ __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, f
       x0 = step_finish<4, LDS_NEW>(a, b, i, s0, pn + a.c + u, pn + u, a.bias, Bb, a.c, u);
       __builtin_amdgcn_sched_barrier(0);
       x1 = step_finish<4, LDS_NEW>(a, b, i, s1, pn + a.c + u + 1, pn + u + 1, a.bias, Bb, a.c, u + 1);
+    } else if (!LDS_NEW && PART && a.T == 1 && a.part && !a.dual) {
+      fold_pair_rows(a, b, i, u, x0, x1);   // HCA's one-token step
     } else if (a.dual) {
       x0 = fold_column<PART>(a, b, p0, i, u, 2 * a.c + u, a.c, a.bias, a.bias + a.m * a.c, a.c, u);
       x1 = fold_column<PART>(a, b, p0, i, u + 1, 2 * a.c + u + 1, a.c, a.bias, a.bias + a.m * a.c, a.c, u + 1);

@@ -209,10 +209,12 @@ def test_q_compress_single_token_steps(idx_fmt):
     assert flips < 50
 
 
-@pytest.mark.parametrize("paged", [False, True])
-def test_hca_compress_matches_oracle(paged):
+@pytest.mark.parametrize("paged,chunks", [(False, (100, 1, 127, 72)), (True, (100, 1, 127, 72)),
+                                          (False, (127, 1, 1, 171))])
+def test_hca_compress_matches_oracle(paged, chunks):
     """HCA (m'=128, single path, no indexer): 2 sequences x 300 tokens in chunks; paged: one
-    entry per 128-token page."""
+    entry per 128-token page.  Chunks (127, 1, 1, 171): the one-token step at position 127
+    completes entry 0 (the one-token fold over all 128 rows of a block)."""
     cfg = synth.config("c5")
     dims = L.Dims.from_config(cfg)
     od = oracle_dims(cfg)
@@ -220,7 +222,8 @@ def test_hca_compress_matches_oracle(paged):
     W = synth.weights(cfg, seed=6, device=DEV)
     Hs = torch.stack([synth.hidden(cfg, b, 0, n, seed=6, device=DEV) for b in range(B)])
     cache = paged_cache(dims, B, 8, 128, seed=6) if paged else L.Cache(dims, B=B, cap=8, win_cap=128)
-    _compress_chunks(dims, W, cache, Hs, [100, 1, 127, 72])
+    print(f"hca compress paged={paged} chunks={chunks}", flush=True)
+    _compress_chunks(dims, W, cache, Hs, list(chunks))
     cache = logical(cache)
     OW = oracle_weights(W)
     for b in range(B):
