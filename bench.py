@@ -372,11 +372,14 @@ def run_decode(args, cfg):
     streamed = B * N * (cfg["c_I"] if has_idx else synth.row_bytes(cfg))
     copies = args.copies or min(16, max(3, -(-2 * MALL_BYTES // streamed) + 1))
     G = copies
-    # Step s runs on copy s % G at position tau_start + s // G: every copy advances one token
-    # per cycle, so one step in m completes (and stores) an entry.  The prefix stops `room`
-    # entries short of the capacity, which leaves room for every entry the steps complete.
+    # Step s runs on copy g = s % G at position tau_start + off[g] + s // G: copy g starts off[g]
+    # tokens into the open block (taken by untimed one-token steps) and advances one token per
+    # cycle.  The offsets spread the copies over the block, so in every cycle about one step in
+    # m completes (and stores) an entry, whatever the number of steps.  The prefix stops
+    # `room` entries short of the capacity, which leaves room for every entry completed.
     cycles = -(-(warm + steps) // G)
-    room = cycles // m + 1
+    offs = [(g * m) // G for g in range(G)]
+    room = (max(offs) + cycles) // m + 2
     N0 = N - room
     tau_start = m * N0
     tau = tau_start
@@ -386,15 +389,20 @@ def run_decode(args, cfg):
     t_build = time.perf_counter() - t_build
     caches = [base] + [clone_cache(base) for _ in range(copies - 1)]
 
-    # per cycle: the new token of each sequence (its hidden state) and its position
+    # per position: the new token of each sequence (its hidden state) and the position
+    npos = max(offs) + cycles
     Hc = [torch.stack([synth.hidden(cfg, b, tau_start + c, tau_start + c + 1, device=dev) for b in range(B)])
-          for c in range(cycles)]
-    posc = [torch.full((B,), tau_start + c, dtype=torch.int32, device=dev) for c in range(cycles)]
+          for c in range(npos)]
+    posc = [torch.full((B,), tau_start + c, dtype=torch.int32, device=dev) for c in range(npos)]
     H1, pos0 = Hc[0], posc[0]
+    ws_c = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_COMPRESS, B=B, T=1)), dtype=torch.uint8, device=dev)
+    for g, c in enumerate(caches):   # each copy to its starting offset (untimed)
+        for j in range(offs[g]):
+            L.csa_compress(dims, lw, c, Hc[j], 1, posc[j], ws_c)
+    torch.cuda.synchronize()
     qs = synth.queries(cfg, B, device=dev, tag="decode", mx_codes=(125, 127))
     q_seq = torch.arange(B, dtype=torch.int32, device=dev)
     q_pos = torch.full((B,), tau, dtype=torch.int32, device=dev)
-    ws_c = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_COMPRESS, B=B, T=1)), dtype=torch.uint8, device=dev)
     ws_a = torch.empty(max(1, L.csa_workspace_size(dims, L.OP_ATTEND, Q=B, cap=N)), dtype=torch.uint8, device=dev)
     out = torch.empty((B, cfg["n_h"], cfg["c"]), dtype=torch.bfloat16, device=dev)
     if has_idx:
@@ -438,8 +446,8 @@ def run_decode(args, cfg):
 
     def step(s):
         # step s: one pass of the whole path through the library's forward entry point, on
-        # copy s % G at position tau_start + s // G
-        c, cyc = caches[s % G], s // G
+        # copy s % G at position tau_start + off[s % G] + s // G
+        c, cyc = caches[s % G], offs[s % G] + s // G
         if args.layer:
             k_qproj(c)
             L.csa_forward(dims, lw, c, Hc[cyc], 1, posc[cyc], q_l, qI_l, w_l, W["gamma_q"], W["sink"], out,
@@ -568,8 +576,9 @@ def run_decode(args, cfg):
         desc += (f"; whole attention layer: query-side projections (d_c {cfg['d_c']}) before the path and the "
                  f"grouped output projection (g {cfg['g']}, d_g {cfg['d_g']}) after it")
     res["config"] = {"workload": f"{cfg['name']}: {desc}", "global_batch": B, "seq_len": cfg["prefix"],
-                     "positions": f"{tau_start} .. {tau_start + cycles - 1} (each copy advances one token per "
-                                  f"cycle; one step in {m} completes an entry)",
+                     "positions": f"{tau_start} .. {tau_start + npos - 1} (copy g starts {offs} tokens into the "
+                                  f"open block and advances one token per cycle; about one step in {m} completes "
+                                  f"an entry)",
                      "parallelism": "single GPU", "launch": f"HIP graphs of {G} steps (one per cache copy)",
                      "cache_copies": G}
     if not args.no_cpu and not args.layer:
