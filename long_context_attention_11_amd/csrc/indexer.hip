@@ -809,11 +809,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int sk = code_spread(bs[t]);
       slow |= (__ballot(max(sq[0], sq[1]) + sk > FP4_EXACT_SPREAD) != 0 ? 1u : 0u) << t;
     }
-    f32x4 acc[2][HT];
     auto mm = [&](int u, f32x4 (&a)[HT]) {
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) a[ht] = mfma_fp4(qa[u & 1][ht], qs[u & 1][ht], b[u >> 1], bs[u >> 1]);
     };
+    // The stage's units; MAY_SLOW: some tile needs the block-wise sum (the wave's flags say
+    // which).  Without it the loop is free of that branch, so the MFMAs of the next unit and
+    // the epilogue of this one are scheduled together.
+    auto run_stage = [&](auto may_slow) {
+    constexpr bool MAY_SLOW = decltype(may_slow)::value;
+    f32x4 acc[2][HT];
     // part[t][qq]: tile t of the current 64-entry run, query qq, the lane's 16 heads
     double part[4][2];
     mm(0, acc[0]);
@@ -822,7 +827,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (u + 1 < NU) mm(u + 1, acc[(u + 1) & 1]);
       const int qq = u & 1, t = (u >> 1) & 3;
       double p = 0.0;
-      if (!((slow >> (u >> 1)) & 1u)) {
+      if (!MAY_SLOW || !((slow >> (u >> 1)) & 1u)) {
         // the head sum of head_sum_f64, in the same order
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
@@ -854,6 +859,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (s < min(V[q2], e_hi)) scores[(size_t)(qt0 + 2 * wave + q2) * ld + s] = bf16_nearest_from_f64(total);
       }
     }
+    };
+    if (slow == 0u) run_stage(std::false_type{});
+    else run_stage(std::true_type{});
     if (st + 1 < nst) lstore((st + 1) & 1, nv, ns);
     __syncthreads();
   }
