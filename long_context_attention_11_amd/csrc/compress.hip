@@ -144,12 +144,13 @@ __global__ __launch_bounds__(64) void k_project_step(ProjectStepArgs a, int unit
 }
 
 // grid: x = T raw rows + (T/m + 1) entry slots (+ state writers), y = sequence.  256
-// threads, 2 columns each.
-template <bool PART>
+// threads, 2 columns each.  EK: index keys projected from the entries (CSA2), a separate
+// instance so that the other layers' folds do not carry its registers.
+template <bool PART, bool EK>
 __global__ __launch_bounds__(256) void k_fold(FoldArgs a) {
   __shared__ float red[4];
-  __shared__ float ybuf[512], kbuf[512];   // CSA2's index keys (c, c_I <= 512)
-  fold_block<4, PART>(a, blockIdx.x, blockIdx.y, red, ybuf, kbuf);
+  __shared__ float ybuf[EK ? 512 : 1], kbuf[EK ? 512 : 1];   // CSA2's index keys (c, c_I <= 512)
+  fold_block<4, PART>(a, blockIdx.x, blockIdx.y, red, EK ? ybuf : nullptr, EK ? kbuf : nullptr);
 }
 
 // Keep the projections of the last S tokens of each sequence: slot j % S.
@@ -320,8 +321,13 @@ hipError_t launch_fold(const csa_dims& d, const csa_weights& w, const csa_cache&
   if (ksplit != 1) return hipErrorInvalidValue;  // partials are summed first
   const FoldArgs a = fold_args(d, w, c, T, pos0, P, part);
   dim3 grid(fold_grid_x(a), c.B);
-  if (a.part) hipLaunchKernelGGL(k_fold<true>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_fold<false>, grid, dim3(256), 0, s, a);
+  if (a.keys_entry) {
+    if (a.part) hipLaunchKernelGGL((k_fold<true, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_fold<false, true>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.part) hipLaunchKernelGGL((k_fold<true, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_fold<false, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -302,21 +302,19 @@ __device__ __forceinline__ void finalize_store(const FoldArgs& a, float x0, floa
                                                uint8_t* dst, float* red, float* ybuf = nullptr) {
   const int t = threadIdx.x, u = 2 * t;
   const bool act = u < a.c;
-  const int rs = a.c - a.r;
-  // the norm weights and the rotation first: neither depends on the block sum, so their
-  // loads and arithmetic overlap its barriers
-  const float g0 = act && a.gamma ? a.gamma[u] : 1.f, g1 = act && a.gamma ? a.gamma[u + 1] : 1.f;
-  float cs = 1.f, sn = 0.f;
-  if (act && u >= rs) rope_cos_sin(pos, (u - rs) >> 1, a.r, a.log2_base, cs, sn);
   float ss = block_sum<NW>(act ? x0 * x0 + x1 * x1 : 0.f, red);
   float inv = 1.0f / sqrtf(ss / (float)a.c + a.eps);
   if (!act) return;
+  float g0 = a.gamma ? a.gamma[u] : 1.f, g1 = a.gamma ? a.gamma[u + 1] : 1.f;
   float y0 = g0 * (x0 * inv), y1 = g1 * (x1 * inv);
   if (ybuf) {
     ybuf[u] = y0;
     ybuf[u + 1] = y1;
   }
+  const int rs = a.c - a.r;
   if (u >= rs) {
+    float cs, sn;
+    rope_cos_sin(pos, (u - rs) >> 1, a.r, a.log2_base, cs, sn);
     float z0 = y0 * cs - y1 * sn, z1 = y0 * sn + y1 * cs;
     y0 = z0;
     y1 = z1;
@@ -466,7 +464,7 @@ __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, f
   const bool step4 = PART && a.T == 1 && a.part && a.m == 4 && (!LDS_NEW || (pnew && nnew <= FOLD_PNEW));
   // With threads to spare (the top-k launch's blocks) CSA's index key is folded by threads
   // c/2 .. c/2 + cI/2 - 1 beside the entry's columns, else by threads 0 .. cI/2 - 1 after.
-  const bool keys_apart = a.dual && 64 * NW >= a.c / 2 + a.cI / 2;
+  const bool keys_apart = NW >= 8 && a.dual && 64 * NW >= a.c / 2 + a.cI / 2;   // (NW < 8: never)
   const int kp = keys_apart ? t - a.c / 2 : t;   // this thread's key pair
   const bool has_key = a.dual && kp >= 0 && 2 * kp < a.cI;
   // the new token's values in LDS: C (C^a) at [0, c), Z (Z^a) at [c, 2c), then (CSA) the
