@@ -334,8 +334,13 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_segment(
     }
   }
   if (!loaded) {
+    // every load issued (a position past V reads the row's last visible score, or its first),
+    // then masked: per-element branches would make each load wait for the one before
+    float v[E];
 #pragma unroll
-    for (int i = 0; i < E; ++i) it.key[i] = first + i < V ? score_key(row[first + i]) : 0u;
+    for (int i = 0; i < E; ++i) v[i] = row[max(0, min(first + i, V - 1))];
+#pragma unroll
+    for (int i = 0; i < E; ++i) it.key[i] = first + i < V ? score_key(v[i]) : 0u;
   }
   const int n = select_topk<E>(it, k, sh, oidx, okey);
   for (int i = n + threadIdx.x; i < k; i += TK_THREADS) {
@@ -529,15 +534,29 @@ __device__ __forceinline__ int final_fast(int q, int nseg, int cs, int N, int k,
   int sg = 0;   // segment of p0: the last with segoff <= p0
   for (int step = TK_MAXSEG; step >= 1; step >>= 1)
     if (sg + step <= nseg && fs.segoff[sg + step] <= p0) sg += step;
+  // the list positions of the thread's items first, then every load at once (a position
+  // past N reads the query's first list slot and is masked): loads in branches would each
+  // wait for the one before
+  size_t at[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     const int p = p0 + i;
     while (sg < nseg && fs.segoff[sg + 1] <= p) ++sg;
     const int sc = min(sg, nseg - 1);
-    const size_t at = ((size_t)q * nseg + sc) * cs + (p - fs.segoff[sc]);
-    const bool ok = p < N;
-    it.id[i] = ok ? cand_idx[at] : -1;
-    it.key[i] = ok ? cand_key[at] : 0u;
+    at[i] = p < N ? ((size_t)q * nseg + sc) * cs + (p - fs.segoff[sc]) : (size_t)q * nseg * cs;
+  }
+  int32_t ci[E];
+  uint32_t ck[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    ci[i] = cand_idx[at[i]];
+    ck[i] = cand_key[at[i]];
+  }
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const bool ok = p0 + i < N;
+    it.id[i] = ok ? ci[i] : -1;
+    it.key[i] = ok ? ck[i] : 0u;
   }
   return select_topk<E>(it, k, fs.sh, out, nullptr);
 }
