@@ -198,7 +198,18 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
   const int col = lane & 15, g = lane >> 4;
   const int q0 = bx * QPW;
   int seq, V[QPW], c_hi, w_lo;
-  if (!indexer_range<QPW>(ia, bx, by, wave, seq, V, c_hi, w_lo)) return;
+  // contiguous keys: the first ring goes out as soon as the sequence is known, bounded by the
+  // chunk and the capacity; the visible count (one more dependent load) bounds the rest
+  const bool spec = ia.rm.bt == nullptr;
+  if (spec) {
+    seq = ia.q_seq ? ia.q_seq[q0] : q0;
+    const int c_lo = by * ia.chunk;
+    c_hi = min(c_lo + ia.chunk, ia.cap);
+    w_lo = c_lo + 16 * wave;
+    if (w_lo >= c_hi) return;
+  } else if (!indexer_range<QPW>(ia, bx, by, wave, seq, V, c_hi, w_lo)) {
+    return;
+  }
   const int stride = 64;  // 4 waves x 16 entries
 
   const WavePages wp = wave_pages(ia.rm, seq, w_lo, c_hi, lane);
@@ -246,6 +257,10 @@ __device__ __forceinline__ void indexer_bf16_body(const IndexerArgs& ia, int bx,
       W[qq][ht][2] = bf16_bits_to_f32(w4.y & 0xffffu);
       W[qq][ht][3] = bf16_bits_to_f32(w4.y >> 16);
     }
+  }
+  if (spec) {
+    int sq, wl;
+    if (!indexer_range<QPW>(ia, bx, by, wave, sq, V, c_hi, wl)) return;
   }
   // Straight-line ring: every wave runs whole rounds of DEPTH tiles.  Loads past the end are
   // clamped to the last entry (same cache line for every lane) and their results discarded,
