@@ -354,7 +354,18 @@ __device__ __forceinline__ void indexer_fp4_body(const IndexerArgs& ia, int bx, 
   const int col = lane & 15, g = lane >> 4;
   const int q0 = bx * QPW;
   int seq, V[QPW], c_hi, w_lo;
-  if (!indexer_range<QPW>(ia, bx, by, wave, seq, V, c_hi, w_lo)) return;
+  // contiguous keys: the first ring goes out before the entry count is known, as in
+  // indexer_bf16_body
+  const bool spec = ia.rm.bt == nullptr;
+  if (spec) {
+    seq = ia.q_seq ? ia.q_seq[q0] : q0;
+    const int c_lo = by * ia.chunk;
+    c_hi = min(c_lo + ia.chunk, ia.cap);
+    w_lo = c_lo + 16 * wave;
+    if (w_lo >= c_hi) return;
+  } else if (!indexer_range<QPW>(ia, bx, by, wave, seq, V, c_hi, w_lo)) {
+    return;
+  }
   const int stride = 64;  // 4 waves x 16 entries
   uint16_t* __restrict__ scores = static_cast<uint16_t*>(ia.scores);
 
@@ -405,6 +416,10 @@ __device__ __forceinline__ void indexer_fp4_body(const IndexerArgs& ia, int bx, 
       W[qq][ht][3] = bf16_bits_to_f32(w4.y >> 16);
     }
     sq[qq] = query_code_spread<HT>(qs[qq]);
+  }
+  if (spec) {
+    int sq2, wl;
+    if (!indexer_range<QPW>(ia, bx, by, wave, sq2, V, c_hi, wl)) return;
   }
   const int rounds = (c_hi - w_lo + stride * DEPTH - 1) / (stride * DEPTH);
   int it = 0;
