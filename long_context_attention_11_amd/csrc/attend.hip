@@ -508,44 +508,43 @@ void k_attend_hs(AttendArgs a) {
   }
 }
 
-// Merge split partials (already rotated back): one wave per (query, head), 8 dims per lane,
-// four (query, head) pairs per workgroup.  Splits are taken 8 at a time (all loads of a chunk
-// in flight), merged with a running max.
+// Merge split partials (already rotated back): one 64-thread workgroup per (query, head), 8
+// dims per lane.  Splits are taken NS at a time, every load of a chunk in flight at once (NS
+// is the smallest of 4, 8, 16 that holds the plan's splits, else 16 and several chunks),
+// merged with a running max.
 constexpr int COMB_MAX = 256;  // most splits a plan uses
-constexpr int COMB_WAVES = 4;
 
-__global__ __launch_bounds__(64 * COMB_WAVES) void k_attend_combine(AttendArgs a) {
-  const int qh = blockIdx.x * COMB_WAVES + (threadIdx.x >> 6);
-  if (qh >= a.Q * a.n_h) return;
+template <int NS>
+__global__ __launch_bounds__(64) void k_attend_combine(AttendArgs a) {
+  const int qh = blockIdx.x;
   const int h = qh % a.n_h;
-  const int d = 8 * (threadIdx.x & 63);
+  const int d = 8 * threadIdx.x;
   const float* ml = a.part_ml + (size_t)qh * a.splits * 2;
   const uint16_t* po = a.part_o + (size_t)qh * a.splits * AC + d;
   const float sink2 = a.sink ? a.sink[h] * LOG2E : NEG_BIG;
   float M = a.sink ? sink2 : NEG_BIG;
   float Lsum = a.sink ? 1.0f : 0.f;   // the sink's term exp2(sink2 - M) with M = sink2
   float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < a.splits; s0 += 8) {
-    float2 mls[8];
-    uint4 ov[8];
+  for (int s0 = 0; s0 < a.splits; s0 += NS) {
+    float2 mls[NS];
+    uint4 ov[NS];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NS; ++i) {
       const int s = min(s0 + i, a.splits - 1);
       mls[i] = *reinterpret_cast<const float2*>(ml + 2 * s);
       ov[i] = *reinterpret_cast<const uint4*>(po + (size_t)s * AC);
     }
     float Mc = M;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NS; ++i)
       if (s0 + i < a.splits) Mc = fmaxf(Mc, mls[i].x);
     const float r = exp2f(M - Mc);
     Lsum *= r;
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] *= r;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (s0 + i >= a.splits) break;
-      const float f = exp2f(mls[i].x - Mc);
+    for (int i = 0; i < NS; ++i) {   // past the last split: a repeat of it, weighted 0
+      const float f = s0 + i < a.splits ? exp2f(mls[i].x - Mc) : 0.f;
       Lsum = fmaf(mls[i].y, f, Lsum);
       const uint32_t w[4] = {ov[i].x, ov[i].y, ov[i].z, ov[i].w};
 #pragma unroll
@@ -773,7 +772,10 @@ hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
 #undef ATT_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL(k_attend_combine, dim3((Q * d.n_h + COMB_WAVES - 1) / COMB_WAVES), dim3(64 * COMB_WAVES), 0, s, a);
+  const dim3 cgrid(Q * d.n_h);
+  if (p.splits <= 4) hipLaunchKernelGGL(k_attend_combine<4>, cgrid, dim3(64), 0, s, a);
+  else if (p.splits <= 8) hipLaunchKernelGGL(k_attend_combine<8>, cgrid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL(k_attend_combine<16>, cgrid, dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
