@@ -20,6 +20,7 @@ namespace {
 
 constexpr int GM_ROWS = 8192;   // rows per pass of the host loops (bounds the workspace)
 constexpr int GM_BIG_M = 256;   // inputs of at least this many rows take the 128x128 tiles
+constexpr int GM_WIDE_M = 4096; // ... and of at least this many the 256x256 tiles
 
 struct GemmArgs {
   const uint16_t* A;   // [M][lda]; group z reads columns z * a_zoff .. + K
@@ -135,6 +136,128 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
     }
 }
 
+// Long inputs: 256x256 output tiles, 8 waves in a 2 x 4 grid, each wave a 128x64 part as 8 x 4
+// MFMA 16x16x32 tiles (128 accumulators per lane, two waves per SIMD).  A stage is BK = 64 deep
+// and double buffered in LDS (rows padded by 8 bf16, 147 KB in all, one workgroup per CU).
+// The LDS read rate bounds the smaller tiles: each fragment read here feeds 4 (A) or 8 (B)
+// MFMAs, so a stage moves 0.5 KB of LDS data per 16x16x32 MFMA (written and read), against
+// 0.81 KB on the 128x128 tiles.  Same arguments and stores as k_gemm_bf16; workgroups are
+// ordered so that the column tiles of one row tile run on the same XCD (its L2 then holds
+// the shared A rows).
+template <int BK>
+__global__ __launch_bounds__(512) void k_gemm_wide(GemmArgs g) {
+  constexpr int BM = 256, BN = 256, LD = BK + 8;
+  constexpr int PR = BK / 8;                 // 16-byte pieces per row of a stage
+  constexpr int RPP = 512 / PR;              // rows covered by one pass of the 512 threads
+  constexpr int PA = BM / RPP, PB = BN / RPP;
+  constexpr int TI = 8, TJ = 4;              // MFMA tiles per wave (128 x 64)
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t ncol = gridDim.x, nxy = gridDim.x * gridDim.y;
+  const uint32_t L = xcd_logical_id(blockIdx.y * ncol + blockIdx.x, nxy);
+  const int m0 = (int)(L / ncol) * BM, n0 = (int)(L % ncol) * BN;
+  const int z = blockIdx.z / g.ksplit, ks = blockIdx.z % g.ksplit;
+  const int k_begin = ks * g.kchunk, k_end = min(g.K, k_begin + g.kchunk);
+  const int lr = tid / PR, lc = (tid % PR) * 8;
+  const uint16_t* arow[PA];
+  const uint16_t* brow[PB];
+  bool aval[PA], bval[PB];
+#pragma unroll
+  for (int h = 0; h < PA; ++h) {
+    const int r = lr + RPP * h;
+    aval[h] = m0 + r < g.M;
+    arow[h] = g.A + (size_t)min(m0 + r, g.M - 1) * g.lda + (size_t)z * g.a_zoff;
+  }
+#pragma unroll
+  for (int h = 0; h < PB; ++h) {
+    const int r = lr + RPP * h;
+    const int n = min(n0 + r, g.N - 1);
+    bval[h] = n0 + r < g.N;
+    brow[h] = (n < g.nb1 ? g.B + (size_t)n * g.ldb : g.B2 + (size_t)(n - g.nb1) * g.ldb) +
+              (size_t)z * g.b_zstride;
+  }
+  uint4 ra[PA], rb[PB];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < PA; ++h)
+      ra[h] = aval[h] ? *reinterpret_cast<const uint4*>(arow[h] + k0 + lc) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < PB; ++h)
+      rb[h] = bval[h] ? *reinterpret_cast<const uint4*>(brow[h] + k0 + lc) : make_uint4(0, 0, 0, 0);
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < PA; ++h) *reinterpret_cast<uint4*>(&As[buf][(lr + RPP * h) * LD + lc]) = ra[h];
+#pragma unroll
+    for (int h = 0; h < PB; ++h) *reinterpret_cast<uint4*>(&Bs[buf][(lr + RPP * h) * LD + lc]) = rb[h];
+  };
+  const int wm = (wave >> 2) * 128, wn = (wave & 3) * 64;
+  const int fr = lane & 15, fg = lane >> 4;
+  f32x4 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+  int buf = 0;
+  if (k_begin < k_end) gload(k_begin);
+  for (int k0 = k_begin; k0 < k_end; k0 += BK) {
+    sstore(buf);
+    __syncthreads();
+    if (k0 + BK < k_end) gload(k0 + BK);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      bf16x8 b[TJ];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        b[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(wn + 16 * j + fr) * LD + kk + fg * 8]);
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&As[buf][(wm + 16 * i + fr) * LD + kk + fg * 8]);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a, acc[i][j], 0, 0, 0);
+      }
+    }
+    buf ^= 1;
+  }
+  // The weights are the MFMA's first operand, so a 16x16 result holds the tile transposed:
+  // lane l has row (l & 15) and the four consecutive columns 4 (l >> 4) + e, stored as one
+  // 8-byte (bf16) or 16-byte (fp32) write when the layout allows it.
+  const bool vec = g.N % 4 == 0 && g.n_bf % 4 == 0 && g.ldd % 4 == 0 && g.d_zoff % 4 == 0 &&
+                   g.ldp % 4 == 0 && g.p_zoff % 4 == 0 && g.p_ks % 4 == 0 &&
+                   (reinterpret_cast<uintptr_t>(g.D) & 7) == 0 && (reinterpret_cast<uintptr_t>(g.P) & 15) == 0;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int row = m0 + wm + 16 * i + fr;
+      const int c0 = n0 + wn + 16 * j + 4 * fg;
+      if (row >= g.M) continue;
+      if (vec) {
+        if (c0 >= g.N) continue;
+        if (c0 < g.n_bf) {
+          *reinterpret_cast<uint2*>(g.D + (size_t)row * g.ldd + (size_t)z * g.d_zoff + c0) =
+              make_uint2(f32_to_bf16_bits(acc[i][j][0]) | (f32_to_bf16_bits(acc[i][j][1]) << 16),
+                         f32_to_bf16_bits(acc[i][j][2]) | (f32_to_bf16_bits(acc[i][j][3]) << 16));
+        } else {
+          *reinterpret_cast<f32x4*>(g.P + (size_t)ks * g.p_ks + (size_t)row * g.ldp + (size_t)z * g.p_zoff +
+                                    (c0 - g.n_bf)) = acc[i][j];
+        }
+        continue;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int col = c0 + e;
+        if (col >= g.N) continue;
+        if (col < g.n_bf)
+          g.D[(size_t)row * g.ldd + (size_t)z * g.d_zoff + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][e]);
+        else
+          g.P[(size_t)ks * g.p_ks + (size_t)row * g.ldp + (size_t)z * g.p_zoff + (col - g.n_bf)] = acc[i][j][e];
+      }
+    }
+}
+
 // Split-K partials of an fp32 block [M][n1 + n2] (row pitch ldp, partial pitch p_ks) summed in
 // partial order and stored in bfloat16: columns c < n1 to D1 [M][ldd1], the rest to D2 [M][ldd2].
 __global__ __launch_bounds__(256) void k_sum_bf16(const float* __restrict__ P, int ksplit, int64_t p_ks,
@@ -207,12 +330,26 @@ __global__ __launch_bounds__(256) void k_finish_q(const float* __restrict__ P, i
 // ks / 256) / ks, with ties going to the workgroup count nearest 512 (two per CU: one
 // workgroup per CU streams slower, e.g. Pro's 256 group tiles unsplit took 122 us against
 // 104 us split in two).  Each K range
-// stays a multiple of the 64-deep stage and at least 256 long.
-int gemm_tile(int M) { return M >= GM_BIG_M ? 128 : 64; }
+// stays a multiple of the 64-deep stage and at least 256 long.  Long inputs (256x256 tiles)
+// are not split once their tiles fill half the CUs: there the float32 partials (written and
+// summed again: 8 x 8192 x 1600 floats for the Flash latent split 8 ways) cost more than the
+// CUs the split would add.
+// The 256x256 tiles run one workgroup per CU, so they are taken only where their rounds of 256
+// workgroups are at least 80 % full (or there are four or more rounds): 8192 x 2560 makes 320
+// tiles, whose second round would leave three CUs in four idle.
+int gemm_tile(int M, int N, int Z) {
+  if (M >= GM_WIDE_M) {
+    const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256) * Z;
+    const int64_t rounds = (tiles + 255) / 256;
+    if (rounds >= 4 || tiles * 5 >= rounds * 256 * 4) return 256;
+  }
+  return M >= GM_BIG_M ? 128 : 64;
+}
 
 int gemm_ksplit(int M, int N, int Z, int K) {
-  const int t = gemm_tile(M);
+  const int t = gemm_tile(M, N, Z);
   const int tiles = ((M + t - 1) / t) * ((N + t - 1) / t) * Z;
+  if (t == 256 && tiles >= 128) return 1;
   int best = 1;
   double best_cost = (double)((tiles + 255) / 256);
   for (int ks = 2; K % (ks * 64) == 0 && K / ks >= 256; ks *= 2) {
@@ -245,9 +382,10 @@ Plan plan_of(int M, int N, int Z, int K, int n_direct) {
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int Z, hipStream_t s) {
-  const int t = gemm_tile(g.M);
+  const int t = gemm_tile(g.M, g.N, Z);
   dim3 grid((g.N + t - 1) / t, (g.M + t - 1) / t, Z * g.ksplit);
-  if (t == 128) hipLaunchKernelGGL((k_gemm_bf16<128, 128, 32>), grid, dim3(256), 0, s, g);
+  if (t == 256) hipLaunchKernelGGL((k_gemm_wide<64>), grid, dim3(512), 0, s, g);
+  else if (t == 128) hipLaunchKernelGGL((k_gemm_bf16<128, 128, 32>), grid, dim3(256), 0, s, g);
   else hipLaunchKernelGGL((k_gemm_bf16<64, 64, 64>), grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }

@@ -164,6 +164,20 @@ def test_projections_pro_prefill_sampled():
     _check_output_exact(cfg, W, o, rows, "pro prefill")
 
 
+def test_projections_flash_long_ragged():
+    """Flash shapes for 4100 tokens: the 256x256-tile kernel of long inputs with a ragged last
+    row tile (4 rows), sampled rows across its row tiles, wave rows and the tail."""
+    cfg = _cfg("c2")
+    W = synth.proj_weights(cfg, 1536, 8, 1024, seed=57, device=DEV, exact_first=True)
+    T = 4100
+    rows = np.array([0, 1, 127, 128, 255, 256, 2047, 4095, 4096, 4099])
+    h = synth.small_ints((T, cfg["d"]), -1, 1, 1.0, DEV, 57, 1).to(torch.bfloat16)
+    _check_query_exact(cfg, W, h, rows, "flash long")
+    del h
+    o = synth.small_ints((T, cfg["n_h"], cfg["c"]), -1, 1, 1.0, DEV, 57, 2).to(torch.bfloat16)
+    _check_output_exact(cfg, W, o, rows, "flash long")
+
+
 def test_projections_realistic_values():
     """N(0,1) hidden states and attention outputs, N(0, 1/fan_in) weights everywhere (Flash,
     300 tokens: the 128-row tiles with a ragged tail): the rounding of the latent and of the
