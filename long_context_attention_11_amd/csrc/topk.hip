@@ -492,18 +492,21 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_filter(FilterArgs fa) {
 }
 
 // The threshold pass and a one-token projection in one launch (they are independent), so the
-// projection's weight stream runs beside the filter.  Blocks [0, Q * nseg) filter; in the
-// rest, waves 0 .. upb - 1 run one projection unit each and the others have nothing to do,
-// upb chosen so that the workgroups of the launch fill the 256 CUs once: each CU then streams
-// its fair share of the weights.
+// projection's weight stream runs beside the filter.  Blocks [0, Q * nseg) filter and then run
+// tpb projection units (waves 0 .. tpb - 1, one unit each: units ncar * upb + tpb * b + wave);
+// in the rest (the carriers) waves 0 .. upb - 1 run one unit each.  The launch fills the 256
+// CUs once, and upb and tpb are chosen so that both kinds of workgroup finish together: each
+// CU then streams its share of the weights.
 template <bool BF>
 __global__ __launch_bounds__(TK_THREADS) void k_topk_filter_project(FilterArgs fa, int Q, ProjectStepArgs pa,
-                                                                     int units, int upb) {
+                                                                     int units, int upb, int tpb, int ncar) {
   __shared__ TopkShared sh;
   const int nf = Q * fa.nseg;
   const int b = blockIdx.x, wave = threadIdx.x >> 6;
   if (b < nf) {
     topk_filter_body<BF>(fa, b % Q, b / Q, 1, sh);
+    const int u = ncar * upb + tpb * b + wave;
+    if (wave < tpb && u < units) project_unit<2>(pa, u);
   } else if (wave < upb) {
     const int u = upb * (b - nf) + wave;
     if (u < units) project_unit<2>(pa, u);
@@ -515,6 +518,28 @@ int carry_units_per_block(int nf, int units) {
   if (nf >= 256) return 0;
   const int upb = (units + (256 - nf) - 1) / (256 - nf);
   return upb <= TK_WAVES ? upb : 0;
+}
+
+// The split of the units between the 256 - nf carriers (upb each) and the nf threshold
+// workgroups (tpb each, after their filter).  One CU streams some 25 GB/s, and a threshold
+// workgroup's filter takes about 4 us, so a threshold workgroup finishes with the carriers
+// when it runs r = 100 KB / (bytes per unit) fewer units (a unit's weights are 2 tiles x 16
+// columns x K / PU_SLICES bf16 = 4 K bytes): upb is the smallest count with nf max(0, upb - r)
+// + (256 - nf) upb >= units, and tpb the fewest the threshold workgroups then need.
+void carry_split(int nf, int units, int K, int* upb, int* tpb) {
+  const int ncar = 256 - nf;
+  const int r = (int)((25000 + K / 2) / K);
+  for (int u = 1; u <= TK_WAVES; ++u) {
+    const int t = std::min(TK_WAVES, std::max(0, u - r));
+    if ((int64_t)nf * t + (int64_t)ncar * u >= units) {
+      *upb = u;
+      const int64_t rest = std::max<int64_t>(0, units - (int64_t)ncar * u);
+      *tpb = (int)((rest + nf - 1) / nf);
+      return;
+    }
+  }
+  *upb = carry_units_per_block(nf, units);
+  *tpb = 0;
 }
 
 struct FinalShared {
@@ -924,10 +949,13 @@ hipError_t launch_topk_t(const csa_dims& d, const csa_cache& c, const int32_t* q
   const FilterArgs fa{scores, ld, q_seq, q_pos, c.n_entries, d.m, k, cs, nseg, spw, ci, ck, cc, fvis};
   if (step) {
     const int units = project_units(step->NP, step->M, 2);
-    const int upb = carry_units_per_block(Q * nseg, units);
-    if (upb == 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_topk_filter_project<BF>, dim3(Q * nseg + (units + upb - 1) / upb), dim3(TK_THREADS), 0, s,
-                       fa, Q, *step, units, upb);
+    if (carry_units_per_block(Q * nseg, units) == 0) return hipErrorInvalidValue;
+    int upb, tpb;
+    carry_split(Q * nseg, units, step->K, &upb, &tpb);
+    // carriers needed once the threshold workgroups have taken their share
+    const int ncar = (int)std::min<int64_t>(256 - Q * nseg, ((int64_t)units + upb - 1) / upb);
+    hipLaunchKernelGGL(k_topk_filter_project<BF>, dim3(Q * nseg + ncar), dim3(TK_THREADS), 0, s,
+                       fa, Q, *step, units, upb, tpb, ncar);
   } else {
     hipLaunchKernelGGL(k_topk_filter<BF>, dim3(Q, (nseg + spw - 1) / spw), dim3(TK_THREADS), 0, s, fa);
   }
