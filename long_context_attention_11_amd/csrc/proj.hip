@@ -56,31 +56,35 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
   const int z = blockIdx.z / g.ksplit, ks = blockIdx.z % g.ksplit;
   const int k_begin = ks * g.kchunk, k_end = min(g.K, k_begin + g.kchunk);
   const int lr = tid / PR, lc = (tid % PR) * 8;
+  // Rows past M (columns past N) load the last row (column) again: they only feed outputs
+  // past M (N), which are not stored, so every load is unconditional (no branch per load).
   const uint16_t* arow[PA];
   const uint16_t* brow[PB];
-  bool aval[PA], bval[PB];
 #pragma unroll
   for (int h = 0; h < PA; ++h) {
     const int r = lr + RPP * h;
-    aval[h] = m0 + r < g.M;
     arow[h] = g.A + (size_t)min(m0 + r, g.M - 1) * g.lda + (size_t)z * g.a_zoff;
   }
 #pragma unroll
   for (int h = 0; h < PB; ++h) {
     const int r = lr + RPP * h;
     const int n = min(n0 + r, g.N - 1);
-    bval[h] = n0 + r < g.N;
     brow[h] = (n < g.nb1 ? g.B + (size_t)n * g.ldb : g.B2 + (size_t)(n - g.nb1) * g.ldb) +
               (size_t)z * g.b_zstride;
   }
   uint4 ra[PA], rb[PB];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int h = 0; h < PA; ++h)
-      ra[h] = aval[h] ? *reinterpret_cast<const uint4*>(arow[h] + k0 + lc) : make_uint4(0, 0, 0, 0);
+    for (int h = 0; h < PA; ++h) {
+      const uint4 v = *reinterpret_cast<const uint4*>(arow[h] + k0 + lc);
+      ra[h] = v;
+    }
 #pragma unroll
-    for (int h = 0; h < PB; ++h)
-      rb[h] = bval[h] ? *reinterpret_cast<const uint4*>(brow[h] + k0 + lc) : make_uint4(0, 0, 0, 0);
+    for (int h = 0; h < PB; ++h) {
+      const uint4 v = *reinterpret_cast<const uint4*>(brow[h] + k0 + lc);
+      rb[h] = v;
+    }
+    asm volatile("" ::: "memory");   // compiler-only fence, as in k_gemm_wide
   };
   auto sstore = [&](int buf) {
 #pragma unroll
