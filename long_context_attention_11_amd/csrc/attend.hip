@@ -17,6 +17,7 @@
 #include <type_traits>
 
 #include "csa_internal.h"
+#include "fold.h"
 
 namespace csa {
 namespace {
@@ -47,6 +48,9 @@ struct AttendArgs {
   uint16_t* out;              // [Q][n_h][512] bf16 (splits == 1)
   uint16_t* part_o;           // [Q][n_h][splits][512] bf16 (splits > 1)
   float* part_ml;             // [Q][n_h][splits][2]
+  int n_att;                  // attention workgroups; with fold_on, the blocks past them fold
+  int fold_on;                // a one-token step's fold shares the launch (dense, T = 1)
+  FoldArgs fo;
 };
 
 // Sum of squares of 8 bf16 values packed in a uint4 (packed bf16 dot products with float32
@@ -182,11 +186,17 @@ void k_attend_hs(AttendArgs a) {
   __shared__ int ridx[NRIDX];
   __shared__ float rope_cs[AR];
 
+  // A one-token step's fold in the same launch: its blocks run the fold kernel's code.
+  if (a.fold_on && (int)blockIdx.x >= a.n_att) {
+    const int f = (int)blockIdx.x - a.n_att, fx = fold_grid_x(a.fo);
+    fold_block<4, true>(a.fo, f % fx, f / fx, &redm[0][0]);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int nhs = a.n_h / 16;
   // the head groups of one (query, split) are adjacent, so they share an XCD's L2
-  const uint32_t L = xcd_logical_id(blockIdx.x, gridDim.x);
+  const uint32_t L = xcd_logical_id(blockIdx.x, a.n_att);
   const int hgrp = L % nhs;
   const int rest = L / nhs;
   const int split = rest % a.splits;
@@ -235,6 +245,26 @@ void k_attend_hs(AttendArgs a) {
   const int nsel = SPARSE ? a.k : V;
   const int nrows = nsel + (tau - w0 + 1);
   const int r_hi = min(nrows, r_lo + a.tiles_per_split * HS_ROWS);
+  // With the fold in this launch the new token's window row may not be in the ring yet: the
+  // workgroups whose part ends with it finalize it from the token's partial projections with
+  // the fold's own code (so the same bytes as the fold stores), store it, and read it back
+  // like any other row.
+  if constexpr (!SPARSE) {
+    if (a.fold_on && r_hi == nrows && r_lo < nrows) {   // uniform over the workgroup
+      const int u = 2 * tid;
+      float x0 = 0.f, x1 = 0.f;
+      if (u < a.fo.c) {
+        x0 = proj<true>(a.fo, seq, tau, tau, u);
+        x1 = proj<true>(a.fo, seq, tau, tau, u + 1);
+      }
+      const int slot = tau % a.win_cap;
+      finalize_store<4>(a.fo, x0, x1, tau, a.fo.win + ((size_t)seq * a.win_cap + slot) * a.fo.rowB, &reds[0][0]);
+      if (tid == 0) a.fo.win_pos[(size_t)seq * a.win_cap + slot] = tau;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+  }
   // paged: row numbers are pool rows (kv is the pool), looked up once per entry here, so
   // that the loop below reads them from LDS like an index list; entries past the visible
   // ones become -1, and only window rows then need the visibility test
@@ -716,9 +746,10 @@ size_t attend_workspace_bytes(const csa_dims& d, int32_t Q, int32_t cap, int whi
 hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
                          const float* gamma_q, const float* sink, const int32_t* q_seq,
                          const int32_t* q_pos, int32_t Q, const int32_t* idx, void* out,
-                         void* ws, hipStream_t s) {
+                         void* ws, hipStream_t s, const FoldArgs* fold) {
   const float scale = d.scale > 0.f ? d.scale : 1.0f / sqrtf((float)d.c);
   if (d.kv_fmt == CSA_FMT_F32) {
+    if (fold) return hipErrorInvalidValue;   // the fold rides only in the quantized kernel
     hipLaunchKernelGGL(k_attend_f32, dim3(Q * d.n_h), dim3(64), 0, s, (const float*)q, gamma_q,
                        sink, q_seq, q_pos, d.n_h, idx, d.top_k, (const float*)c.kv,
                        (const float*)c.win, c.win_pos, c.n_entries, row_map(d, c), c.win_cap, d.m,
@@ -755,7 +786,13 @@ hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
   a.part_o = (uint16_t*)ws;
   const size_t po = ((size_t)Q * d.n_h * p.splits * AC * sizeof(uint16_t) + 255) / 256 * 256;
   a.part_ml = p.splits > 1 ? (float*)((char*)ws + po) : nullptr;
-  const dim3 grid(Q * (d.n_h / 16) * p.splits);
+  a.n_att = Q * (d.n_h / 16) * p.splits;
+  a.fold_on = fold ? 1 : 0;
+  if (fold) {
+    if (idx || fold->T != 1 || !fold->part || fold->keys_entry) return hipErrorInvalidValue;
+    a.fo = *fold;
+  }
+  const dim3 grid(a.n_att + (fold ? fold_grid_x(*fold) * fold->B : 0));
 #define ATT_LAUNCH(F)                                                                         \
   if (a.rm.bt) {                                                                              \
     if (idx) hipLaunchKernelGGL((k_attend_hs<true, true, F>), grid, dim3(256), 0, s, a);      \

@@ -213,6 +213,9 @@ int csa_workspace_size(const csa_dims* dims, int32_t op, int32_t B, int32_t T, i
         phase = std::max(phase, align_up(index_ws_carry(d, Qn, cap), 256) + project_part_bytes(d, B));
       // forward attends a layer with an indexer sparsely
       phase = std::max(phase, attend_workspace_bytes(d, Qn, cap, has_indexer(d) ? 0 : 1));
+      // one-token HCA steps keep the projection partials through the attention launch
+      if (!has_indexer(d) && T == 1 && d.kv_fmt != CSA_FMT_F32)
+        phase = std::max(phase, align_up(attend_workspace_bytes(d, Qn, cap, 1), 256) + compress_ws(d, B, T));
       L.add(2, phase);
       *bytes = L.total;
       return CSA_OK;
@@ -497,6 +500,24 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, const csa_cache* cac
     hipError_t e = launch_attend(d, *cache, q, gamma_q, sink, nullptr, pos0, Qn, idx, out, phase_ws, stream);
     if (e != hipSuccess) return hip_fail(e, "attend launch");
     return CSA_OK;
+  }
+
+  // One new token per sequence of an HCA layer: projection, then attention with the fold as
+  // extra workgroups of its launch (the attention workgroups that need the new token's
+  // window row finalize it themselves), then the merge: one launch fewer than compressing
+  // first.  The query at tau sees floor(tau / m) entries, none of them the one this step may
+  // complete, and the fold's other stores (state ring, entry, count) are not read by it.
+  if (!has_indexer(d) && project_step_ok(d, T) && d.kv_fmt != CSA_FMT_F32) {
+    const size_t att_bytes = align_up(attend_workspace_bytes(d, Qn, cache->cap, 1), 256);
+    if (att_bytes + project_part_bytes(d, cache->B) <= phase_bytes) {
+      float* part = (float*)((char*)phase_ws + att_bytes);
+      hipError_t e = launch_project_step(d, *w, *cache, H, part, stream);
+      if (e != hipSuccess) return hip_fail(e, "projection launch");
+      const FoldArgs fo = fold_args(d, *w, *cache, T, pos0, nullptr, part);
+      e = launch_attend(d, *cache, q, gamma_q, sink, nullptr, pos0, Qn, nullptr, out, phase_ws, stream, &fo);
+      if (e != hipSuccess) return hip_fail(e, "attend launch");
+      return CSA_OK;
+    }
   }
 
   st = csa_compress(dims, w, cache, H, T, pos0, phase_ws, phase_bytes, stream);

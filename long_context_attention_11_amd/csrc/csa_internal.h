@@ -305,10 +305,12 @@ hipError_t launch_topk(const csa_dims& d, const csa_cache& c, const int32_t* q_s
                        int32_t* idx, void* ws, hipStream_t s,
                        const struct ProjectStepArgs* step = nullptr,
                        const struct FoldArgs* fold = nullptr);
+// fold: with dense attention of one-token HCA steps, the step's fold runs as extra
+// workgroups of the attention launch (its partial projections already computed).
 hipError_t launch_attend(const csa_dims& d, const csa_cache& c, const void* q,
                          const float* gamma_q, const float* sink, const int32_t* q_seq,
                          const int32_t* q_pos, int32_t Q, const int32_t* idx, void* out,
-                         void* ws, hipStream_t s);
+                         void* ws, hipStream_t s, const FoldArgs* fold = nullptr);
 hipError_t launch_reduce_partials(const float* P, int32_t ksplit, int64_t n, float* out,
                                   hipStream_t s);
 hipError_t launch_query_meta(int32_t B, int32_t T, const int32_t* pos0, int32_t* q_seq,

@@ -551,6 +551,6 @@ __device__ __forceinline__ void fold_block(const FoldArgs& a, int slot, int b, f
 FoldArgs fold_args(const csa_dims& d, const csa_weights& w, const csa_cache& c, int32_t T,
                    const int32_t* pos0, const float* P, const float* part = nullptr);
 // Blocks per sequence: T raw rows, T/m + 1 entry slots, and with part the state writers.
-inline int fold_grid_x(const FoldArgs& a) { return a.T + a.T / a.m + 1 + (a.part ? (a.NP + 511) / 512 : 0); }
+__host__ __device__ inline int fold_grid_x(const FoldArgs& a) { return a.T + a.T / a.m + 1 + (a.part ? (a.NP + 511) / 512 : 0); }
 
 }  // namespace csa

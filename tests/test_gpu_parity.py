@@ -506,6 +506,46 @@ def test_q_forward_decode_steps(idx_fmt, paged):
             assert_close_q(go, o_ref, f"decode out seq {b} tau={tau}")
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_hca_forward_decode_steps(paged):
+    """Eight one-token forward steps of an HCA layer (m' = 128, tau = 250 .. 257 on 2
+    sequences; the step at 255 completes entry 1 and the next ones attend over it): the path
+    whose fold runs inside the attention launch, the attention workgroups finalizing the new
+    token's window row themselves.  Outputs and the cache afterwards against the oracle."""
+    cfg = synth.config("c5")
+    dims = L.Dims.from_config(cfg)
+    od = oracle_dims(cfg)
+    B, n0, steps = 2, 250, 8
+    W = synth.weights(cfg, seed=29, device=DEV)
+    lw = lib_weights(W, False)
+    Hs = torch.stack([synth.hidden(cfg, b, 0, n0 + steps, seed=29, device=DEV) for b in range(B)])
+    cache = paged_cache(dims, B, 8, 128, seed=29) if paged else L.Cache(dims, B=B, cap=8, win_cap=128)
+    _compress_chunks(dims, W, cache, Hs[:, :n0].contiguous(), [100, 150])
+    qs = synth.queries(cfg, B * steps, seed=29, device=DEV)
+    ws = _ws(L.csa_workspace_size(dims, L.OP_FORWARD, B=B, T=1, cap=cache.cap))
+    outs = []
+    for t in range(steps):
+        print(f"hca forward step tau={n0 + t} paged={paged}", flush=True)
+        rows = [b * steps + t for b in range(B)]
+        out = torch.zeros((B, cfg["n_h"], cfg["c"]), dtype=torch.bfloat16, device=DEV)
+        L.csa_forward(dims, lw, cache, Hs[:, n0 + t:n0 + t + 1].contiguous(), 1, _i32([n0 + t] * B),
+                      qs["q"][rows].contiguous(), None, None, W["gamma_q"], W["sink"], out, None, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    cache = logical(cache)
+    OW = oracle_weights(W)
+    q, sink = host64(qs["q"]), host64(W["sink"])
+    nb = (n0 + steps) // cfg["m"]
+    for b in range(B):
+        comp = R.compress_sequence(host64(Hs[b]), OW, od)
+        _check_cache_vs_oracle(cfg, cache, b, comp, n0 + steps, f"hca decode steps seq {b}")
+        for t in range(steps):
+            tau = n0 + t
+            o_ref = R.query_step(tau, q[b * steps + t], None, None, None, sink, comp["entry"], None,
+                                 lambda p: comp["raw"][p], nb, od)[0]
+            assert_close_q(host64(outs[t][b:b + 1])[0], o_ref, f"hca decode out seq {b} tau={tau}")
+
+
 @pytest.mark.parametrize("idx_fmt", ["e4m3", "mxfp4"])
 def test_index_scores_grouped_equals_plain(idx_fmt):
     """csa_index_scores_grouped (key tiles shared by 16 queries of one sequence, the prefill
