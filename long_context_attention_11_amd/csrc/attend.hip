@@ -186,11 +186,14 @@ void k_attend_hs(AttendArgs a) {
   __shared__ int ridx[NRIDX];
   __shared__ float rope_cs[AR];
 
-  // A one-token step's fold in the same launch: its blocks run the fold kernel's code.
-  if (a.fold_on && (int)blockIdx.x >= a.n_att) {
-    const int f = (int)blockIdx.x - a.n_att, fx = fold_grid_x(a.fo);
-    fold_block<4, true>(a.fo, f % fx, f / fx, &redm[0][0]);
-    return;
+  // A one-token step's fold in the same launch (dense attention only, so the sparse
+  // instances do not carry its registers): its blocks run the fold kernel's code.
+  if constexpr (!SPARSE) {
+    if (a.fold_on && (int)blockIdx.x >= a.n_att) {
+      const int f = (int)blockIdx.x - a.n_att, fx = fold_grid_x(a.fo);
+      fold_block<4, true>(a.fo, f % fx, f / fx, &redm[0][0]);
+      return;
+    }
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
